@@ -1,0 +1,202 @@
+"""fp64 CPU oracle of the NSA forward pass (test infrastructure).
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and ``bench.py``'s CPU-baseline leg may import
+this package.  It loads ``liboracle.so`` built from ``nsa_oracle.c`` with gcc (OpenMP),
+and shares no code with the GPU library.  ``bruteforce`` is an independent dense-mask
+numpy formulation used to pin the C oracle on tiny shapes.
+
+Every function here is a thin ctypes wrapper: arrays go in as contiguous float64 / int32.
+Parity status of each function (what pins it) is listed in ``tests/test_oracle_pins.py``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "nsa_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+_D = ctypes.POINTER(ctypes.c_double)
+_I = ctypes.POINTER(ctypes.c_int)
+
+
+def build(force: bool = True) -> str:
+    """Compile liboracle.so with gcc (-O2 -fopenmp).  Returns the library path."""
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp"
+        subprocess.check_call(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11",
+                               "-Wall", "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            build()
+        L = ctypes.CDLL(_LIB_PATH)
+        L.oracle_compress_linear.argtypes = [ctypes.c_int] * 5 + [_D, _D, _D, _I, ctypes.c_int, _D]
+        L.oracle_compress_mean.argtypes = [ctypes.c_int] * 3 + [_D, _I, ctypes.c_int, _D]
+        L.oracle_score_select.argtypes = ([ctypes.c_int] * 13 + [ctypes.c_double, _D, _I, ctypes.c_int,
+                                          _D, _D, _D, _D, _D, _I, _D])
+        L.oracle_score_select.restype = ctypes.c_int
+        L.oracle_select_from_scores.argtypes = [ctypes.c_int] * 5 + [_I, _D, _I, _D]
+        L.oracle_select_from_scores.restype = ctypes.c_int
+        L.oracle_attend.argtypes = ([ctypes.c_int] * 8 + [ctypes.c_double, ctypes.c_int, _D, _I, ctypes.c_int,
+                                    _D, _D, _I, _D, _D, _D, _D, _D])
+        L.oracle_attend.restype = ctypes.c_int
+        L.oracle_causal_attention.argtypes = [ctypes.c_int] * 4 + [ctypes.c_double, _D, _D, _D, _D]
+        L.oracle_num_threads.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _d(a):
+    return np.ascontiguousarray(a, dtype=np.float64)
+
+
+def _i(a):
+    return np.ascontiguousarray(a, dtype=np.int32)
+
+
+def _pd(a):
+    return None if a is None else a.ctypes.data_as(_D)
+
+
+def _pi(a):
+    return None if a is None else a.ctypes.data_as(_I)
+
+
+def num_threads() -> int:
+    return int(lib().oracle_num_threads())
+
+
+# ---------------------------------------------------------------------------
+# step 1
+# ---------------------------------------------------------------------------
+def compress_linear(X, pe, W, l: int, s: int, blocks=None) -> np.ndarray:
+    """Linear phi of the listed blocks of one head's token rows X [n_tok, d] -> [nblk, d_out]."""
+    X, W = _d(X), _d(W)
+    pe = None if pe is None else _d(pe)
+    n_tok, d = X.shape
+    d_out = W.shape[1]
+    assert W.shape[0] == l * d
+    if blocks is None:
+        blocks = np.arange((n_tok - l) // s + 1 if n_tok >= l else 0)
+    blocks = _i(blocks)
+    assert blocks.size == 0 or (blocks.max() * s + l <= n_tok and blocks.min() >= 0)
+    out = np.zeros((blocks.size, d_out), dtype=np.float64)
+    lib().oracle_compress_linear(n_tok, d, d_out, l, s, _pd(X), _pd(pe), _pd(W), _pi(blocks),
+                                 blocks.size, _pd(out))
+    return out
+
+
+def compress_mean(X, l: int, s: int, blocks=None) -> np.ndarray:
+    X = _d(X)
+    n_tok, d = X.shape
+    if blocks is None:
+        blocks = np.arange((n_tok - l) // s + 1 if n_tok >= l else 0)
+    blocks = _i(blocks)
+    assert blocks.size == 0 or (blocks.max() * s + l <= n_tok and blocks.min() >= 0)
+    out = np.zeros((blocks.size, d), dtype=np.float64)
+    lib().oracle_compress_mean(d, l, s, _pd(X), _pi(blocks), blocks.size, _pd(out))
+    return out
+
+
+# ---------------------------------------------------------------------------
+# steps 2-4
+# ---------------------------------------------------------------------------
+def score_select(cfg, Q_rows, rows, Kc, Vc=None, want_scores=True, want_ocmp=True) -> dict:
+    """Compressed attention + block scores + selection for listed rows of one batch element.
+
+    ``cfg`` needs the attributes of an NSA configuration (num_kv_heads, heads_per_group, d_k,
+    d_v, cmp_block, cmp_stride, slc_block, top_n, n_init, n_local, score_mode, scale,
+    seq_len).  Q_rows [nrows, H, dk]; Kc [Hkv, n_cmp, dk]; Vc [Hkv, n_cmp, dv].
+    Returns dict(lse [nrows,H], o_cmp [nrows,H,dv], scores [nrows,Hkv,n_slc],
+    sel [nrows,Hkv,top_n] int32, gap [nrows,Hkv]).
+    """
+    Hkv, G = cfg.num_kv_heads, cfg.heads_per_group
+    H = Hkv * G
+    Q_rows, Kc = _d(Q_rows), _d(Kc)
+    rows = _i(rows)
+    nrows = rows.size
+    n_cmp = Kc.shape[1]
+    n_slc = -(-cfg.seq_len // cfg.slc_block)
+    mode = int(cfg.score_mode)
+    Vc = None if (Vc is None or mode == 1) else _d(Vc)
+    lse = np.zeros((nrows, H))
+    ocmp = np.zeros((nrows, H, cfg.d_v)) if (want_ocmp and Vc is not None) else None
+    scores = np.zeros((nrows, Hkv, n_slc)) if want_scores else None
+    sel = np.zeros((nrows, Hkv, cfg.top_n), dtype=np.int32)
+    gap = np.zeros((nrows, Hkv))
+    rc = lib().oracle_score_select(mode, Hkv, G, cfg.d_k, cfg.d_v, cfg.cmp_block, cfg.cmp_stride,
+                                   n_cmp, cfg.slc_block, n_slc, cfg.top_n, cfg.n_init, cfg.n_local,
+                                   float(cfg.scale), _pd(Q_rows), _pi(rows), nrows, _pd(Kc), _pd(Vc),
+                                   _pd(lse), _pd(ocmp), _pd(scores), _pi(sel), _pd(gap))
+    if rc != 0:
+        raise ValueError(f"oracle_score_select failed ({rc})")
+    return {"lse": lse, "o_cmp": ocmp, "scores": scores, "sel": sel, "gap": gap}
+
+
+def select_from_scores(scores, jc, top_n: int, n_init: int, n_local: int):
+    """Step 4 alone: scores [nrows, n_slc], own block jc [nrows] -> (sel [nrows, top_n], gap)."""
+    scores = _d(scores)
+    jc = _i(jc)
+    nrows, n_slc = scores.shape
+    sel = np.zeros((nrows, top_n), dtype=np.int32)
+    gap = np.zeros(nrows)
+    rc = lib().oracle_select_from_scores(nrows, n_slc, top_n, n_init, n_local, _pi(jc), _pd(scores),
+                                         _pi(sel), _pd(gap))
+    if rc != 0:
+        raise ValueError("top_n smaller than the number of forced blocks")
+    return sel, gap
+
+
+# ---------------------------------------------------------------------------
+# steps 5-7
+# ---------------------------------------------------------------------------
+def attend(cfg, Q_rows, rows, K, V, sel, o_cmp=None, gates=None, branches=None) -> dict:
+    """Selected + window branches and the gated sum for listed rows of one batch element.
+
+    Q_rows [nrows, H, dk]; K [Hkv, n_tok, dk]; V [Hkv, n_tok, dv]; sel [nrows, Hkv, top_n];
+    o_cmp [nrows, H, dv]; gates [nrows, H, 3] logits (None -> weights 1).
+    Returns dict(out, o_slc, o_win), each [nrows, H, dv].
+    """
+    Hkv, G = cfg.num_kv_heads, cfg.heads_per_group
+    H = Hkv * G
+    branches = cfg.branches if branches is None else branches
+    Q_rows, K, V = _d(Q_rows), _d(K), _d(V)
+    rows, sel = _i(rows), _i(sel)
+    nrows = rows.size
+    n_tok = K.shape[1]
+    if branches & 1:
+        assert o_cmp is not None
+        o_cmp = _d(o_cmp)
+    else:
+        o_cmp = None
+    gates = None if gates is None else _d(gates)
+    out = np.zeros((nrows, H, cfg.d_v))
+    oslc = np.zeros_like(out)
+    owin = np.zeros_like(out)
+    rc = lib().oracle_attend(Hkv, G, cfg.d_k, cfg.d_v, n_tok, cfg.slc_block, sel.shape[-1], cfg.window,
+                             float(cfg.scale), branches, _pd(Q_rows), _pi(rows), nrows, _pd(K), _pd(V),
+                             _pi(sel), _pd(o_cmp), _pd(gates), _pd(out), _pd(oslc), _pd(owin))
+    if rc != 0:
+        raise MemoryError("oracle_attend failed")
+    return {"out": out, "o_slc": oslc, "o_win": owin}
+
+
+def causal_attention(Q, K, V, scale: float, window: int = 0) -> np.ndarray:
+    """Textbook causal (optionally sliding-window) attention of one head: Q [n,dk] -> [n,dv]."""
+    Q, K, V = _d(Q), _d(K), _d(V)
+    n, dk = Q.shape
+    dv = V.shape[1]
+    out = np.zeros((n, dv))
+    lib().oracle_causal_attention(n, dk, dv, window, float(scale), _pd(Q), _pd(K), _pd(V), _pd(out))
+    return out

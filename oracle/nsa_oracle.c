@@ -1,0 +1,426 @@
+/*
+ * nsa_oracle.c - plain, slow, fp64 CPU oracle of the Native Sparse Attention (NSA)
+ * forward pass and of the MoBA-style mean-pooled block selection.
+ *
+ * TEST INFRASTRUCTURE.  Only the tests, the smoke check and the bench's CPU-baseline
+ * leg may load this library.  It shares no code, header, table or helper with the
+ * GPU library; neither includes or links the other.
+ *
+ * Every function takes fp64 host arrays, works on one batch element, and loops in the
+ * plainest order: no tiling, no fusion, no online softmax.  Row-parallel loops use
+ * OpenMP (each row is computed independently, so threading does not change results).
+ *
+ * Sources, by page and section (the pages print no formulas; the steps below follow
+ * their prose, and where the prose is silent the plainest reading is taken):
+ *   [A] youtublog.net "Songlin Yang explains attention mechanisms..." (English page):
+ *       attention = softmax of query/key scores over the keys a query may access,
+ *       weighting the values; causal masking; NSA's three branches (compressed blocks,
+ *       selected blocks, sliding window) mixed by learned gates; a GQA group shares
+ *       one selection made from group-aggregated scores; MoBA mean-pools block keys.
+ *   [B] zjai.club episode notes, section 5 (one key and one value per contiguous
+ *       block; top-k blocks by block score, token-level attention inside them;
+ *       sliding window over nearby tokens), section 6 (each branch output scaled by a
+ *       gate computed from the current token, then summed), section 8 (scores summed
+ *       over the heads of a group, then one top-k), section 16 (MoBA: mean pooling,
+ *       query-mean dot product as the block score).
+ *   [C] sunshychen.top MoBA/NSA comparison: the current block is always attended and
+ *       causally masked; selecting every block gives full attention, selecting none
+ *       gives sliding-window attention; with fixed block sizes the compressed
+ *       attention scores are reused directly as selection scores; the NSA window
+ *       crosses block boundaries.
+ *
+ * Readings where the pages are silent (each is also listed in the design notes):
+ *   - phi is a linear map of the flattened block plus a learned intra-block position
+ *     embedding: cmp[i] = sum_{r<l, e<d} (X[i*s + r][e] + PE[r][e]) * W[r*d + e][:].
+ *   - compressed block i (tokens i*s .. i*s+l-1) is visible to query t only when all
+ *     its tokens are <= t; a query with no visible block has a zero compressed output.
+ *   - the selection score of block j is the sum, over the group's heads and over the
+ *     compressed blocks whose token span intersects block j, of the compressed
+ *     attention probabilities.
+ *   - top_n counts the forced blocks: the first n_init blocks and the n_local blocks
+ *     ending at the query's own block; the free slots take the highest-scoring other
+ *     eligible blocks, ties to the lower block index.
+ *   - the window holds the w most recent tokens including the query itself.
+ *   - the gated combination is a sum sigma(z_c)*o_c over the enabled branches.
+ *   - MoBA scores are the unscaled inner product of the query with the block's mean
+ *     key, over the complete blocks before the query's own block.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORACLE_API __attribute__((visibility("default")))
+
+/* ------------------------------------------------------------------------- */
+/* Step 1: block compression                                                 */
+/* ------------------------------------------------------------------------- */
+
+/* Linear phi over each listed block i:
+ *   out[b][o] = sum_{r<l} sum_{e<d} (X[(i*s + r)*d + e] + pe[r*d + e]) * W[(r*d + e)*d_out + o]
+ * X: [n_tok, d] token rows of one KV head; pe: [l, d] or NULL (zero); W: [l*d, d_out].
+ * blocks: block indices (must satisfy i*s + l <= n_tok); out: [nblk, d_out]. */
+ORACLE_API void oracle_compress_linear(int n_tok, int d, int d_out, int l, int s,
+                                       const double* X, const double* pe, const double* W,
+                                       const int* blocks, int nblk, double* out)
+{
+    (void)n_tok;
+#pragma omp parallel for schedule(dynamic)
+    for (int bi = 0; bi < nblk; ++bi) {
+        const int i = blocks[bi];
+        double* acc = out + (size_t)bi * d_out;
+        for (int o = 0; o < d_out; ++o) acc[o] = 0.0;
+        for (int r = 0; r < l; ++r) {
+            for (int e = 0; e < d; ++e) {
+                double x = X[(size_t)(i * s + r) * d + e];
+                if (pe) x += pe[r * d + e];
+                const double* wrow = W + (size_t)(r * d + e) * d_out;
+                for (int o = 0; o < d_out; ++o) acc[o] += x * wrow[o];
+            }
+        }
+    }
+}
+
+/* Mean-pooled block key (MoBA): out[b][e] = (1/l) * sum_{r<l} X[(i*s + r)*d + e]. */
+ORACLE_API void oracle_compress_mean(int d, int l, int s, const double* X,
+                                     const int* blocks, int nblk, double* out)
+{
+#pragma omp parallel for schedule(static)
+    for (int bi = 0; bi < nblk; ++bi) {
+        const int i = blocks[bi];
+        for (int e = 0; e < d; ++e) {
+            double sum = 0.0;
+            for (int r = 0; r < l; ++r) sum += X[(size_t)(i * s + r) * d + e];
+            out[(size_t)bi * d + e] = sum / (double)l;
+        }
+    }
+}
+
+/* ------------------------------------------------------------------------- */
+/* helpers                                                                   */
+/* ------------------------------------------------------------------------- */
+
+static double dot(const double* a, const double* b, int n)
+{
+    double s = 0.0;
+    for (int i = 0; i < n; ++i) s += a[i] * b[i];
+    return s;
+}
+
+/* Softmax of logits[0..n) into p, returning log(sum exp(logits)).  n >= 1. */
+static double softmax(const double* logits, int n, double* p)
+{
+    double mx = logits[0];
+    for (int i = 1; i < n; ++i) if (logits[i] > mx) mx = logits[i];
+    double sum = 0.0;
+    for (int i = 0; i < n; ++i) { p[i] = exp(logits[i] - mx); sum += p[i]; }
+    for (int i = 0; i < n; ++i) p[i] /= sum;
+    return mx + log(sum);
+}
+
+/* Number of compressed blocks whose whole span lies at or before token t. */
+static int visible_cmp(int t, int l, int s, int n_cmp)
+{
+    if (t < l - 1) return 0;
+    int n = (t - l + 1) / s + 1;
+    return n < n_cmp ? n : n_cmp;
+}
+
+
+typedef struct { double score; int j; } cand_t;
+
+/* Descending score; equal scores: ascending block index. */
+static int cand_cmp(const void* x, const void* y)
+{
+    const cand_t* a = (const cand_t*)x;
+    const cand_t* b = (const cand_t*)y;
+    if (a->score > b->score) return -1;
+    if (a->score < b->score) return 1;
+    return (a->j > b->j) - (a->j < b->j);
+}
+
+static int int_cmp(const void* x, const void* y)
+{
+    int a = *(const int*)x, b = *(const int*)y;
+    return (a > b) - (a < b);
+}
+
+/* Forced blocks for a query whose own block is jc: {0..n_init-1} U {jc-n_local+1..jc},
+ * restricted to 0..jc.  Writes a 0/1 flag per block 0..jc; returns the count. */
+static int forced_blocks(int jc, int n_init, int n_local, unsigned char* flag)
+{
+    int cnt = 0;
+    for (int j = 0; j <= jc; ++j) {
+        flag[j] = (unsigned char)((j < n_init) || (j > jc - n_local));
+        cnt += flag[j];
+    }
+    return cnt;
+}
+
+/* Step 4: pick blocks for one (query, group) from the scores of blocks 0..jc.
+ * sel: top_n entries, ascending, -1 padded.  Returns the score gap between the last
+ * chosen free block and the first rejected one (+inf when no free choice was cut). */
+static double select_blocks(int jc, int top_n, int n_init, int n_local, const double* score,
+                            int* sel, unsigned char* flag, cand_t* cand)
+{
+    const int n_elig = jc + 1;
+    const int n_forced = forced_blocks(jc, n_init, n_local, flag);
+    const int m = top_n < n_elig ? top_n : n_elig;
+    const int k = m - n_forced;           /* free slots (validated >= 0 by the caller) */
+    int nc = 0;
+    for (int j = 0; j <= jc; ++j)
+        if (!flag[j]) { cand[nc].score = score[j]; cand[nc].j = j; ++nc; }
+    qsort(cand, (size_t)nc, sizeof(cand_t), cand_cmp);
+    int cnt = 0;
+    for (int j = 0; j <= jc; ++j) if (flag[j]) sel[cnt++] = j;
+    for (int c = 0; c < k && c < nc; ++c) sel[cnt++] = cand[c].j;
+    qsort(sel, (size_t)cnt, sizeof(int), int_cmp);
+    for (int c = cnt; c < top_n; ++c) sel[c] = -1;
+    if (k > 0 && k < nc) return cand[k - 1].score - cand[k].score;
+    return INFINITY;
+}
+
+/* ------------------------------------------------------------------------- */
+/* Steps 2-4: compressed attention, block scores, group-shared selection      */
+/* ------------------------------------------------------------------------- */
+
+/* For each listed query row (position rows[r]) and each KV group g:
+ *   mode 0 (compressed-overlap scores):
+ *     per head h of the group: logits a_i = scale * <q_h, Kc[g][i]> over the visible
+ *     compressed blocks, p = softmax(a), lse = log sum exp(a), o_cmp = sum_i p_i Vc[g][i];
+ *     score[j] = sum_h sum_{visible i intersecting block j} p_i.
+ *   mode 1 (MoBA mean-key scores):
+ *     score[j] = sum_h <q_h, Kc[g][j]> (unscaled) for complete blocks j before the
+ *     query's own block (Kc holds the mean-pooled block keys); no compressed output.
+ *   then the selection of step 4 over blocks 0 .. rows[r]/lp.
+ *
+ * Q_rows: [nrows, H_kv*G, dk]; Kc: [H_kv, n_cmp, dk]; Vc: [H_kv, n_cmp, dv] (mode 0 only,
+ * may be NULL when o_cmp is not wanted).
+ * Outputs (NULL = not wanted, except sel): lse [nrows, H] (-inf for an empty row),
+ * o_cmp [nrows, H, dv], scores [nrows, H_kv, n_slc] (0 for blocks past the query's own),
+ * sel [nrows, H_kv, top_n], gap [nrows, H_kv].
+ * Returns 0, or -1 when top_n is smaller than the number of forced blocks. */
+ORACLE_API int oracle_score_select(int mode, int H_kv, int G, int dk, int dv,
+                                   int l, int s, int n_cmp, int lp, int n_slc,
+                                   int top_n, int n_init, int n_local, double scale,
+                                   const double* Q_rows, const int* rows, int nrows,
+                                   const double* Kc, const double* Vc,
+                                   double* lse_out, double* ocmp_out, double* scores_out,
+                                   int* sel_out, double* gap_out)
+{
+    const int H = H_kv * G;
+    if (top_n < n_init + n_local) return -1;
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic) reduction(|: bad)
+    for (int rg = 0; rg < nrows * H_kv; ++rg) {
+        const int r = rg / H_kv, g = rg % H_kv;
+        const int t = rows[r];
+        const int jc = t / lp;
+        double* score = (double*)calloc((size_t)n_slc, sizeof(double));
+        double* logit = (double*)malloc(sizeof(double) * (size_t)(n_cmp > 0 ? n_cmp : 1));
+        double* p = (double*)malloc(sizeof(double) * (size_t)(n_cmp > 0 ? n_cmp : 1));
+        unsigned char* flag = (unsigned char*)malloc((size_t)n_slc);
+        cand_t* cand = (cand_t*)malloc(sizeof(cand_t) * (size_t)n_slc);
+        if (!score || !logit || !p || !flag || !cand) { bad = 1; goto done; }
+
+        for (int hh = 0; hh < G; ++hh) {
+            const int h = g * G + hh;
+            const double* q = Q_rows + ((size_t)r * H + h) * dk;
+            if (mode == 0) {
+                const int nv = visible_cmp(t, l, s, n_cmp);
+                if (lse_out) lse_out[(size_t)r * H + h] = -INFINITY;
+                if (ocmp_out) for (int e = 0; e < dv; ++e) ocmp_out[((size_t)r * H + h) * dv + e] = 0.0;
+                if (nv == 0) continue;
+                for (int i = 0; i < nv; ++i)
+                    logit[i] = scale * dot(q, Kc + ((size_t)g * n_cmp + i) * dk, dk);
+                const double lse = softmax(logit, nv, p);
+                if (lse_out) lse_out[(size_t)r * H + h] = lse;
+                if (ocmp_out && Vc) {
+                    double* o = ocmp_out + ((size_t)r * H + h) * dv;
+                    for (int i = 0; i < nv; ++i)
+                        for (int e = 0; e < dv; ++e)
+                            o[e] += p[i] * Vc[((size_t)g * n_cmp + i) * dv + e];
+                }
+                /* compressed block i spans tokens i*s .. i*s+l-1; it counts toward every
+                 * selection block holding one of those tokens */
+                for (int i = 0; i < nv; ++i)
+                    for (int j = (i * s) / lp; j <= (i * s + l - 1) / lp && j < n_slc; ++j)
+                        score[j] += p[i];
+            } else {
+                for (int j = 0; j < jc && j < n_cmp; ++j)
+                    score[j] += dot(q, Kc + ((size_t)g * n_cmp + j) * dk, dk);
+            }
+        }
+        {
+            const double gap = select_blocks(jc, top_n, n_init, n_local, score,
+                                             sel_out + ((size_t)r * H_kv + g) * top_n, flag, cand);
+            if (gap_out) gap_out[(size_t)r * H_kv + g] = gap;
+            if (scores_out) {
+                double* so = scores_out + ((size_t)r * H_kv + g) * n_slc;
+                for (int j = 0; j < n_slc; ++j) so[j] = (j <= jc) ? score[j] : 0.0;
+            }
+        }
+    done:
+        free(score); free(logit); free(p); free(flag); free(cand);
+    }
+    return bad ? -2 : 0;
+}
+
+/* Step 4 alone, from given scores: sel[r][.] for a query whose own block is jc[r].
+ * scores: [nrows, n_slc]; sel: [nrows, top_n]; gap: [nrows] or NULL. */
+ORACLE_API int oracle_select_from_scores(int nrows, int n_slc, int top_n, int n_init, int n_local,
+                                         const int* jc, const double* scores, int* sel, double* gap)
+{
+    if (top_n < n_init + n_local) return -1;
+    unsigned char* flag = (unsigned char*)malloc((size_t)n_slc);
+    cand_t* cand = (cand_t*)malloc(sizeof(cand_t) * (size_t)n_slc);
+    for (int r = 0; r < nrows; ++r) {
+        const double gp = select_blocks(jc[r], top_n, n_init, n_local, scores + (size_t)r * n_slc,
+                                        sel + (size_t)r * top_n, flag, cand);
+        if (gap) gap[r] = gp;
+    }
+    free(flag); free(cand);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------- */
+/* Steps 5-7: selected attention, sliding window, gated sum                  */
+/* ------------------------------------------------------------------------- */
+
+/* Softmax attention of q over an explicit key list: o = sum_k softmax(scale*<q,K[k]>) V[k]. */
+static void attend_list(const double* q, const double* K, const double* V, int dk, int dv,
+                        double scale, const int* keys, int nk, double* logit, double* p, double* o)
+{
+    for (int e = 0; e < dv; ++e) o[e] = 0.0;
+    if (nk == 0) return;
+    for (int c = 0; c < nk; ++c) logit[c] = scale * dot(q, K + (size_t)keys[c] * dk, dk);
+    softmax(logit, nk, p);
+    for (int c = 0; c < nk; ++c)
+        for (int e = 0; e < dv; ++e) o[e] += p[c] * V[(size_t)keys[c] * dv + e];
+}
+
+static double sigmoid(double z) { return 1.0 / (1.0 + exp(-z)); }
+
+/* For each listed query row and head h (group g = h / G):
+ *   o_slc: attention over the tokens of the listed blocks of (row, g) that are <= t;
+ *   o_win: attention over tokens max(0, t-w+1) .. t;
+ *   out = sum over enabled branches of sigmoid(gate) * o_branch
+ *         (branch bits: 1 compressed, 2 selected, 4 window; gate order cmp, slc, win;
+ *          gates NULL -> every gate weight is 1).
+ * Q_rows [nrows, H, dk]; K [H_kv, n_tok, dk]; V [H_kv, n_tok, dv]; sel [nrows, H_kv, top_n]
+ * (entries < 0 ignored); ocmp [nrows, H, dv] (needed when branch 1 is on); gates
+ * [nrows, H, 3]; out, oslc, owin [nrows, H, dv] (oslc/owin may be NULL). */
+ORACLE_API int oracle_attend(int H_kv, int G, int dk, int dv, int n_tok, int lp, int top_n,
+                             int window, double scale, int branches,
+                             const double* Q_rows, const int* rows, int nrows,
+                             const double* K, const double* V, const int* sel,
+                             const double* ocmp, const double* gates,
+                             double* out, double* oslc_out, double* owin_out)
+{
+    const int H = H_kv * G;
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic) reduction(|: bad)
+    for (int rh = 0; rh < nrows * H; ++rh) {
+        const int r = rh / H, h = rh % H, g = h / G;
+        const int t = rows[r];
+        const double* q = Q_rows + ((size_t)r * H + h) * dk;
+        const double* Kg = K + (size_t)g * n_tok * dk;
+        const double* Vg = V + (size_t)g * n_tok * dv;
+        const int cap = top_n * lp + window + 1;
+        int* keys = (int*)malloc(sizeof(int) * (size_t)cap);
+        double* logit = (double*)malloc(sizeof(double) * (size_t)cap);
+        double* p = (double*)malloc(sizeof(double) * (size_t)cap);
+        double* os = (double*)malloc(sizeof(double) * (size_t)dv);
+        double* ow = (double*)malloc(sizeof(double) * (size_t)dv);
+        if (!keys || !logit || !p || !os || !ow) { bad = 1; goto done; }
+
+        /* selected tokens: the union of the listed blocks, restricted to <= t */
+        {
+            int nk = 0;
+            const int* sl = sel + ((size_t)r * H_kv + g) * top_n;
+            for (int c = 0; c < top_n; ++c) {
+                const int j = sl[c];
+                if (j < 0) continue;
+                int dup = 0;
+                for (int c2 = 0; c2 < c; ++c2) dup |= (sl[c2] == j);
+                if (dup) continue;
+                for (int x = j * lp; x < (j + 1) * lp && x <= t; ++x) keys[nk++] = x;
+            }
+            attend_list(q, Kg, Vg, dk, dv, scale, keys, nk, logit, p, os);
+        }
+        /* window tokens */
+        {
+            int nk = 0;
+            const int t0 = (t - window + 1) > 0 ? (t - window + 1) : 0;
+            for (int x = t0; x <= t && window > 0; ++x) keys[nk++] = x;
+            attend_list(q, Kg, Vg, dk, dv, scale, keys, nk, logit, p, ow);
+        }
+        {
+            const double* z = gates ? gates + ((size_t)r * H + h) * 3 : NULL;
+            const double gc = z ? sigmoid(z[0]) : 1.0;
+            const double gs = z ? sigmoid(z[1]) : 1.0;
+            const double gw = z ? sigmoid(z[2]) : 1.0;
+            double* o = out + ((size_t)r * H + h) * dv;
+            for (int e = 0; e < dv; ++e) {
+                double acc = 0.0;
+                if (branches & 1) acc += gc * ocmp[((size_t)r * H + h) * dv + e];
+                if (branches & 2) acc += gs * os[e];
+                if (branches & 4) acc += gw * ow[e];
+                o[e] = acc;
+            }
+            if (oslc_out) memcpy(oslc_out + ((size_t)r * H + h) * dv, os, sizeof(double) * dv);
+            if (owin_out) memcpy(owin_out + ((size_t)r * H + h) * dv, ow, sizeof(double) * dv);
+        }
+    done:
+        free(keys); free(logit); free(p); free(os); free(ow);
+    }
+    return bad ? -2 : 0;
+}
+
+/* ------------------------------------------------------------------------- */
+/* Textbook references used by the oracle's own pins                         */
+/* ------------------------------------------------------------------------- */
+
+/* Causal attention of one head, restricted to keys t-w+1 .. t when w > 0 (w <= 0: all
+ * keys 0 .. t).  Q [n, dk], K [n, dk], V [n, dv], out [n, dv]. */
+ORACLE_API void oracle_causal_attention(int n, int dk, int dv, int w, double scale,
+                                        const double* Q, const double* K, const double* V,
+                                        double* out)
+{
+#pragma omp parallel for schedule(dynamic)
+    for (int t = 0; t < n; ++t) {
+        const int t0 = (w > 0 && t - w + 1 > 0) ? t - w + 1 : 0;
+        const int nk = t - t0 + 1;
+        double* logit = (double*)malloc(sizeof(double) * (size_t)nk);
+        double mx = -INFINITY, sum = 0.0;
+        for (int x = t0; x <= t; ++x) {
+            double a = 0.0;
+            for (int e = 0; e < dk; ++e) a += Q[(size_t)t * dk + e] * K[(size_t)x * dk + e];
+            logit[x - t0] = a * scale;
+            if (logit[x - t0] > mx) mx = logit[x - t0];
+        }
+        for (int c = 0; c < nk; ++c) { logit[c] = exp(logit[c] - mx); sum += logit[c]; }
+        for (int e = 0; e < dv; ++e) {
+            double acc = 0.0;
+            for (int x = t0; x <= t; ++x) acc += logit[x - t0] * V[(size_t)x * dv + e];
+            out[(size_t)t * dv + e] = acc / sum;
+        }
+        free(logit);
+    }
+}
+
+ORACLE_API int oracle_num_threads(void)
+{
+    int n = 1;
+#ifdef _OPENMP
+#pragma omp parallel
+    {
+#pragma omp master
+        n = omp_get_num_threads();
+    }
+#endif
+    return n;
+}

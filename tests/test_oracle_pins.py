@@ -1,0 +1,448 @@
+"""Pins of the fp64 oracle against facts that do not come from the oracle itself.
+
+What pins each oracle function:
+  compress_linear   hand-worked fixture; closed forms (position-embedding-only bias,
+                    linearity against a numpy matmul of the flattened block).
+  compress_mean     hand-worked fixture; numpy mean over reshaped blocks.
+  score_select      dense-mask brute force (independent formulation); hand-worked
+                    overlap fixture; score-sum identity; l=s=1 identity reduces the
+                    compressed branch to full causal attention; early-row boundary.
+  select            hand-worked tie fixture; rank-count brute force; exhaustive
+                    subset search; exact integer ties.
+  attend            dense-mask brute force; select-all == full causal attention;
+                    select-none == sliding window; window 1 == V[t]; hand-worked
+                    softmax; gate isolation; causality under perturbation of the future.
+  MoBA              mean closed form; all blocks == full causal; top-1 == block-local.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import bruteforce as bf
+from oracle import pipeline
+from dynamic_block_sparse_nsa_amd.configs import TINY, MOBA, NSAConfig, BR_ALL, BR_SLC, BR_WIN, BR_CMP
+
+GOLDEN = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "hand_worked.json")))
+
+
+def rand_case(cfg: NSAConfig, seed=0, T=None):
+    """Small fp64 random inputs for one batch element (oracle-only tests)."""
+    rng = np.random.default_rng(1000 + seed)
+    T = cfg.seq_len if T is None else T
+    H, Hkv, dk, dv, l = cfg.num_heads, cfg.num_kv_heads, cfg.d_k, cfg.d_v, cfg.cmp_block
+    c = {
+        "Q": rng.standard_normal((T, H, dk)),
+        "K": rng.standard_normal((Hkv, T, dk)),
+        "V": rng.standard_normal((Hkv, T, dv)),
+        "gates": rng.standard_normal((T, H, 3)),
+    }
+    if cfg.phi == 0:
+        a = math.sqrt(6.0 / (l * dk + dk))
+        c["w_k"] = rng.uniform(-a, a, (l * dk, dk))
+        c["w_v"] = rng.uniform(-math.sqrt(6.0 / (l * dv + dv)), math.sqrt(6.0 / (l * dv + dv)), (l * dv, dv))
+        c["pe_k"] = rng.standard_normal((l, dk))
+        c["pe_v"] = rng.standard_normal((l, dv))
+        c["Kc"], c["Vc"] = pipeline.compress_all(cfg, c["K"], c["V"], c["w_k"], c["w_v"], c["pe_k"],
+                                                 c["pe_v"], round_cmp=False)
+    else:
+        c["Kc"], c["Vc"] = pipeline.compress_all(cfg, c["K"], c["V"], None, None, None, None, round_cmp=False)
+    return c
+
+
+SMALL = TINY.replace(seq_len=512, heads_per_group=4, num_kv_heads=2, d_k=32, d_v=16, window=96)
+
+
+# ---------------------------------------------------------------------------
+# hand-worked fixture
+# ---------------------------------------------------------------------------
+def test_golden_compress_linear():
+    g = GOLDEN["compress_linear"]
+    out = oracle.compress_linear(np.array(g["X"]), np.array(g["pe"]), np.array(g["W"]), g["l"], g["s"])
+    np.testing.assert_array_equal(out, np.array(g["expect"]))
+
+
+def test_golden_compress_mean():
+    g = GOLDEN["compress_mean"]
+    out = oracle.compress_mean(np.array(g["X"]), g["l"], g["s"])
+    np.testing.assert_array_equal(out, np.array(g["expect"]))
+
+
+def test_golden_uniform_attention():
+    g = GOLDEN["uniform_attention"]
+    V = np.array(g["V"])[:, None]
+    Z = np.zeros_like(V)
+    np.testing.assert_allclose(oracle.causal_attention(Z, Z, V, 1.0)[:, 0], g["causal"], rtol=0, atol=1e-15)
+    np.testing.assert_allclose(oracle.causal_attention(Z, Z, V, 1.0, window=g["window"])[:, 0], g["windowed"],
+                               rtol=0, atol=1e-15)
+    # the same through the NSA attend stage: window branch only, gates off (weight 1)
+    cfg = NSAConfig("h", 1, 3, 1, 1, 1, 1, 1, 1, 1, 0, 0, 0, g["window"], branches=BR_WIN)
+    r = oracle.attend(cfg, Z[:, None, :], [0, 1, 2], Z[None], V[None], np.full((3, 1, 1), -1))
+    np.testing.assert_allclose(r["out"][:, 0, 0], g["windowed"], rtol=0, atol=1e-15)
+
+
+def test_golden_two_key_softmax():
+    g = GOLDEN["two_key_softmax"]
+    cfg = NSAConfig("h", 1, 2, 1, 1, 1, 1, 1, 1, 2, 1, 1, 0, 0, branches=BR_SLC, softmax_scale=g["scale"])
+    Q = np.array([[[0.0]], [[g["q"]]]])
+    K = np.array(g["K"])[None, :, None]
+    V = np.array(g["V"])[None, :, None]
+    r = oracle.attend(cfg, Q[1:], [1], K, V, np.array([[[0]]]))
+    assert abs(r["out"][0, 0, 0] - g["expect"]) < 1e-14
+
+
+def test_golden_overlap_scores():
+    g = GOLDEN["overlap_scores"]
+    # one head whose compressed logits reproduce the fixture's probabilities: a_i = log p_i
+    p = np.array(g["p"])
+    n_cmp = len(p)
+    T = (n_cmp - 1) * g["s"] + g["l"]          # the last token sees every compressed block
+    cfg = NSAConfig("h", 1, T, 1, 1, n_cmp, 1, g["l"], g["s"], g["lp"], 3, 0, 0, 0, softmax_scale=1.0)
+    Kc = np.eye(n_cmp)[None]                   # <q, Kc_i> = q_i
+    Q = np.log(p)[None, None, :]
+    r = oracle.score_select(cfg, Q, [T - 1], Kc, np.zeros((1, n_cmp, 1)))
+    np.testing.assert_allclose(r["scores"][0, 0, :3], g["expect"], rtol=0, atol=1e-15)
+    np.testing.assert_allclose(bf.overlap_matrix(n_cmp, 3, g["l"], g["s"], g["lp"]).T @ p, g["expect"],
+                               rtol=0, atol=1e-15)
+
+
+def test_golden_selection_ties():
+    g = GOLDEN["selection_ties"]
+    sc = np.zeros((1, 16))
+    sc[0, :6] = g["scores"]
+    for case in g["cases"]:
+        sel, _ = oracle.select_from_scores(sc, [g["jc"]], case["top_n"], g["n_init"], g["n_local"])
+        assert sel[0].tolist() == case["expect"]
+        assert bf.rank_select(sc[0], g["jc"], case["top_n"], g["n_init"], g["n_local"]) == case["expect"]
+
+
+# ---------------------------------------------------------------------------
+# step 1 closed forms
+# ---------------------------------------------------------------------------
+def test_compress_linear_closed_forms():
+    rng = np.random.default_rng(7)
+    l, s, d, do, T = 8, 4, 6, 5, 40
+    X = rng.standard_normal((T, d))
+    pe = rng.standard_normal((l, d))
+    W = rng.standard_normal((l * d, do))
+    N = (T - l) // s + 1
+    out = oracle.compress_linear(X, pe, W, l, s)
+    # position embedding alone is a bias vec(PE) @ W (phi is linear)
+    bias = pe.reshape(-1) @ W
+    zero = oracle.compress_linear(np.zeros_like(X), pe, W, l, s)
+    np.testing.assert_allclose(zero, np.tile(bias, (N, 1)), rtol=1e-13, atol=1e-13)
+    # block i is the row-major flattening of tokens i*s .. i*s+l-1
+    flat = np.stack([X[i * s:i * s + l].reshape(-1) for i in range(N)])
+    np.testing.assert_allclose(out, flat @ W + bias, rtol=1e-12, atol=1e-12)
+    # listed blocks only
+    sub = oracle.compress_linear(X, pe, W, l, s, blocks=[3, 0])
+    np.testing.assert_allclose(sub, out[[3, 0]], rtol=0, atol=0)
+
+
+def test_compress_mean_closed_form():
+    rng = np.random.default_rng(8)
+    X = rng.standard_normal((64, 3))
+    out = oracle.compress_mean(X, 16, 16)
+    np.testing.assert_allclose(out, X.reshape(4, 16, 3).mean(axis=1), rtol=1e-14, atol=1e-15)
+
+
+# ---------------------------------------------------------------------------
+# dense brute force (independent formulation)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("cfg", [SMALL, SMALL.replace(top_n=6, window=40, seed=1),
+                                 SMALL.replace(cmp_block=16, cmp_stride=8, slc_block=32, top_n=5)])
+def test_bruteforce_matches_oracle(cfg):
+    c = rand_case(cfg)
+    T = cfg.seq_len
+    rows = np.arange(T)
+    r = oracle.score_select(cfg, c["Q"], rows, c["Kc"], c["Vc"])
+    a = oracle.attend(cfg, c["Q"], rows, c["K"], c["V"], r["sel"], r["o_cmp"], c["gates"])
+    d = bf.nsa_dense(cfg, c["Q"], c["K"], c["V"], c["Kc"], c["Vc"], c["gates"])
+    np.testing.assert_allclose(r["o_cmp"], d["o_cmp"], rtol=0, atol=1e-12)
+    n_slc = r["scores"].shape[-1]
+    np.testing.assert_allclose(r["scores"], d["scores"][:, :, :n_slc], rtol=0, atol=1e-12)
+    # selection: identical wherever the decision is not a near tie
+    clear = r["gap"] > 1e-9
+    assert clear.mean() > 0.95
+    np.testing.assert_array_equal(r["sel"][clear], d["sel"][clear])
+    for k in ("o_slc", "o_win", "out"):
+        np.testing.assert_allclose(a[k], d[k], rtol=0, atol=1e-12)
+
+
+def test_selection_exhaustive_subsets():
+    cfg = TINY.replace(seq_len=1024, top_n=6)       # 16 blocks: 3 forced, C(13,3) subsets per row
+    c = rand_case(cfg, seed=3)
+    rows = np.arange(1024 - 96, 1024, 3)
+    r = oracle.score_select(cfg, c["Q"][rows], rows, c["Kc"], c["Vc"])
+    for n, t in enumerate(rows):
+        if r["gap"][n, 0] < 1e-9:
+            continue
+        want = bf.subset_select(r["scores"][n, 0], t // 64, cfg.top_n, cfg.n_init, cfg.n_local)
+        assert r["sel"][n, 0].tolist() == want
+
+
+def test_p12_exact_integer_ties():
+    rng = np.random.default_rng(5)
+    for trial in range(200):
+        jc = int(rng.integers(0, 40))
+        top_n = int(rng.integers(3, 12))
+        sc = rng.integers(0, 4, size=(1, 48)).astype(np.float64)   # many exact ties
+        sel, _ = oracle.select_from_scores(sc, [jc], top_n, 1, 2)
+        assert sel[0].tolist() == bf.rank_select(sc[0], jc, top_n, 1, 2)
+        if jc < 12:
+            assert sel[0].tolist() == bf.subset_select(sc[0], jc, top_n, 1, 2)
+
+
+# ---------------------------------------------------------------------------
+# special cases the pages state
+# ---------------------------------------------------------------------------
+def test_p1_select_all_is_full_causal():
+    cfg = SMALL.replace(top_n=SMALL.n_slc + 3)
+    c = rand_case(cfg, seed=4)
+    rows = np.arange(cfg.seq_len)
+    r = oracle.score_select(cfg, c["Q"], rows, c["Kc"], c["Vc"])
+    a = oracle.attend(cfg, c["Q"], rows, c["K"], c["V"], r["sel"], r["o_cmp"], c["gates"])
+    for h in range(cfg.num_heads):
+        g = h // cfg.heads_per_group
+        full = oracle.causal_attention(c["Q"][:, h], c["K"][g], c["V"][g], cfg.scale)
+        np.testing.assert_allclose(a["o_slc"][:, h], full, rtol=0, atol=1e-12)
+        # and against a numpy softmax with an explicit causal mask
+        A = cfg.scale * c["Q"][:, h] @ c["K"][g].T
+        A = np.where(np.tril(np.ones_like(A, bool)), A, -np.inf)
+        P = np.exp(A - A.max(1, keepdims=True))
+        np.testing.assert_allclose(full, (P / P.sum(1, keepdims=True)) @ c["V"][g], rtol=0, atol=1e-12)
+
+
+def test_p2_select_none_is_sliding_window():
+    cfg = SMALL.replace(top_n=0, n_init=0, n_local=0)
+    c = rand_case(cfg, seed=5)
+    rows = np.arange(cfg.seq_len)
+    r = oracle.score_select(cfg, c["Q"], rows, c["Kc"], c["Vc"])
+    assert (r["sel"] == -1).all() if r["sel"].size else True
+    gates = c["gates"].copy()
+    gates[..., 0] = -np.inf
+    gates[..., 1] = -np.inf
+    a = oracle.attend(cfg, c["Q"], rows, c["K"], c["V"], np.full((len(rows), cfg.num_kv_heads, 1), -1),
+                      r["o_cmp"], gates)
+    for h in range(cfg.num_heads):
+        g = h // cfg.heads_per_group
+        swa = oracle.causal_attention(c["Q"][:, h], c["K"][g], c["V"][g], cfg.scale, window=cfg.window)
+        sig = 1.0 / (1.0 + np.exp(-gates[:, h, 2]))
+        np.testing.assert_allclose(a["out"][:, h], sig[:, None] * swa, rtol=0, atol=1e-12)
+        np.testing.assert_array_equal(a["o_slc"][:, h], 0.0)
+
+
+def test_p2_local_blocks_only_is_block_aligned_local_attention():
+    k = 2
+    cfg = SMALL.replace(top_n=k, n_init=0, n_local=k)
+    c = rand_case(cfg, seed=6)
+    rows = np.arange(cfg.seq_len)
+    r = oracle.score_select(cfg, c["Q"], rows, c["Kc"], c["Vc"])
+    a = oracle.attend(cfg, c["Q"], rows, c["K"], c["V"], r["sel"], r["o_cmp"], None, branches=BR_SLC)
+    lp = cfg.slc_block
+    for h in range(cfg.num_heads):
+        g = h // cfg.heads_per_group
+        for t in (0, 63, 64, 130, 511):
+            lo = max(0, (t // lp - k + 1) * lp)
+            A = cfg.scale * c["K"][g][lo:t + 1] @ c["Q"][t, h]
+            P = np.exp(A - A.max())
+            want = (P / P.sum()) @ c["V"][g][lo:t + 1]
+            np.testing.assert_allclose(a["o_slc"][t, h], want, rtol=0, atol=1e-12)
+
+
+def test_window_closed_forms():
+    cfg = SMALL.replace(window=1)
+    c = rand_case(cfg, seed=7)
+    rows = np.arange(cfg.seq_len)
+    sel = np.full((len(rows), cfg.num_kv_heads, cfg.top_n), -1)
+    a = oracle.attend(cfg, c["Q"], rows, c["K"], c["V"], sel, None, None, branches=BR_WIN)
+    for h in range(cfg.num_heads):
+        np.testing.assert_allclose(a["out"][:, h], c["V"][h // cfg.heads_per_group], rtol=0, atol=1e-14)
+    # a window at least as long as the sequence is full causal attention
+    cfg2 = SMALL.replace(window=10 ** 6)
+    a2 = oracle.attend(cfg2, c["Q"], rows, c["K"], c["V"], sel, None, None, branches=BR_WIN)
+    full = oracle.causal_attention(c["Q"][:, 0], c["K"][0], c["V"][0], cfg.scale)
+    np.testing.assert_allclose(a2["out"][:, 0], full, rtol=0, atol=1e-12)
+
+
+def test_p3_causality_under_future_perturbation():
+    cfg = SMALL
+    c = rand_case(cfg, seed=8)
+    t0 = 300
+    rows = np.arange(t0 + 1)
+
+    def chain(cc):
+        Kc, Vc = pipeline.compress_all(cfg, cc["K"], cc["V"], cc["w_k"], cc["w_v"], cc["pe_k"], cc["pe_v"])
+        return pipeline.forward_rows(cfg, cc["Q"], cc["K"], cc["V"], Kc, Vc, cc["gates"], rows)
+
+    base = chain(c)
+    rng = np.random.default_rng(99)
+    c2 = dict(c)
+    for k in ("Q", "gates"):
+        c2[k] = c[k].copy()
+        c2[k][t0 + 1:] = rng.standard_normal(c2[k][t0 + 1:].shape)
+    for k in ("K", "V"):
+        c2[k] = c[k].copy()
+        c2[k][:, t0 + 1:] = rng.standard_normal(c2[k][:, t0 + 1:].shape) * 5
+    pert = chain(c2)
+    for k in ("out", "o_cmp", "o_slc", "o_win", "lse", "scores", "sel"):
+        np.testing.assert_array_equal(base[k], pert[k], err_msg=k)
+
+
+def test_p4_unit_blocks_make_compressed_branch_full_attention():
+    cfg = SMALL.replace(cmp_block=1, cmp_stride=1, d_v=SMALL.d_k)
+    c = rand_case(cfg, seed=9)
+    eye = np.eye(cfg.d_k)
+    Kc, Vc = pipeline.compress_all(cfg, c["K"], c["V"], eye, eye, np.zeros((1, cfg.d_k)),
+                                   np.zeros((1, cfg.d_k)), round_cmp=False)
+    np.testing.assert_array_equal(Kc, c["K"])
+    rows = np.arange(cfg.seq_len)
+    r = oracle.score_select(cfg, c["Q"], rows, Kc, Vc)
+    for h in range(cfg.num_heads):
+        g = h // cfg.heads_per_group
+        full = oracle.causal_attention(c["Q"][:, h], c["K"][g], c["V"][g], cfg.scale)
+        np.testing.assert_allclose(r["o_cmp"][:, h], full, rtol=0, atol=1e-12)
+
+
+def test_p6_score_sum_identity():
+    cfg = SMALL
+    c = rand_case(cfg, seed=10)
+    rows = np.arange(cfg.seq_len)
+    r = oracle.score_select(cfg, c["Q"], rows, c["Kc"], c["Vc"])
+    d = bf.nsa_dense(cfg, c["Q"], c["K"], c["V"], c["Kc"], c["Vc"], c["gates"])
+    G = cfg.heads_per_group
+    l, s, lp = cfg.cmp_block, cfg.cmp_stride, cfg.slc_block
+    N = c["Kc"].shape[1]
+    # blocks touched by compressed block i: those holding tokens i*s .. i*s+l-1
+    touched = np.array([(i * s + l - 1) // lp - (i * s) // lp + 1 for i in range(N)])
+    total = r["scores"].sum(axis=2)
+    vis = rows >= l - 1
+    assert np.all(total[~vis] == 0)
+    assert np.all(total[vis] >= G - 1e-9) and np.all(total[vis] <= 2 * G + 1e-9)
+    # exact form: sum over heads and visible i of p_i * (#blocks touched by i)
+    for g in range(cfg.num_kv_heads):
+        # reconstruct p from the brute force's compressed attention weights
+        for t in rows[vis][::37]:
+            nv = min(N, (t - l + 1) // s + 1)
+            want = 0.0
+            for hh in range(G):
+                h = g * G + hh
+                A = cfg.scale * c["Kc"][g][:nv] @ c["Q"][t, h]
+                P = np.exp(A - A.max())
+                P /= P.sum()
+                want += (P * touched[:nv]).sum()
+            assert abs(total[t, g] - want) < 1e-12
+
+
+def test_p7_head_permutation_within_group():
+    cfg = SMALL
+    c = rand_case(cfg, seed=11)
+    rows = np.arange(cfg.seq_len)
+    r = oracle.score_select(cfg, c["Q"], rows, c["Kc"], c["Vc"])
+    perm = np.arange(cfg.num_heads).reshape(cfg.num_kv_heads, -1)[:, ::-1].reshape(-1)
+    r2 = oracle.score_select(cfg, c["Q"][:, perm], rows, c["Kc"], c["Vc"])
+    clear = r["gap"] > 1e-9
+    np.testing.assert_array_equal(r["sel"][clear], r2["sel"][clear])
+    np.testing.assert_allclose(r2["o_cmp"], r["o_cmp"][:, perm], rtol=0, atol=1e-14)
+    # one list per group: the selection does not depend on which head is listed first
+    assert r["sel"].shape == (len(rows), cfg.num_kv_heads, cfg.top_n)
+
+
+def test_p8_gate_isolation_and_half_weights():
+    cfg = SMALL
+    c = rand_case(cfg, seed=12)
+    rows = np.arange(0, cfg.seq_len, 5)
+    r = oracle.score_select(cfg, c["Q"][rows], rows, c["Kc"], c["Vc"])
+    for which, key in ((0, "o_cmp"), (1, "o_slc"), (2, "o_win")):
+        z = np.full((len(rows), cfg.num_heads, 3), -np.inf)
+        z[..., which] = np.inf
+        a = oracle.attend(cfg, c["Q"][rows], rows, c["K"], c["V"], r["sel"], r["o_cmp"], z)
+        ref = r["o_cmp"] if key == "o_cmp" else a[key]
+        np.testing.assert_array_equal(a["out"], ref)
+    a = oracle.attend(cfg, c["Q"][rows], rows, c["K"], c["V"], r["sel"], r["o_cmp"],
+                      np.zeros((len(rows), cfg.num_heads, 3)))
+    np.testing.assert_allclose(a["out"], 0.5 * (r["o_cmp"] + a["o_slc"] + a["o_win"]), rtol=0, atol=1e-14)
+
+
+def test_p13_early_rows_without_compressed_blocks():
+    cfg = SMALL
+    c = rand_case(cfg, seed=13)
+    rows = np.arange(cfg.cmp_block - 1)
+    r = oracle.score_select(cfg, c["Q"][rows], rows, c["Kc"], c["Vc"])
+    assert np.all(r["o_cmp"] == 0) and np.all(r["scores"] == 0)
+    assert np.all(np.isneginf(r["lse"]))
+    # block 0 only (rows < 64): the list is [0, -1, ...]
+    assert np.all(r["sel"][:, :, 0] == 0) and np.all(r["sel"][:, :, 1:] == -1)
+    # with zero scores the free picks are the lowest-index candidates
+    sc = np.zeros((1, 16))
+    sel, _ = oracle.select_from_scores(sc, [9], 6, 1, 2)
+    assert sel[0].tolist() == [0, 1, 2, 3, 8, 9]
+
+
+def test_p11_single_row_equals_row_of_full_pass():
+    cfg = SMALL
+    c = rand_case(cfg, seed=14)
+    T = cfg.seq_len
+    full = pipeline.forward_rows(cfg, c["Q"], c["K"], c["V"], c["Kc"], c["Vc"], c["gates"], np.arange(T))
+    last = pipeline.forward_rows(cfg, c["Q"], c["K"], c["V"], c["Kc"], c["Vc"], c["gates"], [T - 1])
+    for k in ("out", "sel", "lse", "scores"):
+        np.testing.assert_array_equal(full[k][-1:], last[k])
+
+
+# ---------------------------------------------------------------------------
+# MoBA mode
+# ---------------------------------------------------------------------------
+MOBA_SMALL = MOBA.replace(seq_len=1024, num_kv_heads=2, d_k=16, d_v=16, cmp_block=64, cmp_stride=64,
+                          slc_block=64)
+
+
+def test_moba_bruteforce_and_current_block():
+    cfg = MOBA_SMALL
+    c = rand_case(cfg, seed=15)
+    rows = np.arange(cfg.seq_len)
+    r = oracle.score_select(cfg, c["Q"], rows, c["Kc"])
+    a = oracle.attend(cfg, c["Q"], rows, c["K"], c["V"], r["sel"], None, None)
+    d = bf.nsa_dense(cfg, c["Q"], c["K"], c["V"], c["Kc"], c["Vc"])
+    np.testing.assert_allclose(r["scores"], d["scores"], rtol=0, atol=1e-12)
+    clear = r["gap"] > 1e-9
+    np.testing.assert_array_equal(r["sel"][clear], d["sel"][clear])
+    np.testing.assert_allclose(a["out"], d["out"], rtol=0, atol=1e-12)
+    # the query's own block is always selected, and at most top_n blocks are
+    for t in rows:
+        for g in range(cfg.num_kv_heads):
+            assert t // cfg.slc_block in r["sel"][t, g].tolist()
+    # scores are unscaled q . mean(K_j) over earlier complete blocks
+    t, g = 700, 1
+    means = c["K"][g][:640].reshape(10, 64, -1).mean(axis=1)
+    np.testing.assert_allclose(r["scores"][t, g, :10], means @ c["Q"][t, g], rtol=1e-12, atol=1e-12)
+    assert np.all(r["scores"][t, g, 10:] == 0)
+
+
+def test_moba_all_blocks_is_full_causal_and_top1_is_block_local():
+    c = rand_case(MOBA_SMALL, seed=16)
+    rows = np.arange(MOBA_SMALL.seq_len)
+    cfg_all = MOBA_SMALL.replace(top_n=MOBA_SMALL.n_slc)
+    r = oracle.score_select(cfg_all, c["Q"], rows, c["Kc"])
+    a = oracle.attend(cfg_all, c["Q"], rows, c["K"], c["V"], r["sel"], None, None)
+    cfg1 = MOBA_SMALL.replace(top_n=1)
+    r1 = oracle.score_select(cfg1, c["Q"], rows, c["Kc"])
+    a1 = oracle.attend(cfg1, c["Q"], rows, c["K"], c["V"], r1["sel"], None, None)
+    lp = MOBA_SMALL.slc_block
+    for h in range(MOBA_SMALL.num_heads):
+        full = oracle.causal_attention(c["Q"][:, h], c["K"][h], c["V"][h], MOBA_SMALL.scale)
+        np.testing.assert_allclose(a["out"][:, h], full, rtol=0, atol=1e-12)
+        for t in (0, 63, 64, 500, 1023):
+            lo = (t // lp) * lp
+            A = MOBA_SMALL.scale * c["K"][h][lo:t + 1] @ c["Q"][t, h]
+            P = np.exp(A - A.max())
+            np.testing.assert_allclose(a1["out"][t, h], (P / P.sum()) @ c["V"][h][lo:t + 1], rtol=0, atol=1e-12)
+
+
+def test_bf16_rounding_helper():
+    # the chain's bf16 rounding: exact representables unchanged, halfway cases to even
+    x = np.array([1.0, 1.0 + 2 ** -7, 1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -2.5, 0.0, 1.0 + 2 ** -8 + 2 ** -30])
+    want = np.array([1.0, 1.0 + 2 ** -7, 1.0, 1.0 + 2 ** -6, -2.5, 0.0, 1.0 + 2 ** -7])
+    np.testing.assert_array_equal(pipeline.round_to_bf16(x), want)
