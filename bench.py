@@ -1,0 +1,314 @@
+#!/usr/bin/env python3
+"""Benchmark of the NSA forward hot path on one MI355X.
+
+A step is one pass of the prefill hot path over the 64K workload (batch 1, 65536 tokens,
+4 KV groups x 16 query heads, d_k 192, d_v 128, compression 32/16, 64-token selection
+blocks, top-16, window 512): nsa_compress -> nsa_score_select -> nsa_sparse_attn_fwd, with
+every input resident in HBM before the timed region.  The headline ``value`` is prefill
+tokens/s; the line also carries the algorithmic TFLOP/s and MFMA-peak fraction, a
+roofline entry for the dominant kernel (timed live with HIP events on the stream it runs
+on), the oracle timed on the host cores on a bounded sample, and the decode step
+(batch 32 x 65536-token caches, HBM GB/s) and MoBA (131072 tokens) figures.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-decode] [--no-moba]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from dynamic_block_sparse_nsa_amd.configs import P64K, DECODE, MOBA, NSAConfig  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+# ---------------------------------------------------------------------------
+# algorithmic work (unmasked (query, head, key) pairs x 2*(d_k + d_v) flops)
+# ---------------------------------------------------------------------------
+def cmp_pairs(cfg: NSAConfig) -> int:
+    t = np.arange(cfg.seq_len, dtype=np.int64)
+    nv = np.where(t >= cfg.cmp_block - 1, np.minimum((t - cfg.cmp_block + 1) // cfg.cmp_stride + 1, cfg.n_cmp), 0)
+    return int(nv.sum()) * cfg.num_heads
+
+
+def slc_pairs(cfg: NSAConfig) -> int:
+    """Selected-branch keys with top_n blocks chosen (the own block causal, the rest full)."""
+    t = np.arange(cfg.seq_len, dtype=np.int64)
+    jc = t // cfg.slc_block
+    m = np.minimum(cfg.top_n, jc + 1)
+    keys = (m - 1) * cfg.slc_block + (t - jc * cfg.slc_block + 1)
+    return int(keys.sum()) * cfg.num_heads
+
+
+def win_pairs(cfg: NSAConfig) -> int:
+    t = np.arange(cfg.seq_len, dtype=np.int64)
+    return int(np.minimum(t + 1, cfg.window).sum()) * cfg.num_heads
+
+
+def prefill_flops(cfg: NSAConfig) -> dict:
+    f = 2 * (cfg.d_k + cfg.d_v)
+    return {"cmp": cmp_pairs(cfg) * f, "slc": slc_pairs(cfg) * f, "win": win_pairs(cfg) * f}
+
+
+def moba_flops(cfg: NSAConfig) -> int:
+    return slc_pairs(cfg) * 2 * (cfg.d_k + cfg.d_v)
+
+
+# ---------------------------------------------------------------------------
+def sha_of(paths) -> str:
+    h = hashlib.sha256()
+    for p in paths:
+        h.update(open(os.path.join(ROOT, p), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel: str, sources) -> dict | None:
+    """HBM traffic per launch from a committed counter summary, if it was taken on the
+    current source of the kernel (otherwise null)."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path)).get(kernel)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_sha") != sha_of(sources):
+        return None
+    return rec
+
+
+def time_calls(fns, steps, warmup, torch):
+    """Run the list of callables per step; per-call and per-step times from HIP events
+    recorded on the current stream."""
+    for _ in range(warmup):
+        for f in fns:
+            f()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)] for _ in range(steps)]
+    t0 = time.perf_counter()
+    for s in range(steps):
+        ev[s][0].record()
+        for i, f in enumerate(fns):
+            f()
+            ev[s][i + 1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_call = np.array([[ev[s][i].elapsed_time(ev[s][i + 1]) for i in range(len(fns))] for s in range(steps)])
+    return per_call, wall
+
+
+def cpu_baseline(cfg: NSAConfig, inp: dict, budget_rows: int = 96) -> dict:
+    """The fp64 oracle on a bounded sample of the same workload, scaled to tokens/s:
+    compression of 256 blocks per KV group (scaled to all N_cmp blocks) plus the score,
+    select and attend stages for the last ``budget_rows`` rows (the most expensive ones;
+    scaled to T rows at that cost, which overstates the CPU's speed on earlier rows only
+    through their shorter compressed history)."""
+    import oracle
+    from dynamic_block_sparse_nsa_amd import inputs as inputs_mod
+    from dynamic_block_sparse_nsa_amd.inputs import bf16_bits_to_f64 as f64
+
+    threads = oracle.num_threads()
+    nb = 256
+    blocks = np.arange(nb)
+    t0 = time.perf_counter()
+    for g in range(cfg.num_kv_heads):
+        oracle.compress_linear(f64(inp["k"][0, g]), f64(inp["pe_k"]), f64(inp["w_k"]), cfg.cmp_block, cfg.cmp_stride,
+                               blocks)
+        oracle.compress_linear(f64(inp["v"][0, g]), f64(inp["pe_v"]), f64(inp["w_v"]), cfg.cmp_block, cfg.cmp_stride,
+                               blocks)
+    t_cmp = (time.perf_counter() - t0) * cfg.n_cmp / nb
+    # stand-alone compressed keys/values for the row stages (their cost is the scaled
+    # compression time above)
+    ckv = inputs_mod.compressed_kv(cfg, seed=100 + cfg.seed)
+    Kc, Vc = f64(ckv["k_cmp"][0]), f64(ckv["v_cmp"][0])
+    rows = np.arange(cfg.seq_len - budget_rows, cfg.seq_len, dtype=np.int32)
+    Qr = f64(inp["q"][0, rows])
+    K, V = f64(inp["k"][0]), f64(inp["v"][0])
+    t1 = time.perf_counter()
+    ss = oracle.score_select(cfg, Qr, rows, Kc, Vc, want_scores=False)
+    oracle.attend(cfg, Qr, rows, K, V, ss["sel"], ss["o_cmp"], inp["gates"][0, rows])
+    t_rows = time.perf_counter() - t1
+    total = t_cmp + t_rows * cfg.seq_len / budget_rows
+    return {"value": round(cfg.seq_len / total, 2), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": (f"fp64 oracle: compression of {nb} of {cfg.n_cmp} blocks per KV group ({t_cmp * nb / cfg.n_cmp:.2f} s, "
+                       f"scaled) + score/select/attend of the last {budget_rows} of {cfg.seq_len} rows "
+                       f"({t_rows:.2f} s, scaled to all rows); {threads} OpenMP threads")}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-moba", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: the NSA forward shards by KV group / batch with no exchange, "
+              "and this build runs on a single MI355X; use --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from dynamic_block_sparse_nsa_amd import inputs, ops
+
+    assert torch.cuda.is_available()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def d(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    # ---------------- prefill 64K ----------------
+    cfg = P64K
+    print(f"[bench] drawing inputs for {cfg.name}", file=sys.stderr, flush=True)
+    inp = inputs.prefill_inputs(cfg)
+    Q, K, V = d(inp["q"]), d(inp["k"]), d(inp["v"])
+    wk, wv, pk, pv = d(inp["w_k"]), d(inp["w_v"]), d(inp["pe_k"]), d(inp["pe_v"])
+    gates = torch.from_numpy(inp["gates"]).to(dev)
+    B, T, H, Hkv = cfg.batch, cfg.seq_len, cfg.num_heads, cfg.num_kv_heads
+    kc = torch.empty((B, Hkv, cfg.n_cmp, cfg.d_k), dtype=torch.bfloat16, device=dev)
+    vc = torch.empty((B, Hkv, cfg.n_cmp, cfg.d_v), dtype=torch.bfloat16, device=dev)
+    sel = torch.empty((B, T, Hkv, cfg.top_n), dtype=torch.int32, device=dev)
+    ocmp = torch.empty((B, T, H, cfg.d_v), dtype=torch.float32, device=dev)
+    out = torch.empty((B, T, H, cfg.d_v), dtype=torch.bfloat16, device=dev)
+    ws = {op: torch.empty(max(ops.workspace_size(cfg, op), 256), dtype=torch.uint8, device=dev) for op in range(3)}
+
+    calls = [
+        lambda: ops.compress(cfg, K, V, wk, wv, pk, pv, out_k=kc, out_v=vc, workspace=ws[0]),
+        lambda: ops.score_select(cfg, Q, kc, vc, sel=sel, o_cmp=ocmp, workspace=ws[1]),
+        lambda: ops.sparse_attn_fwd(cfg, Q, K, V, sel, ocmp, gates, out=out, workspace=ws[2]),
+    ]
+    print("[bench] timing prefill", file=sys.stderr, flush=True)
+    per_call, wall = time_calls(calls, args.steps, args.warmup, torch)
+    step_ms = per_call.sum(axis=1)
+    ms = float(np.mean(step_ms))
+    fl = prefill_flops(cfg)
+    total_flops = sum(fl.values())
+    tflops = total_flops / (ms * 1e-3) / 1e12
+    call_ms = per_call.mean(axis=0)
+    names = ["nsa_compress", "nsa_score_select", "nsa_sparse_attn_fwd"]
+    # the dominant call and its algorithmic work
+    dom = int(np.argmax(call_ms))
+    dom_flops = [2 * (cfg.n_cmp * (cfg.cmp_block * cfg.d_k * cfg.d_k + cfg.cmp_block * cfg.d_v * cfg.d_v)) * Hkv,
+                 fl["cmp"], fl["slc"] + fl["win"]][dom]
+    dom_kernel = ["compress_linear_kernel", "score_select_kernel", "sparse_attn_kernel"][dom]
+    dom_src = [["dynamic_block_sparse_nsa_amd/csrc/compress.hip"],
+               ["dynamic_block_sparse_nsa_amd/csrc/score_select.hip", "dynamic_block_sparse_nsa_amd/csrc/select.hpp"],
+               ["dynamic_block_sparse_nsa_amd/csrc/sparse_attn.hip"]][dom]
+    dom_tf = dom_flops / (call_ms[dom] * 1e-3) / 1e12
+    traffic = load_traffic(dom_kernel, dom_src + ["dynamic_block_sparse_nsa_amd/csrc/common.hpp"])
+    torch.cuda.synchronize()
+
+    result = {
+        "metric": "NSA prefill tokens/s at 64K (also TFLOP/s, % MFMA peak; decode HBM GB/s)",
+        "value": round(B * T / (ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "nsa_prefill_64k", "batch": B, "seq_len": T, "kv_groups": Hkv,
+                   "heads_per_group": cfg.heads_per_group, "d_k": cfg.d_k, "d_v": cfg.d_v,
+                   "cmp_block": cfg.cmp_block, "cmp_stride": cfg.cmp_stride, "slc_block": cfg.slc_block,
+                   "top_n": cfg.top_n, "window": cfg.window},
+        "tflops_algorithmic": round(tflops, 2),
+        "mfma_peak_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "algorithmic_flops": {k: int(v) for k, v in fl.items()},
+        "per_call_ms": {n: round(float(c), 4) for n, c in zip(names, call_ms)},
+        "roofline": {"bound": "mfma", "kernel": dom_kernel, "call": names[dom],
+                     "achieved": round(dom_tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(dom_tf / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None if traffic is None else traffic.get("bytes_per_launch")},
+        "wall_s_timed": round(wall, 3),
+    }
+
+    # ---------------- decode ----------------
+    if not args.no_decode:
+        del Q, K, V, ocmp, out
+        torch.cuda.empty_cache()
+        dc = DECODE
+        print("[bench] decode inputs", file=sys.stderr, flush=True)
+        g = torch.Generator(device=dev).manual_seed(dc.seed)
+        Bd, L = dc.batch, dc.seq_len
+        q = torch.randn((Bd, dc.num_heads, dc.d_k), generator=g, device=dev).to(torch.bfloat16)
+        Kd = torch.randn((Bd, dc.num_kv_heads, L, dc.d_k), generator=g, device=dev).to(torch.bfloat16)
+        Vd = torch.randn((Bd, dc.num_kv_heads, L, dc.d_v), generator=g, device=dev).to(torch.bfloat16)
+        gd = torch.randn((Bd, dc.num_heads, 3), generator=g, device=dev)
+        clen = torch.full((Bd,), L, dtype=torch.int32, device=dev)
+        kcd, vcd = ops.compress(dc, Kd, Vd, wk, wv, pk, pv)
+        od = torch.empty((Bd, dc.num_heads, dc.d_v), dtype=torch.bfloat16, device=dev)
+        sd = torch.empty((Bd, dc.num_kv_heads, dc.top_n), dtype=torch.int32, device=dev)
+        wsd = torch.empty(ops.workspace_size(dc, ops.OP_DECODE), dtype=torch.uint8, device=dev)
+        dcall = [lambda: ops.decode(dc, q, Kd, Vd, clen, kcd, vcd, gd, out=od, sel=sd, workspace=wsd)]
+        pcd, _ = time_calls(dcall, max(20, args.steps), args.warmup + 3, torch)
+        dms = float(pcd.mean())
+        # bytes: compressed caches + raw K/V of the union of selected blocks and the window + q, O
+        s_np = sd.cpu().numpy()
+        raw_tok = 0
+        for b in range(Bd):
+            t = L - 1
+            for gg in range(dc.num_kv_heads):
+                toks = set()
+                for j in s_np[b, gg]:
+                    if j >= 0:
+                        toks.update(range(j * dc.slc_block, min((j + 1) * dc.slc_block, t + 1)))
+                toks.update(range(max(0, t - dc.window + 1), t + 1))
+                raw_tok += len(toks)
+        bytes_step = (kcd.numel() + vcd.numel()) * 2 + raw_tok * (dc.d_k + dc.d_v) * 2 + (q.numel() + od.numel()) * 2
+        gbs = bytes_step / (dms * 1e-3) / 1e9
+        result["decode"] = {"workload": "nsa_decode_b32_l65536", "ms_per_step": round(dms, 4),
+                            "bytes_per_step": int(bytes_step), "hbm_gbs": round(gbs, 1),
+                            "hbm_peak_frac": round(gbs / PEAK_HBM_GBS, 4)}
+        del Kd, Vd, kcd, vcd
+        torch.cuda.empty_cache()
+
+    # ---------------- MoBA ----------------
+    if not args.no_moba:
+        mc = MOBA
+        print("[bench] moba inputs", file=sys.stderr, flush=True)
+        g = torch.Generator(device=dev).manual_seed(mc.seed)
+        Qm = torch.randn((1, mc.seq_len, mc.num_heads, mc.d_k), generator=g, device=dev).to(torch.bfloat16)
+        Km = torch.randn((1, mc.num_kv_heads, mc.seq_len, mc.d_k), generator=g, device=dev).to(torch.bfloat16)
+        Vm = torch.randn((1, mc.num_kv_heads, mc.seq_len, mc.d_v), generator=g, device=dev).to(torch.bfloat16)
+        kbar = torch.empty((1, mc.num_kv_heads, mc.n_cmp, mc.d_k), dtype=torch.bfloat16, device=dev)
+        selm = torch.empty((1, mc.seq_len, mc.num_kv_heads, mc.top_n), dtype=torch.int32, device=dev)
+        om = torch.empty((1, mc.seq_len, mc.num_heads, mc.d_v), dtype=torch.bfloat16, device=dev)
+        wsm = torch.empty(ops.workspace_size(mc, ops.OP_SPARSE_ATTN), dtype=torch.uint8, device=dev)
+        mcalls = [lambda: ops.compress(mc, Km, out_k=kbar),
+                  lambda: ops.score_select(mc, Qm, kbar, sel=selm),
+                  lambda: ops.sparse_attn_fwd(mc, Qm, Km, Vm, selm, out=om, workspace=wsm)]
+        pcm, _ = time_calls(mcalls, 3, 1, torch)
+        mms = float(pcm.sum(axis=1).mean())
+        result["moba"] = {"workload": "moba_131072_h8_d128", "ms_per_step": round(mms, 3),
+                          "tokens_per_s": round(mc.seq_len / (mms * 1e-3), 1),
+                          "tflops_algorithmic": round(moba_flops(mc) / (mms * 1e-3) / 1e12, 2),
+                          "per_call_ms": {n: round(float(c), 3) for n, c in zip(names, pcm.mean(axis=0))}}
+        del Qm, Km, Vm
+        torch.cuda.empty_cache()
+
+    # ---------------- CPU baseline ----------------
+    if not args.no_cpu:
+        print("[bench] cpu baseline (oracle sample)", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(P64K, inp)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

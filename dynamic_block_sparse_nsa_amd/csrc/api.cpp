@@ -1,0 +1,360 @@
+// C ABI of the NSA library (declared in include/nsa.h): argument validation, workspace
+// layout and kernel dispatch.  Nothing here allocates device memory or synchronizes.
+#include "nsa.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstring>
+#include <string>
+
+#include "launch.hpp"
+
+namespace {
+
+thread_local std::string g_detail;
+
+nsa_status fail(nsa_status st, const std::string& msg) {
+    g_detail = msg;
+    return st;
+}
+
+struct Shape {
+    int B, T, Hkv, G, H, dk, dv, l, s, lp, n, n_init, n_local, w, phi, mode, br;
+    int n_cmp, n_slc;
+    float scale;
+};
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+int round_up(int x, int a) { return (x + a - 1) / a * a; }
+
+nsa_status check_config(const nsa_config* c, Shape* sh) {
+    if (!c) return fail(NSA_ERR_NULL, "config is NULL");
+    if (c->struct_size < sizeof(nsa_config)) return fail(NSA_ERR_SHAPE, "config.struct_size too small");
+    Shape s{};
+    s.B = c->batch; s.T = c->seq_len; s.Hkv = c->num_kv_heads; s.G = c->heads_per_group;
+    s.dk = c->d_k; s.dv = c->d_v; s.l = c->cmp_block; s.s = c->cmp_stride; s.lp = c->slc_block;
+    s.n = c->top_n; s.n_init = c->n_init; s.n_local = c->n_local; s.w = c->window;
+    s.phi = c->phi; s.mode = c->score_mode; s.br = c->branches;
+    if (s.B <= 0 || s.T <= 0 || s.Hkv <= 0 || s.G <= 0 || s.dk <= 0 || s.dv <= 0 || s.l <= 0 || s.s <= 0 || s.lp <= 0)
+        return fail(NSA_ERR_SHAPE, "sizes must be positive");
+    if (s.n < 0 || s.n_init < 0 || s.n_local < 0 || s.w < 0) return fail(NSA_ERR_SHAPE, "negative count");
+    if (s.G != 1 && s.G != 2 && s.G != 4 && s.G != 8 && s.G != 16)
+        return fail(NSA_ERR_UNSUPPORTED, "heads_per_group must be 1, 2, 4, 8 or 16");
+    if (!((s.dk == 192 && s.dv == 128) || (s.dk == 128 && s.dv == 128) || (s.dk == 64 && s.dv == 64)))
+        return fail(NSA_ERR_UNSUPPORTED, "(d_k, d_v) must be (192,128), (128,128) or (64,64)");
+    if (s.l % s.s != 0 || s.lp % s.s != 0) return fail(NSA_ERR_UNSUPPORTED, "cmp_stride must divide cmp_block and slc_block");
+    if (s.lp % 32 != 0) return fail(NSA_ERR_UNSUPPORTED, "slc_block must be a multiple of 32");
+    if (s.n > 32) return fail(NSA_ERR_UNSUPPORTED, "top_n must be <= 32");
+    if (s.n < s.n_init + s.n_local) return fail(NSA_ERR_UNSUPPORTED, "top_n smaller than the forced blocks");
+    if (s.phi != NSA_PHI_LINEAR && s.phi != NSA_PHI_MEAN) return fail(NSA_ERR_SHAPE, "unknown phi");
+    if (s.mode != NSA_SCORE_CMP_OVERLAP && s.mode != NSA_SCORE_MEAN_DOT) return fail(NSA_ERR_SHAPE, "unknown score_mode");
+    if (s.br <= 0 || s.br > 7) return fail(NSA_ERR_SHAPE, "branches must be a non-empty OR of NSA_BR_*");
+    if (s.mode == NSA_SCORE_MEAN_DOT) {
+        if (s.l != s.s || s.l != s.lp) return fail(NSA_ERR_UNSUPPORTED, "MEAN_DOT needs cmp_block == cmp_stride == slc_block");
+        if (s.n_local < 1) return fail(NSA_ERR_UNSUPPORTED, "MEAN_DOT needs n_local >= 1 (the own block is incomplete)");
+        if (s.br & NSA_BR_CMP) return fail(NSA_ERR_UNSUPPORTED, "MEAN_DOT has no compressed-branch output");
+    }
+    if ((double)s.B * s.T * s.Hkv * s.G * std::max(s.dk, s.dv) > 4.0e12) return fail(NSA_ERR_SHAPE, "problem too large");
+    s.H = s.Hkv * s.G;
+    s.n_cmp = s.T >= s.l ? (s.T - s.l) / s.s + 1 : 0;
+    s.n_slc = (s.T + s.lp - 1) / s.lp;
+    s.scale = c->softmax_scale > 0.f ? c->softmax_scale : 1.0f / std::sqrt((float)s.dk);
+    *sh = s;
+    return NSA_OK;
+}
+
+nsa_status hip_check(const char* what) {
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(NSA_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+    return NSA_OK;
+}
+
+hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+// ---- workspace layouts ----
+struct CompressWs { size_t wt_k, wt_v, bias_k, bias_v, total; };
+CompressWs compress_ws(const Shape& s) {
+    CompressWs w{};
+    if (s.phi != NSA_PHI_LINEAR) return w;
+    size_t off = 0;
+    w.wt_k = off; off = align_up(off + (size_t)s.l * s.dk * s.dk * 2, 256);
+    w.wt_v = off; off = align_up(off + (size_t)s.l * s.dv * s.dv * 2, 256);
+    w.bias_k = off; off = align_up(off + (size_t)s.dk * 4, 256);
+    w.bias_v = off; off = align_up(off + (size_t)s.dv * 4, 256);
+    w.total = off;
+    return w;
+}
+
+struct SelectWs { size_t m, il, vct, total; int npad; };
+SelectWs select_ws(const Shape& s) {
+    SelectWs w{};
+    if (s.mode != NSA_SCORE_CMP_OVERLAP) return w;
+    w.npad = round_up(std::max(s.n_cmp, 1), 64);
+    size_t off = 0;
+    const size_t rows = (size_t)s.B * s.T * s.H;
+    w.m = off; off = align_up(off + rows * 4, 256);
+    w.il = off; off = align_up(off + rows * 4, 256);
+    w.vct = off; off = align_up(off + (size_t)s.B * s.Hkv * s.dv * w.npad * 2, 256);
+    w.total = off;
+    return w;
+}
+
+struct AttnWs { size_t vt, total; int tpad; };
+AttnWs attn_ws(const Shape& s) {
+    AttnWs w{};
+    w.tpad = round_up(s.T, 64);
+    w.vt = 0;
+    w.total = align_up((size_t)s.B * s.Hkv * s.dv * w.tpad * 2, 256);
+    return w;
+}
+
+struct DecodeWs { size_t pm, pl, po, pa, sel, ocmp, am, al, ao, total; int n_split, jb, n_items; };
+DecodeWs decode_ws(const Shape& s) {
+    DecodeWs w{};
+    w.n_split = std::max(1, (s.n_cmp + nsa::kDecodeSplitKeys - 1) / nsa::kDecodeSplitKeys);
+    w.jb = nsa::decode_jb(s.l, s.s, s.lp);
+    w.n_items = nsa::decode_items(s.n, s.w);
+    const size_t bg = (size_t)s.B * s.Hkv;
+    size_t off = 0;
+    w.pm = off; off = align_up(off + bg * w.n_split * 16 * 4, 256);
+    w.pl = off; off = align_up(off + bg * w.n_split * 16 * 4, 256);
+    w.po = off; off = align_up(off + bg * w.n_split * s.dv * 16 * 4, 256);
+    w.pa = off; off = align_up(off + bg * w.n_split * 16 * w.jb * 4, 256);
+    w.sel = off; off = align_up(off + bg * std::max(s.n, 1) * 4, 256);
+    w.ocmp = off; off = align_up(off + bg * 16 * s.dv * 4, 256);
+    w.am = off; off = align_up(off + bg * w.n_items * 16 * 4, 256);
+    w.al = off; off = align_up(off + bg * w.n_items * 16 * 4, 256);
+    w.ao = off; off = align_up(off + bg * w.n_items * s.dv * 16 * 4, 256);
+    w.total = off;
+    return w;
+}
+
+nsa_status check_ws(void* ws, size_t have, size_t need) {
+    if (need == 0) return NSA_OK;
+    if (!ws) return fail(NSA_ERR_WORKSPACE, "workspace is NULL");
+    if (have < need) return fail(NSA_ERR_WORKSPACE, "workspace too small: need " + std::to_string(need) + " bytes");
+    if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return fail(NSA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+    return NSA_OK;
+}
+
+nsa_status check_align16(const void* p, const char* name) {
+    if ((reinterpret_cast<uintptr_t>(p) & 15u) != 0) return fail(NSA_ERR_SHAPE, std::string(name) + " must be 16-byte aligned");
+    return NSA_OK;
+}
+
+template <typename T>
+T* at(void* base, size_t off) { return reinterpret_cast<T*>(static_cast<char*>(base) + off); }
+
+}  // namespace
+
+extern "C" {
+
+nsa_status nsa_workspace_size(const nsa_config* cfg, int op, size_t* bytes) {
+    g_detail.clear();
+    if (!bytes) return fail(NSA_ERR_NULL, "bytes is NULL");
+    Shape s;
+    nsa_status st = check_config(cfg, &s);
+    if (st != NSA_OK) return st;
+    switch (op) {
+        case NSA_OP_COMPRESS: *bytes = compress_ws(s).total; break;
+        case NSA_OP_SCORE_SELECT: *bytes = select_ws(s).total; break;
+        case NSA_OP_SPARSE_ATTN: *bytes = attn_ws(s).total; break;
+        case NSA_OP_DECODE: *bytes = decode_ws(s).total; break;
+        default: return fail(NSA_ERR_SHAPE, "unknown op");
+    }
+    return NSA_OK;
+}
+
+nsa_status nsa_compress(const nsa_config* cfg, const void* K, const void* V, const void* W_k, const void* W_v,
+                        const void* pe_k, const void* pe_v, void* K_cmp, void* V_cmp, void* ws, size_t ws_bytes,
+                        void* stream) {
+    g_detail.clear();
+    Shape s;
+    nsa_status st = check_config(cfg, &s);
+    if (st != NSA_OK) return st;
+    if (!K || !K_cmp) return fail(NSA_ERR_NULL, "K and K_cmp are required");
+    if (s.n_cmp == 0) return NSA_OK;
+    const int BG = s.B * s.Hkv;
+    const hipStream_t hs = as_stream(stream);
+    using nsa::u16;
+    if (s.phi == NSA_PHI_MEAN) {
+        if (s.dk > 1024) return fail(NSA_ERR_UNSUPPORTED, "d_k too large");
+        nsa::launch_compress_mean(static_cast<const u16*>(K), static_cast<u16*>(K_cmp), BG, s.T, s.dk, s.l, s.s,
+                                  s.n_cmp, hs);
+        return hip_check("compress_mean");
+    }
+    if (!V || !W_k || !W_v || !pe_k || !pe_v || !V_cmp)
+        return fail(NSA_ERR_NULL, "linear phi needs V, W_k, W_v, pe_k, pe_v and V_cmp");
+    const CompressWs w = compress_ws(s);
+    if ((st = check_ws(ws, ws_bytes, w.total)) != NSA_OK) return st;
+    if ((st = check_align16(K, "K")) != NSA_OK || (st = check_align16(V, "V")) != NSA_OK) return st;
+    const int KDk = s.l * s.dk, KDv = s.l * s.dv;
+    u16* wtk = at<u16>(ws, w.wt_k);
+    u16* wtv = at<u16>(ws, w.wt_v);
+    float* bk = at<float>(ws, w.bias_k);
+    float* bv = at<float>(ws, w.bias_v);
+    nsa::launch_transpose_w(static_cast<const u16*>(W_k), wtk, KDk, s.dk, hs);
+    nsa::launch_transpose_w(static_cast<const u16*>(W_v), wtv, KDv, s.dv, hs);
+    nsa::launch_pe_bias(static_cast<const u16*>(pe_k), wtk, bk, KDk, s.dk, hs);
+    nsa::launch_pe_bias(static_cast<const u16*>(pe_v), wtv, bv, KDv, s.dv, hs);
+    nsa::launch_compress_linear(static_cast<const u16*>(K), wtk, bk, static_cast<u16*>(K_cmp), BG, s.T, s.dk, s.dk,
+                                s.l, s.s, s.n_cmp, hs);
+    nsa::launch_compress_linear(static_cast<const u16*>(V), wtv, bv, static_cast<u16*>(V_cmp), BG, s.T, s.dv, s.dv,
+                                s.l, s.s, s.n_cmp, hs);
+    return hip_check("compress_linear");
+}
+
+nsa_status nsa_score_select(const nsa_config* cfg, const void* Q, const void* K_cmp, const void* V_cmp,
+                            int32_t* sel_idx, float* lse_cmp, float* o_cmp, void* ws, size_t ws_bytes,
+                            void* stream) {
+    g_detail.clear();
+    Shape s;
+    nsa_status st = check_config(cfg, &s);
+    if (st != NSA_OK) return st;
+    if (!Q || !sel_idx || !K_cmp) return fail(NSA_ERR_NULL, "Q, K_cmp and sel_idx are required");
+    if (s.n_cmp == 0) return fail(NSA_ERR_UNSUPPORTED, "seq_len shorter than cmp_block");
+    if (s.n_slc > 64 * 32) return fail(NSA_ERR_UNSUPPORTED, "at most 2048 selection blocks");
+    if (s.mode == NSA_SCORE_MEAN_DOT && (lse_cmp || o_cmp))
+        return fail(NSA_ERR_SHAPE, "MEAN_DOT mode produces no lse_cmp / o_cmp");
+    const bool with_o = o_cmp != nullptr;
+    if (with_o && !V_cmp) return fail(NSA_ERR_NULL, "o_cmp needs V_cmp");
+    const int nq = nsa::score_select_nq(s.G, s.mode);
+    const size_t lds = nsa::score_select_lds_bytes(s.dk, s.dv, s.G, s.mode, nq, with_o, s.n_slc);
+    if (lds > 160 * 1024) return fail(NSA_ERR_UNSUPPORTED, "too many selection blocks for one workgroup's LDS");
+    const SelectWs w = select_ws(s);
+    if ((st = check_ws(ws, ws_bytes, w.total)) != NSA_OK) return st;
+    const hipStream_t hs = as_stream(stream);
+    using nsa::u16;
+    nsa::SelParams p{};
+    p.Q = static_cast<const u16*>(Q);
+    p.Kc = static_cast<const u16*>(K_cmp);
+    p.sel = sel_idx;
+    p.T = s.T; p.Hkv = s.Hkv; p.N = s.n_cmp; p.l = s.l; p.s = s.s; p.lp = s.lp;
+    p.n_slc = s.n_slc; p.top_n = s.n; p.n_init = s.n_init; p.n_local = s.n_local;
+    p.scale_log2 = s.scale * nsa::kLog2eHost;
+    if (s.mode == NSA_SCORE_CMP_OVERLAP) {
+        float* m = at<float>(ws, w.m);
+        float* il = at<float>(ws, w.il);
+        if (!nsa::launch_cmp_stats(p.Q, p.Kc, m, il, lse_cmp, s.B, s.T, s.Hkv, s.G, s.dk, s.n_cmp, s.l, s.s,
+                                   p.scale_log2, hs))
+            return fail(NSA_ERR_UNSUPPORTED, "no statistics kernel for this shape");
+        p.stat_m = m;
+        p.stat_il = il;
+        if (with_o) {
+            u16* vct = at<u16>(ws, w.vct);
+            nsa::launch_transpose_v(static_cast<const u16*>(V_cmp), vct, s.B * s.Hkv, s.n_cmp, s.dv, w.npad, hs);
+            p.Vct = vct;
+            p.Npad = w.npad;
+            p.o_cmp = o_cmp;
+        }
+    }
+    if (!nsa::launch_score_select(s.mode, with_o, s.dk, s.dv, s.G, p, s.B, hs))
+        return fail(NSA_ERR_UNSUPPORTED, "no selection kernel for this shape");
+    return hip_check("score_select");
+}
+
+nsa_status nsa_select_from_scores(const nsa_config* cfg, const float* scores, int32_t* sel_idx, void* stream) {
+    g_detail.clear();
+    Shape s;
+    nsa_status st = check_config(cfg, &s);
+    if (st != NSA_OK) return st;
+    if (!scores || !sel_idx) return fail(NSA_ERR_NULL, "scores and sel_idx are required");
+    if (s.n_slc > 64 * 32) return fail(NSA_ERR_UNSUPPORTED, "at most 2048 selection blocks");
+    nsa::launch_select_from_scores(scores, sel_idx, s.B, s.T, s.Hkv, s.n_slc, s.lp, s.n, s.n_init, s.n_local,
+                                   as_stream(stream));
+    return hip_check("select_from_scores");
+}
+
+nsa_status nsa_sparse_attn_fwd(const nsa_config* cfg, const void* Q, const void* K, const void* V,
+                               const int32_t* sel_idx, const float* o_cmp, const float* gate_logits, void* O,
+                               void* ws, size_t ws_bytes, void* stream) {
+    g_detail.clear();
+    Shape s;
+    nsa_status st = check_config(cfg, &s);
+    if (st != NSA_OK) return st;
+    if (!Q || !K || !V || !O) return fail(NSA_ERR_NULL, "Q, K, V and O are required");
+    if ((s.br & NSA_BR_SLC) && !sel_idx) return fail(NSA_ERR_NULL, "sel_idx is required for the selected branch");
+    if ((s.br & NSA_BR_CMP) && !o_cmp) return fail(NSA_ERR_NULL, "o_cmp is required for the compressed branch");
+    if ((s.br & NSA_BR_WIN) && s.w <= 0) return fail(NSA_ERR_SHAPE, "window branch with window = 0");
+    const AttnWs w = attn_ws(s);
+    if ((st = check_ws(ws, ws_bytes, w.total)) != NSA_OK) return st;
+    const hipStream_t hs = as_stream(stream);
+    using nsa::u16;
+    u16* vt = at<u16>(ws, w.vt);
+    nsa::launch_transpose_v(static_cast<const u16*>(V), vt, s.B * s.Hkv, s.T, s.dv, w.tpad, hs);
+    nsa::AttnParams p{};
+    p.Q = static_cast<const u16*>(Q);
+    p.K = static_cast<const u16*>(K);
+    p.Vt = vt;
+    p.sel = sel_idx;
+    p.o_cmp = o_cmp;
+    p.gates = gate_logits;
+    p.O = static_cast<u16*>(O);
+    p.T = s.T; p.Tpad = w.tpad; p.Hkv = s.Hkv; p.G = s.G; p.lp = s.lp; p.top_n = s.n; p.window = s.w;
+    p.branches = s.br;
+    p.scale_log2 = s.scale * nsa::kLog2eHost;
+    if (!nsa::launch_sparse_attn(s.dk, s.dv, p, s.B, hs)) return fail(NSA_ERR_UNSUPPORTED, "no attention kernel");
+    return hip_check("sparse_attn");
+}
+
+nsa_status nsa_decode(const nsa_config* cfg, const void* q, const void* K_cache, const void* V_cache,
+                      const int32_t* cache_len, const void* K_cmp_cache, const void* V_cmp_cache,
+                      const float* gate_logits, void* O, int32_t* sel_idx_out, void* ws, size_t ws_bytes,
+                      void* stream) {
+    g_detail.clear();
+    Shape s;
+    nsa_status st = check_config(cfg, &s);
+    if (st != NSA_OK) return st;
+    if (!q || !K_cache || !V_cache || !cache_len || !O) return fail(NSA_ERR_NULL, "q, caches, cache_len and O are required");
+    if (s.mode != NSA_SCORE_CMP_OVERLAP || s.phi != NSA_PHI_LINEAR)
+        return fail(NSA_ERR_UNSUPPORTED, "decode implements the NSA (linear phi, compressed-overlap) mode");
+    if (s.n_cmp == 0) return fail(NSA_ERR_UNSUPPORTED, "cache capacity shorter than cmp_block");
+    if (!K_cmp_cache || !V_cmp_cache) return fail(NSA_ERR_NULL, "compressed caches are required");
+    if ((s.br & NSA_BR_WIN) && s.w <= 0) return fail(NSA_ERR_SHAPE, "window branch with window = 0");
+    if (s.n_slc > 64 * 32) return fail(NSA_ERR_UNSUPPORTED, "at most 2048 selection blocks");
+    const DecodeWs w = decode_ws(s);
+    if ((st = check_ws(ws, ws_bytes, w.total)) != NSA_OK) return st;
+    using nsa::u16;
+    nsa::DecodeParams p{};
+    p.q = static_cast<const u16*>(q);
+    p.K = static_cast<const u16*>(K_cache);
+    p.V = static_cast<const u16*>(V_cache);
+    p.cache_len = cache_len;
+    p.Kc = static_cast<const u16*>(K_cmp_cache);
+    p.Vc = static_cast<const u16*>(V_cmp_cache);
+    p.gates = gate_logits;
+    p.O = static_cast<u16*>(O);
+    p.sel_out = sel_idx_out;
+    p.part_m = at<float>(ws, w.pm);
+    p.part_l = at<float>(ws, w.pl);
+    p.part_o = at<float>(ws, w.po);
+    p.part_a = at<float>(ws, w.pa);
+    p.sel_ws = at<int32_t>(ws, w.sel);
+    p.ocmp_ws = at<float>(ws, w.ocmp);
+    p.att_m = at<float>(ws, w.am);
+    p.att_l = at<float>(ws, w.al);
+    p.att_o = at<float>(ws, w.ao);
+    p.B = s.B; p.L = s.T; p.Hkv = s.Hkv; p.G = s.G; p.Nc = s.n_cmp; p.l = s.l; p.s = s.s; p.lp = s.lp;
+    p.n_slc = s.n_slc; p.top_n = s.n; p.n_init = s.n_init; p.n_local = s.n_local; p.window = s.w;
+    p.branches = s.br; p.n_split = w.n_split; p.jb = w.jb; p.n_items = w.n_items;
+    p.scale_log2 = s.scale * nsa::kLog2eHost;
+    if (!nsa::launch_decode(s.dk, s.dv, p, as_stream(stream))) return fail(NSA_ERR_UNSUPPORTED, "no decode kernel");
+    return hip_check("decode");
+}
+
+const char* nsa_status_string(nsa_status status) {
+    switch (status) {
+        case NSA_OK: return "ok";
+        case NSA_ERR_NULL: return "required pointer is NULL";
+        case NSA_ERR_SHAPE: return "inconsistent or invalid sizes";
+        case NSA_ERR_UNSUPPORTED: return "shape not implemented by this build";
+        case NSA_ERR_WORKSPACE: return "workspace missing or too small";
+        case NSA_ERR_HIP: return "HIP launch failure";
+    }
+    return "unknown status";
+}
+
+const char* nsa_last_error_detail(void) { return g_detail.c_str(); }
+
+}  // extern "C"

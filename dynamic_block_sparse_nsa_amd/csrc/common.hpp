@@ -1,0 +1,96 @@
+// Internal device helpers shared by the gfx950 kernels of the NSA library.
+//
+// MFMA v_mfma_f32_16x16x32_bf16 operand layout (wave64, checked on gfx950):
+//   A[16][32]: lane l holds row l%16, k = 8*(l/16) .. 8*(l/16)+7 (one 16-byte vector)
+//   B[32][16]: lane l holds column l%16, k = 8*(l/16) .. +7
+//   C[16][16]: lane l holds column l%16, rows 4*(l/16) .. 4*(l/16)+3
+// Attention products are written key-major (S^T = K . Q^T) so that a lane owns one query
+// row (column) and several keys (rows): the softmax row statistics are then mostly
+// in-lane, and P^T comes out of the C layout already in the B-operand layout that the
+// value product O^T = V^T . P^T needs.  For that the value rows are stored transposed
+// (d-major) with each 32-key group permuted so that lane group q (= l/16) finds its
+// keys {4q..4q+3, 16+4q..16+4q+3} as 8 contiguous values (see vt_pos).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nsa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint16_t u16;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+// 16-byte global/LDS load of 8 bf16 values (address must be 16-byte aligned).
+__device__ __forceinline__ bf16x8 ld8(const u16* p) {
+    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(p));
+}
+
+__device__ __forceinline__ bf16x8 zero8() { return __builtin_bit_cast(bf16x8, uint4{0u, 0u, 0u, 0u}); }
+
+__device__ __forceinline__ u16 f2bf(float x) { return __builtin_bit_cast(u16, static_cast<__bf16>(x)); }
+
+__device__ __forceinline__ float bf2f(u16 x) { return __uint_as_float(static_cast<uint32_t>(x) << 16); }
+
+// P^T operand from two 16-key C tiles: slots 0..3 from tile a, 4..7 from tile b.
+__device__ __forceinline__ bf16x8 pack_p(const f32x4& a, const f32x4& b) {
+    bf16x8 r;
+    r[0] = static_cast<__bf16>(a[0]); r[1] = static_cast<__bf16>(a[1]);
+    r[2] = static_cast<__bf16>(a[2]); r[3] = static_cast<__bf16>(a[3]);
+    r[4] = static_cast<__bf16>(b[0]); r[5] = static_cast<__bf16>(b[1]);
+    r[6] = static_cast<__bf16>(b[2]); r[7] = static_cast<__bf16>(b[3]);
+    return r;
+}
+
+// Split P^T into bf16 high and low parts (p ~= hi + lo to about 2^-17 relative), so that
+// V^T.P^T = V^T.hi + V^T.lo keeps the probabilities' fp32 precision on the bf16 MFMA.
+__device__ __forceinline__ void pack_p_split(const f32x4& a, const f32x4& b, bf16x8& hi, bf16x8& lo) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const __bf16 ha = static_cast<__bf16>(a[r]), hb = static_cast<__bf16>(b[r]);
+        hi[r] = ha;
+        hi[4 + r] = hb;
+        lo[r] = static_cast<__bf16>(a[r] - static_cast<float>(ha));
+        lo[4 + r] = static_cast<__bf16>(b[r] - static_cast<float>(hb));
+    }
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Position of key k (0..31) inside its permuted 32-key group of a transposed value row.
+__host__ __device__ __forceinline__ int vt_pos(int k) {
+    return (k < 16) ? (8 * (k >> 2) + (k & 3)) : (8 * ((k - 16) >> 2) + 4 + (k & 3));
+}
+
+// Max / sum over the four lanes that share a query column (lanes l, l^16, l^32, l^48).
+__device__ __forceinline__ float col_max(float v) {
+    v = fmaxf(v, __shfl_xor(v, 16));
+    return fmaxf(v, __shfl_xor(v, 32));
+}
+__device__ __forceinline__ float col_sum(float v) {
+    v += __shfl_xor(v, 16);
+    return v + __shfl_xor(v, 32);
+}
+
+// Sum over aligned groups of G lanes within each 16-lane row (the G heads of a token).
+template <int G>
+__device__ __forceinline__ float head_sum(float v) {
+    if constexpr (G >= 16) v += __shfl_xor(v, 8);
+    if constexpr (G >= 8) v += __shfl_xor(v, 4);
+    if constexpr (G >= 4) v += __shfl_xor(v, 2);
+    if constexpr (G >= 2) v += __shfl_xor(v, 1);
+    return v;
+}
+
+__device__ __forceinline__ float sigmoidf_(float z) { return 1.0f / (1.0f + __expf(-z)); }
+
+}  // namespace nsa

@@ -1,0 +1,150 @@
+// Block compression (zjai.club notes, section 5: one key and one value per contiguous
+// block; MoBA mean pooling, section 16) and the layout transforms used by the
+// attention kernels.
+//
+// Linear phi:  cmp[i, :] = vec(X[i*s : i*s+l, :]) . W + bias,  bias = vec(PE) . W.
+// Row i of the GEMM operand is the l*d contiguous bf16 values starting at token i*s, so
+// the overlapping blocks are read straight from X with a row stride of s*d; W is
+// transposed once into the workspace so that both MFMA operands are 16-byte row loads.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace nsa {
+
+// ---------------------------------------------------------------------------
+// W [KD, dout] -> Wt [dout, KD]  (bf16, 64x64 tiles through LDS)
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void transpose_w_kernel(const u16* __restrict__ W, u16* __restrict__ Wt,
+                                                          int KD, int dout) {
+    __shared__ u16 tile[64][65];
+    const int k0 = blockIdx.x * 64, o0 = blockIdx.y * 64;
+    const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+    for (int r = ty; r < 64; r += 4) {
+        const int k = k0 + r, o = o0 + tx;
+        tile[r][tx] = (k < KD && o < dout) ? W[(size_t)k * dout + o] : (u16)0;
+    }
+    __syncthreads();
+    for (int r = ty; r < 64; r += 4) {
+        const int o = o0 + r, k = k0 + tx;
+        if (o < dout && k < KD) Wt[(size_t)o * KD + k] = tile[tx][r];
+    }
+}
+
+// bias[o] = sum_k pe_flat[k] * W[k][o], fp32, fixed-order tree reduction.
+__global__ __launch_bounds__(256) void pe_bias_kernel(const u16* __restrict__ pe, const u16* __restrict__ Wt,
+                                                      float* __restrict__ bias, int KD) {
+    __shared__ float red[256];
+    const int o = blockIdx.x;
+    float acc = 0.f;
+    for (int k = threadIdx.x; k < KD; k += 256) acc += bf2f(pe[k]) * bf2f(Wt[(size_t)o * KD + k]);
+    red[threadIdx.x] = acc;
+    __syncthreads();
+    for (int w = 128; w > 0; w >>= 1) {
+        if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) bias[o] = red[0];
+}
+
+// ---------------------------------------------------------------------------
+// Linear phi.  Grid (ceil(N/64), dout/64, B*Hkv); 4 waves, wave w owns 16 output rows
+// and 64 output columns.  X: [BG][T][d]; out: [BG][N][dout].
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void compress_linear_kernel(const u16* __restrict__ X,
+                                                              const u16* __restrict__ Wt,
+                                                              const float* __restrict__ bias,
+                                                              u16* __restrict__ out, int T, int d, int dout,
+                                                              int l, int s, int N) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int bg = blockIdx.z;
+    const int KD = l * d;
+    const int row0 = blockIdx.x * 64 + wave * 16;
+    const int col0 = blockIdx.y * 64;
+    const int li = lane & 15, lq = lane >> 4;
+    const int my_row = min(row0 + li, N - 1);  // clamp: rows past N are computed but not stored
+    const u16* xa = X + (size_t)bg * T * d + (size_t)my_row * s * d + lq * 8;
+    const u16* wb = Wt + (size_t)(col0 + li) * KD + lq * 8;
+    f32x4 acc[4] = {zero4(), zero4(), zero4(), zero4()};
+    for (int kk = 0; kk < KD; kk += 32) {
+        const bf16x8 a = ld8(xa + kk);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[c] = mfma16(a, ld8(wb + (size_t)c * 16 * KD + kk), acc[c]);
+    }
+    // C layout: lane owns column col0 + 16c + li and rows row0 + 4*lq + r.
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        const int o = col0 + 16 * c + li;
+        const float bo = bias[o];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int i = row0 + 4 * lq + r;
+            if (i < N) out[((size_t)bg * N + i) * dout + o] = f2bf(acc[c][r] + bo);
+        }
+    }
+}
+
+// Mean pooling: out[bg][i][e] = (1/l) sum_{r<l} X[bg][i*s + r][e]; grid (N, BG), block d.
+__global__ void compress_mean_kernel(const u16* __restrict__ X, u16* __restrict__ out, int T, int d, int l,
+                                     int s, int N) {
+    const int i = blockIdx.x, bg = blockIdx.y, e = threadIdx.x;
+    if (e >= d) return;
+    const u16* x = X + ((size_t)bg * T + (size_t)i * s) * d + e;
+    float acc = 0.f;
+    for (int r = 0; r < l; ++r) acc += bf2f(x[(size_t)r * d]);
+    out[((size_t)bg * N + i) * d + e] = f2bf(acc / (float)l);
+}
+
+// ---------------------------------------------------------------------------
+// Value transpose: X [BG][n][d] -> Xt [BG][d][n_pad], key k of each 32-group stored at
+// vt_pos(k); columns past n are zero (so masked-out keys contribute 0 * 0).
+// Grid (n_pad/64, ceil(d/64), BG).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void transpose_v_kernel(const u16* __restrict__ X, u16* __restrict__ Xt,
+                                                          int n, int d, int n_pad) {
+    __shared__ u16 tile[64][65];
+    const int bg = blockIdx.z;
+    const int t0 = blockIdx.x * 64, e0 = blockIdx.y * 64;
+    const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+    const u16* src = X + (size_t)bg * n * d;
+    for (int r = ty; r < 64; r += 4) {
+        const int t = t0 + r, e = e0 + tx;
+        tile[r][tx] = (t < n && e < d) ? src[(size_t)t * d + e] : (u16)0;
+    }
+    __syncthreads();
+    u16* dst = Xt + (size_t)bg * d * n_pad;
+    for (int r = ty; r < 64; r += 4) {
+        const int e = e0 + r;
+        const int t = t0 + tx;
+        if (e < d) dst[(size_t)e * n_pad + (t & ~31) + vt_pos(t & 31)] = tile[tx][r];
+    }
+}
+
+// ---------------------------------------------------------------------------
+// host launchers
+// ---------------------------------------------------------------------------
+void launch_transpose_w(const u16* W, u16* Wt, int KD, int dout, hipStream_t st) {
+    dim3 grid((KD + 63) / 64, (dout + 63) / 64);
+    transpose_w_kernel<<<grid, 256, 0, st>>>(W, Wt, KD, dout);
+}
+
+void launch_pe_bias(const u16* pe, const u16* Wt, float* bias, int KD, int dout, hipStream_t st) {
+    pe_bias_kernel<<<dout, 256, 0, st>>>(pe, Wt, bias, KD);
+}
+
+void launch_compress_linear(const u16* X, const u16* Wt, const float* bias, u16* out, int BG, int T, int d,
+                            int dout, int l, int s, int N, hipStream_t st) {
+    dim3 grid((N + 63) / 64, dout / 64, BG);
+    compress_linear_kernel<<<grid, 256, 0, st>>>(X, Wt, bias, out, T, d, dout, l, s, N);
+}
+
+void launch_compress_mean(const u16* X, u16* out, int BG, int T, int d, int l, int s, int N, hipStream_t st) {
+    dim3 grid(N, BG);
+    compress_mean_kernel<<<grid, d, 0, st>>>(X, out, T, d, l, s, N);
+}
+
+void launch_transpose_v(const u16* X, u16* Xt, int BG, int n, int d, int n_pad, hipStream_t st) {
+    dim3 grid(n_pad / 64, (d + 63) / 64, BG);
+    transpose_v_kernel<<<grid, 256, 0, st>>>(X, Xt, n, d, n_pad);
+}
+
+}  // namespace nsa

@@ -1,0 +1,88 @@
+// Internal host-side entry points of the kernels (called by the C ABI in api.cpp).
+// Every launcher assumes the arguments were validated by the API layer; launchers that
+// return bool report whether the shape has a compiled kernel.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace nsa {
+
+typedef uint16_t u16;
+
+constexpr float kLog2eHost = 1.4426950408889634f;
+
+// ---- compression and layout ----
+void launch_transpose_w(const u16* W, u16* Wt, int KD, int dout, hipStream_t st);
+void launch_pe_bias(const u16* pe, const u16* Wt, float* bias, int KD, int dout, hipStream_t st);
+void launch_compress_linear(const u16* X, const u16* Wt, const float* bias, u16* out, int BG, int T, int d,
+                            int dout, int l, int s, int N, hipStream_t st);
+void launch_compress_mean(const u16* X, u16* out, int BG, int T, int d, int l, int s, int N, hipStream_t st);
+void launch_transpose_v(const u16* X, u16* Xt, int BG, int n, int d, int n_pad, hipStream_t st);
+
+// ---- compressed attention + selection ----
+struct SelParams {
+    const u16* Q;          // [B,T,H,DK]
+    const u16* Kc;         // [B,Hkv,N,DK]
+    const u16* Vct;        // [B,Hkv,DV,Npad] transposed + permuted (mode 0 with o_cmp)
+    const float* stat_m;   // [B,T,H] running max (base 2) from the statistics pass
+    const float* stat_il;  // [B,T,H] 1 / sum
+    float* o_cmp;          // [B,T,H,DV] or null
+    int32_t* sel;          // [B,T,Hkv,top_n]
+    int T, Hkv, N, Npad, l, s, lp, n_slc, top_n, n_init, n_local;
+    float scale_log2;
+};
+bool launch_cmp_stats(const u16* Q, const u16* Kc, float* m, float* il, float* lse, int B, int T, int Hkv, int G,
+                      int DK, int N, int l, int s, float sl2, hipStream_t st);
+bool launch_score_select(int mode, bool with_o, int DK, int DV, int G, const SelParams& p, int B, hipStream_t st);
+size_t score_select_lds_bytes(int DK, int DV, int G, int mode, int NQ, bool with_o, int n_slc);
+int score_select_nq(int G, int mode);
+void launch_select_from_scores(const float* scores, int32_t* sel, int B, int T, int Hkv, int n_slc, int lp,
+                               int top_n, int n_init, int n_local, hipStream_t st);
+
+// ---- selected + window attention, gated sum ----
+struct AttnParams {
+    const u16* Q;        // [B,T,H,DK]
+    const u16* K;        // [B,Hkv,T,DK]
+    const u16* Vt;       // [B,Hkv,DV,Tpad] transposed + permuted
+    const int32_t* sel;  // [B,T,Hkv,top_n]
+    const float* o_cmp;  // [B,T,H,DV] (branch CMP)
+    const float* gates;  // [B,T,H,3] or null
+    u16* O;              // [B,T,H,DV]
+    int T, Tpad, Hkv, G, lp, top_n, window, branches;
+    float scale_log2;
+};
+bool launch_sparse_attn(int DK, int DV, const AttnParams& p, int B, hipStream_t st);
+
+// ---- decode ----
+struct DecodeParams {
+    const u16* q;              // [B,H,DK]
+    const u16* K;              // [B,Hkv,L,DK]
+    const u16* V;              // [B,Hkv,L,DV]
+    const int32_t* cache_len;  // [B]
+    const u16* Kc;             // [B,Hkv,Nc,DK]
+    const u16* Vc;             // [B,Hkv,Nc,DV]
+    const float* gates;        // [B,H,3] or null
+    u16* O;                    // [B,H,DV]
+    int32_t* sel_out;          // [B,Hkv,top_n] or null
+    // workspace
+    float* part_m;             // [B,Hkv,n_split,16]
+    float* part_l;             // [B,Hkv,n_split,16]
+    float* part_o;             // [B,Hkv,n_split,DV,16]
+    float* part_a;             // [B,Hkv,n_split,16,jb]
+    int32_t* sel_ws;           // [B,Hkv,top_n]
+    float* ocmp_ws;            // [B,Hkv,16,DV]
+    float* att_m;              // [B,Hkv,n_items,16]
+    float* att_l;              // [B,Hkv,n_items,16]
+    float* att_o;              // [B,Hkv,n_items,DV,16]
+    int B, L, Hkv, G, Nc, l, s, lp, n_slc, top_n, n_init, n_local, window, branches;
+    int n_split, jb, n_items;
+    float scale_log2;
+};
+constexpr int kDecodeSplitKeys = 256;
+int decode_jb(int l, int s, int lp);
+int decode_items(int top_n, int window);
+bool launch_decode(int DK, int DV, const DecodeParams& p, hipStream_t st);
+
+}  // namespace nsa

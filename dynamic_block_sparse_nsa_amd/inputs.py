@@ -165,29 +165,55 @@ def compressed_kv(cfg: NSAConfig, seed: int, n_cmp: int | None = None) -> dict:
 def block_lists(cfg: NSAConfig, seed: int, positions: np.ndarray | None = None) -> np.ndarray:
     """Random block index lists ``[B, P, Hkv, top_n]`` int32 with the workload's structure.
 
-    For a query at position t, the candidate blocks are 0 .. t // slc_block.  The first
-    ``n_init`` blocks and the ``n_local`` blocks ending at the query's own block are always
-    in the list; the remaining slots (up to ``top_n`` entries in total, or all candidates
-    if there are fewer) are drawn uniformly without replacement from the other
-    candidates.  Lists are sorted ascending and padded with -1.  ``positions`` defaults to
-    every position 0 .. T-1.
+    For a query at position t the candidate blocks are 0 .. jc with jc = t // slc_block.
+    The first ``n_init`` blocks and the ``n_local`` blocks ending at jc are always in the
+    list; the other candidates form the contiguous range between them, from which the
+    remaining slots (up to ``top_n`` entries in total, or all candidates if there are
+    fewer) are drawn uniformly without replacement (Floyd's method, vectorized over rows).
+    Lists are sorted ascending and padded with -1.  ``positions`` defaults to 0 .. T-1.
     """
     rng = np.random.Generator(np.random.PCG64(seed))
     B, Hkv, n = cfg.batch, cfg.num_kv_heads, cfg.top_n
     pos = np.arange(cfg.seq_len) if positions is None else np.asarray(positions)
-    out = np.full((B, len(pos), Hkv, n), -1, dtype=np.int32)
-    for pi, t in enumerate(pos):
-        jc = int(t) // cfg.slc_block
-        always = set(range(min(cfg.n_init, jc + 1))) | set(range(max(0, jc - cfg.n_local + 1), jc + 1))
-        others = np.array([j for j in range(jc + 1) if j not in always], dtype=np.int64)
-        m = min(n, jc + 1)
-        k = max(0, m - len(always))
-        for b in range(B):
-            for g in range(Hkv):
-                pick = rng.choice(others, size=k, replace=False) if k > 0 else np.empty(0, np.int64)
-                blocks = sorted(always | set(int(x) for x in pick))
-                out[b, pi, g, :len(blocks)] = blocks
-    return out
+    P = len(pos)
+    jc = (pos.astype(np.int64) // cfg.slc_block)
+    jc = np.broadcast_to(jc[None, :, None], (B, P, Hkv)).reshape(-1)
+    R = jc.size
+    f_init = np.minimum(cfg.n_init, jc + 1)
+    f_lo = np.maximum(0, jc - cfg.n_local + 1)
+    lo = f_init                                   # free candidates: lo .. f_lo-1
+    m = np.maximum(0, f_lo - lo)
+    n_forced = f_init + (jc - f_lo + 1) - np.maximum(0, f_init - f_lo)
+    k = np.minimum(np.maximum(0, np.minimum(n, jc + 1) - n_forced), m)
+    kmax = int(k.max()) if R else 0
+    picks = np.full((R, max(kmax, 1)), -1, dtype=np.int64)
+    for i in range(kmax):
+        active = i < k
+        j = m - k + i                             # Floyd: draw from 0 .. j
+        u = rng.random(R)
+        t = np.minimum((u * (j + 1)).astype(np.int64), j)
+        dup = (picks[:, :i] == t[:, None]).any(axis=1) if i else np.zeros(R, bool)
+        val = np.where(dup, j, t)
+        picks[:, i] = np.where(active, val, -1)
+    out = np.full((R, n), -1, dtype=np.int64)
+    # assemble: forced init blocks, free picks (offset by lo), local blocks; then sort
+    cols = np.full((R, n + 1), np.iinfo(np.int64).max, dtype=np.int64)
+    c = 0
+    for i in range(min(cfg.n_init, n)):
+        cols[:, c] = np.where(i < f_init, i, cols[:, c]); c += 1
+    for i in range(kmax):
+        cols[:, c] = np.where(picks[:, i] >= 0, lo + picks[:, i], cols[:, c]); c += 1
+    for i in range(min(cfg.n_local, n)):
+        blk = jc - i
+        ok = (blk >= f_lo) & (blk >= f_init)      # local blocks not already counted as initial
+        cols[:, c] = np.where(ok, blk, cols[:, c]); c += 1
+    cols = np.sort(cols[:, :c], axis=1) if c else cols[:, :0]
+    cnt = np.minimum(n, jc + 1)
+    take = min(n, cols.shape[1])
+    body = cols[:, :take]
+    body = np.where(np.arange(take)[None, :] < cnt[:, None], body, -1)
+    out[:, :take] = body
+    return out.reshape(B, P, Hkv, n).astype(np.int32)
 
 
 def cmp_outputs(cfg: NSAConfig, seed: int) -> np.ndarray:

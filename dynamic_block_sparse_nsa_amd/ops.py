@@ -1,0 +1,245 @@
+"""Python binding of the C ABI in ``include/nsa.h`` (``libnsa.so``).
+
+Argument marshalling only: every function checks tensor dtypes, devices and shapes,
+allocates outputs and workspaces with PyTorch (device memory and streams are all PyTorch
+is used for), and calls the library on the current stream.  No computation happens
+here, and there is no fallback: if the library is missing or a call fails, an
+exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+from .configs import NSAConfig
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libnsa.so")
+
+OP_COMPRESS, OP_SCORE_SELECT, OP_SPARSE_ATTN, OP_DECODE = 0, 1, 2, 3
+STATUS = {0: "ok", 1: "null", 2: "shape", 3: "unsupported", 4: "workspace", 5: "hip"}
+
+
+class NSAError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"nsa status {status} ({STATUS.get(status, '?')}): {detail}")
+        self.status = status
+        self.detail = detail
+
+
+class CConfig(ctypes.Structure):
+    _fields_ = [("struct_size", ctypes.c_uint32)] + [(n, ctypes.c_int32) for n in (
+        "batch", "seq_len", "num_kv_heads", "heads_per_group", "d_k", "d_v", "cmp_block", "cmp_stride",
+        "slc_block", "top_n", "n_init", "n_local", "window", "phi", "score_mode", "branches")] + [
+        ("softmax_scale", ctypes.c_float)]
+
+
+def c_config(cfg: NSAConfig, **over) -> CConfig:
+    c = CConfig()
+    c.struct_size = over.get("struct_size", ctypes.sizeof(CConfig))
+    for f, _ in CConfig._fields_[1:]:
+        setattr(c, f, over.get(f, getattr(cfg, f)))
+    return c
+
+
+_lib = None
+_P = ctypes.c_void_p
+
+
+def lib(build_if_missing: bool = True):
+    """Load libnsa.so (building it first if it is absent)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            if not build_if_missing:
+                raise RuntimeError(f"{LIB_PATH} is not built")
+            from .build import build
+            build()
+        L = ctypes.CDLL(LIB_PATH)
+        cp = ctypes.POINTER(CConfig)
+        L.nsa_workspace_size.argtypes = [cp, ctypes.c_int, ctypes.POINTER(ctypes.c_size_t)]
+        L.nsa_compress.argtypes = [cp] + [_P] * 9 + [ctypes.c_size_t, _P]
+        L.nsa_score_select.argtypes = [cp] + [_P] * 7 + [ctypes.c_size_t, _P]
+        L.nsa_select_from_scores.argtypes = [cp, _P, _P, _P]
+        L.nsa_sparse_attn_fwd.argtypes = [cp] + [_P] * 8 + [ctypes.c_size_t, _P]
+        L.nsa_decode.argtypes = [cp] + [_P] * 10 + [ctypes.c_size_t, _P]
+        for f in ("nsa_workspace_size", "nsa_compress", "nsa_score_select", "nsa_select_from_scores",
+                  "nsa_sparse_attn_fwd", "nsa_decode"):
+            getattr(L, f).restype = ctypes.c_int
+        L.nsa_status_string.argtypes = [ctypes.c_int]
+        L.nsa_status_string.restype = ctypes.c_char_p
+        L.nsa_last_error_detail.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def _check(rc: int):
+    if rc != 0:
+        raise NSAError(rc, lib().nsa_last_error_detail().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _need(t, name, dtype, shape=None):
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    return t
+
+
+def workspace_size(cfg: NSAConfig, op: int, **over) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().nsa_workspace_size(ctypes.byref(c_config(cfg, **over)), op, ctypes.byref(n)))
+    return int(n.value)
+
+
+def _workspace(cfg, op, device, workspace=None, **over):
+    need = workspace_size(cfg, op, **over)
+    if need == 0:
+        return None, 0
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+    if workspace.numel() < need:
+        raise ValueError(f"workspace needs {need} bytes")
+    return workspace, workspace.numel()
+
+
+# ---------------------------------------------------------------------------
+def compress(cfg: NSAConfig, K, V=None, w_k=None, w_v=None, pe_k=None, pe_v=None, *, seq_len=None,
+             out_k=None, out_v=None, workspace=None, stream=None):
+    """nsa_compress.  K [B,Hkv,T,dk] bf16 (T = cfg.seq_len unless ``seq_len`` is given).
+    Returns (K_cmp, V_cmp) ([B,Hkv,N,d] bf16; V_cmp is None in mean mode)."""
+    T = cfg.seq_len if seq_len is None else seq_len
+    c = cfg.replace(seq_len=T)
+    B, Hkv, dk, dv = c.batch, c.num_kv_heads, c.d_k, c.d_v
+    N = c.n_cmp
+    _need(K, "K", torch.bfloat16, (B, Hkv, T, dk))
+    dev = K.device
+    if out_k is None:
+        out_k = torch.empty((B, Hkv, N, dk), dtype=torch.bfloat16, device=dev)
+    _need(out_k, "out_k", torch.bfloat16, (B, Hkv, N, dk))
+    if c.phi == 0:
+        _need(V, "V", torch.bfloat16, (B, Hkv, T, dv))
+        _need(w_k, "w_k", torch.bfloat16, (c.cmp_block * dk, dk))
+        _need(w_v, "w_v", torch.bfloat16, (c.cmp_block * dv, dv))
+        _need(pe_k, "pe_k", torch.bfloat16, (c.cmp_block, dk))
+        _need(pe_v, "pe_v", torch.bfloat16, (c.cmp_block, dv))
+        if out_v is None:
+            out_v = torch.empty((B, Hkv, N, dv), dtype=torch.bfloat16, device=dev)
+        _need(out_v, "out_v", torch.bfloat16, (B, Hkv, N, dv))
+    else:
+        out_v = None
+    ws, nws = _workspace(c, OP_COMPRESS, dev, workspace)
+    _check(lib().nsa_compress(ctypes.byref(c_config(c)), _ptr(K), _ptr(V), _ptr(w_k), _ptr(w_v), _ptr(pe_k),
+                              _ptr(pe_v), _ptr(out_k), _ptr(out_v), _ptr(ws), nws, _stream(stream)))
+    return out_k, out_v
+
+
+def score_select(cfg: NSAConfig, Q, K_cmp, V_cmp=None, *, want_lse=False, want_ocmp=True, sel=None, lse=None,
+                 o_cmp=None, workspace=None, stream=None):
+    """nsa_score_select.  Returns (sel [B,T,Hkv,n] int32, lse [B,T,H] fp32 or None, o_cmp fp32 or None)."""
+    B, T, H, Hkv = cfg.batch, cfg.seq_len, cfg.num_heads, cfg.num_kv_heads
+    _need(Q, "Q", torch.bfloat16, (B, T, H, cfg.d_k))
+    _need(K_cmp, "K_cmp", torch.bfloat16, (B, Hkv, cfg.n_cmp, cfg.d_k))
+    dev = Q.device
+    mean = cfg.score_mode == 1
+    if sel is None:
+        sel = torch.empty((B, T, Hkv, cfg.top_n), dtype=torch.int32, device=dev)
+    _need(sel, "sel", torch.int32, (B, T, Hkv, cfg.top_n))
+    if want_lse and not mean and lse is None:
+        lse = torch.empty((B, T, H), dtype=torch.float32, device=dev)
+    if want_ocmp and not mean:
+        _need(V_cmp, "V_cmp", torch.bfloat16, (B, Hkv, cfg.n_cmp, cfg.d_v))
+        if o_cmp is None:
+            o_cmp = torch.empty((B, T, H, cfg.d_v), dtype=torch.float32, device=dev)
+        _need(o_cmp, "o_cmp", torch.float32, (B, T, H, cfg.d_v))
+    else:
+        o_cmp = None
+    if lse is not None:
+        _need(lse, "lse", torch.float32, (B, T, H))
+    ws, nws = _workspace(cfg, OP_SCORE_SELECT, dev, workspace)
+    _check(lib().nsa_score_select(ctypes.byref(c_config(cfg)), _ptr(Q), _ptr(K_cmp), _ptr(V_cmp if o_cmp is not None else None),
+                                  _ptr(sel), _ptr(lse), _ptr(o_cmp), _ptr(ws), nws, _stream(stream)))
+    return sel, lse, o_cmp
+
+
+def select_from_scores(cfg: NSAConfig, scores, *, sel=None, stream=None):
+    """nsa_select_from_scores.  scores [B,T,Hkv,N_slc] fp32 -> sel [B,T,Hkv,n] int32."""
+    B, T, Hkv = cfg.batch, cfg.seq_len, cfg.num_kv_heads
+    _need(scores, "scores", torch.float32, (B, T, Hkv, cfg.n_slc))
+    if sel is None:
+        sel = torch.empty((B, T, Hkv, cfg.top_n), dtype=torch.int32, device=scores.device)
+    _need(sel, "sel", torch.int32, (B, T, Hkv, cfg.top_n))
+    _check(lib().nsa_select_from_scores(ctypes.byref(c_config(cfg)), _ptr(scores), _ptr(sel), _stream(stream)))
+    return sel
+
+
+def sparse_attn_fwd(cfg: NSAConfig, Q, K, V, sel=None, o_cmp=None, gates=None, *, out=None, workspace=None,
+                    stream=None):
+    """nsa_sparse_attn_fwd.  Returns O [B,T,H,dv] bf16."""
+    B, T, H, Hkv = cfg.batch, cfg.seq_len, cfg.num_heads, cfg.num_kv_heads
+    _need(Q, "Q", torch.bfloat16, (B, T, H, cfg.d_k))
+    _need(K, "K", torch.bfloat16, (B, Hkv, T, cfg.d_k))
+    _need(V, "V", torch.bfloat16, (B, Hkv, T, cfg.d_v))
+    if cfg.branches & 2:
+        _need(sel, "sel", torch.int32, (B, T, Hkv, cfg.top_n))
+    if cfg.branches & 1:
+        _need(o_cmp, "o_cmp", torch.float32, (B, T, H, cfg.d_v))
+    if gates is not None:
+        _need(gates, "gates", torch.float32, (B, T, H, 3))
+    if out is None:
+        out = torch.empty((B, T, H, cfg.d_v), dtype=torch.bfloat16, device=Q.device)
+    _need(out, "out", torch.bfloat16, (B, T, H, cfg.d_v))
+    ws, nws = _workspace(cfg, OP_SPARSE_ATTN, Q.device, workspace)
+    _check(lib().nsa_sparse_attn_fwd(ctypes.byref(c_config(cfg)), _ptr(Q), _ptr(K), _ptr(V),
+                                     _ptr(sel if cfg.branches & 2 else None), _ptr(o_cmp if cfg.branches & 1 else None),
+                                     _ptr(gates), _ptr(out), _ptr(ws), nws, _stream(stream)))
+    return out
+
+
+def decode(cfg: NSAConfig, q, K_cache, V_cache, cache_len, K_cmp, V_cmp, gates=None, *, out=None, sel=None,
+           want_sel=True, workspace=None, stream=None):
+    """nsa_decode.  Returns (O [B,H,dv] bf16, sel [B,Hkv,n] int32 or None)."""
+    B, L, H, Hkv = cfg.batch, cfg.seq_len, cfg.num_heads, cfg.num_kv_heads
+    _need(q, "q", torch.bfloat16, (B, H, cfg.d_k))
+    _need(K_cache, "K_cache", torch.bfloat16, (B, Hkv, L, cfg.d_k))
+    _need(V_cache, "V_cache", torch.bfloat16, (B, Hkv, L, cfg.d_v))
+    _need(cache_len, "cache_len", torch.int32, (B,))
+    _need(K_cmp, "K_cmp", torch.bfloat16, (B, Hkv, cfg.n_cmp, cfg.d_k))
+    _need(V_cmp, "V_cmp", torch.bfloat16, (B, Hkv, cfg.n_cmp, cfg.d_v))
+    if gates is not None:
+        _need(gates, "gates", torch.float32, (B, H, 3))
+    if out is None:
+        out = torch.empty((B, H, cfg.d_v), dtype=torch.bfloat16, device=q.device)
+    if want_sel and sel is None:
+        sel = torch.empty((B, Hkv, cfg.top_n), dtype=torch.int32, device=q.device)
+    ws, nws = _workspace(cfg, OP_DECODE, q.device, workspace)
+    _check(lib().nsa_decode(ctypes.byref(c_config(cfg)), _ptr(q), _ptr(K_cache), _ptr(V_cache), _ptr(cache_len),
+                            _ptr(K_cmp), _ptr(V_cmp), _ptr(gates), _ptr(out), _ptr(sel), _ptr(ws), nws,
+                            _stream(stream)))
+    return out, sel
+
+
+def prefill(cfg: NSAConfig, Q, K, V, w_k=None, w_v=None, pe_k=None, pe_v=None, gates=None, stream=None):
+    """The whole prefill hot path: compress -> score_select -> sparse_attn_fwd.  Returns
+    dict(out, sel, o_cmp, k_cmp, v_cmp)."""
+    k_cmp, v_cmp = compress(cfg, K, V, w_k, w_v, pe_k, pe_v, stream=stream)
+    sel, _, o_cmp = score_select(cfg, Q, k_cmp, v_cmp, want_ocmp=bool(cfg.branches & 1), stream=stream)
+    out = sparse_attn_fwd(cfg, Q, K, V, sel, o_cmp, gates, stream=stream)
+    return {"out": out, "sel": sel, "o_cmp": o_cmp, "k_cmp": k_cmp, "v_cmp": v_cmp}

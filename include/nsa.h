@@ -1,0 +1,176 @@
+/*
+ * nsa.h - C ABI of an MI355X (gfx950) library for the forward pass of Native Sparse
+ * Attention (NSA) and of the MoBA-style mean-pooled block selection.
+ *
+ * What the operations compute (the pages give the method in prose only):
+ *   - youtublog.net, "Songlin Yang explains attention mechanisms from DeepSeek, Kimi and
+ *     MiniMax" (English page): attention weights the values by a softmax of query/key
+ *     scores over the keys a query may access, with a causal mask; NSA has three
+ *     branches - coarse attention over compressed blocks, fine attention over a few
+ *     selected blocks, a sliding window - mixed by learned gates; the heads of a GQA
+ *     group aggregate their scores and share one selection; MoBA represents a block by
+ *     mean pooling and lets each head select its own blocks.
+ *   - zjai.club episode notes, section 5 (each contiguous KV block compressed to one key
+ *     and one value; block scores pick the top-k blocks, whose tokens get token-level
+ *     attention; the window attends to nearby tokens), section 6 (a gate computed from
+ *     the current token scales each branch output, and the three are added), section 8
+ *     (scores summed over the group's heads, then one top-k), section 13 (decoding is
+ *     memory-bound: its cost is the KV bytes read per step), sections 16-17 (MoBA:
+ *     mean-pooled block keys, query-mean inner product as the score, 512-token blocks,
+ *     top 3).
+ *   - sunshychen.top MoBA/NSA comparison: the query's own block is always attended and
+ *     causally masked; with fixed block sizes the compressed attention scores serve
+ *     directly as selection scores; the NSA window crosses block boundaries.
+ *
+ * Conventions for every call:
+ *   - All tensor pointers are DEVICE pointers.  bf16 tensors are raw 16-bit patterns.
+ *   - Layouts (row-major, last index fastest), with H = num_kv_heads * heads_per_group
+ *     and query head h = g * heads_per_group + i belonging to KV group g:
+ *       Q, O            [B, T, H, d]           (prefill)
+ *       K, V            [B, H_kv, T, d]        (also the decode caches, T = capacity)
+ *       K_cmp, V_cmp    [B, H_kv, N_cmp, d]    N_cmp = floor((T - l)/s) + 1
+ *       sel_idx         [B, T, H_kv, top_n]    int32, ascending, padded with -1
+ *       gate_logits     [B, T, H, 3]           fp32, order (compressed, selected, window)
+ *       o_cmp, lse_cmp  [B, T, H, d_v], [B, T, H]   fp32
+ *   - The caller owns every buffer.  The library never allocates device memory; calls
+ *     that need scratch take a caller workspace whose size nsa_workspace_size reports.
+ *   - Calls are asynchronous on the given stream (a hipStream_t; NULL = default stream)
+ *     and never synchronize.  Inputs are read-only; outputs are fully overwritten.
+ *   - Arguments are validated on the host before anything is launched; a failing call
+ *     launches nothing and returns a status (details: nsa_last_error_detail).
+ *   - Calls on different streams with disjoint outputs and workspaces may overlap.
+ */
+#ifndef NSA_H
+#define NSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    NSA_OK = 0,
+    NSA_ERR_NULL = 1,          /* a required pointer is NULL */
+    NSA_ERR_SHAPE = 2,         /* sizes are inconsistent or non-positive */
+    NSA_ERR_UNSUPPORTED = 3,   /* a shape this build's kernels do not implement */
+    NSA_ERR_WORKSPACE = 4,     /* workspace NULL or smaller than nsa_workspace_size */
+    NSA_ERR_HIP = 5            /* a HIP launch failed (see nsa_last_error_detail) */
+} nsa_status;
+
+/* Block representation (step "compress"). */
+typedef enum {
+    NSA_PHI_LINEAR = 0,   /* cmp[i] = vec(X[i*s : i*s+l] + PE) . W  (NSA) */
+    NSA_PHI_MEAN = 1      /* cmp[i] = mean of X[i*s : i*s+l]         (MoBA) */
+} nsa_phi;
+
+/* Block score used for selection. */
+typedef enum {
+    NSA_SCORE_CMP_OVERLAP = 0, /* sum over the group's heads and over the compressed blocks
+                                  overlapping the block of the compressed attention
+                                  probabilities (NSA) */
+    NSA_SCORE_MEAN_DOT = 1     /* sum over the group's heads of <q, mean key of the block>
+                                  over complete earlier blocks (MoBA; needs l = s = l') */
+} nsa_score_mode;
+
+/* Branch bits for nsa_config.branches. */
+enum { NSA_BR_CMP = 1, NSA_BR_SLC = 2, NSA_BR_WIN = 4 };
+
+/* Work items for nsa_workspace_size. */
+enum { NSA_OP_COMPRESS = 0, NSA_OP_SCORE_SELECT = 1, NSA_OP_SPARSE_ATTN = 2, NSA_OP_DECODE = 3 };
+
+typedef struct nsa_config {
+    uint32_t struct_size;      /* sizeof(nsa_config) */
+    int32_t batch;             /* B */
+    int32_t seq_len;           /* T (prefill) or cache capacity L (decode) */
+    int32_t num_kv_heads;      /* H_kv: KV heads = GQA groups */
+    int32_t heads_per_group;   /* G: query heads sharing one KV head (1, 2, 4, 8 or 16) */
+    int32_t d_k;               /* query/key head dim (64, 128 or 192) */
+    int32_t d_v;               /* value head dim (64 or 128) */
+    int32_t cmp_block;         /* l: tokens per compressed block */
+    int32_t cmp_stride;        /* s: stride between compressed blocks (s | l, s | l') */
+    int32_t slc_block;         /* l': tokens per selection block (multiple of 32) */
+    int32_t top_n;             /* n: selected blocks per (query, group), forced ones included (<= 32) */
+    int32_t n_init;            /* blocks 0 .. n_init-1 are always selected */
+    int32_t n_local;           /* the n_local blocks ending at the query's own block are always selected */
+    int32_t window;            /* w: sliding-window length including the query (0 = no window) */
+    int32_t phi;               /* nsa_phi */
+    int32_t score_mode;        /* nsa_score_mode */
+    int32_t branches;          /* OR of NSA_BR_* */
+    float softmax_scale;       /* <= 0 selects 1/sqrt(d_k) (MEAN_DOT scores are never scaled) */
+} nsa_config;
+
+/* Bytes of workspace `op` needs for this configuration (0 is possible). */
+nsa_status nsa_workspace_size(const nsa_config* cfg, int op, size_t* bytes);
+
+/* Step "compress": one key (and, for NSA_PHI_LINEAR, one value) per block of l tokens
+ * taken every s tokens (zjai.club notes, section 5; MoBA mean pooling, section 16).
+ *   NSA_PHI_LINEAR: K_cmp[b,g,i,:] = sum_{r<l, e<d_k} (K[b,g,i*s+r,e] + pe_k[r,e]) * W_k[r*d_k+e, :]
+ *                   and the same for V with W_v [l*d_v, d_v] and pe_v [l, d_v].
+ *                   W_k [l*d_k, d_k] and pe_k [l, d_k] are bf16 and shared by all KV heads.
+ *   NSA_PHI_MEAN:   K_cmp[b,g,i,:] = (1/l) * sum_{r<l} K[b,g,i*s+r,:]; V, W_*, pe_*, V_cmp unused.
+ * Accumulates in fp32 and rounds once to bf16.  Works for the decode caches too (T = L). */
+nsa_status nsa_compress(const nsa_config* cfg, const void* K, const void* V,
+                        const void* W_k, const void* W_v, const void* pe_k, const void* pe_v,
+                        void* K_cmp, void* V_cmp, void* ws, size_t ws_bytes, void* stream);
+
+/* Steps "compressed attention, block scores, selection" (zjai.club notes, sections 5 and 8;
+ * sunshychen.top: compressed scores reused as selection scores).
+ * NSA_SCORE_CMP_OVERLAP: for query t and head h, compressed block i is visible when
+ *   i*s + l - 1 <= t; p = softmax(scale * q . K_cmp) over visible blocks;
+ *   lse_cmp = log sum exp (-inf when nothing is visible);
+ *   o_cmp = sum_i p_i V_cmp[i] (0 when nothing is visible);
+ *   score[j] = sum over the group's heads and visible i whose tokens intersect block j of p_i.
+ * NSA_SCORE_MEAN_DOT: score[j] = sum over the group's heads of q . K_cmp[j] for j < t / l'.
+ * Selection (both modes): with jc = t / l', the forced blocks are 0..n_init-1 and
+ *   jc-n_local+1..jc (within 0..jc); the other blocks 0..jc are taken by descending score,
+ *   ties to the lower index, until min(top_n, jc+1) blocks are chosen.
+ * Outputs: sel_idx (required); lse_cmp and o_cmp optional (NULL = not produced; o_cmp
+ *   needs V_cmp; both must be NULL in MEAN_DOT mode).  Scores are fp32. */
+nsa_status nsa_score_select(const nsa_config* cfg, const void* Q, const void* K_cmp,
+                            const void* V_cmp, int32_t* sel_idx, float* lse_cmp, float* o_cmp,
+                            void* ws, size_t ws_bytes, void* stream);
+
+/* Selection alone, from caller scores [B, T, H_kv, N_slc] fp32 (N_slc = ceil(T / l')),
+ * with the rule of nsa_score_select.  For custom block scores; also exercises the top-n
+ * stage in isolation. */
+nsa_status nsa_select_from_scores(const nsa_config* cfg, const float* scores, int32_t* sel_idx,
+                                  void* stream);
+
+/* Steps "selected attention, sliding window, gated sum" (zjai.club notes, sections 5-6;
+ * sunshychen.top: the window crosses block boundaries, the query's own block is causal).
+ *   o_slc = softmax(scale * q . K) . V over tokens of the listed blocks that are <= t;
+ *   o_win = the same over tokens max(0, t-w+1) .. t;
+ *   O = sum over enabled branches of sigmoid(z_branch) * o_branch, with o_cmp taken from the
+ *   caller (as produced by nsa_score_select) when NSA_BR_CMP is set.
+ * sel_idx entries must be distinct blocks <= t / l' (or -1).  gate_logits NULL = weight 1.
+ * O is bf16 [B, T, H, d_v]. */
+nsa_status nsa_sparse_attn_fwd(const nsa_config* cfg, const void* Q, const void* K, const void* V,
+                               const int32_t* sel_idx, const float* o_cmp, const float* gate_logits,
+                               void* O, void* ws, size_t ws_bytes, void* stream);
+
+/* One decode step (zjai.club notes, section 13): every sequence b has one new query at
+ * position t_b = cache_len[b] - 1 whose K/V are already in the caches; K_cmp_cache /
+ * V_cmp_cache hold the compressed blocks of the cache (nsa_compress over the cache).
+ * Computes exactly the prefill result for row t_b: compressed branch, scores, selection,
+ * selected and window branches, gated sum.
+ *   q [B, H, d_k] bf16; caches [B, H_kv, L, d] bf16; compressed caches [B, H_kv, N_cmp(L), d];
+ *   cache_len [B] int32 device array (1 <= cache_len <= L); gate_logits [B, H, 3] (NULL = 1);
+ *   O [B, H, d_v] bf16; sel_idx_out [B, H_kv, top_n] (optional). */
+nsa_status nsa_decode(const nsa_config* cfg, const void* q, const void* K_cache, const void* V_cache,
+                      const int32_t* cache_len, const void* K_cmp_cache, const void* V_cmp_cache,
+                      const float* gate_logits, void* O, int32_t* sel_idx_out,
+                      void* ws, size_t ws_bytes, void* stream);
+
+/* Static description of a status code. */
+const char* nsa_status_string(nsa_status status);
+
+/* Detail of the last failing call on this thread ("" if none). */
+const char* nsa_last_error_detail(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NSA_H */

@@ -1,0 +1,192 @@
+"""Host-side checks of the C ABI and the input generators (no GPU needed).
+
+Every library call validates its arguments before launching anything, so the error
+paths run here without a device.  The library must load and export every entry point
+that include/nsa.h declares.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from dynamic_block_sparse_nsa_amd import inputs
+from dynamic_block_sparse_nsa_amd.configs import CONFIGS, TINY, P8K, MOBA, DECODE
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "nsa.h")
+
+torch = pytest.importorskip("torch")
+from dynamic_block_sparse_nsa_amd import ops  # noqa: E402
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^(?:nsa_status|const char\*)\s+(nsa_\w+)\(", text, re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = ops.lib()
+    names = declared_functions()
+    assert len(names) >= 8
+    for n in names:
+        assert hasattr(L, n), n
+    # nothing beyond the header is exported under the nsa_ prefix
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", ops.LIB_PATH], capture_output=True, text=True).stdout
+    exported = sorted(set(re.findall(r" T (nsa_\w+)", out)))
+    assert exported == names
+
+
+def test_struct_layout_matches_header():
+    # 1 uint32 + 16 int32 + 1 float
+    assert ctypes.sizeof(ops.CConfig) == 4 * 18
+
+
+def _cfg(c=P8K, **over):
+    return ctypes.byref(ops.c_config(c, **over))
+
+
+def _ws(c=P8K, op=0, **over):
+    n = ctypes.c_size_t(0)
+    rc = ops.lib().nsa_workspace_size(_cfg(c, **over), op, ctypes.byref(n))
+    return rc, n.value
+
+
+@pytest.mark.parametrize("name", list(CONFIGS))
+def test_workspace_sizes(name):
+    c = CONFIGS[name]
+    for op in range(4):
+        rc, n = _ws(c, op)
+        assert rc == 0
+        assert n % 256 == 0
+    # the attention workspace holds the transposed values: B*Hkv*dv*roundup(T,64)*2 bytes
+    rc, n = _ws(c, ops.OP_SPARSE_ATTN)
+    assert n == c.batch * c.num_kv_heads * c.d_v * (-(-c.seq_len // 64) * 64) * 2
+
+
+@pytest.mark.parametrize("over,status", [
+    ({"heads_per_group": 3}, 3),
+    ({"d_k": 96}, 3),
+    ({"cmp_stride": 5}, 3),
+    ({"slc_block": 48}, 3),
+    ({"top_n": 2}, 3),               # fewer than the 3 forced blocks
+    ({"top_n": 40}, 3),
+    ({"batch": 0}, 2),
+    ({"seq_len": -1}, 2),
+    ({"window": -1}, 2),
+    ({"branches": 0}, 2),
+    ({"branches": 9}, 2),
+    ({"phi": 7}, 2),
+    ({"score_mode": 1}, 3),          # mean-key scores need l == s == l'
+    ({"struct_size": 8}, 2),
+])
+def test_config_validation(over, status):
+    rc, _ = _ws(P8K, 0, **over)
+    assert rc == status
+    assert ops.lib().nsa_last_error_detail().decode() != ""
+
+
+def test_null_config_and_output():
+    L = ops.lib()
+    n = ctypes.c_size_t(0)
+    assert L.nsa_workspace_size(None, 0, ctypes.byref(n)) == 1
+    assert L.nsa_workspace_size(_cfg(), 0, None) == 1
+    assert L.nsa_workspace_size(_cfg(), 9, ctypes.byref(n)) == 2
+
+
+def test_calls_reject_null_pointers_before_launch():
+    L = ops.lib()
+    fake = ctypes.c_void_p(0x1000)
+    assert L.nsa_compress(_cfg(), None, fake, fake, fake, fake, fake, fake, fake, None, 0, None) == 1
+    assert L.nsa_compress(_cfg(), fake, None, fake, fake, fake, fake, fake, fake, None, 0, None) == 1
+    assert L.nsa_score_select(_cfg(), None, fake, fake, fake, None, None, None, 0, None) == 1
+    assert L.nsa_score_select(_cfg(), fake, fake, fake, None, None, None, None, 0, None) == 1
+    assert L.nsa_sparse_attn_fwd(_cfg(), fake, fake, None, fake, fake, None, fake, None, 0, None) == 1
+    assert L.nsa_sparse_attn_fwd(_cfg(), fake, fake, fake, None, fake, None, fake, None, 0, None) == 1
+    assert L.nsa_sparse_attn_fwd(_cfg(), fake, fake, fake, fake, None, None, fake, None, 0, None) == 1
+    assert L.nsa_decode(_cfg(DECODE), fake, fake, fake, None, fake, fake, None, fake, None, None, 0, None) == 1
+    assert L.nsa_select_from_scores(_cfg(), None, fake, None) == 1
+
+
+def test_calls_reject_small_workspace_before_launch():
+    L = ops.lib()
+    fake = ctypes.c_void_p(0x1000)
+    assert L.nsa_compress(_cfg(), fake, fake, fake, fake, fake, fake, fake, fake, None, 0, None) == 4
+    assert L.nsa_score_select(_cfg(), fake, fake, fake, fake, None, fake, fake, 16, None) == 4
+    assert L.nsa_sparse_attn_fwd(_cfg(), fake, fake, fake, fake, fake, None, fake, fake, 16, None) == 4
+    assert L.nsa_decode(_cfg(DECODE), fake, fake, fake, fake, fake, fake, None, fake, None, fake, 16, None) == 4
+    # unaligned workspace
+    big = 1 << 40
+    assert L.nsa_sparse_attn_fwd(_cfg(), fake, fake, fake, fake, fake, None, fake, ctypes.c_void_p(0x1001), big,
+                                 None) == 4
+
+
+def test_mode_specific_rules():
+    L = ops.lib()
+    fake = ctypes.c_void_p(0x1000)
+    # MEAN_DOT mode cannot produce o_cmp / lse
+    assert L.nsa_score_select(_cfg(MOBA), fake, fake, None, fake, fake, None, None, 0, None) == 2
+    # decode implements the NSA mode only
+    assert L.nsa_decode(_cfg(MOBA), fake, fake, fake, fake, fake, fake, None, fake, None, fake, 1 << 40, None) == 3
+    # window branch needs a window
+    assert L.nsa_sparse_attn_fwd(_cfg(P8K, window=0), fake, fake, fake, fake, fake, None, fake, None, 0, None) == 2
+    # shorter than one compressed block
+    assert L.nsa_score_select(_cfg(P8K, seq_len=16), fake, fake, fake, fake, None, None, fake, 1 << 40, None) == 3
+
+
+def test_status_strings():
+    L = ops.lib()
+    for code in range(6):
+        assert L.nsa_status_string(code).decode()
+    assert L.nsa_status_string(77).decode() == "unknown status"
+
+
+# ---------------------------------------------------------------------------
+# input generators
+# ---------------------------------------------------------------------------
+def test_bf16_rounding_matches_torch():
+    rng = np.random.default_rng(0)
+    x = (rng.standard_normal(100000) * np.exp(rng.uniform(-20, 20, 100000))).astype(np.float32)
+    x[:8] = [0.0, -0.0, 1.0, 1.00390625, 1.01171875, -3.0078125, 65504.0, 1e-30]
+    ours = inputs.f32_to_bf16_bits(x)
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(ours, ref)
+    np.testing.assert_array_equal(inputs.bf16_bits_to_f32(ours), torch.from_numpy(x).to(torch.bfloat16).float().numpy())
+
+
+def test_chunked_draws_equal_single_draw():
+    a = inputs._normal_bf16(np.random.Generator(np.random.PCG64(3)), (5, (1 << 24) // 5 + 7))
+    b = inputs.f32_to_bf16_bits(np.random.Generator(np.random.PCG64(3)).standard_normal(a.size, dtype=np.float32))
+    np.testing.assert_array_equal(a.reshape(-1), b)
+
+
+def test_prefill_inputs_shapes_and_determinism():
+    a = inputs.prefill_inputs(TINY)
+    b = inputs.prefill_inputs(TINY)
+    for k in ("q", "k", "v", "w_k", "w_v", "pe_k", "pe_v", "gates"):
+        np.testing.assert_array_equal(a[k], b[k])
+    assert a["q"].shape == (1, 1024, 4, 64) and a["k"].shape == (1, 1, 1024, 64)
+    assert a["w_k"].shape == (32 * 64, 64)
+    # the fp32 draws round to the bf16 arrays
+    np.testing.assert_array_equal(inputs.f32_to_bf16_bits(a["raw"]["q"]), a["q"])
+    # Xavier bound
+    wk = inputs.bf16_bits_to_f32(a["w_k"])
+    assert np.abs(wk).max() <= np.sqrt(6.0 / (32 * 64 + 64)) * 1.01
+
+
+def test_block_lists_structure():
+    cfg = TINY.replace(seq_len=700)
+    pos = np.arange(700)
+    sel = inputs.block_lists(cfg, 5, pos)
+    for t in range(0, 700, 7):
+        row = sel[0, t, 0]
+        jc = t // 64
+        valid = row[row >= 0]
+        assert (np.diff(valid) > 0).all()
+        assert valid.max() == jc and valid.min() == 0
+        assert len(valid) == min(cfg.top_n, jc + 1)
+        assert (row[len(valid):] == -1).all()
+        if jc >= 1:
+            assert jc - 1 in valid

@@ -1,0 +1,331 @@
+"""GPU parity of every library call against the fp64 oracle (needs an MI355X).
+
+Each call is checked on its own, with both sides fed identical inputs: the seeded
+generator's draws, or the oracle's own upstream results (never the GPU's).  Sizes span
+several tiles plus ragged tails; the full-size workloads (8K, 64K, decode at 65536, MoBA
+at 131072) are checked on sampled rows that the oracle computes one by one.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import pipeline
+from dynamic_block_sparse_nsa_amd import inputs, ops
+from dynamic_block_sparse_nsa_amd.configs import TINY, P8K, P64K, DECODE, MOBA, BR_SLC, BR_WIN
+from nsa_testlib import (GAP, bf16_dev_to_f64, check_close, check_selection, check_ulp, dev_bf16, dev_f32, dev_i32,
+                         f64_to_dev_bf16, sample_rows)
+
+pytestmark = pytest.mark.gpu
+
+RAGGED = TINY.replace(name="ragged", seq_len=1000, seed=11)
+RAGGED16 = P8K.replace(name="ragged16", seq_len=2085, seed=12)
+
+
+def f64(bits):
+    return inputs.bf16_bits_to_f64(bits)
+
+
+def announce(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+# ---------------------------------------------------------------------------
+# compression
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("cfg", [TINY, RAGGED, P8K], ids=lambda c: c.name)
+def test_compress_linear_all_blocks(cfg):
+    announce(f"compress linear {cfg.name}")
+    inp = inputs.prefill_inputs(cfg)
+    kc, vc = ops.compress(cfg, dev_bf16(inp["k"]), dev_bf16(inp["v"]), dev_bf16(inp["w_k"]), dev_bf16(inp["w_v"]),
+                          dev_bf16(inp["pe_k"]), dev_bf16(inp["pe_v"]))
+    torch.cuda.synchronize()
+    gk, gv = bf16_dev_to_f64(kc), bf16_dev_to_f64(vc)
+    K, V = f64(inp["k"][0]), f64(inp["v"][0])
+    rk, rv = pipeline.compress_all(cfg, K, V, f64(inp["w_k"]), f64(inp["w_v"]), f64(inp["pe_k"]), f64(inp["pe_v"]),
+                                   round_cmp=False)
+    check_ulp(gk[0], rk, f"{cfg.name} K_cmp")
+    check_ulp(gv[0], rv, f"{cfg.name} V_cmp")
+
+
+def test_compress_linear_64k_sampled_blocks():
+    cfg = P64K
+    announce("compress linear 64k sampled")
+    inp = inputs.prefill_inputs(cfg)
+    kc, vc = ops.compress(cfg, dev_bf16(inp["k"]), dev_bf16(inp["v"]), dev_bf16(inp["w_k"]), dev_bf16(inp["w_v"]),
+                          dev_bf16(inp["pe_k"]), dev_bf16(inp["pe_v"]))
+    torch.cuda.synchronize()
+    blocks = np.unique(np.concatenate([[0, 1, 63, 64, cfg.n_cmp - 1],
+                                       np.random.default_rng(5).integers(0, cfg.n_cmp, 40)]))
+    gk, gv = bf16_dev_to_f64(kc), bf16_dev_to_f64(vc)
+    for g in range(cfg.num_kv_heads):
+        rk = oracle.compress_linear(f64(inp["k"][0, g]), f64(inp["pe_k"]), f64(inp["w_k"]), 32, 16, blocks)
+        rv = oracle.compress_linear(f64(inp["v"][0, g]), f64(inp["pe_v"]), f64(inp["w_v"]), 32, 16, blocks)
+        check_ulp(gk[0, g, blocks], rk, f"64k K_cmp g{g}")
+        check_ulp(gv[0, g, blocks], rv, f"64k V_cmp g{g}")
+
+
+def test_compress_mean_moba_full():
+    cfg = MOBA
+    announce("compress mean moba 128k")
+    rng = np.random.Generator(np.random.PCG64(cfg.seed))
+    k = inputs._normal_bf16(rng, (1, cfg.num_kv_heads, cfg.seq_len, cfg.d_k))
+    kc, _ = ops.compress(cfg, dev_bf16(k))
+    torch.cuda.synchronize()
+    g = bf16_dev_to_f64(kc)
+    for h in range(cfg.num_kv_heads):
+        ref = oracle.compress_mean(f64(k[0, h]), cfg.cmp_block, cfg.cmp_stride)
+        check_ulp(g[0, h], ref, f"moba mean key h{h}")
+
+
+# ---------------------------------------------------------------------------
+# compressed attention + selection
+# ---------------------------------------------------------------------------
+def _score_select_case(cfg, rows, use_oracle_cmp):
+    inp = inputs.prefill_inputs(cfg)
+    if use_oracle_cmp:
+        Kc, Vc = pipeline.compress_all(cfg, f64(inp["k"][0]), f64(inp["v"][0]), f64(inp["w_k"]), f64(inp["w_v"]),
+                                       f64(inp["pe_k"]), f64(inp["pe_v"]))
+        kc_dev, vc_dev = f64_to_dev_bf16(Kc[None]), f64_to_dev_bf16(Vc[None])
+    else:
+        ckv = inputs.compressed_kv(cfg, seed=100 + cfg.seed)
+        Kc, Vc = f64(ckv["k_cmp"][0]), f64(ckv["v_cmp"][0])
+        kc_dev, vc_dev = dev_bf16(ckv["k_cmp"]), dev_bf16(ckv["v_cmp"])
+    sel, lse, ocmp = ops.score_select(cfg, dev_bf16(inp["q"]), kc_dev, vc_dev, want_lse=True)
+    torch.cuda.synchronize()
+    gsel = sel.cpu().numpy()[0, rows]
+    glse = lse.cpu().numpy()[0, rows]
+    goc = ocmp.cpu().numpy()[0, rows]
+    ref = oracle.score_select(cfg, f64(inp["q"][0, rows]), rows, Kc, Vc)
+    check_selection(gsel, ref["sel"], ref["gap"], ref["scores"], rows, cfg, f"{cfg.name} selection")
+    fin = np.isfinite(ref["lse"])
+    assert (np.isneginf(glse[~fin])).all()
+    assert np.abs(glse[fin] - ref["lse"][fin]).max() < 1e-4, np.abs(glse[fin] - ref["lse"][fin]).max()
+    check_close(goc, ref["o_cmp"], f"{cfg.name} o_cmp")
+
+
+@pytest.mark.parametrize("cfg", [TINY, RAGGED], ids=lambda c: c.name)
+def test_score_select_all_rows_oracle_compressed(cfg):
+    announce(f"score_select {cfg.name} all rows")
+    _score_select_case(cfg, np.arange(cfg.seq_len, dtype=np.int32), use_oracle_cmp=True)
+
+
+@pytest.mark.parametrize("cfg", [P8K, RAGGED16], ids=lambda c: c.name)
+def test_score_select_mid(cfg):
+    announce(f"score_select {cfg.name}")
+    rows = np.unique(np.concatenate([np.arange(0, cfg.seq_len, 7), sample_rows(cfg.seq_len, 64, 1)])).astype(np.int32)
+    _score_select_case(cfg, rows, use_oracle_cmp=False)
+
+
+def test_score_select_64k_sampled():
+    announce("score_select 64k sampled")
+    _score_select_case(P64K, sample_rows(P64K.seq_len, 48, 2), use_oracle_cmp=False)
+
+
+def test_select_from_scores_exact_ties():
+    cfg = P8K.replace(seq_len=2048, num_kv_heads=2)
+    announce("select_from_scores ties")
+    rng = np.random.default_rng(9)
+    sc = rng.integers(0, 4, size=(1, cfg.seq_len, 2, cfg.n_slc)).astype(np.float32)
+    sel = ops.select_from_scores(cfg, dev_f32(sc))
+    torch.cuda.synchronize()
+    g = sel.cpu().numpy()[0]
+    jc = np.repeat(np.arange(cfg.seq_len) // cfg.slc_block, 2)
+    ref, _ = oracle.select_from_scores(sc[0].reshape(-1, cfg.n_slc), jc, cfg.top_n, cfg.n_init, cfg.n_local)
+    np.testing.assert_array_equal(g.reshape(-1, cfg.top_n), ref)
+
+
+# ---------------------------------------------------------------------------
+# selected + window attention, gate
+# ---------------------------------------------------------------------------
+def _attn_case(cfg, rows, branches=None):
+    cfg = cfg if branches is None else cfg.replace(branches=branches)
+    inp = inputs.prefill_inputs(cfg)
+    sel = inputs.block_lists(cfg, seed=200 + cfg.seed)
+    oc = inputs.cmp_outputs(cfg, seed=300 + cfg.seed) if cfg.branches & 1 else None
+    out = ops.sparse_attn_fwd(cfg, dev_bf16(inp["q"]), dev_bf16(inp["k"]), dev_bf16(inp["v"]), dev_i32(sel),
+                              None if oc is None else dev_f32(oc), dev_f32(inp["gates"]))
+    torch.cuda.synchronize()
+    gout = bf16_dev_to_f64(out)[0, rows]
+    ref = oracle.attend(cfg, f64(inp["q"][0, rows]), rows, f64(inp["k"][0]), f64(inp["v"][0]), sel[0, rows],
+                        None if oc is None else oc[0, rows], inp["gates"][0, rows])
+    check_close(gout, ref["out"], f"{cfg.name} output (branches {cfg.branches})")
+
+
+@pytest.mark.parametrize("cfg", [TINY, RAGGED], ids=lambda c: c.name)
+def test_sparse_attn_all_rows(cfg):
+    announce(f"sparse_attn {cfg.name} all rows")
+    _attn_case(cfg, np.arange(cfg.seq_len, dtype=np.int32))
+
+
+@pytest.mark.parametrize("cfg", [P8K, RAGGED16], ids=lambda c: c.name)
+def test_sparse_attn_mid(cfg):
+    announce(f"sparse_attn {cfg.name}")
+    _attn_case(cfg, sample_rows(cfg.seq_len, 200, 3))
+
+
+def test_sparse_attn_64k_sampled():
+    announce("sparse_attn 64k sampled")
+    _attn_case(P64K, sample_rows(P64K.seq_len, 40, 4))
+
+
+@pytest.mark.parametrize("branches", [BR_SLC, BR_WIN], ids=["slc", "win"])
+def test_sparse_attn_single_branch(branches):
+    announce(f"sparse_attn single branch {branches}")
+    _attn_case(TINY, np.arange(TINY.seq_len, dtype=np.int32), branches=branches)
+
+
+# ---------------------------------------------------------------------------
+# end to end (the GPU chain against the oracle chain)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("cfg", [TINY, P8K], ids=lambda c: c.name)
+def test_prefill_end_to_end(cfg):
+    announce(f"end to end {cfg.name}")
+    inp = inputs.prefill_inputs(cfg)
+    r = ops.prefill(cfg, dev_bf16(inp["q"]), dev_bf16(inp["k"]), dev_bf16(inp["v"]), dev_bf16(inp["w_k"]),
+                    dev_bf16(inp["w_v"]), dev_bf16(inp["pe_k"]), dev_bf16(inp["pe_v"]), dev_f32(inp["gates"]))
+    torch.cuda.synchronize()
+    rows = np.arange(cfg.seq_len, dtype=np.int32) if cfg.seq_len <= 1024 else sample_rows(cfg.seq_len, 300, 6)
+    Kc, Vc = pipeline.compress_all(cfg, f64(inp["k"][0]), f64(inp["v"][0]), f64(inp["w_k"]), f64(inp["w_v"]),
+                                   f64(inp["pe_k"]), f64(inp["pe_v"]))
+    ref = pipeline.forward_rows(cfg, f64(inp["q"][0]), f64(inp["k"][0]), f64(inp["v"][0]), Kc, Vc, inp["gates"][0],
+                                rows)
+    gsel = r["sel"].cpu().numpy()[0, rows]
+    gout = bf16_dev_to_f64(r["out"])[0, rows]
+    agree = (gsel == ref["sel"]).all(axis=-1).all(axis=-1)
+    print(f"[parity] {cfg.name} end-to-end selection agreement {agree.mean():.5f} over {len(rows)} rows", flush=True)
+    # the GPU's compressed keys may differ from the oracle's by one bf16 rounding in a few
+    # elements; rows whose selection then differs must be near ties
+    assert agree.mean() >= 0.99
+    for r_ in np.where(~agree)[0]:
+        assert ref["gap"][r_].min() < 1e-3, (rows[r_], ref["gap"][r_])
+    check_close(gout[agree], ref["out"][agree], f"{cfg.name} end-to-end output")
+
+
+# ---------------------------------------------------------------------------
+# decode
+# ---------------------------------------------------------------------------
+def _decode_case(cfg, cache_len, cmp_from_oracle):
+    inp = inputs.decode_inputs(cfg, cache_len=cache_len)
+    if cmp_from_oracle:
+        per_b = [pipeline.compress_all(cfg, f64(inp["k"][b]), f64(inp["v"][b]), f64(inp["w_k"]), f64(inp["w_v"]),
+                                       f64(inp["pe_k"]), f64(inp["pe_v"])) for b in range(cfg.batch)]
+        kc_f64 = np.stack([x[0] for x in per_b])
+        vc_f64 = np.stack([x[1] for x in per_b])
+        kc_dev, vc_dev = f64_to_dev_bf16(kc_f64), f64_to_dev_bf16(vc_f64)
+    else:
+        ckv = inputs.compressed_kv(cfg, seed=400 + cfg.seed)
+        kc_f64, vc_f64 = f64(ckv["k_cmp"]), f64(ckv["v_cmp"])
+        kc_dev, vc_dev = dev_bf16(ckv["k_cmp"]), dev_bf16(ckv["v_cmp"])
+    out, sel = ops.decode(cfg, dev_bf16(inp["q"]), dev_bf16(inp["k"]), dev_bf16(inp["v"]), dev_i32(inp["cache_len"]),
+                          kc_dev, vc_dev, dev_f32(inp["gates"]))
+    torch.cuda.synchronize()
+    gout = bf16_dev_to_f64(out)
+    gsel = sel.cpu().numpy()
+    refs_out, refs_sel, gaps, scores, pos = [], [], [], [], []
+    for b in range(cfg.batch):
+        t = int(inp["cache_len"][b]) - 1
+        q = f64(inp["q"][b])[None]
+        ss = oracle.score_select(cfg, q, [t], kc_f64[b], vc_f64[b])
+        at = oracle.attend(cfg, q, [t], f64(inp["k"][b]), f64(inp["v"][b]), ss["sel"], ss["o_cmp"],
+                           inp["gates"][b][None])
+        refs_out.append(at["out"][0]); refs_sel.append(ss["sel"][0]); gaps.append(ss["gap"][0])
+        scores.append(ss["scores"][0]); pos.append(t)
+    check_selection(gsel, np.stack(refs_sel), np.stack(gaps), np.stack(scores), np.array(pos), cfg,
+                    f"{cfg.name} decode selection")
+    check_close(gout, np.stack(refs_out), f"{cfg.name} decode output")
+
+
+def test_decode_varlen_small():
+    cfg = DECODE.replace(name="decode_small", batch=6, seq_len=4096, seed=21)
+    announce("decode varlen small")
+    _decode_case(cfg, np.array([4096, 1, 31, 32, 100, 2049], dtype=np.int32), cmp_from_oracle=True)
+
+
+def test_decode_full():
+    announce("decode full 32 x 65536")
+    _decode_case(DECODE, None, cmp_from_oracle=False)
+
+
+def test_decode_equals_prefill_last_row():
+    cfg = P8K.replace(name="dp", batch=2, seq_len=2048, seed=23)
+    announce("decode == prefill last row")
+    inp = inputs.prefill_inputs(cfg)
+    q, k, v = dev_bf16(inp["q"]), dev_bf16(inp["k"]), dev_bf16(inp["v"])
+    wk, wv, pk, pv = (dev_bf16(inp[n]) for n in ("w_k", "w_v", "pe_k", "pe_v"))
+    gates = dev_f32(inp["gates"])
+    r = ops.prefill(cfg, q, k, v, wk, wv, pk, pv, gates)
+    dcfg = cfg.replace(decode=True)
+    L = cfg.seq_len
+    out, sel = ops.decode(dcfg, q[:, L - 1].contiguous(), k, v, dev_i32(np.full(cfg.batch, L)), r["k_cmp"],
+                          r["v_cmp"], gates[:, L - 1].contiguous())
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(sel.cpu().numpy(), r["sel"].cpu().numpy()[:, L - 1])
+    check_close(bf16_dev_to_f64(out), bf16_dev_to_f64(r["out"])[:, L - 1], "decode vs prefill row", atol=1e-2,
+                rel=2e-3)
+
+
+# ---------------------------------------------------------------------------
+# MoBA mode
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("T", [8192, MOBA.seq_len])
+def test_moba(T):
+    cfg = MOBA.replace(seq_len=T)
+    announce(f"moba {T}")
+    inp = inputs.prefill_inputs(cfg)
+    Kbar = pipeline.compress_all(cfg, f64(inp["k"][0]), None, None, None, None, None)[0]
+    rows = sample_rows(T, 40, 7, lp=512, l=512)
+    sel, _, _ = ops.score_select(cfg, dev_bf16(inp["q"]), f64_to_dev_bf16(Kbar[None]))
+    torch.cuda.synchronize()
+    ref = oracle.score_select(cfg, f64(inp["q"][0, rows]), rows, Kbar)
+    check_selection(sel.cpu().numpy()[0, rows], ref["sel"], ref["gap"], ref["scores"], rows, cfg, f"moba{T} selection")
+    lists = inputs.block_lists(cfg, seed=500, positions=None) if T <= 8192 else None
+    if lists is None:
+        lists = inputs.block_lists(cfg.replace(seq_len=T), seed=500)
+    out = ops.sparse_attn_fwd(cfg, dev_bf16(inp["q"]), dev_bf16(inp["k"]), dev_bf16(inp["v"]), dev_i32(lists))
+    torch.cuda.synchronize()
+    at = oracle.attend(cfg, f64(inp["q"][0, rows]), rows, f64(inp["k"][0]), f64(inp["v"][0]), lists[0, rows])
+    check_close(bf16_dev_to_f64(out)[0, rows], at["out"], f"moba{T} output")
+
+
+# ---------------------------------------------------------------------------
+# the pages' special cases, run on the GPU
+# ---------------------------------------------------------------------------
+def test_gpu_select_all_is_full_causal_and_window_only_is_swa():
+    cfg = TINY.replace(top_n=16, branches=BR_SLC)
+    announce("gpu special cases")
+    inp = inputs.prefill_inputs(cfg)
+    T = cfg.seq_len
+    allsel = np.full((1, T, 1, 16), -1, dtype=np.int32)
+    for t in range(T):
+        allsel[0, t, 0, :t // 64 + 1] = np.arange(t // 64 + 1)
+    q, k, v = dev_bf16(inp["q"]), dev_bf16(inp["k"]), dev_bf16(inp["v"])
+    o1 = bf16_dev_to_f64(ops.sparse_attn_fwd(cfg, q, k, v, dev_i32(allsel)))[0]
+    cw = cfg.replace(branches=BR_WIN)
+    o2 = bf16_dev_to_f64(ops.sparse_attn_fwd(cw, q, k, v))[0]
+    Q, K, V = f64(inp["q"][0]), f64(inp["k"][0, 0]), f64(inp["v"][0, 0])
+    for h in range(cfg.num_heads):
+        check_close(o1[:, h], oracle.causal_attention(Q[:, h], K, V, cfg.scale), f"select-all head {h}")
+        check_close(o2[:, h], oracle.causal_attention(Q[:, h], K, V, cfg.scale, window=cfg.window), f"window head {h}")
+
+
+def test_gpu_causality_and_determinism():
+    cfg = P8K.replace(seq_len=2048, seed=31)
+    announce("gpu causality + determinism")
+    inp = inputs.prefill_inputs(cfg)
+    args = [dev_bf16(inp[n]) for n in ("q", "k", "v", "w_k", "w_v", "pe_k", "pe_v")] + [dev_f32(inp["gates"])]
+    a = ops.prefill(cfg, *args)
+    b = ops.prefill(cfg, *args)
+    torch.cuda.synchronize()
+    for key in ("out", "sel", "o_cmp", "k_cmp", "v_cmp"):
+        assert torch.equal(a[key], b[key]), key
+    t0 = 1500
+    pert = [x.clone() for x in args]
+    g = torch.Generator(device="cpu").manual_seed(1)
+    pert[0][:, t0 + 1:] = torch.randn(pert[0][:, t0 + 1:].shape, generator=g).to(pert[0])
+    pert[1][:, :, t0 + 1:] = (5 * torch.randn(pert[1][:, :, t0 + 1:].shape, generator=g)).to(pert[1])
+    pert[2][:, :, t0 + 1:] = (5 * torch.randn(pert[2][:, :, t0 + 1:].shape, generator=g)).to(pert[2])
+    c = ops.prefill(cfg, *pert)
+    torch.cuda.synchronize()
+    assert torch.equal(a["out"][:, :t0 + 1], c["out"][:, :t0 + 1])
+    assert torch.equal(a["sel"][:, :t0 + 1], c["sel"][:, :t0 + 1])
