@@ -86,16 +86,20 @@ CompressWs compress_ws(const Shape& s) {
     return w;
 }
 
-struct SelectWs { size_t m, il, vct, total; int npad; };
+struct SelectWs { size_t m, il, vct, scores, total; int npad; };
 SelectWs select_ws(const Shape& s) {
     SelectWs w{};
-    if (s.mode != NSA_SCORE_CMP_OVERLAP) return w;
-    w.npad = round_up(std::max(s.n_cmp, 1), 64);
     size_t off = 0;
     const size_t rows = (size_t)s.B * s.T * s.H;
-    w.m = off; off = align_up(off + rows * 4, 256);
-    w.il = off; off = align_up(off + rows * 4, 256);
-    w.vct = off; off = align_up(off + (size_t)s.B * s.Hkv * s.dv * w.npad * 2, 256);
+    // +64 keys: keeps the transposed row stride off a power of two (rows of one tile
+    // would otherwise fall on the same memory channel)
+    w.npad = round_up(std::max(s.n_cmp, 1), 64) + 64;
+    if (s.mode == NSA_SCORE_CMP_OVERLAP) {
+        w.m = off; off = align_up(off + rows * 4, 256);
+        w.il = off; off = align_up(off + rows * 4, 256);
+        w.vct = off; off = align_up(off + (size_t)s.B * s.Hkv * s.dv * w.npad * 2, 256);
+    }
+    w.scores = off; off = align_up(off + (size_t)s.B * s.T * s.Hkv * s.n_slc * 4, 256);
     w.total = off;
     return w;
 }
@@ -103,7 +107,7 @@ SelectWs select_ws(const Shape& s) {
 struct AttnWs { size_t vt, total; int tpad; };
 AttnWs attn_ws(const Shape& s) {
     AttnWs w{};
-    w.tpad = round_up(s.T, 64);
+    w.tpad = round_up(s.T, 64) + 64;  // see select_ws
     w.vt = 0;
     w.total = align_up((size_t)s.B * s.Hkv * s.dv * w.tpad * 2, 256);
     return w;
@@ -221,7 +225,12 @@ nsa_status nsa_score_select(const nsa_config* cfg, const void* Q, const void* K_
     if (with_o && !V_cmp) return fail(NSA_ERR_NULL, "o_cmp needs V_cmp");
     const int nq = nsa::score_select_nq(s.G, s.mode);
     const size_t lds = nsa::score_select_lds_bytes(s.dk, s.dv, s.G, s.mode, nq, with_o, s.n_slc);
-    if (lds > 160 * 1024) return fail(NSA_ERR_UNSUPPORTED, "too many selection blocks for one workgroup's LDS");
+    if (lds > 160 * 1024) return fail(NSA_ERR_UNSUPPORTED, "tile too large for one workgroup's LDS");
+    if (s.mode == NSA_SCORE_CMP_OVERLAP) {
+        const int R = s.lp / s.s, L = s.l / s.s;
+        if (64 % R != 0 || L > 64)
+            return fail(NSA_ERR_UNSUPPORTED, "slc_block / cmp_stride must divide 64 and cmp_block / cmp_stride <= 64");
+    }
     const SelectWs w = select_ws(s);
     if ((st = check_ws(ws, ws_bytes, w.total)) != NSA_OK) return st;
     const hipStream_t hs = as_stream(stream);
@@ -229,7 +238,7 @@ nsa_status nsa_score_select(const nsa_config* cfg, const void* Q, const void* K_
     nsa::SelParams p{};
     p.Q = static_cast<const u16*>(Q);
     p.Kc = static_cast<const u16*>(K_cmp);
-    p.sel = sel_idx;
+    p.scores = at<float>(ws, w.scores);
     p.T = s.T; p.Hkv = s.Hkv; p.N = s.n_cmp; p.l = s.l; p.s = s.s; p.lp = s.lp;
     p.n_slc = s.n_slc; p.top_n = s.n; p.n_init = s.n_init; p.n_local = s.n_local;
     p.scale_log2 = s.scale * nsa::kLog2eHost;
@@ -249,8 +258,9 @@ nsa_status nsa_score_select(const nsa_config* cfg, const void* Q, const void* K_
             p.o_cmp = o_cmp;
         }
     }
-    if (!nsa::launch_score_select(s.mode, with_o, s.dk, s.dv, s.G, p, s.B, hs))
-        return fail(NSA_ERR_UNSUPPORTED, "no selection kernel for this shape");
+    if (!nsa::launch_cmp_scores(s.mode, with_o, s.dk, s.dv, s.G, p, s.B, hs))
+        return fail(NSA_ERR_UNSUPPORTED, "no score kernel for this shape");
+    nsa::launch_select_from_scores(p.scores, sel_idx, s.B, s.T, s.Hkv, s.n_slc, s.lp, s.n, s.n_init, s.n_local, hs);
     return hip_check("score_select");
 }
 

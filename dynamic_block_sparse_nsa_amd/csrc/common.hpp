@@ -81,15 +81,39 @@ __device__ __forceinline__ float col_sum(float v) {
     return v + __shfl_xor(v, 32);
 }
 
-// Sum over aligned groups of G lanes within each 16-lane row (the G heads of a token).
-template <int G>
-__device__ __forceinline__ float head_sum(float v) {
-    if constexpr (G >= 16) v += __shfl_xor(v, 8);
-    if constexpr (G >= 8) v += __shfl_xor(v, 4);
-    if constexpr (G >= 4) v += __shfl_xor(v, 2);
-    if constexpr (G >= 2) v += __shfl_xor(v, 1);
+// DPP lane moves within a 16-lane row (VALU, no LDS traffic).
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+constexpr int kDppQuadXor1 = 0xB1;       // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;       // quad_perm [2,3,0,1]
+constexpr int kDppRowHalfMirror = 0x141; // lane i <- lane 7-i within each 8 lanes
+constexpr int kDppRowMirror = 0x140;     // lane i <- lane 15-i within each 16 lanes
+
+// Sum over aligned groups of N lanes (N = 1, 2, 4, 8 or 16) inside a 16-lane row; every
+// lane of a group ends with the group total.
+template <int N>
+__device__ __forceinline__ float lane_group_sum(float v) {
+    if constexpr (N >= 2) v += dpp_mov<kDppQuadXor1>(v);
+    if constexpr (N >= 4) v += dpp_mov<kDppQuadXor2>(v);
+    if constexpr (N >= 8) v += dpp_mov<kDppRowHalfMirror>(v);
+    if constexpr (N >= 16) v += dpp_mov<kDppRowMirror>(v);
     return v;
 }
+
+// Query-row layout of a wave holding NQ MFMA column tiles (16 columns each) of the
+// query rows of one KV group: tile c, column li holds (token, head).  The G heads of a
+// token sit in CL = min(G, NQ) tiles of the same lane and GL = G / CL neighbouring lanes,
+// so a sum over the group's heads is CL-1 in-lane adds plus log2(GL) DPP adds.
+template <int G, int NQ>
+struct QMap {
+    static constexpr int CL = G < NQ ? G : NQ;
+    static constexpr int GL = G / CL;
+    static constexpr int TPW = 16 * NQ / G;  // tokens per wave
+    __device__ static int token(int c, int li) { return (li / GL) * (NQ / CL) + c / CL; }
+    __device__ static int head(int c, int li) { return CL * (li % GL) + c % CL; }
+};
 
 __device__ __forceinline__ float sigmoidf_(float z) { return 1.0f / (1.0f + __expf(-z)); }
 

@@ -29,13 +29,13 @@ struct SelParams {
     const float* stat_m;   // [B,T,H] running max (base 2) from the statistics pass
     const float* stat_il;  // [B,T,H] 1 / sum
     float* o_cmp;          // [B,T,H,DV] or null
-    int32_t* sel;          // [B,T,Hkv,top_n]
+    float* scores;         // [B,T,Hkv,n_slc] block scores (workspace)
     int T, Hkv, N, Npad, l, s, lp, n_slc, top_n, n_init, n_local;
     float scale_log2;
 };
 bool launch_cmp_stats(const u16* Q, const u16* Kc, float* m, float* il, float* lse, int B, int T, int Hkv, int G,
                       int DK, int N, int l, int s, float sl2, hipStream_t st);
-bool launch_score_select(int mode, bool with_o, int DK, int DV, int G, const SelParams& p, int B, hipStream_t st);
+bool launch_cmp_scores(int mode, bool with_o, int DK, int DV, int G, const SelParams& p, int B, hipStream_t st);
 size_t score_select_lds_bytes(int DK, int DV, int G, int mode, int NQ, bool with_o, int n_slc);
 int score_select_nq(int G, int mode);
 void launch_select_from_scores(const float* scores, int32_t* sel, int B, int T, int Hkv, int n_slc, int lp,

@@ -7,16 +7,21 @@
 // forced blocks plus the best-scoring others.  MoBA mode scores a block by the inner
 // product of the query with the block's mean key instead.
 //
-// Kernel structure (per KV group; a workgroup owns 128 query rows = 128/G tokens, each
-// wave 32 rows = two 16-row MFMA column tiles):
-//   cmp_stats_kernel     pass 1: S^T = K_cmp . Q^T tile by tile (64 keys staged in LDS);
-//                        running max m and sum l per query row (base-2 exponentials).
-//   score_select_kernel  pass 2: recompute S^T; p = 2^(x - m) / l (exact normalized
-//                        probabilities, so no rescaling); o_cmp += V_cmp^T . P^T on the
-//                        MFMA; head sums in fp32 via lane shuffles, accumulated per
-//                        (token, block) in LDS in a fixed order; then one wave per token
-//                        selects the blocks (tournament argmax over 64 lanes, 64-bit keys
-//                        = score bits : ~index, so ties go to the lower index).
+// Kernels (per KV group; a workgroup owns 128 query rows = 128/G tokens, each wave two
+// 16-column MFMA tiles laid out by QMap so a token's heads share lanes and tiles):
+//   cmp_stats_kernel   pass 1: S^T = K_cmp . Q^T, 64 compressed keys per LDS tile; running
+//                      max m and sum l per query row (base-2 exponentials).
+//   cmp_scores_kernel  pass 2: recompute S^T; p = 2^(x - m) / l (the exact normalized
+//                      probabilities, so nothing is rescaled); o_cmp += V_cmp^T . P^T on
+//                      the MFMA (P split into bf16 high and low parts); sums over the
+//                      group's heads in fp32 (in-lane + DPP) into a per-key ring in LDS;
+//                      each block's score (sum over its overlapping compressed blocks,
+//                      ascending key order) is written to the score workspace once the
+//                      tile holding its last key is done.  Mode 1 writes the head-summed
+//                      raw dot products with the mean keys directly.
+//   select_kernel      one wave per (token, group): the shared top-n from the scores.
+// Block j of l' tokens takes compressed blocks i with j*R - L + 1 <= i <= j*R + R - 1,
+// R = l'/s and L = l/s, i.e. every compressed block whose token span meets block j.
 #include "common.hpp"
 #include "launch.hpp"
 #include "select.hpp"
@@ -27,6 +32,53 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kKeysPerTile = 64;
+constexpr int kRing = 2 * kKeysPerTile;  // per-token head-sum ring: this tile and the previous one
+
+// Copy rows [k0, k0+64) of a [N][D] bf16 matrix (rows clamped to N-1) into LDS rows of
+// stride LSTR.  All global loads are issued before the first LDS store.
+template <int D, int LSTR>
+__device__ __forceinline__ void stage_rows(const u16* __restrict__ src, int k0, int N, u16* dst) {
+    constexpr int PER_ROW = D / 8;
+    constexpr int TOTAL = kKeysPerTile * PER_ROW;
+    constexpr int ITERS = (TOTAL + 255) / 256;
+    uint4 v[ITERS];
+#pragma unroll
+    for (int i = 0; i < ITERS; ++i) {
+        const int idx = threadIdx.x + 256 * i;
+        const int row = idx / PER_ROW, col = (idx % PER_ROW) * 8;
+        if (TOTAL % 256 == 0 || idx < TOTAL)
+            v[i] = *reinterpret_cast<const uint4*>(src + (size_t)min(k0 + row, N - 1) * D + col);
+    }
+#pragma unroll
+    for (int i = 0; i < ITERS; ++i) {
+        const int idx = threadIdx.x + 256 * i;
+        const int row = idx / PER_ROW, col = (idx % PER_ROW) * 8;
+        if (TOTAL % 256 == 0 || idx < TOTAL) *reinterpret_cast<uint4*>(&dst[row * LSTR + col]) = v[i];
+    }
+}
+
+// Copy columns [k0, k0+64) of a [D][Npad] bf16 matrix (transposed values) into LDS rows
+// of stride LSTR.  All global loads are issued before the first LDS store.
+template <int D, int LSTR>
+__device__ __forceinline__ void stage_cols(const u16* __restrict__ src, int k0, int Npad, u16* dst) {
+    constexpr int PER_ROW = kKeysPerTile / 8;
+    constexpr int TOTAL = D * PER_ROW;
+    constexpr int ITERS = (TOTAL + 255) / 256;
+    uint4 v[ITERS];
+#pragma unroll
+    for (int i = 0; i < ITERS; ++i) {
+        const int idx = threadIdx.x + 256 * i;
+        const int row = idx / PER_ROW, col = (idx % PER_ROW) * 8;
+        if (TOTAL % 256 == 0 || idx < TOTAL)
+            v[i] = *reinterpret_cast<const uint4*>(src + (size_t)row * Npad + k0 + col);
+    }
+#pragma unroll
+    for (int i = 0; i < ITERS; ++i) {
+        const int idx = threadIdx.x + 256 * i;
+        const int row = idx / PER_ROW, col = (idx % PER_ROW) * 8;
+        if (TOTAL % 256 == 0 || idx < TOTAL) *reinterpret_cast<uint4*>(&dst[row * LSTR + col]) = v[i];
+    }
+}
 
 }  // namespace
 
@@ -50,13 +102,13 @@ __global__ __launch_bounds__(256) void cmp_stats_kernel(const u16* __restrict__ 
     const int H = Hkv * G;
     const int tok0 = (gridDim.x - 1 - blockIdx.x) * TQ;
 
+    using M = QMap<G, NQ>;
     bf16x8 qf[NQ][NDS];
     int tok[NQ], hl[NQ], nv[NQ];
 #pragma unroll
     for (int c = 0; c < NQ; ++c) {
-        const int r = (wave * NQ + c) * 16 + li;
-        tok[c] = tok0 + r / G;
-        hl[c] = r % G;
+        tok[c] = tok0 + wave * M::TPW + M::token(c, li);
+        hl[c] = M::head(c, li);
         const int tt = min(tok[c], T - 1);
         nv[c] = tok[c] < T ? visible_count(tok[c], l, s, N) : 0;
         const u16* qp = Q + (((size_t)b * T + tt) * H + g * G + hl[c]) * DK + lq * 8;
@@ -64,6 +116,7 @@ __global__ __launch_bounds__(256) void cmp_stats_kernel(const u16* __restrict__ 
         for (int ds = 0; ds < NDS; ++ds) qf[c][ds] = ld8(qp + 32 * ds);
     }
     const int nv_max = visible_count(min(tok0 + TQ - 1, T - 1), l, s, N);
+    const int nv_min = visible_count(min(tok0, T - 1), l, s, N);
     const u16* kbase = Kc + ((size_t)b * Hkv + g) * (size_t)N * DK;
 
     float m[NQ], lsum[NQ];
@@ -72,12 +125,7 @@ __global__ __launch_bounds__(256) void cmp_stats_kernel(const u16* __restrict__ 
 
     for (int k0 = 0; k0 < nv_max; k0 += kKeysPerTile) {
         __syncthreads();
-        for (int idx = threadIdx.x; idx < kKeysPerTile * (DK / 8); idx += 256) {
-            const int row = idx / (DK / 8), col = (idx % (DK / 8)) * 8;
-            const int kr = min(k0 + row, N - 1);
-            *reinterpret_cast<uint4*>(&ks[row * KSTR + col]) =
-                *reinterpret_cast<const uint4*>(kbase + (size_t)kr * DK + col);
-        }
+        stage_rows<DK, KSTR>(kbase, k0, N, ks);
         __syncthreads();
         f32x4 sacc[4][NQ];
 #pragma unroll
@@ -93,19 +141,25 @@ __global__ __launch_bounds__(256) void cmp_stats_kernel(const u16* __restrict__ 
                 for (int c = 0; c < NQ; ++c) sacc[kt][c] = mfma16(a, qf[c][ds], sacc[kt][c]);
             }
         }
+        const bool full = k0 + kKeysPerTile <= nv_min;  // no key of this tile is masked
 #pragma unroll
         for (int c = 0; c < NQ; ++c) {
             float x[16];
             float tmax = -INFINITY;
+            if (full) {
 #pragma unroll
-            for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int key = k0 + 16 * kt + 4 * lq + r;
-                    const float v = key < nv[c] ? sacc[kt][c][r] * scale_log2 : -INFINITY;
-                    x[kt * 4 + r] = v;
-                    tmax = fmaxf(tmax, v);
+                for (int e = 0; e < 16; ++e) {
+                    x[e] = sacc[e >> 2][c][e & 3] * scale_log2;
+                    tmax = fmaxf(tmax, x[e]);
                 }
+            } else {
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int key = k0 + 16 * (e >> 2) + 4 * lq + (e & 3);
+                    x[e] = key < nv[c] ? sacc[e >> 2][c][e & 3] * scale_log2 : -INFINITY;
+                    tmax = fmaxf(tmax, x[e]);
+                }
+            }
             tmax = col_max(tmax);
             const float mnew = fmaxf(m[c], tmax);
             if (mnew != -INFINITY) {
@@ -130,22 +184,20 @@ __global__ __launch_bounds__(256) void cmp_stats_kernel(const u16* __restrict__ 
 }
 
 // ---------------------------------------------------------------------------
-// pass 2 (MODE 0: compressed-overlap scores, optional o_cmp) and MoBA mean-key scores
-// (MODE 1), followed by the selection.
+// pass 2: block scores (+ o_cmp) into the score workspace
 // ---------------------------------------------------------------------------
-
 template <int DK, int DV, int G, int MODE, int NQ, bool WITH_O>
-__global__ __launch_bounds__(256) void score_select_kernel(SelParams p) {
+__global__ __launch_bounds__(256, 2) void cmp_scores_kernel(SelParams p) {
     constexpr int TQ = kWaves * NQ * 16 / G;
     constexpr int KSTR = DK + 8;
     constexpr int VSTR = kKeysPerTile + 8;
     constexpr int NDS = DK / 32;
     constexpr int NDT = DV / 16;
+    constexpr int TPT = 256 / TQ;  // threads per token when emitting block scores
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     u16* ks = reinterpret_cast<u16*>(smem);
-    u16* vs = ks + kKeysPerTile * KSTR;                                       // WITH_O only
-    float* psum = reinterpret_cast<float*>(vs + (WITH_O ? DV * VSTR : 0));    // [TQ][64]
-    float* sc = psum + TQ * kKeysPerTile;                                     // [TQ][n_slc]
+    u16* vs = ks + kKeysPerTile * KSTR;                                     // WITH_O only
+    float* ring = reinterpret_cast<float*>(vs + (WITH_O ? DV * VSTR : 0));  // [TQ][kRing] (mode 0)
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int li = lane & 15, lq = lane >> 4;
@@ -153,15 +205,16 @@ __global__ __launch_bounds__(256) void score_select_kernel(SelParams p) {
     const int T = p.T, N = p.N;
     const int H = p.Hkv * G;
     const int tok0 = (gridDim.x - 1 - blockIdx.x) * TQ;
+    const int R = p.lp / p.s, L = p.l / p.s;
 
+    using M = QMap<G, NQ>;
     bf16x8 qf[NQ][NDS];
     int tok[NQ], hl[NQ], nv[NQ];
     float rm[NQ], ril[NQ];
 #pragma unroll
     for (int c = 0; c < NQ; ++c) {
-        const int r = (wave * NQ + c) * 16 + li;
-        tok[c] = tok0 + r / G;
-        hl[c] = r % G;
+        tok[c] = tok0 + wave * M::TPW + M::token(c, li);
+        hl[c] = M::head(c, li);
         const int tt = min(tok[c], T - 1);
         const size_t row = ((size_t)b * T + tt) * H + g * G + hl[c];
         const u16* qp = p.Q + row * DK + lq * 8;
@@ -180,8 +233,29 @@ __global__ __launch_bounds__(256) void score_select_kernel(SelParams p) {
     }
     const int t_last = min(tok0 + TQ - 1, T - 1);
     const int nv_max = MODE == 0 ? visible_count(t_last, p.l, p.s, N) : min(t_last / p.lp, N);
+    const int nv_min = MODE == 0 ? visible_count(min(tok0, T - 1), p.l, p.s, N) : min(min(tok0, T - 1) / p.lp, N);
 
-    for (int idx = threadIdx.x; idx < TQ * p.n_slc; idx += 256) sc[idx] = 0.f;
+    // emitter role: thread -> (token tl_e, first block offset je)
+    const int tl_e = threadIdx.x / TPT, je = threadIdx.x % TPT;
+    const int t_e = tok0 + tl_e;
+    const int jc_e = min(t_e, T - 1) / p.lp;
+    float* score_row = p.scores + (((size_t)b * T + min(t_e, T - 1)) * p.Hkv + g) * p.n_slc;
+    const float* ring_e = ring + tl_e * kRing;
+    // score of block j from the ring (keys at or after `kend` count as 0)
+    auto block_score = [&](int j, int kend) {
+        const int ilo = max(0, j * R - L + 1), ihi = min(j * R + R - 1, kend - 1);
+        float acc = 0.f;
+        if (ihi - ilo < 8) {
+            float v[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) v[q] = (ilo + q <= ihi) ? ring_e[(ilo + q) & (kRing - 1)] : 0.f;
+#pragma unroll
+            for (int q = 0; q < 8; ++q) acc += v[q];
+        } else {
+            for (int i = ilo; i <= ihi; ++i) acc += ring_e[i & (kRing - 1)];
+        }
+        return acc;
+    };
 
     f32x4 oacc[WITH_O ? NDT : 1][NQ];
     if constexpr (WITH_O) {
@@ -193,21 +267,11 @@ __global__ __launch_bounds__(256) void score_select_kernel(SelParams p) {
     const u16* kbase = p.Kc + ((size_t)b * p.Hkv + g) * (size_t)N * DK;
     const u16* vbase = WITH_O ? p.Vct + ((size_t)b * p.Hkv + g) * (size_t)DV * p.Npad : nullptr;
 
-    for (int k0 = 0; k0 < nv_max; k0 += kKeysPerTile) {
+    int k0 = 0;
+    for (; k0 < nv_max; k0 += kKeysPerTile) {
         __syncthreads();
-        for (int idx = threadIdx.x; idx < kKeysPerTile * (DK / 8); idx += 256) {
-            const int row = idx / (DK / 8), col = (idx % (DK / 8)) * 8;
-            const int kr = min(k0 + row, N - 1);
-            *reinterpret_cast<uint4*>(&ks[row * KSTR + col]) =
-                *reinterpret_cast<const uint4*>(kbase + (size_t)kr * DK + col);
-        }
-        if constexpr (WITH_O) {
-            for (int idx = threadIdx.x; idx < DV * (kKeysPerTile / 8); idx += 256) {
-                const int row = idx / (kKeysPerTile / 8), col = (idx % (kKeysPerTile / 8)) * 8;
-                *reinterpret_cast<uint4*>(&vs[row * VSTR + col]) =
-                    *reinterpret_cast<const uint4*>(vbase + (size_t)row * p.Npad + k0 + col);
-            }
-        }
+        if constexpr (WITH_O) stage_cols<DV, VSTR>(vbase, k0, p.Npad, vs);
+        stage_rows<DK, KSTR>(kbase, k0, N, ks);
         __syncthreads();
 
         f32x4 sacc[4][NQ];
@@ -224,21 +288,30 @@ __global__ __launch_bounds__(256) void score_select_kernel(SelParams p) {
                 for (int c = 0; c < NQ; ++c) sacc[kt][c] = mfma16(a, qf[c][ds], sacc[kt][c]);
             }
         }
-        // probabilities (MODE 0) or raw scores (MODE 1), zero outside the visible set
+        // probabilities (mode 0) or raw scores (mode 1), zero outside the visible set
+        if (k0 + kKeysPerTile <= nv_min) {
+            if constexpr (MODE == 0) {
 #pragma unroll
-        for (int c = 0; c < NQ; ++c)
+                for (int c = 0; c < NQ; ++c)
 #pragma unroll
-            for (int kt = 0; kt < 4; ++kt)
+                    for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int key = k0 + 16 * kt + 4 * lq + r;
-                    float v = 0.f;
-                    if (key < nv[c]) {
-                        if constexpr (MODE == 0) v = fast_exp2(sacc[kt][c][r] * p.scale_log2 - rm[c]) * ril[c];
-                        else v = sacc[kt][c][r];
+                        for (int r = 0; r < 4; ++r)
+                            sacc[kt][c][r] = fast_exp2(sacc[kt][c][r] * p.scale_log2 - rm[c]) * ril[c];
+            }
+        } else {
+#pragma unroll
+            for (int c = 0; c < NQ; ++c)
+#pragma unroll
+                for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int key = k0 + 16 * kt + 4 * lq + r;
+                        float v = sacc[kt][c][r];
+                        if constexpr (MODE == 0) v = fast_exp2(v * p.scale_log2 - rm[c]) * ril[c];
+                        sacc[kt][c][r] = key < nv[c] ? v : 0.f;
                     }
-                    sacc[kt][c][r] = v;
-                }
+        }
         if constexpr (WITH_O) {
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
@@ -256,41 +329,44 @@ __global__ __launch_bounds__(256) void score_select_kernel(SelParams p) {
                 }
             }
         }
-        // head sums: every lane of a token's G-lane group ends with the group total
+        // sums over the group's heads: in-lane over the token's tiles, then DPP over its lanes
 #pragma unroll
-        for (int c = 0; c < NQ; ++c) {
-            const int tl = ((wave * NQ + c) * 16 + li) / G;
+        for (int cg = 0; cg < NQ / M::CL; ++cg) {
+            const int tl = wave * M::TPW + M::token(cg * M::CL, li);
 #pragma unroll
             for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const float hs = head_sum<G>(sacc[kt][c][r]);
-                    if constexpr (MODE == 0) {
-                        if ((li % G) == 0) psum[tl * kKeysPerTile + 16 * kt + 4 * lq + r] = hs;
-                    } else {
+                    float hs = 0.f;
+#pragma unroll
+                    for (int c = cg * M::CL; c < (cg + 1) * M::CL; ++c) hs += sacc[kt][c][r];
+                    hs = lane_group_sum<M::GL>(hs);
+                    if ((li % M::GL) == 0) {
                         const int key = k0 + 16 * kt + 4 * lq + r;
-                        if ((li % G) == 0 && key < nv[c]) sc[tl * p.n_slc + key] = hs;
+                        if constexpr (MODE == 0) {
+                            ring[tl * kRing + (key & (kRing - 1))] = hs;
+                        } else {
+                            const int t = tok0 + tl;
+                            if (key < nv[cg * M::CL])
+                                p.scores[(((size_t)b * T + t) * p.Hkv + g) * p.n_slc + key] = hs;
+                        }
                     }
                 }
         }
         if constexpr (MODE == 0) {
             __syncthreads();
-            // blocks touched by keys k0 .. k0+63: block j gets keys i with
-            // i*s <= (j+1)*lp - 1 and i*s + l - 1 >= j*lp, added in ascending i
-            const int jlo = (k0 * p.s) / p.lp;
-            const int jhi = min(((k0 + kKeysPerTile - 1) * p.s + p.l - 1) / p.lp, p.n_slc - 1);
-            const int nj = jhi - jlo + 1;
-            for (int idx = threadIdx.x; idx < TQ * nj; idx += 256) {
-                const int tl = idx / nj, j = jlo + idx % nj;
-                const int ilo = max(k0, (j * p.lp - p.l + 1 + p.s - 1 >= 0) ? (j * p.lp - p.l + 1 + p.s - 1) / p.s : 0);
-                const int ihi = min(k0 + kKeysPerTile - 1, (j * p.lp + p.lp - 1) / p.s);
-                float acc = 0.f;
-                for (int i = ilo; i <= ihi; ++i) acc += psum[tl * kKeysPerTile + (i - k0)];
-                sc[tl * p.n_slc + j] += acc;
-            }
+            // blocks whose last compressed key lies in this tile are complete
+            const int kend = k0 + kKeysPerTile;
+            for (int j = k0 / R + je; j < kend / R; j += TPT)
+                if (t_e < T && j <= jc_e) score_row[j] = block_score(j, kend);
         }
     }
-    __syncthreads();
+    if constexpr (MODE == 0) {
+        __syncthreads();
+        // remaining blocks up to the token's own block (their later keys are invisible)
+        for (int j = k0 / R + je; j <= jc_e; j += TPT)
+            if (t_e < T) score_row[j] = block_score(j, k0);
+    }
 
     if constexpr (WITH_O) {
 #pragma unroll
@@ -304,15 +380,9 @@ __global__ __launch_bounds__(256) void score_select_kernel(SelParams p) {
             }
         }
     }
-    for (int tl = wave; tl < TQ; tl += kWaves) {
-        const int t = tok0 + tl;
-        if (t >= T) break;
-        select_blocks_wave(sc + tl * p.n_slc, t / p.lp, p.top_n, p.n_init, p.n_local,
-                           p.sel + (((size_t)b * T + t) * p.Hkv + g) * p.top_n);
-    }
 }
 
-// Selection from caller scores [B,T,Hkv,n_slc]: one wave per (b, t, g).
+// Selection from scores [B,T,Hkv,n_slc]: one wave per (b, t, g).
 __global__ __launch_bounds__(256) void select_from_scores_kernel(const float* __restrict__ scores,
                                                                  int32_t* __restrict__ sel, int T, int Hkv,
                                                                  int n_slc, int lp, int top_n, int n_init,
@@ -336,35 +406,34 @@ void stats_g(const u16* Q, const u16* Kc, float* m, float* il, float* lse, int B
 }
 
 template <int DK, int DV, int G, int MODE, int NQ, bool WITH_O>
-void select_g(const SelParams& p, int B, hipStream_t st) {
+void scores_g(const SelParams& p, int B, hipStream_t st) {
     constexpr int TQ = kWaves * NQ * 16 / G;
     dim3 grid((p.T + TQ - 1) / TQ, p.Hkv, B);
     const size_t lds = score_select_lds_bytes(DK, DV, G, MODE, NQ, WITH_O, p.n_slc);
     if (lds > 65536)
-        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(score_select_kernel<DK, DV, G, MODE, NQ, WITH_O>),
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(cmp_scores_kernel<DK, DV, G, MODE, NQ, WITH_O>),
                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    score_select_kernel<DK, DV, G, MODE, NQ, WITH_O><<<grid, 256, lds, st>>>(p);
+    cmp_scores_kernel<DK, DV, G, MODE, NQ, WITH_O><<<grid, 256, lds, st>>>(p);
 }
 
 template <int DK, int DV, int G>
-bool select_dk(int mode, bool with_o, const SelParams& p, int B, hipStream_t st) {
+bool scores_dk(int mode, bool with_o, const SelParams& p, int B, hipStream_t st) {
     if (mode == 0) {
-        if (with_o) select_g<DK, DV, G, 0, 2, true>(p, B, st);
-        else select_g<DK, DV, G, 0, 2, false>(p, B, st);
+        if (with_o) scores_g<DK, DV, G, 0, 2, true>(p, B, st);
+        else scores_g<DK, DV, G, 0, 2, false>(p, B, st);
     } else {
-        select_g<DK, DV, G, 1, (G == 1 ? 1 : 2), false>(p, B, st);
+        scores_g<DK, DV, G, 1, (G == 1 ? 1 : 2), false>(p, B, st);
     }
     return true;
 }
 }  // namespace
 
 size_t score_select_lds_bytes(int DK, int DV, int G, int mode, int NQ, bool with_o, int n_slc) {
+    (void)n_slc;
     const int TQ = kWaves * NQ * 16 / G;
     size_t bytes = (size_t)kKeysPerTile * (DK + 8) * 2;
     if (with_o) bytes += (size_t)DV * (kKeysPerTile + 8) * 2;
-    bytes += (size_t)TQ * kKeysPerTile * 4;
-    bytes += (size_t)TQ * n_slc * 4;
-    (void)mode;
+    if (mode == 0) bytes += (size_t)TQ * kRing * 4;
     return bytes;
 }
 
@@ -389,10 +458,10 @@ bool launch_cmp_stats(const u16* Q, const u16* Kc, float* m, float* il, float* l
     return true;
 }
 
-bool launch_score_select(int mode, bool with_o, int DK, int DV, int G, const SelParams& p, int B, hipStream_t st) {
-    if (DK == 192 && DV == 128) { NSA_G_SWITCH(G, return select_dk<192, 128, GG>(mode, with_o, p, B, st)); }
-    if (DK == 128 && DV == 128) { NSA_G_SWITCH(G, return select_dk<128, 128, GG>(mode, with_o, p, B, st)); }
-    if (DK == 64 && DV == 64) { NSA_G_SWITCH(G, return select_dk<64, 64, GG>(mode, with_o, p, B, st)); }
+bool launch_cmp_scores(int mode, bool with_o, int DK, int DV, int G, const SelParams& p, int B, hipStream_t st) {
+    if (DK == 192 && DV == 128) { NSA_G_SWITCH(G, return scores_dk<192, 128, GG>(mode, with_o, p, B, st)); }
+    if (DK == 128 && DV == 128) { NSA_G_SWITCH(G, return scores_dk<128, 128, GG>(mode, with_o, p, B, st)); }
+    if (DK == 64 && DV == 64) { NSA_G_SWITCH(G, return scores_dk<64, 64, GG>(mode, with_o, p, B, st)); }
     return false;
 }
 

@@ -144,7 +144,8 @@ nsa_status nsa_select_from_scores(const nsa_config* cfg, const float* scores, in
  *   o_win = the same over tokens max(0, t-w+1) .. t;
  *   O = sum over enabled branches of sigmoid(z_branch) * o_branch, with o_cmp taken from the
  *   caller (as produced by nsa_score_select) when NSA_BR_CMP is set.
- * sel_idx entries must be distinct blocks <= t / l' (or -1).  gate_logits NULL = weight 1.
+ * sel_idx rows must list distinct blocks <= t / l' in ascending order, padded with -1 at the
+ * end (as nsa_score_select writes them).  gate_logits NULL = weight 1.
  * O is bf16 [B, T, H, d_v]. */
 nsa_status nsa_sparse_attn_fwd(const nsa_config* cfg, const void* Q, const void* K, const void* V,
                                const int32_t* sel_idx, const float* o_cmp, const float* gate_logits,
