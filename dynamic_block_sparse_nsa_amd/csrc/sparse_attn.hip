@@ -9,12 +9,13 @@
 // the running max and sum in registers (base-2), then O^T += V^T . P^T with V^T read
 // from a transposed, 32-key-permuted copy of V so both operands are 16-byte loads.
 //
+// Phase B (per token, first): the selected blocks before the window range are contiguous
+//   64-token spans gathered by block index straight from memory in 32-key chunks, two
+//   chunks in flight per wave.
 // Phase A (shared): the window range of the 4 tokens is streamed once through
 //   double-buffered LDS tiles of 32 keys; each wave updates its window softmax and, for
 //   selected blocks lying inside that range (the local blocks), its selected-branch
 //   softmax from the same S tile.
-// Phase B (per token): the other selected blocks are contiguous 64-token spans gathered
-//   by block index straight from memory in 32-key chunks.
 // Epilogue: sigmoid gates on o_cmp (from the caller), o_slc, o_win; bf16 store.
 #include "common.hpp"
 #include "launch.hpp"
@@ -32,7 +33,7 @@ struct SoftmaxState {
     f32x4 o[NDT];
     float m, l;
 
-    __device__ void reset() {
+    __device__ __forceinline__ void reset() {
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) o[dt] = zero4();
         m = -INFINITY;
@@ -41,7 +42,7 @@ struct SoftmaxState {
 
     // One 32-key chunk starting at key0: s0 holds keys key0+4q+r, s1 keys key0+16+4q+r
     // (q = lane/16); keys outside [lo, hi] are masked.  va: the V^T operand per d-tile.
-    __device__ void update(const f32x4& s0, const f32x4& s1, int key0, int lo, int hi, float scale_log2,
+    __device__ __forceinline__ void update(const f32x4& s0, const f32x4& s1, int key0, int lo, int hi, float scale_log2,
                            const bf16x8 (&va)[NDT]) {
         const int lq = (threadIdx.x & 63) >> 4;
         float x[8];
@@ -76,7 +77,7 @@ struct SoftmaxState {
         }
     }
 
-    __device__ void finish() {
+    __device__ __forceinline__ void finish() {
         const float L = col_sum(l);
         const float inv = L > 0.f ? 1.0f / L : 0.f;
 #pragma unroll
@@ -90,45 +91,65 @@ template <int DK, int DV>
 struct WinTile {
     static constexpr int KSTR = DK + 8;
     static constexpr int VSTR = kChunk + 8;
-    static constexpr int KPR = DK / 8;                         // uint4 per K row
-    static constexpr int NK = (kChunk * KPR + 255) / 256;      // K uint4 per thread
-    static constexpr int NV = (DV * (kChunk / 8) + 255) / 256; // V uint4 per thread
-    uint4 rk[NK], rv[NV];
+    static constexpr int KPR = DK / 8;              // uint4 per K row
+    static constexpr int NK = kChunk * KPR / 256;   // K uint4 per thread
+    static constexpr int NV = DV * (kChunk / 8) / 256;  // V uint4 per thread
+    static_assert(kChunk * KPR % 256 == 0 && DV * (kChunk / 8) % 256 == 0, "tile must split evenly");
+    u32x4 rk[NK], rv[NV];
 
-    __device__ void load(const u16* kg, const u16* vtg, int key0, int T, int Tpad) {
+    __device__ __forceinline__ void load(const u16* kg, const u16* vtg, int key0, int T, int Tpad) {
 #pragma unroll
         for (int i = 0; i < NK; ++i) {
             const int idx = threadIdx.x + 256 * i;
-            if (idx < kChunk * KPR) {
-                const int row = idx / KPR, col = (idx % KPR) * 8;
-                rk[i] = *reinterpret_cast<const uint4*>(kg + (size_t)min(key0 + row, T - 1) * DK + col);
-            }
+            const int row = idx / KPR, col = (idx % KPR) * 8;
+            rk[i] = *reinterpret_cast<const u32x4*>(kg + (size_t)min(key0 + row, T - 1) * DK + col);
         }
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
             const int idx = threadIdx.x + 256 * i;
-            if (idx < DV * (kChunk / 8)) {
-                const int row = idx / (kChunk / 8), col = (idx % (kChunk / 8)) * 8;
-                rv[i] = *reinterpret_cast<const uint4*>(vtg + (size_t)row * Tpad + key0 + col);
-            }
+            const int row = idx / (kChunk / 8), col = (idx % (kChunk / 8)) * 8;
+            rv[i] = *reinterpret_cast<const u32x4*>(vtg + (size_t)row * Tpad + key0 + col);
         }
     }
-    __device__ void store(u16* kb, u16* vb) const {
+    __device__ __forceinline__ void store(u16* kb, u16* vb) const {
 #pragma unroll
         for (int i = 0; i < NK; ++i) {
             const int idx = threadIdx.x + 256 * i;
-            if (idx < kChunk * KPR) {
-                const int row = idx / KPR, col = (idx % KPR) * 8;
-                *reinterpret_cast<uint4*>(&kb[row * KSTR + col]) = rk[i];
-            }
+            const int row = idx / KPR, col = (idx % KPR) * 8;
+            *reinterpret_cast<u32x4*>(&kb[row * KSTR + col]) = rk[i];
         }
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
             const int idx = threadIdx.x + 256 * i;
-            if (idx < DV * (kChunk / 8)) {
-                const int row = idx / (kChunk / 8), col = (idx % (kChunk / 8)) * 8;
-                *reinterpret_cast<uint4*>(&vb[row * VSTR + col]) = rv[i];
-            }
+            const int row = idx / (kChunk / 8), col = (idx % (kChunk / 8)) * 8;
+            *reinterpret_cast<u32x4*>(&vb[row * VSTR + col]) = rv[i];
+        }
+    }
+};
+
+// One gathered 32-key chunk held in registers: K rows as the A operands of S^T = K.Q^T
+// and V^T columns as the A operands of O^T += V^T.P^T.
+template <int DK, int DV>
+struct GatherChunk {
+    static constexpr int NDS = DK / 32, NDT = DV / 16;
+    bf16x8 ka[NDS], kb[NDS], va[NDT];
+    __device__ __forceinline__ void load(const u16* kg, const u16* vtg, int key0, int T, int Tpad) {
+        const int lane = threadIdx.x & 63, li = lane & 15, lq = lane >> 4;
+        const u16* k0p = kg + (size_t)min(key0 + li, T - 1) * DK + lq * 8;
+        const u16* k1p = kg + (size_t)min(key0 + 16 + li, T - 1) * DK + lq * 8;
+#pragma unroll
+        for (int ds = 0; ds < NDS; ++ds) { ka[ds] = ld8(k0p + 32 * ds); kb[ds] = ld8(k1p + 32 * ds); }
+        const u16* vp = vtg + (size_t)li * Tpad + key0 + lq * 8;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) va[dt] = ld8(vp + (size_t)16 * dt * Tpad);
+    }
+    __device__ __forceinline__ void scores(const bf16x8 (&qf)[NDS], f32x4& s0, f32x4& s1) const {
+        s0 = zero4();
+        s1 = zero4();
+#pragma unroll
+        for (int ds = 0; ds < NDS; ++ds) {
+            s0 = mfma16(ka[ds], qf[ds], s0);
+            s1 = mfma16(kb[ds], qf[ds], s1);
         }
     }
 };
@@ -163,14 +184,18 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnParams p) {
     }
     const u16* kg = p.K + ((size_t)b * p.Hkv + g) * (size_t)T * DK;
     const u16* vtg = p.Vt + ((size_t)b * p.Hkv + g) * (size_t)DV * p.Tpad;
-    const int32_t* sl = p.sel + (((size_t)b * T + tq) * p.Hkv + g) * p.top_n;
     const bool use_slc = (p.branches & 2) != 0, use_win = (p.branches & 4) != 0;
+    // the token's block list, one entry per lane, read back with readlane (no memory
+    // access on the dependency chain of a gather's address)
+    const int sel_lane = (use_slc && lane < p.top_n)
+                             ? p.sel[(((size_t)b * T + tq) * p.Hkv + g) * p.top_n + lane] : -1;
+    auto sl = [&](int c) { return __builtin_amdgcn_readlane(sel_lane, c); };
 
     SoftmaxState<DV> win, slc;
     win.reset();
     slc.reset();
 
-    // ---- phase A: the window range of the workgroup's tokens, shared through LDS ----
+    // range of keys streamed through LDS for the window (phase A)
     int c_begin = 0, nch = 0;
     if (use_win) {
         const int wlo = max(0, tok0 - p.window + 1);
@@ -178,6 +203,47 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnParams p) {
         c_begin = wlo & ~(kChunk - 1);
         nch = (whi - c_begin) / kChunk + 1;
     }
+
+    // ---- phase B: selected blocks before that range, gathered per token ----
+    // Chunks are software-pipelined: the next chunk's loads are in flight while the
+    // current one is computed (two register buffers used alternately).
+    if (active && use_slc) {
+        int nb = 0;  // leading list entries outside the shared range (the list is ascending)
+        for (; nb < p.top_n; ++nb) {
+            const int j = sl(nb);
+            if (j < 0 || (nch > 0 && j * p.lp >= c_begin)) break;
+        }
+        const int cpb = p.lp / kChunk;
+        int c = 0, u = 0;
+        auto advance = [&](int& key0, int& start) -> bool {
+            while (c < nb) {
+                start = sl(c) * p.lp;
+                key0 = start + kChunk * u;
+                if (u < cpb && key0 <= t) { ++u; return true; }
+                ++c;
+                u = 0;
+            }
+            return false;
+        };
+        GatherChunk<DK, DV> A, B;
+        int keyA = 0, startA = 0, keyB = 0, startB = 0;
+        bool hasA = advance(keyA, startA);
+        if (hasA) A.load(kg, vtg, keyA, T, p.Tpad);
+        while (hasA) {
+            const bool hasB = advance(keyB, startB);
+            if (hasB) B.load(kg, vtg, keyB, T, p.Tpad);
+            f32x4 s0, s1;
+            A.scores(qf, s0, s1);
+            slc.update(s0, s1, keyA, startA, t, p.scale_log2, A.va);
+            if (!hasB) break;
+            hasA = advance(keyA, startA);
+            if (hasA) A.load(kg, vtg, keyA, T, p.Tpad);
+            B.scores(qf, s0, s1);
+            slc.update(s0, s1, keyB, startB, t, p.scale_log2, B.va);
+        }
+    }
+
+    // ---- phase A: the window range of the workgroup's tokens, shared through LDS ----
     Tile tile;
     if (nch > 0) {
         tile.load(kg, vtg, c_begin, T, p.Tpad);
@@ -195,7 +261,7 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnParams p) {
             bool s_any = false;
             if (use_slc && key0 <= t && jch * p.lp >= c_begin) {
                 for (int c = 0; c < p.top_n; ++c) {
-                    const int j = sl[c];
+                    const int j = sl(c);
                     if (j < 0 || j > jch) break;
                     s_any |= (j == jch);
                 }
@@ -219,32 +285,6 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnParams p) {
         __syncthreads();
     }
 
-    // ---- phase B: selected blocks outside the shared range, gathered per token ----
-    if (active && use_slc) {
-        for (int c = 0; c < p.top_n; ++c) {
-            const int j = sl[c];
-            if (j < 0) break;
-            const int start = j * p.lp;
-            if (nch > 0 && start >= c_begin) continue;
-            for (int key0 = start; key0 < start + p.lp && key0 <= t; key0 += kChunk) {
-                const u16* k0p = kg + (size_t)min(key0 + li, T - 1) * DK + lq * 8;
-                const u16* k1p = kg + (size_t)min(key0 + 16 + li, T - 1) * DK + lq * 8;
-                bf16x8 ka[NDS], kb[NDS], va[NDT];
-#pragma unroll
-                for (int ds = 0; ds < NDS; ++ds) { ka[ds] = ld8(k0p + 32 * ds); kb[ds] = ld8(k1p + 32 * ds); }
-                const u16* vp = vtg + (size_t)li * p.Tpad + key0 + lq * 8;
-#pragma unroll
-                for (int dt = 0; dt < NDT; ++dt) va[dt] = ld8(vp + (size_t)16 * dt * p.Tpad);
-                f32x4 s0 = zero4(), s1 = zero4();
-#pragma unroll
-                for (int ds = 0; ds < NDS; ++ds) {
-                    s0 = mfma16(ka[ds], qf[ds], s0);
-                    s1 = mfma16(kb[ds], qf[ds], s1);
-                }
-                slc.update(s0, s1, key0, start, t, p.scale_log2, va);
-            }
-        }
-    }
     if (!active) return;
     win.finish();
     slc.finish();
