@@ -15,7 +15,6 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-deco
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import math
 import os
@@ -66,16 +65,10 @@ def moba_flops(cfg: NSAConfig) -> int:
 
 
 # ---------------------------------------------------------------------------
-def sha_of(paths) -> str:
-    h = hashlib.sha256()
-    for p in paths:
-        h.update(open(os.path.join(ROOT, p), "rb").read())
-    return h.hexdigest()[:16]
-
-
 def load_traffic(kernel: str, sources) -> dict | None:
-    """HBM traffic per launch from a committed counter summary, if it was taken on the
-    current source of the kernel (otherwise null)."""
+    """HBM traffic per launch from the committed counter record, if it was taken on the
+    current sources of the kernel (otherwise None: the kernel changed since)."""
+    from dynamic_block_sparse_nsa_amd.profsum import source_sha
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
@@ -83,7 +76,7 @@ def load_traffic(kernel: str, sources) -> dict | None:
         rec = json.load(open(path)).get(kernel)
     except (OSError, ValueError):
         return None
-    if not rec or rec.get("source_sha") != sha_of(sources):
+    if not rec or sorted(rec.get("sources", [])) != sorted(sources) or rec.get("source_sha") != source_sha(rec["sources"]):
         return None
     return rec
 
@@ -108,9 +101,9 @@ def time_calls(fns, steps, warmup, torch):
     return per_call, wall
 
 
-def cpu_baseline(cfg: NSAConfig, inp: dict, budget_rows: int = 96) -> dict:
+def cpu_baseline(cfg: NSAConfig, inp: dict, budget_rows: int = 3072, nb: int = 2048) -> dict:
     """The fp64 oracle on a bounded sample of the same workload, scaled to tokens/s:
-    compression of 256 blocks per KV group (scaled to all N_cmp blocks) plus the score,
+    compression of ``nb`` blocks per KV group (scaled to all N_cmp blocks) plus the score,
     select and attend stages for the last ``budget_rows`` rows (the most expensive ones;
     scaled to T rows at that cost, which overstates the CPU's speed on earlier rows only
     through their shorter compressed history)."""
@@ -119,7 +112,7 @@ def cpu_baseline(cfg: NSAConfig, inp: dict, budget_rows: int = 96) -> dict:
     from dynamic_block_sparse_nsa_amd.inputs import bf16_bits_to_f64 as f64
 
     threads = oracle.num_threads()
-    nb = 256
+    nb = min(nb, cfg.n_cmp)
     blocks = np.arange(nb)
     t0 = time.perf_counter()
     for g in range(cfg.num_kv_heads):
@@ -154,6 +147,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-moba", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run one elementwise kernel over 1 GiB (reads and writes 1 GiB: the known-size kernel that scales HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: the NSA forward shards by KV group / batch with no exchange, "
@@ -169,6 +164,14 @@ def main():
 
     def d(bits):
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    if args.copy_probe:
+        src = torch.empty(1 << 29, dtype=torch.int16, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        torch.bitwise_not(src, out=dst)   # an elementwise kernel: reads and writes 1 GiB
+        torch.cuda.synchronize()
+        del src, dst
 
     # ---------------- prefill 64K ----------------
     cfg = P64K
@@ -203,7 +206,11 @@ def main():
     dom = int(np.argmax(call_ms))
     dom_flops = [2 * (cfg.n_cmp * (cfg.cmp_block * cfg.d_k * cfg.d_k + cfg.cmp_block * cfg.d_v * cfg.d_v)) * Hkv,
                  fl["cmp"], fl["slc"] + fl["win"]][dom]
-    dom_kernel = ["compress_linear_kernel", "score_select_kernel", "sparse_attn_kernel"][dom]
+    dom_kernel = ["compress_linear_kernel", "cmp_scores_kernel", "sparse_attn_kernel"][dom]
+    # every kernel the dominant call launches (the first is the main one)
+    dom_launches = [["compress_linear_kernel", "transpose_w_kernel", "pe_bias_kernel"],
+                    ["cmp_scores_kernel", "cmp_stats_kernel", "transpose_v_kernel", "select_from_scores_kernel"],
+                    ["sparse_attn_kernel", "transpose_v_kernel"]][dom]
     dom_src = [["dynamic_block_sparse_nsa_amd/csrc/compress.hip"],
                ["dynamic_block_sparse_nsa_amd/csrc/score_select.hip", "dynamic_block_sparse_nsa_amd/csrc/select.hpp"],
                ["dynamic_block_sparse_nsa_amd/csrc/sparse_attn.hip"]][dom]
@@ -232,7 +239,7 @@ def main():
         "mfma_peak_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
         "algorithmic_flops": {k: int(v) for k, v in fl.items()},
         "per_call_ms": {n: round(float(c), 4) for n, c in zip(names, call_ms)},
-        "roofline": {"bound": "mfma", "kernel": dom_kernel, "call": names[dom],
+        "roofline": {"bound": "mfma", "kernel": dom_kernel, "call": names[dom], "call_kernels": dom_launches,
                      "achieved": round(dom_tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(dom_tf / PEAK_BF16_TFLOPS, 4),
                      "traffic": None if traffic is None else traffic.get("bytes_per_launch")},

@@ -1,0 +1,123 @@
+"""Summaries of rocprofv3 output for the benchmark's profile records.
+
+``stats``   kernel_stats.csv (from ``rocprofv3 --kernel-trace --stats -f csv``) -> a short
+            text table (calls, average and total duration per kernel).
+``traffic`` two counter_collection.csv files (``--pmc FETCH_SIZE`` and ``--pmc WRITE_SIZE``)
+            -> HBM bytes per launch of each named kernel, scaled by what the same counter
+            reads for a plain device copy of known size in the same run, written into a
+            JSON record with the hash of the kernel's sources (a record whose hash no
+            longer matches the sources is ignored by the benchmark).
+
+Usage:
+  python -m dynamic_block_sparse_nsa_amd.profsum stats STATS_CSV --cmd "..." --title "..." > out.txt
+  python -m dynamic_block_sparse_nsa_amd.profsum traffic --fetch F.csv --write W.csv \
+      --copy-bytes N --copy-regex REGEX --kernel NAME=SRC[,SRC...] [--kernel ...] --out traffic.json
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import hashlib
+import json
+import os
+import re
+import sys
+from collections import defaultdict
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def source_sha(paths) -> str:
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def short_name(name: str) -> str:
+    if name.startswith(("void at::", "at::")):
+        return "(torch kernel: input generation / copy)"
+    m = re.match(r"(?:void )?(?:nsa::)?([A-Za-z_0-9]+)(<[^()]*>)?", name)
+    return (m.group(1) + (m.group(2) or "")) if m else name
+
+
+def stats(path: str, cmd: str, title: str) -> str:
+    rows = []
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            rows.append((short_name(r["Name"]), int(r["Calls"]), float(r["TotalDurationNs"]) / 1e6,
+                         float(r["AverageNs"]) / 1e3, float(r["Percentage"])))
+    rows.sort(key=lambda r: -r[2])
+    out = [f"# {title}", "", f"command: {cmd}", "",
+           f"{'kernel':64s} {'calls':>6s} {'avg_us':>10s} {'total_ms':>10s} {'pct':>6s}"]
+    for name, calls, tot, avg, pct in rows:
+        out.append(f"{name[:64]:64s} {calls:6d} {avg:10.1f} {tot:10.2f} {pct:6.2f}")
+    return "\n".join(out) + "\n"
+
+
+def per_kernel_counter(path: str, counter: str) -> dict:
+    """Mean of a counter's per-dispatch value, per kernel name."""
+    acc = defaultdict(list)
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] != counter:
+                continue
+            acc[r["Kernel_Name"]].append(float(r["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in acc.items()}
+
+
+def pick(values: dict, regex: str) -> float:
+    hits = [v for k, v in values.items() if re.search(regex, k)]
+    if not hits:
+        raise SystemExit(f"no kernel matches {regex!r} among {sorted(values)[:8]}")
+    return max(hits)
+
+
+def traffic(fetch_csv, write_csv, copy_bytes, copy_regex, kernels, out_path, cmd):
+    fetch = per_kernel_counter(fetch_csv, "FETCH_SIZE")
+    write = per_kernel_counter(write_csv, "WRITE_SIZE")
+    # counters are in KiB per dispatch; the copy reads and writes copy_bytes exactly
+    f_scale = copy_bytes / (pick(fetch, copy_regex) * 1024.0)
+    w_scale = copy_bytes / (pick(write, copy_regex) * 1024.0)
+    rec = json.load(open(out_path)) if os.path.exists(out_path) else {}
+    for spec in kernels:
+        name, srcs = spec.split("=", 1)
+        srcs = srcs.split(",")
+        fb = pick(fetch, rf"\b{re.escape(name)}\b") * 1024.0 * f_scale
+        wb = pick(write, rf"\b{re.escape(name)}\b") * 1024.0 * w_scale
+        rec[name] = {"fetch_bytes_per_launch": int(fb), "write_bytes_per_launch": int(wb),
+                     "bytes_per_launch": int(fb + wb), "fetch_scale": round(f_scale, 4),
+                     "write_scale": round(w_scale, 4), "copy_bytes": copy_bytes,
+                     "sources": srcs, "source_sha": source_sha(srcs), "command": cmd}
+    with open(out_path, "w") as f:
+        json.dump(rec, f, indent=1, sort_keys=True)
+        f.write("\n")
+    return rec
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="what", required=True)
+    a = sub.add_parser("stats")
+    a.add_argument("csv")
+    a.add_argument("--cmd", required=True)
+    a.add_argument("--title", required=True)
+    b = sub.add_parser("traffic")
+    b.add_argument("--fetch", required=True)
+    b.add_argument("--write", required=True)
+    b.add_argument("--copy-bytes", type=int, required=True)
+    b.add_argument("--copy-regex", required=True)
+    b.add_argument("--kernel", action="append", required=True)
+    b.add_argument("--out", required=True)
+    b.add_argument("--cmd", default="")
+    args = ap.parse_args(argv)
+    if args.what == "stats":
+        sys.stdout.write(stats(args.csv, args.cmd, args.title))
+    else:
+        rec = traffic(args.fetch, args.write, args.copy_bytes, args.copy_regex, args.kernel, args.out, args.cmd)
+        print(json.dumps(rec, indent=1))
+
+
+if __name__ == "__main__":
+    main()
