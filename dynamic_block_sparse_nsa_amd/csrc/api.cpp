@@ -113,7 +113,7 @@ AttnWs attn_ws(const Shape& s) {
     return w;
 }
 
-struct DecodeWs { size_t pm, pl, po, pa, sel, ocmp, am, al, ao, total; int n_split, jb, n_items; };
+struct DecodeWs { size_t pm, pl, po, pa, sel, cw, am, al, ao, total; int n_split, jb, n_items; };
 DecodeWs decode_ws(const Shape& s) {
     DecodeWs w{};
     w.n_split = std::max(1, (s.n_cmp + nsa::kDecodeSplitKeys - 1) / nsa::kDecodeSplitKeys);
@@ -126,7 +126,7 @@ DecodeWs decode_ws(const Shape& s) {
     w.po = off; off = align_up(off + bg * w.n_split * s.dv * 16 * 4, 256);
     w.pa = off; off = align_up(off + bg * w.n_split * 16 * w.jb * 4, 256);
     w.sel = off; off = align_up(off + bg * std::max(s.n, 1) * 4, 256);
-    w.ocmp = off; off = align_up(off + bg * 16 * s.dv * 4, 256);
+    w.cw = off; off = align_up(off + bg * w.n_split * 16 * 4, 256);
     w.am = off; off = align_up(off + bg * w.n_items * 16 * 4, 256);
     w.al = off; off = align_up(off + bg * w.n_items * 16 * 4, 256);
     w.ao = off; off = align_up(off + bg * w.n_items * s.dv * 16 * 4, 256);
@@ -324,6 +324,13 @@ nsa_status nsa_decode(const nsa_config* cfg, const void* q, const void* K_cache,
     if ((s.br & NSA_BR_WIN) && s.w <= 0) return fail(NSA_ERR_SHAPE, "window branch with window = 0");
     if (s.n_slc > 64 * 32) return fail(NSA_ERR_UNSUPPORTED, "at most 2048 selection blocks");
     const DecodeWs w = decode_ws(s);
+    if (w.n_items - s.n > nsa::kDecodeMaxItems)
+        return fail(NSA_ERR_UNSUPPORTED, "decode supports windows up to " +
+                                             std::to_string(64 * (nsa::kDecodeMaxItems - 2)) + " tokens");
+    if (w.n_split > nsa::kDecodeMaxSplits)
+        return fail(NSA_ERR_UNSUPPORTED, "decode supports at most " +
+                                             std::to_string(nsa::kDecodeMaxSplits * nsa::kDecodeSplitKeys) +
+                                             " compressed keys");
     if ((st = check_ws(ws, ws_bytes, w.total)) != NSA_OK) return st;
     using nsa::u16;
     nsa::DecodeParams p{};
@@ -341,7 +348,7 @@ nsa_status nsa_decode(const nsa_config* cfg, const void* q, const void* K_cache,
     p.part_o = at<float>(ws, w.po);
     p.part_a = at<float>(ws, w.pa);
     p.sel_ws = at<int32_t>(ws, w.sel);
-    p.ocmp_ws = at<float>(ws, w.ocmp);
+    p.cmp_w = at<float>(ws, w.cw);
     p.att_m = at<float>(ws, w.am);
     p.att_l = at<float>(ws, w.al);
     p.att_o = at<float>(ws, w.ao);

@@ -117,6 +117,35 @@ struct QMap {
     __device__ static int head(int c, int li) { return CL * (li % GL) + c % CL; }
 };
 
+// Offset (in elements) of the 8 contraction elements a lane of row-group lq holds for
+// MFMA step ds when a row of the operand is read straight from memory.  The contraction
+// is order-free, so steps 2p and 2p+1 take a lane's two adjacent 16-byte pieces of the
+// 64-element span p: every lane reads 32 contiguous bytes and four lanes a full 128-byte
+// line.  Both operands of a product must use the same mapping (d must be a multiple of 64).
+__device__ __forceinline__ int kpair_off(int ds, int lq) { return 64 * (ds >> 1) + 16 * lq + 8 * (ds & 1); }
+
+// gfx950 transposing LDS read (ds_read_b64_tr_b16).  Inside each 16-lane row, lane c
+// names 4 consecutive 16-bit values; lane j receives, as its element r, value j % 4 of
+// the 4 values named by lane 4r + j / 4 of the same row.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ s16x4 lds_read_tr16(const u16* p) {
+    typedef __attribute__((address_space(3))) s16x4* lds_ptr;
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_ptr)(p));
+}
+
+// V^T operand of O^T += V^T.P^T from a row-major value tile in LDS (row = key, STR
+// elements per row, 8-byte aligned rows): lane (li, lq) receives V[key0 + k][d0 + li] for
+// k = 4lq..4lq+3 and 16+4lq..16+4lq+3, the key order of pack_p / pack_p_split.
+__device__ __forceinline__ bf16x8 ld_vt_tr(const u16* tile, int STR, int key0, int d0) {
+    const int lane = threadIdx.x & 63, c = lane & 15, lq = (lane >> 4) & 3;
+    const u16* a = tile + (key0 + 4 * lq + (c >> 2)) * STR + d0 + 4 * (c & 3);
+    const s16x4 x = lds_read_tr16(a);
+    const s16x4 y = lds_read_tr16(a + 16 * STR);
+    const s16x8 v = __builtin_shufflevector(x, y, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(bf16x8, v);
+}
+
 __device__ __forceinline__ float sigmoidf_(float z) { return 1.0f / (1.0f + __expf(-z)); }
 
 }  // namespace nsa

@@ -6,20 +6,22 @@
 // is streamed exactly once, split over many workgroups:
 //   decode_cmp_kernel     split s covers 256 compressed keys of one (sequence, group);
 //                         4 waves x 64 keys, the group's heads packed in the MFMA column
-//                         tile.  Emits, relative to the split's per-head max m: the sum
-//                         l, the unnormalized o^T, and per-head partial block sums
+//                         tile; every load of the split is issued before any math.
+//                         Emits, relative to the split's per-head max m: the sum l, the
+//                         unnormalized o^T, and per-head partial block sums
 //                         A[h][j] = sum over this split's keys overlapping block j of
 //                         2^(x - m).
-//   decode_select_kernel  per (sequence, group): lse per head from the split (m, l);
-//                         o_cmp = sum_s 2^(m_s - lse) o_s; block score
-//                         score[j] = sum_h sum_s 2^(m_s,h - lse_h) A_s[h][j] (the exact
-//                         normalized compressed probabilities, summed as in prefill);
-//                         then the shared top-n.
+//   decode_select_kernel  per (sequence, group): lse per head from the split (m, l) and
+//                         the split weights w_s = 2^(m_s - lse); block score
+//                         score[j] = sum_h sum_s w_s,h A_s[h][j] (the exact normalized
+//                         compressed probabilities, summed as in prefill); then the
+//                         shared top-n.
 //   decode_attn_kernel    one wave per item: a selected block, or a 64-token piece of the
-//                         window; online softmax over its keys, partial (m, l, o^T).
-//   decode_merge_kernel   merges the items of each branch and applies the gates.
-// Value rows are key-major in the caches, so each wave transposes its value tile into
-// LDS (d-major, 32-key groups permuted as in the prefill kernels) before the MFMA.
+//                         window; exact softmax over its keys, partial (m, l, o^T).
+//   decode_merge_kernel   o_cmp = sum_s w_s o_s, merges the items of each branch and
+//                         applies the gates; one thread per output element.
+// Value rows stay key-major: each wave stores its value tile row-major in LDS and builds
+// the V^T MFMA operand with the gfx950 transposing LDS read.
 #include "common.hpp"
 #include "launch.hpp"
 #include "select.hpp"
@@ -32,43 +34,80 @@ int decode_items(int top_n, int window) { return top_n + (window > 0 ? window / 
 
 namespace {
 
+constexpr int kPsumStride = kDecodeSplitKeys + 4;   // padded row of the per-head probabilities
+
 __device__ __forceinline__ int query_pos(const int32_t* cache_len, int b, int L) {
     const int n = min(max(cache_len[b], 1), L);
     return n - 1;
 }
 
-// Stage value rows [key0, key0 + NK) (clamped to < nrows) of a key-major tile into
-// LDS transposed: vt[d * VSTR + (k & ~31) + vt_pos(k & 31)], k relative to key0.
-template <int DV, int NK, int VSTR>
-__device__ __forceinline__ void stage_vt(const u16* __restrict__ V, int key0, int nrows, u16* vt) {
-    const int lane = threadIdx.x & 63;
-    for (int idx = lane; idx < NK * (DV / 8); idx += 64) {
-        const int k = idx / (DV / 8), d8 = (idx % (DV / 8)) * 8;
-        const int row = min(key0 + k, nrows - 1);
-        const uint4 v = *reinterpret_cast<const uint4*>(V + (size_t)row * DV + d8);
-        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-        const int pos = (k & ~31) + vt_pos(k & 31);
+// A wave's 64-key tile: K rows as the A operands of S^T = K.Q^T (4 tiles of 16 keys) and
+// the value rows (clamped to < nrows), loaded to registers in one burst.
+template <int DK, int DV>
+struct KeyTile64 {
+    static constexpr int NDS = DK / 32;
+    static constexpr int NVC = 64 * DV / 8 / 64;   // 16-byte value chunks per lane
+    bf16x8 ka[4][NDS];
+    u32x4 vr[NVC];
+    __device__ __forceinline__ void load(const u16* kg, const u16* vg, int key0, int nrows) {
+        const int lane = threadIdx.x & 63, li = lane & 15, lq = lane >> 4;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            vt[(d8 + 2 * i) * VSTR + pos] = (u16)(w[i] & 0xFFFFu);
-            vt[(d8 + 2 * i + 1) * VSTR + pos] = (u16)(w[i] >> 16);
+        for (int kt = 0; kt < 4; ++kt) {
+            const u16* kp = kg + (size_t)min(key0 + 16 * kt + li, nrows - 1) * DK;
+#pragma unroll
+            for (int ds = 0; ds < NDS; ++ds) ka[kt][ds] = ld8(kp + kpair_off(ds, lq));
+        }
+#pragma unroll
+        for (int i = 0; i < NVC; ++i) {
+            const int idx = lane + 64 * i;
+            const int row = idx / (DV / 8), col = (idx % (DV / 8)) * 8;
+            vr[i] = *reinterpret_cast<const u32x4*>(vg + (size_t)min(key0 + row, nrows - 1) * DV + col);
         }
     }
+    // value rows to a row-major LDS tile [64][STR]
+    template <int STR>
+    __device__ __forceinline__ void store_v(u16* vs) const {
+        const int lane = threadIdx.x & 63;
+#pragma unroll
+        for (int i = 0; i < NVC; ++i) {
+            const int idx = lane + 64 * i;
+            const int row = idx / (DV / 8), col = (idx % (DV / 8)) * 8;
+            *reinterpret_cast<u32x4*>(&vs[row * STR + col]) = vr[i];
+        }
+    }
+    __device__ __forceinline__ void scores(const bf16x8 (&qf)[NDS], f32x4 (&s)[4]) const {
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) {
+            s[kt] = zero4();
+#pragma unroll
+            for (int ds = 0; ds < NDS; ++ds) s[kt] = mfma16(ka[kt][ds], qf[ds], s[kt]);
+        }
+    }
+};
+
+template <int DK>
+__device__ __forceinline__ void load_q(const u16* q, int b, int H, int g, int G, bf16x8 (&qf)[DK / 32]) {
+    const int lane = threadIdx.x & 63, li = lane & 15, lq = lane >> 4;
+    const int h = g * G + min(li, G - 1);
+    const u16* qp = q + ((size_t)b * H + h) * DK;
+#pragma unroll
+    for (int ds = 0; ds < DK / 32; ++ds) qf[ds] = li < G ? ld8(qp + kpair_off(ds, lq)) : zero8();
 }
 
 }  // namespace
 
 // ---------------------------------------------------------------------------
 template <int DK, int DV>
-__global__ __launch_bounds__(256) void decode_cmp_kernel(DecodeParams p) {
+__global__ __launch_bounds__(256, 2) void decode_cmp_kernel(DecodeParams p) {
     constexpr int NDS = DK / 32, NDT = DV / 16;
-    constexpr int VSTR = 64 + 8;
+    constexpr int VSTR = DV + 16;
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-    u16* vt_all = reinterpret_cast<u16*>(smem);                             // [4][DV][VSTR]
-    float* psum = reinterpret_cast<float*>(vt_all + 4 * DV * VSTR);          // [16][256]
-    float* wm = psum + 16 * kDecodeSplitKeys;                               // [4][16]
-    float* wl = wm + 64;                                                    // [4][16]
-    float* po = reinterpret_cast<float*>(smem);                              // [4][DV][16] (reuses vt)
+    u16* vs_all = reinterpret_cast<u16*>(smem);                              // [4][64][VSTR]
+    float* wm = reinterpret_cast<float*>(vs_all + 4 * 64 * VSTR);            // [4][16]
+    float* wl = wm + 64;                                                     // [4][16]
+    // after the value products the tile region is reused:
+    float* po = reinterpret_cast<float*>(smem);                              // [4][DV][16]
+    float* psum = po + 4 * DV * 16;                                          // [16][kPsumStride]
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int li = lane & 15, lq = lane >> 4;
@@ -86,27 +125,15 @@ __global__ __launch_bounds__(256) void decode_cmp_kernel(DecodeParams p) {
         }
         return;
     }
-    const bool head_ok = li < G;
-    const int h = g * G + min(li, G - 1);
+    KeyTile64<DK, DV> tile;
+    tile.load(p.Kc + ((size_t)b * p.Hkv + g) * (size_t)Nc * DK, p.Vc + ((size_t)b * p.Hkv + g) * (size_t)Nc * DV, kw,
+              Nc);
     bf16x8 qf[NDS];
-    {
-        const u16* qp = p.q + ((size_t)b * H + h) * DK + lq * 8;
-#pragma unroll
-        for (int ds = 0; ds < NDS; ++ds) qf[ds] = head_ok ? ld8(qp + 32 * ds) : zero8();
-    }
-    const u16* kc = p.Kc + ((size_t)b * p.Hkv + g) * (size_t)Nc * DK;
-    const u16* vc = p.Vc + ((size_t)b * p.Hkv + g) * (size_t)Nc * DV;
-    u16* vt = vt_all + wave * DV * VSTR;
-
+    load_q<DK>(p.q, b, H, g, G, qf);
     f32x4 sacc[4];
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-        sacc[kt] = zero4();
-        const u16* kp = kc + (size_t)min(kw + 16 * kt + li, Nc - 1) * DK + lq * 8;
-#pragma unroll
-        for (int ds = 0; ds < NDS; ++ds) sacc[kt] = mfma16(ld8(kp + 32 * ds), qf[ds], sacc[kt]);
-    }
-    stage_vt<DV, 64, VSTR>(vc, kw, Nc, vt);
+    tile.scores(qf, sacc);
+    u16* vs = vs_all + wave * 64 * VSTR;
+    tile.template store_v<VSTR>(vs);
 
     float x[16];
     float tmax = -INFINITY;
@@ -131,7 +158,6 @@ __global__ __launch_bounds__(256) void decode_cmp_kernel(DecodeParams p) {
             const float pr = fast_exp2(x[kt * 4 + r] - M);
             pv[kt][r] = pr;
             ls += pr;
-            psum[li * kDecodeSplitKeys + 64 * wave + 16 * kt + 4 * lq + r] = pr;
         }
     ls = col_sum(ls);
     if (lq == 0) wl[wave * 16 + li] = ls;
@@ -144,16 +170,20 @@ __global__ __launch_bounds__(256) void decode_cmp_kernel(DecodeParams p) {
         pack_p_split(pv[2 * u], pv[2 * u + 1], bh, bl);
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) {
-            const bf16x8 a = ld8(&vt[(16 * dt + li) * VSTR + 32 * u + lq * 8]);
+            const bf16x8 a = ld_vt_tr(vs, VSTR, 32 * u, 16 * dt);
             oacc[dt] = mfma16(a, bh, oacc[dt]);
             oacc[dt] = mfma16(a, bl, oacc[dt]);
         }
     }
-    __syncthreads();  // every wave is done with its vt region: reuse as po
+    __syncthreads();  // every wave is done with its value tile: reuse the region
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
         for (int r = 0; r < 4; ++r) po[(wave * DV + 16 * dt + 4 * lq + r) * 16 + li] = oacc[dt][r];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) psum[li * kPsumStride + 64 * wave + 16 * kt + 4 * lq + r] = pv[kt][r];
     __syncthreads();
     for (int idx = threadIdx.x; idx < DV * 16; idx += 256) {
         const float v = po[idx] + po[DV * 16 + idx] + po[2 * DV * 16 + idx] + po[3 * DV * 16 + idx];
@@ -174,64 +204,88 @@ __global__ __launch_bounds__(256) void decode_cmp_kernel(DecodeParams p) {
         const int ilo = max(kbeg, num > 0 ? (num + p.s - 1) / p.s : 0);
         const int ihi = min(kbeg + kDecodeSplitKeys - 1, (j * p.lp + p.lp - 1) / p.s);
         float acc = 0.f;
-        for (int i = ilo; i <= ihi; ++i) acc += psum[hh * kDecodeSplitKeys + (i - kbeg)];
+        for (int i = ilo; i <= ihi; ++i) acc += psum[hh * kPsumStride + (i - kbeg)];
         p.part_a[(pbase * 16 + hh) * p.jb + (j - jlo)] = acc;
     }
 }
 
 // ---------------------------------------------------------------------------
-template <int DV>
-__global__ __launch_bounds__(256) void decode_select_kernel(DecodeParams p) {
+template <int NU>
+__global__ __launch_bounds__(1024) void decode_select_kernel(DecodeParams p) {
     extern __shared__ float sm[];
     float* f = sm;                       // [n_split][16]
     float* sc = f + p.n_split * 16;      // [n_slc]
     const int g = blockIdx.x, b = blockIdx.y;
+    const int lane = threadIdx.x & 63;
     const int t = query_pos(p.cache_len, b, p.L);
     const int nv = visible_count(t, p.l, p.s, p.Nc);
     const int ns = (nv + kDecodeSplitKeys - 1) / kDecodeSplitKeys;
     const int jc = t / p.lp;
-    const size_t pb0 = ((size_t)b * p.Hkv + g) * p.n_split;
-    if (threadIdx.x < 16) {
-        const int hh = threadIdx.x;
+    const size_t bg = (size_t)b * p.Hkv + g;
+    const size_t pb0 = bg * p.n_split;
+    // per-head log-sum-exp over the splits: lane = head + 16 * q holds splits q + 4i
+    // (at most kDecodeMaxSplits splits, all loads issued together)
+    if (threadIdx.x < 64) {
+        constexpr int NI = kDecodeMaxSplits / 4;
+        const int hh = lane & 15, q = lane >> 4;
+        float mv[NI], lv[NI];
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            const int s0 = q + 4 * i;
+            mv[i] = s0 < ns ? p.part_m[(pb0 + s0) * 16 + hh] : -INFINITY;
+            lv[i] = s0 < ns ? p.part_l[(pb0 + s0) * 16 + hh] : 0.f;
+        }
         float M = -INFINITY;
-        for (int sp = 0; sp < ns; ++sp) M = fmaxf(M, p.part_m[(pb0 + sp) * 16 + hh]);
+#pragma unroll
+        for (int i = 0; i < NI; ++i) M = fmaxf(M, mv[i]);
+        M = col_max(M);
         float L = 0.f;
-        for (int sp = 0; sp < ns; ++sp) L += p.part_l[(pb0 + sp) * 16 + hh] * fast_exp2(p.part_m[(pb0 + sp) * 16 + hh] - M);
+#pragma unroll
+        for (int i = 0; i < NI; ++i)
+            if (mv[i] > -INFINITY) L += lv[i] * fast_exp2(mv[i] - M);
+        L = col_sum(L);
         const float lse2 = M + __log2f(L);
-        for (int sp = 0; sp < ns; ++sp) f[sp * 16 + hh] = fast_exp2(p.part_m[(pb0 + sp) * 16 + hh] - lse2);
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            const int s0 = q + 4 * i;
+            if (s0 < ns) {
+                const float w = (L > 0.f && mv[i] > -INFINITY) ? fast_exp2(mv[i] - lse2) : 0.f;
+                f[s0 * 16 + hh] = w;
+                p.cmp_w[(pb0 + s0) * 16 + hh] = w;
+            }
+        }
     }
     __syncthreads();
-    for (int idx = threadIdx.x; idx < 16 * DV; idx += 256) {
-        const int hh = idx / DV, d = idx % DV;
+    // block scores: compressed keys [ilo, ihi] overlap block j; at most two splits hold them
+    for (int j = threadIdx.x; j <= jc; j += 1024) {
+        const int num = j * p.lp - p.l + 1;
+        const int ilo = num > 0 ? (num + p.s - 1) / p.s : 0;
+        const int ihi = min((j * p.lp + p.lp - 1) / p.s, nv - 1);
         float acc = 0.f;
-        for (int sp = 0; sp < ns; ++sp) acc += f[sp * 16 + hh] * p.part_o[((pb0 + sp) * DV + d) * 16 + hh];
-        p.ocmp_ws[(((size_t)b * p.Hkv + g) * 16 + hh) * DV + d] = acc;
-    }
-    for (int j = threadIdx.x; j <= jc; j += 256) {
-        float acc = 0.f;
-        for (int sp = 0; sp < ns; ++sp) {
-            const int kbeg = sp * kDecodeSplitKeys;
-            const int jlo = (kbeg * p.s) / p.lp;
-            const int jhi = min(((kbeg + kDecodeSplitKeys - 1) * p.s + p.l - 1) / p.lp, p.n_slc - 1);
-            if (j < jlo || j > jhi) continue;
-            for (int hh = 0; hh < p.G; ++hh) acc += f[sp * 16 + hh] * p.part_a[((pb0 + sp) * 16 + hh) * p.jb + (j - jlo)];
+        if (ilo <= ihi) {
+            const int sa = ilo / kDecodeSplitKeys, sb = ihi / kDecodeSplitKeys;
+            for (int s0 = sa; s0 <= sb; ++s0) {
+                const int jlo = (s0 * kDecodeSplitKeys * p.s) / p.lp;
+                const float* pa = p.part_a + (pb0 + s0) * 16 * p.jb + (j - jlo);
+#pragma unroll
+                for (int hh = 0; hh < 16; ++hh)
+                    if (hh < p.G) acc += f[s0 * 16 + hh] * pa[hh * p.jb];
+            }
         }
         sc[j] = acc;
     }
     __syncthreads();
-    if (threadIdx.x < 64) {
-        select_blocks_wave(sc, jc, p.top_n, p.n_init, p.n_local, p.sel_ws + ((size_t)b * p.Hkv + g) * p.top_n);
-        if (p.sel_out)
-            select_blocks_wave(sc, jc, p.top_n, p.n_init, p.n_local, p.sel_out + ((size_t)b * p.Hkv + g) * p.top_n);
-    }
+    if (threadIdx.x < 64)
+        select_blocks_wave<NU>(sc, jc, p.top_n, p.n_init, p.n_local, p.sel_ws + bg * p.top_n,
+                               p.sel_out ? p.sel_out + bg * p.top_n : nullptr);
 }
 
 // ---------------------------------------------------------------------------
 template <int DK, int DV>
 __global__ __launch_bounds__(64) void decode_attn_kernel(DecodeParams p) {
     constexpr int NDS = DK / 32, NDT = DV / 16;
-    constexpr int VSTR = 32 + 8;
-    __shared__ __attribute__((aligned(16))) u16 vt[DV * VSTR];
+    constexpr int VSTR = DV + 16;
+    __shared__ __attribute__((aligned(16))) u16 vs[64 * VSTR];
     const int lane = threadIdx.x, li = lane & 15, lq = lane >> 4;
     const int it = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
     const int G = p.G, H = p.Hkv * G;
@@ -247,70 +301,67 @@ __global__ __launch_bounds__(64) void decode_attn_kernel(DecodeParams p) {
         const int base = (t0 & ~63) + 64 * (it - p.top_n);
         if (base <= t) { lo = max(t0, base); hi = min(t, base + 63); c0 = base; }
     }
-    if (hi < lo) {
+    if (hi < lo) {   // empty item: weight 0 in the merge, zero values (never stale memory)
         if (lq == 0) {
             p.att_m[ib * 16 + li] = -INFINITY;
             p.att_l[ib * 16 + li] = 0.f;
         }
+        for (int idx = lane; idx < DV * 16; idx += 64) p.att_o[ib * DV * 16 + idx] = 0.f;
         return;
     }
-    const bool head_ok = li < G;
-    const int h = g * G + min(li, G - 1);
     bf16x8 qf[NDS];
-    {
-        const u16* qp = p.q + ((size_t)b * H + h) * DK + lq * 8;
-#pragma unroll
-        for (int ds = 0; ds < NDS; ++ds) qf[ds] = head_ok ? ld8(qp + 32 * ds) : zero8();
-    }
+    load_q<DK>(p.q, b, H, g, G, qf);
     const u16* kg = p.K + ((size_t)b * p.Hkv + g) * (size_t)p.L * DK;
     const u16* vg = p.V + ((size_t)b * p.Hkv + g) * (size_t)p.L * DV;
     float m = -INFINITY, l = 0.f;
     f32x4 o[NDT];
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) o[dt] = zero4();
-    for (int key0 = c0; key0 <= hi; key0 += 32) {
-        f32x4 s0 = zero4(), s1 = zero4();
-        const u16* k0p = kg + (size_t)min(key0 + li, p.L - 1) * DK + lq * 8;
-        const u16* k1p = kg + (size_t)min(key0 + 16 + li, p.L - 1) * DK + lq * 8;
-#pragma unroll
-        for (int ds = 0; ds < NDS; ++ds) {
-            s0 = mfma16(ld8(k0p + 32 * ds), qf[ds], s0);
-            s1 = mfma16(ld8(k1p + 32 * ds), qf[ds], s1);
-        }
+    // a selection block spans l' / 64 pieces of 64 keys; a window piece is one
+    for (int key0 = c0; key0 <= hi; key0 += 64) {
+        KeyTile64<DK, DV> tile;
+        tile.load(kg, vg, key0, p.L);
+        f32x4 sacc[4];
+        tile.scores(qf, sacc);
+        __syncthreads();   // the previous piece's value reads are done
+        tile.template store_v<VSTR>(vs);
         __syncthreads();
-        stage_vt<DV, 32, VSTR>(vg, key0, p.L, vt);
-        __syncthreads();
-        float x[8];
+        float x[16];
         float tmax = -INFINITY;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int ka = key0 + 4 * lq + r, kb = key0 + 16 + 4 * lq + r;
-            x[r] = (ka >= lo && ka <= hi) ? s0[r] * p.scale_log2 : -INFINITY;
-            x[4 + r] = (kb >= lo && kb <= hi) ? s1[r] * p.scale_log2 : -INFINITY;
-            tmax = fmaxf(tmax, fmaxf(x[r], x[4 + r]));
-        }
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int key = key0 + 16 * kt + 4 * lq + r;
+                x[kt * 4 + r] = (key >= lo && key <= hi) ? sacc[kt][r] * p.scale_log2 : -INFINITY;
+                tmax = fmaxf(tmax, x[kt * 4 + r]);
+            }
         tmax = col_max(tmax);
         const float mnew = fmaxf(m, tmax);
-        if (mnew == -INFINITY) continue;
         const float alpha = fast_exp2(m - mnew);
-        f32x4 pa, pb;
+        f32x4 pv[4];
         float ps = 0.f;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            pa[r] = fast_exp2(x[r] - mnew);
-            pb[r] = fast_exp2(x[4 + r] - mnew);
-            ps += pa[r] + pb[r];
-        }
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                pv[kt][r] = fast_exp2(x[kt * 4 + r] - mnew);
+                ps += pv[kt][r];
+            }
         l = l * alpha + ps;
         m = mnew;
-        bf16x8 bh, bl;
-        pack_p_split(pa, pb, bh, bl);
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) {
-            const bf16x8 a = ld8(&vt[(16 * dt + li) * VSTR + lq * 8]);
-            o[dt] *= alpha;
-            o[dt] = mfma16(a, bh, o[dt]);
-            o[dt] = mfma16(a, bl, o[dt]);
+        for (int dt = 0; dt < NDT; ++dt) o[dt] *= alpha;
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            bf16x8 bh, bl;
+            pack_p_split(pv[2 * u], pv[2 * u + 1], bh, bl);
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt) {
+                const bf16x8 a = ld_vt_tr(vs, VSTR, 32 * u, 16 * dt);
+                o[dt] = mfma16(a, bh, o[dt]);
+                o[dt] = mfma16(a, bl, o[dt]);
+            }
         }
     }
     l = col_sum(l);
@@ -325,43 +376,94 @@ __global__ __launch_bounds__(64) void decode_attn_kernel(DecodeParams p) {
 }
 
 // ---------------------------------------------------------------------------
+// grid (DV / 16, Hkv, B): each thread owns one output (d, head) of the group; the
+// weights of the partial results are recomputed per workgroup (a few hundred values).
 template <int DV>
 __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p) {
-    const int g = blockIdx.x, b = blockIdx.y;
+    extern __shared__ float wsm[];       // [n_items][16] merge weights
+    const int g = blockIdx.y, b = blockIdx.z;
     const int G = p.G, H = p.Hkv * G;
-    const size_t ib0 = ((size_t)b * p.Hkv + g) * p.n_items;
-    for (int idx = threadIdx.x; idx < G * DV; idx += 256) {
-        const int hh = idx / DV, d = idx % DV;
-        const int h = g * G + hh;
-        float ob[2] = {0.f, 0.f};
-        for (int br = 0; br < 2; ++br) {
-            const int i0 = br == 0 ? 0 : p.top_n, i1 = br == 0 ? p.top_n : p.n_items;
-            float M = -INFINITY;
-            for (int i = i0; i < i1; ++i) M = fmaxf(M, p.att_m[(ib0 + i) * 16 + hh]);
-            if (M == -INFINITY) continue;
-            float L = 0.f, acc = 0.f;
-            for (int i = i0; i < i1; ++i) {
-                const float mi = p.att_m[(ib0 + i) * 16 + hh];
-                if (mi == -INFINITY) continue;
-                const float w = fast_exp2(mi - M);
-                L += w * p.att_l[(ib0 + i) * 16 + hh];
-                acc += w * p.att_o[((ib0 + i) * DV + d) * 16 + hh];
-            }
-            ob[br] = acc / L;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const size_t bg = (size_t)b * p.Hkv + g;
+    const size_t ib0 = bg * p.n_items;
+    // wave 0: selected-branch items, wave 1: window items; lane = head + 16 * q holds
+    // items i0 + q + 4i (at most kDecodeMaxItems per branch, loads issued together)
+    if (wave < 2) {
+        constexpr int NI = kDecodeMaxItems / 4;
+        const int hh = lane & 15, q = lane >> 4;
+        const int i0 = wave == 0 ? 0 : p.top_n, i1 = wave == 0 ? p.top_n : p.n_items;
+        float mv[NI], lv[NI];
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            const int it = i0 + q + 4 * i;
+            mv[i] = it < i1 ? p.att_m[(ib0 + it) * 16 + hh] : -INFINITY;
+            lv[i] = it < i1 ? p.att_l[(ib0 + it) * 16 + hh] : 0.f;
         }
-        float gc = 1.f, gs = 1.f, gw = 1.f;
-        if (p.gates) {
-            const float* z = p.gates + ((size_t)b * H + h) * 3;
-            gc = sigmoidf_(z[0]);
-            gs = sigmoidf_(z[1]);
-            gw = sigmoidf_(z[2]);
+        float M = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < NI; ++i) M = fmaxf(M, mv[i]);
+        M = col_max(M);
+        float L = 0.f;
+#pragma unroll
+        for (int i = 0; i < NI; ++i)
+            if (mv[i] > -INFINITY) L += fast_exp2(mv[i] - M) * lv[i];
+        L = col_sum(L);
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            const int it = i0 + q + 4 * i;
+            if (it < i1) wsm[it * 16 + hh] = (mv[i] > -INFINITY && L > 0.f) ? fast_exp2(mv[i] - M) / L : 0.f;
         }
-        float y = 0.f;
-        if (p.branches & 1) y += gc * p.ocmp_ws[(((size_t)b * p.Hkv + g) * 16 + hh) * DV + d];
-        if (p.branches & 2) y += gs * ob[0];
-        if (p.branches & 4) y += gw * ob[1];
-        p.O[((size_t)b * H + h) * DV + d] = f2bf(y);
     }
+    __syncthreads();
+    const int idx = blockIdx.x * 256 + threadIdx.x;   // (d, head) = (idx / 16, idx % 16)
+    const int hh = idx & 15, d = idx >> 4;
+    if (hh >= G) return;
+    const int t = query_pos(p.cache_len, b, p.L);
+    const int ns = (visible_count(t, p.l, p.s, p.Nc) + kDecodeSplitKeys - 1) / kDecodeSplitKeys;
+    float oc = 0.f, os = 0.f, ow = 0.f;
+    if (p.branches & 1) {
+        const size_t pb0 = bg * p.n_split;
+        for (int s0 = 0; s0 < ns; s0 += 8) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int sp = s0 + i;
+                const float w = sp < ns ? p.cmp_w[(pb0 + sp) * 16 + hh] : 0.f;
+                const float v = sp < ns ? p.part_o[(pb0 + sp) * DV * 16 + idx] : 0.f;
+                oc += w * v;
+            }
+        }
+    }
+    if (p.branches & 2) {
+        for (int i0 = 0; i0 < p.top_n; i0 += 8) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int it = i0 + i;
+                if (it < p.top_n) os += wsm[it * 16 + hh] * p.att_o[(ib0 + it) * DV * 16 + idx];
+            }
+        }
+    }
+    if (p.branches & 4) {
+        for (int i0 = p.top_n; i0 < p.n_items; i0 += 8) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int it = i0 + i;
+                if (it < p.n_items) ow += wsm[it * 16 + hh] * p.att_o[(ib0 + it) * DV * 16 + idx];
+            }
+        }
+    }
+    const int h = g * G + hh;
+    float gc = 1.f, gs = 1.f, gw = 1.f;
+    if (p.gates) {
+        const float* z = p.gates + ((size_t)b * H + h) * 3;
+        gc = sigmoidf_(z[0]);
+        gs = sigmoidf_(z[1]);
+        gw = sigmoidf_(z[2]);
+    }
+    float y = 0.f;
+    if (p.branches & 1) y += gc * oc;
+    if (p.branches & 2) y += gs * os;
+    if (p.branches & 4) y += gw * ow;
+    p.O[((size_t)b * H + h) * DV + d] = f2bf(y);
 }
 
 // ---------------------------------------------------------------------------
@@ -375,14 +477,18 @@ void allow_lds(K kernel, size_t bytes) {
 
 template <int DK, int DV>
 void decode_impl(const DecodeParams& p, hipStream_t st) {
-    const size_t lds1 = (size_t)4 * DV * (64 + 8) * 2 + 16 * kDecodeSplitKeys * 4 + 128 * 4;
+    const size_t tiles = (size_t)4 * 64 * (DV + 16) * 2;
+    const size_t reuse = (size_t)4 * DV * 16 * 4 + (size_t)16 * kPsumStride * 4;
+    const size_t lds1 = (tiles > reuse ? tiles : reuse) + 128 * 4;
     allow_lds(decode_cmp_kernel<DK, DV>, lds1);
     decode_cmp_kernel<DK, DV><<<dim3(p.n_split, p.Hkv, p.B), 256, lds1, st>>>(p);
     const size_t lds2 = ((size_t)p.n_split * 16 + p.n_slc) * 4;
-    allow_lds(decode_select_kernel<DV>, lds2);
-    decode_select_kernel<DV><<<dim3(p.Hkv, p.B), 256, lds2, st>>>(p);
+    NSA_NU_SWITCH(p.n_slc, {
+        allow_lds(decode_select_kernel<NU>, lds2);
+        decode_select_kernel<NU><<<dim3(p.Hkv, p.B), 1024, lds2, st>>>(p);
+    });
     decode_attn_kernel<DK, DV><<<dim3(p.n_items, p.Hkv, p.B), 64, 0, st>>>(p);
-    decode_merge_kernel<DV><<<dim3(p.Hkv, p.B), 256, 0, st>>>(p);
+    decode_merge_kernel<DV><<<dim3(DV / 16, p.Hkv, p.B), 256, (size_t)p.n_items * 16 * 4, st>>>(p);
 }
 }  // namespace
 

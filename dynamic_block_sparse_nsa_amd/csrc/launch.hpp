@@ -72,7 +72,7 @@ struct DecodeParams {
     float* part_o;             // [B,Hkv,n_split,DV,16]
     float* part_a;             // [B,Hkv,n_split,16,jb]
     int32_t* sel_ws;           // [B,Hkv,top_n]
-    float* ocmp_ws;            // [B,Hkv,16,DV]
+    float* cmp_w;              // [B,Hkv,n_split,16] weight 2^(m_split - lse) of each split
     float* att_m;              // [B,Hkv,n_items,16]
     float* att_l;              // [B,Hkv,n_items,16]
     float* att_o;              // [B,Hkv,n_items,DV,16]
@@ -81,6 +81,8 @@ struct DecodeParams {
     float scale_log2;
 };
 constexpr int kDecodeSplitKeys = 256;
+constexpr int kDecodeMaxSplits = 32;   // compressed keys per decode call <= 256 * 32
+constexpr int kDecodeMaxItems = 32;    // work items per branch (top_n <= 32, window <= 1920)
 int decode_jb(int l, int s, int lp);
 int decode_items(int top_n, int window);
 bool launch_decode(int DK, int DV, const DecodeParams& p, hipStream_t st);

@@ -383,6 +383,7 @@ __global__ __launch_bounds__(256, 2) void cmp_scores_kernel(SelParams p) {
 }
 
 // Selection from scores [B,T,Hkv,n_slc]: one wave per (b, t, g).
+template <int NU>
 __global__ __launch_bounds__(256) void select_from_scores_kernel(const float* __restrict__ scores,
                                                                  int32_t* __restrict__ sel, int T, int Hkv,
                                                                  int n_slc, int lp, int top_n, int n_init,
@@ -390,7 +391,7 @@ __global__ __launch_bounds__(256) void select_from_scores_kernel(const float* __
     const long row = (long)blockIdx.x * kWaves + (threadIdx.x >> 6);
     if (row >= rows) return;
     const int t = (int)((row / Hkv) % T);
-    select_blocks_wave(scores + row * n_slc, t / lp, top_n, n_init, n_local, sel + row * top_n);
+    select_blocks_wave<NU>(scores + row * n_slc, t / lp, top_n, n_init, n_local, sel + row * top_n);
 }
 
 // ---------------------------------------------------------------------------
@@ -469,8 +470,8 @@ void launch_select_from_scores(const float* scores, int32_t* sel, int B, int T, 
                                int top_n, int n_init, int n_local, hipStream_t st) {
     const long rows = (long)B * T * Hkv;
     const long blocks = (rows + kWaves - 1) / kWaves;
-    select_from_scores_kernel<<<(unsigned)blocks, 256, 0, st>>>(scores, sel, T, Hkv, n_slc, lp, top_n, n_init,
-                                                                n_local, rows);
+    NSA_NU_SWITCH(n_slc, select_from_scores_kernel<NU><<<(unsigned)blocks, 256, 0, st>>>(
+                             scores, sel, T, Hkv, n_slc, lp, top_n, n_init, n_local, rows));
 }
 
 }  // namespace nsa

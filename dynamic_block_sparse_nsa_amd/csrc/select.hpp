@@ -23,9 +23,23 @@ __device__ __forceinline__ uint32_t f2key(float x) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+template <int CTRL>
+__device__ __forceinline__ uint64_t max_dpp_u64(uint64_t v) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, CTRL, 0xF, 0xF, false);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), CTRL, 0xF, 0xF, false);
+    const uint64_t o = ((uint64_t)hi << 32) | lo;
+    return o > v ? o : v;
+}
+
+// Maximum over the 64 lanes (all lanes active): DPP moves inside each 16-lane row, then
+// two cross-row lane shuffles.
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+    v = max_dpp_u64<kDppQuadXor1>(v);
+    v = max_dpp_u64<kDppQuadXor2>(v);
+    v = max_dpp_u64<kDppRowHalfMirror>(v);
+    v = max_dpp_u64<kDppRowMirror>(v);
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
+    for (int off = 16; off < 64; off <<= 1) {
         const uint32_t lo = __shfl_xor((uint32_t)v, off);
         const uint32_t hi = __shfl_xor((uint32_t)(v >> 32), off);
         const uint64_t o = ((uint64_t)hi << 32) | lo;
@@ -35,9 +49,13 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
 }
 
 // One wave selects the blocks of one (token, group) from scores sc[0..jc] and writes
-// top_n entries (ascending, -1 padded) to out.  All 64 lanes must call it.
+// top_n entries (ascending, -1 padded) to out (and to out2 when it is not null).  All 64
+// lanes must call it; NU * 64 must cover jc + 1.  Each lane keeps its candidates
+// (blocks lane, lane + 64, ...) in registers as 64-bit keys score:~index, so one wave
+// maximum per pick yields the best score and, among equal scores, the lowest index.
+template <int NU>
 __device__ inline void select_blocks_wave(const float* sc, int jc, int top_n, int n_init, int n_local,
-                                   int32_t* __restrict__ out) {
+                                          int32_t* __restrict__ out, int32_t* __restrict__ out2 = nullptr) {
     const int lane = threadIdx.x & 63;
     const int n_elig = jc + 1;
     const int f_init = min(n_init, n_elig);
@@ -45,43 +63,63 @@ __device__ inline void select_blocks_wave(const float* sc, int jc, int top_n, in
     const int n_forced = f_init + (jc - f_loc_lo + 1) - max(0, f_init - f_loc_lo);
     const int m = min(top_n, n_elig);
     const int k = m - n_forced;
-    const int nu = (n_elig + 63) >> 6;
-    uint32_t picked = 0;  // bit u: candidate lane + 64u already taken
-
     auto is_forced = [&](int j) { return j < f_init || j >= f_loc_lo; };
-    auto local_best = [&]() -> uint64_t {
-        uint64_t best = 0;
-        for (int u = 0; u < nu; ++u) {
-            const int j = lane + 64 * u;
-            if (j < n_elig && !is_forced(j) && !((picked >> u) & 1u)) {
-                const uint64_t key = ((uint64_t)f2key(sc[j]) << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)j);
-                best = key > best ? key : best;
-            }
-        }
-        return best;
-    };
-    uint64_t mine = local_best();
+
+    uint64_t key[NU];
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+        const int j = lane + 64 * u;
+        const bool cand = j < n_elig && !is_forced(j);
+        key[u] = cand ? (((uint64_t)f2key(sc[j]) << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)j)) : 0ull;
+    }
+    uint32_t picked = 0;  // bit u: candidate lane + 64u taken
     for (int r = 0; r < k; ++r) {
-        const uint64_t win = wave_max_u64(mine);
+        uint64_t best = 0;
+#pragma unroll
+        for (int u = 0; u < NU; ++u) best = key[u] > best ? key[u] : best;
+        const uint64_t win = wave_max_u64(best);
         if (win == 0) break;  // no candidate left (cannot happen for a valid configuration)
         const int jw = (int)(0xFFFFFFFFu - (uint32_t)win);
         if ((jw & 63) == lane) {
+#pragma unroll
+            for (int u = 0; u < NU; ++u)
+                if (u == (jw >> 6)) key[u] = 0ull;
             picked |= 1u << (jw >> 6);
-            mine = local_best();
         }
     }
     // compaction in ascending block order
     int base = 0;
-    for (int u = 0; u < nu; ++u) {
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
         const int j = lane + 64 * u;
         const bool take = j < n_elig && (is_forced(j) || ((picked >> u) & 1u));
         const uint64_t mask = __ballot(take);
         const int pos = base + __popcll(mask & ((1ull << lane) - 1ull));
-        if (take) out[pos] = j;
+        if (take) {
+            out[pos] = j;
+            if (out2) out2[pos] = j;
+        }
         base += __popcll(mask);
     }
-    for (int c = base + lane; c < top_n; c += 64) out[c] = -1;
+    for (int c = base + lane; c < top_n; c += 64) {
+        out[c] = -1;
+        if (out2) out2[c] = -1;
+    }
 }
 
+// Candidates per lane for n_slc selection blocks (a power of two, at most 32).
+__host__ __device__ constexpr int select_nu(int n_slc) {
+    return n_slc <= 64 ? 1 : n_slc <= 128 ? 2 : n_slc <= 256 ? 4 : n_slc <= 512 ? 8 : n_slc <= 1024 ? 16 : 32;
+}
+
+#define NSA_NU_SWITCH(NSLC, ...)                                        \
+    switch (select_nu(NSLC)) {                                          \
+        case 1: { constexpr int NU = 1; __VA_ARGS__; } break;           \
+        case 2: { constexpr int NU = 2; __VA_ARGS__; } break;           \
+        case 4: { constexpr int NU = 4; __VA_ARGS__; } break;           \
+        case 8: { constexpr int NU = 8; __VA_ARGS__; } break;           \
+        case 16: { constexpr int NU = 16; __VA_ARGS__; } break;         \
+        default: { constexpr int NU = 32; __VA_ARGS__; } break;         \
+    }
 
 }  // namespace nsa
