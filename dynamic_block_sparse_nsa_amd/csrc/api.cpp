@@ -104,12 +104,16 @@ SelectWs select_ws(const Shape& s) {
     return w;
 }
 
-struct AttnWs { size_t vt, total; int tpad; };
+// K and V copied into MFMA fragment order, padded to a multiple of 64 keys
+struct AttnWs { size_t kf, vf, total; int tpad; };
 AttnWs attn_ws(const Shape& s) {
     AttnWs w{};
-    w.tpad = round_up(s.T, 64) + 64;  // see select_ws
-    w.vt = 0;
-    w.total = align_up((size_t)s.B * s.Hkv * s.dv * w.tpad * 2, 256);
+    w.tpad = round_up(s.T, 64);
+    const size_t bg = (size_t)s.B * s.Hkv;
+    size_t off = 0;
+    w.kf = off; off = align_up(off + bg * w.tpad * s.dk * 2, 256);
+    w.vf = off; off = align_up(off + bg * w.tpad * s.dv * 2, 256);
+    w.total = off;
     return w;
 }
 
@@ -291,12 +295,15 @@ nsa_status nsa_sparse_attn_fwd(const nsa_config* cfg, const void* Q, const void*
     if ((st = check_ws(ws, ws_bytes, w.total)) != NSA_OK) return st;
     const hipStream_t hs = as_stream(stream);
     using nsa::u16;
-    u16* vt = at<u16>(ws, w.vt);
-    nsa::launch_transpose_v(static_cast<const u16*>(V), vt, s.B * s.Hkv, s.T, s.dv, w.tpad, hs);
+    u16* kf = at<u16>(ws, w.kf);
+    u16* vf = at<u16>(ws, w.vf);
+    if (!nsa::launch_tile_kv(s.dk, s.dv, static_cast<const u16*>(K), static_cast<const u16*>(V), kf, vf, s.B * s.Hkv,
+                             s.T, w.tpad, hs))
+        return fail(NSA_ERR_UNSUPPORTED, "no layout kernel");
     nsa::AttnParams p{};
     p.Q = static_cast<const u16*>(Q);
-    p.K = static_cast<const u16*>(K);
-    p.Vt = vt;
+    p.Kf = kf;
+    p.Vf = vf;
     p.sel = sel_idx;
     p.o_cmp = o_cmp;
     p.gates = gate_logits;

@@ -42,10 +42,14 @@ void launch_select_from_scores(const float* scores, int32_t* sel, int B, int T, 
                                int top_n, int n_init, int n_local, hipStream_t st);
 
 // ---- selected + window attention, gated sum ----
+// K and V in MFMA fragment order (written by launch_tile_kv): for every 16-key group kt
+// and contraction step ds, the 64 lanes' K operands are 1 KB contiguous
+// (Kf[bg][kt][ds][lane][8]); for every 32-key chunk c and 16-wide value slice dt, the
+// lanes' V^T operands likewise (Vf[bg][c][dt][lane][8]).  Keys >= T are zero.
 struct AttnParams {
     const u16* Q;        // [B,T,H,DK]
-    const u16* K;        // [B,Hkv,T,DK]
-    const u16* Vt;       // [B,Hkv,DV,Tpad] transposed + permuted
+    const u16* Kf;       // [B,Hkv,Tpad/16,DK/32,64,8]
+    const u16* Vf;       // [B,Hkv,Tpad/32,DV/16,64,8]
     const int32_t* sel;  // [B,T,Hkv,top_n]
     const float* o_cmp;  // [B,T,H,DV] (branch CMP)
     const float* gates;  // [B,T,H,3] or null
@@ -54,6 +58,8 @@ struct AttnParams {
     float scale_log2;
 };
 bool launch_sparse_attn(int DK, int DV, const AttnParams& p, int B, hipStream_t st);
+bool launch_tile_kv(int DK, int DV, const u16* K, const u16* V, u16* Kf, u16* Vf, int BG, int T, int Tpad,
+                    hipStream_t st);
 
 // ---- decode ----
 struct DecodeParams {

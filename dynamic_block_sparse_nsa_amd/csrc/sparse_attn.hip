@@ -6,8 +6,13 @@
 // G query heads form the 16-wide MFMA column tile (the pages' NSA kernel packs the
 // group's heads into the matrix dimension so every KV tile feeds all of them at once).
 // Every attention product is key-major: S^T = K . Q^T on the MFMA, online softmax with
-// the running max and sum in registers (base-2), then O^T += V^T . P^T with V^T read
-// from a transposed, 32-key-permuted copy of V so both operands are 16-byte loads.
+// the running max and sum in registers (base-2), then O^T += V^T . P^T.
+//
+// K and V are first copied into MFMA fragment order (tile_kv_kernel): the operands a
+// wave needs for 16 keys x 32 dims of K, or 32 keys x 16 dims of V^T, are 1 KB of
+// contiguous memory in lane order.  Operand loads straight from row-major K would have
+// each lane read a different key row, so every 16-byte lane access costs the address
+// unit a cycle; in fragment order a wave's load is one contiguous, coalesced 1 KB.
 //
 // Phase B (per token, first): the selected blocks before the window range are contiguous
 //   64-token spans gathered by block index straight from memory in 32-key chunks, two
@@ -85,63 +90,57 @@ struct SoftmaxState {
     }
 };
 
-// Window-range tile staging: K rows [key0, key0+32) (clamped to T-1) and V^T columns
-// [key0, key0+32) of the transposed copy.
+// Fragment-order addressing (elements): K operands of the 16-key group kt, step ds;
+// V^T operands of the 32-key chunk c, value slice dt.  A lane reads 8 elements at +8*lane.
+template <int DK>
+__device__ __forceinline__ size_t kfrag(int kt, int ds) { return ((size_t)kt * (DK / 32) + ds) * 512; }
+template <int DV>
+__device__ __forceinline__ size_t vfrag(int c, int dt) { return ((size_t)c * (DV / 16) + dt) * 512; }
+
+// Window-range tile staging: the fragments of keys [key0, key0 + 32) copied to LDS in
+// the same order (a plain contiguous copy, 16 bytes per thread and step).
 template <int DK, int DV>
 struct WinTile {
-    static constexpr int KSTR = DK + 8;
-    static constexpr int VSTR = kChunk + 8;
-    static constexpr int KPR = DK / 8;              // uint4 per K row
-    static constexpr int NK = kChunk * KPR / 256;   // K uint4 per thread
-    static constexpr int NV = DV * (kChunk / 8) / 256;  // V uint4 per thread
-    static_assert(kChunk * KPR % 256 == 0 && DV * (kChunk / 8) % 256 == 0, "tile must split evenly");
+    static constexpr int KE = 2 * (DK / 32) * 512;   // K elements of a 32-key tile
+    static constexpr int VE = (DV / 16) * 512;       // V elements
+    static constexpr int NK = KE / 8 / 256;           // 16-byte pieces per thread
+    static constexpr int NV = VE / 8 / 256;
+    static_assert(KE % 2048 == 0 && VE % 2048 == 0, "tile must split evenly");
     u32x4 rk[NK], rv[NV];
 
-    __device__ __forceinline__ void load(const u16* kg, const u16* vtg, int key0, int T, int Tpad) {
+    __device__ __forceinline__ void load(const u16* kg, const u16* vg, int key0) {
+        const u16* ks = kg + kfrag<DK>(key0 / 16, 0);
+        const u16* vs = vg + vfrag<DV>(key0 / 32, 0);
 #pragma unroll
-        for (int i = 0; i < NK; ++i) {
-            const int idx = threadIdx.x + 256 * i;
-            const int row = idx / KPR, col = (idx % KPR) * 8;
-            rk[i] = *reinterpret_cast<const u32x4*>(kg + (size_t)min(key0 + row, T - 1) * DK + col);
-        }
+        for (int i = 0; i < NK; ++i) rk[i] = *reinterpret_cast<const u32x4*>(ks + (threadIdx.x + 256 * i) * 8);
 #pragma unroll
-        for (int i = 0; i < NV; ++i) {
-            const int idx = threadIdx.x + 256 * i;
-            const int row = idx / (kChunk / 8), col = (idx % (kChunk / 8)) * 8;
-            rv[i] = *reinterpret_cast<const u32x4*>(vtg + (size_t)row * Tpad + key0 + col);
-        }
+        for (int i = 0; i < NV; ++i) rv[i] = *reinterpret_cast<const u32x4*>(vs + (threadIdx.x + 256 * i) * 8);
     }
     __device__ __forceinline__ void store(u16* kb, u16* vb) const {
 #pragma unroll
-        for (int i = 0; i < NK; ++i) {
-            const int idx = threadIdx.x + 256 * i;
-            const int row = idx / KPR, col = (idx % KPR) * 8;
-            *reinterpret_cast<u32x4*>(&kb[row * KSTR + col]) = rk[i];
-        }
+        for (int i = 0; i < NK; ++i) *reinterpret_cast<u32x4*>(&kb[(threadIdx.x + 256 * i) * 8]) = rk[i];
 #pragma unroll
-        for (int i = 0; i < NV; ++i) {
-            const int idx = threadIdx.x + 256 * i;
-            const int row = idx / (kChunk / 8), col = (idx % (kChunk / 8)) * 8;
-            *reinterpret_cast<u32x4*>(&vb[row * VSTR + col]) = rv[i];
-        }
+        for (int i = 0; i < NV; ++i) *reinterpret_cast<u32x4*>(&vb[(threadIdx.x + 256 * i) * 8]) = rv[i];
     }
 };
 
 // One gathered 32-key chunk held in registers: K rows as the A operands of S^T = K.Q^T
-// and V^T columns as the A operands of O^T += V^T.P^T.
+// and V^T columns as the A operands of O^T += V^T.P^T (each a contiguous 1 KB load).
 template <int DK, int DV>
 struct GatherChunk {
     static constexpr int NDS = DK / 32, NDT = DV / 16;
     bf16x8 ka[NDS], kb[NDS], va[NDT];
-    __device__ __forceinline__ void load(const u16* kg, const u16* vtg, int key0, int T, int Tpad) {
-        const int lane = threadIdx.x & 63, li = lane & 15, lq = lane >> 4;
-        const u16* k0p = kg + (size_t)min(key0 + li, T - 1) * DK + lq * 8;
-        const u16* k1p = kg + (size_t)min(key0 + 16 + li, T - 1) * DK + lq * 8;
+    __device__ __forceinline__ void load(const u16* kg, const u16* vg, int key0) {
+        const int lane = threadIdx.x & 63;
+        const u16* k0 = kg + kfrag<DK>(key0 / 16, 0) + lane * 8;
+        const u16* v0 = vg + vfrag<DV>(key0 / 32, 0) + lane * 8;
 #pragma unroll
-        for (int ds = 0; ds < NDS; ++ds) { ka[ds] = ld8(k0p + 32 * ds); kb[ds] = ld8(k1p + 32 * ds); }
-        const u16* vp = vtg + (size_t)li * Tpad + key0 + lq * 8;
+        for (int ds = 0; ds < NDS; ++ds) {
+            ka[ds] = ld8(k0 + ds * 512);
+            kb[ds] = ld8(k0 + (NDS + ds) * 512);
+        }
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) va[dt] = ld8(vp + (size_t)16 * dt * Tpad);
+        for (int dt = 0; dt < NDT; ++dt) va[dt] = ld8(v0 + dt * 512);
     }
     __device__ __forceinline__ void scores(const bf16x8 (&qf)[NDS], f32x4& s0, f32x4& s1) const {
         s0 = zero4();
@@ -154,6 +153,46 @@ struct GatherChunk {
     }
 };
 
+// Copy of K and V into fragment order, one workgroup per 32-key chunk of one (b, g):
+// row-major tiles are staged in LDS with coalesced loads; K fragments are plain 16-byte
+// pieces of a row, V^T fragments come from the transposing LDS read.
+template <int DK, int DV>
+__global__ __launch_bounds__(256) void tile_kv_kernel(const u16* __restrict__ K, const u16* __restrict__ V,
+                                                      u16* __restrict__ Kf, u16* __restrict__ Vf, int T, int Tpad) {
+    constexpr int NDS = DK / 32, NDT = DV / 16;
+    constexpr int KSTR = DK + 8, VSTR = DV + 16;
+    __shared__ __attribute__((aligned(16))) u16 ks[32 * KSTR];
+    __shared__ __attribute__((aligned(16))) u16 vs[32 * VSTR];
+    const int c = blockIdx.x;
+    const size_t bg = blockIdx.y;
+    const u16* kg = K + bg * (size_t)T * DK;
+    const u16* vg = V + bg * (size_t)T * DV;
+    for (int idx = threadIdx.x; idx < 32 * DK / 8; idx += 256) {
+        const int r = idx / (DK / 8), col = (idx % (DK / 8)) * 8;
+        const int key = 32 * c + r;
+        const u32x4 v = key < T ? *reinterpret_cast<const u32x4*>(kg + (size_t)key * DK + col) : u32x4{0u, 0u, 0u, 0u};
+        *reinterpret_cast<u32x4*>(&ks[r * KSTR + col]) = v;
+    }
+    for (int idx = threadIdx.x; idx < 32 * DV / 8; idx += 256) {
+        const int r = idx / (DV / 8), col = (idx % (DV / 8)) * 8;
+        const int key = 32 * c + r;
+        const u32x4 v = key < T ? *reinterpret_cast<const u32x4*>(vg + (size_t)key * DV + col) : u32x4{0u, 0u, 0u, 0u};
+        *reinterpret_cast<u32x4*>(&vs[r * VSTR + col]) = v;
+    }
+    __syncthreads();
+    u16* kout = Kf + bg * (size_t)Tpad * DK + kfrag<DK>(2 * c, 0);
+    for (int idx = threadIdx.x; idx < 2 * NDS * 64; idx += 256) {
+        const int kk = idx / (NDS * 64), ds = (idx / 64) % NDS, ln = idx % 64;
+        const int li = ln & 15, lq = ln >> 4;
+        *reinterpret_cast<u32x4*>(kout + (size_t)idx * 8) =
+            *reinterpret_cast<const u32x4*>(&ks[(16 * kk + li) * KSTR + 32 * ds + 8 * lq]);
+    }
+    u16* vout = Vf + bg * (size_t)Tpad * DV + vfrag<DV>(c, 0);
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    for (int dt = wave; dt < NDT; dt += 4)
+        *reinterpret_cast<bf16x8*>(vout + (size_t)(dt * 64 + lane) * 8) = ld_vt_tr(vs, VSTR, 0, 16 * dt);
+}
+
 }  // namespace
 
 template <int DK, int DV>
@@ -161,8 +200,8 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnParams p) {
     constexpr int NDS = DK / 32;
     constexpr int NDT = DV / 16;
     using Tile = WinTile<DK, DV>;
-    __shared__ __attribute__((aligned(16))) u16 kbuf[2][kChunk * Tile::KSTR];
-    __shared__ __attribute__((aligned(16))) u16 vbuf[2][DV * Tile::VSTR];
+    __shared__ __attribute__((aligned(16))) u16 kbuf[2][Tile::KE];
+    __shared__ __attribute__((aligned(16))) u16 vbuf[2][Tile::VE];
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int li = lane & 15, lq = lane >> 4;
@@ -178,12 +217,12 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnParams p) {
 
     bf16x8 qf[NDS];
     {
-        const u16* qp = p.Q + (((size_t)b * T + tq) * H + h) * DK + lq * 8;
+        const u16* qp = p.Q + (((size_t)b * T + tq) * H + h) * DK;
 #pragma unroll
-        for (int ds = 0; ds < NDS; ++ds) qf[ds] = head_ok ? ld8(qp + 32 * ds) : zero8();
+        for (int ds = 0; ds < NDS; ++ds) qf[ds] = head_ok ? ld8(qp + 32 * ds + 8 * lq) : zero8();
     }
-    const u16* kg = p.K + ((size_t)b * p.Hkv + g) * (size_t)T * DK;
-    const u16* vtg = p.Vt + ((size_t)b * p.Hkv + g) * (size_t)DV * p.Tpad;
+    const u16* kg = p.Kf + ((size_t)b * p.Hkv + g) * (size_t)p.Tpad * DK;
+    const u16* vg = p.Vf + ((size_t)b * p.Hkv + g) * (size_t)p.Tpad * DV;
     const bool use_slc = (p.branches & 2) != 0, use_win = (p.branches & 4) != 0;
     // the token's block list, one entry per lane, read back with readlane (no memory
     // access on the dependency chain of a gather's address)
@@ -206,7 +245,9 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnParams p) {
 
     // ---- phase B: selected blocks before that range, gathered per token ----
     // Chunks are software-pipelined: the next chunk's loads are in flight while the
-    // current one is computed (two register buffers used alternately).
+    // current one is computed (two register buffers used alternately).  Every load is
+    // unconditional (a chunk index past the list is clamped to the last chunk and its
+    // keys masked), so each wait names only the chunk it consumes.
     if (active && use_slc) {
         int nb = 0;  // leading list entries outside the shared range (the list is ascending)
         for (; nb < p.top_n; ++nb) {
@@ -214,39 +255,31 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnParams p) {
             if (j < 0 || (nch > 0 && j * p.lp >= c_begin)) break;
         }
         const int cpb = p.lp / kChunk;
-        int c = 0, u = 0;
-        auto advance = [&](int& key0, int& start) -> bool {
-            while (c < nb) {
-                start = sl(c) * p.lp;
-                key0 = start + kChunk * u;
-                if (u < cpb && key0 <= t) { ++u; return true; }
-                ++c;
-                u = 0;
-            }
-            return false;
+        const int nck = nb * cpb;
+        auto ckey = [&](int c) {
+            const int cc = min(c, nck - 1);
+            return sl(cc / cpb) * p.lp + kChunk * (cc % cpb);
         };
-        GatherChunk<DK, DV> A, B;
-        int keyA = 0, startA = 0, keyB = 0, startB = 0;
-        bool hasA = advance(keyA, startA);
-        if (hasA) A.load(kg, vtg, keyA, T, p.Tpad);
-        while (hasA) {
-            const bool hasB = advance(keyB, startB);
-            if (hasB) B.load(kg, vtg, keyB, T, p.Tpad);
-            f32x4 s0, s1;
-            A.scores(qf, s0, s1);
-            slc.update(s0, s1, keyA, startA, t, p.scale_log2, A.va);
-            if (!hasB) break;
-            hasA = advance(keyA, startA);
-            if (hasA) A.load(kg, vtg, keyA, T, p.Tpad);
-            B.scores(qf, s0, s1);
-            slc.update(s0, s1, keyB, startB, t, p.scale_log2, B.va);
+        if (nck > 0) {
+            GatherChunk<DK, DV> A, B;
+            A.load(kg, vg, ckey(0));
+            for (int c = 0; c < nck; c += 2) {
+                const int kA = ckey(c), kB = ckey(c + 1);
+                B.load(kg, vg, kB);
+                f32x4 s0, s1;
+                A.scores(qf, s0, s1);
+                slc.update(s0, s1, kA, kA, t, p.scale_log2, A.va);
+                A.load(kg, vg, ckey(c + 2));
+                B.scores(qf, s0, s1);
+                slc.update(s0, s1, kB, c + 1 < nck ? kB : INT_MAX, t, p.scale_log2, B.va);
+            }
         }
     }
 
     // ---- phase A: the window range of the workgroup's tokens, shared through LDS ----
     Tile tile;
     if (nch > 0) {
-        tile.load(kg, vtg, c_begin, T, p.Tpad);
+        tile.load(kg, vg, c_begin);
         tile.store(kbuf[0], vbuf[0]);
     }
     __syncthreads();
@@ -254,7 +287,9 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnParams p) {
     for (int i = 0; i < nch; ++i) {
         const int key0 = c_begin + kChunk * i;
         const int buf = i & 1;
-        if (i + 1 < nch) tile.load(kg, vtg, key0 + kChunk, T, p.Tpad);
+        // prefetch of the next tile (the last iteration reloads its own tile into the
+        // unused buffer, so no load is conditional)
+        tile.load(kg, vg, key0 + (i + 1 < nch ? kChunk : 0));
         if (active) {
             const bool w_any = key0 + kChunk - 1 >= wlo_t && key0 <= t;
             const int jch = key0 / p.lp;
@@ -268,20 +303,21 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnParams p) {
             }
             if (w_any || s_any) {
                 f32x4 s0 = zero4(), s1 = zero4();
-                const u16* kb = kbuf[buf];
+                const u16* kb = kbuf[buf] + lane * 8;
 #pragma unroll
                 for (int ds = 0; ds < NDS; ++ds) {
-                    s0 = mfma16(ld8(&kb[li * Tile::KSTR + 32 * ds + lq * 8]), qf[ds], s0);
-                    s1 = mfma16(ld8(&kb[(16 + li) * Tile::KSTR + 32 * ds + lq * 8]), qf[ds], s1);
+                    s0 = mfma16(ld8(kb + ds * 512), qf[ds], s0);
+                    s1 = mfma16(ld8(kb + (NDS + ds) * 512), qf[ds], s1);
                 }
                 bf16x8 va[NDT];
 #pragma unroll
-                for (int dt = 0; dt < NDT; ++dt) va[dt] = ld8(&vbuf[buf][(16 * dt + li) * Tile::VSTR + lq * 8]);
+                for (int dt = 0; dt < NDT; ++dt) va[dt] = ld8(vbuf[buf] + (dt * 64 + lane) * 8);
                 if (w_any) win.update(s0, s1, key0, wlo_t, t, p.scale_log2, va);
                 if (s_any) slc.update(s0, s1, key0, jch * p.lp, t, p.scale_log2, va);
             }
         }
-        if (i + 1 < nch) tile.store(kbuf[buf ^ 1], vbuf[buf ^ 1]);
+        __builtin_amdgcn_sched_barrier(0);   // keep the staging stores after this tile's math
+        tile.store(kbuf[buf ^ 1], vbuf[buf ^ 1]);
         __syncthreads();
     }
 
@@ -316,6 +352,16 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnParams p) {
         const uint32_t w1 = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);
         *reinterpret_cast<uint2*>(p.O + row * DV + d0) = make_uint2(w0, w1);
     }
+}
+
+bool launch_tile_kv(int DK, int DV, const u16* K, const u16* V, u16* Kf, u16* Vf, int BG, int T, int Tpad,
+                    hipStream_t st) {
+    dim3 grid(Tpad / 32, BG);
+    if (DK == 192 && DV == 128) tile_kv_kernel<192, 128><<<grid, 256, 0, st>>>(K, V, Kf, Vf, T, Tpad);
+    else if (DK == 128 && DV == 128) tile_kv_kernel<128, 128><<<grid, 256, 0, st>>>(K, V, Kf, Vf, T, Tpad);
+    else if (DK == 64 && DV == 64) tile_kv_kernel<64, 64><<<grid, 256, 0, st>>>(K, V, Kf, Vf, T, Tpad);
+    else return false;
+    return true;
 }
 
 bool launch_sparse_attn(int DK, int DV, const AttnParams& p, int B, hipStream_t st) {

@@ -61,9 +61,12 @@ def test_workspace_sizes(name):
         rc, n = _ws(c, op)
         assert rc == 0
         assert n % 256 == 0
-    # the attention workspace holds the transposed values: B*Hkv*dv*(roundup(T,64)+64)*2 bytes
+    # the attention workspace holds K and V in MFMA fragment order, padded to 64 keys:
+    # B*Hkv*(d_k + d_v)*roundup(T,64)*2 bytes (each part 256-byte aligned)
     rc, n = _ws(c, ops.OP_SPARSE_ATTN)
-    assert n == c.batch * c.num_kv_heads * c.d_v * (-(-c.seq_len // 64) * 64 + 64) * 2
+    tp = -(-c.seq_len // 64) * 64
+    part = lambda d: -(-(c.batch * c.num_kv_heads * d * tp * 2) // 256) * 256
+    assert n == part(c.d_k) + part(c.d_v)
 
 
 @pytest.mark.parametrize("over,status", [
