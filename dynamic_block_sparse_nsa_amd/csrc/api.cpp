@@ -104,15 +104,36 @@ SelectWs select_ws(const Shape& s) {
     return w;
 }
 
-// K and V copied into MFMA fragment order, padded to a multiple of 64 keys
-struct AttnWs { size_t kf, vf, total; int tpad; };
+// One query head per KV head with only the selected branch (the MoBA configuration) runs
+// the block-major schedule of moba.hip.
+bool use_block_major(const Shape& s) { return s.G == 1 && s.br == NSA_BR_SLC; }
+
+// K and V copied into MFMA fragment order, padded with 64 zero keys past a multiple of 64; for the
+// block-major schedule also the bucket lists and the per-slot partial results.
+struct AttnWs {
+    size_t kf, vf, hist, bcnt, bstart, tstart, entries, pm, pl, po, total;
+    int tpad, n_chunk, n_bucket;
+};
 AttnWs attn_ws(const Shape& s) {
     AttnWs w{};
-    w.tpad = round_up(s.T, 64);
+    w.tpad = round_up(s.T, 64) + 64;   // a 64-key tile may start at any multiple of 32 below T
     const size_t bg = (size_t)s.B * s.Hkv;
     size_t off = 0;
     w.kf = off; off = align_up(off + bg * w.tpad * s.dk * 2, 256);
     w.vf = off; off = align_up(off + bg * w.tpad * s.dv * 2, 256);
+    if (use_block_major(s)) {
+        w.n_chunk = nsa::moba_n_chunk(s.T);
+        w.n_bucket = (int)(bg * s.n_slc);
+        const size_t rows = bg * s.T * s.n;   // (b, t, h, slot)
+        w.hist = off; off = align_up(off + bg * w.n_chunk * s.n_slc * 4, 256);
+        w.bcnt = off; off = align_up(off + (size_t)w.n_bucket * 4, 256);
+        w.bstart = off; off = align_up(off + (size_t)(w.n_bucket + 1) * 4, 256);
+        w.tstart = off; off = align_up(off + (size_t)(w.n_bucket + 1) * 4, 256);
+        w.entries = off; off = align_up(off + rows * 4, 256);
+        w.pm = off; off = align_up(off + rows * 4, 256);
+        w.pl = off; off = align_up(off + rows * 4, 256);
+        w.po = off; off = align_up(off + rows * s.dv * 4, 256);
+    }
     w.total = off;
     return w;
 }
@@ -300,6 +321,29 @@ nsa_status nsa_sparse_attn_fwd(const nsa_config* cfg, const void* Q, const void*
     if (!nsa::launch_tile_kv(s.dk, s.dv, static_cast<const u16*>(K), static_cast<const u16*>(V), kf, vf, s.B * s.Hkv,
                              s.T, w.tpad, hs))
         return fail(NSA_ERR_UNSUPPORTED, "no layout kernel");
+    if (use_block_major(s)) {
+        if ((long long)s.T >= (1LL << 26)) return fail(NSA_ERR_UNSUPPORTED, "sequence too long for the block lists");
+        nsa::MobaParams m{};
+        m.Q = static_cast<const u16*>(Q);
+        m.Kf = kf;
+        m.Vf = vf;
+        m.sel = sel_idx;
+        m.gates = gate_logits;
+        m.O = static_cast<u16*>(O);
+        m.hist = at<int>(ws, w.hist);
+        m.bucket_cnt = at<int>(ws, w.bcnt);
+        m.bucket_start = at<int>(ws, w.bstart);
+        m.tile_start = at<int>(ws, w.tstart);
+        m.entries = at<int>(ws, w.entries);
+        m.part_m = at<float>(ws, w.pm);
+        m.part_l = at<float>(ws, w.pl);
+        m.part_o = at<float>(ws, w.po);
+        m.B = s.B; m.T = s.T; m.Tpad = w.tpad; m.Hkv = s.Hkv; m.lp = s.lp; m.n_slc = s.n_slc; m.top_n = s.n;
+        m.n_chunk = w.n_chunk; m.n_bucket = w.n_bucket; m.n_own = nsa::moba_n_own(s.B * s.Hkv, s.n_slc, s.lp);
+        m.scale_log2 = s.scale * nsa::kLog2eHost;
+        if (!nsa::launch_moba_attn(s.dk, s.dv, m, hs)) return fail(NSA_ERR_UNSUPPORTED, "no block-major kernel");
+        return hip_check("sparse_attn");
+    }
     nsa::AttnParams p{};
     p.Q = static_cast<const u16*>(Q);
     p.Kf = kf;

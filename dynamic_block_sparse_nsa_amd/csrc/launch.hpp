@@ -61,6 +61,32 @@ bool launch_sparse_attn(int DK, int DV, const AttnParams& p, int B, hipStream_t 
 bool launch_tile_kv(int DK, int DV, const u16* K, const u16* V, u16* Kf, u16* Vf, int BG, int T, int Tpad,
                     hipStream_t st);
 
+// ---- G = 1 selected-only attention (MoBA): inverted, block-major schedule ----
+constexpr int kMobaChunk = 1024;   // tokens per histogram / scatter workgroup
+struct MobaParams {
+    const u16* Q;              // [B,T,H,DK] (H = Hkv)
+    const u16* Kf;             // fragment-order K (see AttnParams)
+    const u16* Vf;             // fragment-order V
+    const int32_t* sel;        // [B,T,Hkv,top_n]
+    const float* gates;        // [B,T,H,3] or null (slot 1 is used)
+    u16* O;                    // [B,T,H,DV]
+    // workspace
+    int* hist;                 // [B*Hkv, n_chunk, n_slc] counts, then prefix over chunks
+    int* bucket_cnt;           // [n_bucket]
+    int* bucket_start;         // [n_bucket + 1]
+    int* tile_start;           // [n_bucket + 1]
+    int* entries;              // [B*Hkv*T*top_n] (token << 5 | slot), grouped by bucket
+    float* part_m;             // [B,T,Hkv,top_n]
+    float* part_l;             // [B,T,Hkv,top_n]
+    float* part_o;             // [B,T,Hkv,top_n,DV]
+    int B, T, Tpad, Hkv, lp, n_slc, top_n, n_chunk, n_bucket, n_own;
+    float scale_log2;
+};
+int moba_n_chunk(int T);
+int moba_n_own(int BH, int n_slc, int lp);
+int moba_max_tiles(int BH, int T, int top_n, int n_slc);
+bool launch_moba_attn(int DK, int DV, const MobaParams& p, hipStream_t st);
+
 // ---- decode ----
 struct DecodeParams {
     const u16* q;              // [B,H,DK]

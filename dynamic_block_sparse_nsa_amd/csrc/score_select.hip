@@ -57,6 +57,33 @@ __device__ __forceinline__ void stage_rows(const u16* __restrict__ src, int k0, 
     }
 }
 
+// Rows [k0, k0+64) of a [N][D] bf16 matrix (rows clamped to N-1) held in registers
+// between a load issued before a tile's math and the LDS store after it.
+template <int D, int LSTR>
+struct RowTile {
+    static constexpr int PER_ROW = D / 8;
+    static constexpr int TOTAL = kKeysPerTile * PER_ROW;
+    static constexpr int ITERS = (TOTAL + 255) / 256;
+    u32x4 v[ITERS];
+    __device__ __forceinline__ void load(const u16* __restrict__ src, int k0, int N) {
+#pragma unroll
+        for (int i = 0; i < ITERS; ++i) {
+            const int idx = threadIdx.x + 256 * i;
+            const int row = idx / PER_ROW, col = (idx % PER_ROW) * 8;
+            if (TOTAL % 256 == 0 || idx < TOTAL)
+                v[i] = *reinterpret_cast<const u32x4*>(src + (size_t)min(k0 + row, N - 1) * D + col);
+        }
+    }
+    __device__ __forceinline__ void store(u16* dst) const {
+#pragma unroll
+        for (int i = 0; i < ITERS; ++i) {
+            const int idx = threadIdx.x + 256 * i;
+            const int row = idx / PER_ROW, col = (idx % PER_ROW) * 8;
+            if (TOTAL % 256 == 0 || idx < TOTAL) *reinterpret_cast<u32x4*>(&dst[row * LSTR + col]) = v[i];
+        }
+    }
+};
+
 // Copy columns [k0, k0+64) of a [D][Npad] bf16 matrix (transposed values) into LDS rows
 // of stride LSTR.  All global loads are issued before the first LDS store.
 template <int D, int LSTR>
@@ -86,7 +113,7 @@ __device__ __forceinline__ void stage_cols(const u16* __restrict__ src, int k0, 
 // pass 1: per query row, m = max_i x_i and l = sum_i 2^(x_i - m), x = scale*log2(e)*q.k
 // ---------------------------------------------------------------------------
 template <int DK, int G>
-__global__ __launch_bounds__(256) void cmp_stats_kernel(const u16* __restrict__ Q, const u16* __restrict__ Kc,
+__global__ __launch_bounds__(256, 3) void cmp_stats_kernel(const u16* __restrict__ Q, const u16* __restrict__ Kc,
                                                         float* __restrict__ stat_m, float* __restrict__ stat_il,
                                                         float* __restrict__ lse_out, int T, int Hkv, int N, int l,
                                                         int s, float scale_log2) {
@@ -123,10 +150,14 @@ __global__ __launch_bounds__(256) void cmp_stats_kernel(const u16* __restrict__ 
 #pragma unroll
     for (int c = 0; c < NQ; ++c) { m[c] = -INFINITY; lsum[c] = 0.f; }
 
+    // the next tile's rows are in flight (registers) while this tile is computed
+    RowTile<DK, KSTR> pre;
+    pre.load(kbase, 0, N);
     for (int k0 = 0; k0 < nv_max; k0 += kKeysPerTile) {
         __syncthreads();
-        stage_rows<DK, KSTR>(kbase, k0, N, ks);
+        pre.store(ks);
         __syncthreads();
+        pre.load(kbase, k0 + kKeysPerTile, N);
         f32x4 sacc[4][NQ];
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt)

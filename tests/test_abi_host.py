@@ -61,12 +61,20 @@ def test_workspace_sizes(name):
         rc, n = _ws(c, op)
         assert rc == 0
         assert n % 256 == 0
-    # the attention workspace holds K and V in MFMA fragment order, padded to 64 keys:
-    # B*Hkv*(d_k + d_v)*roundup(T,64)*2 bytes (each part 256-byte aligned)
+    # the attention workspace holds K and V in MFMA fragment order, padded:
+    # B*Hkv*(d_k + d_v)*(roundup(T,64)+64)*2 bytes (each part 256-byte aligned)
+    # (G = 1 with only the selected branch adds the block lists and per-slot partials)
     rc, n = _ws(c, ops.OP_SPARSE_ATTN)
-    tp = -(-c.seq_len // 64) * 64
-    part = lambda d: -(-(c.batch * c.num_kv_heads * d * tp * 2) // 256) * 256
-    assert n == part(c.d_k) + part(c.d_v)
+    tp = -(-c.seq_len // 64) * 64 + 64
+    al = lambda x: -(-x // 256) * 256
+    bg = c.batch * c.num_kv_heads
+    want = al(bg * c.d_k * tp * 2) + al(bg * c.d_v * tp * 2)
+    if c.heads_per_group == 1 and c.branches == 2:
+        n_chunk = -(-c.seq_len // 1024)
+        rows = bg * c.seq_len * c.top_n
+        want += (al(bg * n_chunk * c.n_slc * 4) + al(bg * c.n_slc * 4) + 2 * al((bg * c.n_slc + 1) * 4)
+                 + 3 * al(rows * 4) + al(rows * c.d_v * 4))
+    assert n == want
 
 
 @pytest.mark.parametrize("over,status", [

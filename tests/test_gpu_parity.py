@@ -12,7 +12,8 @@ import torch
 import oracle
 from oracle import pipeline
 from dynamic_block_sparse_nsa_amd import inputs, ops
-from dynamic_block_sparse_nsa_amd.configs import TINY, P8K, P64K, DECODE, MOBA, BR_SLC, BR_WIN
+from dynamic_block_sparse_nsa_amd.configs import (TINY, P8K, P64K, DECODE, MOBA, BR_SLC, BR_WIN, PHI_LINEAR,
+                                                  SCORE_CMP_OVERLAP)
 from nsa_testlib import (GAP, bf16_dev_to_f64, check_close, check_selection, check_ulp, dev_bf16, dev_f32, dev_i32,
                          f64_to_dev_bf16, sample_rows)
 
@@ -286,6 +287,35 @@ def test_moba(T):
     torch.cuda.synchronize()
     at = oracle.attend(cfg, f64(inp["q"][0, rows]), rows, f64(inp["k"][0]), f64(inp["v"][0]), lists[0, rows])
     check_close(bf16_dev_to_f64(out)[0, rows], at["out"], f"moba{T} output")
+
+
+@pytest.mark.parametrize("case", ["b2_lp64_gated", "lp128_own_optional"])
+def test_block_major_all_rows(case):
+    """G = 1 with only the selected branch runs the block-major schedule (per-block query
+    lists, per-slot partials, merge); every row of a ragged batch is checked."""
+    if case == "b2_lp64_gated":
+        cfg = MOBA.replace(name=case, batch=2, seq_len=1000, num_kv_heads=3, cmp_block=64, cmp_stride=64,
+                           slc_block=64, top_n=3, seed=21)
+    else:   # the own block is not forced, so some lists lack it (overlap scoring allows n_local = 0)
+        cfg = MOBA.replace(name=case, batch=1, seq_len=1500, num_kv_heads=2, cmp_block=128, cmp_stride=128,
+                           slc_block=128, top_n=4, n_local=0, n_init=1, phi=PHI_LINEAR,
+                           score_mode=SCORE_CMP_OVERLAP, seed=22)
+    announce(f"block-major {case}")
+    inp = inputs.prefill_inputs(cfg)
+    lists = inputs.block_lists(cfg, seed=600)
+    gates = None
+    if case == "b2_lp64_gated":
+        gates = np.random.Generator(np.random.PCG64(7)).standard_normal(
+            (cfg.batch, cfg.seq_len, cfg.num_heads, 3)).astype(np.float32)
+    out = ops.sparse_attn_fwd(cfg, dev_bf16(inp["q"]), dev_bf16(inp["k"]), dev_bf16(inp["v"]), dev_i32(lists),
+                              None, None if gates is None else dev_f32(gates))
+    torch.cuda.synchronize()
+    got = bf16_dev_to_f64(out)
+    rows = np.arange(cfg.seq_len, dtype=np.int32)
+    for b in range(cfg.batch):
+        at = oracle.attend(cfg, f64(inp["q"][b]), rows, f64(inp["k"][b]), f64(inp["v"][b]), lists[b],
+                           gates=None if gates is None else gates[b])
+        check_close(got[b], at["out"], f"{case} batch {b} output")
 
 
 # ---------------------------------------------------------------------------
