@@ -86,18 +86,18 @@ CompressWs compress_ws(const Shape& s) {
     return w;
 }
 
-struct SelectWs { size_t m, il, vct, scores, total; int npad; };
+// compressed keys and values in fragment order with the values' scaling (mode 0), block scores
+struct SelectWs { size_t kf, vf, vmax, vexp, scores, total; int npad; };
 SelectWs select_ws(const Shape& s) {
     SelectWs w{};
     size_t off = 0;
-    const size_t rows = (size_t)s.B * s.T * s.H;
-    // +64 keys: keeps the transposed row stride off a power of two (rows of one tile
-    // would otherwise fall on the same memory channel)
-    w.npad = round_up(std::max(s.n_cmp, 1), 64) + 64;
+    w.npad = round_up(std::max(s.n_cmp, 1), 64);
     if (s.mode == NSA_SCORE_CMP_OVERLAP) {
-        w.m = off; off = align_up(off + rows * 4, 256);
-        w.il = off; off = align_up(off + rows * 4, 256);
-        w.vct = off; off = align_up(off + (size_t)s.B * s.Hkv * s.dv * w.npad * 2, 256);
+        const size_t bg = (size_t)s.B * s.Hkv;
+        w.kf = off; off = align_up(off + bg * w.npad * s.dk * 2, 256);
+        w.vf = off; off = align_up(off + bg * w.npad * s.dv * 2, 256);
+        w.vmax = off; off = align_up(off + bg * nsa::cmp_vmax_parts() * 4, 256);
+        w.vexp = off; off = align_up(off + bg * 4, 256);
     }
     w.scores = off; off = align_up(off + (size_t)s.B * s.T * s.Hkv * s.n_slc * 4, 256);
     w.total = off;
@@ -248,9 +248,8 @@ nsa_status nsa_score_select(const nsa_config* cfg, const void* Q, const void* K_
         return fail(NSA_ERR_SHAPE, "MEAN_DOT mode produces no lse_cmp / o_cmp");
     const bool with_o = o_cmp != nullptr;
     if (with_o && !V_cmp) return fail(NSA_ERR_NULL, "o_cmp needs V_cmp");
-    const int nq = nsa::score_select_nq(s.G, s.mode);
-    const size_t lds = nsa::score_select_lds_bytes(s.dk, s.dv, s.G, s.mode, nq, with_o, s.n_slc);
-    if (lds > 160 * 1024) return fail(NSA_ERR_UNSUPPORTED, "tile too large for one workgroup's LDS");
+    if (s.mode == NSA_SCORE_CMP_OVERLAP && nsa::cmp_attn_lds_bytes(s.dk, s.dv, s.G, with_o) > 160 * 1024)
+        return fail(NSA_ERR_UNSUPPORTED, "tile too large for one workgroup's LDS");
     if (s.mode == NSA_SCORE_CMP_OVERLAP) {
         const int R = s.lp / s.s, L = s.l / s.s;
         if (64 % R != 0 || L > 64)
@@ -264,27 +263,26 @@ nsa_status nsa_score_select(const nsa_config* cfg, const void* Q, const void* K_
     p.Q = static_cast<const u16*>(Q);
     p.Kc = static_cast<const u16*>(K_cmp);
     p.scores = at<float>(ws, w.scores);
-    p.T = s.T; p.Hkv = s.Hkv; p.N = s.n_cmp; p.l = s.l; p.s = s.s; p.lp = s.lp;
-    p.n_slc = s.n_slc; p.top_n = s.n; p.n_init = s.n_init; p.n_local = s.n_local;
+    p.B = s.B; p.T = s.T; p.Hkv = s.Hkv; p.N = s.n_cmp; p.Npad = w.npad; p.l = s.l; p.s = s.s; p.lp = s.lp;
+    p.n_slc = s.n_slc;
     p.scale_log2 = s.scale * nsa::kLog2eHost;
     if (s.mode == NSA_SCORE_CMP_OVERLAP) {
-        float* m = at<float>(ws, w.m);
-        float* il = at<float>(ws, w.il);
-        if (!nsa::launch_cmp_stats(p.Q, p.Kc, m, il, lse_cmp, s.B, s.T, s.Hkv, s.G, s.dk, s.n_cmp, s.l, s.s,
-                                   p.scale_log2, hs))
-            return fail(NSA_ERR_UNSUPPORTED, "no statistics kernel for this shape");
-        p.stat_m = m;
-        p.stat_il = il;
-        if (with_o) {
-            u16* vct = at<u16>(ws, w.vct);
-            nsa::launch_transpose_v(static_cast<const u16*>(V_cmp), vct, s.B * s.Hkv, s.n_cmp, s.dv, w.npad, hs);
-            p.Vct = vct;
-            p.Npad = w.npad;
-            p.o_cmp = o_cmp;
-        }
-    }
-    if (!nsa::launch_cmp_scores(s.mode, with_o, s.dk, s.dv, s.G, p, s.B, hs))
+        u16* kf = at<u16>(ws, w.kf);
+        u16* vf = with_o ? at<u16>(ws, w.vf) : nullptr;
+        if (!nsa::launch_tile_cmp(s.dk, s.dv, p.Kc, with_o ? static_cast<const u16*>(V_cmp) : nullptr,
+                                  at<uint32_t>(ws, w.vmax), at<int>(ws, w.vexp), kf, vf, s.B * s.Hkv, s.n_cmp, w.npad,
+                                  hs))
+            return fail(NSA_ERR_UNSUPPORTED, "no layout kernel for this shape");
+        p.Kf = kf;
+        p.Vf = vf;
+        p.vexp = at<int>(ws, w.vexp);
+        p.lse = lse_cmp;
+        p.o_cmp = o_cmp;
+        if (!nsa::launch_cmp_attn(with_o, s.dk, s.dv, s.G, p, hs))
+            return fail(NSA_ERR_UNSUPPORTED, "no compressed-attention kernel for this shape");
+    } else if (!nsa::launch_mean_scores(s.dk, s.G, p, hs)) {
         return fail(NSA_ERR_UNSUPPORTED, "no score kernel for this shape");
+    }
     nsa::launch_select_from_scores(p.scores, sel_idx, s.B, s.T, s.Hkv, s.n_slc, s.lp, s.n, s.n_init, s.n_local, hs);
     return hip_check("score_select");
 }

@@ -30,6 +30,12 @@ __device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const 
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// fp16 variant (P in fp16, 2^-11 relative rounding, against fp16 values)
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ f32x4 mfma16h(const f16x8& a, const f16x8& b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
 // 16-byte global/LDS load of 8 bf16 values (address must be 16-byte aligned).
@@ -51,6 +57,21 @@ __device__ __forceinline__ bf16x8 pack_p(const f32x4& a, const f32x4& b) {
     r[4] = static_cast<__bf16>(b[0]); r[5] = static_cast<__bf16>(b[1]);
     r[6] = static_cast<__bf16>(b[2]); r[7] = static_cast<__bf16>(b[3]);
     return r;
+}
+
+// P^T operand in fp16 (round to nearest even), same slot order as pack_p.
+__device__ __forceinline__ f16x8 pack_p_h(const f32x4& a, const f32x4& b) {
+    f16x8 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        r[i] = static_cast<_Float16>(a[i]);
+        r[4 + i] = static_cast<_Float16>(b[i]);
+    }
+    return r;
+}
+
+__device__ __forceinline__ f16x8 ld8h(const u16* p) {
+    return __builtin_bit_cast(f16x8, *reinterpret_cast<const uint4*>(p));
 }
 
 // Split P^T into bf16 high and low parts (p ~= hi + lo to about 2^-17 relative), so that

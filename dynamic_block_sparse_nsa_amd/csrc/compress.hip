@@ -95,31 +95,6 @@ __global__ void compress_mean_kernel(const u16* __restrict__ X, u16* __restrict_
 }
 
 // ---------------------------------------------------------------------------
-// Value transpose: X [BG][n][d] -> Xt [BG][d][n_pad], key k of each 32-group stored at
-// vt_pos(k); columns past n are zero (so masked-out keys contribute 0 * 0).
-// Grid (n_pad/64, ceil(d/64), BG).
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void transpose_v_kernel(const u16* __restrict__ X, u16* __restrict__ Xt,
-                                                          int n, int d, int n_pad) {
-    __shared__ u16 tile[64][65];
-    const int bg = blockIdx.z;
-    const int t0 = blockIdx.x * 64, e0 = blockIdx.y * 64;
-    const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-    const u16* src = X + (size_t)bg * n * d;
-    for (int r = ty; r < 64; r += 4) {
-        const int t = t0 + r, e = e0 + tx;
-        tile[r][tx] = (t < n && e < d) ? src[(size_t)t * d + e] : (u16)0;
-    }
-    __syncthreads();
-    u16* dst = Xt + (size_t)bg * d * n_pad;
-    for (int r = ty; r < 64; r += 4) {
-        const int e = e0 + r;
-        const int t = t0 + tx;
-        if (e < d) dst[(size_t)e * n_pad + (t & ~31) + vt_pos(t & 31)] = tile[tx][r];
-    }
-}
-
-// ---------------------------------------------------------------------------
 // host launchers
 // ---------------------------------------------------------------------------
 void launch_transpose_w(const u16* W, u16* Wt, int KD, int dout, hipStream_t st) {
@@ -140,11 +115,6 @@ void launch_compress_linear(const u16* X, const u16* Wt, const float* bias, u16*
 void launch_compress_mean(const u16* X, u16* out, int BG, int T, int d, int l, int s, int N, hipStream_t st) {
     dim3 grid(N, BG);
     compress_mean_kernel<<<grid, d, 0, st>>>(X, out, T, d, l, s, N);
-}
-
-void launch_transpose_v(const u16* X, u16* Xt, int BG, int n, int d, int n_pad, hipStream_t st) {
-    dim3 grid(n_pad / 64, (d + 63) / 64, BG);
-    transpose_v_kernel<<<grid, 256, 0, st>>>(X, Xt, n, d, n_pad);
 }
 
 }  // namespace nsa

@@ -19,25 +19,26 @@ void launch_pe_bias(const u16* pe, const u16* Wt, float* bias, int KD, int dout,
 void launch_compress_linear(const u16* X, const u16* Wt, const float* bias, u16* out, int BG, int T, int d,
                             int dout, int l, int s, int N, hipStream_t st);
 void launch_compress_mean(const u16* X, u16* out, int BG, int T, int d, int l, int s, int N, hipStream_t st);
-void launch_transpose_v(const u16* X, u16* Xt, int BG, int n, int d, int n_pad, hipStream_t st);
 
 // ---- compressed attention + selection ----
 struct SelParams {
     const u16* Q;          // [B,T,H,DK]
-    const u16* Kc;         // [B,Hkv,N,DK]
-    const u16* Vct;        // [B,Hkv,DV,Npad] transposed + permuted (mode 0 with o_cmp)
-    const float* stat_m;   // [B,T,H] running max (base 2) from the statistics pass
-    const float* stat_il;  // [B,T,H] 1 / sum
+    const u16* Kc;         // [B,Hkv,N,DK] (mode 1)
+    const u16* Kf;         // compressed keys in fragment order, Npad keys per unit (mode 0)
+    const u16* Vf;         // compressed values in fragment order, fp16 scaled by 2^-vexp (mode 0 with o_cmp)
+    const int* vexp;       // [B*Hkv] scaling exponent of Vf
+    float* lse;            // [B,T,H] natural-log LSE of the compressed branch, or null
     float* o_cmp;          // [B,T,H,DV] or null
     float* scores;         // [B,T,Hkv,n_slc] block scores (workspace)
-    int T, Hkv, N, Npad, l, s, lp, n_slc, top_n, n_init, n_local;
+    int B, T, Hkv, N, Npad, l, s, lp, n_slc;
     float scale_log2;
 };
-bool launch_cmp_stats(const u16* Q, const u16* Kc, float* m, float* il, float* lse, int B, int T, int Hkv, int G,
-                      int DK, int N, int l, int s, float sl2, hipStream_t st);
-bool launch_cmp_scores(int mode, bool with_o, int DK, int DV, int G, const SelParams& p, int B, hipStream_t st);
-size_t score_select_lds_bytes(int DK, int DV, int G, int mode, int NQ, bool with_o, int n_slc);
-int score_select_nq(int G, int mode);
+int cmp_vmax_parts();
+bool launch_tile_cmp(int DK, int DV, const u16* K, const u16* V, uint32_t* vmax_part, int* vexp, u16* Kf, u16* Vf,
+                     int BG, int N, int Npad, hipStream_t st);
+bool launch_cmp_attn(bool with_o, int DK, int DV, int G, const SelParams& p, hipStream_t st);
+size_t cmp_attn_lds_bytes(int DK, int DV, int G, bool with_o);
+bool launch_mean_scores(int DK, int G, const SelParams& p, hipStream_t st);
 void launch_select_from_scores(const float* scores, int32_t* sel, int B, int T, int Hkv, int n_slc, int lp,
                                int top_n, int n_init, int n_local, hipStream_t st);
 

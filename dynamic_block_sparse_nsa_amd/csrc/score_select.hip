@@ -9,16 +9,18 @@
 //
 // Kernels (per KV group; a workgroup owns 128 query rows = 128/G tokens, each wave two
 // 16-column MFMA tiles laid out by QMap so a token's heads share lanes and tiles):
-//   cmp_stats_kernel   pass 1: S^T = K_cmp . Q^T, 64 compressed keys per LDS tile; running
-//                      max m and sum l per query row (base-2 exponentials).
-//   cmp_scores_kernel  pass 2: recompute S^T; p = 2^(x - m) / l (the exact normalized
-//                      probabilities, so nothing is rescaled); o_cmp += V_cmp^T . P^T on
-//                      the MFMA (P split into bf16 high and low parts); sums over the
-//                      group's heads in fp32 (in-lane + DPP) into a per-key ring in LDS;
-//                      each block's score (sum over its overlapping compressed blocks,
-//                      ascending key order) is written to the score workspace once the
-//                      tile holding its last key is done.  Mode 1 writes the head-summed
-//                      raw dot products with the mean keys directly.
+//   cmp_attn_kernel    sweep 1: S^T = K_cmp . Q^T over 64-key tiles, per-lane running max
+//                      and sum, combined into the log-sum-exp b (base 2) of every query row.
+//                      Sweep 2: the same S^T again; p = 2^(x - b) are the normalized
+//                      probabilities (nothing is rescaled afterwards); o_cmp += V_cmp^T.P^T
+//                      on the MFMA; p summed over the group's heads in fp32 (in-lane + DPP)
+//                      into a per-token ring in LDS; one tile later, every selection block
+//                      whose last compressed key is complete gets its score (sum over its
+//                      overlapping compressed blocks, ascending key order) written to the
+//                      score workspace.  The compressed keys and values are read in MFMA
+//                      fragment order (tile_cmp_kernel), so a tile is one contiguous span
+//                      copied to LDS through registers while the previous tile is computed.
+//   mean_scores_kernel mode 1: head-summed raw dot products with the mean keys.
 //   select_kernel      one wave per (token, group): the shared top-n from the scores.
 // Block j of l' tokens takes compressed blocks i with j*R - L + 1 <= i <= j*R + R - 1,
 // R = l'/s and L = l/s, i.e. every compressed block whose token span meets block j.
@@ -32,102 +34,206 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kKeysPerTile = 64;
-constexpr int kRing = 2 * kKeysPerTile;  // per-token head-sum ring: this tile and the previous one
+constexpr int kRing = 4 * kKeysPerTile;  // per-token ring: the tile being written and the two before it
+constexpr int kVmaxParts = 64;           // partial maxima of |V_cmp| per unit
 
-// Copy rows [k0, k0+64) of a [N][D] bf16 matrix (rows clamped to N-1) into LDS rows of
+// Workgroup -> (unit, tile) with unit = b * Hkv + g and tile 0 holding the last tokens.
+// Workgroups are dispatched to the 8 XCDs round-robin (workgroup L runs on XCD L % 8).
+// When the units split evenly over the XCDs, every XCD serves one unit (or a fixed set),
+// so the unit's compressed keys and values stay in that XCD's L2; within a unit the
+// longest rows go first.
+__device__ __forceinline__ bool map_tile(int L, int U, int n_tiles, int& u, int& it) {
+    const int xcd = L & 7, r = L >> 3;
+    if (8 % U == 0) {
+        const int xpu = 8 / U;   // XCDs per unit, tiles interleaved between them
+        u = xcd / xpu;
+        it = r * xpu + xcd % xpu;
+    } else if (U % 8 == 0) {
+        u = xcd + 8 * (r / n_tiles);
+        it = r % n_tiles;
+    } else {
+        u = L % U;
+        it = L / U;
+    }
+    return u < U && it < n_tiles;
+}
+
+int map_grid(int U, int n_tiles) {
+    if (8 % U == 0) return 8 * ((n_tiles + 8 / U - 1) / (8 / U));
+    return U * n_tiles;
+}
+
+// A 64-key tile of fragment-order K (and V) held in registers between its load (issued
+// before the previous tile's math) and its store to LDS (after it).
+template <int KE, int VE>
+struct FragStage {
+    static constexpr int NK = KE / 2048, NV = VE / 2048;   // 16-byte pieces per thread
+    u32x4 rk[NK], rv[NV > 0 ? NV : 1];
+    __device__ __forceinline__ void load_k(const u16* __restrict__ k) {
+#pragma unroll
+        for (int i = 0; i < NK; ++i) rk[i] = *reinterpret_cast<const u32x4*>(k + (threadIdx.x + 256 * i) * 8);
+    }
+    __device__ __forceinline__ void load_v(const u16* __restrict__ v) {
+#pragma unroll
+        for (int i = 0; i < NV; ++i) rv[i] = *reinterpret_cast<const u32x4*>(v + (threadIdx.x + 256 * i) * 8);
+    }
+    __device__ __forceinline__ void store_k(u16* kb) const {
+#pragma unroll
+        for (int i = 0; i < NK; ++i) *reinterpret_cast<u32x4*>(&kb[(threadIdx.x + 256 * i) * 8]) = rk[i];
+    }
+    __device__ __forceinline__ void store_v(u16* vb) const {
+#pragma unroll
+        for (int i = 0; i < NV; ++i) *reinterpret_cast<u32x4*>(&vb[(threadIdx.x + 256 * i) * 8]) = rv[i];
+    }
+};
+
+// Rows [k0, k0+64) of a [N][D] bf16 matrix (rows clamped to N-1) into LDS rows of
 // stride LSTR.  All global loads are issued before the first LDS store.
 template <int D, int LSTR>
 __device__ __forceinline__ void stage_rows(const u16* __restrict__ src, int k0, int N, u16* dst) {
     constexpr int PER_ROW = D / 8;
     constexpr int TOTAL = kKeysPerTile * PER_ROW;
     constexpr int ITERS = (TOTAL + 255) / 256;
-    uint4 v[ITERS];
-#pragma unroll
-    for (int i = 0; i < ITERS; ++i) {
-        const int idx = threadIdx.x + 256 * i;
-        const int row = idx / PER_ROW, col = (idx % PER_ROW) * 8;
-        if (TOTAL % 256 == 0 || idx < TOTAL)
-            v[i] = *reinterpret_cast<const uint4*>(src + (size_t)min(k0 + row, N - 1) * D + col);
-    }
-#pragma unroll
-    for (int i = 0; i < ITERS; ++i) {
-        const int idx = threadIdx.x + 256 * i;
-        const int row = idx / PER_ROW, col = (idx % PER_ROW) * 8;
-        if (TOTAL % 256 == 0 || idx < TOTAL) *reinterpret_cast<uint4*>(&dst[row * LSTR + col]) = v[i];
-    }
-}
-
-// Rows [k0, k0+64) of a [N][D] bf16 matrix (rows clamped to N-1) held in registers
-// between a load issued before a tile's math and the LDS store after it.
-template <int D, int LSTR>
-struct RowTile {
-    static constexpr int PER_ROW = D / 8;
-    static constexpr int TOTAL = kKeysPerTile * PER_ROW;
-    static constexpr int ITERS = (TOTAL + 255) / 256;
     u32x4 v[ITERS];
-    __device__ __forceinline__ void load(const u16* __restrict__ src, int k0, int N) {
-#pragma unroll
-        for (int i = 0; i < ITERS; ++i) {
-            const int idx = threadIdx.x + 256 * i;
-            const int row = idx / PER_ROW, col = (idx % PER_ROW) * 8;
-            if (TOTAL % 256 == 0 || idx < TOTAL)
-                v[i] = *reinterpret_cast<const u32x4*>(src + (size_t)min(k0 + row, N - 1) * D + col);
-        }
-    }
-    __device__ __forceinline__ void store(u16* dst) const {
-#pragma unroll
-        for (int i = 0; i < ITERS; ++i) {
-            const int idx = threadIdx.x + 256 * i;
-            const int row = idx / PER_ROW, col = (idx % PER_ROW) * 8;
-            if (TOTAL % 256 == 0 || idx < TOTAL) *reinterpret_cast<u32x4*>(&dst[row * LSTR + col]) = v[i];
-        }
-    }
-};
-
-// Copy columns [k0, k0+64) of a [D][Npad] bf16 matrix (transposed values) into LDS rows
-// of stride LSTR.  All global loads are issued before the first LDS store.
-template <int D, int LSTR>
-__device__ __forceinline__ void stage_cols(const u16* __restrict__ src, int k0, int Npad, u16* dst) {
-    constexpr int PER_ROW = kKeysPerTile / 8;
-    constexpr int TOTAL = D * PER_ROW;
-    constexpr int ITERS = (TOTAL + 255) / 256;
-    uint4 v[ITERS];
 #pragma unroll
     for (int i = 0; i < ITERS; ++i) {
         const int idx = threadIdx.x + 256 * i;
         const int row = idx / PER_ROW, col = (idx % PER_ROW) * 8;
         if (TOTAL % 256 == 0 || idx < TOTAL)
-            v[i] = *reinterpret_cast<const uint4*>(src + (size_t)row * Npad + k0 + col);
+            v[i] = *reinterpret_cast<const u32x4*>(src + (size_t)min(k0 + row, N - 1) * D + col);
     }
 #pragma unroll
     for (int i = 0; i < ITERS; ++i) {
         const int idx = threadIdx.x + 256 * i;
         const int row = idx / PER_ROW, col = (idx % PER_ROW) * 8;
-        if (TOTAL % 256 == 0 || idx < TOTAL) *reinterpret_cast<uint4*>(&dst[row * LSTR + col]) = v[i];
+        if (TOTAL % 256 == 0 || idx < TOTAL) *reinterpret_cast<u32x4*>(&dst[row * LSTR + col]) = v[i];
     }
 }
 
 }  // namespace
 
 // ---------------------------------------------------------------------------
-// pass 1: per query row, m = max_i x_i and l = sum_i 2^(x_i - m), x = scale*log2(e)*q.k
+// Largest |V_cmp| per unit, in 64 partial maxima (bf16 magnitudes compare as integers).
 // ---------------------------------------------------------------------------
-template <int DK, int G>
-__global__ __launch_bounds__(256, 3) void cmp_stats_kernel(const u16* __restrict__ Q, const u16* __restrict__ Kc,
-                                                        float* __restrict__ stat_m, float* __restrict__ stat_il,
-                                                        float* __restrict__ lse_out, int T, int Hkv, int N, int l,
-                                                        int s, float scale_log2) {
-    constexpr int NQ = 2;
-    constexpr int TQ = kWaves * NQ * 16 / G;
-    constexpr int KSTR = DK + 8;
-    constexpr int NDS = DK / 32;
-    __shared__ __attribute__((aligned(16))) u16 ks[kKeysPerTile * KSTR];
+__global__ __launch_bounds__(256) void cmp_vmax_kernel(const u16* __restrict__ V, uint32_t* __restrict__ part,
+                                                       int N, int DV) {
+    __shared__ uint32_t red[256];
+    const size_t unit = blockIdx.y;
+    const size_t n = (size_t)N * DV, per = (n + kVmaxParts - 1) / kVmaxParts;
+    const size_t lo = blockIdx.x * per, hi = min(lo + per, n);
+    const u16* v = V + unit * n;
+    uint32_t mx = 0;
+    for (size_t i = lo + threadIdx.x; i < hi; i += 256) mx = max(mx, (uint32_t)(v[i] & 0x7FFFu));
+    red[threadIdx.x] = mx;
+    __syncthreads();
+    for (int off = 128; off > 0; off >>= 1) {
+        if (threadIdx.x < off) red[threadIdx.x] = max(red[threadIdx.x], red[threadIdx.x + off]);
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) part[unit * kVmaxParts + blockIdx.x] = red[0];
+}
+
+// Power-of-two exponent e that brings the unit's largest |V_cmp| into (2^13, 2^14]: the
+// fp16 copy holds V_cmp * 2^-e (exact unless a value falls below fp16's normal range
+// relative to the largest one) and o_cmp is rescaled by 2^e in fp32.
+__device__ __forceinline__ int cmp_v_exponent(const uint32_t* part) {
+    uint32_t mx = 0;
+    for (int i = 0; i < kVmaxParts; ++i) mx = max(mx, part[i]);
+    const float m = bf2f((u16)mx);
+    if (!(m > 0.f) || !(m < INFINITY)) return 0;
+    int k;
+    (void)frexpf(m, &k);   // m <= 2^k
+    return min(max(k - 14, -100), 100);
+}
+
+// ---------------------------------------------------------------------------
+// Fragment order of the compressed keys / values (the layout of the attention kernel's
+// K and V copies): for 16-key group kt and contraction step ds, lane (li, lq) of the A
+// operand holds K[16kt + li][32ds + 8lq .. +7], the 64 lanes' pieces contiguous; for
+// 32-key chunk c and value slice dt, lane (li, lq) holds V^T[16dt + li] at keys
+// 32c + {4lq..4lq+3, 16+4lq..16+4lq+3}, as fp16 scaled by 2^-e (cmp_v_exponent; e is
+// written to vexp[unit]).  Keys >= N are zero.
+// ---------------------------------------------------------------------------
+template <int DK, int DV>
+__global__ __launch_bounds__(256) void tile_cmp_kernel(const u16* __restrict__ K, const u16* __restrict__ V,
+                                                       const uint32_t* __restrict__ vmax_part,
+                                                       int* __restrict__ vexp, u16* __restrict__ Kf,
+                                                       u16* __restrict__ Vf, int N, int Npad) {
+    constexpr int NDS = DK / 32, NDT = DV / 16;
+    constexpr int KSTR = DK + 8, VSTR = DV + 16;
+    __shared__ __attribute__((aligned(16))) u16 ks[32 * KSTR];
+    __shared__ __attribute__((aligned(16))) u16 vs[32 * VSTR];
+    const int c = blockIdx.x;
+    const size_t bg = blockIdx.y;
+    const u16* kg = K + bg * (size_t)N * DK;
+    for (int idx = threadIdx.x; idx < 32 * DK / 8; idx += 256) {
+        const int r = idx / (DK / 8), col = (idx % (DK / 8)) * 8;
+        const int key = 32 * c + r;
+        const u32x4 v = key < N ? *reinterpret_cast<const u32x4*>(kg + (size_t)key * DK + col) : u32x4{0u, 0u, 0u, 0u};
+        *reinterpret_cast<u32x4*>(&ks[r * KSTR + col]) = v;
+    }
+    if (V) {
+        const int e = cmp_v_exponent(vmax_part + bg * kVmaxParts);
+        if (c == 0 && threadIdx.x == 0) vexp[bg] = e;
+        const float sc = ldexpf(1.0f, -e);
+        const u16* vg = V + bg * (size_t)N * DV;
+        for (int idx = threadIdx.x; idx < 32 * DV / 8; idx += 256) {
+            const int r = idx / (DV / 8), col = (idx % (DV / 8)) * 8;
+            const int key = 32 * c + r;
+            const u32x4 v =
+                key < N ? *reinterpret_cast<const u32x4*>(vg + (size_t)key * DV + col) : u32x4{0u, 0u, 0u, 0u};
+            u16 h[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const u16 bits = (u16)(v[i >> 1] >> (16 * (i & 1)));
+                h[i] = __builtin_bit_cast(u16, static_cast<_Float16>(bf2f(bits) * sc));
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) vs[r * VSTR + col + i] = h[i];
+        }
+    }
+    __syncthreads();
+    u16* kout = Kf + bg * (size_t)Npad * DK + (size_t)(2 * c) * NDS * 512;
+    for (int idx = threadIdx.x; idx < 2 * NDS * 64; idx += 256) {
+        const int kk = idx / (NDS * 64), ds = (idx / 64) % NDS, ln = idx % 64;
+        const int li = ln & 15, lq = ln >> 4;
+        *reinterpret_cast<u32x4*>(kout + (size_t)idx * 8) =
+            *reinterpret_cast<const u32x4*>(&ks[(16 * kk + li) * KSTR + 32 * ds + 8 * lq]);
+    }
+    if (V) {
+        u16* vout = Vf + bg * (size_t)Npad * DV + (size_t)c * NDT * 512;
+        const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+        for (int dt = wave; dt < NDT; dt += 4)
+            *reinterpret_cast<bf16x8*>(vout + (size_t)(dt * 64 + lane) * 8) = ld_vt_tr(vs, VSTR, 0, 16 * dt);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// mode 0: compressed attention (log-sum-exp, o_cmp) and block scores, one kernel
+// ---------------------------------------------------------------------------
+template <int DK, int DV, int G, int NQ, bool WITH_O>
+__global__ __launch_bounds__(256, 2) void cmp_attn_kernel(SelParams p) {
+    constexpr int TQ = kWaves * NQ * 16 / G;   // tokens per workgroup
+    constexpr int NDS = DK / 32, NDT = DV / 16;
+    constexpr int KE = 4 * NDS * 512;          // K elements of a 64-key tile
+    constexpr int VE = WITH_O ? 2 * NDT * 512 : 0;
+    constexpr int TPT = 256 / TQ;              // threads per token when emitting block scores
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    u16* kbuf = reinterpret_cast<u16*>(smem);
+    u16* vbuf = kbuf + KE;
+    float* ring = reinterpret_cast<float*>(vbuf + VE);   // [TQ][kRing]
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int li = lane & 15, lq = lane >> 4;
-    const int b = blockIdx.z, g = blockIdx.y;
-    const int H = Hkv * G;
-    const int tok0 = (gridDim.x - 1 - blockIdx.x) * TQ;
+    const int T = p.T, N = p.N;
+    const int n_tiles = (T + TQ - 1) / TQ;
+    int unit, it;
+    if (!map_tile(blockIdx.x, p.B * p.Hkv, n_tiles, unit, it)) return;
+    const int b = unit / p.Hkv, g = unit % p.Hkv;
+    const int H = p.Hkv * G;
+    const int tok0 = (n_tiles - 1 - it) * TQ;
+    const int R = p.lp / p.s, L = p.l / p.s;
+    const float sl2 = p.scale_log2;
 
     using M = QMap<G, NQ>;
     bf16x8 qf[NQ][NDS];
@@ -137,61 +243,67 @@ __global__ __launch_bounds__(256, 3) void cmp_stats_kernel(const u16* __restrict
         tok[c] = tok0 + wave * M::TPW + M::token(c, li);
         hl[c] = M::head(c, li);
         const int tt = min(tok[c], T - 1);
-        nv[c] = tok[c] < T ? visible_count(tok[c], l, s, N) : 0;
-        const u16* qp = Q + (((size_t)b * T + tt) * H + g * G + hl[c]) * DK + lq * 8;
+        const u16* qp = p.Q + (((size_t)b * T + tt) * H + g * G + hl[c]) * DK + lq * 8;
 #pragma unroll
         for (int ds = 0; ds < NDS; ++ds) qf[c][ds] = ld8(qp + 32 * ds);
+        nv[c] = tok[c] < T ? visible_count(tok[c], p.l, p.s, N) : 0;
     }
-    const int nv_max = visible_count(min(tok0 + TQ - 1, T - 1), l, s, N);
-    const int nv_min = visible_count(min(tok0, T - 1), l, s, N);
-    const u16* kbase = Kc + ((size_t)b * Hkv + g) * (size_t)N * DK;
+    const int t_last = min(tok0 + TQ - 1, T - 1);
+    const int nv_max = visible_count(t_last, p.l, p.s, N);
+    const int nv_min = visible_count(min(tok0, T - 1), p.l, p.s, N);
+    const int ntile = (nv_max + kKeysPerTile - 1) / kKeysPerTile;
+    const u16* kg = p.Kf + (size_t)unit * p.Npad * DK;
+    const u16* vg = WITH_O ? p.Vf + (size_t)unit * p.Npad * DV : nullptr;
+    auto ktile = [&](int tix) { return kg + (size_t)tix * KE; };
+    auto vtile = [&](int tix) { return vg + (size_t)tix * (2 * NDT * 512); };
 
-    float m[NQ], lsum[NQ];
-#pragma unroll
-    for (int c = 0; c < NQ; ++c) { m[c] = -INFINITY; lsum[c] = 0.f; }
-
-    // the next tile's rows are in flight (registers) while this tile is computed
-    RowTile<DK, KSTR> pre;
-    pre.load(kbase, 0, N);
-    for (int k0 = 0; k0 < nv_max; k0 += kKeysPerTile) {
-        __syncthreads();
-        pre.store(ks);
-        __syncthreads();
-        pre.load(kbase, k0 + kKeysPerTile, N);
-        f32x4 sacc[4][NQ];
+    // S^T tile (64 keys x this wave's 16*NQ query columns) from the K tile in LDS
+    auto qk = [&](f32x4 (&s)[4][NQ]) {
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-            for (int c = 0; c < NQ; ++c) sacc[kt][c] = zero4();
+            for (int c = 0; c < NQ; ++c) s[kt][c] = zero4();
 #pragma unroll
-        for (int ds = 0; ds < NDS; ++ds) {
+        for (int ds = 0; ds < NDS; ++ds)
 #pragma unroll
             for (int kt = 0; kt < 4; ++kt) {
-                const bf16x8 a = ld8(&ks[(16 * kt + li) * KSTR + 32 * ds + lq * 8]);
+                const bf16x8 a = ld8(&kbuf[((kt * NDS + ds) * 64 + lane) * 8]);
 #pragma unroll
-                for (int c = 0; c < NQ; ++c) sacc[kt][c] = mfma16(a, qf[c][ds], sacc[kt][c]);
+                for (int c = 0; c < NQ; ++c) s[kt][c] = mfma16(a, qf[c][ds], s[kt][c]);
             }
+    };
+
+    FragStage<KE, VE> stage;
+
+    // ---- sweep 1: per-lane running max and sum over the lane's keys ----
+    float m[NQ], lsum[NQ];
+#pragma unroll
+    for (int c = 0; c < NQ; ++c) { m[c] = -INFINITY; lsum[c] = 0.f; }
+    if (ntile > 0) stage.load_k(ktile(0));
+    for (int tix = 0; tix < ntile; ++tix) {
+        __syncthreads();
+        stage.store_k(kbuf);
+        __syncthreads();
+        if (tix + 1 < ntile) {
+            stage.load_k(ktile(tix + 1));
+        } else {   // the first tile of sweep 2
+            stage.load_k(ktile(0));
+            if constexpr (WITH_O) stage.load_v(vtile(0));
         }
-        const bool full = k0 + kKeysPerTile <= nv_min;  // no key of this tile is masked
+        f32x4 s[4][NQ];
+        qk(s);
+        const int k0 = tix * kKeysPerTile;
+        const bool full = k0 + kKeysPerTile <= nv_min;
 #pragma unroll
         for (int c = 0; c < NQ; ++c) {
             float x[16];
             float tmax = -INFINITY;
-            if (full) {
 #pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    x[e] = sacc[e >> 2][c][e & 3] * scale_log2;
-                    tmax = fmaxf(tmax, x[e]);
-                }
-            } else {
-#pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const int key = k0 + 16 * (e >> 2) + 4 * lq + (e & 3);
-                    x[e] = key < nv[c] ? sacc[e >> 2][c][e & 3] * scale_log2 : -INFINITY;
-                    tmax = fmaxf(tmax, x[e]);
-                }
+            for (int e = 0; e < 16; ++e) {
+                const int key = k0 + 16 * (e >> 2) + 4 * lq + (e & 3);
+                x[e] = (full || key < nv[c]) ? s[e >> 2][c][e & 3] * sl2 : -INFINITY;
+                tmax = fmaxf(tmax, x[e]);
             }
-            tmax = col_max(tmax);
             const float mnew = fmaxf(m[c], tmax);
             if (mnew != -INFINITY) {
                 float acc = lsum[c] * fast_exp2(m[c] - mnew);
@@ -202,77 +314,25 @@ __global__ __launch_bounds__(256, 3) void cmp_stats_kernel(const u16* __restrict
             }
         }
     }
+    // log-sum-exp (base 2) of each query row from the four lanes that share its column
+    float bias[NQ];
 #pragma unroll
     for (int c = 0; c < NQ; ++c) {
-        const float L = col_sum(lsum[c]);
-        if (lq == 0 && tok[c] < T) {
-            const size_t o = ((size_t)b * T + tok[c]) * H + g * G + hl[c];
-            stat_m[o] = m[c];
-            stat_il[o] = L > 0.f ? 1.0f / L : 0.f;
-            if (lse_out) lse_out[o] = L > 0.f ? (m[c] + __log2f(L)) * kLn2 : -INFINITY;
-        }
+        const float Mx = col_max(m[c]);
+        const float part = m[c] == -INFINITY ? 0.f : lsum[c] * fast_exp2(m[c] - Mx);
+        const float Ls = col_sum(part);
+        bias[c] = Ls > 0.f ? Mx + __log2f(Ls) : INFINITY;
+        if (p.lse && lq == 0 && tok[c] < T)
+            p.lse[((size_t)b * T + tok[c]) * H + g * G + hl[c]] = Ls > 0.f ? bias[c] * kLn2 : -INFINITY;
     }
-}
 
-// ---------------------------------------------------------------------------
-// pass 2: block scores (+ o_cmp) into the score workspace
-// ---------------------------------------------------------------------------
-template <int DK, int DV, int G, int MODE, int NQ, bool WITH_O>
-__global__ __launch_bounds__(256, 2) void cmp_scores_kernel(SelParams p) {
-    constexpr int TQ = kWaves * NQ * 16 / G;
-    constexpr int KSTR = DK + 8;
-    constexpr int VSTR = kKeysPerTile + 8;
-    constexpr int NDS = DK / 32;
-    constexpr int NDT = DV / 16;
-    constexpr int TPT = 256 / TQ;  // threads per token when emitting block scores
-    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-    u16* ks = reinterpret_cast<u16*>(smem);
-    u16* vs = ks + kKeysPerTile * KSTR;                                     // WITH_O only
-    float* ring = reinterpret_cast<float*>(vs + (WITH_O ? DV * VSTR : 0));  // [TQ][kRing] (mode 0)
-
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int li = lane & 15, lq = lane >> 4;
-    const int b = blockIdx.z, g = blockIdx.y;
-    const int T = p.T, N = p.N;
-    const int H = p.Hkv * G;
-    const int tok0 = (gridDim.x - 1 - blockIdx.x) * TQ;
-    const int R = p.lp / p.s, L = p.l / p.s;
-
-    using M = QMap<G, NQ>;
-    bf16x8 qf[NQ][NDS];
-    int tok[NQ], hl[NQ], nv[NQ];
-    float rm[NQ], ril[NQ];
-#pragma unroll
-    for (int c = 0; c < NQ; ++c) {
-        tok[c] = tok0 + wave * M::TPW + M::token(c, li);
-        hl[c] = M::head(c, li);
-        const int tt = min(tok[c], T - 1);
-        const size_t row = ((size_t)b * T + tt) * H + g * G + hl[c];
-        const u16* qp = p.Q + row * DK + lq * 8;
-#pragma unroll
-        for (int ds = 0; ds < NDS; ++ds) qf[c][ds] = ld8(qp + 32 * ds);
-        if constexpr (MODE == 0) {
-            nv[c] = tok[c] < T ? visible_count(tok[c], p.l, p.s, N) : 0;
-            rm[c] = p.stat_m[row];
-            ril[c] = p.stat_il[row];
-        } else {
-            // complete blocks before the query's own block (requires l == s == lp)
-            nv[c] = tok[c] < T ? min(tok[c] / p.lp, N) : 0;
-            rm[c] = 0.f;
-            ril[c] = 0.f;
-        }
-    }
-    const int t_last = min(tok0 + TQ - 1, T - 1);
-    const int nv_max = MODE == 0 ? visible_count(t_last, p.l, p.s, N) : min(t_last / p.lp, N);
-    const int nv_min = MODE == 0 ? visible_count(min(tok0, T - 1), p.l, p.s, N) : min(min(tok0, T - 1) / p.lp, N);
-
-    // emitter role: thread -> (token tl_e, first block offset je)
-    const int tl_e = threadIdx.x / TPT, je = threadIdx.x % TPT;
+    // ---- sweep 2: probabilities, o_cmp, head sums, block scores ----
+    const int tl_e = threadIdx.x / TPT, je = threadIdx.x % TPT;   // emitter role
     const int t_e = tok0 + tl_e;
     const int jc_e = min(t_e, T - 1) / p.lp;
     float* score_row = p.scores + (((size_t)b * T + min(t_e, T - 1)) * p.Hkv + g) * p.n_slc;
     const float* ring_e = ring + tl_e * kRing;
-    // score of block j from the ring (keys at or after `kend` count as 0)
+    // score of block j from the ring (keys at or after kend count as 0)
     auto block_score = [&](int j, int kend) {
         const int ilo = max(0, j * R - L + 1), ihi = min(j * R + R - 1, kend - 1);
         float acc = 0.f;
@@ -287,6 +347,12 @@ __global__ __launch_bounds__(256, 2) void cmp_scores_kernel(SelParams p) {
         }
         return acc;
     };
+    // blocks whose last compressed key lies in tile e (keys of tile e and e-1 are in the ring)
+    auto emit_tile = [&](int e) {
+        const int kend = (e + 1) * kKeysPerTile;
+        for (int j = e * kKeysPerTile / R + je; j < kend / R; j += TPT)
+            if (t_e < T && j <= jc_e) score_row[j] = block_score(j, kend);
+    };
 
     f32x4 oacc[WITH_O ? NDT : 1][NQ];
     if constexpr (WITH_O) {
@@ -295,41 +361,27 @@ __global__ __launch_bounds__(256, 2) void cmp_scores_kernel(SelParams p) {
 #pragma unroll
             for (int c = 0; c < NQ; ++c) oacc[dt][c] = zero4();
     }
-    const u16* kbase = p.Kc + ((size_t)b * p.Hkv + g) * (size_t)N * DK;
-    const u16* vbase = WITH_O ? p.Vct + ((size_t)b * p.Hkv + g) * (size_t)DV * p.Npad : nullptr;
-
-    int k0 = 0;
-    for (; k0 < nv_max; k0 += kKeysPerTile) {
+    for (int tix = 0; tix < ntile; ++tix) {
         __syncthreads();
-        if constexpr (WITH_O) stage_cols<DV, VSTR>(vbase, k0, p.Npad, vs);
-        stage_rows<DK, KSTR>(kbase, k0, N, ks);
+        stage.store_k(kbuf);
+        if constexpr (WITH_O) stage.store_v(vbuf);
         __syncthreads();
-
-        f32x4 sacc[4][NQ];
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-            for (int c = 0; c < NQ; ++c) sacc[kt][c] = zero4();
-#pragma unroll
-        for (int ds = 0; ds < NDS; ++ds) {
-#pragma unroll
-            for (int kt = 0; kt < 4; ++kt) {
-                const bf16x8 a = ld8(&ks[(16 * kt + li) * KSTR + 32 * ds + lq * 8]);
-#pragma unroll
-                for (int c = 0; c < NQ; ++c) sacc[kt][c] = mfma16(a, qf[c][ds], sacc[kt][c]);
-            }
+        {
+            const int nx = min(tix + 1, ntile - 1);
+            stage.load_k(ktile(nx));
+            if constexpr (WITH_O) stage.load_v(vtile(nx));
         }
-        // probabilities (mode 0) or raw scores (mode 1), zero outside the visible set
+        if (tix > 0) emit_tile(tix - 1);
+        f32x4 s[4][NQ];
+        qk(s);
+        const int k0 = tix * kKeysPerTile;
         if (k0 + kKeysPerTile <= nv_min) {
-            if constexpr (MODE == 0) {
 #pragma unroll
-                for (int c = 0; c < NQ; ++c)
+            for (int c = 0; c < NQ; ++c)
 #pragma unroll
-                    for (int kt = 0; kt < 4; ++kt)
+                for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-                        for (int r = 0; r < 4; ++r)
-                            sacc[kt][c][r] = fast_exp2(sacc[kt][c][r] * p.scale_log2 - rm[c]) * ril[c];
-            }
+                    for (int r = 0; r < 4; ++r) s[kt][c][r] = fast_exp2(s[kt][c][r] * sl2 - bias[c]);
         } else {
 #pragma unroll
             for (int c = 0; c < NQ; ++c)
@@ -338,25 +390,21 @@ __global__ __launch_bounds__(256, 2) void cmp_scores_kernel(SelParams p) {
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         const int key = k0 + 16 * kt + 4 * lq + r;
-                        float v = sacc[kt][c][r];
-                        if constexpr (MODE == 0) v = fast_exp2(v * p.scale_log2 - rm[c]) * ril[c];
-                        sacc[kt][c][r] = key < nv[c] ? v : 0.f;
+                        const float v = fast_exp2(s[kt][c][r] * sl2 - bias[c]);
+                        s[kt][c][r] = key < nv[c] ? v : 0.f;
                     }
         }
-        if constexpr (WITH_O) {
+        if constexpr (WITH_O) {   // fp16 P (2^-11 relative) against the fp16 copy of V_cmp
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
-                bf16x8 bh[NQ], bl[NQ];
+                f16x8 pb[NQ];
 #pragma unroll
-                for (int c = 0; c < NQ; ++c) pack_p_split(sacc[2 * u][c], sacc[2 * u + 1][c], bh[c], bl[c]);
+                for (int c = 0; c < NQ; ++c) pb[c] = pack_p_h(s[2 * u][c], s[2 * u + 1][c]);
 #pragma unroll
                 for (int dt = 0; dt < NDT; ++dt) {
-                    const bf16x8 a = ld8(&vs[(16 * dt + li) * VSTR + 32 * u + lq * 8]);
+                    const f16x8 a = ld8h(&vbuf[((u * NDT + dt) * 64 + lane) * 8]);
 #pragma unroll
-                    for (int c = 0; c < NQ; ++c) {
-                        oacc[dt][c] = mfma16(a, bh[c], oacc[dt][c]);
-                        oacc[dt][c] = mfma16(a, bl[c], oacc[dt][c]);
-                    }
+                    for (int c = 0; c < NQ; ++c) oacc[dt][c] = mfma16h(a, pb[c], oacc[dt][c]);
                 }
             }
         }
@@ -370,45 +418,103 @@ __global__ __launch_bounds__(256, 2) void cmp_scores_kernel(SelParams p) {
                 for (int r = 0; r < 4; ++r) {
                     float hs = 0.f;
 #pragma unroll
-                    for (int c = cg * M::CL; c < (cg + 1) * M::CL; ++c) hs += sacc[kt][c][r];
+                    for (int c = cg * M::CL; c < (cg + 1) * M::CL; ++c) hs += s[kt][c][r];
                     hs = lane_group_sum<M::GL>(hs);
-                    if ((li % M::GL) == 0) {
-                        const int key = k0 + 16 * kt + 4 * lq + r;
-                        if constexpr (MODE == 0) {
-                            ring[tl * kRing + (key & (kRing - 1))] = hs;
-                        } else {
-                            const int t = tok0 + tl;
-                            if (key < nv[cg * M::CL])
-                                p.scores[(((size_t)b * T + t) * p.Hkv + g) * p.n_slc + key] = hs;
-                        }
-                    }
+                    if ((li % M::GL) == 0) ring[tl * kRing + ((k0 + 16 * kt + 4 * lq + r) & (kRing - 1))] = hs;
                 }
         }
-        if constexpr (MODE == 0) {
-            __syncthreads();
-            // blocks whose last compressed key lies in this tile are complete
-            const int kend = k0 + kKeysPerTile;
-            for (int j = k0 / R + je; j < kend / R; j += TPT)
-                if (t_e < T && j <= jc_e) score_row[j] = block_score(j, kend);
-        }
     }
-    if constexpr (MODE == 0) {
-        __syncthreads();
-        // remaining blocks up to the token's own block (their later keys are invisible)
-        for (int j = k0 / R + je; j <= jc_e; j += TPT)
-            if (t_e < T) score_row[j] = block_score(j, k0);
-    }
+    __syncthreads();
+    if (ntile > 0) emit_tile(ntile - 1);
+    // remaining blocks up to the token's own block (their later keys are invisible)
+    for (int j = ntile * kKeysPerTile / R + je; j <= jc_e; j += TPT)
+        if (t_e < T) score_row[j] = block_score(j, ntile * kKeysPerTile);
 
     if constexpr (WITH_O) {
+        const float vs = ldexpf(1.0f, p.vexp[unit]);   // undo the fp16 copy's scaling
 #pragma unroll
         for (int c = 0; c < NQ; ++c) {
             if (tok[c] < T) {
                 float* op = p.o_cmp + (((size_t)b * T + tok[c]) * H + g * G + hl[c]) * DV + 4 * lq;
 #pragma unroll
                 for (int dt = 0; dt < NDT; ++dt)
-                    *reinterpret_cast<float4*>(op + 16 * dt) =
-                        make_float4(oacc[dt][c][0], oacc[dt][c][1], oacc[dt][c][2], oacc[dt][c][3]);
+                    *reinterpret_cast<float4*>(op + 16 * dt) = make_float4(
+                        oacc[dt][c][0] * vs, oacc[dt][c][1] * vs, oacc[dt][c][2] * vs, oacc[dt][c][3] * vs);
             }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// mode 1: block score = sum over the group's heads of q . (mean key of the block), for
+// the complete blocks before the query's own block (requires l == s == l')
+// ---------------------------------------------------------------------------
+template <int DK, int G, int NQ>
+__global__ __launch_bounds__(256, 2) void mean_scores_kernel(SelParams p) {
+    constexpr int TQ = kWaves * NQ * 16 / G;
+    constexpr int KSTR = DK + 8;
+    constexpr int NDS = DK / 32;
+    __shared__ __attribute__((aligned(16))) u16 ks[kKeysPerTile * KSTR];
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int li = lane & 15, lq = lane >> 4;
+    const int T = p.T, N = p.N;
+    const int n_tiles = (T + TQ - 1) / TQ;
+    int unit, it;
+    if (!map_tile(blockIdx.x, p.B * p.Hkv, n_tiles, unit, it)) return;
+    const int b = unit / p.Hkv, g = unit % p.Hkv;
+    const int H = p.Hkv * G;
+    const int tok0 = (n_tiles - 1 - it) * TQ;
+
+    using M = QMap<G, NQ>;
+    bf16x8 qf[NQ][NDS];
+    int tok[NQ], hl[NQ], nv[NQ];
+#pragma unroll
+    for (int c = 0; c < NQ; ++c) {
+        tok[c] = tok0 + wave * M::TPW + M::token(c, li);
+        hl[c] = M::head(c, li);
+        const int tt = min(tok[c], T - 1);
+        const u16* qp = p.Q + (((size_t)b * T + tt) * H + g * G + hl[c]) * DK + lq * 8;
+#pragma unroll
+        for (int ds = 0; ds < NDS; ++ds) qf[c][ds] = ld8(qp + 32 * ds);
+        nv[c] = tok[c] < T ? min(tok[c] / p.lp, N) : 0;
+    }
+    const int t_last = min(tok0 + TQ - 1, T - 1);
+    const int nv_max = min(t_last / p.lp, N);
+    const u16* kbase = p.Kc + (size_t)unit * N * DK;
+
+    for (int k0 = 0; k0 < nv_max; k0 += kKeysPerTile) {
+        __syncthreads();
+        stage_rows<DK, KSTR>(kbase, k0, N, ks);
+        __syncthreads();
+        f32x4 s[4][NQ];
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+            for (int c = 0; c < NQ; ++c) s[kt][c] = zero4();
+#pragma unroll
+        for (int ds = 0; ds < NDS; ++ds)
+#pragma unroll
+            for (int kt = 0; kt < 4; ++kt) {
+                const bf16x8 a = ld8(&ks[(16 * kt + li) * KSTR + 32 * ds + lq * 8]);
+#pragma unroll
+                for (int c = 0; c < NQ; ++c) s[kt][c] = mfma16(a, qf[c][ds], s[kt][c]);
+            }
+#pragma unroll
+        for (int cg = 0; cg < NQ / M::CL; ++cg) {
+            const int tl = wave * M::TPW + M::token(cg * M::CL, li);
+#pragma unroll
+            for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    float hs = 0.f;
+#pragma unroll
+                    for (int c = cg * M::CL; c < (cg + 1) * M::CL; ++c) hs += s[kt][c][r];
+                    hs = lane_group_sum<M::GL>(hs);
+                    const int key = k0 + 16 * kt + 4 * lq + r;
+                    if ((li % M::GL) == 0 && key < nv[cg * M::CL])
+                        p.scores[(((size_t)b * T + tok0 + tl) * p.Hkv + g) * p.n_slc + key] = hs;
+                }
         }
     }
 }
@@ -429,47 +535,41 @@ __global__ __launch_bounds__(256) void select_from_scores_kernel(const float* __
 // host launchers
 // ---------------------------------------------------------------------------
 namespace {
-template <int DK, int G>
-void stats_g(const u16* Q, const u16* Kc, float* m, float* il, float* lse, int B, int T, int Hkv, int N, int l,
-             int s, float sl2, hipStream_t st) {
-    constexpr int TQ = kWaves * 2 * 16 / G;
-    dim3 grid((T + TQ - 1) / TQ, Hkv, B);
-    cmp_stats_kernel<DK, G><<<grid, 256, 0, st>>>(Q, Kc, m, il, lse, T, Hkv, N, l, s, sl2);
-}
 
-template <int DK, int DV, int G, int MODE, int NQ, bool WITH_O>
-void scores_g(const SelParams& p, int B, hipStream_t st) {
+template <int DK, int DV, int G, int NQ, bool WITH_O>
+void cmp_attn_g(const SelParams& p, hipStream_t st) {
     constexpr int TQ = kWaves * NQ * 16 / G;
-    dim3 grid((p.T + TQ - 1) / TQ, p.Hkv, B);
-    const size_t lds = score_select_lds_bytes(DK, DV, G, MODE, NQ, WITH_O, p.n_slc);
-    if (lds > 65536)
-        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(cmp_scores_kernel<DK, DV, G, MODE, NQ, WITH_O>),
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    cmp_scores_kernel<DK, DV, G, MODE, NQ, WITH_O><<<grid, 256, lds, st>>>(p);
+    const int n_tiles = (p.T + TQ - 1) / TQ;
+    const size_t lds = cmp_attn_lds_bytes(DK, DV, G, WITH_O);
+    const void* fn = reinterpret_cast<const void*>(cmp_attn_kernel<DK, DV, G, NQ, WITH_O>);
+    if (lds > 65536) (void)hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    cmp_attn_kernel<DK, DV, G, NQ, WITH_O><<<map_grid(p.B * p.Hkv, n_tiles), 256, lds, st>>>(p);
 }
 
 template <int DK, int DV, int G>
-bool scores_dk(int mode, bool with_o, const SelParams& p, int B, hipStream_t st) {
-    if (mode == 0) {
-        if (with_o) scores_g<DK, DV, G, 0, 2, true>(p, B, st);
-        else scores_g<DK, DV, G, 0, 2, false>(p, B, st);
-    } else {
-        scores_g<DK, DV, G, 1, (G == 1 ? 1 : 2), false>(p, B, st);
-    }
-    return true;
+void cmp_attn_dk(bool with_o, const SelParams& p, hipStream_t st) {
+    constexpr int NQ = G == 1 ? 1 : 2;
+    if (with_o) cmp_attn_g<DK, DV, G, NQ, true>(p, st);
+    else cmp_attn_g<DK, DV, G, NQ, false>(p, st);
 }
+
+template <int DK, int G>
+void mean_scores_g(const SelParams& p, hipStream_t st) {
+    constexpr int NQ = G == 1 ? 1 : 2;
+    constexpr int TQ = kWaves * NQ * 16 / G;
+    const int n_tiles = (p.T + TQ - 1) / TQ;
+    mean_scores_kernel<DK, G, NQ><<<map_grid(p.B * p.Hkv, n_tiles), 256, 0, st>>>(p);
+}
+
 }  // namespace
 
-size_t score_select_lds_bytes(int DK, int DV, int G, int mode, int NQ, bool with_o, int n_slc) {
-    (void)n_slc;
+size_t cmp_attn_lds_bytes(int DK, int DV, int G, bool with_o) {
+    const int NQ = G == 1 ? 1 : 2;
     const int TQ = kWaves * NQ * 16 / G;
-    size_t bytes = (size_t)kKeysPerTile * (DK + 8) * 2;
-    if (with_o) bytes += (size_t)DV * (kKeysPerTile + 8) * 2;
-    if (mode == 0) bytes += (size_t)TQ * kRing * 4;
-    return bytes;
+    size_t bytes = (size_t)kKeysPerTile * DK * 2;
+    if (with_o) bytes += (size_t)kKeysPerTile * DV * 2;
+    return bytes + (size_t)TQ * kRing * 4;
 }
-
-int score_select_nq(int G, int mode) { return (mode == 1 && G == 1) ? 1 : 2; }
 
 #define NSA_G_SWITCH(G, ...)                                       \
     switch (G) {                                                   \
@@ -481,20 +581,36 @@ int score_select_nq(int G, int mode) { return (mode == 1 && G == 1) ? 1 : 2; }
         default: return false;                                     \
     }
 
-bool launch_cmp_stats(const u16* Q, const u16* Kc, float* m, float* il, float* lse, int B, int T, int Hkv, int G,
-                      int DK, int N, int l, int s, float sl2, hipStream_t st) {
-    if (DK == 192) { NSA_G_SWITCH(G, stats_g<192, GG>(Q, Kc, m, il, lse, B, T, Hkv, N, l, s, sl2, st)); }
-    else if (DK == 128) { NSA_G_SWITCH(G, stats_g<128, GG>(Q, Kc, m, il, lse, B, T, Hkv, N, l, s, sl2, st)); }
-    else if (DK == 64) { NSA_G_SWITCH(G, stats_g<64, GG>(Q, Kc, m, il, lse, B, T, Hkv, N, l, s, sl2, st)); }
+int cmp_vmax_parts() { return kVmaxParts; }
+
+bool launch_tile_cmp(int DK, int DV, const u16* K, const u16* V, uint32_t* vmax_part, int* vexp, u16* Kf, u16* Vf,
+                     int BG, int N, int Npad, hipStream_t st) {
+    if (V) cmp_vmax_kernel<<<dim3(kVmaxParts, BG), 256, 0, st>>>(V, vmax_part, N, DV);
+    dim3 grid(Npad / 32, BG);
+    if (DK == 192 && DV == 128)
+        tile_cmp_kernel<192, 128><<<grid, 256, 0, st>>>(K, V, vmax_part, vexp, Kf, Vf, N, Npad);
+    else if (DK == 128 && DV == 128)
+        tile_cmp_kernel<128, 128><<<grid, 256, 0, st>>>(K, V, vmax_part, vexp, Kf, Vf, N, Npad);
+    else if (DK == 64 && DV == 64)
+        tile_cmp_kernel<64, 64><<<grid, 256, 0, st>>>(K, V, vmax_part, vexp, Kf, Vf, N, Npad);
     else return false;
     return true;
 }
 
-bool launch_cmp_scores(int mode, bool with_o, int DK, int DV, int G, const SelParams& p, int B, hipStream_t st) {
-    if (DK == 192 && DV == 128) { NSA_G_SWITCH(G, return scores_dk<192, 128, GG>(mode, with_o, p, B, st)); }
-    if (DK == 128 && DV == 128) { NSA_G_SWITCH(G, return scores_dk<128, 128, GG>(mode, with_o, p, B, st)); }
-    if (DK == 64 && DV == 64) { NSA_G_SWITCH(G, return scores_dk<64, 64, GG>(mode, with_o, p, B, st)); }
-    return false;
+bool launch_cmp_attn(bool with_o, int DK, int DV, int G, const SelParams& p, hipStream_t st) {
+    if (DK == 192 && DV == 128) { NSA_G_SWITCH(G, cmp_attn_dk<192, 128, GG>(with_o, p, st)); }
+    else if (DK == 128 && DV == 128) { NSA_G_SWITCH(G, cmp_attn_dk<128, 128, GG>(with_o, p, st)); }
+    else if (DK == 64 && DV == 64) { NSA_G_SWITCH(G, cmp_attn_dk<64, 64, GG>(with_o, p, st)); }
+    else return false;
+    return true;
+}
+
+bool launch_mean_scores(int DK, int G, const SelParams& p, hipStream_t st) {
+    if (DK == 192) { NSA_G_SWITCH(G, mean_scores_g<192, GG>(p, st)); }
+    else if (DK == 128) { NSA_G_SWITCH(G, mean_scores_g<128, GG>(p, st)); }
+    else if (DK == 64) { NSA_G_SWITCH(G, mean_scores_g<64, GG>(p, st)); }
+    else return false;
+    return true;
 }
 
 void launch_select_from_scores(const float* scores, int32_t* sel, int B, int T, int Hkv, int n_slc, int lp,

@@ -14,8 +14,8 @@ from oracle import pipeline
 from dynamic_block_sparse_nsa_amd import inputs, ops
 from dynamic_block_sparse_nsa_amd.configs import (TINY, P8K, P64K, DECODE, MOBA, BR_SLC, BR_WIN, PHI_LINEAR,
                                                   SCORE_CMP_OVERLAP)
-from nsa_testlib import (GAP, bf16_dev_to_f64, check_close, check_selection, check_ulp, dev_bf16, dev_f32, dev_i32,
-                         f64_to_dev_bf16, sample_rows)
+from nsa_testlib import (GAP, bf16_dev_to_f64, bf16_ulp, check_close, check_selection, check_ulp, dev_bf16, dev_f32,
+                         dev_i32, f64_to_dev_bf16, sample_rows)
 
 pytestmark = pytest.mark.gpu
 
@@ -262,8 +262,13 @@ def test_decode_equals_prefill_last_row():
                           r["v_cmp"], gates[:, L - 1].contiguous())
     torch.cuda.synchronize()
     np.testing.assert_array_equal(sel.cpu().numpy(), r["sel"].cpu().numpy()[:, L - 1])
-    check_close(bf16_dev_to_f64(out), bf16_dev_to_f64(r["out"])[:, L - 1], "decode vs prefill row", atol=1e-2,
-                rel=2e-3)
+    # Both paths round an fp32 result with an absolute arithmetic error of about 1e-3 to
+    # bf16, so two values may sit on either side of a rounding midpoint: they may differ by
+    # one ulp of the larger magnitude plus the two arithmetic errors.
+    got, want = bf16_dev_to_f64(out), bf16_dev_to_f64(r["out"])[:, L - 1]
+    check_close(got, want, "decode vs prefill row", atol=2e-2, rel=2e-3)
+    lim = bf16_ulp(np.maximum(np.abs(got), np.abs(want))) + 2e-3
+    assert (np.abs(got - want) <= lim).all(), np.abs(got - want).max()
 
 
 # ---------------------------------------------------------------------------
