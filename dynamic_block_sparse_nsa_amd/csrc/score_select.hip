@@ -63,29 +63,12 @@ int map_grid(int U, int n_tiles) {
     return U * n_tiles;
 }
 
-// A 64-key tile of fragment-order K (and V) held in registers between its load (issued
-// before the previous tile's math) and its store to LDS (after it).
-template <int KE, int VE>
-struct FragStage {
-    static constexpr int NK = KE / 2048, NV = VE / 2048;   // 16-byte pieces per thread
-    u32x4 rk[NK], rv[NV > 0 ? NV : 1];
-    __device__ __forceinline__ void load_k(const u16* __restrict__ k) {
-#pragma unroll
-        for (int i = 0; i < NK; ++i) rk[i] = *reinterpret_cast<const u32x4*>(k + (threadIdx.x + 256 * i) * 8);
-    }
-    __device__ __forceinline__ void load_v(const u16* __restrict__ v) {
-#pragma unroll
-        for (int i = 0; i < NV; ++i) rv[i] = *reinterpret_cast<const u32x4*>(v + (threadIdx.x + 256 * i) * 8);
-    }
-    __device__ __forceinline__ void store_k(u16* kb) const {
-#pragma unroll
-        for (int i = 0; i < NK; ++i) *reinterpret_cast<u32x4*>(&kb[(threadIdx.x + 256 * i) * 8]) = rk[i];
-    }
-    __device__ __forceinline__ void store_v(u16* vb) const {
-#pragma unroll
-        for (int i = 0; i < NV; ++i) *reinterpret_cast<u32x4*>(&vb[(threadIdx.x + 256 * i) * 8]) = rv[i];
-    }
-};
+// Waves per workgroup of the compressed-attention kernel.  Two workgroups share a CU
+// (64 KB of LDS each for G = 16), so the two waves on a SIMD belong to different
+// workgroups and drift apart: one's MFMAs overlap the other's VALU work.
+__host__ __device__ constexpr int cmp_waves(int) { return 4; }
+
+typedef __attribute__((address_space(3))) void lds_void;
 
 // Rows [k0, k0+64) of a [N][D] bf16 matrix (rows clamped to N-1) into LDS rows of
 // stride LSTR.  All global loads are issued before the first LDS store.
@@ -212,18 +195,24 @@ __global__ __launch_bounds__(256) void tile_cmp_kernel(const u16* __restrict__ K
 // mode 0: compressed attention (log-sum-exp, o_cmp) and block scores, one kernel
 // ---------------------------------------------------------------------------
 template <int DK, int DV, int G, int NQ, bool WITH_O>
-__global__ __launch_bounds__(256, 2) void cmp_attn_kernel(SelParams p) {
-    constexpr int TQ = kWaves * NQ * 16 / G;   // tokens per workgroup
+__global__ __launch_bounds__(64 * cmp_waves(G), 2) void cmp_attn_kernel(SelParams p) {
+    constexpr int WAVES = cmp_waves(G);
+    constexpr int NT = 64 * WAVES;             // threads
+    constexpr int TQ = WAVES * NQ * 16 / G;    // tokens per workgroup
     constexpr int NDS = DK / 32, NDT = DV / 16;
-    constexpr int KE = 4 * NDS * 512;          // K elements of a 64-key tile
+    constexpr int KE = 4 * NDS * 512;          // K elements of a 64-key tile (fragment order)
     constexpr int VE = WITH_O ? 2 * NDT * 512 : 0;
-    constexpr int TPT = 256 / TQ;              // threads per token when emitting block scores
+    constexpr int TPT = NT / TQ;               // threads per token when emitting block scores
+    // LDS: the K tile, two V tiles (sweep 1 double-buffers K tiles in the K slot and the
+    // V slots), then the ring [TQ][kRing]
+    constexpr int VSLOT = (2 * VE > KE) ? 2 * VE : KE;
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     u16* kbuf = reinterpret_cast<u16*>(smem);
-    u16* vbuf = kbuf + KE;
-    float* ring = reinterpret_cast<float*>(vbuf + VE);   // [TQ][kRing]
+    u16* vbuf = kbuf + KE;   // [2][VE] in sweep 2, a second K tile in sweep 1
+    float* ring = reinterpret_cast<float*>(vbuf + VSLOT);
 
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: scalar addressing
     const int li = lane & 15, lq = lane >> 4;
     const int T = p.T, N = p.N;
     const int n_tiles = (T + TQ - 1) / TQ;
@@ -254,66 +243,89 @@ __global__ __launch_bounds__(256, 2) void cmp_attn_kernel(SelParams p) {
     const int ntile = (nv_max + kKeysPerTile - 1) / kKeysPerTile;
     const u16* kg = p.Kf + (size_t)unit * p.Npad * DK;
     const u16* vg = WITH_O ? p.Vf + (size_t)unit * p.Npad * DV : nullptr;
-    auto ktile = [&](int tix) { return kg + (size_t)tix * KE; };
-    auto vtile = [&](int tix) { return vg + (size_t)tix * (2 * NDT * 512); };
 
-    // S^T tile (64 keys x this wave's 16*NQ query columns) from the K tile in LDS
-    auto qk = [&](f32x4 (&s)[4][NQ]) {
+    // Asynchronous copies of a tile's K (KE elements) or V (VE elements), contiguous in
+    // fragment order, into LDS: 1 KB per wave instruction, each lane's 16 bytes at lane * 16.
+    auto issue_k = [&](int tix, u16* dst) {
+        const u16* src = kg + (size_t)tix * KE;
+        for (int ch = wave; ch < KE / 512; ch += WAVES)
+            __builtin_amdgcn_global_load_lds(src + ch * 512 + lane * 8, (lds_void*)(dst + ch * 512), 16, 0, 0);
+    };
+    auto issue_v = [&](int tix, u16* dst) {
+        if constexpr (WITH_O) {
+            const u16* src = vg + (size_t)tix * VE;
+            for (int ch = wave; ch < VE / 512; ch += WAVES)
+                __builtin_amdgcn_global_load_lds(src + ch * 512 + lane * 8, (lds_void*)(dst + ch * 512), 16, 0, 0);
+        }
+    };
+    // this thread's copies have landed, then every thread's have; every wave is past the
+    // reads of whatever the next copies overwrite
+    auto copies_done = [&]() {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+    };
+
+    // S^T rows of key sub-tiles 2h, 2h+1 (this wave's 16*NQ query columns)
+    auto qk_half = [&](const u16* kb, f32x4 (&s)[4][NQ], int h) {
 #pragma unroll
-        for (int kt = 0; kt < 4; ++kt)
+        for (int kt = 2 * h; kt < 2 * h + 2; ++kt)
 #pragma unroll
             for (int c = 0; c < NQ; ++c) s[kt][c] = zero4();
 #pragma unroll
         for (int ds = 0; ds < NDS; ++ds)
 #pragma unroll
-            for (int kt = 0; kt < 4; ++kt) {
-                const bf16x8 a = ld8(&kbuf[((kt * NDS + ds) * 64 + lane) * 8]);
+            for (int kt = 2 * h; kt < 2 * h + 2; ++kt) {
+                const bf16x8 a = ld8(&kb[((kt * NDS + ds) * 64 + lane) * 8]);
 #pragma unroll
                 for (int c = 0; c < NQ; ++c) s[kt][c] = mfma16(a, qf[c][ds], s[kt][c]);
             }
     };
 
-    FragStage<KE, VE> stage;
+    int nb = 0;   // sweep 1: K slot of the current tile
 
     // ---- sweep 1: per-lane running max and sum over the lane's keys ----
     float m[NQ], lsum[NQ];
 #pragma unroll
     for (int c = 0; c < NQ; ++c) { m[c] = -INFINITY; lsum[c] = 0.f; }
-    if (ntile > 0) stage.load_k(ktile(0));
-    for (int tix = 0; tix < ntile; ++tix) {
-        __syncthreads();
-        stage.store_k(kbuf);
-        __syncthreads();
-        if (tix + 1 < ntile) {
-            stage.load_k(ktile(tix + 1));
-        } else {   // the first tile of sweep 2
-            stage.load_k(ktile(0));
-            if constexpr (WITH_O) stage.load_v(vtile(0));
-        }
+    const int nfull = nv_min / kKeysPerTile;   // tiles [0, nfull) are visible to every row
+    auto k1buf = [&](int buf) { return buf ? vbuf : kbuf; };
+    auto step1 = [&](int tix, bool full) {
+        copies_done();
+        if (tix + 1 < ntile) issue_k(tix + 1, k1buf(nb ^ 1));
+        const u16* kb = k1buf(nb);
         f32x4 s[4][NQ];
-        qk(s);
-        const int k0 = tix * kKeysPerTile;
-        const bool full = k0 + kKeysPerTile <= nv_min;
+        qk_half(kb, s, 0);
+        qk_half(kb, s, 1);
+        if (!full) {
+            const int k0 = tix * kKeysPerTile;
+#pragma unroll
+            for (int c = 0; c < NQ; ++c)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int key = k0 + 16 * (e >> 2) + 4 * lq + (e & 3);
+                    if (key >= nv[c]) s[e >> 2][c][e & 3] = -INFINITY;
+                }
+        }
+        // the scale is positive: max of raw scores, one fma per exponent
 #pragma unroll
         for (int c = 0; c < NQ; ++c) {
-            float x[16];
             float tmax = -INFINITY;
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int key = k0 + 16 * (e >> 2) + 4 * lq + (e & 3);
-                x[e] = (full || key < nv[c]) ? s[e >> 2][c][e & 3] * sl2 : -INFINITY;
-                tmax = fmaxf(tmax, x[e]);
-            }
-            const float mnew = fmaxf(m[c], tmax);
+            for (int e = 0; e < 16; ++e) tmax = fmaxf(tmax, s[e >> 2][c][e & 3]);
+            const float mnew = fmaxf(m[c], tmax * sl2);
             if (mnew != -INFINITY) {
                 float acc = lsum[c] * fast_exp2(m[c] - mnew);
 #pragma unroll
-                for (int e = 0; e < 16; ++e) acc += fast_exp2(x[e] - mnew);
+                for (int e = 0; e < 16; ++e) acc += fast_exp2(__builtin_fmaf(s[e >> 2][c][e & 3], sl2, -mnew));
                 lsum[c] = acc;
                 m[c] = mnew;
             }
         }
-    }
+        nb ^= 1;
+    };
+    if (ntile > 0) issue_k(0, kbuf);
+    for (int tix = 0; tix < nfull; ++tix) step1(tix, true);
+    for (int tix = nfull; tix < ntile; ++tix) step1(tix, false);
     // log-sum-exp (base 2) of each query row from the four lanes that share its column
     float bias[NQ];
 #pragma unroll
@@ -361,57 +373,37 @@ __global__ __launch_bounds__(256, 2) void cmp_attn_kernel(SelParams p) {
 #pragma unroll
             for (int c = 0; c < NQ; ++c) oacc[dt][c] = zero4();
     }
-    for (int tix = 0; tix < ntile; ++tix) {
-        __syncthreads();
-        stage.store_k(kbuf);
-        if constexpr (WITH_O) stage.store_v(vbuf);
-        __syncthreads();
-        {
-            const int nx = min(tix + 1, ntile - 1);
-            stage.load_k(ktile(nx));
-            if constexpr (WITH_O) stage.load_v(vtile(nx));
-        }
-        if (tix > 0) emit_tile(tix - 1);
-        f32x4 s[4][NQ];
-        qk(s);
-        const int k0 = tix * kKeysPerTile;
-        if (k0 + kKeysPerTile <= nv_min) {
+    auto probs_half = [&](f32x4 (&s)[4][NQ], int h, bool full, int k0) {   // p = 2^(x - lse), 0 if invisible
 #pragma unroll
-            for (int c = 0; c < NQ; ++c)
+        for (int c = 0; c < NQ; ++c)
 #pragma unroll
-                for (int kt = 0; kt < 4; ++kt)
+            for (int kt = 2 * h; kt < 2 * h + 2; ++kt)
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) s[kt][c][r] = fast_exp2(s[kt][c][r] * sl2 - bias[c]);
-        } else {
-#pragma unroll
-            for (int c = 0; c < NQ; ++c)
-#pragma unroll
-                for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int key = k0 + 16 * kt + 4 * lq + r;
-                        const float v = fast_exp2(s[kt][c][r] * sl2 - bias[c]);
-                        s[kt][c][r] = key < nv[c] ? v : 0.f;
-                    }
-        }
-        if constexpr (WITH_O) {   // fp16 P (2^-11 relative) against the fp16 copy of V_cmp
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                f16x8 pb[NQ];
-#pragma unroll
-                for (int c = 0; c < NQ; ++c) pb[c] = pack_p_h(s[2 * u][c], s[2 * u + 1][c]);
-#pragma unroll
-                for (int dt = 0; dt < NDT; ++dt) {
-                    const f16x8 a = ld8h(&vbuf[((u * NDT + dt) * 64 + lane) * 8]);
-#pragma unroll
-                    for (int c = 0; c < NQ; ++c) oacc[dt][c] = mfma16h(a, pb[c], oacc[dt][c]);
+                for (int r = 0; r < 4; ++r) {
+                    const float v = fast_exp2(__builtin_fmaf(s[kt][c][r], sl2, -bias[c]));
+                    s[kt][c][r] = (full || k0 + 16 * kt + 4 * lq + r < nv[c]) ? v : 0.f;
                 }
+    };
+    auto pv_half = [&](const u16* vb, const f32x4 (&s)[4][NQ], int u) {   // fp16 P against fp16 V_cmp
+        if constexpr (WITH_O) {
+            f16x8 pb[NQ];
+#pragma unroll
+            for (int c = 0; c < NQ; ++c) pb[c] = pack_p_h(s[2 * u][c], s[2 * u + 1][c]);
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt) {
+                const f16x8 a = ld8h(&vb[((u * NDT + dt) * 64 + lane) * 8]);
+#pragma unroll
+                for (int c = 0; c < NQ; ++c) oacc[dt][c] = mfma16h(a, pb[c], oacc[dt][c]);
             }
         }
-        // sums over the group's heads: in-lane over the token's tiles, then DPP over its lanes
+    };
+    // sums over the group's heads (in-lane over the token's tiles, then DPP over its lanes)
+    // into the ring; every lane of a head group writes the same value to the same slot
+    auto head_sums = [&](const f32x4 (&s)[4][NQ], int k0) {
 #pragma unroll
         for (int cg = 0; cg < NQ / M::CL; ++cg) {
-            const int tl = wave * M::TPW + M::token(cg * M::CL, li);
+            // k0 is a multiple of 64, so a tile's 64 slots never wrap around the ring
+            float* rt = ring + (wave * M::TPW + M::token(cg * M::CL, li)) * kRing + (k0 & (kRing - 1)) + 4 * lq;
 #pragma unroll
             for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
@@ -419,11 +411,76 @@ __global__ __launch_bounds__(256, 2) void cmp_attn_kernel(SelParams p) {
                     float hs = 0.f;
 #pragma unroll
                     for (int c = cg * M::CL; c < (cg + 1) * M::CL; ++c) hs += s[kt][c][r];
-                    hs = lane_group_sum<M::GL>(hs);
-                    if ((li % M::GL) == 0) ring[tl * kRing + ((k0 + 16 * kt + 4 * lq + r) & (kRing - 1))] = hs;
+                    rt[16 * kt + r] = lane_group_sum<M::GL>(hs);
                 }
         }
+    };
+
+    // Sweep 2 tile t: K(t) in kbuf, V(t) in vbuf[t & 1].  V(t+1) is copied at the start of
+    // tile t, K(t+1) as soon as every wave has finished its QK products of tile t.
+    auto step2 = [&](int tix, bool full) {
+        copies_done();
+        if (tix + 1 < ntile) issue_v(tix + 1, vbuf + ((tix + 1) & 1) * VE);
+        const u16* kb = kbuf;
+        const u16* vb = vbuf + (tix & 1) * VE;
+        const int k0 = tix * kKeysPerTile;
+        f32x4 s[4][NQ];
+        auto k_free = [&]() {   // every wave's QK products of this tile are done
+            __syncthreads();
+            if (tix + 1 < ntile) issue_k(tix + 1, kbuf);
+        };
+        if (full) {
+            // Every key visible to every row.  The VALU work of one half rides in the shadow
+            // of the other half's MFMAs: exponentials of keys 0-31 under the QK products of
+            // keys 32-63, those of keys 32-63 under the PV products of keys 0-31, head sums
+            // under the PV products of keys 32-63.
+            qk_half(kb, s, 0);
+            qk_half(kb, s, 1);
+            k_free();
+            probs_half(s, 0, true, k0);
+            pv_half(vb, s, 0);
+            probs_half(s, 1, true, k0);
+            pv_half(vb, s, 1);
+            head_sums(s, k0);
+            constexpr int NMQ = 2 * NDS * NQ;           // MFMAs of a QK half
+            constexpr int NMP = WITH_O ? NDT * NQ : 0;  // MFMAs of a PV half
+#pragma unroll
+            for (int i = 0; i < NMQ; ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+#pragma unroll
+            for (int i = 0; i < NMQ; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);   // VALU
+            }
+#pragma unroll
+            for (int i = 0; i < NMP; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+            }
+#pragma unroll
+            for (int i = 0; i < NMP; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+            }
+        } else {
+            qk_half(kb, s, 0);
+            qk_half(kb, s, 1);
+            k_free();
+            probs_half(s, 0, false, k0);
+            probs_half(s, 1, false, k0);
+            pv_half(vb, s, 0);
+            pv_half(vb, s, 1);
+            head_sums(s, k0);
+        }
+        if (tix > 0) emit_tile(tix - 1);
+    };
+    // sweep 2's first tiles: every wave is done with sweep 1's buffers
+    __syncthreads();
+    if (ntile > 0) {
+        issue_k(0, kbuf);
+        issue_v(0, vbuf);
     }
+    for (int tix = 0; tix < nfull; ++tix) step2(tix, true);
+    for (int tix = nfull; tix < ntile; ++tix) step2(tix, false);
     __syncthreads();
     if (ntile > 0) emit_tile(ntile - 1);
     // remaining blocks up to the token's own block (their later keys are invisible)
@@ -538,12 +595,12 @@ namespace {
 
 template <int DK, int DV, int G, int NQ, bool WITH_O>
 void cmp_attn_g(const SelParams& p, hipStream_t st) {
-    constexpr int TQ = kWaves * NQ * 16 / G;
+    constexpr int TQ = cmp_waves(G) * NQ * 16 / G;
     const int n_tiles = (p.T + TQ - 1) / TQ;
     const size_t lds = cmp_attn_lds_bytes(DK, DV, G, WITH_O);
     const void* fn = reinterpret_cast<const void*>(cmp_attn_kernel<DK, DV, G, NQ, WITH_O>);
     if (lds > 65536) (void)hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    cmp_attn_kernel<DK, DV, G, NQ, WITH_O><<<map_grid(p.B * p.Hkv, n_tiles), 256, lds, st>>>(p);
+    cmp_attn_kernel<DK, DV, G, NQ, WITH_O><<<map_grid(p.B * p.Hkv, n_tiles), 64 * cmp_waves(G), lds, st>>>(p);
 }
 
 template <int DK, int DV, int G>
@@ -565,10 +622,9 @@ void mean_scores_g(const SelParams& p, hipStream_t st) {
 
 size_t cmp_attn_lds_bytes(int DK, int DV, int G, bool with_o) {
     const int NQ = G == 1 ? 1 : 2;
-    const int TQ = kWaves * NQ * 16 / G;
-    size_t bytes = (size_t)kKeysPerTile * DK * 2;
-    if (with_o) bytes += (size_t)kKeysPerTile * DV * 2;
-    return bytes + (size_t)TQ * kRing * 4;
+    const int TQ = cmp_waves(G) * NQ * 16 / G;
+    const size_t k = (size_t)kKeysPerTile * DK * 2, v = with_o ? (size_t)kKeysPerTile * DV * 2 : 0;
+    return k + (2 * v > k ? 2 * v : k) + (size_t)TQ * kRing * 4;
 }
 
 #define NSA_G_SWITCH(G, ...)                                       \
