@@ -350,7 +350,7 @@ nsa_status nsa_sparse_attn_fwd(const nsa_config* cfg, const void* Q, const void*
     p.o_cmp = o_cmp;
     p.gates = gate_logits;
     p.O = static_cast<u16*>(O);
-    p.T = s.T; p.Tpad = w.tpad; p.Hkv = s.Hkv; p.G = s.G; p.lp = s.lp; p.top_n = s.n; p.window = s.w;
+    p.B = s.B; p.T = s.T; p.Tpad = w.tpad; p.Hkv = s.Hkv; p.G = s.G; p.lp = s.lp; p.top_n = s.n; p.window = s.w;
     p.branches = s.br;
     p.scale_log2 = s.scale * nsa::kLog2eHost;
     if (!nsa::launch_sparse_attn(s.dk, s.dv, p, s.B, hs)) return fail(NSA_ERR_UNSUPPORTED, "no attention kernel");

@@ -169,4 +169,37 @@ __device__ __forceinline__ bf16x8 ld_vt_tr(const u16* tile, int STR, int key0, i
 
 __device__ __forceinline__ float sigmoidf_(float z) { return 1.0f / (1.0f + __expf(-z)); }
 
+// Workgroup -> (unit, tile) for a 1-D grid over units (unit = b * Hkv + g, one KV group of
+// one sequence) and n_tiles tiles per unit.  Workgroups are dispatched to the 8 XCDs
+// round-robin (workgroup L runs on XCD L % 8).  When the units split evenly over the
+// XCDs, every XCD serves one unit (or a fixed set), so the unit's keys and values stay in
+// that XCD's L2; otherwise units are interleaved tile by tile.
+__device__ __forceinline__ bool xcd_map_tile(int L, int U, int n_tiles, int& u, int& it) {
+    const int xcd = L & 7, r = L >> 3;
+    if (8 % U == 0) {
+        const int xpu = 8 / U;   // XCDs per unit, tiles interleaved between them
+        u = xcd / xpu;
+        it = r * xpu + xcd % xpu;
+    } else if (U % 8 == 0) {
+        u = xcd + 8 * (r / n_tiles);
+        it = r % n_tiles;
+    } else {
+        u = L % U;
+        it = L / U;
+    }
+    return u < U && it < n_tiles;
+}
+
+// Grid size that xcd_map_tile covers.
+inline int xcd_grid(int U, int n_tiles) {
+    if (8 % U == 0) return 8 * ((n_tiles + 8 / U - 1) / (8 / U));
+    return U * n_tiles;
+}
+
+// Loads and stores of data touched once (streaming: not worth keeping in the caches).
+template <typename V>
+__device__ __forceinline__ V ld_stream(const V* p) { return __builtin_nontemporal_load(p); }
+template <typename V>
+__device__ __forceinline__ void st_stream(V v, V* p) { __builtin_nontemporal_store(v, p); }
+
 }  // namespace nsa

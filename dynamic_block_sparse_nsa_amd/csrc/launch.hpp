@@ -55,7 +55,7 @@ struct AttnParams {
     const float* o_cmp;  // [B,T,H,DV] (branch CMP)
     const float* gates;  // [B,T,H,3] or null
     u16* O;              // [B,T,H,DV]
-    int T, Tpad, Hkv, G, lp, top_n, window, branches;
+    int B, T, Tpad, Hkv, G, lp, top_n, window, branches;
     float scale_log2;
 };
 bool launch_sparse_attn(int DK, int DV, const AttnParams& p, int B, hipStream_t st);

@@ -37,34 +37,8 @@ constexpr int kKeysPerTile = 64;
 constexpr int kRing = 4 * kKeysPerTile;  // per-token ring: the tile being written and the two before it
 constexpr int kVmaxParts = 64;           // partial maxima of |V_cmp| per unit
 
-// Workgroup -> (unit, tile) with unit = b * Hkv + g and tile 0 holding the last tokens.
-// Workgroups are dispatched to the 8 XCDs round-robin (workgroup L runs on XCD L % 8).
-// When the units split evenly over the XCDs, every XCD serves one unit (or a fixed set),
-// so the unit's compressed keys and values stay in that XCD's L2; within a unit the
-// longest rows go first.
-__device__ __forceinline__ bool map_tile(int L, int U, int n_tiles, int& u, int& it) {
-    const int xcd = L & 7, r = L >> 3;
-    if (8 % U == 0) {
-        const int xpu = 8 / U;   // XCDs per unit, tiles interleaved between them
-        u = xcd / xpu;
-        it = r * xpu + xcd % xpu;
-    } else if (U % 8 == 0) {
-        u = xcd + 8 * (r / n_tiles);
-        it = r % n_tiles;
-    } else {
-        u = L % U;
-        it = L / U;
-    }
-    return u < U && it < n_tiles;
-}
-
-int map_grid(int U, int n_tiles) {
-    if (8 % U == 0) return 8 * ((n_tiles + 8 / U - 1) / (8 / U));
-    return U * n_tiles;
-}
-
 // Waves per workgroup of the compressed-attention kernel.  Two workgroups share a CU
-// (64 KB of LDS each for G = 16), so the two waves on a SIMD belong to different
+// (72 KB of LDS each for G = 16), so the two waves on a SIMD belong to different
 // workgroups and drift apart: one's MFMAs overlap the other's VALU work.
 __host__ __device__ constexpr int cmp_waves(int) { return 4; }
 
@@ -203,13 +177,11 @@ __global__ __launch_bounds__(64 * cmp_waves(G), 2) void cmp_attn_kernel(SelParam
     constexpr int KE = 4 * NDS * 512;          // K elements of a 64-key tile (fragment order)
     constexpr int VE = WITH_O ? 2 * NDT * 512 : 0;
     constexpr int TPT = NT / TQ;               // threads per token when emitting block scores
-    // LDS: the K tile, two V tiles (sweep 1 double-buffers K tiles in the K slot and the
-    // V slots), then the ring [TQ][kRing]
-    constexpr int VSLOT = (2 * VE > KE) ? 2 * VE : KE;
+    // LDS: two K tile slots, one V tile slot, then the ring [TQ][kRing]
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-    u16* kbuf = reinterpret_cast<u16*>(smem);
-    u16* vbuf = kbuf + KE;   // [2][VE] in sweep 2, a second K tile in sweep 1
-    float* ring = reinterpret_cast<float*>(vbuf + VSLOT);
+    u16* kslot = reinterpret_cast<u16*>(smem);   // [2][KE]
+    u16* vbuf = kslot + 2 * KE;                   // [VE]
+    float* ring = reinterpret_cast<float*>(vbuf + VE);
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: scalar addressing
@@ -217,7 +189,7 @@ __global__ __launch_bounds__(64 * cmp_waves(G), 2) void cmp_attn_kernel(SelParam
     const int T = p.T, N = p.N;
     const int n_tiles = (T + TQ - 1) / TQ;
     int unit, it;
-    if (!map_tile(blockIdx.x, p.B * p.Hkv, n_tiles, unit, it)) return;
+    if (!xcd_map_tile(blockIdx.x, p.B * p.Hkv, n_tiles, unit, it)) return;
     const int b = unit / p.Hkv, g = unit % p.Hkv;
     const int H = p.Hkv * G;
     const int tok0 = (n_tiles - 1 - it) * TQ;
@@ -288,25 +260,71 @@ __global__ __launch_bounds__(64 * cmp_waves(G), 2) void cmp_attn_kernel(SelParam
 #pragma unroll
     for (int c = 0; c < NQ; ++c) { m[c] = -INFINITY; lsum[c] = 0.f; }
     const int nfull = nv_min / kKeysPerTile;   // tiles [0, nfull) are visible to every row
-    auto k1buf = [&](int buf) { return buf ? vbuf : kbuf; };
-    auto step1 = [&](int tix, bool full) {
+    auto k1buf = [&](int buf) { return kslot + buf * KE; };
+    // statistics update from key sub-tiles 2h, 2h+1 of s (all keys visible: mnew is finite,
+    // and a first update from m = -inf, lsum = 0 gives 0 * 0)
+    auto stats_half = [&](const f32x4 (&s)[4][NQ], int h) {
+#pragma unroll
+        for (int c = 0; c < NQ; ++c) {
+            float tmax = fmaxf(s[2 * h][c][0], s[2 * h][c][1]);
+#pragma unroll
+            for (int e = 2; e < 8; ++e) tmax = fmaxf(tmax, s[2 * h + (e >> 2)][c][e & 3]);
+            const float mnew = fmaxf(m[c], tmax * sl2);
+            float acc = lsum[c] * fast_exp2(m[c] - mnew);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc += fast_exp2(__builtin_fmaf(s[2 * h + (e >> 2)][c][e & 3], sl2, -mnew));
+            lsum[c] = acc;
+            m[c] = mnew;
+        }
+    };
+    auto tile_start1 = [&](int tix) {   // tile tix landed; copy of tile tix + 1 under way
         copies_done();
         if (tix + 1 < ntile) issue_k(tix + 1, k1buf(nb ^ 1));
         const u16* kb = k1buf(nb);
+        nb ^= 1;
+        return kb;
+    };
+    if (ntile > 0) issue_k(0, kslot);
+    // Tiles visible to every row, software-pipelined: the statistics of each half tile are
+    // updated under the QK products of the next half (across the tile barrier too).
+    if (nfull > 0) {
+        f32x4 s[4][NQ];
+        const u16* kb = tile_start1(0);
+        qk_half(kb, s, 0);
+        qk_half(kb, s, 1);
+        stats_half(s, 0);
+        for (int tix = 1; tix < nfull; ++tix) {
+            f32x4 prev[4][NQ];
+#pragma unroll
+            for (int c = 0; c < NQ; ++c) { prev[2][c] = s[2][c]; prev[3][c] = s[3][c]; }
+            kb = tile_start1(tix);
+            qk_half(kb, s, 0);
+            stats_half(prev, 1);
+            qk_half(kb, s, 1);
+            stats_half(s, 0);
+            constexpr int NMQ = 2 * NDS * NQ;   // MFMAs of a QK half
+#pragma unroll
+            for (int i = 0; i < 2 * NMQ; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);   // VALU
+            }
+        }
+        stats_half(s, 1);
+    }
+    // tiles with keys invisible to some rows
+    for (int tix = nfull; tix < ntile; ++tix) {
+        const u16* kb = tile_start1(tix);
         f32x4 s[4][NQ];
         qk_half(kb, s, 0);
         qk_half(kb, s, 1);
-        if (!full) {
-            const int k0 = tix * kKeysPerTile;
+        const int k0 = tix * kKeysPerTile;
 #pragma unroll
-            for (int c = 0; c < NQ; ++c)
+        for (int c = 0; c < NQ; ++c)
 #pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const int key = k0 + 16 * (e >> 2) + 4 * lq + (e & 3);
-                    if (key >= nv[c]) s[e >> 2][c][e & 3] = -INFINITY;
-                }
-        }
-        // the scale is positive: max of raw scores, one fma per exponent
+            for (int e = 0; e < 16; ++e) {
+                const int key = k0 + 16 * (e >> 2) + 4 * lq + (e & 3);
+                if (key >= nv[c]) s[e >> 2][c][e & 3] = -INFINITY;
+            }
 #pragma unroll
         for (int c = 0; c < NQ; ++c) {
             float tmax = -INFINITY;
@@ -321,11 +339,7 @@ __global__ __launch_bounds__(64 * cmp_waves(G), 2) void cmp_attn_kernel(SelParam
                 m[c] = mnew;
             }
         }
-        nb ^= 1;
-    };
-    if (ntile > 0) issue_k(0, kbuf);
-    for (int tix = 0; tix < nfull; ++tix) step1(tix, true);
-    for (int tix = nfull; tix < ntile; ++tix) step1(tix, false);
+    }
     // log-sum-exp (base 2) of each query row from the four lanes that share its column
     float bias[NQ];
 #pragma unroll
@@ -416,19 +430,18 @@ __global__ __launch_bounds__(64 * cmp_waves(G), 2) void cmp_attn_kernel(SelParam
         }
     };
 
-    // Sweep 2 tile t: K(t) in kbuf, V(t) in vbuf[t & 1].  V(t+1) is copied at the start of
-    // tile t, K(t+1) as soon as every wave has finished its QK products of tile t.
+    // Sweep 2 tile t: K(t) in K slot t & 1, V(t) in the V slot.  K(t+1) is copied at the
+    // start of tile t, V(t+1) as soon as every wave has finished its PV products of tile t.
     auto step2 = [&](int tix, bool full) {
         copies_done();
-        if (tix + 1 < ntile) issue_v(tix + 1, vbuf + ((tix + 1) & 1) * VE);
-        const u16* kb = kbuf;
-        const u16* vb = vbuf + (tix & 1) * VE;
+        if (tix + 1 < ntile) issue_k(tix + 1, kslot + ((tix + 1) & 1) * KE);
+        // scores of the blocks tile tix-1 completed; stored now, so they are long done by
+        // the next wait on this thread's memory counter
+        if (tix > 0) emit_tile(tix - 1);
+        const u16* kb = kslot + (tix & 1) * KE;
+        const u16* vb = vbuf;
         const int k0 = tix * kKeysPerTile;
         f32x4 s[4][NQ];
-        auto k_free = [&]() {   // every wave's QK products of this tile are done
-            __syncthreads();
-            if (tix + 1 < ntile) issue_k(tix + 1, kbuf);
-        };
         if (full) {
             // Every key visible to every row.  The VALU work of one half rides in the shadow
             // of the other half's MFMAs: exponentials of keys 0-31 under the QK products of
@@ -436,7 +449,6 @@ __global__ __launch_bounds__(64 * cmp_waves(G), 2) void cmp_attn_kernel(SelParam
             // under the PV products of keys 32-63.
             qk_half(kb, s, 0);
             qk_half(kb, s, 1);
-            k_free();
             probs_half(s, 0, true, k0);
             pv_half(vb, s, 0);
             probs_half(s, 1, true, k0);
@@ -464,19 +476,23 @@ __global__ __launch_bounds__(64 * cmp_waves(G), 2) void cmp_attn_kernel(SelParam
         } else {
             qk_half(kb, s, 0);
             qk_half(kb, s, 1);
-            k_free();
             probs_half(s, 0, false, k0);
             probs_half(s, 1, false, k0);
             pv_half(vb, s, 0);
             pv_half(vb, s, 1);
             head_sums(s, k0);
         }
-        if (tix > 0) emit_tile(tix - 1);
+        if constexpr (WITH_O) {
+            // Every wave has issued its PV products of this tile, so its reads of the V slot
+            // have returned.  A bare barrier: no wait for this thread's copies and stores.
+            asm volatile("s_barrier" ::: "memory");
+            if (tix + 1 < ntile) issue_v(tix + 1, vbuf);
+        }
     };
     // sweep 2's first tiles: every wave is done with sweep 1's buffers
     __syncthreads();
     if (ntile > 0) {
-        issue_k(0, kbuf);
+        issue_k(0, kslot);
         issue_v(0, vbuf);
     }
     for (int tix = 0; tix < nfull; ++tix) step2(tix, true);
@@ -518,7 +534,7 @@ __global__ __launch_bounds__(256, 2) void mean_scores_kernel(SelParams p) {
     const int T = p.T, N = p.N;
     const int n_tiles = (T + TQ - 1) / TQ;
     int unit, it;
-    if (!map_tile(blockIdx.x, p.B * p.Hkv, n_tiles, unit, it)) return;
+    if (!xcd_map_tile(blockIdx.x, p.B * p.Hkv, n_tiles, unit, it)) return;
     const int b = unit / p.Hkv, g = unit % p.Hkv;
     const int H = p.Hkv * G;
     const int tok0 = (n_tiles - 1 - it) * TQ;
@@ -600,7 +616,7 @@ void cmp_attn_g(const SelParams& p, hipStream_t st) {
     const size_t lds = cmp_attn_lds_bytes(DK, DV, G, WITH_O);
     const void* fn = reinterpret_cast<const void*>(cmp_attn_kernel<DK, DV, G, NQ, WITH_O>);
     if (lds > 65536) (void)hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    cmp_attn_kernel<DK, DV, G, NQ, WITH_O><<<map_grid(p.B * p.Hkv, n_tiles), 64 * cmp_waves(G), lds, st>>>(p);
+    cmp_attn_kernel<DK, DV, G, NQ, WITH_O><<<xcd_grid(p.B * p.Hkv, n_tiles), 64 * cmp_waves(G), lds, st>>>(p);
 }
 
 template <int DK, int DV, int G>
@@ -615,7 +631,7 @@ void mean_scores_g(const SelParams& p, hipStream_t st) {
     constexpr int NQ = G == 1 ? 1 : 2;
     constexpr int TQ = kWaves * NQ * 16 / G;
     const int n_tiles = (p.T + TQ - 1) / TQ;
-    mean_scores_kernel<DK, G, NQ><<<map_grid(p.B * p.Hkv, n_tiles), 256, 0, st>>>(p);
+    mean_scores_kernel<DK, G, NQ><<<xcd_grid(p.B * p.Hkv, n_tiles), 256, 0, st>>>(p);
 }
 
 }  // namespace
@@ -624,7 +640,7 @@ size_t cmp_attn_lds_bytes(int DK, int DV, int G, bool with_o) {
     const int NQ = G == 1 ? 1 : 2;
     const int TQ = cmp_waves(G) * NQ * 16 / G;
     const size_t k = (size_t)kKeysPerTile * DK * 2, v = with_o ? (size_t)kKeysPerTile * DV * 2 : 0;
-    return k + (2 * v > k ? 2 * v : k) + (size_t)TQ * kRing * 4;
+    return 2 * k + v + (size_t)TQ * kRing * 4;
 }
 
 #define NSA_G_SWITCH(G, ...)                                       \

@@ -205,9 +205,11 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnParams p) {
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int li = lane & 15, lq = lane >> 4;
-    const int b = blockIdx.z, g = blockIdx.y;
     const int T = p.T;
-    const int tok0 = blockIdx.x * kTok;
+    int unit, it;
+    if (!xcd_map_tile(blockIdx.x, p.B * p.Hkv, (T + kTok - 1) / kTok, unit, it)) return;
+    const int b = unit / p.Hkv, g = unit % p.Hkv;
+    const int tok0 = it * kTok;
     const int t = tok0 + wave;
     const bool active = t < T;
     const int tq = min(t, T - 1);
@@ -219,7 +221,9 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnParams p) {
     {
         const u16* qp = p.Q + (((size_t)b * T + tq) * H + h) * DK;
 #pragma unroll
-        for (int ds = 0; ds < NDS; ++ds) qf[ds] = head_ok ? ld8(qp + 32 * ds + 8 * lq) : zero8();
+        for (int ds = 0; ds < NDS; ++ds)
+            qf[ds] = head_ok ? __builtin_bit_cast(bf16x8, ld_stream(reinterpret_cast<const u32x4*>(qp + 32 * ds + 8 * lq)))
+                             : zero8();
     }
     const u16* kg = p.Kf + ((size_t)b * p.Hkv + g) * (size_t)p.Tpad * DK;
     const u16* vg = p.Vf + ((size_t)b * p.Hkv + g) * (size_t)p.Tpad * DV;
@@ -336,9 +340,9 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnParams p) {
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
         const int d0 = 16 * dt + 4 * lq;
-        float4 oc = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (p.branches & 1) oc = *reinterpret_cast<const float4*>(p.o_cmp + row * DV + d0);
-        const float vc[4] = {oc.x, oc.y, oc.z, oc.w};
+        f32x4 oc = zero4();
+        if (p.branches & 1) oc = ld_stream(reinterpret_cast<const f32x4*>(p.o_cmp + row * DV + d0));
+        const float vc[4] = {oc[0], oc[1], oc[2], oc[3]};
         float v[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -350,7 +354,8 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnParams p) {
         }
         const uint32_t w0 = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
         const uint32_t w1 = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);
-        *reinterpret_cast<uint2*>(p.O + row * DV + d0) = make_uint2(w0, w1);
+        typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+        st_stream(u32x2{w0, w1}, reinterpret_cast<u32x2*>(p.O + row * DV + d0));
     }
 }
 
@@ -365,7 +370,8 @@ bool launch_tile_kv(int DK, int DV, const u16* K, const u16* V, u16* Kf, u16* Vf
 }
 
 bool launch_sparse_attn(int DK, int DV, const AttnParams& p, int B, hipStream_t st) {
-    dim3 grid((p.T + kTok - 1) / kTok, p.Hkv, B);
+    (void)B;
+    const int grid = xcd_grid(p.B * p.Hkv, (p.T + kTok - 1) / kTok);
     if (DK == 192 && DV == 128) sparse_attn_kernel<192, 128><<<grid, 256, 0, st>>>(p);
     else if (DK == 128 && DV == 128) sparse_attn_kernel<128, 128><<<grid, 256, 0, st>>>(p);
     else if (DK == 64 && DV == 64) sparse_attn_kernel<64, 64><<<grid, 256, 0, st>>>(p);
