@@ -195,8 +195,7 @@ def main():
     ]
     print("[bench] timing prefill", file=sys.stderr, flush=True)
     per_call, wall = time_calls(calls, args.steps, args.warmup, torch)
-    step_ms = per_call.sum(axis=1)
-    ms = float(np.mean(step_ms))
+    ms = wall / args.steps * 1e3   # the K timed steps between two synchronizations
     fl = prefill_flops(cfg)
     total_flops = sum(fl.values())
     tflops = total_flops / (ms * 1e-3) / 1e12
@@ -206,10 +205,10 @@ def main():
     dom = int(np.argmax(call_ms))
     dom_flops = [2 * (cfg.n_cmp * (cfg.cmp_block * cfg.d_k * cfg.d_k + cfg.cmp_block * cfg.d_v * cfg.d_v)) * Hkv,
                  fl["cmp"], fl["slc"] + fl["win"]][dom]
-    dom_kernel = ["compress_linear_kernel", "cmp_scores_kernel", "sparse_attn_kernel"][dom]
+    dom_kernel = ["compress_linear_kernel", "cmp_attn_kernel", "sparse_attn_kernel"][dom]
     # every kernel the dominant call launches (the first is the main one)
     dom_launches = [["compress_linear_kernel", "transpose_w_kernel", "pe_bias_kernel"],
-                    ["cmp_scores_kernel", "cmp_stats_kernel", "transpose_v_kernel", "select_from_scores_kernel"],
+                    ["cmp_attn_kernel", "cmp_vmax_kernel", "tile_cmp_kernel", "select_from_scores_kernel"],
                     ["sparse_attn_kernel", "tile_kv_kernel"]][dom]
     dom_src = [["dynamic_block_sparse_nsa_amd/csrc/compress.hip"],
                ["dynamic_block_sparse_nsa_amd/csrc/score_select.hip", "dynamic_block_sparse_nsa_amd/csrc/select.hpp"],
@@ -245,6 +244,19 @@ def main():
                      "traffic": None if traffic is None else traffic.get("bytes_per_launch")},
         "wall_s_timed": round(wall, 3),
     }
+    if dom_kernel == "sparse_attn_kernel":
+        # The selected branch reads each chosen block's keys and values per (token, group):
+        # (d_k + d_v) * 2 bytes per selected key.  Part of it is served by L2; the counter
+        # record gives the bytes that reached HBM per launch (FETCH_SIZE + WRITE_SIZE).
+        gathered = slc_pairs(cfg) // cfg.heads_per_group * (cfg.d_k + cfg.d_v) * 2
+        sec = call_ms[dom] * 1e-3
+        result["roofline_gather"] = {
+            "kernel": dom_kernel, "gathered_bytes": int(gathered),
+            "gathered_gbs": round(gathered / sec / 1e9, 1),
+            "hbm_bytes": None if traffic is None else traffic.get("bytes_per_launch"),
+            "hbm_gbs": None if traffic is None else round(traffic["bytes_per_launch"] / sec / 1e9, 1),
+            "hbm_peak_gbs": PEAK_HBM_GBS,
+            "hbm_frac": None if traffic is None else round(traffic["bytes_per_launch"] / sec / 1e9 / PEAK_HBM_GBS, 4)}
 
     # ---------------- decode ----------------
     if not args.no_decode:

@@ -38,6 +38,7 @@ def source_sha(paths) -> str:
 def short_name(name: str) -> str:
     if name.startswith(("void at::", "at::")):
         return "(torch kernel: input generation / copy)"
+    name = name.replace("(anonymous namespace)::", "")
     m = re.match(r"(?:void )?(?:nsa::)?([A-Za-z_0-9]+)(<[^()]*>)?", name)
     return (m.group(1) + (m.group(2) or "")) if m else name
 
