@@ -52,6 +52,8 @@ def lib():
                                     _D, _D, _I, _D, _D, _D, _D, _D])
         L.oracle_attend.restype = ctypes.c_int
         L.oracle_causal_attention.argtypes = [ctypes.c_int] * 4 + [ctypes.c_double, _D, _D, _D, _D]
+        L.oracle_causal_attention_rows.argtypes = [ctypes.c_int, _I, ctypes.c_int, ctypes.c_int, ctypes.c_double,
+                                                   _D, _D, _D, _D]
         L.oracle_num_threads.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -190,6 +192,18 @@ def attend(cfg, Q_rows, rows, K, V, sel, o_cmp=None, gates=None, branches=None) 
     if rc != 0:
         raise MemoryError("oracle_attend failed")
     return {"out": out, "o_slc": oslc, "o_win": owin}
+
+
+def causal_attention_rows(Q_rows, rows, K, V, scale: float) -> np.ndarray:
+    """Causal attention of one head for listed rows of a sequence: row rows[k] (query
+    Q_rows[k]) attends keys 0 .. rows[k] of K [n,dk], V [n,dv].  Returns [nrows, dv]."""
+    Q, K, V = _d(Q_rows), _d(K), _d(V)
+    rows = _i(rows)
+    assert rows.min() >= 0 and rows.max() < K.shape[0]
+    out = np.zeros((len(rows), V.shape[1]))
+    lib().oracle_causal_attention_rows(len(rows), _pi(rows), Q.shape[1], V.shape[1], float(scale), _pd(Q), _pd(K),
+                                       _pd(V), _pd(out))
+    return out
 
 
 def causal_attention(Q, K, V, scale: float, window: int = 0) -> np.ndarray:

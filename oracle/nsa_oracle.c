@@ -412,6 +412,33 @@ ORACLE_API void oracle_causal_attention(int n, int dk, int dv, int w, double sca
     }
 }
 
+/* Causal attention of listed query rows (row rows[k] attends keys 0 .. rows[k]): the same
+ * textbook softmax as oracle_causal_attention, for rows taken from a long sequence. */
+ORACLE_API void oracle_causal_attention_rows(int nrows, const int* rows, int dk, int dv, double scale,
+                                             const double* Qrows, const double* K, const double* V,
+                                             double* out)
+{
+#pragma omp parallel for schedule(dynamic)
+    for (int k = 0; k < nrows; ++k) {
+        const int t = rows[k];
+        double* logit = (double*)malloc(sizeof(double) * (size_t)(t + 1));
+        double mx = -INFINITY, sum = 0.0;
+        for (int x = 0; x <= t; ++x) {
+            double a = 0.0;
+            for (int e = 0; e < dk; ++e) a += Qrows[(size_t)k * dk + e] * K[(size_t)x * dk + e];
+            logit[x] = a * scale;
+            if (logit[x] > mx) mx = logit[x];
+        }
+        for (int x = 0; x <= t; ++x) { logit[x] = exp(logit[x] - mx); sum += logit[x]; }
+        for (int e = 0; e < dv; ++e) {
+            double acc = 0.0;
+            for (int x = 0; x <= t; ++x) acc += logit[x] * V[(size_t)x * dv + e];
+            out[(size_t)k * dv + e] = acc / sum;
+        }
+        free(logit);
+    }
+}
+
 ORACLE_API int oracle_num_threads(void)
 {
     int n = 1;

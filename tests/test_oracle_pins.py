@@ -216,6 +216,23 @@ def test_p1_select_all_is_full_causal():
         np.testing.assert_allclose(full, (P / P.sum(1, keepdims=True)) @ c["V"][g], rtol=0, atol=1e-12)
 
 
+def test_causal_attention_rows_matches_full_pass():
+    """The row-listed causal attention (used for sampled rows of long sequences) equals
+    the rows of the all-rows routine, and the explicit-mask numpy softmax, for any row
+    order and subset."""
+    rng = np.random.default_rng(31)
+    n, dk, dv = 97, 24, 16
+    Q, K, V = rng.standard_normal((n, dk)), rng.standard_normal((n, dk)), rng.standard_normal((n, dv))
+    full = oracle.causal_attention(Q, K, V, 0.3)
+    rows = np.array([96, 0, 45, 1, 63, 64, 7, 96], dtype=np.int32)
+    got = oracle.causal_attention_rows(Q[rows], rows, K, V, 0.3)
+    np.testing.assert_allclose(got, full[rows], rtol=0, atol=1e-13)
+    A = 0.3 * Q @ K.T
+    A = np.where(np.tril(np.ones_like(A, bool)), A, -np.inf)
+    P = np.exp(A - A.max(1, keepdims=True))
+    np.testing.assert_allclose(got, ((P / P.sum(1, keepdims=True)) @ V)[rows], rtol=0, atol=1e-12)
+
+
 def test_p2_select_none_is_sliding_window():
     cfg = SMALL.replace(top_n=0, n_init=0, n_local=0)
     c = rand_case(cfg, seed=5)
