@@ -104,6 +104,21 @@ SelectWs select_ws(const Shape& s) {
     return w;
 }
 
+// dense causal attention: keys in fragment order, values as a scaled fp16 copy
+struct FullWs { size_t kf, vf, vmax, vexp, total; int tpad; };
+FullWs full_ws(const Shape& s) {
+    FullWs w{};
+    w.tpad = round_up(s.T, 64);
+    const size_t bg = (size_t)s.B * s.Hkv;
+    size_t off = 0;
+    w.kf = off; off = align_up(off + bg * w.tpad * s.dk * 2, 256);
+    w.vf = off; off = align_up(off + bg * w.tpad * s.dv * 2, 256);
+    w.vmax = off; off = align_up(off + bg * nsa::cmp_vmax_parts() * 4, 256);
+    w.vexp = off; off = align_up(off + bg * 4, 256);
+    w.total = off;
+    return w;
+}
+
 // One query head per KV head with only the selected branch (the MoBA configuration) runs
 // the block-major schedule of moba.hip.
 bool use_block_major(const Shape& s) { return s.G == 1 && s.br == NSA_BR_SLC; }
@@ -190,6 +205,7 @@ nsa_status nsa_workspace_size(const nsa_config* cfg, int op, size_t* bytes) {
         case NSA_OP_SCORE_SELECT: *bytes = select_ws(s).total; break;
         case NSA_OP_SPARSE_ATTN: *bytes = attn_ws(s).total; break;
         case NSA_OP_DECODE: *bytes = decode_ws(s).total; break;
+        case NSA_OP_FULL_ATTN: *bytes = full_ws(s).total; break;
         default: return fail(NSA_ERR_SHAPE, "unknown op");
     }
     return NSA_OK;
@@ -355,6 +371,34 @@ nsa_status nsa_sparse_attn_fwd(const nsa_config* cfg, const void* Q, const void*
     p.scale_log2 = s.scale * nsa::kLog2eHost;
     if (!nsa::launch_sparse_attn(s.dk, s.dv, p, s.B, hs)) return fail(NSA_ERR_UNSUPPORTED, "no attention kernel");
     return hip_check("sparse_attn");
+}
+
+nsa_status nsa_full_attn_fwd(const nsa_config* cfg, const void* Q, const void* K, const void* V, void* O, void* ws,
+                             size_t ws_bytes, void* stream) {
+    g_detail.clear();
+    Shape s;
+    nsa_status st = check_config(cfg, &s);
+    if (st != NSA_OK) return st;
+    if (!Q || !K || !V || !O) return fail(NSA_ERR_NULL, "Q, K, V and O are required");
+    const FullWs w = full_ws(s);
+    if ((st = check_ws(ws, ws_bytes, w.total)) != NSA_OK) return st;
+    const hipStream_t hs = as_stream(stream);
+    using nsa::u16;
+    u16* kf = at<u16>(ws, w.kf);
+    u16* vf = at<u16>(ws, w.vf);
+    if (!nsa::launch_tile_cmp(s.dk, s.dv, static_cast<const u16*>(K), static_cast<const u16*>(V),
+                              at<uint32_t>(ws, w.vmax), at<int>(ws, w.vexp), kf, vf, s.B * s.Hkv, s.T, w.tpad, hs))
+        return fail(NSA_ERR_UNSUPPORTED, "no layout kernel for this shape");
+    nsa::FullParams p{};
+    p.Q = static_cast<const u16*>(Q);
+    p.Kf = kf;
+    p.Vf = vf;
+    p.vexp = at<int>(ws, w.vexp);
+    p.O = static_cast<u16*>(O);
+    p.B = s.B; p.T = s.T; p.Tpad = w.tpad; p.Hkv = s.Hkv;
+    p.scale_log2 = s.scale * nsa::kLog2eHost;
+    if (!nsa::launch_full_attn(s.dk, s.dv, s.G, p, hs)) return fail(NSA_ERR_UNSUPPORTED, "no dense attention kernel");
+    return hip_check("full_attn");
 }
 
 nsa_status nsa_decode(const nsa_config* cfg, const void* q, const void* K_cache, const void* V_cache,

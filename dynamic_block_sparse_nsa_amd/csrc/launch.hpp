@@ -88,6 +88,19 @@ int moba_n_own(int BH, int n_slc, int lp);
 int moba_max_tiles(int BH, int T, int top_n, int n_slc);
 bool launch_moba_attn(int DK, int DV, const MobaParams& p, hipStream_t st);
 
+// ---- dense causal attention ----
+struct FullParams {
+    const u16* Q;        // [B,T,H,DK]
+    const u16* Kf;       // keys in fragment order (tile_cmp layout), Tpad per unit
+    const u16* Vf;       // values in fragment order, fp16 scaled by 2^-vexp
+    const int* vexp;     // [B*Hkv]
+    u16* O;              // [B,T,H,DV]
+    int B, T, Tpad, Hkv;
+    float scale_log2;
+};
+size_t full_attn_lds_bytes(int DK, int DV);
+bool launch_full_attn(int DK, int DV, int G, const FullParams& p, hipStream_t st);
+
 // ---- decode ----
 struct DecodeParams {
     const u16* q;              // [B,H,DK]

@@ -18,7 +18,7 @@ from .configs import NSAConfig
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libnsa.so")
 
-OP_COMPRESS, OP_SCORE_SELECT, OP_SPARSE_ATTN, OP_DECODE = 0, 1, 2, 3
+OP_COMPRESS, OP_SCORE_SELECT, OP_SPARSE_ATTN, OP_DECODE, OP_FULL_ATTN = 0, 1, 2, 3, 4
 STATUS = {0: "ok", 1: "null", 2: "shape", 3: "unsupported", 4: "workspace", 5: "hip"}
 
 
@@ -65,8 +65,9 @@ def lib(build_if_missing: bool = True):
         L.nsa_select_from_scores.argtypes = [cp, _P, _P, _P]
         L.nsa_sparse_attn_fwd.argtypes = [cp] + [_P] * 8 + [ctypes.c_size_t, _P]
         L.nsa_decode.argtypes = [cp] + [_P] * 10 + [ctypes.c_size_t, _P]
+        L.nsa_full_attn_fwd.argtypes = [cp] + [_P] * 5 + [ctypes.c_size_t, _P]
         for f in ("nsa_workspace_size", "nsa_compress", "nsa_score_select", "nsa_select_from_scores",
-                  "nsa_sparse_attn_fwd", "nsa_decode"):
+                  "nsa_sparse_attn_fwd", "nsa_decode", "nsa_full_attn_fwd"):
             getattr(L, f).restype = ctypes.c_int
         L.nsa_status_string.argtypes = [ctypes.c_int]
         L.nsa_status_string.restype = ctypes.c_char_p
@@ -210,6 +211,21 @@ def sparse_attn_fwd(cfg: NSAConfig, Q, K, V, sel=None, o_cmp=None, gates=None, *
     _check(lib().nsa_sparse_attn_fwd(ctypes.byref(c_config(cfg)), _ptr(Q), _ptr(K), _ptr(V),
                                      _ptr(sel if cfg.branches & 2 else None), _ptr(o_cmp if cfg.branches & 1 else None),
                                      _ptr(gates), _ptr(out), _ptr(ws), nws, _stream(stream)))
+    return out
+
+
+def full_attn_fwd(cfg: NSAConfig, Q, K, V, *, out=None, workspace=None, stream=None):
+    """nsa_full_attn_fwd (dense causal attention).  Returns O [B,T,H,dv] bf16."""
+    B, T, H, Hkv = cfg.batch, cfg.seq_len, cfg.num_heads, cfg.num_kv_heads
+    _need(Q, "Q", torch.bfloat16, (B, T, H, cfg.d_k))
+    _need(K, "K", torch.bfloat16, (B, Hkv, T, cfg.d_k))
+    _need(V, "V", torch.bfloat16, (B, Hkv, T, cfg.d_v))
+    if out is None:
+        out = torch.empty((B, T, H, cfg.d_v), dtype=torch.bfloat16, device=Q.device)
+    _need(out, "out", torch.bfloat16, (B, T, H, cfg.d_v))
+    ws, nws = _workspace(cfg, OP_FULL_ATTN, Q.device, workspace)
+    _check(lib().nsa_full_attn_fwd(ctypes.byref(c_config(cfg)), _ptr(Q), _ptr(K), _ptr(V), _ptr(out), _ptr(ws), nws,
+                                   _stream(stream)))
     return out
 
 

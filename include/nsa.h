@@ -78,7 +78,8 @@ typedef enum {
 enum { NSA_BR_CMP = 1, NSA_BR_SLC = 2, NSA_BR_WIN = 4 };
 
 /* Work items for nsa_workspace_size. */
-enum { NSA_OP_COMPRESS = 0, NSA_OP_SCORE_SELECT = 1, NSA_OP_SPARSE_ATTN = 2, NSA_OP_DECODE = 3 };
+enum { NSA_OP_COMPRESS = 0, NSA_OP_SCORE_SELECT = 1, NSA_OP_SPARSE_ATTN = 2, NSA_OP_DECODE = 3,
+       NSA_OP_FULL_ATTN = 4 };
 
 typedef struct nsa_config {
     uint32_t struct_size;      /* sizeof(nsa_config) */
@@ -163,6 +164,17 @@ nsa_status nsa_decode(const nsa_config* cfg, const void* q, const void* K_cache,
                       const int32_t* cache_len, const void* K_cmp_cache, const void* V_cmp_cache,
                       const float* gate_logits, void* O, int32_t* sel_idx_out,
                       void* ws, size_t ws_bytes, void* stream);
+
+/* Dense causal attention, the computation NSA is compared against (zjai.club notes, summary
+ * bullets and section 13: a full-attention kernel written the same way as the NSA kernel):
+ *   O[b,t,h,:] = softmax(scale * q . K[b,g,x,:] over x = 0..t) . V[b,g,x,:],  g = h / G.
+ * cfg must be a valid configuration; only batch, seq_len, num_kv_heads, heads_per_group, d_k,
+ * d_v and softmax_scale are used (workspace: nsa_workspace_size with NSA_OP_FULL_ATTN).
+ * Q [B, T, H, d_k], K [B, H_kv, T, d_k], V [B, H_kv, T, d_v] bf16; O bf16 [B, T, H, d_v].
+ * Probabilities enter the value product in fp16 against an fp16 copy of V scaled by a power
+ * of two per (b, g) (workspace). */
+nsa_status nsa_full_attn_fwd(const nsa_config* cfg, const void* Q, const void* K, const void* V, void* O,
+                             void* ws, size_t ws_bytes, void* stream);
 
 /* Static description of a status code. */
 const char* nsa_status_string(nsa_status status);

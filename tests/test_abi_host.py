@@ -57,10 +57,17 @@ def _ws(c=P8K, op=0, **over):
 @pytest.mark.parametrize("name", list(CONFIGS))
 def test_workspace_sizes(name):
     c = CONFIGS[name]
-    for op in range(4):
+    for op in range(5):
         rc, n = _ws(c, op)
         assert rc == 0
         assert n % 256 == 0
+    # dense attention: K in bf16 and V in fp16, fragment order, roundup(T, 64) keys, plus the
+    # value scaling (64 partial maxima and one exponent per (b, g))
+    rc, n = _ws(c, ops.OP_FULL_ATTN)
+    tp = -(-c.seq_len // 64) * 64
+    al = lambda x: -(-x // 256) * 256
+    bg = c.batch * c.num_kv_heads
+    assert n == al(bg * c.d_k * tp * 2) + al(bg * c.d_v * tp * 2) + al(bg * 64 * 4) + al(bg * 4)
     # the attention workspace holds K and V in MFMA fragment order, padded:
     # B*Hkv*(d_k + d_v)*(roundup(T,64)+64)*2 bytes (each part 256-byte aligned)
     # (G = 1 with only the selected branch adds the block lists and per-slot partials)
@@ -119,6 +126,8 @@ def test_calls_reject_null_pointers_before_launch():
     assert L.nsa_sparse_attn_fwd(_cfg(), fake, fake, fake, fake, None, None, fake, None, 0, None) == 1
     assert L.nsa_decode(_cfg(DECODE), fake, fake, fake, None, fake, fake, None, fake, None, None, 0, None) == 1
     assert L.nsa_select_from_scores(_cfg(), None, fake, None) == 1
+    assert L.nsa_full_attn_fwd(_cfg(), fake, fake, fake, None, fake, 1 << 40, None) == 1
+    assert L.nsa_full_attn_fwd(_cfg(), None, fake, fake, fake, fake, 1 << 40, None) == 1
 
 
 def test_calls_reject_small_workspace_before_launch():
@@ -128,6 +137,7 @@ def test_calls_reject_small_workspace_before_launch():
     assert L.nsa_score_select(_cfg(), fake, fake, fake, fake, None, fake, fake, 16, None) == 4
     assert L.nsa_sparse_attn_fwd(_cfg(), fake, fake, fake, fake, fake, None, fake, fake, 16, None) == 4
     assert L.nsa_decode(_cfg(DECODE), fake, fake, fake, fake, fake, fake, None, fake, None, fake, 16, None) == 4
+    assert L.nsa_full_attn_fwd(_cfg(), fake, fake, fake, fake, fake, 16, None) == 4
     # unaligned workspace
     big = 1 << 40
     assert L.nsa_sparse_attn_fwd(_cfg(), fake, fake, fake, fake, fake, None, fake, ctypes.c_void_p(0x1001), big,

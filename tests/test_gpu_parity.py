@@ -324,6 +324,54 @@ def test_block_major_all_rows(case):
 
 
 # ---------------------------------------------------------------------------
+# dense causal attention (the comparison kernel)
+# ---------------------------------------------------------------------------
+def _full_case(cfg, rows):
+    inp = inputs.prefill_inputs(cfg)
+    out = ops.full_attn_fwd(cfg, dev_bf16(inp["q"]), dev_bf16(inp["k"]), dev_bf16(inp["v"]))
+    torch.cuda.synchronize()
+    got = bf16_dev_to_f64(out)[0, rows]
+    ref = np.zeros_like(got)
+    for h in range(cfg.num_heads):
+        g = h // cfg.heads_per_group
+        ref[:, h] = oracle.causal_attention_rows(f64(inp["q"][0, rows, h]), rows, f64(inp["k"][0, g]),
+                                                 f64(inp["v"][0, g]), cfg.scale)
+    check_close(got, ref, f"{cfg.name} dense causal attention")
+
+
+@pytest.mark.parametrize("cfg", [TINY, RAGGED], ids=lambda c: c.name)
+def test_full_attn_all_rows(cfg):
+    announce(f"dense attention {cfg.name} all rows")
+    _full_case(cfg, np.arange(cfg.seq_len, dtype=np.int32))
+
+
+@pytest.mark.parametrize("cfg", [P8K, RAGGED16, P64K], ids=lambda c: c.name)
+def test_full_attn_sampled(cfg):
+    announce(f"dense attention {cfg.name} sampled rows")
+    _full_case(cfg, sample_rows(cfg.seq_len, 24 if cfg.seq_len > 10000 else 48, 8))
+
+
+def test_select_all_blocks_equals_dense_attention_on_gpu():
+    """Selecting every block makes the selected branch full causal attention (sunshychen.top);
+    checked GPU against GPU on 2048 tokens, 32 blocks of 64."""
+    cfg = P8K.replace(name="all32", seq_len=2048, top_n=32, branches=BR_SLC, seed=27)
+    announce("select-all == dense attention (GPU)")
+    inp = inputs.prefill_inputs(cfg)
+    jc = np.arange(cfg.seq_len) // cfg.slc_block
+    sel = np.where(np.arange(cfg.top_n)[None, :] <= jc[:, None], np.arange(cfg.top_n)[None, :], -1).astype(np.int32)
+    sel = np.broadcast_to(sel[None, :, None, :], (1, cfg.seq_len, cfg.num_kv_heads, cfg.top_n)).copy()
+    q, k, v = dev_bf16(inp["q"]), dev_bf16(inp["k"]), dev_bf16(inp["v"])
+    slc = ops.sparse_attn_fwd(cfg, q, k, v, dev_i32(sel))
+    full = ops.full_attn_fwd(cfg, q, k, v)
+    torch.cuda.synchronize()
+    a, b = bf16_dev_to_f64(slc), bf16_dev_to_f64(full)
+    check_close(a, b, "select-all vs dense", atol=2e-2, rel=2e-3)
+    # two GPU paths with ~1e-3 arithmetic error each, rounded to bf16
+    lim = bf16_ulp(np.maximum(np.abs(a), np.abs(b))) + 2e-3
+    assert (np.abs(a - b) <= lim).all(), np.abs(a - b).max()
+
+
+# ---------------------------------------------------------------------------
 # the pages' special cases, run on the GPU
 # ---------------------------------------------------------------------------
 def test_gpu_select_all_is_full_causal_and_window_only_is_swa():
