@@ -26,7 +26,7 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-from dynamic_block_sparse_nsa_amd.configs import P64K, DECODE, MOBA, NSAConfig  # noqa: E402
+from dynamic_block_sparse_nsa_amd.configs import P8K, P64K, DECODE, MOBA, NSAConfig  # noqa: E402
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
@@ -147,6 +147,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-moba", action="store_true")
+    ap.add_argument("--no-dense", action="store_true", help="skip the dense causal attention comparison")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run one elementwise kernel over 1 GiB (reads and writes 1 GiB: the known-size kernel that scales HBM counters)")
     args = ap.parse_args()
@@ -259,6 +260,40 @@ def main():
             "hbm_frac": None if traffic is None else round(traffic["bytes_per_launch"] / sec / 1e9 / PEAK_HBM_GBS, 4)}
 
     # ---------------- decode ----------------
+    # ---------------- dense causal attention on the same inputs ----------------
+    if not args.no_dense:
+        print("[bench] dense causal attention", file=sys.stderr, flush=True)
+        wsf = torch.empty(ops.workspace_size(cfg, ops.OP_FULL_ATTN), dtype=torch.uint8, device=dev)
+        pcf, _ = time_calls([lambda: ops.full_attn_fwd(cfg, Q, K, V, out=out, workspace=wsf)], 3, 1, torch)
+        fms = float(pcf.mean())
+        dfl = 2 * (cfg.d_k + cfg.d_v) * H * T * (T + 1) / 2
+        cmp8 = {}
+        # the same comparison at 8K tokens (NSA's three calls against the dense kernel)
+        c8 = P8K
+        g8 = torch.Generator(device=dev).manual_seed(c8.seed)
+        r8 = lambda *sh: torch.randn(sh, generator=g8, device=dev).to(torch.bfloat16)
+        Q8, K8, V8 = (r8(1, c8.seq_len, c8.num_heads, c8.d_k), r8(1, c8.num_kv_heads, c8.seq_len, c8.d_k),
+                      r8(1, c8.num_kv_heads, c8.seq_len, c8.d_v))
+        w8 = (r8(c8.cmp_block * c8.d_k, c8.d_k) * 0.03, r8(c8.cmp_block * c8.d_v, c8.d_v) * 0.03,
+              r8(c8.cmp_block, c8.d_k), r8(c8.cmp_block, c8.d_v))
+        gt8 = torch.randn((1, c8.seq_len, c8.num_heads, 3), generator=g8, device=dev)
+        kc8, vc8 = ops.compress(c8, K8, V8, *w8)
+        sel8, _, oc8 = ops.score_select(c8, Q8, kc8, vc8)
+        o8 = torch.empty((1, c8.seq_len, c8.num_heads, c8.d_v), dtype=torch.bfloat16, device=dev)
+        n8, _ = time_calls([lambda: ops.compress(c8, K8, V8, *w8, out_k=kc8, out_v=vc8),
+                            lambda: ops.score_select(c8, Q8, kc8, vc8, sel=sel8, o_cmp=oc8),
+                            lambda: ops.sparse_attn_fwd(c8, Q8, K8, V8, sel8, oc8, gt8, out=o8)], 10, 2, torch)
+        f8, _ = time_calls([lambda: ops.full_attn_fwd(c8, Q8, K8, V8, out=o8)], 10, 2, torch)
+        n8ms, f8ms = float(n8.sum(axis=1).mean()), float(f8.mean())
+        result["vs_dense"] = {
+            "workload": "dense_causal_64k", "kernel": "full_attn_kernel", "dense_ms": round(fms, 3),
+            "dense_tflops": round(dfl / (fms * 1e-3) / 1e12, 1),
+            "dense_mfma_frac": round(dfl / (fms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "nsa_ms": round(ms, 3), "nsa_speedup": round(fms / ms, 2),
+            "at_8k": {"nsa_ms": round(n8ms, 3), "dense_ms": round(f8ms, 3), "nsa_speedup": round(f8ms / n8ms, 2)}}
+        del Q8, K8, V8, kc8, vc8, sel8, oc8, o8, wsf
+        torch.cuda.empty_cache()
+
     if not args.no_decode:
         del Q, K, V, ocmp, out
         torch.cuda.empty_cache()

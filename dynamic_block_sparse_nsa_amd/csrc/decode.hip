@@ -16,9 +16,10 @@
 //                         score[j] = sum_h sum_s w_s,h A_s[h][j] (the exact normalized
 //                         compressed probabilities, summed as in prefill); then the
 //                         shared top-n.
-//   decode_attn_kernel    one wave per item: a selected block, or a 64-token piece of the
-//                         window; exact softmax over its keys, partial (m, l, o^T).
-//   decode_merge_kernel   o_cmp = sum_s w_s o_s, merges the items of each branch and
+//   decode_attn_kernel    one wave per item (a selected block, or a 64-token piece of the
+//                         window): exact softmax over its keys; the 4 items of a workgroup
+//                         (same branch) are combined in LDS into one partial (m, l, o^T).
+//   decode_merge_kernel   o_cmp = sum_s w_s o_s, merges the partials of each branch and
 //                         applies the gates; one thread per output element.
 // Value rows stay key-major: each wave stores its value tile row-major in LDS and builds
 // the V^T MFMA operand with the gfx950 transposing LDS read.
@@ -281,33 +282,36 @@ __global__ __launch_bounds__(1024) void decode_select_kernel(DecodeParams p) {
 }
 
 // ---------------------------------------------------------------------------
+// A workgroup holds 4 waves; wave w takes item 4*gi + w of one branch (a selected block,
+// or a 64-token piece of the window) and computes its exact softmax partial (m, l, o^T);
+// the 4 partials are combined in LDS and one partial per workgroup is written.
 template <int DK, int DV>
-__global__ __launch_bounds__(64) void decode_attn_kernel(DecodeParams p) {
+__global__ __launch_bounds__(256, 2) void decode_attn_kernel(DecodeParams p) {
     constexpr int NDS = DK / 32, NDT = DV / 16;
     constexpr int VSTR = DV + 16;
-    __shared__ __attribute__((aligned(16))) u16 vs[64 * VSTR];
-    const int lane = threadIdx.x, li = lane & 15, lq = lane >> 4;
-    const int it = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, li = lane & 15, lq = lane >> 4;
+    u16* vs = reinterpret_cast<u16*>(smem) + wave * 64 * VSTR;   // this wave's value tile
+    // after the items: [4][DV][16] partial o, then [4][16] m and l
+    float* mo = reinterpret_cast<float*>(smem);
+    float* mm = mo + 4 * DV * 16;
+    float* ml = mm + 64;
+    const int gi = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
     const int G = p.G, H = p.Hkv * G;
     const int t = query_pos(p.cache_len, b, p.L);
-    const size_t ib = ((size_t)b * p.Hkv + g) * p.n_items + it;
+    const int n_sg = (p.top_n + 3) / 4;
+    const int n_win = p.n_items - p.top_n;
 
     int lo = 0, hi = -1, c0 = 0;
-    if (it < p.top_n) {
-        const int j = (p.branches & 2) ? p.sel_ws[((size_t)b * p.Hkv + g) * p.top_n + it] : -1;
+    if (gi < n_sg) {
+        const int it = 4 * gi + wave;
+        const int j = ((p.branches & 2) && it < p.top_n) ? p.sel_ws[((size_t)b * p.Hkv + g) * p.top_n + it] : -1;
         if (j >= 0) { lo = j * p.lp; hi = min(j * p.lp + p.lp - 1, t); c0 = lo; }
     } else if (p.branches & 4) {
+        const int it = 4 * (gi - n_sg) + wave;
         const int t0 = max(0, t - p.window + 1);
-        const int base = (t0 & ~63) + 64 * (it - p.top_n);
-        if (base <= t) { lo = max(t0, base); hi = min(t, base + 63); c0 = base; }
-    }
-    if (hi < lo) {   // empty item: weight 0 in the merge, zero values (never stale memory)
-        if (lq == 0) {
-            p.att_m[ib * 16 + li] = -INFINITY;
-            p.att_l[ib * 16 + li] = 0.f;
-        }
-        for (int idx = lane; idx < DV * 16; idx += 64) p.att_o[ib * DV * 16 + idx] = 0.f;
-        return;
+        const int base = (t0 & ~63) + 64 * it;
+        if (it < n_win && base <= t) { lo = max(t0, base); hi = min(t, base + 63); c0 = base; }
     }
     bf16x8 qf[NDS];
     load_q<DK>(p.q, b, H, g, G, qf);
@@ -317,15 +321,20 @@ __global__ __launch_bounds__(64) void decode_attn_kernel(DecodeParams p) {
     f32x4 o[NDT];
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) o[dt] = zero4();
-    // a selection block spans l' / 64 pieces of 64 keys; a window piece is one
+    // a selection block spans l' / 64 pieces of 64 keys; a window piece is one.  Only this
+    // wave touches its value tile: a wave-scope barrier orders its LDS accesses.
     for (int key0 = c0; key0 <= hi; key0 += 64) {
         KeyTile64<DK, DV> tile;
         tile.load(kg, vg, key0, p.L);
         f32x4 sacc[4];
         tile.scores(qf, sacc);
-        __syncthreads();   // the previous piece's value reads are done
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         tile.template store_v<VSTR>(vs);
-        __syncthreads();
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         float x[16];
         float tmax = -INFINITY;
 #pragma unroll
@@ -365,14 +374,38 @@ __global__ __launch_bounds__(64) void decode_attn_kernel(DecodeParams p) {
         }
     }
     l = col_sum(l);
-    if (lq == 0) {
-        p.att_m[ib * 16 + li] = m;
-        p.att_l[ib * 16 + li] = l;
-    }
+    __syncthreads();   // every wave is done with its value tile: reuse the region
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) p.att_o[(ib * DV + 16 * dt + 4 * lq + r) * 16 + li] = o[dt][r];
+        for (int r = 0; r < 4; ++r) mo[(wave * DV + 16 * dt + 4 * lq + r) * 16 + li] = o[dt][r];
+    if (lq == 0) {
+        mm[wave * 16 + li] = m;
+        ml[wave * 16 + li] = l;
+    }
+    __syncthreads();
+    // combine the four partials of every (d, head); empty items carry m = -inf, l = 0, o = 0
+    const size_t ib = ((size_t)b * p.Hkv + g) * p.n_items + gi;
+    for (int idx = threadIdx.x; idx < DV * 16; idx += 256) {
+        const int hh = idx & 15;
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) M = fmaxf(M, mm[w * 16 + hh]);
+        float acc = 0.f, L = 0.f;
+        if (M > -INFINITY) {
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const float e = fast_exp2(mm[w * 16 + hh] - M);
+                acc += e * mo[w * DV * 16 + idx];
+                L += e * ml[w * 16 + hh];
+            }
+        }
+        p.att_o[ib * DV * 16 + idx] = acc;
+        if (idx < 16) {
+            p.att_m[ib * 16 + hh] = M;
+            p.att_l[ib * 16 + hh] = L;
+        }
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -388,10 +421,12 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p) {
     const size_t ib0 = bg * p.n_items;
     // wave 0: selected-branch items, wave 1: window items; lane = head + 16 * q holds
     // items i0 + q + 4i (at most kDecodeMaxItems per branch, loads issued together)
+    // partials: the selected branch's groups of 4 items, then the window's
+    const int n_sg = (p.top_n + 3) / 4, n_grp = n_sg + (p.n_items - p.top_n + 3) / 4;
     if (wave < 2) {
         constexpr int NI = kDecodeMaxItems / 4;
         const int hh = lane & 15, q = lane >> 4;
-        const int i0 = wave == 0 ? 0 : p.top_n, i1 = wave == 0 ? p.top_n : p.n_items;
+        const int i0 = wave == 0 ? 0 : n_sg, i1 = wave == 0 ? n_sg : n_grp;
         float mv[NI], lv[NI];
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
@@ -434,21 +469,15 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p) {
         }
     }
     if (p.branches & 2) {
-        for (int i0 = 0; i0 < p.top_n; i0 += 8) {
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int it = i0 + i;
-                if (it < p.top_n) os += wsm[it * 16 + hh] * p.att_o[(ib0 + it) * DV * 16 + idx];
-            }
-        }
+        for (int it = 0; it < 8; ++it)
+            if (it < n_sg) os += wsm[it * 16 + hh] * p.att_o[(ib0 + it) * DV * 16 + idx];
     }
     if (p.branches & 4) {
-        for (int i0 = p.top_n; i0 < p.n_items; i0 += 8) {
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int it = i0 + i;
-                if (it < p.n_items) ow += wsm[it * 16 + hh] * p.att_o[(ib0 + it) * DV * 16 + idx];
-            }
+        for (int i = 0; i < 8; ++i) {
+            const int it = n_sg + i;
+            if (it < n_grp) ow += wsm[it * 16 + hh] * p.att_o[(ib0 + it) * DV * 16 + idx];
         }
     }
     const int h = g * G + hh;
@@ -487,7 +516,10 @@ void decode_impl(const DecodeParams& p, hipStream_t st) {
         allow_lds(decode_select_kernel<NU>, lds2);
         decode_select_kernel<NU><<<dim3(p.Hkv, p.B), 1024, lds2, st>>>(p);
     });
-    decode_attn_kernel<DK, DV><<<dim3(p.n_items, p.Hkv, p.B), 64, 0, st>>>(p);
+    const int n_grp = (p.top_n + 3) / 4 + (p.n_items - p.top_n + 3) / 4;
+    const size_t lds3 = (size_t)4 * 64 * (DV + 16) * 2;   // >= the combine buffers
+    allow_lds(decode_attn_kernel<DK, DV>, lds3);
+    decode_attn_kernel<DK, DV><<<dim3(n_grp, p.Hkv, p.B), 256, lds3, st>>>(p);
     decode_merge_kernel<DV><<<dim3(DV / 16, p.Hkv, p.B), 256, (size_t)p.n_items * 16 * 4, st>>>(p);
 }
 }  // namespace

@@ -333,20 +333,22 @@ __global__ __launch_bounds__(256, 2) void moba_attn_kernel(MobaParams p) {
     }
 }
 
-// one wave per (token, head): combine the slots of the token's list
+// per (token, head): combine the slots of the token's list.  A row of DV values is DV/4
+// lanes with one float4 each (a wave covers 64*4/DV rows); the slots' partial outputs are
+// read once (non-temporal) and the bf16 row is stored with 8-byte writes.
 template <int DV>
 __global__ __launch_bounds__(256) void moba_merge_kernel(MobaParams p) {
-    const size_t row = (size_t)blockIdx.x * 4 + (threadIdx.x >> 6);   // (b, t, h)
-    const int lane = threadIdx.x & 63;
+    constexpr int LPR = DV / 4;      // lanes per row
+    constexpr int RPB = 256 / LPR;   // rows per workgroup
+    const size_t row = (size_t)blockIdx.x * RPB + threadIdx.x / LPR;   // (b, t, h)
+    const int li = threadIdx.x % LPR;
     if (row >= (size_t)p.B * p.T * p.Hkv) return;
     const int32_t* sel = p.sel + row * p.top_n;
     float M = -INFINITY;
     for (int s = 0; s < p.top_n; ++s)
         if (sel[s] >= 0) M = fmaxf(M, p.part_m[row * p.top_n + s]);
     float L = 0.f;
-    float acc[DV / 64];
-#pragma unroll
-    for (int i = 0; i < DV / 64; ++i) acc[i] = 0.f;
+    f32x4 acc = zero4();
     if (M > -INFINITY) {
         for (int s = 0; s < p.top_n; ++s) {
             if (sel[s] < 0) continue;
@@ -354,15 +356,15 @@ __global__ __launch_bounds__(256) void moba_merge_kernel(MobaParams p) {
             if (ms == -INFINITY) continue;
             const float w = fast_exp2(ms - M);
             L += w * p.part_l[row * p.top_n + s];
-            const float* op = p.part_o + (row * p.top_n + s) * DV;
-#pragma unroll
-            for (int i = 0; i < DV / 64; ++i) acc[i] += w * op[lane + 64 * i];
+            acc += w * ld_stream(reinterpret_cast<const f32x4*>(p.part_o + (row * p.top_n + s) * DV) + li);
         }
     }
     const float g = p.gates ? sigmoidf_(p.gates[row * 3 + 1]) : 1.f;
     const float inv = L > 0.f ? g / L : 0.f;
-#pragma unroll
-    for (int i = 0; i < DV / 64; ++i) p.O[row * DV + lane + 64 * i] = f2bf(acc[i] * inv);
+    typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+    const u32x2 v = {(uint32_t)f2bf(acc[0] * inv) | ((uint32_t)f2bf(acc[1] * inv) << 16),
+                     (uint32_t)f2bf(acc[2] * inv) | ((uint32_t)f2bf(acc[3] * inv) << 16)};
+    st_stream(v, reinterpret_cast<u32x2*>(p.O + row * DV) + li);
 }
 
 // ---------------------------------------------------------------------------
@@ -388,8 +390,8 @@ bool launch_moba_attn(int DK, int DV, const MobaParams& p, hipStream_t st) {
     else if (DK == 192 && DV == 128) moba_attn_kernel<192, 128><<<nwg, 256, 0, st>>>(p);
     else return false;
     const size_t rows = (size_t)p.B * p.T * p.Hkv;
-    if (DV == 128) moba_merge_kernel<128><<<(unsigned)((rows + 3) / 4), 256, 0, st>>>(p);
-    else moba_merge_kernel<64><<<(unsigned)((rows + 3) / 4), 256, 0, st>>>(p);
+    if (DV == 128) moba_merge_kernel<128><<<(unsigned)((rows + 7) / 8), 256, 0, st>>>(p);
+    else moba_merge_kernel<64><<<(unsigned)((rows + 15) / 16), 256, 0, st>>>(p);
     return true;
 }
 
