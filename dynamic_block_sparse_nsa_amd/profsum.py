@@ -1,15 +1,17 @@
 """Summaries of rocprofv3 output for the benchmark's profile records.
 
-``stats``   kernel_stats.csv (from ``rocprofv3 --kernel-trace --stats -f csv``) -> a short
-            text table (calls, average and total duration per kernel).
+``stats``   kernel_trace.csv (from ``rocprofv3 --kernel-trace -f csv``) -> a short text table
+            of calls, average and total duration per kernel and launch size (workgroups),
+            so launches of one kernel on different workloads get rows of their own.
 ``traffic`` two counter_collection.csv files (``--pmc FETCH_SIZE`` and ``--pmc WRITE_SIZE``)
-            -> HBM bytes per launch of each named kernel, scaled by what the same counter
-            reads for a plain device copy of known size in the same run, written into a
+            -> HBM bytes per launch of each named kernel (its largest launch, the headline
+            workload), scaled by what the same counter reads for a plain device copy of
+            known size in the same run, written into a
             JSON record with the hash of the kernel's sources (a record whose hash no
             longer matches the sources is ignored by the benchmark).
 
 Usage:
-  python -m dynamic_block_sparse_nsa_amd.profsum stats STATS_CSV --cmd "..." --title "..." > out.txt
+  python -m dynamic_block_sparse_nsa_amd.profsum stats TRACE_CSV --cmd "..." --title "..." > out.txt
   python -m dynamic_block_sparse_nsa_amd.profsum traffic --fetch F.csv --write W.csv \
       --copy-bytes N --copy-regex REGEX --kernel NAME=SRC[,SRC...] [--kernel ...] --out traffic.json
 """
@@ -44,28 +46,36 @@ def short_name(name: str) -> str:
 
 
 def stats(path: str, cmd: str, title: str) -> str:
-    rows = []
+    groups = defaultdict(list)
     with open(path) as f:
         for r in csv.DictReader(f):
-            rows.append((short_name(r["Name"]), int(r["Calls"]), float(r["TotalDurationNs"]) / 1e6,
-                         float(r["AverageNs"]) / 1e3, float(r["Percentage"])))
-    rows.sort(key=lambda r: -r[2])
+            grid = int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"])
+            wg = int(r["Workgroup_Size_X"]) * int(r["Workgroup_Size_Y"]) * int(r["Workgroup_Size_Z"])
+            dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+            groups[(short_name(r["Kernel_Name"]), grid // max(wg, 1))].append(dur)
+    total = sum(sum(v) for v in groups.values())
+    rows = sorted(((n, w, len(v), sum(v) / len(v), sum(v)) for (n, w), v in groups.items()), key=lambda r: -r[4])
     out = [f"# {title}", "", f"command: {cmd}", "",
-           f"{'kernel':64s} {'calls':>6s} {'avg_us':>10s} {'total_ms':>10s} {'pct':>6s}"]
-    for name, calls, tot, avg, pct in rows:
-        out.append(f"{name[:64]:64s} {calls:6d} {avg:10.1f} {tot:10.2f} {pct:6.2f}")
+           f"{'kernel':52s} {'wgs':>8s} {'calls':>6s} {'avg_us':>10s} {'total_ms':>10s} {'pct':>6s}"]
+    for name, wgs, calls, avg, tot in rows:
+        out.append(f"{name[:52]:52s} {wgs:8d} {calls:6d} {avg:10.1f} {tot / 1e3:10.2f} {100 * tot / total:6.2f}")
     return "\n".join(out) + "\n"
 
 
 def per_kernel_counter(path: str, counter: str) -> dict:
-    """Mean of a counter's per-dispatch value, per kernel name."""
-    acc = defaultdict(list)
+    """Mean of a counter's per-dispatch value per kernel name, over that kernel's largest
+    launches (the headline workload when one kernel also runs on smaller ones)."""
+    acc = defaultdict(lambda: defaultdict(list))
     with open(path) as f:
         for r in csv.DictReader(f):
             if r["Counter_Name"] != counter:
                 continue
-            acc[r["Kernel_Name"]].append(float(r["Counter_Value"]))
-    return {k: sum(v) / len(v) for k, v in acc.items()}
+            acc[r["Kernel_Name"]][int(r["Grid_Size"])].append(float(r["Counter_Value"]))
+    out = {}
+    for k, by_grid in acc.items():
+        v = by_grid[max(by_grid)]
+        out[k] = sum(v) / len(v)
+    return out
 
 
 def pick(values: dict, regex: str) -> float:
