@@ -420,6 +420,9 @@ nsa_status nsa_decode(const nsa_config* cfg, const void* q, const void* K_cache,
     if (w.n_items - s.n > nsa::kDecodeMaxItems)
         return fail(NSA_ERR_UNSUPPORTED, "decode supports windows up to " +
                                              std::to_string(64 * (nsa::kDecodeMaxItems - 2)) + " tokens");
+    if (s.lp / s.s + s.l / s.s - 1 > nsa::kDecodeSplitKeys)
+        return fail(NSA_ERR_UNSUPPORTED, "decode needs (slc_block + cmp_block) / cmp_stride - 1 <= " +
+                                             std::to_string(nsa::kDecodeSplitKeys));
     if (w.n_split > nsa::kDecodeMaxSplits)
         return fail(NSA_ERR_UNSUPPORTED, "decode supports at most " +
                                              std::to_string(nsa::kDecodeMaxSplits * nsa::kDecodeSplitKeys) +

@@ -94,14 +94,29 @@ __host__ __device__ __forceinline__ int vt_pos(int k) {
     return (k < 16) ? (8 * (k >> 2) + (k & 3)) : (8 * ((k - 16) >> 2) + 4 + (k & 3));
 }
 
-// Max / sum over the four lanes that share a query column (lanes l, l^16, l^32, l^48).
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+// Exchanges across 16-lane rows without the LDS crossbar: gfx950's v_permlane16_swap
+// (v_permlane32_swap) swaps the odd rows (upper half) of one register with the even rows
+// (lower half) of another.  Swapping a value with itself leaves, in each lane, v[i] in one
+// result and v[i ^ 16] (v[i ^ 32]) in the other, so a commutative op of the two results
+// combines lane i with its partner.  All 64 lanes must be active.
+__device__ __forceinline__ u32x2 swap16(uint32_t v) { return __builtin_amdgcn_permlane16_swap(v, v, false, false); }
+__device__ __forceinline__ u32x2 swap32(uint32_t v) { return __builtin_amdgcn_permlane32_swap(v, v, false, false); }
+
+// Max / sum over the four lanes that share a query column (lanes l, l^16, l^32, l^48);
+// every lane ends with the result.
 __device__ __forceinline__ float col_max(float v) {
-    v = fmaxf(v, __shfl_xor(v, 16));
-    return fmaxf(v, __shfl_xor(v, 32));
+    u32x2 r = swap16(__float_as_uint(v));
+    v = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    r = swap32(__float_as_uint(v));
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float col_sum(float v) {
-    v += __shfl_xor(v, 16);
-    return v + __shfl_xor(v, 32);
+    u32x2 r = swap16(__float_as_uint(v));
+    v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    r = swap32(__float_as_uint(v));
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 // DPP lane moves within a 16-lane row (VALU, no LDS traffic).
@@ -137,6 +152,11 @@ struct QMap {
     __device__ static int token(int c, int li) { return (li / GL) * (NQ / CL) + c / CL; }
     __device__ static int head(int c, int li) { return CL * (li % GL) + c % CL; }
 };
+
+// Workgroup barrier that orders LDS accesses only: this wave's LDS operations complete,
+// then s_barrier.  Unlike __syncthreads it does not wait for outstanding global loads or
+// stores, so prefetched tiles stay in flight across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // Offset (in elements) of the 8 contraction elements a lane of row-group lq holds for
 // MFMA step ds when a row of the operand is read straight from memory.  The contraction

@@ -10,15 +10,17 @@
 //                         Emits, relative to the split's per-head max m: the sum l, the
 //                         unnormalized o^T, and per-head partial block sums
 //                         A[h][j] = sum over this split's keys overlapping block j of
-//                         2^(x - m).
+//                         2^(x - m).  The same launch runs the sliding window's item
+//                         groups (below), which do not depend on the selection.
 //   decode_select_kernel  per (sequence, group): lse per head from the split (m, l) and
 //                         the split weights w_s = 2^(m_s - lse); block score
 //                         score[j] = sum_h sum_s w_s,h A_s[h][j] (the exact normalized
 //                         compressed probabilities, summed as in prefill); then the
 //                         shared top-n.
-//   decode_attn_kernel    one wave per item (a selected block, or a 64-token piece of the
-//                         window): exact softmax over its keys; the 4 items of a workgroup
-//                         (same branch) are combined in LDS into one partial (m, l, o^T).
+//   decode_attn_kernel    the selected blocks' item groups.  An item group is 4 waves, one
+//                         item each (a selected block, or a 64-token piece of the window):
+//                         exact softmax over its keys; the 4 items are combined in LDS into
+//                         one partial (m, l, o^T).
 //   decode_merge_kernel   o_cmp = sum_s w_s o_s, merges the partials of each branch and
 //                         applies the gates; one thread per output element.
 // Value rows stay key-major: each wave stores its value tile row-major in LDS and builds
@@ -50,7 +52,7 @@ struct KeyTile64 {
     static constexpr int NVC = 64 * DV / 8 / 64;   // 16-byte value chunks per lane
     bf16x8 ka[4][NDS];
     u32x4 vr[NVC];
-    __device__ __forceinline__ void load(const u16* kg, const u16* vg, int key0, int nrows) {
+    __device__ __forceinline__ void load_k(const u16* kg, int key0, int nrows) {
         const int lane = threadIdx.x & 63, li = lane & 15, lq = lane >> 4;
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt) {
@@ -58,12 +60,19 @@ struct KeyTile64 {
 #pragma unroll
             for (int ds = 0; ds < NDS; ++ds) ka[kt][ds] = ld8(kp + kpair_off(ds, lq));
         }
+    }
+    __device__ __forceinline__ void load_v(const u16* vg, int key0, int nrows) {
+        const int lane = threadIdx.x & 63;
 #pragma unroll
         for (int i = 0; i < NVC; ++i) {
             const int idx = lane + 64 * i;
             const int row = idx / (DV / 8), col = (idx % (DV / 8)) * 8;
             vr[i] = *reinterpret_cast<const u32x4*>(vg + (size_t)min(key0 + row, nrows - 1) * DV + col);
         }
+    }
+    __device__ __forceinline__ void load(const u16* kg, const u16* vg, int key0, int nrows) {
+        load_k(kg, key0, nrows);
+        load_v(vg, key0, nrows);
     }
     // value rows to a row-major LDS tile [64][STR]
     template <int STR>
@@ -98,205 +107,19 @@ __device__ __forceinline__ void load_q(const u16* q, int b, int H, int g, int G,
 }  // namespace
 
 // ---------------------------------------------------------------------------
-template <int DK, int DV>
-__global__ __launch_bounds__(256, 2) void decode_cmp_kernel(DecodeParams p) {
-    constexpr int NDS = DK / 32, NDT = DV / 16;
-    constexpr int VSTR = DV + 16;
-    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-    u16* vs_all = reinterpret_cast<u16*>(smem);                              // [4][64][VSTR]
-    float* wm = reinterpret_cast<float*>(vs_all + 4 * 64 * VSTR);            // [4][16]
-    float* wl = wm + 64;                                                     // [4][16]
-    // after the value products the tile region is reused:
-    float* po = reinterpret_cast<float*>(smem);                              // [4][DV][16]
-    float* psum = po + 4 * DV * 16;                                          // [16][kPsumStride]
-
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int li = lane & 15, lq = lane >> 4;
-    const int b = blockIdx.z, g = blockIdx.y, sp = blockIdx.x;
-    const int G = p.G, H = p.Hkv * G, Nc = p.Nc;
-    const int t = query_pos(p.cache_len, b, p.L);
-    const int nv = visible_count(t, p.l, p.s, Nc);
-    const int kbeg = sp * kDecodeSplitKeys;
-    const int kw = kbeg + 64 * wave;
-    const size_t pbase = ((size_t)b * p.Hkv + g) * p.n_split + sp;
-    if (kbeg >= nv) {
-        if (threadIdx.x < 16) {
-            p.part_m[pbase * 16 + threadIdx.x] = -INFINITY;
-            p.part_l[pbase * 16 + threadIdx.x] = 0.f;
-        }
-        return;
-    }
-    KeyTile64<DK, DV> tile;
-    tile.load(p.Kc + ((size_t)b * p.Hkv + g) * (size_t)Nc * DK, p.Vc + ((size_t)b * p.Hkv + g) * (size_t)Nc * DV, kw,
-              Nc);
-    bf16x8 qf[NDS];
-    load_q<DK>(p.q, b, H, g, G, qf);
-    f32x4 sacc[4];
-    tile.scores(qf, sacc);
-    u16* vs = vs_all + wave * 64 * VSTR;
-    tile.template store_v<VSTR>(vs);
-
-    float x[16];
-    float tmax = -INFINITY;
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int key = kw + 16 * kt + 4 * lq + r;
-            x[kt * 4 + r] = key < nv ? sacc[kt][r] * p.scale_log2 : -INFINITY;
-            tmax = fmaxf(tmax, x[kt * 4 + r]);
-        }
-    tmax = col_max(tmax);
-    if (lq == 0) wm[wave * 16 + li] = tmax;
-    __syncthreads();
-    const float M = fmaxf(fmaxf(wm[li], wm[16 + li]), fmaxf(wm[32 + li], wm[48 + li]));
-    f32x4 pv[4];
-    float ls = 0.f;
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const float pr = fast_exp2(x[kt * 4 + r] - M);
-            pv[kt][r] = pr;
-            ls += pr;
-        }
-    ls = col_sum(ls);
-    if (lq == 0) wl[wave * 16 + li] = ls;
-    f32x4 oacc[NDT];
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) oacc[dt] = zero4();
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        bf16x8 bh, bl;
-        pack_p_split(pv[2 * u], pv[2 * u + 1], bh, bl);
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) {
-            const bf16x8 a = ld_vt_tr(vs, VSTR, 32 * u, 16 * dt);
-            oacc[dt] = mfma16(a, bh, oacc[dt]);
-            oacc[dt] = mfma16(a, bl, oacc[dt]);
-        }
-    }
-    __syncthreads();  // every wave is done with its value tile: reuse the region
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) po[(wave * DV + 16 * dt + 4 * lq + r) * 16 + li] = oacc[dt][r];
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) psum[li * kPsumStride + 64 * wave + 16 * kt + 4 * lq + r] = pv[kt][r];
-    __syncthreads();
-    for (int idx = threadIdx.x; idx < DV * 16; idx += 256) {
-        const float v = po[idx] + po[DV * 16 + idx] + po[2 * DV * 16 + idx] + po[3 * DV * 16 + idx];
-        p.part_o[pbase * DV * 16 + idx] = v;
-    }
-    if (threadIdx.x < 16) {
-        const int hh = threadIdx.x;
-        p.part_m[pbase * 16 + hh] = fmaxf(fmaxf(wm[hh], wm[16 + hh]), fmaxf(wm[32 + hh], wm[48 + hh]));
-        p.part_l[pbase * 16 + hh] = wl[hh] + wl[16 + hh] + wl[32 + hh] + wl[48 + hh];
-    }
-    // per-head partial block sums over this split's keys (ascending key order)
-    const int jlo = (kbeg * p.s) / p.lp;
-    const int jhi = min(((kbeg + kDecodeSplitKeys - 1) * p.s + p.l - 1) / p.lp, p.n_slc - 1);
-    const int nj = jhi - jlo + 1;
-    for (int idx = threadIdx.x; idx < G * nj; idx += 256) {
-        const int hh = idx / nj, j = jlo + idx % nj;
-        const int num = j * p.lp - p.l + 1;
-        const int ilo = max(kbeg, num > 0 ? (num + p.s - 1) / p.s : 0);
-        const int ihi = min(kbeg + kDecodeSplitKeys - 1, (j * p.lp + p.lp - 1) / p.s);
-        float acc = 0.f;
-        for (int i = ilo; i <= ihi; ++i) acc += psum[hh * kPsumStride + (i - kbeg)];
-        p.part_a[(pbase * 16 + hh) * p.jb + (j - jlo)] = acc;
-    }
-}
-
-// ---------------------------------------------------------------------------
-template <int NU>
-__global__ __launch_bounds__(1024) void decode_select_kernel(DecodeParams p) {
-    extern __shared__ float sm[];
-    float* f = sm;                       // [n_split][16]
-    float* sc = f + p.n_split * 16;      // [n_slc]
-    const int g = blockIdx.x, b = blockIdx.y;
-    const int lane = threadIdx.x & 63;
-    const int t = query_pos(p.cache_len, b, p.L);
-    const int nv = visible_count(t, p.l, p.s, p.Nc);
-    const int ns = (nv + kDecodeSplitKeys - 1) / kDecodeSplitKeys;
-    const int jc = t / p.lp;
-    const size_t bg = (size_t)b * p.Hkv + g;
-    const size_t pb0 = bg * p.n_split;
-    // per-head log-sum-exp over the splits: lane = head + 16 * q holds splits q + 4i
-    // (at most kDecodeMaxSplits splits, all loads issued together)
-    if (threadIdx.x < 64) {
-        constexpr int NI = kDecodeMaxSplits / 4;
-        const int hh = lane & 15, q = lane >> 4;
-        float mv[NI], lv[NI];
-#pragma unroll
-        for (int i = 0; i < NI; ++i) {
-            const int s0 = q + 4 * i;
-            mv[i] = s0 < ns ? p.part_m[(pb0 + s0) * 16 + hh] : -INFINITY;
-            lv[i] = s0 < ns ? p.part_l[(pb0 + s0) * 16 + hh] : 0.f;
-        }
-        float M = -INFINITY;
-#pragma unroll
-        for (int i = 0; i < NI; ++i) M = fmaxf(M, mv[i]);
-        M = col_max(M);
-        float L = 0.f;
-#pragma unroll
-        for (int i = 0; i < NI; ++i)
-            if (mv[i] > -INFINITY) L += lv[i] * fast_exp2(mv[i] - M);
-        L = col_sum(L);
-        const float lse2 = M + __log2f(L);
-#pragma unroll
-        for (int i = 0; i < NI; ++i) {
-            const int s0 = q + 4 * i;
-            if (s0 < ns) {
-                const float w = (L > 0.f && mv[i] > -INFINITY) ? fast_exp2(mv[i] - lse2) : 0.f;
-                f[s0 * 16 + hh] = w;
-                p.cmp_w[(pb0 + s0) * 16 + hh] = w;
-            }
-        }
-    }
-    __syncthreads();
-    // block scores: compressed keys [ilo, ihi] overlap block j; at most two splits hold them
-    for (int j = threadIdx.x; j <= jc; j += 1024) {
-        const int num = j * p.lp - p.l + 1;
-        const int ilo = num > 0 ? (num + p.s - 1) / p.s : 0;
-        const int ihi = min((j * p.lp + p.lp - 1) / p.s, nv - 1);
-        float acc = 0.f;
-        if (ilo <= ihi) {
-            const int sa = ilo / kDecodeSplitKeys, sb = ihi / kDecodeSplitKeys;
-            for (int s0 = sa; s0 <= sb; ++s0) {
-                const int jlo = (s0 * kDecodeSplitKeys * p.s) / p.lp;
-                const float* pa = p.part_a + (pb0 + s0) * 16 * p.jb + (j - jlo);
-#pragma unroll
-                for (int hh = 0; hh < 16; ++hh)
-                    if (hh < p.G) acc += f[s0 * 16 + hh] * pa[hh * p.jb];
-            }
-        }
-        sc[j] = acc;
-    }
-    __syncthreads();
-    if (threadIdx.x < 64)
-        select_blocks_wave<NU>(sc, jc, p.top_n, p.n_init, p.n_local, p.sel_ws + bg * p.top_n,
-                               p.sel_out ? p.sel_out + bg * p.top_n : nullptr);
-}
-
-// ---------------------------------------------------------------------------
 // A workgroup holds 4 waves; wave w takes item 4*gi + w of one branch (a selected block,
 // or a 64-token piece of the window) and computes its exact softmax partial (m, l, o^T);
 // the 4 partials are combined in LDS and one partial per workgroup is written.
 template <int DK, int DV>
-__global__ __launch_bounds__(256, 2) void decode_attn_kernel(DecodeParams p) {
+__device__ void attn_group(const DecodeParams& p, int gi, int g, int b, unsigned char* smem) {
     constexpr int NDS = DK / 32, NDT = DV / 16;
     constexpr int VSTR = DV + 16;
-    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, li = lane & 15, lq = lane >> 4;
     u16* vs = reinterpret_cast<u16*>(smem) + wave * 64 * VSTR;   // this wave's value tile
     // after the items: [4][DV][16] partial o, then [4][16] m and l
     float* mo = reinterpret_cast<float*>(smem);
     float* mm = mo + 4 * DV * 16;
     float* ml = mm + 64;
-    const int gi = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
     const int G = p.G, H = p.Hkv * G;
     const int t = query_pos(p.cache_len, b, p.L);
     const int n_sg = (p.top_n + 3) / 4;
@@ -409,6 +232,238 @@ __global__ __launch_bounds__(256, 2) void decode_attn_kernel(DecodeParams p) {
 }
 
 // ---------------------------------------------------------------------------
+template <int DK, int DV>
+__global__ __launch_bounds__(256, 2) void decode_cmp_kernel(DecodeParams p) {
+    constexpr int NDS = DK / 32, NDT = DV / 16;
+    constexpr int VSTR = DV + 16;
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    u16* vs_all = reinterpret_cast<u16*>(smem);                              // [4][64][VSTR]
+    float* wm = reinterpret_cast<float*>(vs_all + 4 * 64 * VSTR);            // [4][16]
+    float* wl = wm + 64;                                                     // [4][16]
+    // after the value products the tile region is reused:
+    float* po = reinterpret_cast<float*>(smem);                              // [4][DV][16]
+    float* psum = po + 4 * DV * 16;                                          // [16][kPsumStride]
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int li = lane & 15, lq = lane >> 4;
+    const int b = blockIdx.z, g = blockIdx.y, sp = blockIdx.x;
+    if (sp >= p.n_split) {   // a window item group (independent of the selection)
+        attn_group<DK, DV>(p, (p.top_n + 3) / 4 + sp - p.n_split, g, b, smem);
+        return;
+    }
+    const int G = p.G, H = p.Hkv * G, Nc = p.Nc;
+    const int t = query_pos(p.cache_len, b, p.L);
+    const int nv = visible_count(t, p.l, p.s, Nc);
+    const int kbeg = sp * kDecodeSplitKeys;
+    const int kw = kbeg + 64 * wave;
+    const size_t pbase = ((size_t)b * p.Hkv + g) * p.n_split + sp;
+    if (kbeg >= nv) {
+        if (threadIdx.x < 16) {
+            p.part_m[pbase * 16 + threadIdx.x] = -INFINITY;
+            p.part_l[pbase * 16 + threadIdx.x] = 0.f;
+        }
+        return;
+    }
+    KeyTile64<DK, DV> tile;
+    tile.load(p.Kc + ((size_t)b * p.Hkv + g) * (size_t)Nc * DK, p.Vc + ((size_t)b * p.Hkv + g) * (size_t)Nc * DV, kw,
+              Nc);
+    bf16x8 qf[NDS];
+    load_q<DK>(p.q, b, H, g, G, qf);
+    f32x4 sacc[4];
+    tile.scores(qf, sacc);
+    u16* vs = vs_all + wave * 64 * VSTR;
+    tile.template store_v<VSTR>(vs);
+
+    float x[16];
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int key = kw + 16 * kt + 4 * lq + r;
+            x[kt * 4 + r] = key < nv ? sacc[kt][r] * p.scale_log2 : -INFINITY;
+            tmax = fmaxf(tmax, x[kt * 4 + r]);
+        }
+    tmax = col_max(tmax);
+    if (lq == 0) wm[wave * 16 + li] = tmax;
+    __syncthreads();
+    const float M = fmaxf(fmaxf(wm[li], wm[16 + li]), fmaxf(wm[32 + li], wm[48 + li]));
+    f32x4 pv[4];
+    float ls = 0.f;
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float pr = fast_exp2(x[kt * 4 + r] - M);
+            pv[kt][r] = pr;
+            ls += pr;
+        }
+    ls = col_sum(ls);
+    if (lq == 0) wl[wave * 16 + li] = ls;
+    f32x4 oacc[NDT];
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) oacc[dt] = zero4();
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        bf16x8 bh, bl;
+        pack_p_split(pv[2 * u], pv[2 * u + 1], bh, bl);
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+            const bf16x8 a = ld_vt_tr(vs, VSTR, 32 * u, 16 * dt);
+            oacc[dt] = mfma16(a, bh, oacc[dt]);
+            oacc[dt] = mfma16(a, bl, oacc[dt]);
+        }
+    }
+    __syncthreads();  // every wave is done with its value tile: reuse the region
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) po[(wave * DV + 16 * dt + 4 * lq + r) * 16 + li] = oacc[dt][r];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) psum[li * kPsumStride + 64 * wave + 16 * kt + 4 * lq + r] = pv[kt][r];
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < DV * 16; idx += 256) {
+        const float v = po[idx] + po[DV * 16 + idx] + po[2 * DV * 16 + idx] + po[3 * DV * 16 + idx];
+        p.part_o[pbase * DV * 16 + idx] = v;
+    }
+    if (threadIdx.x < 16) {
+        const int hh = threadIdx.x;
+        p.part_m[pbase * 16 + hh] = fmaxf(fmaxf(wm[hh], wm[16 + hh]), fmaxf(wm[32 + hh], wm[48 + hh]));
+        p.part_l[pbase * 16 + hh] = wl[hh] + wl[16 + hh] + wl[32 + hh] + wl[48 + hh];
+    }
+    // per-head partial block sums over this split's keys (ascending key order).  With
+    // s | l and s | l', compressed key i overlaps block j iff j*a - c < i < j*a + a, where
+    // a = l'/s and c = l/s.  Thread (jj, hh) takes head hh of blocks jlo + jj + 16k.
+    const int a = p.lp / p.s, c = p.l / p.s;
+    const int jlo = kbeg / a;
+    const int jhi = min((kbeg + kDecodeSplitKeys - 1 + c - 1) / a, p.n_slc - 1);
+    const int hh = threadIdx.x & 15;
+    if (hh < G) {
+        const float* row = psum + hh * kPsumStride - kbeg;
+        for (int j = jlo + (threadIdx.x >> 4); j <= jhi; j += 16) {
+            const int ilo = max(kbeg, j * a - c + 1);
+            const int ihi = min(kbeg + kDecodeSplitKeys - 1, j * a + a - 1);
+            float acc = 0.f;
+            for (int i = ilo; i <= ihi; ++i) acc += row[i];
+            p.part_a[(pbase * p.jb + (j - jlo)) * 16 + hh] = acc;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Selection of one (sequence, group) by a 1024-thread workgroup (the block-score loads of
+// 16 waves in flight together); sm holds n_split * 16 + n_slc floats.
+template <int NU>
+__device__ void select_unit(const DecodeParams& p, int g, int b, float* sm) {
+    float* f = sm;                       // [n_split][16]
+    float* sc = f + p.n_split * 16;      // [n_slc]
+    const int lane = threadIdx.x & 63;
+    const int t = query_pos(p.cache_len, b, p.L);
+    const int nv = visible_count(t, p.l, p.s, p.Nc);
+    const int ns = (nv + kDecodeSplitKeys - 1) / kDecodeSplitKeys;
+    const int jc = t / p.lp;
+    const size_t bg = (size_t)b * p.Hkv + g;
+    const size_t pb0 = bg * p.n_split;
+    // per-head log-sum-exp over the splits: lane = head + 16 * q holds splits q + 4i
+    // (at most kDecodeMaxSplits splits, all loads issued together)
+    if (threadIdx.x < 64) {
+        constexpr int NI = kDecodeMaxSplits / 4;
+        const int hh = lane & 15, q = lane >> 4;
+        float mv[NI], lv[NI];
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            const int s0 = q + 4 * i;
+            mv[i] = s0 < ns ? p.part_m[(pb0 + s0) * 16 + hh] : -INFINITY;
+            lv[i] = s0 < ns ? p.part_l[(pb0 + s0) * 16 + hh] : 0.f;
+        }
+        float M = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < NI; ++i) M = fmaxf(M, mv[i]);
+        M = col_max(M);
+        float L = 0.f;
+#pragma unroll
+        for (int i = 0; i < NI; ++i)
+            if (mv[i] > -INFINITY) L += lv[i] * fast_exp2(mv[i] - M);
+        L = col_sum(L);
+        const float lse2 = M + __log2f(L);
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            const int s0 = q + 4 * i;
+            if (s0 < ns) {
+                const float w = (L > 0.f && mv[i] > -INFINITY) ? fast_exp2(mv[i] - lse2) : 0.f;
+                f[s0 * 16 + hh] = w;
+                p.cmp_w[(pb0 + s0) * 16 + hh] = w;
+            }
+        }
+    }
+    __syncthreads();
+    // block scores: compressed keys [ilo, ihi] overlap block j (s | l and s | l': with
+    // a = l'/s and c = l/s they are j*a - c + 1 .. j*a + a - 1); at most two splits hold them
+    // Thread tid scores blocks tid + 1024r (NU * 64 / 1024 of them); every load is issued
+    // before any sum.  Rows past jc read block jc's rows and are not stored.
+    const int a = p.lp / p.s, c = p.l / p.s;
+    constexpr int NR = NU * 64 / 1024 > 0 ? NU * 64 / 1024 : 1;
+    f32x4 v[NR][2][4];
+    int sa[NR], sb[NR];
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+        const int j = min((int)threadIdx.x + 1024 * r, jc);
+        const int ilo = max(0, j * a - c + 1);
+        const int ihi = max(ilo, min(j * a + a - 1, nv - 1));
+        sa[r] = ilo / kDecodeSplitKeys;
+        sb[r] = ihi / kDecodeSplitKeys;
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+            // clamped into the workspace; a clamped (unused) row may be any split's
+            const int s0 = min(min(sa[r] + h2, sb[r]), p.n_split - 1);
+            const int jj = min(max(j - (s0 * kDecodeSplitKeys) / a, 0), p.jb - 1);
+            const f32x4* pa = reinterpret_cast<const f32x4*>(p.part_a + ((pb0 + s0) * p.jb + jj) * 16);
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) v[r][h2][q4] = pa[q4];
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+        const int j = (int)threadIdx.x + 1024 * r;
+        if (j > jc) continue;
+        const int ilo = max(0, j * a - c + 1);
+        const int ihi = min(j * a + a - 1, nv - 1);
+        float acc = 0.f;
+        if (ilo <= ihi) {
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2) {
+                if (sa[r] + h2 > sb[r]) continue;
+                const int s0 = sa[r] + h2;
+#pragma unroll
+                for (int hh = 0; hh < 16; ++hh)
+                    acc += hh < p.G ? f[s0 * 16 + hh] * v[r][h2][hh >> 2][hh & 3] : 0.f;
+            }
+        }
+        sc[j] = acc;
+    }
+    __syncthreads();
+    if (threadIdx.x < 64)
+        select_blocks_wave<NU>(sc, jc, p.top_n, p.n_init, p.n_local, p.sel_ws + bg * p.top_n,
+                               p.sel_out ? p.sel_out + bg * p.top_n : nullptr);
+}
+
+// ---------------------------------------------------------------------------
+template <int NU>
+__global__ __launch_bounds__(1024) void decode_select_kernel(DecodeParams p) {
+    extern __shared__ float sm[];
+    select_unit<NU>(p, blockIdx.x, blockIdx.y, sm);
+}
+
+// The selected blocks' item groups: grid (ceil(top_n / 4), Hkv, B).
+template <int DK, int DV>
+__global__ __launch_bounds__(256, 2) void decode_attn_kernel(DecodeParams p) {
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    attn_group<DK, DV>(p, blockIdx.x, blockIdx.y, blockIdx.z, smem);
+}
+
+// ---------------------------------------------------------------------------
 // grid (DV / 16, Hkv, B): each thread owns one output (d, head) of the group; the
 // weights of the partial results are recomputed per workgroup (a few hundred values).
 template <int DV>
@@ -419,20 +474,55 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const size_t bg = (size_t)b * p.Hkv + g;
     const size_t ib0 = bg * p.n_items;
-    // wave 0: selected-branch items, wave 1: window items; lane = head + 16 * q holds
-    // items i0 + q + 4i (at most kDecodeMaxItems per branch, loads issued together)
     // partials: the selected branch's groups of 4 items, then the window's
     const int n_sg = (p.top_n + 3) / 4, n_grp = n_sg + (p.n_items - p.top_n + 3) / 4;
+    const int idx = blockIdx.x * 256 + threadIdx.x;   // (d, head) = (idx / 16, idx % 16)
+    const int hh = idx & 15, d = idx >> 4;
+    const int t = query_pos(p.cache_len, b, p.L);
+    const int ns = (visible_count(t, p.l, p.s, p.Nc) + kDecodeSplitKeys - 1) / kDecodeSplitKeys;
+    const bool use_c = (p.branches & 1) && ns > 0, use_s = (p.branches & 2) && n_sg > 0,
+               use_w = (p.branches & 4) && n_grp > n_sg;
+    // this thread's partial outputs and gate logits, all requested before the weights are
+    // known (indices clamped to valid partials; the sums below skip the clamped ones)
+    constexpr int NS = kDecodeMaxSplits, NG = kDecodeMaxItems / 4;
+    float cw[NS], co[NS], so[NG], wo[NG], z[3] = {0.f, 0.f, 0.f};
+    if (hh < G) {
+        if (use_c) {
+            const size_t pb0 = bg * p.n_split;
+#pragma unroll
+            for (int i = 0; i < NS; ++i) {
+                const int sp = min(i, ns - 1);
+                cw[i] = p.cmp_w[(pb0 + sp) * 16 + hh];
+                co[i] = p.part_o[(pb0 + sp) * DV * 16 + idx];
+            }
+        }
+        if (use_s) {
+#pragma unroll
+            for (int i = 0; i < NG; ++i) so[i] = p.att_o[(ib0 + min(i, n_sg - 1)) * DV * 16 + idx];
+        }
+        if (use_w) {
+#pragma unroll
+            for (int i = 0; i < NG; ++i) wo[i] = p.att_o[(ib0 + min(n_sg + i, n_grp - 1)) * DV * 16 + idx];
+        }
+        if (p.gates) {
+            const float* zp = p.gates + ((size_t)b * H + g * G + hh) * 3;
+            z[0] = zp[0];
+            z[1] = zp[1];
+            z[2] = zp[2];
+        }
+    }
+    // wave 0: selected-branch partials, wave 1: window partials; lane = head + 16 * q holds
+    // partials i0 + q + 4i (loads issued together)
     if (wave < 2) {
         constexpr int NI = kDecodeMaxItems / 4;
-        const int hh = lane & 15, q = lane >> 4;
+        const int h4 = lane & 15, q = lane >> 4;
         const int i0 = wave == 0 ? 0 : n_sg, i1 = wave == 0 ? n_sg : n_grp;
         float mv[NI], lv[NI];
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
             const int it = i0 + q + 4 * i;
-            mv[i] = it < i1 ? p.att_m[(ib0 + it) * 16 + hh] : -INFINITY;
-            lv[i] = it < i1 ? p.att_l[(ib0 + it) * 16 + hh] : 0.f;
+            mv[i] = it < i1 ? p.att_m[(ib0 + it) * 16 + h4] : -INFINITY;
+            lv[i] = it < i1 ? p.att_l[(ib0 + it) * 16 + h4] : 0.f;
         }
         float M = -INFINITY;
 #pragma unroll
@@ -446,44 +536,26 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p) {
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
             const int it = i0 + q + 4 * i;
-            if (it < i1) wsm[it * 16 + hh] = (mv[i] > -INFINITY && L > 0.f) ? fast_exp2(mv[i] - M) / L : 0.f;
+            if (it < i1) wsm[it * 16 + h4] = (mv[i] > -INFINITY && L > 0.f) ? fast_exp2(mv[i] - M) / L : 0.f;
         }
     }
     __syncthreads();
-    const int idx = blockIdx.x * 256 + threadIdx.x;   // (d, head) = (idx / 16, idx % 16)
-    const int hh = idx & 15, d = idx >> 4;
     if (hh >= G) return;
-    const int t = query_pos(p.cache_len, b, p.L);
-    const int ns = (visible_count(t, p.l, p.s, p.Nc) + kDecodeSplitKeys - 1) / kDecodeSplitKeys;
     float oc = 0.f, os = 0.f, ow = 0.f;
-    if (p.branches & 1) {
-        const size_t pb0 = bg * p.n_split;
-        for (int s0 = 0; s0 < ns; s0 += 8) {
+    if (use_c) {
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int sp = s0 + i;
-                const float w = sp < ns ? p.cmp_w[(pb0 + sp) * 16 + hh] : 0.f;
-                const float v = sp < ns ? p.part_o[(pb0 + sp) * DV * 16 + idx] : 0.f;
-                oc += w * v;
-            }
-        }
+        for (int i = 0; i < NS; ++i) oc += i < ns ? cw[i] * co[i] : 0.f;
     }
-    if (p.branches & 2) {
+    if (use_s) {
 #pragma unroll
-        for (int it = 0; it < 8; ++it)
-            if (it < n_sg) os += wsm[it * 16 + hh] * p.att_o[(ib0 + it) * DV * 16 + idx];
+        for (int i = 0; i < NG; ++i) os += i < n_sg ? wsm[i * 16 + hh] * so[i] : 0.f;
     }
-    if (p.branches & 4) {
+    if (use_w) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int it = n_sg + i;
-            if (it < n_grp) ow += wsm[it * 16 + hh] * p.att_o[(ib0 + it) * DV * 16 + idx];
-        }
+        for (int i = 0; i < NG; ++i) ow += n_sg + i < n_grp ? wsm[(n_sg + i) * 16 + hh] * wo[i] : 0.f;
     }
-    const int h = g * G + hh;
     float gc = 1.f, gs = 1.f, gw = 1.f;
     if (p.gates) {
-        const float* z = p.gates + ((size_t)b * H + h) * 3;
         gc = sigmoidf_(z[0]);
         gs = sigmoidf_(z[1]);
         gw = sigmoidf_(z[2]);
@@ -492,7 +564,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p) {
     if (p.branches & 1) y += gc * oc;
     if (p.branches & 2) y += gs * os;
     if (p.branches & 4) y += gw * ow;
-    p.O[((size_t)b * H + h) * DV + d] = f2bf(y);
+    p.O[((size_t)b * H + g * G + hh) * DV + d] = f2bf(y);
 }
 
 // ---------------------------------------------------------------------------
@@ -506,20 +578,21 @@ void allow_lds(K kernel, size_t bytes) {
 
 template <int DK, int DV>
 void decode_impl(const DecodeParams& p, hipStream_t st) {
-    const size_t tiles = (size_t)4 * 64 * (DV + 16) * 2;
+    const size_t lds_attn = (size_t)4 * 64 * (DV + 16) * 2;   // >= the combine buffers
     const size_t reuse = (size_t)4 * DV * 16 * 4 + (size_t)16 * kPsumStride * 4;
-    const size_t lds1 = (tiles > reuse ? tiles : reuse) + 128 * 4;
+    const size_t lds1 = (lds_attn > reuse ? lds_attn : reuse) + 128 * 4;
+    const int n_sg = (p.top_n + 3) / 4, n_wg = (p.n_items - p.top_n + 3) / 4;
     allow_lds(decode_cmp_kernel<DK, DV>, lds1);
-    decode_cmp_kernel<DK, DV><<<dim3(p.n_split, p.Hkv, p.B), 256, lds1, st>>>(p);
+    decode_cmp_kernel<DK, DV><<<dim3(p.n_split + n_wg, p.Hkv, p.B), 256, lds1, st>>>(p);
     const size_t lds2 = ((size_t)p.n_split * 16 + p.n_slc) * 4;
     NSA_NU_SWITCH(p.n_slc, {
         allow_lds(decode_select_kernel<NU>, lds2);
         decode_select_kernel<NU><<<dim3(p.Hkv, p.B), 1024, lds2, st>>>(p);
     });
-    const int n_grp = (p.top_n + 3) / 4 + (p.n_items - p.top_n + 3) / 4;
-    const size_t lds3 = (size_t)4 * 64 * (DV + 16) * 2;   // >= the combine buffers
-    allow_lds(decode_attn_kernel<DK, DV>, lds3);
-    decode_attn_kernel<DK, DV><<<dim3(n_grp, p.Hkv, p.B), 256, lds3, st>>>(p);
+    if (n_sg > 0) {
+        allow_lds(decode_attn_kernel<DK, DV>, lds_attn);
+        decode_attn_kernel<DK, DV><<<dim3(n_sg, p.Hkv, p.B), 256, lds_attn, st>>>(p);
+    }
     decode_merge_kernel<DV><<<dim3(DV / 16, p.Hkv, p.B), 256, (size_t)p.n_items * 16 * 4, st>>>(p);
 }
 }  // namespace

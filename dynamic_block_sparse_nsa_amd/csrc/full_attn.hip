@@ -189,7 +189,6 @@ __global__ __launch_bounds__(256, 2) void full_attn_kernel(FullParams p) {
         for (int dt = 0; dt < NDT; ++dt) {
             const uint32_t w0 = (uint32_t)f2bf(oacc[dt][c][0] * inv) | ((uint32_t)f2bf(oacc[dt][c][1] * inv) << 16);
             const uint32_t w1 = (uint32_t)f2bf(oacc[dt][c][2] * inv) | ((uint32_t)f2bf(oacc[dt][c][3] * inv) << 16);
-            typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
             st_stream(u32x2{w0, w1}, reinterpret_cast<u32x2*>(op + 16 * dt));
         }
     }

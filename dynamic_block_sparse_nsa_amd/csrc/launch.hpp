@@ -116,7 +116,7 @@ struct DecodeParams {
     float* part_m;             // [B,Hkv,n_split,16]
     float* part_l;             // [B,Hkv,n_split,16]
     float* part_o;             // [B,Hkv,n_split,DV,16]
-    float* part_a;             // [B,Hkv,n_split,16,jb]
+    float* part_a;             // [B,Hkv,n_split,jb,16]
     int32_t* sel_ws;           // [B,Hkv,top_n]
     float* cmp_w;              // [B,Hkv,n_split,16] weight 2^(m_split - lse) of each split
     float* att_m;              // [B,Hkv,n_items,16]

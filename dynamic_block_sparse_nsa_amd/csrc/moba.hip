@@ -361,7 +361,6 @@ __global__ __launch_bounds__(256) void moba_merge_kernel(MobaParams p) {
     }
     const float g = p.gates ? sigmoidf_(p.gates[row * 3 + 1]) : 1.f;
     const float inv = L > 0.f ? g / L : 0.f;
-    typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
     const u32x2 v = {(uint32_t)f2bf(acc[0] * inv) | ((uint32_t)f2bf(acc[1] * inv) << 16),
                      (uint32_t)f2bf(acc[2] * inv) | ((uint32_t)f2bf(acc[3] * inv) << 16)};
     st_stream(v, reinterpret_cast<u32x2*>(p.O + row * DV) + li);

@@ -24,75 +24,69 @@ __device__ __forceinline__ uint32_t f2key(float x) {
 }
 
 template <int CTRL>
-__device__ __forceinline__ uint64_t max_dpp_u64(uint64_t v) {
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, CTRL, 0xF, 0xF, false);
-    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), CTRL, 0xF, 0xF, false);
-    const uint64_t o = ((uint64_t)hi << 32) | lo;
+__device__ __forceinline__ uint32_t max_dpp_u32(uint32_t v) {
+    const uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
     return o > v ? o : v;
 }
 
-// Maximum over the 64 lanes (all lanes active): DPP moves inside each 16-lane row, then
-// two cross-row lane shuffles.
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-    v = max_dpp_u64<kDppQuadXor1>(v);
-    v = max_dpp_u64<kDppQuadXor2>(v);
-    v = max_dpp_u64<kDppRowHalfMirror>(v);
-    v = max_dpp_u64<kDppRowMirror>(v);
-#pragma unroll
-    for (int off = 16; off < 64; off <<= 1) {
-        const uint32_t lo = __shfl_xor((uint32_t)v, off);
-        const uint32_t hi = __shfl_xor((uint32_t)(v >> 32), off);
-        const uint64_t o = ((uint64_t)hi << 32) | lo;
-        v = o > v ? o : v;
-    }
-    return v;
+template <int CTRL>
+__device__ __forceinline__ uint32_t min_dpp_u32(uint32_t v) {
+    const uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)v, CTRL, 0xF, 0xF, false);
+    return o < v ? o : v;
 }
 
-// One wave selects the blocks of one (token, group) from scores sc[0..jc] and writes
-// top_n entries (ascending, -1 padded) to out (and to out2 when it is not null).  All 64
-// lanes must call it; NU * 64 must cover jc + 1.  Each lane keeps its candidates
-// (blocks lane, lane + 64, ...) in registers as 64-bit keys score:~index, so one wave
-// maximum per pick yields the best score and, among equal scores, the lowest index.
-template <int NU>
-__device__ inline void select_blocks_wave(const float* sc, int jc, int top_n, int n_init, int n_local,
-                                          int32_t* __restrict__ out, int32_t* __restrict__ out2 = nullptr) {
-    const int lane = threadIdx.x & 63;
-    const int n_elig = jc + 1;
-    const int f_init = min(n_init, n_elig);
-    const int f_loc_lo = max(0, jc - n_local + 1);
-    const int n_forced = f_init + (jc - f_loc_lo + 1) - max(0, f_init - f_loc_lo);
-    const int m = min(top_n, n_elig);
-    const int k = m - n_forced;
-    auto is_forced = [&](int j) { return j < f_init || j >= f_loc_lo; };
+// Minimum over the 64 lanes (all lanes active), wave-uniform.
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+    v = min_dpp_u32<kDppQuadXor1>(v);
+    v = min_dpp_u32<kDppQuadXor2>(v);
+    v = min_dpp_u32<kDppRowHalfMirror>(v);
+    v = min_dpp_u32<kDppRowMirror>(v);
+    u32x2 r = swap16(v);
+    v = r[0] < r[1] ? r[0] : r[1];
+    r = swap32(v);
+    v = r[0] < r[1] ? r[0] : r[1];
+    return (uint32_t)__builtin_amdgcn_readfirstlane((int)v);
+}
 
-    uint64_t key[NU];
-#pragma unroll
-    for (int u = 0; u < NU; ++u) {
-        const int j = lane + 64 * u;
-        const bool cand = j < n_elig && !is_forced(j);
-        key[u] = cand ? (((uint64_t)f2key(sc[j]) << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)j)) : 0ull;
+// Maximum over the 64 lanes (all lanes active): DPP moves inside each 16-lane row, then
+// the two row-swapping permutes; returned as a wave-uniform value.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+    v = max_dpp_u32<kDppQuadXor1>(v);
+    v = max_dpp_u32<kDppQuadXor2>(v);
+    v = max_dpp_u32<kDppRowHalfMirror>(v);
+    v = max_dpp_u32<kDppRowMirror>(v);
+    u32x2 r = swap16(v);
+    v = r[0] > r[1] ? r[0] : r[1];
+    r = swap32(v);
+    v = r[0] > r[1] ? r[0] : r[1];
+    return (uint32_t)__builtin_amdgcn_readfirstlane((int)v);
+}
+
+// Forced blocks of the query's own block jc: blocks 0..f_init-1 and f_loc_lo..jc.
+struct ForcedBlocks {
+    int n_elig, f_init, f_loc_lo, k;
+    __device__ ForcedBlocks(int jc, int top_n, int n_init, int n_local) {
+        n_elig = jc + 1;
+        f_init = min(n_init, n_elig);
+        f_loc_lo = max(0, jc - n_local + 1);
+        const int n_forced = f_init + (jc - f_loc_lo + 1) - max(0, f_init - f_loc_lo);
+        k = min(top_n, n_elig) - n_forced;   // picks left for the scores
     }
-    uint32_t picked = 0;  // bit u: candidate lane + 64u taken
-    for (int r = 0; r < k; ++r) {
-        uint64_t best = 0;
-#pragma unroll
-        for (int u = 0; u < NU; ++u) best = key[u] > best ? key[u] : best;
-        const uint64_t win = wave_max_u64(best);
-        if (win == 0) break;  // no candidate left (cannot happen for a valid configuration)
-        const int jw = (int)(0xFFFFFFFFu - (uint32_t)win);
-        if ((jw & 63) == lane) {
-#pragma unroll
-            for (int u = 0; u < NU; ++u)
-                if (u == (jw >> 6)) key[u] = 0ull;
-            picked |= 1u << (jw >> 6);
-        }
-    }
-    // compaction in ascending block order
+    __device__ bool forced(int j) const { return j < f_init || j >= f_loc_lo; }
+    __device__ bool candidate(int j) const { return j < n_elig && !forced(j); }
+};
+
+// Writes the forced blocks and the blocks flagged by taken(u) (slot u of this lane, block
+// lane + 64u) to out (and out2) in ascending order, padded with -1 to top_n.
+template <int NU, typename Taken>
+__device__ __forceinline__ void emit_selection(const ForcedBlocks& fb, int top_n, Taken taken,
+                                               int32_t* __restrict__ out, int32_t* __restrict__ out2) {
+    const int lane = threadIdx.x & 63;
     int base = 0;
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
         const int j = lane + 64 * u;
-        const bool take = j < n_elig && (is_forced(j) || ((picked >> u) & 1u));
+        const bool take = j < fb.n_elig && (fb.forced(j) || taken(u));
         const uint64_t mask = __ballot(take);
         const int pos = base + __popcll(mask & ((1ull << lane) - 1ull));
         if (take) {
@@ -105,6 +99,62 @@ __device__ inline void select_blocks_wave(const float* sc, int jc, int top_n, in
         out[c] = -1;
         if (out2) out2[c] = -1;
     }
+}
+
+// One wave selects the blocks of one (token, group) from scores sc[0..jc] and writes
+// top_n entries (ascending, -1 padded) to out (and to out2 when it is not null).  All 64
+// lanes must call it; NU * 64 must cover jc + 1.  Lane l holds the candidates l, l + 64,
+// ... as 64-bit entries key:slot (key: order-preserving 32-bit image of the score; slot u
+// stored as NU-1-u, so a larger entry is a better score or, for equal scores, the lower
+// block index).  Each lane sorts its entries once (bitonic network, best first); a pick is
+// then a wave maximum over the lanes' heads, and the winning lane shifts its list.
+template <int NU>
+__device__ inline void select_blocks_wave(const float* sc, int jc, int top_n, int n_init, int n_local,
+                                          int32_t* __restrict__ out, int32_t* __restrict__ out2 = nullptr) {
+    const int lane = threadIdx.x & 63;
+    const ForcedBlocks fb(jc, top_n, n_init, n_local);
+    uint64_t e[NU];
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+        const int j = lane + 64 * u;
+        e[u] = fb.candidate(j) ? (((uint64_t)f2key(sc[j]) << 32) | (uint32_t)(NU - 1 - u)) : 0ull;
+    }
+    // bitonic sort, descending
+#pragma unroll
+    for (int kk = 2; kk <= NU; kk <<= 1)
+#pragma unroll
+        for (int jj = kk >> 1; jj > 0; jj >>= 1)
+#pragma unroll
+            for (int i = 0; i < NU; ++i) {
+                const int l = i ^ jj;
+                if (l > i) {
+                    const bool desc = (i & kk) == 0;
+                    const uint64_t a = e[i], b = e[l];
+                    const bool sw = desc ? (b > a) : (a > b);
+                    e[i] = sw ? b : a;
+                    e[l] = sw ? a : b;
+                }
+            }
+    uint32_t picked = 0;  // bit u: candidate lane + 64u taken
+    for (int r = 0; r < fb.k; ++r) {
+        const uint32_t hk = (uint32_t)(e[0] >> 32);
+        const uint32_t m = wave_max_u32(hk);
+        if (m == 0) break;  // no candidate left (cannot happen for a valid configuration)
+        // the lowest block index among the heads scoring m
+        const int hu = NU - 1 - (int)(uint32_t)e[0];
+        const uint32_t jl = hk == m ? (uint32_t)(lane + 64 * hu) : 0xFFFFFFFFu;
+        const uint64_t holders = __ballot(hk == m);
+        const uint32_t jw = __popcll(holders) == 1
+                                ? (uint32_t)__builtin_amdgcn_readlane((int)jl, (int)__builtin_ctzll(holders))
+                                : wave_min_u32(jl);
+        if (jl == jw) {
+            picked |= 1u << hu;
+#pragma unroll
+            for (int u = 0; u + 1 < NU; ++u) e[u] = e[u + 1];
+            e[NU - 1] = 0ull;
+        }
+    }
+    emit_selection<NU>(fb, top_n, [&](int u) { return ((picked >> u) & 1u) != 0; }, out, out2);
 }
 
 // Candidates per lane for n_slc selection blocks (a power of two, at most 32).

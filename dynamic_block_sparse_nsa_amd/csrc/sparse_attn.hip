@@ -354,7 +354,6 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnParams p) {
         }
         const uint32_t w0 = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
         const uint32_t w1 = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);
-        typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
         st_stream(u32x2{w0, w1}, reinterpret_cast<u32x2*>(p.O + row * DV + d0));
     }
 }

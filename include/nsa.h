@@ -159,7 +159,10 @@ nsa_status nsa_sparse_attn_fwd(const nsa_config* cfg, const void* Q, const void*
  * selected and window branches, gated sum.
  *   q [B, H, d_k] bf16; caches [B, H_kv, L, d] bf16; compressed caches [B, H_kv, N_cmp(L), d];
  *   cache_len [B] int32 device array (1 <= cache_len <= L); gate_logits [B, H, 3] (NULL = 1);
- *   O [B, H, d_v] bf16; sel_idx_out [B, H_kv, top_n] (optional). */
+ *   O [B, H, d_v] bf16; sel_idx_out [B, H_kv, top_n] (optional).
+ * NSA_ERR_UNSUPPORTED for a mode other than linear phi with compressed-overlap scores, more
+ * than 8192 compressed keys, top_n > 32, windows over 1920 tokens, or
+ * (slc_block + cmp_block) / cmp_stride - 1 > 256. */
 nsa_status nsa_decode(const nsa_config* cfg, const void* q, const void* K_cache, const void* V_cache,
                       const int32_t* cache_len, const void* K_cmp_cache, const void* V_cmp_cache,
                       const float* gate_logits, void* O, int32_t* sel_idx_out,

@@ -151,6 +151,10 @@ def test_mode_specific_rules():
     assert L.nsa_score_select(_cfg(MOBA), fake, fake, None, fake, fake, None, None, 0, None) == 2
     # decode implements the NSA mode only
     assert L.nsa_decode(_cfg(MOBA), fake, fake, fake, fake, fake, fake, None, fake, None, fake, 1 << 40, None) == 3
+    # decode: a selection block overlapping more compressed keys than one 256-key split holds
+    wide = _cfg(DECODE, cmp_stride=1, slc_block=256, seq_len=1024)
+    assert L.nsa_decode(wide, fake, fake, fake, fake, fake, fake, None, fake, None, fake, 1 << 40, None) == 3
+    assert "cmp_stride" in L.nsa_last_error_detail().decode()
     # window branch needs a window
     assert L.nsa_sparse_attn_fwd(_cfg(P8K, window=0), fake, fake, fake, fake, fake, None, fake, None, 0, None) == 2
     # shorter than one compressed block

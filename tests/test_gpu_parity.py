@@ -243,6 +243,17 @@ def test_decode_varlen_small():
     _decode_case(cfg, np.array([4096, 1, 31, 32, 100, 2049], dtype=np.int32), cmp_from_oracle=True)
 
 
+def test_decode_varlen_multi_round():
+    # 32 x 32768: the compressed branch's workgroups take two 256-key splits each; the
+    # lengths put split and workgroup boundaries inside, at and just past the visible keys
+    cfg = DECODE.replace(name="decode_varlen_rounds", seq_len=32768, seed=29)
+    fixed = [32768, 1, 17, 31, 32, 33, 4111, 4112, 4127, 8207, 8208, 8223, 16384, 32767]
+    rng = np.random.default_rng(29)
+    lens = np.array(fixed + list(rng.integers(1, 32769, cfg.batch - len(fixed))), dtype=np.int32)
+    announce("decode varlen multi-round 32 x 32768")
+    _decode_case(cfg, lens, cmp_from_oracle=False)
+
+
 def test_decode_full():
     announce("decode full 32 x 65536")
     _decode_case(DECODE, None, cmp_from_oracle=False)
