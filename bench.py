@@ -330,6 +330,15 @@ def main():
         result["decode"] = {"workload": "nsa_decode_b32_l65536", "ms_per_step": round(dms, 4),
                             "bytes_per_step": int(bytes_step), "hbm_gbs": round(gbs, 1),
                             "hbm_peak_frac": round(gbs / PEAK_HBM_GBS, 4)}
+        # cache maintenance before each step: one new token per sequence into the caches,
+        # a new compressed entry every s calls (timed over 2*s calls, after the decode timing)
+        prep = ops.compress_prepare(dc, wk, wv, pk, pv)
+        kn = torch.randn((Bd, dc.num_kv_heads, 1, dc.d_k), generator=g, device=dev).to(torch.bfloat16)
+        vn = torch.randn((Bd, dc.num_kv_heads, 1, dc.d_v), generator=g, device=dev).to(torch.bfloat16)
+        clen2 = torch.full((Bd,), L - 4 * dc.cmp_stride * 4, dtype=torch.int32, device=dev)
+        acall = [lambda: ops.cache_append(dc, kn, vn, Kd, Vd, clen2, kcd, vcd, prep)]
+        pca, _ = time_calls(acall, 2 * dc.cmp_stride, 2, torch)
+        result["decode"]["append_us_per_token"] = round(float(pca.mean()) * 1e3, 2)
         del Kd, Vd, kcd, vcd
         torch.cuda.empty_cache()
 

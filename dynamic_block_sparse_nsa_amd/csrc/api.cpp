@@ -211,6 +211,20 @@ nsa_status nsa_workspace_size(const nsa_config* cfg, int op, size_t* bytes) {
     return NSA_OK;
 }
 
+// W^T and the position-embedding bias vec(pe) . W of both linear maps, into a buffer laid
+// out as compress_ws.
+void prepare_weights(const Shape& s, const CompressWs& w, const void* W_k, const void* W_v, const void* pe_k,
+                     const void* pe_v, void* ws, hipStream_t hs) {
+    using nsa::u16;
+    const int KDk = s.l * s.dk, KDv = s.l * s.dv;
+    u16* wtk = at<u16>(ws, w.wt_k);
+    u16* wtv = at<u16>(ws, w.wt_v);
+    nsa::launch_transpose_w(static_cast<const u16*>(W_k), wtk, KDk, s.dk, hs);
+    nsa::launch_transpose_w(static_cast<const u16*>(W_v), wtv, KDv, s.dv, hs);
+    nsa::launch_pe_bias(static_cast<const u16*>(pe_k), wtk, at<float>(ws, w.bias_k), KDk, s.dk, hs);
+    nsa::launch_pe_bias(static_cast<const u16*>(pe_v), wtv, at<float>(ws, w.bias_v), KDv, s.dv, hs);
+}
+
 nsa_status nsa_compress(const nsa_config* cfg, const void* K, const void* V, const void* W_k, const void* W_v,
                         const void* pe_k, const void* pe_v, void* K_cmp, void* V_cmp, void* ws, size_t ws_bytes,
                         void* stream) {
@@ -234,15 +248,11 @@ nsa_status nsa_compress(const nsa_config* cfg, const void* K, const void* V, con
     const CompressWs w = compress_ws(s);
     if ((st = check_ws(ws, ws_bytes, w.total)) != NSA_OK) return st;
     if ((st = check_align16(K, "K")) != NSA_OK || (st = check_align16(V, "V")) != NSA_OK) return st;
-    const int KDk = s.l * s.dk, KDv = s.l * s.dv;
+    prepare_weights(s, w, W_k, W_v, pe_k, pe_v, ws, hs);
     u16* wtk = at<u16>(ws, w.wt_k);
     u16* wtv = at<u16>(ws, w.wt_v);
     float* bk = at<float>(ws, w.bias_k);
     float* bv = at<float>(ws, w.bias_v);
-    nsa::launch_transpose_w(static_cast<const u16*>(W_k), wtk, KDk, s.dk, hs);
-    nsa::launch_transpose_w(static_cast<const u16*>(W_v), wtv, KDv, s.dv, hs);
-    nsa::launch_pe_bias(static_cast<const u16*>(pe_k), wtk, bk, KDk, s.dk, hs);
-    nsa::launch_pe_bias(static_cast<const u16*>(pe_v), wtv, bv, KDv, s.dv, hs);
     nsa::launch_compress_linear(static_cast<const u16*>(K), wtk, bk, static_cast<u16*>(K_cmp), BG, s.T, s.dk, s.dk,
                                 s.l, s.s, s.n_cmp, hs);
     nsa::launch_compress_linear(static_cast<const u16*>(V), wtv, bv, static_cast<u16*>(V_cmp), BG, s.T, s.dv, s.dv,
@@ -371,6 +381,57 @@ nsa_status nsa_sparse_attn_fwd(const nsa_config* cfg, const void* Q, const void*
     p.scale_log2 = s.scale * nsa::kLog2eHost;
     if (!nsa::launch_sparse_attn(s.dk, s.dv, p, s.B, hs)) return fail(NSA_ERR_UNSUPPORTED, "no attention kernel");
     return hip_check("sparse_attn");
+}
+
+nsa_status nsa_compress_prepare(const nsa_config* cfg, const void* W_k, const void* W_v, const void* pe_k,
+                                const void* pe_v, void* prep, size_t prep_bytes, void* stream) {
+    g_detail.clear();
+    Shape s;
+    nsa_status st = check_config(cfg, &s);
+    if (st != NSA_OK) return st;
+    if (s.phi != NSA_PHI_LINEAR) return fail(NSA_ERR_UNSUPPORTED, "prepared weights exist for the linear phi only");
+    if (!W_k || !W_v || !pe_k || !pe_v) return fail(NSA_ERR_NULL, "W_k, W_v, pe_k and pe_v are required");
+    const CompressWs w = compress_ws(s);
+    if ((st = check_ws(prep, prep_bytes, w.total)) != NSA_OK) return st;
+    prepare_weights(s, w, W_k, W_v, pe_k, pe_v, prep, as_stream(stream));
+    return hip_check("compress_prepare");
+}
+
+nsa_status nsa_cache_append(const nsa_config* cfg, const void* K_new, const void* V_new, int32_t n_new,
+                            void* K_cache, void* V_cache, int32_t* cache_len, void* K_cmp_cache, void* V_cmp_cache,
+                            const void* prep, size_t prep_bytes, void* stream) {
+    g_detail.clear();
+    Shape s;
+    nsa_status st = check_config(cfg, &s);
+    if (st != NSA_OK) return st;
+    if (s.phi != NSA_PHI_LINEAR) return fail(NSA_ERR_UNSUPPORTED, "cache maintenance implements the linear phi");
+    if (!K_new || !V_new || !K_cache || !V_cache || !cache_len || !prep)
+        return fail(NSA_ERR_NULL, "new tokens, caches, cache_len and the prepared weights are required");
+    if (s.n_cmp > 0 && (!K_cmp_cache || !V_cmp_cache)) return fail(NSA_ERR_NULL, "compressed caches are required");
+    if (n_new < 1 || n_new > s.T) return fail(NSA_ERR_SHAPE, "n_new must be in [1, capacity]");
+    const CompressWs w = compress_ws(s);
+    if ((st = check_ws(const_cast<void*>(prep), prep_bytes, w.total)) != NSA_OK) return st;
+    if ((st = check_align16(K_new, "K_new")) != NSA_OK || (st = check_align16(V_new, "V_new")) != NSA_OK ||
+        (st = check_align16(K_cache, "K_cache")) != NSA_OK || (st = check_align16(V_cache, "V_cache")) != NSA_OK)
+        return st;
+    using nsa::u16;
+    nsa::AppendParams p{};
+    p.K_new = static_cast<const u16*>(K_new);
+    p.V_new = static_cast<const u16*>(V_new);
+    p.K_cache = static_cast<u16*>(K_cache);
+    p.V_cache = static_cast<u16*>(V_cache);
+    p.cache_len = cache_len;
+    p.wt_k = at<const u16>(const_cast<void*>(prep), w.wt_k);
+    p.wt_v = at<const u16>(const_cast<void*>(prep), w.wt_v);
+    p.bias_k = at<const float>(const_cast<void*>(prep), w.bias_k);
+    p.bias_v = at<const float>(const_cast<void*>(prep), w.bias_v);
+    p.K_cmp = static_cast<u16*>(K_cmp_cache);
+    p.V_cmp = static_cast<u16*>(V_cmp_cache);
+    p.B = s.B; p.Hkv = s.Hkv; p.L = s.T; p.dk = s.dk; p.dv = s.dv; p.l = s.l; p.s = s.s; p.N = s.n_cmp;
+    p.n_new = n_new;
+    p.R = nsa::append_rows_per_group(n_new, s.s);
+    nsa::launch_cache_append(p, as_stream(stream));
+    return hip_check("cache_append");
 }
 
 nsa_status nsa_full_attn_fwd(const nsa_config* cfg, const void* Q, const void* K, const void* V, void* O, void* ws,

@@ -133,4 +133,23 @@ int decode_jb(int l, int s, int lp);
 int decode_items(int top_n, int window);
 bool launch_decode(int DK, int DV, const DecodeParams& p, hipStream_t st);
 
+// ---- decode cache maintenance ----
+struct AppendParams {
+    const u16* K_new;          // [B,Hkv,n_new,dk]
+    const u16* V_new;          // [B,Hkv,n_new,dv]
+    u16* K_cache;              // [B,Hkv,L,dk]
+    u16* V_cache;              // [B,Hkv,L,dv]
+    int32_t* cache_len;        // [B], advanced by n_new
+    const u16* wt_k;           // prepared weights: W_k^T [dk, l*dk], W_v^T [dv, l*dv]
+    const u16* wt_v;
+    const float* bias_k;       // vec(pe_k) . W_k [dk], vec(pe_v) . W_v [dv]
+    const float* bias_v;
+    u16* K_cmp;                // [B,Hkv,N,dk]
+    u16* V_cmp;                // [B,Hkv,N,dv]
+    int B, Hkv, L, dk, dv, l, s, N, n_new;
+    int R;                     // candidate blocks per group: append_rows_per_group(n_new, s)
+};
+int append_rows_per_group(int n_new, int s);
+void launch_cache_append(const AppendParams& p, hipStream_t st);
+
 }  // namespace nsa

@@ -66,8 +66,11 @@ def lib(build_if_missing: bool = True):
         L.nsa_sparse_attn_fwd.argtypes = [cp] + [_P] * 8 + [ctypes.c_size_t, _P]
         L.nsa_decode.argtypes = [cp] + [_P] * 10 + [ctypes.c_size_t, _P]
         L.nsa_full_attn_fwd.argtypes = [cp] + [_P] * 5 + [ctypes.c_size_t, _P]
+        L.nsa_compress_prepare.argtypes = [cp] + [_P] * 5 + [ctypes.c_size_t, _P]
+        L.nsa_cache_append.argtypes = [cp, _P, _P, ctypes.c_int32] + [_P] * 6 + [ctypes.c_size_t, _P]
         for f in ("nsa_workspace_size", "nsa_compress", "nsa_score_select", "nsa_select_from_scores",
-                  "nsa_sparse_attn_fwd", "nsa_decode", "nsa_full_attn_fwd"):
+                  "nsa_sparse_attn_fwd", "nsa_decode", "nsa_full_attn_fwd", "nsa_compress_prepare",
+                  "nsa_cache_append"):
             getattr(L, f).restype = ctypes.c_int
         L.nsa_status_string.argtypes = [ctypes.c_int]
         L.nsa_status_string.restype = ctypes.c_char_p
@@ -250,6 +253,39 @@ def decode(cfg: NSAConfig, q, K_cache, V_cache, cache_len, K_cmp, V_cmp, gates=N
                             _ptr(K_cmp), _ptr(V_cmp), _ptr(gates), _ptr(out), _ptr(sel), _ptr(ws), nws,
                             _stream(stream)))
     return out, sel
+
+
+def compress_prepare(cfg: NSAConfig, w_k, w_v, pe_k, pe_v, *, out=None, stream=None):
+    """nsa_compress_prepare: the prepared linear maps (a uint8 device buffer) for cache_append."""
+    l, dk, dv = cfg.cmp_block, cfg.d_k, cfg.d_v
+    _need(w_k, "w_k", torch.bfloat16, (l * dk, dk))
+    _need(w_v, "w_v", torch.bfloat16, (l * dv, dv))
+    _need(pe_k, "pe_k", torch.bfloat16, (l, dk))
+    _need(pe_v, "pe_v", torch.bfloat16, (l, dv))
+    prep, n = _workspace(cfg, OP_COMPRESS, w_k.device, out)
+    _check(lib().nsa_compress_prepare(ctypes.byref(c_config(cfg)), _ptr(w_k), _ptr(w_v), _ptr(pe_k), _ptr(pe_v),
+                                      _ptr(prep), n, _stream(stream)))
+    return prep
+
+
+def cache_append(cfg: NSAConfig, K_new, V_new, K_cache, V_cache, cache_len, K_cmp, V_cmp, prep, stream=None):
+    """nsa_cache_append: K_new/V_new [B,Hkv,n_new,d] into the caches at cache_len, new
+    compressed entries into K_cmp/V_cmp, cache_len advanced by n_new (all in place)."""
+    B, L, Hkv = cfg.batch, cfg.seq_len, cfg.num_kv_heads
+    if K_new is None or K_new.dim() != 4:
+        raise ValueError("K_new must be [B, Hkv, n_new, d_k]")
+    n_new = int(K_new.shape[2])
+    _need(K_new, "K_new", torch.bfloat16, (B, Hkv, n_new, cfg.d_k))
+    _need(V_new, "V_new", torch.bfloat16, (B, Hkv, n_new, cfg.d_v))
+    _need(K_cache, "K_cache", torch.bfloat16, (B, Hkv, L, cfg.d_k))
+    _need(V_cache, "V_cache", torch.bfloat16, (B, Hkv, L, cfg.d_v))
+    _need(cache_len, "cache_len", torch.int32, (B,))
+    _need(K_cmp, "K_cmp", torch.bfloat16, (B, Hkv, cfg.n_cmp, cfg.d_k))
+    _need(V_cmp, "V_cmp", torch.bfloat16, (B, Hkv, cfg.n_cmp, cfg.d_v))
+    _need(prep, "prep", torch.uint8)
+    _check(lib().nsa_cache_append(ctypes.byref(c_config(cfg)), _ptr(K_new), _ptr(V_new), n_new, _ptr(K_cache),
+                                  _ptr(V_cache), _ptr(cache_len), _ptr(K_cmp), _ptr(V_cmp), _ptr(prep),
+                                  prep.numel(), _stream(stream)))
 
 
 def prefill(cfg: NSAConfig, Q, K, V, w_k=None, w_v=None, pe_k=None, pe_v=None, gates=None, stream=None):

@@ -168,6 +168,30 @@ nsa_status nsa_decode(const nsa_config* cfg, const void* q, const void* K_cache,
                       const float* gate_logits, void* O, int32_t* sel_idx_out,
                       void* ws, size_t ws_bytes, void* stream);
 
+/* Decode cache maintenance (zjai.club notes, section 5: the compressed cache gains one entry
+ * every s tokens; section 13: decoding runs against these caches).
+ *
+ * nsa_compress_prepare writes the transposed linear maps and the position-embedding biases
+ * vec(pe) . W of both maps into `prep` (nsa_workspace_size(cfg, NSA_OP_COMPRESS) bytes,
+ * 256-byte aligned, caller-owned); prepare once per set of weights, reuse for every append.
+ * NSA_PHI_LINEAR only.
+ *
+ * nsa_cache_append appends n_new tokens per sequence: K_new [B, H_kv, n_new, d_k] and V_new
+ * [B, H_kv, n_new, d_v] (bf16) go to K_cache / V_cache [B, H_kv, L, d] at positions
+ * cache_len[b] .. cache_len[b] + n_new - 1, and every compressed block whose last token is
+ * one of them is written to K_cmp_cache / V_cmp_cache [B, H_kv, N_cmp(L), d] with the
+ * arithmetic of nsa_compress (the result equals nsa_compress over the grown cache, bit for
+ * bit).  Then cache_len[b] += n_new on the device, so a following nsa_decode on the same
+ * stream sees the new lengths.  Tokens that would land at or past L are dropped (cache_len
+ * saturates at L); the caller keeps cache_len[b] + n_new <= L.  Raw caches and new tokens
+ * must be 16-byte aligned.  Errors: NSA_ERR_SHAPE for n_new outside [1, L] or a misaligned array,
+ * NSA_ERR_UNSUPPORTED for a non-linear phi, NSA_ERR_WORKSPACE for a short or unaligned prep. */
+nsa_status nsa_compress_prepare(const nsa_config* cfg, const void* W_k, const void* W_v, const void* pe_k,
+                                const void* pe_v, void* prep, size_t prep_bytes, void* stream);
+nsa_status nsa_cache_append(const nsa_config* cfg, const void* K_new, const void* V_new, int32_t n_new,
+                            void* K_cache, void* V_cache, int32_t* cache_len, void* K_cmp_cache, void* V_cmp_cache,
+                            const void* prep, size_t prep_bytes, void* stream);
+
 /* Dense causal attention, the computation NSA is compared against (zjai.club notes, summary
  * bullets and section 13: a full-attention kernel written the same way as the NSA kernel):
  *   O[b,t,h,:] = softmax(scale * q . K[b,g,x,:] over x = 0..t) . V[b,g,x,:],  g = h / G.

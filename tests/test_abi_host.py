@@ -161,6 +161,28 @@ def test_mode_specific_rules():
     assert L.nsa_score_select(_cfg(P8K, seq_len=16), fake, fake, fake, fake, None, None, fake, 1 << 40, None) == 3
 
 
+def test_cache_maintenance_validation():
+    L = ops.lib()
+    fake = ctypes.c_void_p(0x1000)
+    big = 1 << 40
+    prep_ok = ctypes.c_void_p(0x100000)
+    # prepare: null weights, short or unaligned buffer, non-linear phi
+    assert L.nsa_compress_prepare(_cfg(DECODE), None, fake, fake, fake, prep_ok, big, None) == 1
+    assert L.nsa_compress_prepare(_cfg(DECODE), fake, fake, fake, fake, prep_ok, 16, None) == 4
+    assert L.nsa_compress_prepare(_cfg(DECODE), fake, fake, fake, fake, ctypes.c_void_p(0x100010), big, None) == 4
+    assert L.nsa_compress_prepare(_cfg(MOBA), fake, fake, fake, fake, prep_ok, big, None) == 3
+    # append: null arguments, n_new outside [1, L], short prep, unaligned tokens, mean phi
+    args = lambda n_new, prep_bytes=big, knew=fake: (knew, fake, n_new, fake, fake, fake, fake, fake, prep_ok,
+                                                     prep_bytes, None)
+    assert L.nsa_cache_append(_cfg(DECODE), *args(1, knew=None)) == 1
+    assert L.nsa_cache_append(_cfg(DECODE), *args(0)) == 2
+    assert L.nsa_cache_append(_cfg(DECODE), *args(DECODE.seq_len + 1)) == 2
+    assert L.nsa_cache_append(_cfg(DECODE), *args(1, prep_bytes=16)) == 4
+    assert L.nsa_cache_append(_cfg(DECODE), *args(1, knew=ctypes.c_void_p(0x1008))) == 2
+    assert L.nsa_cache_append(_cfg(MOBA), *args(1)) == 3
+    assert L.nsa_last_error_detail().decode() != ""
+
+
 def test_status_strings():
     L = ops.lib()
     for code in range(6):
