@@ -2,8 +2,9 @@
 // entry every s tokens; section 13: decoding runs against these caches).  Appending n_new
 // tokens to a sequence writes them into the raw caches and computes every compressed block
 // whose last token is among them, with exactly the arithmetic of the prefill compression
-// (compress_linear_kernel: the same MFMA order over the flattened block, the same fp32 bias
-// vec(PE).W, one bf16 rounding), so an appended entry equals the prefill's bit for bit.
+// (compress_linear_kernel: the same four reduction ranges, each in the same MFMA order, added
+// in the same order, the same fp32 bias vec(PE).W, one bf16 rounding), so an appended entry
+// equals the prefill's bit for bit.
 //
 // cache_append_kernel, grid (ceil(BG * R / 64), n_ct + 1): rows are (sequence-group,
 // candidate block) pairs, R candidates per group (the most blocks one append can complete);
@@ -80,18 +81,23 @@ __global__ __launch_bounds__(256) void cache_append_kernel(AppendParams p) {
     }
     if (!__any(valid)) return;
     const u16* wb = Wt + (size_t)(col0 + li) * KD + lq * 8;
-    f32x4 acc[4] = {zero4(), zero4(), zero4(), zero4()};
     // flattened block element kk + 8*lq: token kk / d of the block (32 | d), dim kk % d + 8*lq
-    for (int tok = 0; tok < p.l; ++tok) {
+    auto xa_at = [&](int kk) {
+        const int tok = kk / d, e = kk - tok * d;
         const int pos = blk * p.s + tok;
         const u16* src = pos >= c0 ? fresh + ((size_t)bg * p.n_new + (pos - c0)) * d
                                    : cache + ((size_t)bg * p.L + pos) * d;
-        for (int e0 = 0; e0 < d; e0 += 32) {
-            const int kk = tok * d + e0;
-            const bf16x8 a = ld8(src + e0 + lq * 8);
+        return src + e + lq * 8;
+    };
+    // the prefill compression's order: four reduction ranges, each ascending, added in order
+    f32x4 acc[4];
+    for (int q = 0; q < 4; ++q) {
+        int k_lo, k_hi;
+        compress_k_range(KD, q, k_lo, k_hi);
+        f32x4 part[4] = {zero4(), zero4(), zero4(), zero4()};
+        compress_mfma_range_at(xa_at, wb, KD, k_lo, k_hi, part);
 #pragma unroll
-            for (int c = 0; c < 4; ++c) acc[c] = mfma16(a, ld8(wb + (size_t)c * 16 * KD + kk), acc[c]);
-        }
+        for (int c = 0; c < 4; ++c) acc[c] = q == 0 ? part[c] : acc[c] + part[c];
     }
     // C layout: lane owns column col0 + 16c + li and rows 4*lq + r of the wave's 16
 #pragma unroll

@@ -153,6 +153,47 @@ struct QMap {
     __device__ static int head(int c, int li) { return CL * (li % GL) + c % CL; }
 };
 
+// The linear block map's reduction (KD = l*d elements) split into four 32-aligned ranges,
+// one per wave; range w is [k_lo, k_hi).
+__device__ __forceinline__ void compress_k_range(int KD, int w, int& k_lo, int& k_hi) {
+    const int steps = KD / 32;
+    k_lo = 32 * (steps * w / 4);
+    k_hi = 32 * (steps * (w + 1) / 4);
+}
+
+// acc[c] += A . B over k in [k_lo, k_hi) (ascending, 32 per MFMA) for the 16-row A operand
+// at xa (element kk of this lane's row at xa + kk) and the four 16-column B tiles at
+// wb + c*16*KD; loads are issued 8 steps ahead of their products.
+template <typename XAt>
+__device__ __forceinline__ void compress_mfma_range_at(XAt xa_at, const u16* wb, int KD, int k_lo, int k_hi,
+                                                       f32x4 (&acc)[4]) {
+    constexpr int U = 8;
+    int kk = k_lo;
+    for (; kk + 32 * U <= k_hi; kk += 32 * U) {
+        bf16x8 a[U], bw[U][4];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            a[u] = ld8(xa_at(kk + 32 * u));
+#pragma unroll
+            for (int c = 0; c < 4; ++c) bw[u][c] = ld8(wb + (size_t)c * 16 * KD + kk + 32 * u);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) acc[c] = mfma16(a[u], bw[u][c], acc[c]);
+    }
+    for (; kk < k_hi; kk += 32) {
+        const bf16x8 a = ld8(xa_at(kk));
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[c] = mfma16(a, ld8(wb + (size_t)c * 16 * KD + kk), acc[c]);
+    }
+}
+
+__device__ __forceinline__ void compress_mfma_range(const u16* xa, const u16* wb, int KD, int k_lo, int k_hi,
+                                                    f32x4 (&acc)[4]) {
+    compress_mfma_range_at([&](int kk) { return xa + kk; }, wb, KD, k_lo, k_hi, acc);
+}
+
 // Workgroup barrier that orders LDS accesses only: this wave's LDS operations complete,
 // then s_barrier.  Unlike __syncthreads it does not wait for outstanding global loads or
 // stores, so prefetched tiles stay in flight across it.

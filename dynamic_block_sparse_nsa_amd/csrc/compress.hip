@@ -47,28 +47,40 @@ __global__ __launch_bounds__(256) void pe_bias_kernel(const u16* __restrict__ pe
 }
 
 // ---------------------------------------------------------------------------
-// Linear phi.  Grid (ceil(N/64), dout/64, B*Hkv); 4 waves, wave w owns 16 output rows
-// and 64 output columns.  X: [BG][T][d]; out: [BG][N][dout].
+// Linear phi.  Grid (ceil(N/16), dout/64, B*Hkv): a workgroup owns 16 output rows x 64
+// output columns, and its 4 waves split the reduction (KD = l*d) into four 32-aligned
+// ranges (compress_k_range); each wave's products run in ascending k with its loads issued
+// 8 steps ahead, and the partials are added in wave order, then the bias.  The decode
+// cache append reproduces exactly this order.  X: [BG][T][d]; out: [BG][N][dout].
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void compress_linear_kernel(const u16* __restrict__ X,
                                                               const u16* __restrict__ Wt,
                                                               const float* __restrict__ bias,
                                                               u16* __restrict__ out, int T, int d, int dout,
                                                               int l, int s, int N) {
+    __shared__ f32x4 part[3][4][64];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int bg = blockIdx.z;
     const int KD = l * d;
-    const int row0 = blockIdx.x * 64 + wave * 16;
+    const int row0 = blockIdx.x * 16;
     const int col0 = blockIdx.y * 64;
     const int li = lane & 15, lq = lane >> 4;
     const int my_row = min(row0 + li, N - 1);  // clamp: rows past N are computed but not stored
     const u16* xa = X + (size_t)bg * T * d + (size_t)my_row * s * d + lq * 8;
     const u16* wb = Wt + (size_t)(col0 + li) * KD + lq * 8;
+    int k_lo, k_hi;
+    compress_k_range(KD, wave, k_lo, k_hi);
     f32x4 acc[4] = {zero4(), zero4(), zero4(), zero4()};
-    for (int kk = 0; kk < KD; kk += 32) {
-        const bf16x8 a = ld8(xa + kk);
+    compress_mfma_range(xa, wb, KD, k_lo, k_hi, acc);
+    if (wave > 0) {
 #pragma unroll
-        for (int c = 0; c < 4; ++c) acc[c] = mfma16(a, ld8(wb + (size_t)c * 16 * KD + kk), acc[c]);
+        for (int c = 0; c < 4; ++c) part[wave - 1][c][lane] = acc[c];
+    }
+    __syncthreads();
+    if (wave > 0) return;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        acc[c] = ((acc[c] + part[0][c][lane]) + part[1][c][lane]) + part[2][c][lane];
     }
     // C layout: lane owns column col0 + 16c + li and rows row0 + 4*lq + r.
 #pragma unroll
@@ -108,7 +120,7 @@ void launch_pe_bias(const u16* pe, const u16* Wt, float* bias, int KD, int dout,
 
 void launch_compress_linear(const u16* X, const u16* Wt, const float* bias, u16* out, int BG, int T, int d,
                             int dout, int l, int s, int N, hipStream_t st) {
-    dim3 grid((N + 63) / 64, dout / 64, BG);
+    dim3 grid((N + 15) / 16, dout / 64, BG);
     compress_linear_kernel<<<grid, 256, 0, st>>>(X, Wt, bias, out, T, d, dout, l, s, N);
 }
 
