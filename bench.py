@@ -8,7 +8,7 @@ every input resident in HBM before the timed region.  The headline ``value`` is 
 tokens/s; the line also carries the algorithmic TFLOP/s and MFMA-peak fraction, a
 roofline entry for the dominant kernel (timed live with HIP events on the stream it runs
 on), the oracle timed on the host cores on a bounded sample, and the decode step
-(batch 32 x 65536-token caches, HBM GB/s) and MoBA (131072 tokens) figures.
+(batch 32 x 65536-token caches, HBM GB/s) and MoBA (131072 and 1048576 tokens) figures.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-decode] [--no-moba]
 """
@@ -342,29 +342,29 @@ def main():
         del Kd, Vd, kcd, vcd
         torch.cuda.empty_cache()
 
-    # ---------------- MoBA ----------------
+    # ---------------- MoBA (the 128K workload, and 1M tokens) ----------------
     if not args.no_moba:
-        mc = MOBA
-        print("[bench] moba inputs", file=sys.stderr, flush=True)
-        g = torch.Generator(device=dev).manual_seed(mc.seed)
-        Qm = torch.randn((1, mc.seq_len, mc.num_heads, mc.d_k), generator=g, device=dev).to(torch.bfloat16)
-        Km = torch.randn((1, mc.num_kv_heads, mc.seq_len, mc.d_k), generator=g, device=dev).to(torch.bfloat16)
-        Vm = torch.randn((1, mc.num_kv_heads, mc.seq_len, mc.d_v), generator=g, device=dev).to(torch.bfloat16)
-        kbar = torch.empty((1, mc.num_kv_heads, mc.n_cmp, mc.d_k), dtype=torch.bfloat16, device=dev)
-        selm = torch.empty((1, mc.seq_len, mc.num_kv_heads, mc.top_n), dtype=torch.int32, device=dev)
-        om = torch.empty((1, mc.seq_len, mc.num_heads, mc.d_v), dtype=torch.bfloat16, device=dev)
-        wsm = torch.empty(ops.workspace_size(mc, ops.OP_SPARSE_ATTN), dtype=torch.uint8, device=dev)
-        mcalls = [lambda: ops.compress(mc, Km, out_k=kbar),
-                  lambda: ops.score_select(mc, Qm, kbar, sel=selm),
-                  lambda: ops.sparse_attn_fwd(mc, Qm, Km, Vm, selm, out=om, workspace=wsm)]
-        pcm, _ = time_calls(mcalls, 3, 1, torch)
-        mms = float(pcm.sum(axis=1).mean())
-        result["moba"] = {"workload": "moba_131072_h8_d128", "ms_per_step": round(mms, 3),
-                          "tokens_per_s": round(mc.seq_len / (mms * 1e-3), 1),
-                          "tflops_algorithmic": round(moba_flops(mc) / (mms * 1e-3) / 1e12, 2),
-                          "per_call_ms": {n: round(float(c), 3) for n, c in zip(names, pcm.mean(axis=0))}}
-        del Qm, Km, Vm
-        torch.cuda.empty_cache()
+        for mc, key, steps in ((MOBA, "moba", 3), (MOBA.replace(name="moba_1m", seq_len=1 << 20), "moba_1m", 2)):
+            print(f"[bench] {key} inputs", file=sys.stderr, flush=True)
+            g = torch.Generator(device=dev).manual_seed(mc.seed)
+            Qm = torch.randn((1, mc.seq_len, mc.num_heads, mc.d_k), generator=g, device=dev).to(torch.bfloat16)
+            Km = torch.randn((1, mc.num_kv_heads, mc.seq_len, mc.d_k), generator=g, device=dev).to(torch.bfloat16)
+            Vm = torch.randn((1, mc.num_kv_heads, mc.seq_len, mc.d_v), generator=g, device=dev).to(torch.bfloat16)
+            kbar = torch.empty((1, mc.num_kv_heads, mc.n_cmp, mc.d_k), dtype=torch.bfloat16, device=dev)
+            selm = torch.empty((1, mc.seq_len, mc.num_kv_heads, mc.top_n), dtype=torch.int32, device=dev)
+            om = torch.empty((1, mc.seq_len, mc.num_heads, mc.d_v), dtype=torch.bfloat16, device=dev)
+            wsm = torch.empty(ops.workspace_size(mc, ops.OP_SPARSE_ATTN), dtype=torch.uint8, device=dev)
+            mcalls = [lambda: ops.compress(mc, Km, out_k=kbar),
+                      lambda: ops.score_select(mc, Qm, kbar, sel=selm),
+                      lambda: ops.sparse_attn_fwd(mc, Qm, Km, Vm, selm, out=om, workspace=wsm)]
+            pcm, _ = time_calls(mcalls, steps, 1, torch)
+            mms = float(pcm.sum(axis=1).mean())
+            result[key] = {"workload": f"moba_{mc.seq_len}_h8_d128", "ms_per_step": round(mms, 3),
+                           "tokens_per_s": round(mc.seq_len / (mms * 1e-3), 1),
+                           "tflops_algorithmic": round(moba_flops(mc) / (mms * 1e-3) / 1e12, 2),
+                           "per_call_ms": {n: round(float(c), 3) for n, c in zip(names, pcm.mean(axis=0))}}
+            del Qm, Km, Vm, kbar, selm, om, wsm
+            torch.cuda.empty_cache()
 
     # ---------------- CPU baseline ----------------
     if not args.no_cpu:

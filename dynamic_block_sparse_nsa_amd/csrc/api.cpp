@@ -87,6 +87,12 @@ CompressWs compress_ws(const Shape& s) {
 }
 
 // compressed keys and values in fragment order with the values' scaling (mode 0), block scores
+// MEAN_DOT scoring with one query head per KV head and few picks selects inside the
+// scoring kernel: no scores workspace.
+bool fused_mean_select(const Shape& s) {
+    return s.mode == NSA_SCORE_MEAN_DOT && s.G == 1 && s.n - s.n_local <= nsa::kFusedMaxPicks;
+}
+
 struct SelectWs { size_t kf, vf, vmax, vexp, scores, total; int npad; };
 SelectWs select_ws(const Shape& s) {
     SelectWs w{};
@@ -99,7 +105,8 @@ SelectWs select_ws(const Shape& s) {
         w.vmax = off; off = align_up(off + bg * nsa::cmp_vmax_parts() * 4, 256);
         w.vexp = off; off = align_up(off + bg * 4, 256);
     }
-    w.scores = off; off = align_up(off + (size_t)s.B * s.T * s.Hkv * s.n_slc * 4, 256);
+    w.scores = off;
+    if (!fused_mean_select(s)) off = align_up(off + (size_t)s.B * s.T * s.Hkv * s.n_slc * 4, 256);
     w.total = off;
     return w;
 }
@@ -306,6 +313,11 @@ nsa_status nsa_score_select(const nsa_config* cfg, const void* Q, const void* K_
         p.o_cmp = o_cmp;
         if (!nsa::launch_cmp_attn(with_o, s.dk, s.dv, s.G, p, hs))
             return fail(NSA_ERR_UNSUPPORTED, "no compressed-attention kernel for this shape");
+    } else if (fused_mean_select(s)) {
+        p.sel = sel_idx;
+        p.top_n = s.n; p.n_init = s.n_init; p.n_local = s.n_local;
+        if (!nsa::launch_mean_select(s.dk, p, hs)) return fail(NSA_ERR_UNSUPPORTED, "no score kernel for this shape");
+        return hip_check("score_select");
     } else if (!nsa::launch_mean_scores(s.dk, s.G, p, hs)) {
         return fail(NSA_ERR_UNSUPPORTED, "no score kernel for this shape");
     }

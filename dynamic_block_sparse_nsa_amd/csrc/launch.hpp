@@ -30,6 +30,8 @@ struct SelParams {
     float* lse;            // [B,T,H] natural-log LSE of the compressed branch, or null
     float* o_cmp;          // [B,T,H,DV] or null
     float* scores;         // [B,T,Hkv,n_slc] block scores (workspace)
+    int32_t* sel;          // [B,T,Hkv,top_n] selection (written by the fused mean-score selection)
+    int top_n, n_init, n_local;
     int B, T, Hkv, N, Npad, l, s, lp, n_slc;
     float scale_log2;
 };
@@ -39,6 +41,10 @@ bool launch_tile_cmp(int DK, int DV, const u16* K, const u16* V, uint32_t* vmax_
 bool launch_cmp_attn(bool with_o, int DK, int DV, int G, const SelParams& p, hipStream_t st);
 size_t cmp_attn_lds_bytes(int DK, int DV, int G, bool with_o);
 bool launch_mean_scores(int DK, int G, const SelParams& p, hipStream_t st);
+// Mean-key scores with the selection fused (no scores workspace): G = 1 and at most
+// kFusedMaxPicks blocks picked besides the forced ones (top_n - n_local).
+constexpr int kFusedMaxPicks = 4;
+bool launch_mean_select(int DK, const SelParams& p, hipStream_t st);
 void launch_select_from_scores(const float* scores, int32_t* sel, int B, int T, int Hkv, int n_slc, int lp,
                                int top_n, int n_init, int n_local, hipStream_t st);
 

@@ -24,6 +24,8 @@
 //   select_kernel      one wave per (token, group): the shared top-n from the scores.
 // Block j of l' tokens takes compressed blocks i with j*R - L + 1 <= i <= j*R + R - 1,
 // R = l'/s and L = l/s, i.e. every compressed block whose token span meets block j.
+#include <climits>
+
 #include "common.hpp"
 #include "launch.hpp"
 #include "select.hpp"
@@ -592,6 +594,137 @@ __global__ __launch_bounds__(256, 2) void mean_scores_kernel(SelParams p) {
     }
 }
 
+// mode 1 with the selection fused, for one query head per KV head (G = 1) and at most
+// kFusedMaxPicks picks besides the forced blocks (the MoBA configuration: top-3 with the
+// own block forced).  A workgroup owns 64 tokens (a wave's 16 MFMA columns are 16 tokens);
+// each lane keeps, for its column, the best kFusedMaxPicks candidates among the keys it
+// holds as 64-bit entries score-key:~index (larger = better score, then lower index), so no
+// score row is ever stored.  A tile is skipped when no lane of the wave has a candidate
+// above its current fourth best.  The four lanes of a column merge their lists (bitonic
+// top-K of two sorted lists, then a sort) across the 16- and 32-lane swaps.
+template <int DK>
+__global__ __launch_bounds__(256, 2) void mean_select_kernel(SelParams p) {
+    constexpr int K = kFusedMaxPicks;
+    constexpr int TQ = kWaves * 16;
+    constexpr int KSTR = DK + 8;
+    constexpr int NDS = DK / 32;
+    __shared__ __attribute__((aligned(16))) u16 ks[kKeysPerTile * KSTR];
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int li = lane & 15, lq = lane >> 4;
+    const int T = p.T, N = p.N;
+    const int n_tiles = (T + TQ - 1) / TQ;
+    int unit, it;
+    if (!xcd_map_tile(blockIdx.x, p.B * p.Hkv, n_tiles, unit, it)) return;
+    const int b = unit / p.Hkv, g = unit % p.Hkv;
+    const int tok0 = (n_tiles - 1 - it) * TQ;
+    const int tok = tok0 + wave * 16 + li;
+    const int tt = min(tok, T - 1);
+    bf16x8 qf[NDS];
+    {
+        const u16* qp = p.Q + (((size_t)b * T + tt) * p.Hkv + g) * DK + lq * 8;
+#pragma unroll
+        for (int ds = 0; ds < NDS; ++ds) qf[ds] = ld8(qp + 32 * ds);
+    }
+    const ForcedBlocks fb(tt / p.lp, p.top_n, p.n_init, p.n_local);
+    const bool live = tok < T;
+    const int t_last = min(tok0 + TQ - 1, T - 1);
+    const int nv_max = min(t_last / p.lp, N);
+    const u16* kbase = p.Kc + (size_t)unit * N * DK;
+
+    uint64_t best[K];
+#pragma unroll
+    for (int i = 0; i < K; ++i) best[i] = 0ull;
+    for (int k0 = 0; k0 < nv_max; k0 += kKeysPerTile) {
+        __syncthreads();
+        stage_rows<DK, KSTR>(kbase, k0, N, ks);
+        __syncthreads();
+        f32x4 s[4];
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) s[kt] = zero4();
+#pragma unroll
+        for (int ds = 0; ds < NDS; ++ds)
+#pragma unroll
+            for (int kt = 0; kt < 4; ++kt) s[kt] = mfma16(ld8(&ks[(16 * kt + li) * KSTR + 32 * ds + lq * 8]), qf[ds], s[kt]);
+        uint64_t c[16];
+        bool improves = false;
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int j = k0 + 16 * kt + 4 * lq + r;
+                // candidates are complete earlier blocks: the own block is forced (n_local >= 1)
+                const bool ok = live && fb.candidate(j);
+                const uint64_t e = ok ? (((uint64_t)f2key(s[kt][r]) << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)j)) : 0ull;
+                c[4 * kt + r] = e;
+                improves |= e > best[K - 1];
+            }
+        if (__any(improves)) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                uint64_t e = c[i];
+#pragma unroll
+                for (int q = 0; q < K; ++q) {   // insert into the descending list
+                    const uint64_t hi = e > best[q] ? e : best[q];
+                    e = e > best[q] ? best[q] : e;
+                    best[q] = hi;
+                }
+            }
+        }
+    }
+    // merge the column's four lists: lanes l and l ^ 16, then l and l ^ 32
+#pragma unroll
+    for (int step = 0; step < 2; ++step) {
+        uint64_t other[K];
+#pragma unroll
+        for (int q = 0; q < K; ++q) {
+            const u32x2 lo = step == 0 ? swap16((uint32_t)best[q]) : swap32((uint32_t)best[q]);
+            const u32x2 hi = step == 0 ? swap16((uint32_t)(best[q] >> 32)) : swap32((uint32_t)(best[q] >> 32));
+            const bool upper = step == 0 ? (lane & 16) != 0 : (lane & 32) != 0;
+            other[q] = ((uint64_t)(upper ? hi[0] : hi[1]) << 32) | (upper ? lo[0] : lo[1]);
+        }
+        // the top K of two descending lists is max(a[i], b[K-1-i]) (a bitonic sequence) ...
+#pragma unroll
+        for (int q = 0; q < K; ++q) best[q] = best[q] > other[K - 1 - q] ? best[q] : other[K - 1 - q];
+        // ... sorted descending by a bitonic half-cleaner cascade
+#pragma unroll
+        for (int w = K / 2; w >= 1; w /= 2)
+#pragma unroll
+            for (int q = 0; q < K; ++q)
+                if ((q & w) == 0) {
+                    const uint64_t a = best[q], bb = best[q + w];
+                    best[q] = a > bb ? a : bb;
+                    best[q + w] = a > bb ? bb : a;
+                }
+    }
+    if (lq != 0 || !live) return;
+    // the row: initial blocks, the picks (ascending), the local blocks; -1 padded
+    int pk[K];
+    int np = 0;
+#pragma unroll
+    for (int q = 0; q < K; ++q) {
+        const bool take = q < fb.k && best[q] != 0ull;
+        pk[q] = take ? (int)(0xFFFFFFFFu - (uint32_t)best[q]) : INT_MAX;
+        np += take ? 1 : 0;
+    }
+#pragma unroll
+    for (int a = 0; a < K; ++a)
+#pragma unroll
+        for (int q = 0; q + 1 < K; ++q) {
+            const int lo = min(pk[q], pk[q + 1]), hi = max(pk[q], pk[q + 1]);
+            pk[q] = lo;
+            pk[q + 1] = hi;
+        }
+    int32_t* out = p.sel + ((size_t)(b * T + tok) * p.Hkv + g) * p.top_n;
+    int pos = 0;
+    for (int j = 0; j < fb.f_init; ++j) out[pos++] = j;
+#pragma unroll
+    for (int q = 0; q < K; ++q)
+        if (q < np) out[pos++] = pk[q];
+    for (int j = max(fb.f_loc_lo, fb.f_init); j <= fb.n_elig - 1; ++j) out[pos++] = j;
+    for (; pos < p.top_n; ++pos) out[pos] = -1;
+}
+
 // Selection from scores [B,T,Hkv,n_slc]: one wave per (b, t, g).
 template <int NU>
 __global__ __launch_bounds__(256) void select_from_scores_kernel(const float* __restrict__ scores,
@@ -673,6 +806,16 @@ bool launch_cmp_attn(bool with_o, int DK, int DV, int G, const SelParams& p, hip
     if (DK == 192 && DV == 128) { NSA_G_SWITCH(G, cmp_attn_dk<192, 128, GG>(with_o, p, st)); }
     else if (DK == 128 && DV == 128) { NSA_G_SWITCH(G, cmp_attn_dk<128, 128, GG>(with_o, p, st)); }
     else if (DK == 64 && DV == 64) { NSA_G_SWITCH(G, cmp_attn_dk<64, 64, GG>(with_o, p, st)); }
+    else return false;
+    return true;
+}
+
+bool launch_mean_select(int DK, const SelParams& p, hipStream_t st) {
+    constexpr int TQ = kWaves * 16;
+    const int grid = xcd_grid(p.B * p.Hkv, (p.T + TQ - 1) / TQ);
+    if (DK == 192) mean_select_kernel<192><<<grid, 256, 0, st>>>(p);
+    else if (DK == 128) mean_select_kernel<128><<<grid, 256, 0, st>>>(p);
+    else if (DK == 64) mean_select_kernel<64><<<grid, 256, 0, st>>>(p);
     else return false;
     return true;
 }

@@ -106,8 +106,9 @@ __device__ __forceinline__ void emit_selection(const ForcedBlocks& fb, int top_n
 // lanes must call it; NU * 64 must cover jc + 1.  Lane l holds the candidates l, l + 64,
 // ... as 64-bit entries key:slot (key: order-preserving 32-bit image of the score; slot u
 // stored as NU-1-u, so a larger entry is a better score or, for equal scores, the lower
-// block index).  Each lane sorts its entries once (bitonic network, best first); a pick is
-// then a wave maximum over the lanes' heads, and the winning lane shifts its list.
+// block index).  For more than 4 picks each lane sorts its entries once (bitonic network,
+// best first) and a pick is a wave maximum over the lanes' heads, the winning lane shifting
+// its list; for up to 4 picks each pick rescans the lane's entries instead.
 template <int NU>
 __device__ inline void select_blocks_wave(const float* sc, int jc, int top_n, int n_init, int n_local,
                                           int32_t* __restrict__ out, int32_t* __restrict__ out2 = nullptr) {
@@ -118,6 +119,31 @@ __device__ inline void select_blocks_wave(const float* sc, int jc, int top_n, in
     for (int u = 0; u < NU; ++u) {
         const int j = lane + 64 * u;
         e[u] = fb.candidate(j) ? (((uint64_t)f2key(sc[j]) << 32) | (uint32_t)(NU - 1 - u)) : 0ull;
+    }
+    uint32_t picked = 0;  // bit u: candidate lane + 64u taken
+    if (fb.k <= 4) {
+        // few picks: rescan the lane's entries per pick instead of sorting them
+        for (int r = 0; r < fb.k; ++r) {
+            uint64_t t = e[0];
+#pragma unroll
+            for (int u = 1; u < NU; ++u) t = e[u] > t ? e[u] : t;
+            const uint32_t hk = (uint32_t)(t >> 32);
+            const uint32_t m = wave_max_u32(hk);
+            if (m == 0) break;
+            const int hu = NU - 1 - (int)(uint32_t)t;
+            const uint32_t jl = hk == m ? (uint32_t)(lane + 64 * hu) : 0xFFFFFFFFu;
+            const uint64_t holders = __ballot(hk == m);
+            const uint32_t jw = __popcll(holders) == 1
+                                    ? (uint32_t)__builtin_amdgcn_readlane((int)jl, (int)__builtin_ctzll(holders))
+                                    : wave_min_u32(jl);
+            if (jl == jw) {
+                picked |= 1u << hu;
+#pragma unroll
+                for (int u = 0; u < NU; ++u) e[u] = u == hu ? 0ull : e[u];
+            }
+        }
+        emit_selection<NU>(fb, top_n, [&](int u) { return ((picked >> u) & 1u) != 0; }, out, out2);
+        return;
     }
     // bitonic sort, descending
 #pragma unroll
@@ -135,7 +161,6 @@ __device__ inline void select_blocks_wave(const float* sc, int jc, int top_n, in
                     e[l] = sw ? a : b;
                 }
             }
-    uint32_t picked = 0;  // bit u: candidate lane + 64u taken
     for (int r = 0; r < fb.k; ++r) {
         const uint32_t hk = (uint32_t)(e[0] >> 32);
         const uint32_t m = wave_max_u32(hk);

@@ -61,6 +61,14 @@ def test_workspace_sizes(name):
         rc, n = _ws(c, op)
         assert rc == 0
         assert n % 256 == 0
+    # the scores workspace (B*T*Hkv*N_slc fp32), absent when mean-key scoring with one query
+    # head per KV head and at most 4 free picks selects inside the scoring kernel
+    rc, n = _ws(c, ops.OP_SCORE_SELECT)
+    al = lambda x: -(-x // 256) * 256
+    if c.score_mode == 1 and c.heads_per_group == 1 and c.top_n - c.n_local <= 4:
+        assert n == 0
+    else:
+        assert n >= al(c.batch * c.seq_len * c.num_kv_heads * c.n_slc * 4)
     # dense attention: K in bf16 and V in fp16, fragment order, roundup(T, 64) keys, plus the
     # value scaling (64 partial maxima and one exponent per (b, g))
     rc, n = _ws(c, ops.OP_FULL_ATTN)

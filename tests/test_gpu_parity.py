@@ -285,10 +285,14 @@ def test_decode_equals_prefill_last_row():
 # ---------------------------------------------------------------------------
 # MoBA mode
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("T", [8192, MOBA.seq_len])
-def test_moba(T):
-    cfg = MOBA.replace(seq_len=T)
-    announce(f"moba {T}")
+@pytest.mark.parametrize("T,top_n", [(8192, 3), (MOBA.seq_len, 3), (1 << 20, 3), (8192, 8)],
+                         ids=["8k", "128k", "1m", "8k_top8"])
+def test_moba(T, top_n):
+    """MoBA mode at 8K, at the 128K workload, and at 1M tokens (2048 blocks of 512: the
+    longest context the selection supports), on sampled rows.  Top-3 selects inside the
+    scoring kernel; top-8 (7 free picks) goes through the scores workspace."""
+    cfg = MOBA.replace(seq_len=T, top_n=top_n)
+    announce(f"moba {T} top{top_n}")
     inp = inputs.prefill_inputs(cfg)
     Kbar = pipeline.compress_all(cfg, f64(inp["k"][0]), None, None, None, None, None)[0]
     rows = sample_rows(T, 40, 7, lp=512, l=512)
