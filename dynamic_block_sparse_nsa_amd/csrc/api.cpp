@@ -170,13 +170,13 @@ DecodeWs decode_ws(const Shape& s) {
     size_t off = 0;
     w.pm = off; off = align_up(off + bg * w.n_split * 16 * 4, 256);
     w.pl = off; off = align_up(off + bg * w.n_split * 16 * 4, 256);
-    w.po = off; off = align_up(off + bg * w.n_split * s.dv * 16 * 4, 256);
+    w.po = off; off = align_up(off + bg * w.n_split * s.dv * 16 * 2, 256);
     w.pa = off; off = align_up(off + bg * w.n_split * 16 * w.jb * 4, 256);
     w.sel = off; off = align_up(off + bg * std::max(s.n, 1) * 4, 256);
     w.cw = off; off = align_up(off + bg * w.n_split * 16 * 4, 256);
     w.am = off; off = align_up(off + bg * w.n_items * 16 * 4, 256);
     w.al = off; off = align_up(off + bg * w.n_items * 16 * 4, 256);
-    w.ao = off; off = align_up(off + bg * w.n_items * s.dv * 16 * 4, 256);
+    w.ao = off; off = align_up(off + bg * w.n_items * s.dv * 16 * 2, 256);
     w.total = off;
     return w;
 }
@@ -514,13 +514,13 @@ nsa_status nsa_decode(const nsa_config* cfg, const void* q, const void* K_cache,
     p.sel_out = sel_idx_out;
     p.part_m = at<float>(ws, w.pm);
     p.part_l = at<float>(ws, w.pl);
-    p.part_o = at<float>(ws, w.po);
+    p.part_o = at<nsa::u16>(ws, w.po);
     p.part_a = at<float>(ws, w.pa);
     p.sel_ws = at<int32_t>(ws, w.sel);
     p.cmp_w = at<float>(ws, w.cw);
     p.att_m = at<float>(ws, w.am);
     p.att_l = at<float>(ws, w.al);
-    p.att_o = at<float>(ws, w.ao);
+    p.att_o = at<nsa::u16>(ws, w.ao);
     p.B = s.B; p.L = s.T; p.Hkv = s.Hkv; p.G = s.G; p.Nc = s.n_cmp; p.l = s.l; p.s = s.s; p.lp = s.lp;
     p.n_slc = s.n_slc; p.top_n = s.n; p.n_init = s.n_init; p.n_local = s.n_local; p.window = s.w;
     p.branches = s.br; p.n_split = w.n_split; p.jb = w.jb; p.n_items = w.n_items;

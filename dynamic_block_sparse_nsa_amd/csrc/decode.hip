@@ -39,6 +39,54 @@ namespace {
 
 constexpr int kPsumStride = kDecodeSplitKeys + 4;   // padded row of the per-head probabilities
 
+// A wave's partial o^T in LDS, head-major: [16 heads][DV + 4] fp32 (lane li holds head li,
+// d = 16dt + 4lq + r of its accumulators: one 16-byte store per dt).
+template <int DV>
+__device__ __forceinline__ void store_partial(float* po_w, const f32x4 (&o)[DV / 16]) {
+    const int lane = threadIdx.x & 63, li = lane & 15, lq = lane >> 4;
+#pragma unroll
+    for (int dt = 0; dt < DV / 16; ++dt) *reinterpret_cast<f32x4*>(&po_w[li * (DV + 4) + 16 * dt + 4 * lq]) = o[dt];
+}
+
+// Partial outputs in memory are fp16 [16 heads][DV]: thread (h, d0) of a 256-thread
+// workgroup owns DV/16 consecutive dims of head h.
+template <int DV>
+struct OutSlice {
+    static constexpr int N = DV / 16;
+    int h, d0;
+    __device__ OutSlice() : h(threadIdx.x >> 4), d0((threadIdx.x & 15) * N) {}
+};
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+template <int N>
+__device__ __forceinline__ void store_f16(u16* dst, const float (&v)[N]) {
+    static_assert(N == 4 || N == 8, "4 or 8 values");
+    if constexpr (N == 8) {
+        f16x8 h;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) h[i] = (_Float16)v[i];
+        *reinterpret_cast<f16x8*>(dst) = h;
+    } else {
+        f16x4 h;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) h[i] = (_Float16)v[i];
+        *reinterpret_cast<f16x4*>(dst) = h;
+    }
+}
+template <int N>
+struct HalfSlice;
+template <>
+struct HalfSlice<8> {
+    f16x8 v;
+    __device__ void load(const u16* src) { v = *reinterpret_cast<const f16x8*>(src); }
+    __device__ float operator[](int i) const { return (float)v[i]; }
+};
+template <>
+struct HalfSlice<4> {
+    f16x4 v;
+    __device__ void load(const u16* src) { v = *reinterpret_cast<const f16x4*>(src); }
+    __device__ float operator[](int i) const { return (float)v[i]; }
+};
+
 __device__ __forceinline__ int query_pos(const int32_t* cache_len, int b, int L) {
     const int n = min(max(cache_len[b], 1), L);
     return n - 1;
@@ -116,9 +164,9 @@ __device__ void attn_group(const DecodeParams& p, int gi, int g, int b, unsigned
     constexpr int VSTR = DV + 16;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, li = lane & 15, lq = lane >> 4;
     u16* vs = reinterpret_cast<u16*>(smem) + wave * 64 * VSTR;   // this wave's value tile
-    // after the items: [4][DV][16] partial o, then [4][16] m and l
+    // after the items: [4 waves][16][DV + 4] partial o, then [4][16] m and l
     float* mo = reinterpret_cast<float*>(smem);
-    float* mm = mo + 4 * DV * 16;
+    float* mm = mo + 4 * 16 * (DV + 4);
     float* ml = mm + 64;
     const int G = p.G, H = p.Hkv * G;
     const int t = query_pos(p.cache_len, b, p.L);
@@ -198,36 +246,36 @@ __device__ void attn_group(const DecodeParams& p, int gi, int g, int b, unsigned
     }
     l = col_sum(l);
     __syncthreads();   // every wave is done with its value tile: reuse the region
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) mo[(wave * DV + 16 * dt + 4 * lq + r) * 16 + li] = o[dt][r];
+    store_partial<DV>(mo + wave * 16 * (DV + 4), o);
     if (lq == 0) {
         mm[wave * 16 + li] = m;
         ml[wave * 16 + li] = l;
     }
     __syncthreads();
-    // combine the four partials of every (d, head); empty items carry m = -inf, l = 0, o = 0
+    // combine the four partials of every (head, d); empty items carry m = -inf, l = 0, o = 0
     const size_t ib = ((size_t)b * p.Hkv + g) * p.n_items + gi;
-    for (int idx = threadIdx.x; idx < DV * 16; idx += 256) {
-        const int hh = idx & 15;
-        float M = -INFINITY;
+    const OutSlice<DV> os;
+    float M = -INFINITY;
 #pragma unroll
-        for (int w = 0; w < 4; ++w) M = fmaxf(M, mm[w * 16 + hh]);
-        float acc = 0.f, L = 0.f;
-        if (M > -INFINITY) {
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, mm[w * 16 + os.h]);
+    float e[4], L = 0.f;
 #pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                const float e = fast_exp2(mm[w * 16 + hh] - M);
-                acc += e * mo[w * DV * 16 + idx];
-                L += e * ml[w * 16 + hh];
-            }
-        }
-        p.att_o[ib * DV * 16 + idx] = acc;
-        if (idx < 16) {
-            p.att_m[ib * 16 + hh] = M;
-            p.att_l[ib * 16 + hh] = L;
-        }
+    for (int w = 0; w < 4; ++w) {
+        e[w] = M > -INFINITY ? fast_exp2(mm[w * 16 + os.h] - M) : 0.f;
+        L += e[w] * ml[w * 16 + os.h];
+    }
+    float acc[OutSlice<DV>::N];
+#pragma unroll
+    for (int i = 0; i < OutSlice<DV>::N; ++i) {
+        float a = 0.f;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) a += e[w] * mo[(w * 16 + os.h) * (DV + 4) + os.d0 + i];
+        acc[i] = a;
+    }
+    store_f16(p.att_o + (ib * 16 + os.h) * DV + os.d0, acc);
+    if (os.d0 == 0) {
+        p.att_m[ib * 16 + os.h] = M;
+        p.att_l[ib * 16 + os.h] = L;
     }
 }
 
@@ -241,8 +289,8 @@ __global__ __launch_bounds__(256, 2) void decode_cmp_kernel(DecodeParams p) {
     float* wm = reinterpret_cast<float*>(vs_all + 4 * 64 * VSTR);            // [4][16]
     float* wl = wm + 64;                                                     // [4][16]
     // after the value products the tile region is reused:
-    float* po = reinterpret_cast<float*>(smem);                              // [4][DV][16]
-    float* psum = po + 4 * DV * 16;                                          // [16][kPsumStride]
+    float* po = reinterpret_cast<float*>(smem);                              // [4][16][DV + 4]
+    float* psum = po + 4 * 16 * (DV + 4);                                    // [16][kPsumStride]
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int li = lane & 15, lq = lane >> 4;
@@ -315,18 +363,21 @@ __global__ __launch_bounds__(256, 2) void decode_cmp_kernel(DecodeParams p) {
         }
     }
     __syncthreads();  // every wave is done with its value tile: reuse the region
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) po[(wave * DV + 16 * dt + 4 * lq + r) * 16 + li] = oacc[dt][r];
+    store_partial<DV>(po + wave * 16 * (DV + 4), oacc);
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
         for (int r = 0; r < 4; ++r) psum[li * kPsumStride + 64 * wave + 16 * kt + 4 * lq + r] = pv[kt][r];
     __syncthreads();
-    for (int idx = threadIdx.x; idx < DV * 16; idx += 256) {
-        const float v = po[idx] + po[DV * 16 + idx] + po[2 * DV * 16 + idx] + po[3 * DV * 16 + idx];
-        p.part_o[pbase * DV * 16 + idx] = v;
+    {
+        const OutSlice<DV> os;
+        float v[OutSlice<DV>::N];
+#pragma unroll
+        for (int i = 0; i < OutSlice<DV>::N; ++i) {
+            const float* q = po + os.h * (DV + 4) + os.d0 + i;
+            v[i] = ((q[0] + q[16 * (DV + 4)]) + q[2 * 16 * (DV + 4)]) + q[3 * 16 * (DV + 4)];
+        }
+        store_f16(p.part_o + (pbase * 16 + os.h) * DV + os.d0, v);
     }
     if (threadIdx.x < 16) {
         const int hh = threadIdx.x;
@@ -464,45 +515,44 @@ __global__ __launch_bounds__(256, 2) void decode_attn_kernel(DecodeParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// grid (DV / 16, Hkv, B): each thread owns one output (d, head) of the group; the
-// weights of the partial results are recomputed per workgroup (a few hundred values).
+// One workgroup per (sequence, group); thread (h, d0) owns DV/16 consecutive outputs of head
+// h and reads one fp16 slice per partial, every load issued before the merge weights are
+// known (indices clamped to valid partials; the sums skip the clamped ones).
 template <int DV>
-__global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p) {
-    extern __shared__ float wsm[];       // [n_items][16] merge weights
-    const int g = blockIdx.y, b = blockIdx.z;
+__device__ void merge_unit(const DecodeParams& p, int g, int b, float* wsm) {   // wsm: [n_items][16]
+    constexpr int NO = DV / 16, SB = 16, NG = kDecodeMaxItems / 4;
     const int G = p.G, H = p.Hkv * G;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const size_t bg = (size_t)b * p.Hkv + g;
     const size_t ib0 = bg * p.n_items;
     // partials: the selected branch's groups of 4 items, then the window's
     const int n_sg = (p.top_n + 3) / 4, n_grp = n_sg + (p.n_items - p.top_n + 3) / 4;
-    const int idx = blockIdx.x * 256 + threadIdx.x;   // (d, head) = (idx / 16, idx % 16)
-    const int hh = idx & 15, d = idx >> 4;
+    const OutSlice<DV> os;
+    const int hh = os.h;
     const int t = query_pos(p.cache_len, b, p.L);
     const int ns = (visible_count(t, p.l, p.s, p.Nc) + kDecodeSplitKeys - 1) / kDecodeSplitKeys;
     const bool use_c = (p.branches & 1) && ns > 0, use_s = (p.branches & 2) && n_sg > 0,
                use_w = (p.branches & 4) && n_grp > n_sg;
-    // this thread's partial outputs and gate logits, all requested before the weights are
-    // known (indices clamped to valid partials; the sums below skip the clamped ones)
-    constexpr int NS = kDecodeMaxSplits, NG = kDecodeMaxItems / 4;
-    float cw[NS], co[NS], so[NG], wo[NG], z[3] = {0.f, 0.f, 0.f};
+    const size_t pb0 = bg * p.n_split;
+    HalfSlice<NO> so[NG], wo[NG], co[SB];
+    float cw[SB], z[3] = {0.f, 0.f, 0.f};
     if (hh < G) {
-        if (use_c) {
-            const size_t pb0 = bg * p.n_split;
+        if (use_c) {   // the first SB splits (the rest below)
 #pragma unroll
-            for (int i = 0; i < NS; ++i) {
+            for (int i = 0; i < SB; ++i) {
                 const int sp = min(i, ns - 1);
                 cw[i] = p.cmp_w[(pb0 + sp) * 16 + hh];
-                co[i] = p.part_o[(pb0 + sp) * DV * 16 + idx];
+                co[i].load(p.part_o + ((pb0 + sp) * 16 + hh) * DV + os.d0);
             }
         }
         if (use_s) {
 #pragma unroll
-            for (int i = 0; i < NG; ++i) so[i] = p.att_o[(ib0 + min(i, n_sg - 1)) * DV * 16 + idx];
+            for (int i = 0; i < NG; ++i) so[i].load(p.att_o + ((ib0 + min(i, n_sg - 1)) * 16 + hh) * DV + os.d0);
         }
         if (use_w) {
 #pragma unroll
-            for (int i = 0; i < NG; ++i) wo[i] = p.att_o[(ib0 + min(n_sg + i, n_grp - 1)) * DV * 16 + idx];
+            for (int i = 0; i < NG; ++i)
+                wo[i].load(p.att_o + ((ib0 + min(n_sg + i, n_grp - 1)) * 16 + hh) * DV + os.d0);
         }
         if (p.gates) {
             const float* zp = p.gates + ((size_t)b * H + g * G + hh) * 3;
@@ -541,18 +591,38 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p) {
     }
     __syncthreads();
     if (hh >= G) return;
-    float oc = 0.f, os = 0.f, ow = 0.f;
+    float oc[NO], osl[NO], ow[NO];
+#pragma unroll
+    for (int k = 0; k < NO; ++k) oc[k] = osl[k] = ow[k] = 0.f;
     if (use_c) {
 #pragma unroll
-        for (int i = 0; i < NS; ++i) oc += i < ns ? cw[i] * co[i] : 0.f;
+        for (int i = 0; i < SB; ++i)
+#pragma unroll
+            for (int k = 0; k < NO; ++k) oc[k] += i < ns ? cw[i] * co[i][k] : 0.f;
+        for (int s0 = SB; s0 < ns; s0 += SB) {   // more than SB splits (caches past 65536 tokens)
+#pragma unroll
+            for (int i = 0; i < SB; ++i) {
+                const int sp = min(s0 + i, ns - 1);
+                cw[i] = p.cmp_w[(pb0 + sp) * 16 + hh];
+                co[i].load(p.part_o + ((pb0 + sp) * 16 + hh) * DV + os.d0);
+            }
+#pragma unroll
+            for (int i = 0; i < SB; ++i)
+#pragma unroll
+                for (int k = 0; k < NO; ++k) oc[k] += s0 + i < ns ? cw[i] * co[i][k] : 0.f;
+        }
     }
     if (use_s) {
 #pragma unroll
-        for (int i = 0; i < NG; ++i) os += i < n_sg ? wsm[i * 16 + hh] * so[i] : 0.f;
+        for (int i = 0; i < NG; ++i)
+#pragma unroll
+            for (int k = 0; k < NO; ++k) osl[k] += i < n_sg ? wsm[i * 16 + hh] * so[i][k] : 0.f;
     }
     if (use_w) {
 #pragma unroll
-        for (int i = 0; i < NG; ++i) ow += n_sg + i < n_grp ? wsm[(n_sg + i) * 16 + hh] * wo[i] : 0.f;
+        for (int i = 0; i < NG; ++i)
+#pragma unroll
+            for (int k = 0; k < NO; ++k) ow[k] += n_sg + i < n_grp ? wsm[(n_sg + i) * 16 + hh] * wo[i][k] : 0.f;
     }
     float gc = 1.f, gs = 1.f, gw = 1.f;
     if (p.gates) {
@@ -560,11 +630,24 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p) {
         gs = sigmoidf_(z[1]);
         gw = sigmoidf_(z[2]);
     }
-    float y = 0.f;
-    if (p.branches & 1) y += gc * oc;
-    if (p.branches & 2) y += gs * os;
-    if (p.branches & 4) y += gw * ow;
-    p.O[((size_t)b * H + g * G + hh) * DV + d] = f2bf(y);
+    u16 y[NO];
+#pragma unroll
+    for (int k = 0; k < NO; ++k) {
+        float v = 0.f;
+        if (p.branches & 1) v += gc * oc[k];
+        if (p.branches & 2) v += gs * osl[k];
+        if (p.branches & 4) v += gw * ow[k];
+        y[k] = f2bf(v);
+    }
+    u16* op = p.O + ((size_t)b * H + g * G + hh) * DV + os.d0;
+#pragma unroll
+    for (int k = 0; k < NO; ++k) op[k] = y[k];
+}
+
+template <int DV>
+__global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p) {
+    extern __shared__ float wsm[];
+    merge_unit<DV>(p, blockIdx.x, blockIdx.y, wsm);
 }
 
 // ---------------------------------------------------------------------------
@@ -579,7 +662,7 @@ void allow_lds(K kernel, size_t bytes) {
 template <int DK, int DV>
 void decode_impl(const DecodeParams& p, hipStream_t st) {
     const size_t lds_attn = (size_t)4 * 64 * (DV + 16) * 2;   // >= the combine buffers
-    const size_t reuse = (size_t)4 * DV * 16 * 4 + (size_t)16 * kPsumStride * 4;
+    const size_t reuse = (size_t)4 * 16 * (DV + 4) * 4 + (size_t)16 * kPsumStride * 4;
     const size_t lds1 = (lds_attn > reuse ? lds_attn : reuse) + 128 * 4;
     const int n_sg = (p.top_n + 3) / 4, n_wg = (p.n_items - p.top_n + 3) / 4;
     allow_lds(decode_cmp_kernel<DK, DV>, lds1);
@@ -593,7 +676,7 @@ void decode_impl(const DecodeParams& p, hipStream_t st) {
         allow_lds(decode_attn_kernel<DK, DV>, lds_attn);
         decode_attn_kernel<DK, DV><<<dim3(n_sg, p.Hkv, p.B), 256, lds_attn, st>>>(p);
     }
-    decode_merge_kernel<DV><<<dim3(DV / 16, p.Hkv, p.B), 256, (size_t)p.n_items * 16 * 4, st>>>(p);
+    decode_merge_kernel<DV><<<dim3(p.Hkv, p.B), 256, (size_t)p.n_items * 16 * 4, st>>>(p);
 }
 }  // namespace
 

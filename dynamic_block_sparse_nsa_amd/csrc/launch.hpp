@@ -121,13 +121,13 @@ struct DecodeParams {
     // workspace
     float* part_m;             // [B,Hkv,n_split,16]
     float* part_l;             // [B,Hkv,n_split,16]
-    float* part_o;             // [B,Hkv,n_split,DV,16]
+    u16* part_o;               // [B,Hkv,n_split,16,DV] fp16
     float* part_a;             // [B,Hkv,n_split,jb,16]
     int32_t* sel_ws;           // [B,Hkv,top_n]
     float* cmp_w;              // [B,Hkv,n_split,16] weight 2^(m_split - lse) of each split
     float* att_m;              // [B,Hkv,n_items,16]
     float* att_l;              // [B,Hkv,n_items,16]
-    float* att_o;              // [B,Hkv,n_items,DV,16]
+    u16* att_o;                // [B,Hkv,n_items,16,DV] fp16
     int B, L, Hkv, G, Nc, l, s, lp, n_slc, top_n, n_init, n_local, window, branches;
     int n_split, jb, n_items;
     float scale_log2;
