@@ -181,26 +181,69 @@ def test_sparse_attn_single_branch(branches):
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("cfg", [TINY, P8K], ids=lambda c: c.name)
 def test_prefill_end_to_end(cfg):
+    _prefill_end_to_end(cfg)
+
+
+def _prefill_end_to_end(cfg):
     announce(f"end to end {cfg.name}")
     inp = inputs.prefill_inputs(cfg)
     r = ops.prefill(cfg, dev_bf16(inp["q"]), dev_bf16(inp["k"]), dev_bf16(inp["v"]), dev_bf16(inp["w_k"]),
                     dev_bf16(inp["w_v"]), dev_bf16(inp["pe_k"]), dev_bf16(inp["pe_v"]), dev_f32(inp["gates"]))
     torch.cuda.synchronize()
-    rows = np.arange(cfg.seq_len, dtype=np.int32) if cfg.seq_len <= 1024 else sample_rows(cfg.seq_len, 300, 6)
-    Kc, Vc = pipeline.compress_all(cfg, f64(inp["k"][0]), f64(inp["v"][0]), f64(inp["w_k"]), f64(inp["w_v"]),
-                                   f64(inp["pe_k"]), f64(inp["pe_v"]))
-    ref = pipeline.forward_rows(cfg, f64(inp["q"][0]), f64(inp["k"][0]), f64(inp["v"][0]), Kc, Vc, inp["gates"][0],
-                                rows)
-    gsel = r["sel"].cpu().numpy()[0, rows]
-    gout = bf16_dev_to_f64(r["out"])[0, rows]
-    agree = (gsel == ref["sel"]).all(axis=-1).all(axis=-1)
-    print(f"[parity] {cfg.name} end-to-end selection agreement {agree.mean():.5f} over {len(rows)} rows", flush=True)
-    # the GPU's compressed keys may differ from the oracle's by one bf16 rounding in a few
-    # elements; rows whose selection then differs must be near ties
-    assert agree.mean() >= 0.99
-    for r_ in np.where(~agree)[0]:
-        assert ref["gap"][r_].min() < 1e-3, (rows[r_], ref["gap"][r_])
-    check_close(gout[agree], ref["out"][agree], f"{cfg.name} end-to-end output")
+    rows = np.arange(cfg.seq_len, dtype=np.int32) if cfg.seq_len <= 2100 else sample_rows(cfg.seq_len, 300, 6)
+    for b in range(cfg.batch):
+        Kc, Vc = pipeline.compress_all(cfg, f64(inp["k"][b]), f64(inp["v"][b]), f64(inp["w_k"]), f64(inp["w_v"]),
+                                       f64(inp["pe_k"]), f64(inp["pe_v"]))
+        ref = pipeline.forward_rows(cfg, f64(inp["q"][b]), f64(inp["k"][b]), f64(inp["v"][b]), Kc, Vc,
+                                    inp["gates"][b], rows)
+        gsel = r["sel"].cpu().numpy()[b, rows]
+        gout = bf16_dev_to_f64(r["out"])[b, rows]
+        agree = (gsel == ref["sel"]).all(axis=-1).all(axis=-1)
+        print(f"[parity] {cfg.name} b={b} end-to-end selection agreement {agree.mean():.5f} over {len(rows)} rows",
+              flush=True)
+        # the GPU's compressed keys may differ from the oracle's by one bf16 rounding in a
+        # few elements; rows whose selection then differs must be near ties
+        assert agree.mean() >= 0.99
+        for r_ in np.where(~agree)[0]:
+            assert ref["gap"][r_].min() < 1e-3, (rows[r_], ref["gap"][r_])
+        check_close(gout[agree], ref["out"][agree], f"{cfg.name} b={b} end-to-end output")
+
+
+# Other shapes the kernels support: group sizes 1, 2, 8; head dims 128/128 and 64/64;
+# other block geometries, top-n and windows; a batch of two; every row checked.
+SHAPES = [
+    TINY.replace(name="g2_d128_b2", batch=2, seq_len=1500, num_kv_heads=2, heads_per_group=2, d_k=128, d_v=128,
+                 top_n=8, window=256, seed=41),
+    TINY.replace(name="g8_d64_l64", seq_len=2100, num_kv_heads=1, heads_per_group=8, d_k=64, d_v=64,
+                 cmp_block=64, cmp_stride=32, slc_block=128, top_n=6, n_init=2, n_local=1, window=200, seed=42),
+    TINY.replace(name="g1_d128_nsa", seq_len=1200, num_kv_heads=3, heads_per_group=1, d_k=128, d_v=128,
+                 top_n=5, window=100, seed=43),
+    TINY.replace(name="g16_d192_w0", seq_len=900, num_kv_heads=1, heads_per_group=16, d_k=192, d_v=128,
+                 top_n=4, window=0, branches=3, seed=44),
+]
+
+
+@pytest.mark.parametrize("cfg", SHAPES, ids=lambda c: c.name)
+def test_prefill_shape_matrix(cfg):
+    _prefill_end_to_end(cfg)
+
+
+DECODE_SHAPES = [
+    DECODE.replace(name="dec_g4_d128", batch=3, seq_len=3000, num_kv_heads=2, heads_per_group=4, d_k=128, d_v=128,
+                   top_n=8, window=256, seed=51),
+    DECODE.replace(name="dec_g8_d64_nowin", batch=2, seq_len=2500, num_kv_heads=1, heads_per_group=8, d_k=64,
+                   d_v=64, window=0, branches=3, seed=52),
+    DECODE.replace(name="dec_g16_l64", batch=2, seq_len=5000, cmp_block=64, cmp_stride=32, slc_block=128,
+                   top_n=12, window=300, seed=53),
+]
+
+
+@pytest.mark.parametrize("cfg", DECODE_SHAPES, ids=lambda c: c.name)
+def test_decode_shape_matrix(cfg):
+    announce(f"decode shape {cfg.name}")
+    rng = np.random.default_rng(cfg.seed)
+    lens = np.concatenate([[cfg.seq_len], rng.integers(1, cfg.seq_len + 1, cfg.batch - 1)]).astype(np.int32)
+    _decode_case(cfg, lens, cmp_from_oracle=True)
 
 
 # ---------------------------------------------------------------------------
