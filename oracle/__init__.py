@@ -1,4 +1,4 @@
-"""fp64 CPU oracle of the NSA forward pass (test infrastructure).
+"""fp64 CPU oracle of the NSA forward and backward passes (test infrastructure).
 
 Only ``tests/``, ``__graft_entry__.smoke()`` and ``bench.py``'s CPU-baseline leg may import
 this package.  It loads ``liboracle.so`` built from ``nsa_oracle.c`` with gcc (OpenMP),
@@ -54,6 +54,10 @@ def lib():
         L.oracle_causal_attention.argtypes = [ctypes.c_int] * 4 + [ctypes.c_double, _D, _D, _D, _D]
         L.oracle_causal_attention_rows.argtypes = [ctypes.c_int, _I, ctypes.c_int, ctypes.c_int, ctypes.c_double,
                                                    _D, _D, _D, _D]
+        L.oracle_nsa_bwd.argtypes = ([ctypes.c_int] * 11 + [ctypes.c_double, ctypes.c_int] + [_D] * 5 + [_I]
+                                     + [_D] * 8)
+        L.oracle_nsa_bwd.restype = ctypes.c_int
+        L.oracle_compress_linear_bwd.argtypes = [ctypes.c_int] * 6 + [_D] * 7
         L.oracle_num_threads.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -213,4 +217,52 @@ def causal_attention(Q, K, V, scale: float, window: int = 0) -> np.ndarray:
     dv = V.shape[1]
     out = np.zeros((n, dv))
     lib().oracle_causal_attention(n, dk, dv, window, float(scale), _pd(Q), _pd(K), _pd(V), _pd(out))
+    return out
+
+
+# ---------------------------------------------------------------------------
+# backward (the selection held fixed)
+# ---------------------------------------------------------------------------
+def nsa_bwd(cfg, Q, K, V, Kc, Vc, sel, gates, dO, branches=None) -> dict:
+    """Gradients of the gated output of every row of one batch element.
+
+    Q [T,H,dk]; K [Hkv,T,dk]; V [Hkv,T,dv]; Kc [Hkv,N,dk]; Vc [Hkv,N,dv] (None when the
+    compressed branch is off); sel [T,Hkv,top_n]; gates [T,H,3] logits or None (weights 1);
+    dO [T,H,dv].  Returns dict(dq, dk, dv, dkc, dvc, dgates) shaped like their inputs
+    (dgates None without gates; dkc/dvc None without the compressed branch).
+    """
+    Hkv, G = cfg.num_kv_heads, cfg.heads_per_group
+    branches = cfg.branches if branches is None else branches
+    Q, K, V, dO = _d(Q), _d(K), _d(V), _d(dO)
+    sel = _i(sel)
+    T = Q.shape[0]
+    use_c = bool(branches & 1)
+    Kc = _d(Kc) if use_c else None
+    Vc = _d(Vc) if use_c else None
+    n_cmp = Kc.shape[1] if use_c else 0
+    gates = None if gates is None else _d(gates)
+    out = {"dq": np.zeros_like(Q), "dk": np.zeros_like(K), "dv": np.zeros_like(V),
+           "dkc": np.zeros_like(Kc) if use_c else None, "dvc": np.zeros_like(Vc) if use_c else None,
+           "dgates": np.zeros_like(gates) if gates is not None else None}
+    rc = lib().oracle_nsa_bwd(Hkv, G, cfg.d_k, cfg.d_v, T, n_cmp, cfg.cmp_block, cfg.cmp_stride, cfg.slc_block,
+                              sel.shape[-1], cfg.window, float(cfg.scale), branches, _pd(Q), _pd(K), _pd(V),
+                              _pd(Kc), _pd(Vc), _pi(sel), _pd(gates), _pd(dO), _pd(out["dq"]), _pd(out["dk"]),
+                              _pd(out["dv"]), _pd(out["dkc"]), _pd(out["dvc"]), _pd(out["dgates"]))
+    if rc != 0:
+        raise MemoryError("oracle_nsa_bwd failed")
+    return out
+
+
+def compress_linear_bwd(X, pe, W, dY, l: int, s: int) -> dict:
+    """Backward of the linear phi over blocks 0 .. dY.shape[0]-1 of one head's token rows
+    X [n_tok, d]: returns dict(dx [n_tok,d], dw [l*d,d_out], dpe [l,d])."""
+    X, W, dY = _d(X), _d(W), _d(dY)
+    pe = None if pe is None else _d(pe)
+    n_tok, d = X.shape
+    d_out = W.shape[1]
+    nblk = dY.shape[0]
+    assert W.shape[0] == l * d and (nblk == 0 or (nblk - 1) * s + l <= n_tok)
+    out = {"dx": np.zeros_like(X), "dw": np.zeros_like(W), "dpe": np.zeros((l, d))}
+    lib().oracle_compress_linear_bwd(n_tok, d, d_out, l, s, nblk, _pd(X), _pd(pe), _pd(W), _pd(dY),
+                                     _pd(out["dx"]), _pd(out["dw"]), _pd(out["dpe"]))
     return out

@@ -1,6 +1,7 @@
 /*
  * nsa_oracle.c - plain, slow, fp64 CPU oracle of the Native Sparse Attention (NSA)
- * forward pass and of the MoBA-style mean-pooled block selection.
+ * forward pass, its backward pass (gradients through the compression and the three
+ * branches, the selection held fixed) and the MoBA-style mean-pooled block selection.
  *
  * TEST INFRASTRUCTURE.  Only the tests, the smoke check and the bench's CPU-baseline
  * leg may load this library.  It shares no code, header, table or helper with the
@@ -436,6 +437,185 @@ ORACLE_API void oracle_causal_attention_rows(int nrows, const int* rows, int dk,
             out[(size_t)k * dv + e] = acc / sum;
         }
         free(logit);
+    }
+}
+
+/* ------------------------------------------------------------------------- */
+/* Backward pass (gradients of the output, the selection held fixed)         */
+/* ------------------------------------------------------------------------- */
+/*
+ * zjai.club [B], section 4 (the method is trained natively, forward and backward),
+ * section 13 (its speed claims cover the backward pass too) and section 14 (the top-k
+ * choice has no derivative; the compressed branch's output is what carries the loss's
+ * gradient into the block representations): the backward pass is the chain rule through
+ * steps 1, 2 and 5-7.  The block choice of steps 3-4 is a discrete function of the scores
+ * and passes no gradient; the listed blocks are an input here.
+ *
+ * For one softmax attention o = sum_k p_k v_k, p = softmax(a), a_k = scale <q, k_k>, and an
+ * upstream gradient go of o (the textbook derivative of a softmax-weighted sum):
+ *   dv_k += p_k go
+ *   dp_k  = <go, v_k>
+ *   da_k  = p_k (dp_k - sum_j p_j dp_j)
+ *   dq   += scale sum_k da_k k_k
+ *   dk_k += scale da_k q
+ * For the gated sum out = sum_c sigma(z_c) o_c: go_c = sigma(z_c) dout and
+ * dz_c = sigma(z_c) (1 - sigma(z_c)) <dout, o_c>.
+ */
+
+/* Backward of one attention over an explicit key list (indices into K / V).  Adds into
+ * dq [dk], dK, dV (rows indexed like K, V).  Returns <dout, o>, o recomputed here. */
+static double attend_list_bwd(const double* q, const double* K, const double* V, int dk, int dv, double scale,
+                              const int* keys, int nk, const double* dout, double sig,
+                              double* logit, double* p, double* o,
+                              double* dq, double* dK, double* dV)
+{
+    if (nk == 0) return 0.0;
+    for (int c = 0; c < nk; ++c) logit[c] = scale * dot(q, K + (size_t)keys[c] * dk, dk);
+    softmax(logit, nk, p);
+    for (int e = 0; e < dv; ++e) o[e] = 0.0;
+    for (int c = 0; c < nk; ++c)
+        for (int e = 0; e < dv; ++e) o[e] += p[c] * V[(size_t)keys[c] * dv + e];
+    /* dp_k = <sig * dout, v_k>; logit[] is reused to hold dp */
+    double pdp = 0.0;
+    for (int c = 0; c < nk; ++c) {
+        logit[c] = sig * dot(dout, V + (size_t)keys[c] * dv, dv);
+        pdp += p[c] * logit[c];
+    }
+    for (int c = 0; c < nk; ++c) {
+        const int x = keys[c];
+        const double da = p[c] * (logit[c] - pdp);
+        for (int e = 0; e < dk; ++e) {
+            dq[e] += scale * da * K[(size_t)x * dk + e];
+            dK[(size_t)x * dk + e] += scale * da * q[e];
+        }
+        for (int e = 0; e < dv; ++e) dV[(size_t)x * dv + e] += p[c] * sig * dout[e];
+    }
+    return dot(dout, o, dv);
+}
+
+/* Gradients of the gated output of every row t = 0 .. n_tok-1 of one batch element with
+ * respect to Q, K, V (selected and window branches), the compressed keys and values Kc, Vc
+ * (compressed branch) and the gate logits, for the upstream gradient dO.  The branches
+ * and visibility rules are those of the forward functions above: compressed blocks i with
+ * i*s + l - 1 <= t; the tokens <= t of the listed blocks; tokens max(0, t-w+1) .. t.
+ * Q [n_tok, H, dk]; K [H_kv, n_tok, dk]; V [H_kv, n_tok, dv]; Kc [H_kv, n_cmp, dk];
+ * Vc [H_kv, n_cmp, dv]; sel [n_tok, H_kv, top_n]; gates [n_tok, H, 3] or NULL (weights 1,
+ * dgates not written); dO [n_tok, H, dv].  Every output is overwritten (dKc, dVc and
+ * dgates may be NULL when unused).  Returns 0, or -2 when memory runs out. */
+ORACLE_API int oracle_nsa_bwd(int H_kv, int G, int dk, int dv, int n_tok, int n_cmp, int l, int s, int lp,
+                              int top_n, int window, double scale, int branches,
+                              const double* Q, const double* K, const double* V,
+                              const double* Kc, const double* Vc, const int* sel,
+                              const double* gates, const double* dO,
+                              double* dQ, double* dK, double* dV, double* dKc, double* dVc, double* dgates)
+{
+    const int H = H_kv * G;
+    const size_t nK = (size_t)H_kv * n_tok, nC = (size_t)H_kv * n_cmp;
+    memset(dQ, 0, sizeof(double) * (size_t)n_tok * H * dk);
+    memset(dK, 0, sizeof(double) * nK * dk);
+    memset(dV, 0, sizeof(double) * nK * dv);
+    if (dKc) memset(dKc, 0, sizeof(double) * nC * dk);
+    if (dVc) memset(dVc, 0, sizeof(double) * nC * dv);
+    if (dgates) memset(dgates, 0, sizeof(double) * (size_t)n_tok * H * 3);
+    int bad = 0;
+#pragma omp parallel reduction(|: bad)
+    {
+        /* per-thread sums of the key-side gradients, added up once at the end */
+        double* tK = (double*)calloc(nK * dk, sizeof(double));
+        double* tV = (double*)calloc(nK * dv, sizeof(double));
+        double* tKc = (double*)calloc(nC * dk + 1, sizeof(double));
+        double* tVc = (double*)calloc(nC * dv + 1, sizeof(double));
+        const int cap = n_cmp + top_n * lp + window + 1;
+        int* keys = (int*)malloc(sizeof(int) * (size_t)cap);
+        double* logit = (double*)malloc(sizeof(double) * (size_t)cap);
+        double* p = (double*)malloc(sizeof(double) * (size_t)cap);
+        double* o = (double*)malloc(sizeof(double) * (size_t)dv);
+        if (!tK || !tV || !tKc || !tVc || !keys || !logit || !p || !o) bad = 1;
+        else {
+#pragma omp for schedule(dynamic)
+            for (int th = 0; th < n_tok * H; ++th) {
+                const int t = th / H, h = th % H, g = h / G;
+                const double* q = Q + (size_t)th * dk;
+                const double* dout = dO + (size_t)th * dv;
+                double* dq = dQ + (size_t)th * dk;
+                const double* z = gates ? gates + (size_t)th * 3 : NULL;
+                double sig[3];
+                for (int c = 0; c < 3; ++c) sig[c] = z ? sigmoid(z[c]) : 1.0;
+                double od[3] = {0.0, 0.0, 0.0};
+                const size_t kg = (size_t)g * n_tok, cg = (size_t)g * n_cmp;
+                if (branches & 1) {
+                    const int nk = visible_cmp(t, l, s, n_cmp);
+                    for (int i = 0; i < nk; ++i) keys[i] = i;
+                    od[0] = attend_list_bwd(q, Kc + cg * dk, Vc + cg * dv, dk, dv, scale, keys, nk, dout, sig[0],
+                                            logit, p, o, dq, tKc + cg * dk, tVc + cg * dv);
+                }
+                if (branches & 2) {
+                    int nk = 0;
+                    const int* sl = sel + ((size_t)t * H_kv + g) * top_n;
+                    for (int c = 0; c < top_n; ++c) {
+                        const int j = sl[c];
+                        if (j < 0) continue;
+                        int dup = 0;
+                        for (int c2 = 0; c2 < c; ++c2) dup |= (sl[c2] == j);
+                        if (dup) continue;
+                        for (int x = j * lp; x < (j + 1) * lp && x <= t; ++x) keys[nk++] = x;
+                    }
+                    od[1] = attend_list_bwd(q, K + kg * dk, V + kg * dv, dk, dv, scale, keys, nk, dout, sig[1],
+                                            logit, p, o, dq, tK + kg * dk, tV + kg * dv);
+                }
+                if (branches & 4) {
+                    int nk = 0;
+                    const int t0 = (t - window + 1) > 0 ? (t - window + 1) : 0;
+                    for (int x = t0; x <= t && window > 0; ++x) keys[nk++] = x;
+                    od[2] = attend_list_bwd(q, K + kg * dk, V + kg * dv, dk, dv, scale, keys, nk, dout, sig[2],
+                                            logit, p, o, dq, tK + kg * dk, tV + kg * dv);
+                }
+                if (dgates)
+                    for (int c = 0; c < 3; ++c)
+                        if (branches & (1 << c)) dgates[(size_t)th * 3 + c] = sig[c] * (1.0 - sig[c]) * od[c];
+            }
+#pragma omp critical
+            {
+                for (size_t i = 0; i < nK * dk; ++i) dK[i] += tK[i];
+                for (size_t i = 0; i < nK * dv; ++i) dV[i] += tV[i];
+                if (dKc) for (size_t i = 0; i < nC * dk; ++i) dKc[i] += tKc[i];
+                if (dVc) for (size_t i = 0; i < nC * dv; ++i) dVc[i] += tVc[i];
+            }
+        }
+        free(tK); free(tV); free(tKc); free(tVc); free(keys); free(logit); free(p); free(o);
+    }
+    return bad ? -2 : 0;
+}
+
+/* Backward of the linear block map of step 1 over blocks 0 .. nblk-1 (block i covers
+ * tokens i*s .. i*s+l-1), for the gradient dY [nblk, d_out] of its output.  Since
+ * Y[i][o] = sum_{r,e} (X[i*s+r][e] + pe[r][e]) W[r*d+e][o]:
+ *   dX[i*s+r][e] += sum_o W[r*d+e][o] dY[i][o]     (a token in several blocks sums them)
+ *   dpe[r][e]    += the same sum
+ *   dW[r*d+e][o] += (X[i*s+r][e] + pe[r][e]) dY[i][o]
+ * X [n_tok, d]; pe [l, d] or NULL; W [l*d, d_out]; dX [n_tok, d]; dW [l*d, d_out]; dpe
+ * [l, d] or NULL.  Accumulates (the caller zeroes), so heads and sequences can be summed. */
+ORACLE_API void oracle_compress_linear_bwd(int n_tok, int d, int d_out, int l, int s, int nblk,
+                                           const double* X, const double* pe, const double* W,
+                                           const double* dY, double* dX, double* dW, double* dpe)
+{
+    (void)n_tok;
+    for (int i = 0; i < nblk; ++i) {
+        const double* dy = dY + (size_t)i * d_out;
+        for (int r = 0; r < l; ++r) {
+            for (int e = 0; e < d; ++e) {
+                const double* wrow = W + (size_t)(r * d + e) * d_out;
+                double x = X[(size_t)(i * s + r) * d + e];
+                if (pe) x += pe[r * d + e];
+                double gx = 0.0;
+                for (int o = 0; o < d_out; ++o) {
+                    gx += wrow[o] * dy[o];
+                    dW[(size_t)(r * d + e) * d_out + o] += x * dy[o];
+                }
+                dX[(size_t)(i * s + r) * d + e] += gx;
+                if (dpe) dpe[r * d + e] += gx;
+            }
+        }
     }
 }
 

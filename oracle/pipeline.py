@@ -11,7 +11,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from . import attend, compress_linear, compress_mean, score_select
+from . import attend, compress_linear, compress_linear_bwd, compress_mean, nsa_bwd, score_select
 
 
 def round_to_bf16(x) -> np.ndarray:
@@ -49,3 +49,32 @@ def forward_rows(cfg, Q, K, V, Kc, Vc, gates, rows) -> dict:
     at = attend(cfg, Qr, rows, K, V, ss["sel"], ss["o_cmp"], gr)
     ss.update(at)
     return ss
+
+
+def backward(cfg, Q, K, V, w_k, w_v, pe_k, pe_v, sel, gates, dO, branches=None) -> dict:
+    """Gradients of one batch element's gated output through steps 1, 2 and 5-7 (the
+    selection ``sel`` held fixed), with the compressed keys/values kept in fp64.
+
+    Returns dict(dq, dk, dv, dgates, dkc, dvc, dw_k, dw_v, dpe_k, dpe_v): dk/dv include the
+    compressed branch's contribution through the block map; dw_*/dpe_* are the block map's
+    weight and position-embedding gradients summed over the KV heads.
+    """
+    branches = cfg.branches if branches is None else branches
+    Kc, Vc = compress_all(cfg, K, V, w_k, w_v, pe_k, pe_v, round_cmp=False)
+    g = nsa_bwd(cfg, Q, K, V, Kc, Vc, sel, gates, dO, branches)
+    out = dict(g)
+    out["dw_k"] = np.zeros_like(np.asarray(w_k, dtype=np.float64))
+    out["dw_v"] = np.zeros_like(np.asarray(w_v, dtype=np.float64))
+    out["dpe_k"] = np.zeros((cfg.cmp_block, cfg.d_k))
+    out["dpe_v"] = np.zeros((cfg.cmp_block, cfg.d_v))
+    if branches & 1:
+        for h in range(K.shape[0]):
+            bk = compress_linear_bwd(K[h], pe_k, w_k, g["dkc"][h], cfg.cmp_block, cfg.cmp_stride)
+            bv = compress_linear_bwd(V[h], pe_v, w_v, g["dvc"][h], cfg.cmp_block, cfg.cmp_stride)
+            out["dk"][h] += bk["dx"]
+            out["dv"][h] += bv["dx"]
+            out["dw_k"] += bk["dw"]
+            out["dw_v"] += bv["dw"]
+            out["dpe_k"] += bk["dpe"]
+            out["dpe_v"] += bv["dpe"]
+    return out
