@@ -181,6 +181,36 @@ DecodeWs decode_ws(const Shape& s) {
     return w;
 }
 
+// backward of the branches: K, V in fragment order for the statistics pass, the per-row
+// statistics, and the selected branch's block lists (own block included)
+struct BwdWs {
+    size_t kf, vf, stats, hist, bcnt, bstart, tstart, entries, total;
+    int tpad, n_chunk, n_bucket;
+};
+BwdWs bwd_ws(const Shape& s) {
+    BwdWs w{};
+    w.tpad = round_up(s.T, 64) + 64;
+    const size_t bg = (size_t)s.B * s.Hkv;
+    size_t off = 0;
+    w.kf = off; off = align_up(off + bg * w.tpad * s.dk * 2, 256);
+    w.vf = off; off = align_up(off + bg * w.tpad * s.dv * 2, 256);
+    w.stats = off; off = align_up(off + (size_t)s.B * s.T * s.H * 12 * 4, 256);
+    if (s.br & NSA_BR_SLC) {
+        w.n_chunk = nsa::moba_n_chunk(s.T);
+        w.n_bucket = (int)(bg * s.n_slc);
+        w.hist = off; off = align_up(off + bg * w.n_chunk * s.n_slc * 4, 256);
+        w.bcnt = off; off = align_up(off + (size_t)w.n_bucket * 4, 256);
+        w.bstart = off; off = align_up(off + (size_t)(w.n_bucket + 1) * 4, 256);
+        w.tstart = off; off = align_up(off + (size_t)(w.n_bucket + 1) * 4, 256);
+        w.entries = off; off = align_up(off + bg * s.T * s.n * 4, 256);
+    }
+    w.total = off;
+    return w;
+}
+
+// backward of the linear block map: one column-sum vector per map
+size_t compress_bwd_ws(const Shape& s) { return align_up((size_t)s.dk * 4, 256) + align_up((size_t)s.dv * 4, 256); }
+
 nsa_status check_ws(void* ws, size_t have, size_t need) {
     if (need == 0) return NSA_OK;
     if (!ws) return fail(NSA_ERR_WORKSPACE, "workspace is NULL");
@@ -213,6 +243,8 @@ nsa_status nsa_workspace_size(const nsa_config* cfg, int op, size_t* bytes) {
         case NSA_OP_SPARSE_ATTN: *bytes = attn_ws(s).total; break;
         case NSA_OP_DECODE: *bytes = decode_ws(s).total; break;
         case NSA_OP_FULL_ATTN: *bytes = full_ws(s).total; break;
+        case NSA_OP_SPARSE_BWD: *bytes = bwd_ws(s).total; break;
+        case NSA_OP_COMPRESS_BWD: *bytes = compress_bwd_ws(s); break;
         default: return fail(NSA_ERR_SHAPE, "unknown op");
     }
     return NSA_OK;
@@ -527,6 +559,140 @@ nsa_status nsa_decode(const nsa_config* cfg, const void* q, const void* K_cache,
     p.scale_log2 = s.scale * nsa::kLog2eHost;
     if (!nsa::launch_decode(s.dk, s.dv, p, as_stream(stream))) return fail(NSA_ERR_UNSUPPORTED, "no decode kernel");
     return hip_check("decode");
+}
+
+nsa_status nsa_sparse_attn_bwd(const nsa_config* cfg, const void* Q, const void* K, const void* V,
+                               const void* K_cmp, const void* V_cmp, const int32_t* sel_idx, const float* lse_cmp,
+                               const float* o_cmp, const float* gate_logits, const void* dO, float* dQ, float* dK,
+                               float* dV, float* dK_cmp, float* dV_cmp, float* d_gate_logits, void* ws,
+                               size_t ws_bytes, void* stream) {
+    g_detail.clear();
+    Shape s;
+    nsa_status st = check_config(cfg, &s);
+    if (st != NSA_OK) return st;
+    if (!Q || !K || !V || !dO || !dQ || !dK || !dV) return fail(NSA_ERR_NULL, "Q, K, V, dO, dQ, dK and dV are required");
+    if ((s.br & NSA_BR_SLC) && !sel_idx) return fail(NSA_ERR_NULL, "sel_idx is required for the selected branch");
+    if ((s.br & NSA_BR_CMP) && (!K_cmp || !V_cmp || !lse_cmp || !o_cmp || !dK_cmp || !dV_cmp))
+        return fail(NSA_ERR_NULL, "the compressed branch needs K_cmp, V_cmp, lse_cmp, o_cmp, dK_cmp and dV_cmp");
+    if (d_gate_logits && !gate_logits) return fail(NSA_ERR_NULL, "d_gate_logits needs gate_logits");
+    if ((s.br & NSA_BR_WIN) && s.w <= 0) return fail(NSA_ERR_SHAPE, "window branch with window = 0");
+    if ((long long)s.T >= (1LL << 26)) return fail(NSA_ERR_UNSUPPORTED, "sequence too long for the block lists");
+    const BwdWs w = bwd_ws(s);
+    if ((st = check_ws(ws, ws_bytes, w.total)) != NSA_OK) return st;
+    const void* ptrs[] = {Q, K, V, dO, dQ, dK, dV};
+    const char* names[] = {"Q", "K", "V", "dO", "dQ", "dK", "dV"};
+    for (int i = 0; i < 7; ++i)
+        if ((st = check_align16(ptrs[i], names[i])) != NSA_OK) return st;
+    if ((s.br & NSA_BR_CMP) &&
+        ((st = check_align16(dK_cmp, "dK_cmp")) != NSA_OK || (st = check_align16(dV_cmp, "dV_cmp")) != NSA_OK))
+        return st;
+    const hipStream_t hs = as_stream(stream);
+    using nsa::u16;
+    const size_t bg = (size_t)s.B * s.Hkv;
+    const bool cmp = (s.br & NSA_BR_CMP) != 0;
+    nsa::launch_fill_zero(dK, bg * s.T * s.dk, hs);
+    nsa::launch_fill_zero(dV, bg * s.T * s.dv, hs);
+    if (cmp) {
+        nsa::launch_fill_zero(dK_cmp, bg * s.n_cmp * s.dk, hs);
+        nsa::launch_fill_zero(dV_cmp, bg * s.n_cmp * s.dv, hs);
+    }
+    // 1. per-row statistics (the forward's selected and window branches recomputed)
+    u16* kf = at<u16>(ws, w.kf);
+    u16* vf = at<u16>(ws, w.vf);
+    if (!nsa::launch_tile_kv(s.dk, s.dv, static_cast<const u16*>(K), static_cast<const u16*>(V), kf, vf, (int)bg, s.T,
+                             w.tpad, hs))
+        return fail(NSA_ERR_UNSUPPORTED, "no layout kernel");
+    nsa::AttnParams a{};
+    a.Q = static_cast<const u16*>(Q);
+    a.Kf = kf;
+    a.Vf = vf;
+    a.sel = sel_idx;
+    a.o_cmp = o_cmp;
+    a.gates = gate_logits;
+    a.lse_cmp = lse_cmp;
+    a.dO = static_cast<const u16*>(dO);
+    a.stats = at<float>(ws, w.stats);
+    a.dgates = d_gate_logits;
+    a.B = s.B; a.T = s.T; a.Tpad = w.tpad; a.Hkv = s.Hkv; a.G = s.G; a.lp = s.lp; a.top_n = s.n; a.window = s.w;
+    a.branches = s.br;
+    a.scale_log2 = s.scale * nsa::kLog2eHost;
+    if (!nsa::launch_sparse_attn_stats(s.dk, s.dv, a, hs)) return fail(NSA_ERR_UNSUPPORTED, "no statistics kernel");
+    // 2. dQ
+    nsa::BwdParams p{};
+    p.Q = static_cast<const u16*>(Q);
+    p.K = static_cast<const u16*>(K);
+    p.V = static_cast<const u16*>(V);
+    p.Kc = static_cast<const u16*>(K_cmp);
+    p.Vc = static_cast<const u16*>(V_cmp);
+    p.sel = sel_idx;
+    p.dO = static_cast<const u16*>(dO);
+    p.stats = a.stats;
+    p.dQ = dQ; p.dK = dK; p.dV = dV; p.dKc = dK_cmp; p.dVc = dV_cmp;
+    p.B = s.B; p.T = s.T; p.Hkv = s.Hkv; p.G = s.G; p.N = s.n_cmp; p.l = s.l; p.s = s.s; p.lp = s.lp; p.top_n = s.n;
+    p.window = s.w; p.branches = s.br; p.n_slc = s.n_slc;
+    p.scale = s.scale;
+    p.scale_log2 = s.scale * nsa::kLog2eHost;
+    if (!nsa::launch_bwd_dq(s.dk, s.dv, p, hs)) return fail(NSA_ERR_UNSUPPORTED, "no dQ kernel");
+    // 3. block lists of the selected branch
+    long long n_slc_items = 0;
+    if (s.br & NSA_BR_SLC) {
+        nsa::MobaParams m{};
+        m.sel = sel_idx;
+        m.hist = at<int>(ws, w.hist);
+        m.bucket_cnt = at<int>(ws, w.bcnt);
+        m.bucket_start = at<int>(ws, w.bstart);
+        m.tile_start = at<int>(ws, w.tstart);
+        m.entries = at<int>(ws, w.entries);
+        m.B = s.B; m.T = s.T; m.Hkv = s.Hkv; m.lp = s.lp; m.n_slc = s.n_slc; m.top_n = s.n;
+        m.n_chunk = w.n_chunk; m.n_bucket = w.n_bucket; m.keep_own = 1;
+        nsa::launch_block_lists(m, hs);
+        p.bucket_start = m.bucket_start;
+        p.tile_start = m.tile_start;
+        p.entries = m.entries;
+        p.n_bucket = w.n_bucket;
+        p.nsb = (s.lp + 63) / 64;
+        n_slc_items = (long long)nsa::moba_max_tiles((int)bg, s.T, s.n, s.n_slc) * p.nsb;
+    }
+    // 4. dK, dV, dK_cmp, dV_cmp
+    p.n_qt = (s.T + nsa::kBwdTile - 1) / nsa::kBwdTile;
+    p.n_kb_cmp = cmp ? (s.n_cmp + 63) / 64 : 0;
+    p.n_cmp_items = (int)(bg * p.n_kb_cmp * p.n_qt);
+    p.n_kb_win = (s.br & NSA_BR_WIN) ? (s.T + 63) / 64 : 0;
+    p.n_qt_win = (64 + s.w - 1 + nsa::kBwdTile - 1) / nsa::kBwdTile;
+    p.n_win_items = (int)(bg * p.n_kb_win * p.n_qt_win);
+    const long long n_items = (long long)p.n_cmp_items + p.n_win_items + n_slc_items;
+    if (n_items >= (1LL << 31)) return fail(NSA_ERR_SHAPE, "problem too large");
+    if (!nsa::launch_bwd_dkv(s.dk, s.dv, p, (int)n_items, hs)) return fail(NSA_ERR_UNSUPPORTED, "no dK/dV kernel");
+    return hip_check("sparse_attn_bwd");
+}
+
+nsa_status nsa_compress_bwd(const nsa_config* cfg, const void* K, const void* V, const void* W_k, const void* W_v,
+                            const void* pe_k, const void* pe_v, const float* dK_cmp, const float* dV_cmp, float* dK,
+                            float* dV, float* dW_k, float* dW_v, float* dpe_k, float* dpe_v, void* ws,
+                            size_t ws_bytes, void* stream) {
+    g_detail.clear();
+    Shape s;
+    nsa_status st = check_config(cfg, &s);
+    if (st != NSA_OK) return st;
+    if (s.phi != NSA_PHI_LINEAR) return fail(NSA_ERR_UNSUPPORTED, "the block-map backward implements the linear phi");
+    if (!K || !V || !W_k || !W_v || !pe_k || !pe_v || !dK_cmp || !dV_cmp || !dK || !dV || !dW_k || !dW_v || !dpe_k ||
+        !dpe_v)
+        return fail(NSA_ERR_NULL, "every argument is required");
+    if ((st = check_ws(ws, ws_bytes, compress_bwd_ws(s))) != NSA_OK) return st;
+    const void* ptrs[] = {dW_k, dW_v, dpe_k, dpe_v};
+    const char* names[] = {"dW_k", "dW_v", "dpe_k", "dpe_v"};
+    for (int i = 0; i < 4; ++i)
+        if ((st = check_align16(ptrs[i], names[i])) != NSA_OK) return st;
+    const hipStream_t hs = as_stream(stream);
+    using nsa::u16;
+    const int BG = s.B * s.Hkv;
+    float* ck = at<float>(ws, 0);
+    float* cv = at<float>(ws, align_up((size_t)s.dk * 4, 256));
+    nsa::launch_compress_bwd(static_cast<const u16*>(K), static_cast<const u16*>(W_k), static_cast<const u16*>(pe_k),
+                             dK_cmp, dK, dW_k, dpe_k, ck, BG, s.T, s.n_cmp, s.dk, s.l, s.s, hs);
+    nsa::launch_compress_bwd(static_cast<const u16*>(V), static_cast<const u16*>(W_v), static_cast<const u16*>(pe_v),
+                             dV_cmp, dV, dW_v, dpe_v, cv, BG, s.T, s.n_cmp, s.dv, s.l, s.s, hs);
+    return hip_check("compress_bwd");
 }
 
 const char* nsa_status_string(nsa_status status) {

@@ -1,0 +1,490 @@
+// Backward pass of the three branches and of the linear block map (zjai.club notes, section 4:
+// the method trains natively, forward and backward; section 14: the top-k choice has no
+// derivative, so the selection is held fixed and the compressed branch carries the gradient
+// into the block representations).
+//
+// For one softmax attention o = sum_k p_k v_k with p = softmax(tau q.k) and upstream gradient
+// go = sigma dO (sigma: the branch's gate weight), with D = sigma <dO, o> and
+// P = exp2(scaled score - lse2) recomputed from the forward's statistics:
+//   dS = P (sigma dP - D), dP = <dO, v>;   dq = tau sum_k dS k;   dk = tau dS q;   dv = sigma P dO.
+//
+// bwd_dq_kernel    one wave per (token, KV group): the group's G heads are the 16-wide MFMA
+//                  column tile (as in the forward); for each branch its keys are walked in
+//                  32-key chunks: S^T = K.Q^T and dP^T = V.dO^T on the MFMA, dS^T in
+//                  registers, dQ^T += K^T.dS^T with K^T read through the transposing LDS
+//                  read from a row-major chunk staged in LDS.
+// bwd_dkv_kernel   one workgroup per (64 keys, <= 128 query tokens) work item, a wave per
+//                  16 keys: the item's tokens are taken two at a time (32 head rows staged
+//                  in LDS), S = Q.K^T and dP = dO.V^T with the keys' fragments held in
+//                  registers, then dV^T += dO^T.(sigma P) and dK^T += Q^T.dS; the item's
+//                  sums are added to the fp32 gradients with atomics.  Items: compressed
+//                  keys x 128-token query tiles (tokens that see the keys), window key
+//                  blocks x the tokens whose window covers them, and for the selected
+//                  branch a selection block x 128 of the tokens that selected it (the
+//                  inverted lists of the block-major forward, own block included).
+// compress_bwd_*   the linear block map: column sums of dY, dPE = W.colsum, dW = X^T.dY
+//                  (X = block rows + PE, split over row ranges, atomics), dX = dY.W^T added
+//                  into the raw key/value gradients (a token lies in l/s blocks).  fp32 FMA.
+#include <algorithm>
+
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace nsa {
+
+namespace {
+
+constexpr int kItemKeys = 64;    // keys per dK/dV work item (4 waves x 16)
+
+// key `key` of a work item is attended by query token t in branch `kind`
+__device__ __forceinline__ bool bwd_visible(const BwdParams& p, int kind, int key, int t) {
+    if (t < 0) return false;
+    if (kind == 0) return key * p.s + p.l - 1 <= t;
+    if (kind == 1) return key <= t;
+    return key <= t && key >= t - p.window + 1;
+}
+
+}  // namespace
+
+__global__ __launch_bounds__(256) void fill_zero_kernel(float* __restrict__ x, size_t n) {
+    const size_t stride = (size_t)gridDim.x * 256;
+    const size_t n4 = n / 4;
+    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += stride)
+        reinterpret_cast<f32x4*>(x)[i] = zero4();
+    for (size_t i = n4 * 4 + (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += stride) x[i] = 0.f;
+}
+
+// ---------------------------------------------------------------------------
+template <int DK, int DV>
+__global__ __launch_bounds__(64) void bwd_dq_kernel(BwdParams p) {
+    constexpr int NDS = DK / 32, NDD = DV / 32, NDK = DK / 16;
+    constexpr int KSTR = DK + 16;   // 8-byte aligned rows for the transposing read
+    __shared__ __attribute__((aligned(16))) u16 kt[32 * KSTR];
+    const int lane = threadIdx.x, li = lane & 15, lq = lane >> 4;
+    const int t = blockIdx.x, bg = blockIdx.y;
+    const int b = bg / p.Hkv, g = bg % p.Hkv;
+    const int G = p.G, H = p.Hkv * G;
+    const bool head_ok = li < G;
+    const size_t row = ((size_t)b * p.T + t) * H + g * G + min(li, G - 1);
+
+    bf16x8 qf[NDS], df[NDD];
+#pragma unroll
+    for (int ds = 0; ds < NDS; ++ds) qf[ds] = head_ok ? ld8(p.Q + row * DK + 32 * ds + 8 * lq) : zero8();
+#pragma unroll
+    for (int dd = 0; dd < NDD; ++dd) df[dd] = head_ok ? ld8(p.dO + row * DV + 32 * dd + 8 * lq) : zero8();
+    f32x4 acc[NDK];
+#pragma unroll
+    for (int dt = 0; dt < NDK; ++dt) acc[dt] = zero4();
+
+    // keys key0 .. key0+31 of Kb/Vb (rows >= nrows read as zero); keys outside [lo, hi] masked
+    auto chunk = [&](const u16* Kb, const u16* Vb, int nrows, int key0, int lo, int hi, const f32x4& st) {
+        __syncthreads();   // the previous chunk's LDS reads are complete
+        for (int i = lane; i < 32 * (DK / 8); i += 64) {
+            const int r = i / (DK / 8), col = (i % (DK / 8)) * 8;
+            const int key = key0 + r;
+            u32x4 v = {0u, 0u, 0u, 0u};
+            if (key < nrows) v = *reinterpret_cast<const u32x4*>(Kb + (size_t)key * DK + col);
+            *reinterpret_cast<u32x4*>(&kt[r * KSTR + col]) = v;
+        }
+        bf16x8 va[2][NDD];
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+            const int key = key0 + 16 * tt + li;
+#pragma unroll
+            for (int dd = 0; dd < NDD; ++dd)
+                va[tt][dd] = key < nrows ? ld8(Vb + (size_t)key * DV + 32 * dd + 8 * lq) : zero8();
+        }
+        __syncthreads();
+        f32x4 s0 = zero4(), s1 = zero4(), d0 = zero4(), d1 = zero4();
+#pragma unroll
+        for (int ds = 0; ds < NDS; ++ds) {
+            s0 = mfma16(ld8(&kt[li * KSTR + 32 * ds + 8 * lq]), qf[ds], s0);
+            s1 = mfma16(ld8(&kt[(16 + li) * KSTR + 32 * ds + 8 * lq]), qf[ds], s1);
+        }
+#pragma unroll
+        for (int dd = 0; dd < NDD; ++dd) {
+            d0 = mfma16(va[0][dd], df[dd], d0);
+            d1 = mfma16(va[1][dd], df[dd], d1);
+        }
+        // C rows: keys key0 + 4lq + r (tile 0) and key0 + 16 + 4lq + r (tile 1); column: head
+        f32x4 ga, gb;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int ka = key0 + 4 * lq + r, kb = ka + 16;
+            const float pa = (head_ok && ka >= lo && ka <= hi) ? fast_exp2(s0[r] * p.scale_log2 - st[0]) : 0.f;
+            const float pb = (head_ok && kb >= lo && kb <= hi) ? fast_exp2(s1[r] * p.scale_log2 - st[0]) : 0.f;
+            ga[r] = pa * (st[2] * d0[r] - st[1]);
+            gb[r] = pb * (st[2] * d1[r] - st[1]);
+        }
+        bf16x8 gh, gl;
+        pack_p_split(ga, gb, gh, gl);
+#pragma unroll
+        for (int dt = 0; dt < NDK; ++dt) {
+            const bf16x8 a = ld_vt_tr(kt, KSTR, 0, 16 * dt);
+            acc[dt] = mfma16(a, gh, acc[dt]);
+            acc[dt] = mfma16(a, gl, acc[dt]);
+        }
+    };
+
+    if (p.branches & 1) {
+        const f32x4 st = *reinterpret_cast<const f32x4*>(p.stats + row * 12);
+        const int nc = t < p.l - 1 ? 0 : min((t - p.l + 1) / p.s + 1, p.N);
+        const u16* Kb = p.Kc + (size_t)bg * p.N * DK;
+        const u16* Vb = p.Vc + (size_t)bg * p.N * DV;
+        for (int key0 = 0; key0 < nc; key0 += 32) chunk(Kb, Vb, p.N, key0, 0, nc - 1, st);
+    }
+    const u16* Kb = p.K + (size_t)bg * p.T * DK;
+    const u16* Vb = p.V + (size_t)bg * p.T * DV;
+    if (p.branches & 2) {
+        const f32x4 st = *reinterpret_cast<const f32x4*>(p.stats + row * 12 + 4);
+        const int32_t* sl = p.sel + (((size_t)b * p.T + t) * p.Hkv + g) * p.top_n;
+        for (int c = 0; c < p.top_n; ++c) {
+            const int j = sl[c];
+            if (j < 0 || j * p.lp > t) continue;
+            const int lo = j * p.lp, hi = min(t, lo + p.lp - 1);
+            for (int key0 = lo; key0 <= hi; key0 += 32) chunk(Kb, Vb, p.T, key0, lo, hi, st);
+        }
+    }
+    if (p.branches & 4) {
+        const f32x4 st = *reinterpret_cast<const f32x4*>(p.stats + row * 12 + 8);
+        const int wlo = max(0, t - p.window + 1);
+        for (int key0 = wlo & ~31; key0 <= t; key0 += 32) chunk(Kb, Vb, p.T, key0, wlo, t, st);
+    }
+    if (!head_ok) return;
+    // dQ^T C layout: rows d = 16 dt + 4 lq + r of head li
+#pragma unroll
+    for (int dt = 0; dt < NDK; ++dt)
+        *reinterpret_cast<f32x4*>(p.dQ + row * DK + 16 * dt + 4 * lq) = acc[dt] * p.scale;
+}
+
+// ---------------------------------------------------------------------------
+template <int DK, int DV>
+__global__ __launch_bounds__(256) void bwd_dkv_kernel(BwdParams p) {
+    constexpr int NDS = DK / 32, NDD = DV / 32, NDK = DK / 16, NDV = DV / 16;
+    constexpr int QSTR = DK + 16, OSTR = DV + 16;
+    __shared__ __attribute__((aligned(16))) u16 qs[32 * QSTR];   // rows: token A heads, token B heads
+    __shared__ __attribute__((aligned(16))) u16 os[32 * OSTR];
+    __shared__ __attribute__((aligned(16))) float rs[32 * 4];   // lse2, D, sigma per row
+    __shared__ int toks[kBwdTile];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, li = lane & 15, lq = lane >> 4;
+    const int G = p.G, H = p.Hkv * G;
+
+    // ---- work item: kind (0 compressed, 1 selected, 2 window), group, keys, query tokens ----
+    int kind, bg, kbase, kend, nq;
+    int x = blockIdx.x;
+    int t0 = 0, e0 = 0;
+    if (x < p.n_cmp_items) {
+        kind = 0;
+        const int per_bg = p.n_kb_cmp * p.n_qt;
+        bg = x / per_bg;
+        const int r = x % per_bg, kb = r / p.n_qt, qt = r % p.n_qt;
+        kbase = kb * kItemKeys;
+        kend = min(kbase + kItemKeys, p.N);
+        t0 = max(qt * kBwdTile, kbase * p.s + p.l - 1);   // first token that sees key kbase
+        const int t1 = min((qt + 1) * kBwdTile, p.T);
+        if (t0 >= t1) return;
+        nq = t1 - t0;
+    } else if ((x -= p.n_cmp_items) < p.n_win_items) {
+        kind = 2;
+        const int per_bg = p.n_kb_win * p.n_qt_win;
+        bg = x / per_bg;
+        const int r = x % per_bg, kb = r / p.n_qt_win, qt = r % p.n_qt_win;
+        kbase = kb * kItemKeys;
+        kend = min(kbase + kItemKeys, p.T);
+        t0 = kbase + qt * kBwdTile;
+        const int t1 = min(min(t0 + kBwdTile, kbase + kItemKeys + p.window - 1), p.T);
+        if (t0 >= t1) return;
+        nq = t1 - t0;
+    } else {
+        x -= p.n_win_items;
+        kind = 1;
+        const int sub = x % p.nsb;
+        x /= p.nsb;
+        if (x >= p.tile_start[p.n_bucket]) return;
+        int lo = 0, hi = p.n_bucket - 1;   // the bucket owning list tile x
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (p.tile_start[mid] <= x) lo = mid;
+            else hi = mid - 1;
+        }
+        bg = lo / p.n_slc;
+        const int j = lo % p.n_slc;
+        kbase = j * p.lp + kItemKeys * sub;
+        kend = min(j * p.lp + p.lp, p.T);
+        if (kbase >= kend) return;
+        e0 = p.bucket_start[lo] + (x - p.tile_start[lo]) * kBwdTile;
+        nq = min(kBwdTile, p.bucket_start[lo + 1] - e0);
+    }
+    for (int i = threadIdx.x; i < kBwdTile; i += 256)
+        toks[i] = i >= nq ? -1 : kind == 1 ? (p.entries[e0 + i] >> 5) : t0 + i;
+    const int b = bg / p.Hkv, g = bg % p.Hkv;
+    const int nrows = kind == 0 ? p.N : p.T;
+    const u16* Kb = kind == 0 ? p.Kc + (size_t)bg * p.N * DK : p.K + (size_t)bg * p.T * DK;
+    const u16* Vb = kind == 0 ? p.Vc + (size_t)bg * p.N * DV : p.V + (size_t)bg * p.T * DV;
+    const int key = kbase + 16 * wave + li;
+    const bool key_ok = key < kend && key < nrows;
+
+    // this lane's key row as the B operand of Q.K^T and dO.V^T
+    bf16x8 kfr[NDS], vfr[NDD];
+#pragma unroll
+    for (int ds = 0; ds < NDS; ++ds) kfr[ds] = key_ok ? ld8(Kb + (size_t)key * DK + 32 * ds + 8 * lq) : zero8();
+#pragma unroll
+    for (int dd = 0; dd < NDD; ++dd) vfr[dd] = key_ok ? ld8(Vb + (size_t)key * DV + 32 * dd + 8 * lq) : zero8();
+    f32x4 dk_acc[NDK], dv_acc[NDV];
+#pragma unroll
+    for (int dt = 0; dt < NDK; ++dt) dk_acc[dt] = zero4();
+#pragma unroll
+    for (int dt = 0; dt < NDV; ++dt) dv_acc[dt] = zero4();
+
+    for (int i = 0; i < nq; i += 2) {
+        __syncthreads();   // token list written / the previous pair's LDS reads complete
+        const int tA = toks[i], tB = i + 1 < nq ? toks[i + 1] : -1;
+        for (int idx = threadIdx.x; idx < 32 * (DK / 8); idx += 256) {
+            const int r = idx / (DK / 8), col = (idx % (DK / 8)) * 8;
+            const int tk = r < 16 ? tA : tB, hh = r & 15;
+            u32x4 v = {0u, 0u, 0u, 0u};
+            if (tk >= 0 && hh < G)
+                v = *reinterpret_cast<const u32x4*>(p.Q + (((size_t)b * p.T + tk) * H + g * G + hh) * DK + col);
+            *reinterpret_cast<u32x4*>(&qs[r * QSTR + col]) = v;
+        }
+        for (int idx = threadIdx.x; idx < 32 * (DV / 8); idx += 256) {
+            const int r = idx / (DV / 8), col = (idx % (DV / 8)) * 8;
+            const int tk = r < 16 ? tA : tB, hh = r & 15;
+            u32x4 v = {0u, 0u, 0u, 0u};
+            if (tk >= 0 && hh < G)
+                v = *reinterpret_cast<const u32x4*>(p.dO + (((size_t)b * p.T + tk) * H + g * G + hh) * DV + col);
+            *reinterpret_cast<u32x4*>(&os[r * OSTR + col]) = v;
+        }
+        if (threadIdx.x < 32) {
+            const int r = threadIdx.x, tk = r < 16 ? tA : tB, hh = r & 15;
+            f32x4 st = zero4();
+            if (tk >= 0 && hh < G)
+                st = *reinterpret_cast<const f32x4*>(p.stats + ((((size_t)b * p.T + tk) * H + g * G + hh) * 3 + kind) * 4);
+            *reinterpret_cast<f32x4*>(&rs[r * 4]) = st;
+        }
+        __syncthreads();
+        // S = Q.K^T and dP = dO.V^T: C lane (li = key, lq) holds head rows 4 lq + r
+        f32x4 sA = zero4(), sB = zero4(), pA = zero4(), pB = zero4();
+#pragma unroll
+        for (int ds = 0; ds < NDS; ++ds) {
+            sA = mfma16(ld8(&qs[li * QSTR + 32 * ds + 8 * lq]), kfr[ds], sA);
+            sB = mfma16(ld8(&qs[(16 + li) * QSTR + 32 * ds + 8 * lq]), kfr[ds], sB);
+        }
+#pragma unroll
+        for (int dd = 0; dd < NDD; ++dd) {
+            pA = mfma16(ld8(&os[li * OSTR + 32 * dd + 8 * lq]), vfr[dd], pA);
+            pB = mfma16(ld8(&os[(16 + li) * OSTR + 32 * dd + 8 * lq]), vfr[dd], pB);
+        }
+        const bool vA = key_ok && bwd_visible(p, kind, key, tA);
+        const bool vB = key_ok && bwd_visible(p, kind, key, tB);
+        f32x4 wA, wB, gA, gB;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int hr = 4 * lq + r;
+            const f32x4 stA = *reinterpret_cast<const f32x4*>(&rs[hr * 4]);
+            const f32x4 stB = *reinterpret_cast<const f32x4*>(&rs[(16 + hr) * 4]);
+            const float PA = (vA && hr < G) ? fast_exp2(sA[r] * p.scale_log2 - stA[0]) : 0.f;
+            const float PB = (vB && hr < G) ? fast_exp2(sB[r] * p.scale_log2 - stB[0]) : 0.f;
+            wA[r] = stA[2] * PA;
+            wB[r] = stB[2] * PB;
+            gA[r] = PA * (stA[2] * pA[r] - stA[1]);
+            gB[r] = PB * (stB[2] * pB[r] - stB[1]);
+        }
+        // dV^T += dO^T . (sigma P) and dK^T += Q^T . dS; the row slots of pack_p_split (head
+        // rows 4lq..4lq+3 of token A, then of token B) match the transposing read's key order
+        bf16x8 h8, l8;
+        pack_p_split(wA, wB, h8, l8);
+#pragma unroll
+        for (int dt = 0; dt < NDV; ++dt) {
+            const bf16x8 a = ld_vt_tr(os, OSTR, 0, 16 * dt);
+            dv_acc[dt] = mfma16(a, h8, dv_acc[dt]);
+            dv_acc[dt] = mfma16(a, l8, dv_acc[dt]);
+        }
+        pack_p_split(gA, gB, h8, l8);
+#pragma unroll
+        for (int dt = 0; dt < NDK; ++dt) {
+            const bf16x8 a = ld_vt_tr(qs, QSTR, 0, 16 * dt);
+            dk_acc[dt] = mfma16(a, h8, dk_acc[dt]);
+            dk_acc[dt] = mfma16(a, l8, dk_acc[dt]);
+        }
+    }
+    if (!key_ok) return;
+    // C layout of dK^T / dV^T: lane (li = key, lq) holds dims 16 dt + 4 lq + r
+    float* dKr = (kind == 0 ? p.dKc + (size_t)bg * p.N * DK : p.dK + (size_t)bg * p.T * DK) + (size_t)key * DK;
+    float* dVr = (kind == 0 ? p.dVc + (size_t)bg * p.N * DV : p.dV + (size_t)bg * p.T * DV) + (size_t)key * DV;
+#pragma unroll
+    for (int dt = 0; dt < NDK; ++dt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) unsafeAtomicAdd(dKr + 16 * dt + 4 * lq + r, dk_acc[dt][r] * p.scale);
+#pragma unroll
+    for (int dt = 0; dt < NDV; ++dt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) unsafeAtomicAdd(dVr + 16 * dt + 4 * lq + r, dv_acc[dt][r]);
+}
+
+// ---------------------------------------------------------------------------
+// Linear block map.  Rows of dY are (sequence-group bg, block i), bg-major; X[row][m] for
+// m = r*d + e is K[bg][i*s + r][e] + pe[r][e].
+
+// colsum[o] += sum over 64 rows of dY[row][o]; one thread per column
+__global__ __launch_bounds__(256) void compress_bwd_colsum_kernel(const float* __restrict__ dY, int rows, int d,
+                                                                  float* __restrict__ colsum) {
+    const int o = threadIdx.x;
+    if (o >= d) return;
+    const int r0 = blockIdx.x * 64, r1 = min(r0 + 64, rows);
+    float s = 0.f;
+    for (int r = r0; r < r1; ++r) s += dY[(size_t)r * d + o];
+    unsafeAtomicAdd(colsum + o, s);
+}
+
+// dpe[m] = sum_o W[m][o] colsum[o]
+__global__ __launch_bounds__(256) void compress_bwd_dpe_kernel(const u16* __restrict__ W, const float* __restrict__ colsum,
+                                                               int KD, int d, float* __restrict__ dpe) {
+    const int m = blockIdx.x * 256 + threadIdx.x;
+    if (m >= KD) return;
+    float s = 0.f;
+    for (int o = 0; o < d; ++o) s += bf2f(W[(size_t)m * d + o]) * colsum[o];
+    dpe[m] = s;
+}
+
+// dW[m][o] += sum over this workgroup's 256 rows of X[row][m] dY[row][o]: 64 x 64 output tile,
+// 4 x 4 per thread, 16 rows per LDS step
+__global__ __launch_bounds__(256) void compress_bwd_dw_kernel(const u16* __restrict__ X, const u16* __restrict__ pe,
+                                                              const float* __restrict__ dY, float* __restrict__ dW,
+                                                              int rows, int N, int T, int d, int l, int s) {
+    __shared__ float xs[16][64 + 4], ys[16][64 + 4];
+    const int KD = l * d;
+    const int m0 = blockIdx.x * 64, o0 = blockIdx.y * 64;
+    const int rbeg = blockIdx.z * 256, rend = min(rbeg + 256, rows);
+    const int tm = threadIdx.x % 16, to = threadIdx.x / 16;
+    float acc[4][4] = {};
+    const int rr = m0 / d;   // block offset r of this tile (d is a multiple of 64)
+    for (int r0 = rbeg; r0 < rend; r0 += 16) {
+        __syncthreads();
+        for (int idx = threadIdx.x; idx < 16 * 64; idx += 256) {
+            const int k = idx / 64, c = idx % 64, row = r0 + k;
+            float xv = 0.f, yv = 0.f;
+            if (row < rend) {
+                const int bg = row / N, i = row % N;
+                const int e = m0 % d + c;
+                xv = bf2f(X[((size_t)bg * T + (size_t)i * s + rr) * d + e]) + bf2f(pe[(size_t)rr * d + e]);
+                if (o0 + c < d) yv = dY[(size_t)row * d + o0 + c];
+            }
+            xs[k][c] = xv;
+            ys[k][c] = yv;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            float a[4], bv[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                a[u] = xs[k][tm + 16 * u];
+                bv[u] = ys[k][to + 16 * u];
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) acc[u][v] += a[u] * bv[v];
+        }
+    }
+    (void)KD;
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int m = m0 + tm + 16 * u, o = o0 + to + 16 * v;
+            if (o < d) unsafeAtomicAdd(dW + (size_t)m * d + o, acc[u][v]);
+        }
+}
+
+// dX[row][m] = sum_o dY[row][o] W[m][o], added to dK[bg][i*s + r][e]: 64 rows x 64 m per
+// workgroup, 4 x 4 per thread, 16 o per LDS step
+__global__ __launch_bounds__(256) void compress_bwd_dx_kernel(const float* __restrict__ dY, const u16* __restrict__ W,
+                                                              float* __restrict__ dX, int rows, int N, int T, int d,
+                                                              int l, int s) {
+    __shared__ float ys[16][64 + 4], ws[16][64 + 4];
+    const int KD = l * d;
+    const int row0 = blockIdx.x * 64, m0 = blockIdx.y * 64;
+    const int tr = threadIdx.x % 16, tm = threadIdx.x / 16;
+    float acc[4][4] = {};
+    for (int k0 = 0; k0 < d; k0 += 16) {
+        __syncthreads();
+        for (int idx = threadIdx.x; idx < 16 * 64; idx += 256) {
+            const int k = idx % 16, c = idx / 16;
+            const int row = row0 + c, m = m0 + c;
+            ys[k][c] = row < rows ? dY[(size_t)row * d + k0 + k] : 0.f;
+            ws[k][c] = m < KD ? bf2f(W[(size_t)m * d + k0 + k]) : 0.f;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            float a[4], bv[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                a[u] = ys[k][tr + 16 * u];
+                bv[u] = ws[k][tm + 16 * u];
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) acc[u][v] += a[u] * bv[v];
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int row = row0 + tr + 16 * u;
+        if (row >= rows) continue;
+        const int bg = row / N, i = row % N;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int m = m0 + tm + 16 * v;
+            if (m >= KD) continue;
+            const int r = m / d, e = m % d;
+            unsafeAtomicAdd(dX + ((size_t)bg * T + (size_t)i * s + r) * d + e, acc[u][v]);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+void launch_fill_zero(float* x, size_t n, hipStream_t st) {
+    if (n == 0) return;
+    const size_t blocks = std::min<size_t>((n / 4 + 255) / 256 + 1, 8192);
+    fill_zero_kernel<<<(unsigned)blocks, 256, 0, st>>>(x, n);
+}
+
+bool launch_bwd_dq(int DK, int DV, const BwdParams& p, hipStream_t st) {
+    const dim3 grid(p.T, p.B * p.Hkv);
+    if (DK == 192 && DV == 128) bwd_dq_kernel<192, 128><<<grid, 64, 0, st>>>(p);
+    else if (DK == 128 && DV == 128) bwd_dq_kernel<128, 128><<<grid, 64, 0, st>>>(p);
+    else if (DK == 64 && DV == 64) bwd_dq_kernel<64, 64><<<grid, 64, 0, st>>>(p);
+    else return false;
+    return true;
+}
+
+bool launch_bwd_dkv(int DK, int DV, const BwdParams& p, int n_items, hipStream_t st) {
+    if (n_items <= 0) return true;
+    if (DK == 192 && DV == 128) bwd_dkv_kernel<192, 128><<<n_items, 256, 0, st>>>(p);
+    else if (DK == 128 && DV == 128) bwd_dkv_kernel<128, 128><<<n_items, 256, 0, st>>>(p);
+    else if (DK == 64 && DV == 64) bwd_dkv_kernel<64, 64><<<n_items, 256, 0, st>>>(p);
+    else return false;
+    return true;
+}
+
+void launch_compress_bwd(const u16* X, const u16* W, const u16* pe, const float* dY, float* dX, float* dW, float* dpe,
+                         float* colsum, int BG, int T, int N, int d, int l, int s, hipStream_t st) {
+    const int rows = BG * N, KD = l * d;
+    launch_fill_zero(colsum, (size_t)d, st);
+    launch_fill_zero(dW, (size_t)KD * d, st);
+    if (rows == 0) {
+        launch_fill_zero(dpe, (size_t)KD, st);
+        return;
+    }
+    compress_bwd_colsum_kernel<<<(rows + 63) / 64, 256, 0, st>>>(dY, rows, d, colsum);
+    compress_bwd_dpe_kernel<<<(KD + 255) / 256, 256, 0, st>>>(W, colsum, KD, d, dpe);
+    compress_bwd_dw_kernel<<<dim3(KD / 64, (d + 63) / 64, (rows + 255) / 256), 256, 0, st>>>(X, pe, dY, dW, rows, N, T,
+                                                                                           d, l, s);
+    compress_bwd_dx_kernel<<<dim3((rows + 63) / 64, (KD + 63) / 64), 256, 0, st>>>(dY, W, dX, rows, N, T, d, l, s);
+}
+
+}  // namespace nsa

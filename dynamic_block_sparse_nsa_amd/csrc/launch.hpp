@@ -61,10 +61,17 @@ struct AttnParams {
     const float* o_cmp;  // [B,T,H,DV] (branch CMP)
     const float* gates;  // [B,T,H,3] or null
     u16* O;              // [B,T,H,DV]
+    // backward statistics mode (launch_sparse_attn_stats): instead of O, per (token, head)
+    // and branch c (cmp, slc, win) the base-2 LSE, D_c = sigma_c <dO, o_c> and sigma_c
+    const float* lse_cmp;  // [B,T,H] natural-log LSE of the compressed branch
+    const u16* dO;         // [B,T,H,DV]
+    float* stats;          // [B,T,H,3,4]: lse2, D, sigma, 0
+    float* dgates;         // [B,T,H,3] or null
     int B, T, Tpad, Hkv, G, lp, top_n, window, branches;
     float scale_log2;
 };
 bool launch_sparse_attn(int DK, int DV, const AttnParams& p, int B, hipStream_t st);
+bool launch_sparse_attn_stats(int DK, int DV, const AttnParams& p, hipStream_t st);
 bool launch_tile_kv(int DK, int DV, const u16* K, const u16* V, u16* Kf, u16* Vf, int BG, int T, int Tpad,
                     hipStream_t st);
 
@@ -87,12 +94,50 @@ struct MobaParams {
     float* part_l;             // [B,T,Hkv,top_n]
     float* part_o;             // [B,T,Hkv,top_n,DV]
     int B, T, Tpad, Hkv, lp, n_slc, top_n, n_chunk, n_bucket, n_own;
+    int keep_own;              // 1: the query's own block is listed too (backward lists)
     float scale_log2;
 };
+// the bucket lists alone (hist, prefix, scan, scatter); uses sel, T, Hkv, lp, n_slc, top_n,
+// n_chunk, n_bucket, keep_own and the list buffers
+void launch_block_lists(const MobaParams& p, hipStream_t st);
 int moba_n_chunk(int T);
 int moba_n_own(int BH, int n_slc, int lp);
 int moba_max_tiles(int BH, int T, int top_n, int n_slc);
 bool launch_moba_attn(int DK, int DV, const MobaParams& p, hipStream_t st);
+
+// ---- backward ----
+constexpr int kBwdTile = 128;   // query tokens per dK/dV work item (= the block lists' tile)
+struct BwdParams {
+    const u16* Q;              // [B,T,H,DK]
+    const u16* K;              // [B,Hkv,T,DK] row-major
+    const u16* V;              // [B,Hkv,T,DV]
+    const u16* Kc;             // [B,Hkv,N,DK] (compressed branch)
+    const u16* Vc;             // [B,Hkv,N,DV]
+    const int32_t* sel;        // [B,T,Hkv,top_n]
+    const u16* dO;             // [B,T,H,DV]
+    const float* stats;        // [B,T,H,3,4] lse2, D, sigma (see AttnParams)
+    float* dQ;                 // [B,T,H,DK], written
+    float* dK;                 // [B,Hkv,T,DK], accumulated
+    float* dV;
+    float* dKc;                // [B,Hkv,N,DK], accumulated
+    float* dVc;
+    const int* bucket_start;   // block lists of the selected branch (launch_block_lists)
+    const int* tile_start;
+    const int* entries;
+    int B, T, Hkv, G, N, l, s, lp, top_n, window, branches, n_slc, n_bucket;
+    int nsb;                   // 64-key sub-blocks per selection block
+    int n_kb_cmp, n_qt;        // compressed key blocks, 128-token query tiles
+    int n_kb_win, n_qt_win;    // window key blocks, query tiles per window key block
+    int n_cmp_items, n_win_items;
+    float scale, scale_log2;
+};
+void launch_fill_zero(float* x, size_t n, hipStream_t st);
+bool launch_bwd_dq(int DK, int DV, const BwdParams& p, hipStream_t st);
+bool launch_bwd_dkv(int DK, int DV, const BwdParams& p, int n_items, hipStream_t st);
+// linear block map backward for one of K / V: dX += dY.W^T scattered to tokens, dW and dpe
+// overwritten; colsum: d floats of scratch
+void launch_compress_bwd(const u16* X, const u16* W, const u16* pe, const float* dY, float* dX, float* dW, float* dpe,
+                         float* colsum, int BG, int T, int N, int d, int l, int s, hipStream_t st);
 
 // ---- dense causal attention ----
 struct FullParams {

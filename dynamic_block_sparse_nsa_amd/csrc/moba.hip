@@ -27,6 +27,7 @@ namespace {
 
 constexpr int kCol = 128;    // query columns per work item (4 waves x 2 tiles x 16)
 constexpr int kKeys = 64;    // keys per LDS tile
+static_assert(kCol == kBwdTile, "the backward's work items use the lists' 128-entry tiles");
 
 }  // namespace
 
@@ -41,7 +42,7 @@ __global__ __launch_bounds__(256) void moba_hist_kernel(MobaParams p) {
     for (int e = threadIdx.x; e < (t1 - t0) * p.top_n; e += 256) {
         const int t = t0 + e / p.top_n, s = e % p.top_n;
         const int j = p.sel[(((size_t)b * p.T + t) * p.Hkv + h) * p.top_n + s];
-        if (j >= 0 && j < p.n_slc && j != t / p.lp) atomicAdd(&hist[j], 1);
+        if (j >= 0 && j < p.n_slc && (p.keep_own || j != t / p.lp)) atomicAdd(&hist[j], 1);
     }
     __syncthreads();
     int* out = p.hist + ((size_t)bh * p.n_chunk + c) * p.n_slc;
@@ -122,7 +123,7 @@ __global__ __launch_bounds__(256) void moba_scatter_kernel(MobaParams p) {
     for (int e = threadIdx.x; e < (t1 - t0) * p.top_n; e += 256) {
         const int t = t0 + e / p.top_n, s = e % p.top_n;
         const int j = p.sel[(((size_t)b * p.T + t) * p.Hkv + h) * p.top_n + s];
-        if (j >= 0 && j < p.n_slc && j != t / p.lp) {
+        if (j >= 0 && j < p.n_slc && (p.keep_own || j != t / p.lp)) {
             const int pos = atomicAdd(&cursor[j], 1);
             p.entries[pos] = (t << 5) | s;
         }
@@ -376,12 +377,16 @@ int moba_max_tiles(int BH, int T, int top_n, int n_slc) {
     return (int)(((long long)BH * T * top_n) / kCol) + BH * n_slc;
 }
 
-bool launch_moba_attn(int DK, int DV, const MobaParams& p, hipStream_t st) {
+void launch_block_lists(const MobaParams& p, hipStream_t st) {
     const size_t lds_cnt = (size_t)p.n_slc * 4;
     moba_hist_kernel<<<dim3(p.n_chunk, p.B * p.Hkv), 256, lds_cnt, st>>>(p);
     moba_prefix_kernel<<<(p.n_bucket + 255) / 256, 256, 0, st>>>(p);
     moba_scan_kernel<<<1, 1024, 0, st>>>(p);
     moba_scatter_kernel<<<dim3(p.n_chunk, p.B * p.Hkv), 256, lds_cnt, st>>>(p);
+}
+
+bool launch_moba_attn(int DK, int DV, const MobaParams& p, hipStream_t st) {
+    launch_block_lists(p, st);
     int nwg = p.n_own + moba_max_tiles(p.B * p.Hkv, p.T, p.top_n, p.n_slc);
     nwg = (nwg + 7) / 8 * 8;
     if (DK == 128 && DV == 128) moba_attn_kernel<128, 128><<<nwg, 256, 0, st>>>(p);

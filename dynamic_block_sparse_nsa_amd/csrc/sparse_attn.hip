@@ -82,11 +82,13 @@ struct SoftmaxState {
         }
     }
 
-    __device__ __forceinline__ void finish() {
+    // normalizes o; returns the column's sum of exp2(x - m)
+    __device__ __forceinline__ float finish() {
         const float L = col_sum(l);
         const float inv = L > 0.f ? 1.0f / L : 0.f;
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) o[dt] *= inv;
+        return L;
     }
 };
 
@@ -195,7 +197,12 @@ __global__ __launch_bounds__(256) void tile_kv_kernel(const u16* __restrict__ K,
 
 }  // namespace
 
-template <int DK, int DV>
+// STATS: the backward pass's statistics instead of the gated output.  Per (token, head)
+// and branch c: lse2_c = log2 of the branch's sum of exp2(scaled scores), D_c =
+// sigma_c <dO, o_c> and sigma_c (1 without gates); dgates = (1 - sigma_c) D_c, the gate
+// logit's gradient sigma (1 - sigma) <dO, o_c>.  The compressed branch takes its LSE and
+// o_cmp from the caller.
+template <int DK, int DV, bool STATS = false>
 __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnParams p) {
     constexpr int NDS = DK / 32;
     constexpr int NDT = DV / 16;
@@ -326,8 +333,51 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnParams p) {
     }
 
     if (!active) return;
-    win.finish();
-    slc.finish();
+    const float Lw = win.finish();
+    const float Ls = slc.finish();
+    if constexpr (STATS) {
+        const size_t row = ((size_t)b * T + t) * H + h;
+        float sg[3] = {1.f, 1.f, 1.f};
+        if (p.gates && head_ok) {
+#pragma unroll
+            for (int c = 0; c < 3; ++c) sg[c] = sigmoidf_(p.gates[row * 3 + c]);
+        }
+        float dc = 0.f, dsl = 0.f, dwn = 0.f;   // <dO, o_c> partial over this lane's dims
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+            const int d0 = 16 * dt + 4 * lq;
+            u32x2 raw = {0u, 0u};
+            f32x4 oc = zero4();
+            if (head_ok) {
+                raw = *reinterpret_cast<const u32x2*>(p.dO + row * DV + d0);
+                if (p.branches & 1) oc = *reinterpret_cast<const f32x4*>(p.o_cmp + row * DV + d0);
+            }
+            const float g4[4] = {bf2f((u16)(raw[0] & 0xFFFFu)), bf2f((u16)(raw[0] >> 16)),
+                                 bf2f((u16)(raw[1] & 0xFFFFu)), bf2f((u16)(raw[1] >> 16))};
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                dc += g4[r] * oc[r];
+                dsl += g4[r] * slc.o[dt][r];
+                dwn += g4[r] * win.o[dt][r];
+            }
+        }
+        dc = col_sum(dc);
+        dsl = col_sum(dsl);
+        dwn = col_sum(dwn);
+        if (head_ok && lq == 0) {
+            const bool on[3] = {(p.branches & 1) != 0, use_slc, use_win};
+            const float lse2[3] = {on[0] ? p.lse_cmp[row] * kLog2e : 0.f, use_slc ? slc.m + __log2f(Ls) : 0.f,
+                                   use_win ? win.m + __log2f(Lw) : 0.f};
+            const float dot[3] = {dc, dsl, dwn};
+            f32x4* so = reinterpret_cast<f32x4*>(p.stats + row * 12);
+#pragma unroll
+            for (int c = 0; c < 3; ++c) {
+                so[c] = f32x4{lse2[c], on[c] ? sg[c] * dot[c] : 0.f, sg[c], 0.f};
+                if (p.dgates) p.dgates[row * 3 + c] = on[c] ? sg[c] * (1.f - sg[c]) * dot[c] : 0.f;
+            }
+        }
+        return;
+    }
     if (!head_ok) return;
 
     float gc = 1.f, gs = 1.f, gw = 1.f;
@@ -356,6 +406,15 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnParams p) {
         const uint32_t w1 = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);
         st_stream(u32x2{w0, w1}, reinterpret_cast<u32x2*>(p.O + row * DV + d0));
     }
+}
+
+bool launch_sparse_attn_stats(int DK, int DV, const AttnParams& p, hipStream_t st) {
+    const int grid = xcd_grid(p.B * p.Hkv, (p.T + kTok - 1) / kTok);
+    if (DK == 192 && DV == 128) sparse_attn_kernel<192, 128, true><<<grid, 256, 0, st>>>(p);
+    else if (DK == 128 && DV == 128) sparse_attn_kernel<128, 128, true><<<grid, 256, 0, st>>>(p);
+    else if (DK == 64 && DV == 64) sparse_attn_kernel<64, 64, true><<<grid, 256, 0, st>>>(p);
+    else return false;
+    return true;
 }
 
 bool launch_tile_kv(int DK, int DV, const u16* K, const u16* V, u16* Kf, u16* Vf, int BG, int T, int Tpad,

@@ -126,6 +126,13 @@ def prefill_inputs(cfg: NSAConfig, seed: int | None = None) -> dict:
     return out
 
 
+def grad_output(cfg: NSAConfig, seed: int | None = None) -> np.ndarray:
+    """Upstream gradient dO of a prefill's output: bf16 bits [B,T,H,dv] ~ N(0,1), drawn from
+    its own stream (seed + 1000) so the forward inputs are unchanged."""
+    rng = np.random.Generator(np.random.PCG64((cfg.seed if seed is None else seed) + 1000))
+    return _normal_bf16(rng, (cfg.batch, cfg.seq_len, cfg.num_heads, cfg.d_v))
+
+
 def decode_inputs(cfg: NSAConfig, seed: int | None = None, cache_len: np.ndarray | None = None) -> dict:
     """Inputs of one decode step: ``q [B,H,dk]``, caches ``k [B,Hkv,L,dk]``, ``v [B,Hkv,L,dv]``,
     compression weights, ``gates [B,H,3]`` and ``cache_len [B]`` (default: all L)."""

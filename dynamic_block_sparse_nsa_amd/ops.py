@@ -18,7 +18,7 @@ from .configs import NSAConfig
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libnsa.so")
 
-OP_COMPRESS, OP_SCORE_SELECT, OP_SPARSE_ATTN, OP_DECODE, OP_FULL_ATTN = 0, 1, 2, 3, 4
+OP_COMPRESS, OP_SCORE_SELECT, OP_SPARSE_ATTN, OP_DECODE, OP_FULL_ATTN, OP_SPARSE_BWD, OP_COMPRESS_BWD = range(7)
 STATUS = {0: "ok", 1: "null", 2: "shape", 3: "unsupported", 4: "workspace", 5: "hip"}
 
 
@@ -68,6 +68,8 @@ def lib(build_if_missing: bool = True):
         L.nsa_full_attn_fwd.argtypes = [cp] + [_P] * 5 + [ctypes.c_size_t, _P]
         L.nsa_compress_prepare.argtypes = [cp] + [_P] * 5 + [ctypes.c_size_t, _P]
         L.nsa_cache_append.argtypes = [cp, _P, _P, ctypes.c_int32] + [_P] * 6 + [ctypes.c_size_t, _P]
+        L.nsa_sparse_attn_bwd.argtypes = [cp] + [_P] * 17 + [ctypes.c_size_t, _P]
+        L.nsa_compress_bwd.argtypes = [cp] + [_P] * 15 + [ctypes.c_size_t, _P]
         for f in ("nsa_workspace_size", "nsa_compress", "nsa_score_select", "nsa_select_from_scores",
                   "nsa_sparse_attn_fwd", "nsa_decode", "nsa_full_attn_fwd", "nsa_compress_prepare",
                   "nsa_cache_append"):
@@ -290,8 +292,85 @@ def cache_append(cfg: NSAConfig, K_new, V_new, K_cache, V_cache, cache_len, K_cm
 
 def prefill(cfg: NSAConfig, Q, K, V, w_k=None, w_v=None, pe_k=None, pe_v=None, gates=None, stream=None):
     """The whole prefill hot path: compress -> score_select -> sparse_attn_fwd.  Returns
-    dict(out, sel, o_cmp, k_cmp, v_cmp)."""
+    dict(out, sel, o_cmp, lse, k_cmp, v_cmp) (o_cmp and lse: compressed branch only)."""
     k_cmp, v_cmp = compress(cfg, K, V, w_k, w_v, pe_k, pe_v, stream=stream)
-    sel, _, o_cmp = score_select(cfg, Q, k_cmp, v_cmp, want_ocmp=bool(cfg.branches & 1), stream=stream)
+    use_c = bool(cfg.branches & 1)
+    sel, lse, o_cmp = score_select(cfg, Q, k_cmp, v_cmp, want_lse=use_c, want_ocmp=use_c, stream=stream)
     out = sparse_attn_fwd(cfg, Q, K, V, sel, o_cmp, gates, stream=stream)
-    return {"out": out, "sel": sel, "o_cmp": o_cmp, "k_cmp": k_cmp, "v_cmp": v_cmp}
+    return {"out": out, "sel": sel, "o_cmp": o_cmp, "lse": lse, "k_cmp": k_cmp, "v_cmp": v_cmp}
+
+
+# ---------------------------------------------------------------------------
+def sparse_attn_bwd(cfg: NSAConfig, Q, K, V, K_cmp, V_cmp, sel, lse_cmp, o_cmp, gates, dO, *, want_dgates=True,
+                    workspace=None, stream=None) -> dict:
+    """nsa_sparse_attn_bwd.  Returns dict(dq, dk, dv, dk_cmp, dv_cmp, dgates) of fp32 tensors
+    (dk_cmp/dv_cmp None without the compressed branch, dgates None without gates)."""
+    B, T, H, Hkv, N = cfg.batch, cfg.seq_len, cfg.num_heads, cfg.num_kv_heads, cfg.n_cmp
+    dk, dv = cfg.d_k, cfg.d_v
+    _need(Q, "Q", torch.bfloat16, (B, T, H, dk))
+    _need(K, "K", torch.bfloat16, (B, Hkv, T, dk))
+    _need(V, "V", torch.bfloat16, (B, Hkv, T, dv))
+    _need(dO, "dO", torch.bfloat16, (B, T, H, dv))
+    use_c = bool(cfg.branches & 1)
+    if use_c:
+        _need(K_cmp, "K_cmp", torch.bfloat16, (B, Hkv, N, dk))
+        _need(V_cmp, "V_cmp", torch.bfloat16, (B, Hkv, N, dv))
+        _need(lse_cmp, "lse_cmp", torch.float32, (B, T, H))
+        _need(o_cmp, "o_cmp", torch.float32, (B, T, H, dv))
+    if cfg.branches & 2:
+        _need(sel, "sel", torch.int32, (B, T, Hkv, cfg.top_n))
+    if gates is not None:
+        _need(gates, "gates", torch.float32, (B, T, H, 3))
+    dev = Q.device
+    f32 = dict(dtype=torch.float32, device=dev)
+    out = {"dq": torch.empty((B, T, H, dk), **f32), "dk": torch.empty((B, Hkv, T, dk), **f32),
+           "dv": torch.empty((B, Hkv, T, dv), **f32),
+           "dk_cmp": torch.empty((B, Hkv, N, dk), **f32) if use_c else None,
+           "dv_cmp": torch.empty((B, Hkv, N, dv), **f32) if use_c else None,
+           "dgates": torch.empty((B, T, H, 3), **f32) if (gates is not None and want_dgates) else None}
+    ws, nws = _workspace(cfg, OP_SPARSE_BWD, dev, workspace)
+    _check(lib().nsa_sparse_attn_bwd(
+        ctypes.byref(c_config(cfg)), _ptr(Q), _ptr(K), _ptr(V), _ptr(K_cmp if use_c else None),
+        _ptr(V_cmp if use_c else None), _ptr(sel if cfg.branches & 2 else None), _ptr(lse_cmp if use_c else None),
+        _ptr(o_cmp if use_c else None), _ptr(gates), _ptr(dO), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]),
+        _ptr(out["dk_cmp"]), _ptr(out["dv_cmp"]), _ptr(out["dgates"]), _ptr(ws), nws, _stream(stream)))
+    return out
+
+
+def compress_bwd(cfg: NSAConfig, K, V, w_k, w_v, pe_k, pe_v, dK_cmp, dV_cmp, dK, dV, *, workspace=None,
+                 stream=None) -> dict:
+    """nsa_compress_bwd: adds the block map's share into dK, dV (fp32, in place) and returns
+    dict(dw_k, dw_v, dpe_k, dpe_v) (fp32)."""
+    B, T, Hkv, N, l = cfg.batch, cfg.seq_len, cfg.num_kv_heads, cfg.n_cmp, cfg.cmp_block
+    dk, dv = cfg.d_k, cfg.d_v
+    _need(K, "K", torch.bfloat16, (B, Hkv, T, dk))
+    _need(V, "V", torch.bfloat16, (B, Hkv, T, dv))
+    _need(w_k, "w_k", torch.bfloat16, (l * dk, dk))
+    _need(w_v, "w_v", torch.bfloat16, (l * dv, dv))
+    _need(pe_k, "pe_k", torch.bfloat16, (l, dk))
+    _need(pe_v, "pe_v", torch.bfloat16, (l, dv))
+    _need(dK_cmp, "dK_cmp", torch.float32, (B, Hkv, N, dk))
+    _need(dV_cmp, "dV_cmp", torch.float32, (B, Hkv, N, dv))
+    _need(dK, "dK", torch.float32, (B, Hkv, T, dk))
+    _need(dV, "dV", torch.float32, (B, Hkv, T, dv))
+    f32 = dict(dtype=torch.float32, device=K.device)
+    out = {"dw_k": torch.empty((l * dk, dk), **f32), "dw_v": torch.empty((l * dv, dv), **f32),
+           "dpe_k": torch.empty((l, dk), **f32), "dpe_v": torch.empty((l, dv), **f32)}
+    ws, nws = _workspace(cfg, OP_COMPRESS_BWD, K.device, workspace)
+    _check(lib().nsa_compress_bwd(ctypes.byref(c_config(cfg)), _ptr(K), _ptr(V), _ptr(w_k), _ptr(w_v), _ptr(pe_k),
+                                  _ptr(pe_v), _ptr(dK_cmp), _ptr(dV_cmp), _ptr(dK), _ptr(dV), _ptr(out["dw_k"]),
+                                  _ptr(out["dw_v"]), _ptr(out["dpe_k"]), _ptr(out["dpe_v"]), _ptr(ws), nws,
+                                  _stream(stream)))
+    return out
+
+
+def backward(cfg: NSAConfig, fwd: dict, Q, K, V, w_k, w_v, pe_k, pe_v, gates, dO, stream=None) -> dict:
+    """The whole backward of ``prefill`` (its returned dict ``fwd`` plus an LSE of the
+    compressed branch in fwd["lse"]): nsa_sparse_attn_bwd then nsa_compress_bwd.  Returns
+    dict(dq, dk, dv, dgates, dk_cmp, dv_cmp, dw_k, dw_v, dpe_k, dpe_v)."""
+    g = sparse_attn_bwd(cfg, Q, K, V, fwd["k_cmp"], fwd["v_cmp"], fwd["sel"], fwd.get("lse"), fwd["o_cmp"], gates,
+                        dO, stream=stream)
+    if cfg.branches & 1:
+        g.update(compress_bwd(cfg, K, V, w_k, w_v, pe_k, pe_v, g["dk_cmp"], g["dv_cmp"], g["dk"], g["dv"],
+                              stream=stream))
+    return g

@@ -79,7 +79,7 @@ enum { NSA_BR_CMP = 1, NSA_BR_SLC = 2, NSA_BR_WIN = 4 };
 
 /* Work items for nsa_workspace_size. */
 enum { NSA_OP_COMPRESS = 0, NSA_OP_SCORE_SELECT = 1, NSA_OP_SPARSE_ATTN = 2, NSA_OP_DECODE = 3,
-       NSA_OP_FULL_ATTN = 4 };
+       NSA_OP_FULL_ATTN = 4, NSA_OP_SPARSE_BWD = 5, NSA_OP_COMPRESS_BWD = 6 };
 
 typedef struct nsa_config {
     uint32_t struct_size;      /* sizeof(nsa_config) */
@@ -202,6 +202,52 @@ nsa_status nsa_cache_append(const nsa_config* cfg, const void* K_new, const void
  * of two per (b, g) (workspace). */
 nsa_status nsa_full_attn_fwd(const nsa_config* cfg, const void* Q, const void* K, const void* V, void* O,
                              void* ws, size_t ws_bytes, void* stream);
+
+/* Backward of the three branches and the gated sum (zjai.club notes, section 4: the method
+ * is trained natively, forward and backward; section 14: the top-k choice has no derivative,
+ * so sel_idx is held fixed and the compressed branch's output carries the gradient into the
+ * compressed keys and values).  For the upstream gradient dO of O (the gated sum returned by
+ * nsa_sparse_attn_fwd for the same inputs), with sigma_c = sigmoid(gate logit c) (1 without
+ * gates) and, per branch, p = softmax(scale q.k) over that branch's keys and o_c its output:
+ *   dq += scale sum_k p_k (sigma_c <dO, v_k> - sigma_c <dO, o_c>) k_k   (the same factor times q
+ *   goes to dk_k), dv_k += sigma_c p_k dO, d_gate_c = sigma_c (1 - sigma_c) <dO, o_c>.
+ * Keys per branch are those of the forward: compressed blocks i with i*s + l - 1 <= t, tokens
+ * <= t of the listed blocks, tokens t-w+1 .. t.
+ * Inputs as for the forward (bf16 Q [B,T,H,d_k], K/V [B,H_kv,T,d], K_cmp/V_cmp [B,H_kv,N,d],
+ * sel_idx [B,T,H_kv,top_n], gate_logits [B,T,H,3] fp32 or NULL) plus lse_cmp [B,T,H] and o_cmp
+ * [B,T,H,d_v] fp32 as written by nsa_score_select, and dO bf16 [B,T,H,d_v].
+ * Outputs, fp32, overwritten: dQ [B,T,H,d_k], dK [B,H_kv,T,d_k], dV [B,H_kv,T,d_v], dK_cmp
+ * [B,H_kv,N,d_k], dV_cmp [B,H_kv,N,d_v] (compressed branch only, else unused and may be NULL),
+ * d_gate_logits [B,T,H,3] (may be NULL; zero for a disabled branch).  dK/dV hold the selected
+ * and window branches' share; nsa_compress_bwd adds the compressed branch's share through the
+ * block map.  Workspace: nsa_workspace_size(cfg, NSA_OP_SPARSE_BWD).  Q, K, V, dO, dQ, dK and
+ * dV must be 16-byte aligned.  Key-side gradients are summed with fp32 atomics, so their
+ * rounding depends on the order of the sums.  Errors: NSA_ERR_NULL for a missing required
+ * pointer; NSA_ERR_SHAPE / NSA_ERR_UNSUPPORTED as for the forward, or seq_len >= 2^26. */
+nsa_status nsa_sparse_attn_bwd(const nsa_config* cfg, const void* Q, const void* K, const void* V,
+                               const void* K_cmp, const void* V_cmp, const int32_t* sel_idx,
+                               const float* lse_cmp, const float* o_cmp, const float* gate_logits,
+                               const void* dO, float* dQ, float* dK, float* dV, float* dK_cmp,
+                               float* dV_cmp, float* d_gate_logits, void* ws, size_t ws_bytes,
+                               void* stream);
+
+/* Backward of the linear block map of nsa_compress (NSA_PHI_LINEAR; zjai.club notes,
+ * section 14: the loss reaches the block representations through the compressed branch).
+ * For the gradients dK_cmp, dV_cmp (fp32 [B,H_kv,N,d]) of its outputs:
+ *   dK[b,g,i*s+r,e] += sum_o W_k[r*d_k+e,o] dK_cmp[b,g,i,o]     (accumulated into dK; a token
+ *                                                                 in several blocks sums them)
+ *   dpe_k[r,e]       = sum_{b,g,i,o} W_k[r*d_k+e,o] dK_cmp[b,g,i,o]
+ *   dW_k[r*d_k+e,o]  = sum_{b,g,i} (K[b,g,i*s+r,e] + pe_k[r,e]) dK_cmp[b,g,i,o]
+ * and the same for V.  K, V, W_*, pe_* bf16 as for nsa_compress; dK, dV fp32 [B,H_kv,T,d]
+ * (accumulated); dW_k [l*d_k,d_k], dW_v [l*d_v,d_v], dpe_k [l,d_k], dpe_v [l,d_v] fp32,
+ * overwritten.  fp32 arithmetic, sums across blocks by fp32 atomics.  Workspace:
+ * nsa_workspace_size(cfg, NSA_OP_COMPRESS_BWD).  Errors: NSA_ERR_NULL for any missing
+ * pointer, NSA_ERR_UNSUPPORTED for NSA_PHI_MEAN. */
+nsa_status nsa_compress_bwd(const nsa_config* cfg, const void* K, const void* V, const void* W_k,
+                            const void* W_v, const void* pe_k, const void* pe_v,
+                            const float* dK_cmp, const float* dV_cmp, float* dK, float* dV,
+                            float* dW_k, float* dW_v, float* dpe_k, float* dpe_v, void* ws,
+                            size_t ws_bytes, void* stream);
 
 /* Static description of a status code. */
 const char* nsa_status_string(nsa_status status);

@@ -1,0 +1,156 @@
+"""GPU parity of the backward pass (nsa_sparse_attn_bwd, nsa_compress_bwd) against the fp64
+oracle (oracle.nsa_bwd, oracle.compress_linear_bwd), whose own pins are in
+test_oracle_bwd_pins.py.
+
+Staged like the forward: the oracle is fed the exact bf16 inputs, the GPU's compressed keys
+and values and the GPU's selection (the selection passes no gradient).  Gradients are fp32;
+the bar is the output bar applied to gradients scaled by their largest magnitude: max abs
+error <= 2e-2 * max|ref| and relative L2 error <= 5e-3.  Expected error: the compressed
+branch's o_cmp enters D_cmp = sigma <dO, o_cmp> with its forward rounding (fp16
+probabilities against an fp16 value copy, 2^-11 relative), probabilities and dS enter the
+MFMA as bf16 high + low parts (about 2^-17), everything else is fp32 accumulation, so the
+expected relative error is about 1e-3 at worst, well inside the bar.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from dynamic_block_sparse_nsa_amd import inputs, ops
+from dynamic_block_sparse_nsa_amd.configs import TINY, BR_ALL, BR_CMP, BR_SLC, BR_WIN, PHI_MEAN, SCORE_MEAN_DOT
+from nsa_testlib import bf16_dev_to_f64, check_close, dev_bf16, OUT_ATOL, OUT_REL_L2
+
+pytestmark = pytest.mark.gpu
+
+f64 = inputs.bf16_bits_to_f64
+
+
+def check_grad(gpu, ref, what):
+    ref = np.asarray(ref, dtype=np.float64)
+    scale = max(float(np.abs(ref).max()), 1e-30)
+    check_close(np.asarray(gpu, dtype=np.float64) / scale, ref / scale, what, atol=OUT_ATOL, rel=OUT_REL_L2)
+
+
+GQA = TINY.replace(name="bwd_gqa16", num_kv_heads=2, heads_per_group=16, d_k=192, d_v=128, top_n=8, window=256,
+                   fp32_inputs=False, seed=41)
+RAGGED = TINY.replace(name="bwd_ragged", seq_len=1000, num_kv_heads=2, heads_per_group=8, d_k=128, d_v=128, top_n=6,
+                      window=200, fp32_inputs=False, seed=42)
+LP128 = TINY.replace(name="bwd_lp128", seq_len=1536, num_kv_heads=1, heads_per_group=16, d_k=64, d_v=64,
+                     slc_block=128, top_n=5, window=96, fp32_inputs=False, seed=43)
+LP32 = TINY.replace(name="bwd_lp32", seq_len=700, num_kv_heads=1, heads_per_group=2, d_k=64, d_v=64, slc_block=32,
+                    cmp_block=16, cmp_stride=8, top_n=7, n_init=2, n_local=2, window=64, fp32_inputs=False, seed=44)
+CASES = [
+    (TINY.replace(fp32_inputs=False, seed=40), True),
+    (GQA, True),
+    (RAGGED, True),
+    (LP128, True),
+    (LP32, False),
+    (GQA.replace(name="bwd_slc_only", branches=BR_SLC), False),
+    (GQA.replace(name="bwd_cmp_only", branches=BR_CMP), True),
+    (RAGGED.replace(name="bwd_win_only", branches=BR_WIN), True),
+]
+
+
+def _run(cfg, with_gates):
+    print(f"[case] backward {cfg.name} T={cfg.seq_len} Hkv={cfg.num_kv_heads} G={cfg.heads_per_group} "
+          f"d={cfg.d_k}/{cfg.d_v} br={cfg.branches} gates={with_gates}", flush=True)
+    inp = inputs.prefill_inputs(cfg)
+    dO_bits = inputs.grad_output(cfg)
+    q, k, v = dev_bf16(inp["q"]), dev_bf16(inp["k"]), dev_bf16(inp["v"])
+    wk, wv, pk, pv = ((dev_bf16(inp[n]) if cfg.phi == 0 else None) for n in ("w_k", "w_v", "pe_k", "pe_v"))
+    gates = torch.as_tensor(inp["gates"], device="cuda") if with_gates else None
+    dO = dev_bf16(dO_bits)
+    fwd = ops.prefill(cfg, q, k, v, wk, wv, pk, pv, gates)
+    g = ops.backward(cfg, fwd, q, k, v, wk, wv, pk, pv, gates, dO)
+    torch.cuda.synchronize()
+    return inp, dO_bits, fwd, g
+
+
+@pytest.mark.parametrize("cfg,with_gates", CASES, ids=[c.name + ("_g" if wg else "") for c, wg in CASES])
+def test_backward_matches_oracle(cfg, with_gates):
+    inp, dO_bits, fwd, g = _run(cfg, with_gates)
+    use_c = bool(cfg.branches & 1)
+    b = 0
+    kc = bf16_dev_to_f64(fwd["k_cmp"][b]) if use_c else None
+    vc = bf16_dev_to_f64(fwd["v_cmp"][b]) if use_c else None
+    sel = fwd["sel"][b].cpu().numpy()
+    gates = inp["gates"][b].astype(np.float64) if with_gates else None
+    ref = oracle.nsa_bwd(cfg, f64(inp["q"][b]), f64(inp["k"][b]), f64(inp["v"][b]), kc, vc, sel, gates,
+                         f64(dO_bits[b]))
+    name = cfg.name
+    check_grad(g["dq"][b].cpu().numpy(), ref["dq"], f"{name} dQ")
+    if with_gates:
+        check_grad(g["dgates"][b].cpu().numpy(), ref["dgates"], f"{name} dgates")
+    if use_c:
+        check_grad(g["dk_cmp"][b].cpu().numpy(), ref["dkc"], f"{name} dK_cmp")
+        check_grad(g["dv_cmp"][b].cpu().numpy(), ref["dvc"], f"{name} dV_cmp")
+        # the block map's backward on the oracle's dK_cmp / dV_cmp (staged through the GPU's)
+        dk_tot, dv_tot = ref["dk"].copy(), ref["dv"].copy()
+        dwk = np.zeros(inp["w_k"].shape)
+        dwv = np.zeros(inp["w_v"].shape)
+        dpk = np.zeros(inp["pe_k"].shape)
+        dpv = np.zeros(inp["pe_v"].shape)
+        gk = g["dk_cmp"][b].cpu().numpy().astype(np.float64)
+        gv = g["dv_cmp"][b].cpu().numpy().astype(np.float64)
+        for h in range(cfg.num_kv_heads):
+            rk = oracle.compress_linear_bwd(f64(inp["k"][b, h]), f64(inp["pe_k"]), f64(inp["w_k"]), gk[h],
+                                            cfg.cmp_block, cfg.cmp_stride)
+            rv = oracle.compress_linear_bwd(f64(inp["v"][b, h]), f64(inp["pe_v"]), f64(inp["w_v"]), gv[h],
+                                            cfg.cmp_block, cfg.cmp_stride)
+            dk_tot[h] += rk["dx"]
+            dv_tot[h] += rv["dx"]
+            dwk += rk["dw"]
+            dwv += rv["dw"]
+            dpk += rk["dpe"]
+            dpv += rv["dpe"]
+        check_grad(g["dk"][b].cpu().numpy(), dk_tot, f"{name} dK (all branches)")
+        check_grad(g["dv"][b].cpu().numpy(), dv_tot, f"{name} dV (all branches)")
+        check_grad(g["dw_k"].cpu().numpy(), dwk, f"{name} dW_k")
+        check_grad(g["dw_v"].cpu().numpy(), dwv, f"{name} dW_v")
+        check_grad(g["dpe_k"].cpu().numpy(), dpk, f"{name} dpe_k")
+        check_grad(g["dpe_v"].cpu().numpy(), dpv, f"{name} dpe_v")
+    else:
+        check_grad(g["dk"][b].cpu().numpy(), ref["dk"], f"{name} dK")
+        check_grad(g["dv"][b].cpu().numpy(), ref["dv"], f"{name} dV")
+
+
+def test_backward_batch_two():
+    """Two sequences: every gradient of the second batch element against the oracle."""
+    cfg = RAGGED.replace(name="bwd_batch2", batch=2, seed=45)
+    inp, dO_bits, fwd, g = _run(cfg, True)
+    for b in range(2):
+        ref = oracle.nsa_bwd(cfg, f64(inp["q"][b]), f64(inp["k"][b]), f64(inp["v"][b]),
+                             bf16_dev_to_f64(fwd["k_cmp"][b]), bf16_dev_to_f64(fwd["v_cmp"][b]),
+                             fwd["sel"][b].cpu().numpy(), inp["gates"][b].astype(np.float64), f64(dO_bits[b]))
+        check_grad(g["dq"][b].cpu().numpy(), ref["dq"], f"batch {b} dQ")
+        check_grad(g["dk_cmp"][b].cpu().numpy(), ref["dkc"], f"batch {b} dK_cmp")
+        check_grad(g["dgates"][b].cpu().numpy(), ref["dgates"], f"batch {b} dgates")
+
+
+def test_backward_moba_mode():
+    """MoBA mode (mean-pooled block keys, G = 1, selected branch only): the selected-branch
+    backward on its own block lists."""
+    cfg = TINY.replace(name="bwd_moba", seq_len=2048, num_kv_heads=2, heads_per_group=1, d_k=128, d_v=128,
+                       cmp_block=128, cmp_stride=128, slc_block=128, top_n=3, n_init=0, n_local=1, window=0,
+                       phi=PHI_MEAN, score_mode=SCORE_MEAN_DOT, branches=BR_SLC, fp32_inputs=False, seed=46)
+    inp, dO_bits, fwd, g = _run(cfg, False)
+    ref = oracle.nsa_bwd(cfg, f64(inp["q"][0]), f64(inp["k"][0]), f64(inp["v"][0]), None, None,
+                         fwd["sel"][0].cpu().numpy(), None, f64(dO_bits[0]))
+    for k, r in (("dq", "dq"), ("dk", "dk"), ("dv", "dv")):
+        check_grad(g[k][0].cpu().numpy(), ref[r], f"moba {k}")
+
+
+def test_backward_repeatable_shapes():
+    """Two calls in a row give the same dQ bit for bit (dQ has no atomics) and dK within
+    the atomics' reordering."""
+    cfg = GQA.replace(name="bwd_repeat", seed=47)
+    inp, dO_bits, fwd, g1 = _run(cfg, True)
+    q, k, v = dev_bf16(inp["q"]), dev_bf16(inp["k"]), dev_bf16(inp["v"])
+    wk, wv, pk, pv = (dev_bf16(inp[n]) for n in ("w_k", "w_v", "pe_k", "pe_v"))
+    g2 = ops.backward(cfg, fwd, q, k, v, wk, wv, pk, pv, torch.as_tensor(inp["gates"], device="cuda"),
+                      dev_bf16(dO_bits))
+    torch.cuda.synchronize()
+    assert torch.equal(g1["dq"], g2["dq"])
+    assert torch.equal(g1["dgates"], g2["dgates"])
+    d = (g1["dk"] - g2["dk"]).abs().max().item()
+    assert d <= 1e-5 * max(g1["dk"].abs().max().item(), 1.0)
