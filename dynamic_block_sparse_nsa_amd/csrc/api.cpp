@@ -650,19 +650,21 @@ nsa_status nsa_sparse_attn_bwd(const nsa_config* cfg, const void* Q, const void*
         p.tile_start = m.tile_start;
         p.entries = m.entries;
         p.n_bucket = w.n_bucket;
-        p.nsb = (s.lp + 63) / 64;
+        p.nsb = (s.lp + 16 * nsa::kDkvWavesSlc - 1) / (16 * nsa::kDkvWavesSlc);
         n_slc_items = (long long)nsa::moba_max_tiles((int)bg, s.T, s.n, s.n_slc) * p.nsb;
     }
     // 4. dK, dV, dK_cmp, dV_cmp
-    p.n_qt = (s.T + nsa::kBwdTile - 1) / nsa::kBwdTile;
-    p.n_kb_cmp = cmp ? (s.n_cmp + 63) / 64 : 0;
+    const int dense_keys = 16 * nsa::kDkvWavesDense;
+    p.qt_cmp = nsa::kBwdCmpTile;
+    p.n_qt = (s.T + p.qt_cmp - 1) / p.qt_cmp;
+    p.n_kb_cmp = cmp ? (s.n_cmp + dense_keys - 1) / dense_keys : 0;
+    p.n_kb_win = (s.br & NSA_BR_WIN) ? (s.T + dense_keys - 1) / dense_keys : 0;
+    p.n_qt_win = (dense_keys + s.w - 1 + nsa::kBwdTile - 1) / nsa::kBwdTile;
+    const long long n_dense = (long long)bg * p.n_kb_cmp * p.n_qt + (long long)bg * p.n_kb_win * p.n_qt_win;
+    if (n_dense + n_slc_items >= (1LL << 31)) return fail(NSA_ERR_SHAPE, "problem too large");
     p.n_cmp_items = (int)(bg * p.n_kb_cmp * p.n_qt);
-    p.n_kb_win = (s.br & NSA_BR_WIN) ? (s.T + 63) / 64 : 0;
-    p.n_qt_win = (64 + s.w - 1 + nsa::kBwdTile - 1) / nsa::kBwdTile;
     p.n_win_items = (int)(bg * p.n_kb_win * p.n_qt_win);
-    const long long n_items = (long long)p.n_cmp_items + p.n_win_items + n_slc_items;
-    if (n_items >= (1LL << 31)) return fail(NSA_ERR_SHAPE, "problem too large");
-    if (!nsa::launch_bwd_dkv(s.dk, s.dv, p, (int)n_items, hs)) return fail(NSA_ERR_UNSUPPORTED, "no dK/dV kernel");
+    if (!nsa::launch_bwd_dkv(s.dk, s.dv, p, (int)n_slc_items, hs)) return fail(NSA_ERR_UNSUPPORTED, "no dK/dV kernel");
     return hip_check("sparse_attn_bwd");
 }
 

@@ -55,17 +55,63 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(float* __restrict__ x, s
 }
 
 // ---------------------------------------------------------------------------
+// dQ.  A workgroup owns kDqTok consecutive tokens of one (sequence, group), a wave per token.
+// The compressed keys and the window range are shared by the tokens: their 32-key chunks go
+// through one LDS tile (the next chunk's loads in flight in registers while the current one
+// is computed).  The selected blocks differ per token: each wave stages its own chunks.
+constexpr int kDqTok = 4;
+
 template <int DK, int DV>
-__global__ __launch_bounds__(64) void bwd_dq_kernel(BwdParams p) {
+struct DqChunk {   // one 32-key chunk of K and V rows, staged by the whole workgroup
+    static constexpr int NK = DK / 64, NV = DV / 64;   // 16-byte pieces per thread
+    u32x4 rk[NK], rv[NV];
+    __device__ __forceinline__ void load(const u16* Kb, const u16* Vb, int nrows, int key0) {
+#pragma unroll
+        for (int i = 0; i < NK; ++i) {
+            const int idx = threadIdx.x + 256 * i, r = idx / (DK / 8), col = (idx % (DK / 8)) * 8;
+            rk[i] = key0 + r < nrows ? *reinterpret_cast<const u32x4*>(Kb + (size_t)(key0 + r) * DK + col)
+                                     : u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const int idx = threadIdx.x + 256 * i, r = idx / (DV / 8), col = (idx % (DV / 8)) * 8;
+            rv[i] = key0 + r < nrows ? *reinterpret_cast<const u32x4*>(Vb + (size_t)(key0 + r) * DV + col)
+                                     : u32x4{0u, 0u, 0u, 0u};
+        }
+    }
+    __device__ __forceinline__ void store(u16* sk, int kstr, u16* sv, int vstr) const {
+#pragma unroll
+        for (int i = 0; i < NK; ++i) {
+            const int idx = threadIdx.x + 256 * i, r = idx / (DK / 8), col = (idx % (DK / 8)) * 8;
+            *reinterpret_cast<u32x4*>(&sk[r * kstr + col]) = rk[i];
+        }
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const int idx = threadIdx.x + 256 * i, r = idx / (DV / 8), col = (idx % (DV / 8)) * 8;
+            *reinterpret_cast<u32x4*>(&sv[r * vstr + col]) = rv[i];
+        }
+    }
+};
+
+// orders this wave's LDS writes before its later reads (no other wave shares the region)
+__device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+template <int DK, int DV>
+__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p) {
     constexpr int NDS = DK / 32, NDD = DV / 32, NDK = DK / 16;
-    constexpr int KSTR = DK + 16;   // 8-byte aligned rows for the transposing read
-    __shared__ __attribute__((aligned(16))) u16 kt[32 * KSTR];
-    const int lane = threadIdx.x, li = lane & 15, lq = lane >> 4;
-    const int t = blockIdx.x, bg = blockIdx.y;
+    constexpr int KSTR = DK + 16, VSTR = DV + 16;   // 8-byte aligned rows for the transposing read
+    __shared__ __attribute__((aligned(16))) u16 sk[32 * KSTR];
+    __shared__ __attribute__((aligned(16))) u16 sv[32 * VSTR];
+    __shared__ __attribute__((aligned(16))) u16 wk[kDqTok][32 * KSTR];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, li = lane & 15, lq = lane >> 4;
+    int bg, it;
+    if (!xcd_map_tile(blockIdx.x, p.B * p.Hkv, (p.T + kDqTok - 1) / kDqTok, bg, it)) return;
     const int b = bg / p.Hkv, g = bg % p.Hkv;
+    const int t0 = it * kDqTok, t = t0 + wave, tlast = min(t0 + kDqTok, p.T) - 1;
+    const bool active = t < p.T;
     const int G = p.G, H = p.Hkv * G;
-    const bool head_ok = li < G;
-    const size_t row = ((size_t)b * p.T + t) * H + g * G + min(li, G - 1);
+    const bool head_ok = li < G && active;
+    const size_t row = ((size_t)b * p.T + min(t, p.T - 1)) * H + g * G + min(li, G - 1);
 
     bf16x8 qf[NDS], df[NDD];
 #pragma unroll
@@ -76,25 +122,9 @@ __global__ __launch_bounds__(64) void bwd_dq_kernel(BwdParams p) {
 #pragma unroll
     for (int dt = 0; dt < NDK; ++dt) acc[dt] = zero4();
 
-    // keys key0 .. key0+31 of Kb/Vb (rows >= nrows read as zero); keys outside [lo, hi] masked
-    auto chunk = [&](const u16* Kb, const u16* Vb, int nrows, int key0, int lo, int hi, const f32x4& st) {
-        __syncthreads();   // the previous chunk's LDS reads are complete
-        for (int i = lane; i < 32 * (DK / 8); i += 64) {
-            const int r = i / (DK / 8), col = (i % (DK / 8)) * 8;
-            const int key = key0 + r;
-            u32x4 v = {0u, 0u, 0u, 0u};
-            if (key < nrows) v = *reinterpret_cast<const u32x4*>(Kb + (size_t)key * DK + col);
-            *reinterpret_cast<u32x4*>(&kt[r * KSTR + col]) = v;
-        }
-        bf16x8 va[2][NDD];
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-            const int key = key0 + 16 * tt + li;
-#pragma unroll
-            for (int dd = 0; dd < NDD; ++dd)
-                va[tt][dd] = key < nrows ? ld8(Vb + (size_t)key * DV + 32 * dd + 8 * lq) : zero8();
-        }
-        __syncthreads();
+    // dQ^T += K^T.dS^T for the 32 keys at key0 of the row-major tile kt (stride KSTR), values
+    // va (A operands of V.dO^T); keys outside [lo, hi] masked
+    auto math = [&](const u16* kt, const bf16x8 (&va)[2][NDD], int key0, int lo, int hi, const f32x4& st) {
         f32x4 s0 = zero4(), s1 = zero4(), d0 = zero4(), d1 = zero4();
 #pragma unroll
         for (int ds = 0; ds < NDS; ++ds) {
@@ -126,29 +156,76 @@ __global__ __launch_bounds__(64) void bwd_dq_kernel(BwdParams p) {
         }
     };
 
+    // keys kfirst .. klast of Kb/Vb shared by the workgroup's tokens; this wave's token
+    // attends [lo, hi]
+    auto shared_range = [&](const u16* Kb, const u16* Vb, int nrows, int kfirst, int klast, int lo, int hi,
+                            const f32x4& st) {
+        if (klast < kfirst) return;   // uniform over the workgroup
+        const int c0 = kfirst & ~31, nch = (klast - c0) / 32 + 1;
+        DqChunk<DK, DV> ch;
+        ch.load(Kb, Vb, nrows, c0);
+        __syncthreads();   // the previous range's LDS reads are complete
+        ch.store(sk, KSTR, sv, VSTR);
+        __syncthreads();
+        for (int i = 0; i < nch; ++i) {
+            const int key0 = c0 + 32 * i;
+            ch.load(Kb, Vb, nrows, c0 + 32 * min(i + 1, nch - 1));   // the last chunk reloads itself
+            // wave-uniform condition: the MFMA reads every lane's operands, so no lane may
+            // skip the loads (heads past G are masked inside math)
+            if (active && key0 + 31 >= lo && key0 <= hi) {
+                bf16x8 va[2][NDD];
+#pragma unroll
+                for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                    for (int dd = 0; dd < NDD; ++dd) va[tt][dd] = ld8(&sv[(16 * tt + li) * VSTR + 32 * dd + 8 * lq]);
+                math(sk, va, key0, lo, hi, st);
+            }
+            __syncthreads();
+            ch.store(sk, KSTR, sv, VSTR);
+            __syncthreads();
+        }
+    };
+
     if (p.branches & 1) {
         const f32x4 st = *reinterpret_cast<const f32x4*>(p.stats + row * 12);
-        const int nc = t < p.l - 1 ? 0 : min((t - p.l + 1) / p.s + 1, p.N);
-        const u16* Kb = p.Kc + (size_t)bg * p.N * DK;
-        const u16* Vb = p.Vc + (size_t)bg * p.N * DV;
-        for (int key0 = 0; key0 < nc; key0 += 32) chunk(Kb, Vb, p.N, key0, 0, nc - 1, st);
+        auto ncmp = [&](int tt) { return tt < p.l - 1 ? 0 : min((tt - p.l + 1) / p.s + 1, p.N); };
+        shared_range(p.Kc + (size_t)bg * p.N * DK, p.Vc + (size_t)bg * p.N * DV, p.N, 0, ncmp(tlast) - 1, 0,
+                     ncmp(t) - 1, st);
     }
     const u16* Kb = p.K + (size_t)bg * p.T * DK;
     const u16* Vb = p.V + (size_t)bg * p.T * DV;
-    if (p.branches & 2) {
+    if (p.branches & 4) {
+        const f32x4 st = *reinterpret_cast<const f32x4*>(p.stats + row * 12 + 8);
+        shared_range(Kb, Vb, p.T, max(0, t0 - p.window + 1), tlast, max(0, t - p.window + 1), t, st);
+    }
+    if ((p.branches & 2) && active) {   // per wave from here on: no workgroup barrier
         const f32x4 st = *reinterpret_cast<const f32x4*>(p.stats + row * 12 + 4);
         const int32_t* sl = p.sel + (((size_t)b * p.T + t) * p.Hkv + g) * p.top_n;
+        u16* kt = wk[wave];
         for (int c = 0; c < p.top_n; ++c) {
             const int j = sl[c];
             if (j < 0 || j * p.lp > t) continue;
             const int lo = j * p.lp, hi = min(t, lo + p.lp - 1);
-            for (int key0 = lo; key0 <= hi; key0 += 32) chunk(Kb, Vb, p.T, key0, lo, hi, st);
+            for (int key0 = lo; key0 <= hi; key0 += 32) {
+                wave_lds_sync();   // the previous chunk's reads are complete
+                for (int i = lane; i < 32 * (DK / 8); i += 64) {
+                    const int r = i / (DK / 8), col = (i % (DK / 8)) * 8;
+                    *reinterpret_cast<u32x4*>(&kt[r * KSTR + col]) =
+                        key0 + r < p.T ? *reinterpret_cast<const u32x4*>(Kb + (size_t)(key0 + r) * DK + col)
+                                       : u32x4{0u, 0u, 0u, 0u};
+                }
+                bf16x8 va[2][NDD];
+#pragma unroll
+                for (int tt = 0; tt < 2; ++tt) {
+                    const int key = key0 + 16 * tt + li;
+#pragma unroll
+                    for (int dd = 0; dd < NDD; ++dd)
+                        va[tt][dd] = key < p.T ? ld8(Vb + (size_t)key * DV + 32 * dd + 8 * lq) : zero8();
+                }
+                wave_lds_sync();
+                math(kt, va, key0, lo, hi, st);
+            }
         }
-    }
-    if (p.branches & 4) {
-        const f32x4 st = *reinterpret_cast<const f32x4*>(p.stats + row * 12 + 8);
-        const int wlo = max(0, t - p.window + 1);
-        for (int key0 = wlo & ~31; key0 <= t; key0 += 32) chunk(Kb, Vb, p.T, key0, wlo, t, st);
     }
     if (!head_ok) return;
     // dQ^T C layout: rows d = 16 dt + 4 lq + r of head li
@@ -158,30 +235,77 @@ __global__ __launch_bounds__(64) void bwd_dq_kernel(BwdParams p) {
 }
 
 // ---------------------------------------------------------------------------
-template <int DK, int DV>
-__global__ __launch_bounds__(256) void bwd_dkv_kernel(BwdParams p) {
+// dK, dV.  NW waves, 16 keys each; the item's query tokens two at a time.
+template <int DK, int DV, int NW>
+struct PairStage {   // Q and dO rows of two tokens (32 head rows) and their statistics
+    static constexpr int NT = 64 * NW;
+    static constexpr int NQ = (32 * DK / 8 + NT - 1) / NT, NO = (32 * DV / 8 + NT - 1) / NT;
+    u32x4 rq[NQ], ro[NO];
+    f32x4 rst;
+    __device__ __forceinline__ void load(const BwdParams& p, int b, int g, int kind, int tA, int tB) {
+        const int G = p.G, H = p.Hkv * G;
+#pragma unroll
+        for (int i = 0; i < NQ; ++i) {
+            const int idx = threadIdx.x + NT * i, r = idx / (DK / 8), col = (idx % (DK / 8)) * 8;
+            const int tk = r < 16 ? tA : tB, hh = r & 15;
+            rq[i] = (idx < 32 * DK / 8 && tk >= 0 && hh < G)
+                        ? *reinterpret_cast<const u32x4*>(p.Q + (((size_t)b * p.T + tk) * H + g * G + hh) * DK + col)
+                        : u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int i = 0; i < NO; ++i) {
+            const int idx = threadIdx.x + NT * i, r = idx / (DV / 8), col = (idx % (DV / 8)) * 8;
+            const int tk = r < 16 ? tA : tB, hh = r & 15;
+            ro[i] = (idx < 32 * DV / 8 && tk >= 0 && hh < G)
+                        ? *reinterpret_cast<const u32x4*>(p.dO + (((size_t)b * p.T + tk) * H + g * G + hh) * DV + col)
+                        : u32x4{0u, 0u, 0u, 0u};
+        }
+        rst = zero4();
+        if (threadIdx.x < 32) {
+            const int r = threadIdx.x, tk = r < 16 ? tA : tB, hh = r & 15;
+            if (tk >= 0 && hh < G)
+                rst = *reinterpret_cast<const f32x4*>(p.stats +
+                                                      ((((size_t)b * p.T + tk) * H + g * G + hh) * 3 + kind) * 4);
+        }
+    }
+    __device__ __forceinline__ void store(u16* qs, int qstr, u16* os, int ostr, float* rs) const {
+#pragma unroll
+        for (int i = 0; i < NQ; ++i) {
+            const int idx = threadIdx.x + NT * i, r = idx / (DK / 8), col = (idx % (DK / 8)) * 8;
+            if (idx < 32 * DK / 8) *reinterpret_cast<u32x4*>(&qs[r * qstr + col]) = rq[i];
+        }
+#pragma unroll
+        for (int i = 0; i < NO; ++i) {
+            const int idx = threadIdx.x + NT * i, r = idx / (DV / 8), col = (idx % (DV / 8)) * 8;
+            if (idx < 32 * DV / 8) *reinterpret_cast<u32x4*>(&os[r * ostr + col]) = ro[i];
+        }
+        if (threadIdx.x < 32) *reinterpret_cast<f32x4*>(&rs[threadIdx.x * 4]) = rst;
+    }
+};
+
+template <int DK, int DV, int NW>
+__global__ __launch_bounds__(64 * NW, 8 / NW) void bwd_dkv_kernel(BwdParams p, int item0) {
     constexpr int NDS = DK / 32, NDD = DV / 32, NDK = DK / 16, NDV = DV / 16;
     constexpr int QSTR = DK + 16, OSTR = DV + 16;
+    constexpr int KEYS = 16 * NW;
     __shared__ __attribute__((aligned(16))) u16 qs[32 * QSTR];   // rows: token A heads, token B heads
     __shared__ __attribute__((aligned(16))) u16 os[32 * OSTR];
     __shared__ __attribute__((aligned(16))) float rs[32 * 4];   // lse2, D, sigma per row
     __shared__ int toks[kBwdTile];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, li = lane & 15, lq = lane >> 4;
-    const int G = p.G, H = p.Hkv * G;
 
     // ---- work item: kind (0 compressed, 1 selected, 2 window), group, keys, query tokens ----
-    int kind, bg, kbase, kend, nq;
-    int x = blockIdx.x;
-    int t0 = 0, e0 = 0;
+    int kind, bg, kbase, kend, nq, t0 = 0;
+    int x = blockIdx.x + item0;
     if (x < p.n_cmp_items) {
         kind = 0;
         const int per_bg = p.n_kb_cmp * p.n_qt;
         bg = x / per_bg;
         const int r = x % per_bg, kb = r / p.n_qt, qt = r % p.n_qt;
-        kbase = kb * kItemKeys;
-        kend = min(kbase + kItemKeys, p.N);
-        t0 = max(qt * kBwdTile, kbase * p.s + p.l - 1);   // first token that sees key kbase
-        const int t1 = min((qt + 1) * kBwdTile, p.T);
+        kbase = kb * KEYS;
+        kend = min(kbase + KEYS, p.N);
+        t0 = max(qt * p.qt_cmp, kbase * p.s + p.l - 1);   // first token that sees key kbase
+        const int t1 = min((qt + 1) * p.qt_cmp, p.T);
         if (t0 >= t1) return;
         nq = t1 - t0;
     } else if ((x -= p.n_cmp_items) < p.n_win_items) {
@@ -189,10 +313,10 @@ __global__ __launch_bounds__(256) void bwd_dkv_kernel(BwdParams p) {
         const int per_bg = p.n_kb_win * p.n_qt_win;
         bg = x / per_bg;
         const int r = x % per_bg, kb = r / p.n_qt_win, qt = r % p.n_qt_win;
-        kbase = kb * kItemKeys;
-        kend = min(kbase + kItemKeys, p.T);
+        kbase = kb * KEYS;
+        kend = min(kbase + KEYS, p.T);
         t0 = kbase + qt * kBwdTile;
-        const int t1 = min(min(t0 + kBwdTile, kbase + kItemKeys + p.window - 1), p.T);
+        const int t1 = min(min(t0 + kBwdTile, kbase + KEYS + p.window - 1), p.T);
         if (t0 >= t1) return;
         nq = t1 - t0;
     } else {
@@ -209,15 +333,17 @@ __global__ __launch_bounds__(256) void bwd_dkv_kernel(BwdParams p) {
         }
         bg = lo / p.n_slc;
         const int j = lo % p.n_slc;
-        kbase = j * p.lp + kItemKeys * sub;
+        kbase = j * p.lp + KEYS * sub;
         kend = min(j * p.lp + p.lp, p.T);
         if (kbase >= kend) return;
-        e0 = p.bucket_start[lo] + (x - p.tile_start[lo]) * kBwdTile;
+        const int e0 = p.bucket_start[lo] + (x - p.tile_start[lo]) * kBwdTile;
         nq = min(kBwdTile, p.bucket_start[lo + 1] - e0);
+        for (int i = threadIdx.x; i < kBwdTile; i += 64 * NW) toks[i] = i < nq ? (p.entries[e0 + i] >> 5) : -1;
     }
-    for (int i = threadIdx.x; i < kBwdTile; i += 256)
-        toks[i] = i >= nq ? -1 : kind == 1 ? (p.entries[e0 + i] >> 5) : t0 + i;
+    __syncthreads();
+    auto tok = [&](int i) { return i >= nq ? -1 : kind == 1 ? toks[i] : t0 + i; };
     const int b = bg / p.Hkv, g = bg % p.Hkv;
+    const int G = p.G;
     const int nrows = kind == 0 ? p.N : p.T;
     const u16* Kb = kind == 0 ? p.Kc + (size_t)bg * p.N * DK : p.K + (size_t)bg * p.T * DK;
     const u16* Vb = kind == 0 ? p.Vc + (size_t)bg * p.N * DV : p.V + (size_t)bg * p.T * DV;
@@ -236,33 +362,14 @@ __global__ __launch_bounds__(256) void bwd_dkv_kernel(BwdParams p) {
 #pragma unroll
     for (int dt = 0; dt < NDV; ++dt) dv_acc[dt] = zero4();
 
+    PairStage<DK, DV, NW> stage;
+    stage.load(p, b, g, kind, tok(0), tok(1));
     for (int i = 0; i < nq; i += 2) {
-        __syncthreads();   // token list written / the previous pair's LDS reads complete
-        const int tA = toks[i], tB = i + 1 < nq ? toks[i + 1] : -1;
-        for (int idx = threadIdx.x; idx < 32 * (DK / 8); idx += 256) {
-            const int r = idx / (DK / 8), col = (idx % (DK / 8)) * 8;
-            const int tk = r < 16 ? tA : tB, hh = r & 15;
-            u32x4 v = {0u, 0u, 0u, 0u};
-            if (tk >= 0 && hh < G)
-                v = *reinterpret_cast<const u32x4*>(p.Q + (((size_t)b * p.T + tk) * H + g * G + hh) * DK + col);
-            *reinterpret_cast<u32x4*>(&qs[r * QSTR + col]) = v;
-        }
-        for (int idx = threadIdx.x; idx < 32 * (DV / 8); idx += 256) {
-            const int r = idx / (DV / 8), col = (idx % (DV / 8)) * 8;
-            const int tk = r < 16 ? tA : tB, hh = r & 15;
-            u32x4 v = {0u, 0u, 0u, 0u};
-            if (tk >= 0 && hh < G)
-                v = *reinterpret_cast<const u32x4*>(p.dO + (((size_t)b * p.T + tk) * H + g * G + hh) * DV + col);
-            *reinterpret_cast<u32x4*>(&os[r * OSTR + col]) = v;
-        }
-        if (threadIdx.x < 32) {
-            const int r = threadIdx.x, tk = r < 16 ? tA : tB, hh = r & 15;
-            f32x4 st = zero4();
-            if (tk >= 0 && hh < G)
-                st = *reinterpret_cast<const f32x4*>(p.stats + ((((size_t)b * p.T + tk) * H + g * G + hh) * 3 + kind) * 4);
-            *reinterpret_cast<f32x4*>(&rs[r * 4]) = st;
-        }
+        const int tA = tok(i), tB = tok(i + 1);
+        __syncthreads();   // the previous pair's LDS reads are complete
+        stage.store(qs, QSTR, os, OSTR, rs);
         __syncthreads();
+        stage.load(p, b, g, kind, tok(i + 2), tok(i + 3));   // in flight during this pair's math
         // S = Q.K^T and dP = dO.V^T: C lane (li = key, lq) holds head rows 4 lq + r
         f32x4 sA = zero4(), sB = zero4(), pA = zero4(), pB = zero4();
 #pragma unroll
@@ -454,21 +561,28 @@ void launch_fill_zero(float* x, size_t n, hipStream_t st) {
 }
 
 bool launch_bwd_dq(int DK, int DV, const BwdParams& p, hipStream_t st) {
-    const dim3 grid(p.T, p.B * p.Hkv);
-    if (DK == 192 && DV == 128) bwd_dq_kernel<192, 128><<<grid, 64, 0, st>>>(p);
-    else if (DK == 128 && DV == 128) bwd_dq_kernel<128, 128><<<grid, 64, 0, st>>>(p);
-    else if (DK == 64 && DV == 64) bwd_dq_kernel<64, 64><<<grid, 64, 0, st>>>(p);
+    const int grid = xcd_grid(p.B * p.Hkv, (p.T + kDqTok - 1) / kDqTok);
+    if (DK == 192 && DV == 128) bwd_dq_kernel<192, 128><<<grid, 256, 0, st>>>(p);
+    else if (DK == 128 && DV == 128) bwd_dq_kernel<128, 128><<<grid, 256, 0, st>>>(p);
+    else if (DK == 64 && DV == 64) bwd_dq_kernel<64, 64><<<grid, 256, 0, st>>>(p);
     else return false;
     return true;
 }
 
-bool launch_bwd_dkv(int DK, int DV, const BwdParams& p, int n_items, hipStream_t st) {
-    if (n_items <= 0) return true;
-    if (DK == 192 && DV == 128) bwd_dkv_kernel<192, 128><<<n_items, 256, 0, st>>>(p);
-    else if (DK == 128 && DV == 128) bwd_dkv_kernel<128, 128><<<n_items, 256, 0, st>>>(p);
-    else if (DK == 64 && DV == 64) bwd_dkv_kernel<64, 64><<<n_items, 256, 0, st>>>(p);
+template <int NW>
+bool launch_dkv_nw(int DK, int DV, const BwdParams& p, int item0, int n, hipStream_t st) {
+    if (n <= 0) return true;
+    if (DK == 192 && DV == 128) bwd_dkv_kernel<192, 128, NW><<<n, 64 * NW, 0, st>>>(p, item0);
+    else if (DK == 128 && DV == 128) bwd_dkv_kernel<128, 128, NW><<<n, 64 * NW, 0, st>>>(p, item0);
+    else if (DK == 64 && DV == 64) bwd_dkv_kernel<64, 64, NW><<<n, 64 * NW, 0, st>>>(p, item0);
     else return false;
     return true;
+}
+
+// compressed and window items: 128 keys (8 waves); selected items: 64 keys (4 waves)
+bool launch_bwd_dkv(int DK, int DV, const BwdParams& p, int n_slc_items, hipStream_t st) {
+    return launch_dkv_nw<kDkvWavesDense>(DK, DV, p, 0, p.n_cmp_items + p.n_win_items, st) &&
+           launch_dkv_nw<kDkvWavesSlc>(DK, DV, p, p.n_cmp_items + p.n_win_items, n_slc_items, st);
 }
 
 void launch_compress_bwd(const u16* X, const u16* W, const u16* pe, const float* dY, float* dX, float* dW, float* dpe,

@@ -107,6 +107,9 @@ bool launch_moba_attn(int DK, int DV, const MobaParams& p, hipStream_t st);
 
 // ---- backward ----
 constexpr int kBwdTile = 128;   // query tokens per dK/dV work item (= the block lists' tile)
+constexpr int kBwdCmpTile = 512;   // query tokens per compressed-branch dK/dV work item
+constexpr int kDkvWavesDense = 8;  // compressed / window items: 128 keys per workgroup
+constexpr int kDkvWavesSlc = 4;    // selected items: 64 keys per workgroup
 struct BwdParams {
     const u16* Q;              // [B,T,H,DK]
     const u16* K;              // [B,Hkv,T,DK] row-major
@@ -126,14 +129,14 @@ struct BwdParams {
     const int* entries;
     int B, T, Hkv, G, N, l, s, lp, top_n, window, branches, n_slc, n_bucket;
     int nsb;                   // 64-key sub-blocks per selection block
-    int n_kb_cmp, n_qt;        // compressed key blocks, 128-token query tiles
+    int n_kb_cmp, n_qt, qt_cmp;   // compressed key blocks, query tiles, tokens per tile
     int n_kb_win, n_qt_win;    // window key blocks, query tiles per window key block
     int n_cmp_items, n_win_items;
     float scale, scale_log2;
 };
 void launch_fill_zero(float* x, size_t n, hipStream_t st);
 bool launch_bwd_dq(int DK, int DV, const BwdParams& p, hipStream_t st);
-bool launch_bwd_dkv(int DK, int DV, const BwdParams& p, int n_items, hipStream_t st);
+bool launch_bwd_dkv(int DK, int DV, const BwdParams& p, int n_slc_items, hipStream_t st);
 // linear block map backward for one of K / V: dX += dY.W^T scattered to tokens, dW and dpe
 // overwritten; colsum: d floats of scratch
 void launch_compress_bwd(const u16* X, const u16* W, const u16* pe, const float* dY, float* dX, float* dW, float* dpe,
