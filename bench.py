@@ -7,10 +7,12 @@ blocks, top-16, window 512): nsa_compress -> nsa_score_select -> nsa_sparse_attn
 every input resident in HBM before the timed region.  The headline ``value`` is prefill
 tokens/s; the line also carries the algorithmic TFLOP/s and MFMA-peak fraction, a
 roofline entry for the dominant kernel (timed live with HIP events on the stream it runs
-on), the oracle timed on the host cores on a bounded sample, and the decode step
-(batch 32 x 65536-token caches, HBM GB/s) and MoBA (131072 and 1048576 tokens) figures.
+on), the oracle timed on the host cores on a bounded sample, the backward pass of the same
+64K step (nsa_sparse_attn_bwd + nsa_compress_bwd), and the decode step (batch 32 x
+65536-token caches, HBM GB/s) and MoBA (131072 and 1048576 tokens) figures.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-decode] [--no-moba]
+                       [--no-dense] [--no-backward]
 """
 from __future__ import annotations
 
@@ -62,6 +64,14 @@ def prefill_flops(cfg: NSAConfig) -> dict:
 
 def moba_flops(cfg: NSAConfig) -> int:
     return slc_pairs(cfg) * 2 * (cfg.d_k + cfg.d_v)
+
+
+def backward_flops(cfg: NSAConfig) -> dict:
+    """Five products per unmasked pair (S recomputed, dP = dO.v, dV, dQ, dK):
+    2 * (3 d_k + 2 d_v) flops; the block map: dX = dY.W^T and dW = X^T.dY for keys and values."""
+    pairs = cmp_pairs(cfg) + slc_pairs(cfg) + win_pairs(cfg)
+    bm = 2 * 2 * cfg.batch * cfg.num_kv_heads * cfg.n_cmp * cfg.cmp_block * (cfg.d_k * cfg.d_k + cfg.d_v * cfg.d_v)
+    return {"attention": pairs * 2 * (3 * cfg.d_k + 2 * cfg.d_v), "block_map": bm}
 
 
 # ---------------------------------------------------------------------------
@@ -148,6 +158,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-moba", action="store_true")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense causal attention comparison")
+    ap.add_argument("--no-backward", action="store_true", help="skip the backward pass timing")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run one elementwise kernel over 1 GiB (reads and writes 1 GiB: the known-size kernel that scales HBM counters)")
     args = ap.parse_args()
@@ -292,6 +303,38 @@ def main():
             "nsa_ms": round(ms, 3), "nsa_speedup": round(fms / ms, 2),
             "at_8k": {"nsa_ms": round(n8ms, 3), "dense_ms": round(f8ms, 3), "nsa_speedup": round(f8ms / n8ms, 2)}}
         del Q8, K8, V8, kc8, vc8, sel8, oc8, o8, wsf
+        torch.cuda.empty_cache()
+
+    # ---------------- backward of the same step ----------------
+    if not args.no_backward:
+        print("[bench] backward", file=sys.stderr, flush=True)
+        lse = torch.empty((B, T, H), dtype=torch.float32, device=dev)
+        ops.score_select(cfg, Q, kc, vc, sel=sel, lse=lse, o_cmp=ocmp, workspace=ws[1])
+        gdo = torch.Generator(device=dev).manual_seed(cfg.seed + 1000)
+        dO = torch.randn((B, T, H, cfg.d_v), generator=gdo, device=dev).to(torch.bfloat16)
+        wsb = torch.empty(ops.workspace_size(cfg, ops.OP_SPARSE_BWD), dtype=torch.uint8, device=dev)
+        wsc = torch.empty(max(ops.workspace_size(cfg, ops.OP_COMPRESS_BWD), 256), dtype=torch.uint8, device=dev)
+        grads = {}
+
+        def bwd_attn():
+            grads.update(ops.sparse_attn_bwd(cfg, Q, K, V, kc, vc, sel, lse, ocmp, gates, dO, workspace=wsb))
+
+        def bwd_map():
+            grads.update(ops.compress_bwd(cfg, K, V, wk, wv, pk, pv, grads["dk_cmp"], grads["dv_cmp"], grads["dk"],
+                                          grads["dv"], workspace=wsc))
+
+        pcb, wallb = time_calls([bwd_attn, bwd_map], 3, 1, torch)
+        bms = float(pcb.sum(axis=1).mean())
+        bfl = backward_flops(cfg)
+        btf = sum(bfl.values()) / (bms * 1e-3) / 1e12
+        result["backward"] = {
+            "workload": "nsa_backward_64k", "ms_per_step": round(bms, 3),
+            "tokens_per_s": round(B * T / (bms * 1e-3), 1),
+            "per_call_ms": {"nsa_sparse_attn_bwd": round(float(pcb[:, 0].mean()), 3),
+                            "nsa_compress_bwd": round(float(pcb[:, 1].mean()), 3)},
+            "algorithmic_flops": {k: int(v) for k, v in bfl.items()},
+            "tflops_algorithmic": round(btf, 2), "mfma_peak_frac": round(btf / PEAK_BF16_TFLOPS, 4)}
+        del grads, dO, wsb, wsc, lse
         torch.cuda.empty_cache()
 
     if not args.no_decode:
