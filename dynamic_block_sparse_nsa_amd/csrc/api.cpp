@@ -369,13 +369,16 @@ nsa_status nsa_select_from_scores(const nsa_config* cfg, const float* scores, in
     return hip_check("select_from_scores");
 }
 
-nsa_status nsa_sparse_attn_fwd(const nsa_config* cfg, const void* Q, const void* K, const void* V,
-                               const int32_t* sel_idx, const float* o_cmp, const float* gate_logits, void* O,
-                               void* ws, size_t ws_bytes, void* stream) {
+namespace {
+nsa_status sparse_attn_fwd_impl(const nsa_config* cfg, const void* Q, const void* K, const void* V,
+                                const int32_t* sel_idx, const float* o_cmp, const float* gate_logits, void* O,
+                                float* saved_lse, float* saved_o, void* ws, size_t ws_bytes, void* stream) {
     g_detail.clear();
     Shape s;
     nsa_status st = check_config(cfg, &s);
     if (st != NSA_OK) return st;
+    const bool train = saved_lse != nullptr || saved_o != nullptr;
+    if (train && (!saved_lse || !saved_o)) return fail(NSA_ERR_NULL, "saved_lse and saved_o go together");
     if (!Q || !K || !V || !O) return fail(NSA_ERR_NULL, "Q, K, V and O are required");
     if ((s.br & NSA_BR_SLC) && !sel_idx) return fail(NSA_ERR_NULL, "sel_idx is required for the selected branch");
     if ((s.br & NSA_BR_CMP) && !o_cmp) return fail(NSA_ERR_NULL, "o_cmp is required for the compressed branch");
@@ -389,7 +392,7 @@ nsa_status nsa_sparse_attn_fwd(const nsa_config* cfg, const void* Q, const void*
     if (!nsa::launch_tile_kv(s.dk, s.dv, static_cast<const u16*>(K), static_cast<const u16*>(V), kf, vf, s.B * s.Hkv,
                              s.T, w.tpad, hs))
         return fail(NSA_ERR_UNSUPPORTED, "no layout kernel");
-    if (use_block_major(s)) {
+    if (use_block_major(s) && !train) {
         if ((long long)s.T >= (1LL << 26)) return fail(NSA_ERR_UNSUPPORTED, "sequence too long for the block lists");
         nsa::MobaParams m{};
         m.Q = static_cast<const u16*>(Q);
@@ -420,11 +423,36 @@ nsa_status nsa_sparse_attn_fwd(const nsa_config* cfg, const void* Q, const void*
     p.o_cmp = o_cmp;
     p.gates = gate_logits;
     p.O = static_cast<u16*>(O);
+    p.saved_lse = saved_lse;
+    p.saved_o = saved_o;
     p.B = s.B; p.T = s.T; p.Tpad = w.tpad; p.Hkv = s.Hkv; p.G = s.G; p.lp = s.lp; p.top_n = s.n; p.window = s.w;
     p.branches = s.br;
     p.scale_log2 = s.scale * nsa::kLog2eHost;
     if (!nsa::launch_sparse_attn(s.dk, s.dv, p, s.B, hs)) return fail(NSA_ERR_UNSUPPORTED, "no attention kernel");
     return hip_check("sparse_attn");
+}
+}  // namespace
+
+nsa_status nsa_sparse_attn_fwd(const nsa_config* cfg, const void* Q, const void* K, const void* V,
+                               const int32_t* sel_idx, const float* o_cmp, const float* gate_logits, void* O,
+                               void* ws, size_t ws_bytes, void* stream) {
+    return sparse_attn_fwd_impl(cfg, Q, K, V, sel_idx, o_cmp, gate_logits, O, nullptr, nullptr, ws, ws_bytes,
+                                stream);
+}
+
+nsa_status nsa_sparse_attn_fwd_train(const nsa_config* cfg, const void* Q, const void* K, const void* V,
+                                     const int32_t* sel_idx, const float* o_cmp, const float* gate_logits, void* O,
+                                     float* saved_lse, float* saved_o, void* ws, size_t ws_bytes, void* stream) {
+    if (!saved_lse || !saved_o) {
+        g_detail.clear();
+        return fail(NSA_ERR_NULL, "saved_lse and saved_o are required");
+    }
+    if ((reinterpret_cast<uintptr_t>(saved_o) & 15u) != 0 || (reinterpret_cast<uintptr_t>(saved_lse) & 7u) != 0) {
+        g_detail.clear();
+        return fail(NSA_ERR_SHAPE, "saved_o must be 16-byte and saved_lse 8-byte aligned");
+    }
+    return sparse_attn_fwd_impl(cfg, Q, K, V, sel_idx, o_cmp, gate_logits, O, saved_lse, saved_o, ws, ws_bytes,
+                                stream);
 }
 
 nsa_status nsa_compress_prepare(const nsa_config* cfg, const void* W_k, const void* W_v, const void* pe_k,
@@ -563,9 +591,10 @@ nsa_status nsa_decode(const nsa_config* cfg, const void* q, const void* K_cache,
 
 nsa_status nsa_sparse_attn_bwd(const nsa_config* cfg, const void* Q, const void* K, const void* V,
                                const void* K_cmp, const void* V_cmp, const int32_t* sel_idx, const float* lse_cmp,
-                               const float* o_cmp, const float* gate_logits, const void* dO, float* dQ, float* dK,
-                               float* dV, float* dK_cmp, float* dV_cmp, float* d_gate_logits, void* ws,
-                               size_t ws_bytes, void* stream) {
+                               const float* o_cmp, const float* gate_logits, const float* saved_lse,
+                               const float* saved_o, const void* dO, float* dQ, float* dK, float* dV,
+                               float* dK_cmp, float* dV_cmp, float* d_gate_logits, void* ws, size_t ws_bytes,
+                               void* stream) {
     g_detail.clear();
     Shape s;
     nsa_status st = check_config(cfg, &s);
@@ -575,6 +604,7 @@ nsa_status nsa_sparse_attn_bwd(const nsa_config* cfg, const void* Q, const void*
     if ((s.br & NSA_BR_CMP) && (!K_cmp || !V_cmp || !lse_cmp || !o_cmp || !dK_cmp || !dV_cmp))
         return fail(NSA_ERR_NULL, "the compressed branch needs K_cmp, V_cmp, lse_cmp, o_cmp, dK_cmp and dV_cmp");
     if (d_gate_logits && !gate_logits) return fail(NSA_ERR_NULL, "d_gate_logits needs gate_logits");
+    if ((saved_lse == nullptr) != (saved_o == nullptr)) return fail(NSA_ERR_NULL, "saved_lse and saved_o go together");
     if ((s.br & NSA_BR_WIN) && s.w <= 0) return fail(NSA_ERR_SHAPE, "window branch with window = 0");
     if ((long long)s.T >= (1LL << 26)) return fail(NSA_ERR_UNSUPPORTED, "sequence too long for the block lists");
     const BwdWs w = bwd_ws(s);
@@ -596,11 +626,12 @@ nsa_status nsa_sparse_attn_bwd(const nsa_config* cfg, const void* Q, const void*
         nsa::launch_fill_zero(dK_cmp, bg * s.n_cmp * s.dk, hs);
         nsa::launch_fill_zero(dV_cmp, bg * s.n_cmp * s.dv, hs);
     }
-    // 1. per-row statistics (the forward's selected and window branches recomputed)
+    // 1. per-row statistics: from the training forward's saved outputs, or the forward's
+    //    selected and window branches recomputed
     u16* kf = at<u16>(ws, w.kf);
     u16* vf = at<u16>(ws, w.vf);
-    if (!nsa::launch_tile_kv(s.dk, s.dv, static_cast<const u16*>(K), static_cast<const u16*>(V), kf, vf, (int)bg, s.T,
-                             w.tpad, hs))
+    if (!saved_o && !nsa::launch_tile_kv(s.dk, s.dv, static_cast<const u16*>(K), static_cast<const u16*>(V), kf, vf,
+                                         (int)bg, s.T, w.tpad, hs))
         return fail(NSA_ERR_UNSUPPORTED, "no layout kernel");
     nsa::AttnParams a{};
     a.Q = static_cast<const u16*>(Q);
@@ -616,7 +647,11 @@ nsa_status nsa_sparse_attn_bwd(const nsa_config* cfg, const void* Q, const void*
     a.B = s.B; a.T = s.T; a.Tpad = w.tpad; a.Hkv = s.Hkv; a.G = s.G; a.lp = s.lp; a.top_n = s.n; a.window = s.w;
     a.branches = s.br;
     a.scale_log2 = s.scale * nsa::kLog2eHost;
-    if (!nsa::launch_sparse_attn_stats(s.dk, s.dv, a, hs)) return fail(NSA_ERR_UNSUPPORTED, "no statistics kernel");
+    a.saved_lse = const_cast<float*>(saved_lse);
+    a.saved_o = const_cast<float*>(saved_o);
+    if (saved_o) nsa::launch_stats_from_saved(s.dv, a, hs);
+    else if (!nsa::launch_sparse_attn_stats(s.dk, s.dv, a, hs))
+        return fail(NSA_ERR_UNSUPPORTED, "no statistics kernel");
     // 2. dQ
     nsa::BwdParams p{};
     p.Q = static_cast<const u16*>(Q);

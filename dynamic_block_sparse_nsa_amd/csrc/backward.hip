@@ -56,9 +56,11 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(float* __restrict__ x, s
 
 // ---------------------------------------------------------------------------
 // dQ.  A workgroup owns kDqTok consecutive tokens of one (sequence, group), a wave per token.
-// The compressed keys and the window range are shared by the tokens: their 32-key chunks go
-// through one LDS tile (the next chunk's loads in flight in registers while the current one
-// is computed).  The selected blocks differ per token: each wave stages its own chunks.
+// bwd_dq_kernel: the compressed keys and the window range are shared by the tokens: their
+// 32-key chunks go through one LDS tile (the next chunk's loads in flight in registers while
+// the current one is computed); it writes dQ.  bwd_dq_slc_kernel: the selected blocks differ
+// per token, so each wave walks its own chunks through its own LDS tile, the next chunk's K
+// rows and V fragments in flight in registers; it adds into dQ.
 constexpr int kDqTok = 4;
 
 template <int DK, int DV>
@@ -96,13 +98,54 @@ struct DqChunk {   // one 32-key chunk of K and V rows, staged by the whole work
 // orders this wave's LDS writes before its later reads (no other wave shares the region)
 __device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
+// dQ^T += K^T.dS^T for the 32 keys at key0 of the row-major LDS tile kt (stride KSTR), V rows
+// va (A operands of V.dO^T); keys outside [lo, hi] and heads past G masked.  st: lse2, D,
+// sigma of this lane's (token, head).  Every lane must take part (MFMA operands).  mid() runs
+// once va is consumed (the caller may reload it there).
+template <int DK, int DV, typename Mid>
+__device__ __forceinline__ void dq_chunk(const u16* kt, const bf16x8 (&va)[2][DV / 32], const bf16x8 (&qf)[DK / 32],
+                                         const bf16x8 (&df)[DV / 32], f32x4 (&acc)[DK / 16], int key0, int lo, int hi,
+                                         const f32x4& st, bool head_ok, float scale_log2, Mid mid) {
+    constexpr int NDS = DK / 32, NDD = DV / 32, NDK = DK / 16, KSTR = DK + 16;
+    const int lane = threadIdx.x & 63, li = lane & 15, lq = lane >> 4;
+    f32x4 s0 = zero4(), s1 = zero4(), d0 = zero4(), d1 = zero4();
+#pragma unroll
+    for (int ds = 0; ds < NDS; ++ds) {
+        s0 = mfma16(ld8(&kt[li * KSTR + 32 * ds + 8 * lq]), qf[ds], s0);
+        s1 = mfma16(ld8(&kt[(16 + li) * KSTR + 32 * ds + 8 * lq]), qf[ds], s1);
+    }
+#pragma unroll
+    for (int dd = 0; dd < NDD; ++dd) {
+        d0 = mfma16(va[0][dd], df[dd], d0);
+        d1 = mfma16(va[1][dd], df[dd], d1);
+    }
+    mid();
+    // C rows: keys key0 + 4lq + r (tile 0) and key0 + 16 + 4lq + r (tile 1); column: head
+    f32x4 ga, gb;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int ka = key0 + 4 * lq + r, kb = ka + 16;
+        const float pa = (head_ok && ka >= lo && ka <= hi) ? fast_exp2(s0[r] * scale_log2 - st[0]) : 0.f;
+        const float pb = (head_ok && kb >= lo && kb <= hi) ? fast_exp2(s1[r] * scale_log2 - st[0]) : 0.f;
+        ga[r] = pa * (st[2] * d0[r] - st[1]);
+        gb[r] = pb * (st[2] * d1[r] - st[1]);
+    }
+    bf16x8 gh, gl;
+    pack_p_split(ga, gb, gh, gl);
+#pragma unroll
+    for (int dt = 0; dt < NDK; ++dt) {
+        const bf16x8 a = ld_vt_tr(kt, KSTR, 0, 16 * dt);
+        acc[dt] = mfma16(a, gh, acc[dt]);
+        acc[dt] = mfma16(a, gl, acc[dt]);
+    }
+}
+
 template <int DK, int DV>
 __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p) {
     constexpr int NDS = DK / 32, NDD = DV / 32, NDK = DK / 16;
     constexpr int KSTR = DK + 16, VSTR = DV + 16;   // 8-byte aligned rows for the transposing read
     __shared__ __attribute__((aligned(16))) u16 sk[32 * KSTR];
     __shared__ __attribute__((aligned(16))) u16 sv[32 * VSTR];
-    __shared__ __attribute__((aligned(16))) u16 wk[kDqTok][32 * KSTR];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, li = lane & 15, lq = lane >> 4;
     int bg, it;
     if (!xcd_map_tile(blockIdx.x, p.B * p.Hkv, (p.T + kDqTok - 1) / kDqTok, bg, it)) return;
@@ -122,38 +165,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p) {
 #pragma unroll
     for (int dt = 0; dt < NDK; ++dt) acc[dt] = zero4();
 
-    // dQ^T += K^T.dS^T for the 32 keys at key0 of the row-major tile kt (stride KSTR), values
-    // va (A operands of V.dO^T); keys outside [lo, hi] masked
     auto math = [&](const u16* kt, const bf16x8 (&va)[2][NDD], int key0, int lo, int hi, const f32x4& st) {
-        f32x4 s0 = zero4(), s1 = zero4(), d0 = zero4(), d1 = zero4();
-#pragma unroll
-        for (int ds = 0; ds < NDS; ++ds) {
-            s0 = mfma16(ld8(&kt[li * KSTR + 32 * ds + 8 * lq]), qf[ds], s0);
-            s1 = mfma16(ld8(&kt[(16 + li) * KSTR + 32 * ds + 8 * lq]), qf[ds], s1);
-        }
-#pragma unroll
-        for (int dd = 0; dd < NDD; ++dd) {
-            d0 = mfma16(va[0][dd], df[dd], d0);
-            d1 = mfma16(va[1][dd], df[dd], d1);
-        }
-        // C rows: keys key0 + 4lq + r (tile 0) and key0 + 16 + 4lq + r (tile 1); column: head
-        f32x4 ga, gb;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int ka = key0 + 4 * lq + r, kb = ka + 16;
-            const float pa = (head_ok && ka >= lo && ka <= hi) ? fast_exp2(s0[r] * p.scale_log2 - st[0]) : 0.f;
-            const float pb = (head_ok && kb >= lo && kb <= hi) ? fast_exp2(s1[r] * p.scale_log2 - st[0]) : 0.f;
-            ga[r] = pa * (st[2] * d0[r] - st[1]);
-            gb[r] = pb * (st[2] * d1[r] - st[1]);
-        }
-        bf16x8 gh, gl;
-        pack_p_split(ga, gb, gh, gl);
-#pragma unroll
-        for (int dt = 0; dt < NDK; ++dt) {
-            const bf16x8 a = ld_vt_tr(kt, KSTR, 0, 16 * dt);
-            acc[dt] = mfma16(a, gh, acc[dt]);
-            acc[dt] = mfma16(a, gl, acc[dt]);
-        }
+        dq_chunk<DK, DV>(kt, va, qf, df, acc, key0, lo, hi, st, head_ok, p.scale_log2, [] {});
     };
 
     // keys kfirst .. klast of Kb/Vb shared by the workgroup's tokens; this wave's token
@@ -198,40 +211,102 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p) {
         const f32x4 st = *reinterpret_cast<const f32x4*>(p.stats + row * 12 + 8);
         shared_range(Kb, Vb, p.T, max(0, t0 - p.window + 1), tlast, max(0, t - p.window + 1), t, st);
     }
-    if ((p.branches & 2) && active) {   // per wave from here on: no workgroup barrier
-        const f32x4 st = *reinterpret_cast<const f32x4*>(p.stats + row * 12 + 4);
-        const int32_t* sl = p.sel + (((size_t)b * p.T + t) * p.Hkv + g) * p.top_n;
-        u16* kt = wk[wave];
-        for (int c = 0; c < p.top_n; ++c) {
-            const int j = sl[c];
-            if (j < 0 || j * p.lp > t) continue;
-            const int lo = j * p.lp, hi = min(t, lo + p.lp - 1);
-            for (int key0 = lo; key0 <= hi; key0 += 32) {
-                wave_lds_sync();   // the previous chunk's reads are complete
-                for (int i = lane; i < 32 * (DK / 8); i += 64) {
-                    const int r = i / (DK / 8), col = (i % (DK / 8)) * 8;
-                    *reinterpret_cast<u32x4*>(&kt[r * KSTR + col]) =
-                        key0 + r < p.T ? *reinterpret_cast<const u32x4*>(Kb + (size_t)(key0 + r) * DK + col)
-                                       : u32x4{0u, 0u, 0u, 0u};
-                }
-                bf16x8 va[2][NDD];
-#pragma unroll
-                for (int tt = 0; tt < 2; ++tt) {
-                    const int key = key0 + 16 * tt + li;
-#pragma unroll
-                    for (int dd = 0; dd < NDD; ++dd)
-                        va[tt][dd] = key < p.T ? ld8(Vb + (size_t)key * DV + 32 * dd + 8 * lq) : zero8();
-                }
-                wave_lds_sync();
-                math(kt, va, key0, lo, hi, st);
-            }
-        }
-    }
     if (!head_ok) return;
     // dQ^T C layout: rows d = 16 dt + 4 lq + r of head li
 #pragma unroll
     for (int dt = 0; dt < NDK; ++dt)
         *reinterpret_cast<f32x4*>(p.dQ + row * DK + 16 * dt + 4 * lq) = acc[dt] * p.scale;
+}
+
+template <int DK, int DV>
+__global__ __launch_bounds__(256, 2) void bwd_dq_slc_kernel(BwdParams p) {
+    constexpr int NDS = DK / 32, NDD = DV / 32, NDK = DK / 16;
+    constexpr int KSTR = DK + 16;
+    constexpr int NKR = 32 * DK / 8 / 64;   // 16-byte pieces of a 32-key K chunk per lane
+    __shared__ __attribute__((aligned(16))) u16 wk[kDqTok][32 * KSTR];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, li = lane & 15, lq = lane >> 4;
+    int bg, it;
+    if (!xcd_map_tile(blockIdx.x, p.B * p.Hkv, (p.T + kDqTok - 1) / kDqTok, bg, it)) return;
+    const int b = bg / p.Hkv, g = bg % p.Hkv;
+    const int t = it * kDqTok + wave;
+    if (t >= p.T) return;   // whole wave; no workgroup barrier in this kernel
+    const int G = p.G, H = p.Hkv * G;
+    const bool head_ok = li < G;
+    const size_t row = ((size_t)b * p.T + t) * H + g * G + min(li, G - 1);
+    bf16x8 qf[NDS], df[NDD];
+#pragma unroll
+    for (int ds = 0; ds < NDS; ++ds) qf[ds] = head_ok ? ld8(p.Q + row * DK + 32 * ds + 8 * lq) : zero8();
+#pragma unroll
+    for (int dd = 0; dd < NDD; ++dd) df[dd] = head_ok ? ld8(p.dO + row * DV + 32 * dd + 8 * lq) : zero8();
+    const f32x4 st = *reinterpret_cast<const f32x4*>(p.stats + row * 12 + 4);
+    f32x4 acc[NDK];
+#pragma unroll
+    for (int dt = 0; dt < NDK; ++dt) acc[dt] = zero4();
+    const u16* Kb = p.K + (size_t)bg * p.T * DK;
+    const u16* Vb = p.V + (size_t)bg * p.T * DV;
+    u16* kt = wk[wave];
+    // the token's block list, one entry per lane, read back with readlane
+    const int sel_lane = lane < p.top_n ? p.sel[(((size_t)b * p.T + t) * p.Hkv + g) * p.top_n + lane] : -1;
+    auto sl = [&](int c) { return __builtin_amdgcn_readlane(sel_lane, c); };
+    // chunk after (c, q) in list order: block slot c, sub-chunk q (32 keys); false past the end
+    auto next = [&](int& c, int& q) {
+        ++q;
+        for (; c < p.top_n; ++c, q = 0) {
+            const int j = sl(c);
+            if (j >= 0 && j * p.lp <= t && j * p.lp + 32 * q <= min(t, j * p.lp + p.lp - 1)) return true;
+        }
+        return false;
+    };
+    int c = 0, q = -1;
+    if (!next(c, q)) return;
+    // loads of a chunk: K rows into kr (stored to LDS at the next step), V rows as A operands;
+    // rows past the sequence are read from its last token (those keys are masked)
+    u32x4 kr[NKR];
+    bf16x8 va[2][NDD];
+    auto load_k = [&](int key0) {
+#pragma unroll
+        for (int i = 0; i < NKR; ++i) {
+            const int idx = lane + 64 * i, r = idx / (DK / 8), col = (idx % (DK / 8)) * 8;
+            kr[i] = *reinterpret_cast<const u32x4*>(Kb + (size_t)min(key0 + r, p.T - 1) * DK + col);
+        }
+    };
+    auto load_v = [&](int key0) {
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+            for (int dd = 0; dd < NDD; ++dd)
+                va[tt][dd] = ld8(Vb + (size_t)min(key0 + 16 * tt + li, p.T - 1) * DV + 32 * dd + 8 * lq);
+    };
+    int key0 = sl(c) * p.lp + 32 * q;
+    load_k(key0);
+    load_v(key0);
+    for (;;) {
+        const int j = sl(c);
+        const int lo = j * p.lp, hi = min(t, lo + p.lp - 1);
+        wave_lds_sync();   // the previous chunk's LDS reads are complete
+#pragma unroll
+        for (int i = 0; i < NKR; ++i) {
+            const int idx = lane + 64 * i, r = idx / (DK / 8), col = (idx % (DK / 8)) * 8;
+            *reinterpret_cast<u32x4*>(&kt[r * KSTR + col]) = kr[i];
+        }
+        int cn = c, qn = q;
+        const bool more = next(cn, qn);
+        const int key_n = more ? sl(cn) * p.lp + 32 * qn : key0;   // the last chunk reloads itself
+        load_k(key_n);   // in flight during this chunk's math
+        wave_lds_sync();
+        // the next chunk's V rows are requested as soon as this chunk's dP has used va
+        dq_chunk<DK, DV>(kt, va, qf, df, acc, key0, lo, hi, st, head_ok, p.scale_log2, [&] { load_v(key_n); });
+        if (!more) break;
+        c = cn;
+        q = qn;
+        key0 = key_n;
+    }
+    if (!head_ok) return;
+#pragma unroll
+    for (int dt = 0; dt < NDK; ++dt) {
+        f32x4* o = reinterpret_cast<f32x4*>(p.dQ + row * DK + 16 * dt + 4 * lq);
+        *o = *o + acc[dt] * p.scale;
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -554,6 +629,47 @@ __global__ __launch_bounds__(256) void compress_bwd_dx_kernel(const float* __res
 }
 
 // ---------------------------------------------------------------------------
+// Statistics from a training forward's saved outputs: one wave per (token, head) row,
+// D_c = sigma_c <dO, o_c> reduced over the lanes, the LSEs copied (base 2).
+template <int DV>
+__global__ __launch_bounds__(256) void stats_from_saved_kernel(AttnParams p) {
+    const int lane = threadIdx.x & 63;
+    const size_t rows = (size_t)p.B * p.T * p.Hkv * p.G;
+    const size_t row = (size_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= rows) return;
+    const bool on[3] = {(p.branches & 1) != 0, (p.branches & 2) != 0, (p.branches & 4) != 0};
+    float dot[3] = {0.f, 0.f, 0.f};
+    for (int d = lane; d < DV; d += 64) {
+        const float g = bf2f(p.dO[row * DV + d]);
+        if (on[0]) dot[0] += g * p.o_cmp[row * DV + d];
+        if (on[1]) dot[1] += g * p.saved_o[row * 2 * DV + d];
+        if (on[2]) dot[2] += g * p.saved_o[(row * 2 + 1) * DV + d];
+    }
+#pragma unroll
+    for (int c = 0; c < 3; ++c)
+#pragma unroll
+        for (int m = 32; m > 0; m >>= 1) dot[c] += __shfl_xor(dot[c], m);
+    if (lane != 0) return;
+    float sg[3] = {1.f, 1.f, 1.f};
+    if (p.gates)
+#pragma unroll
+        for (int c = 0; c < 3; ++c) sg[c] = sigmoidf_(p.gates[row * 3 + c]);
+    const float lse2[3] = {on[0] ? p.lse_cmp[row] * kLog2e : 0.f, p.saved_lse[row * 2], p.saved_lse[row * 2 + 1]};
+    f32x4* so = reinterpret_cast<f32x4*>(p.stats + row * 12);
+#pragma unroll
+    for (int c = 0; c < 3; ++c) {
+        so[c] = f32x4{lse2[c], on[c] ? sg[c] * dot[c] : 0.f, sg[c], 0.f};
+        if (p.dgates) p.dgates[row * 3 + c] = on[c] ? sg[c] * (1.f - sg[c]) * dot[c] : 0.f;
+    }
+}
+
+void launch_stats_from_saved(int DV, const AttnParams& p, hipStream_t st) {
+    const size_t rows = (size_t)p.B * p.T * p.Hkv * p.G;
+    const unsigned grid = (unsigned)((rows + 3) / 4);
+    if (DV == 128) stats_from_saved_kernel<128><<<grid, 256, 0, st>>>(p);
+    else stats_from_saved_kernel<64><<<grid, 256, 0, st>>>(p);
+}
+
 void launch_fill_zero(float* x, size_t n, hipStream_t st) {
     if (n == 0) return;
     const size_t blocks = std::min<size_t>((n / 4 + 255) / 256 + 1, 8192);
@@ -562,10 +678,19 @@ void launch_fill_zero(float* x, size_t n, hipStream_t st) {
 
 bool launch_bwd_dq(int DK, int DV, const BwdParams& p, hipStream_t st) {
     const int grid = xcd_grid(p.B * p.Hkv, (p.T + kDqTok - 1) / kDqTok);
-    if (DK == 192 && DV == 128) bwd_dq_kernel<192, 128><<<grid, 256, 0, st>>>(p);
-    else if (DK == 128 && DV == 128) bwd_dq_kernel<128, 128><<<grid, 256, 0, st>>>(p);
-    else if (DK == 64 && DV == 64) bwd_dq_kernel<64, 64><<<grid, 256, 0, st>>>(p);
-    else return false;
+    const bool slc = (p.branches & 2) != 0;
+    if (DK == 192 && DV == 128) {
+        bwd_dq_kernel<192, 128><<<grid, 256, 0, st>>>(p);
+        if (slc) bwd_dq_slc_kernel<192, 128><<<grid, 256, 0, st>>>(p);
+    } else if (DK == 128 && DV == 128) {
+        bwd_dq_kernel<128, 128><<<grid, 256, 0, st>>>(p);
+        if (slc) bwd_dq_slc_kernel<128, 128><<<grid, 256, 0, st>>>(p);
+    } else if (DK == 64 && DV == 64) {
+        bwd_dq_kernel<64, 64><<<grid, 256, 0, st>>>(p);
+        if (slc) bwd_dq_slc_kernel<64, 64><<<grid, 256, 0, st>>>(p);
+    } else {
+        return false;
+    }
     return true;
 }
 

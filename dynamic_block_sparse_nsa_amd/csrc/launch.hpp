@@ -67,11 +67,17 @@ struct AttnParams {
     const u16* dO;         // [B,T,H,DV]
     float* stats;          // [B,T,H,3,4]: lse2, D, sigma, 0
     float* dgates;         // [B,T,H,3] or null
+    // training forward (forward mode, both non-null): the selected and window branches'
+    // base-2 LSE and normalized outputs, saved for the backward
+    float* saved_lse;      // [B,T,H,2]
+    float* saved_o;        // [B,T,H,2,DV]
     int B, T, Tpad, Hkv, G, lp, top_n, window, branches;
     float scale_log2;
 };
 bool launch_sparse_attn(int DK, int DV, const AttnParams& p, int B, hipStream_t st);
 bool launch_sparse_attn_stats(int DK, int DV, const AttnParams& p, hipStream_t st);
+// the backward statistics from a training forward's saved LSE and outputs (no recompute)
+void launch_stats_from_saved(int DV, const AttnParams& p, hipStream_t st);
 bool launch_tile_kv(int DK, int DV, const u16* K, const u16* V, u16* Kf, u16* Vf, int BG, int T, int Tpad,
                     hipStream_t st);
 

@@ -382,6 +382,17 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnParams p) {
 
     float gc = 1.f, gs = 1.f, gw = 1.f;
     const size_t row = ((size_t)b * T + t) * H + h;
+    if (p.saved_o) {   // training forward: what the backward needs of the two branches
+        if (lq == 0)
+            *reinterpret_cast<float2*>(p.saved_lse + row * 2) =
+                float2{use_slc ? slc.m + __log2f(Ls) : 0.f, use_win ? win.m + __log2f(Lw) : 0.f};
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+            const int d0 = 16 * dt + 4 * lq;
+            st_stream(slc.o[dt], reinterpret_cast<f32x4*>(p.saved_o + row * 2 * DV + d0));
+            st_stream(win.o[dt], reinterpret_cast<f32x4*>(p.saved_o + (row * 2 + 1) * DV + d0));
+        }
+    }
     if (p.gates) {
         gc = sigmoidf_(p.gates[row * 3 + 0]);
         gs = sigmoidf_(p.gates[row * 3 + 1]);

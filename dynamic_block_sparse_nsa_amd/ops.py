@@ -68,7 +68,8 @@ def lib(build_if_missing: bool = True):
         L.nsa_full_attn_fwd.argtypes = [cp] + [_P] * 5 + [ctypes.c_size_t, _P]
         L.nsa_compress_prepare.argtypes = [cp] + [_P] * 5 + [ctypes.c_size_t, _P]
         L.nsa_cache_append.argtypes = [cp, _P, _P, ctypes.c_int32] + [_P] * 6 + [ctypes.c_size_t, _P]
-        L.nsa_sparse_attn_bwd.argtypes = [cp] + [_P] * 17 + [ctypes.c_size_t, _P]
+        L.nsa_sparse_attn_bwd.argtypes = [cp] + [_P] * 19 + [ctypes.c_size_t, _P]
+        L.nsa_sparse_attn_fwd_train.argtypes = [cp] + [_P] * 10 + [ctypes.c_size_t, _P]
         L.nsa_compress_bwd.argtypes = [cp] + [_P] * 15 + [ctypes.c_size_t, _P]
         for f in ("nsa_workspace_size", "nsa_compress", "nsa_score_select", "nsa_select_from_scores",
                   "nsa_sparse_attn_fwd", "nsa_decode", "nsa_full_attn_fwd", "nsa_compress_prepare",
@@ -290,21 +291,54 @@ def cache_append(cfg: NSAConfig, K_new, V_new, K_cache, V_cache, cache_len, K_cm
                                   prep.numel(), _stream(stream)))
 
 
-def prefill(cfg: NSAConfig, Q, K, V, w_k=None, w_v=None, pe_k=None, pe_v=None, gates=None, stream=None):
-    """The whole prefill hot path: compress -> score_select -> sparse_attn_fwd.  Returns
-    dict(out, sel, o_cmp, lse, k_cmp, v_cmp) (o_cmp and lse: compressed branch only)."""
+def prefill(cfg: NSAConfig, Q, K, V, w_k=None, w_v=None, pe_k=None, pe_v=None, gates=None, stream=None,
+            train=False):
+    """The whole prefill hot path: compress -> score_select -> sparse_attn_fwd (or, with
+    ``train``, sparse_attn_fwd_train).  Returns dict(out, sel, o_cmp, lse, k_cmp, v_cmp and,
+    with ``train``, saved_lse, saved_o) (o_cmp and lse: compressed branch only)."""
     k_cmp, v_cmp = compress(cfg, K, V, w_k, w_v, pe_k, pe_v, stream=stream)
     use_c = bool(cfg.branches & 1)
     sel, lse, o_cmp = score_select(cfg, Q, k_cmp, v_cmp, want_lse=use_c, want_ocmp=use_c, stream=stream)
-    out = sparse_attn_fwd(cfg, Q, K, V, sel, o_cmp, gates, stream=stream)
-    return {"out": out, "sel": sel, "o_cmp": o_cmp, "lse": lse, "k_cmp": k_cmp, "v_cmp": v_cmp}
+    r = {"sel": sel, "o_cmp": o_cmp, "lse": lse, "k_cmp": k_cmp, "v_cmp": v_cmp}
+    if train:
+        r["out"], r["saved_lse"], r["saved_o"] = sparse_attn_fwd_train(cfg, Q, K, V, sel, o_cmp, gates, stream=stream)
+    else:
+        r["out"] = sparse_attn_fwd(cfg, Q, K, V, sel, o_cmp, gates, stream=stream)
+    return r
 
 
 # ---------------------------------------------------------------------------
-def sparse_attn_bwd(cfg: NSAConfig, Q, K, V, K_cmp, V_cmp, sel, lse_cmp, o_cmp, gates, dO, *, want_dgates=True,
-                    workspace=None, stream=None) -> dict:
+def sparse_attn_fwd_train(cfg: NSAConfig, Q, K, V, sel=None, o_cmp=None, gates=None, *, out=None, workspace=None,
+                          stream=None):
+    """nsa_sparse_attn_fwd_train.  Returns (O [B,T,H,dv] bf16, saved_lse [B,T,H,2] fp32,
+    saved_o [B,T,H,2,dv] fp32)."""
+    B, T, H, Hkv = cfg.batch, cfg.seq_len, cfg.num_heads, cfg.num_kv_heads
+    _need(Q, "Q", torch.bfloat16, (B, T, H, cfg.d_k))
+    _need(K, "K", torch.bfloat16, (B, Hkv, T, cfg.d_k))
+    _need(V, "V", torch.bfloat16, (B, Hkv, T, cfg.d_v))
+    if cfg.branches & 2:
+        _need(sel, "sel", torch.int32, (B, T, Hkv, cfg.top_n))
+    if cfg.branches & 1:
+        _need(o_cmp, "o_cmp", torch.float32, (B, T, H, cfg.d_v))
+    if gates is not None:
+        _need(gates, "gates", torch.float32, (B, T, H, 3))
+    if out is None:
+        out = torch.empty((B, T, H, cfg.d_v), dtype=torch.bfloat16, device=Q.device)
+    saved_lse = torch.empty((B, T, H, 2), dtype=torch.float32, device=Q.device)
+    saved_o = torch.empty((B, T, H, 2, cfg.d_v), dtype=torch.float32, device=Q.device)
+    ws, nws = _workspace(cfg, OP_SPARSE_ATTN, Q.device, workspace)
+    _check(lib().nsa_sparse_attn_fwd_train(ctypes.byref(c_config(cfg)), _ptr(Q), _ptr(K), _ptr(V),
+                                           _ptr(sel if cfg.branches & 2 else None),
+                                           _ptr(o_cmp if cfg.branches & 1 else None), _ptr(gates), _ptr(out),
+                                           _ptr(saved_lse), _ptr(saved_o), _ptr(ws), nws, _stream(stream)))
+    return out, saved_lse, saved_o
+
+
+def sparse_attn_bwd(cfg: NSAConfig, Q, K, V, K_cmp, V_cmp, sel, lse_cmp, o_cmp, gates, dO, *, saved_lse=None,
+                    saved_o=None, want_dgates=True, workspace=None, stream=None) -> dict:
     """nsa_sparse_attn_bwd.  Returns dict(dq, dk, dv, dk_cmp, dv_cmp, dgates) of fp32 tensors
-    (dk_cmp/dv_cmp None without the compressed branch, dgates None without gates)."""
+    (dk_cmp/dv_cmp None without the compressed branch, dgates None without gates).
+    saved_lse/saved_o: from sparse_attn_fwd_train (None: recomputed)."""
     B, T, H, Hkv, N = cfg.batch, cfg.seq_len, cfg.num_heads, cfg.num_kv_heads, cfg.n_cmp
     dk, dv = cfg.d_k, cfg.d_v
     _need(Q, "Q", torch.bfloat16, (B, T, H, dk))
@@ -321,6 +355,9 @@ def sparse_attn_bwd(cfg: NSAConfig, Q, K, V, K_cmp, V_cmp, sel, lse_cmp, o_cmp, 
         _need(sel, "sel", torch.int32, (B, T, Hkv, cfg.top_n))
     if gates is not None:
         _need(gates, "gates", torch.float32, (B, T, H, 3))
+    if saved_o is not None:
+        _need(saved_lse, "saved_lse", torch.float32, (B, T, H, 2))
+        _need(saved_o, "saved_o", torch.float32, (B, T, H, 2, dv))
     dev = Q.device
     f32 = dict(dtype=torch.float32, device=dev)
     out = {"dq": torch.empty((B, T, H, dk), **f32), "dk": torch.empty((B, Hkv, T, dk), **f32),
@@ -332,7 +369,8 @@ def sparse_attn_bwd(cfg: NSAConfig, Q, K, V, K_cmp, V_cmp, sel, lse_cmp, o_cmp, 
     _check(lib().nsa_sparse_attn_bwd(
         ctypes.byref(c_config(cfg)), _ptr(Q), _ptr(K), _ptr(V), _ptr(K_cmp if use_c else None),
         _ptr(V_cmp if use_c else None), _ptr(sel if cfg.branches & 2 else None), _ptr(lse_cmp if use_c else None),
-        _ptr(o_cmp if use_c else None), _ptr(gates), _ptr(dO), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]),
+        _ptr(o_cmp if use_c else None), _ptr(gates), _ptr(saved_lse), _ptr(saved_o), _ptr(dO), _ptr(out["dq"]),
+        _ptr(out["dk"]), _ptr(out["dv"]),
         _ptr(out["dk_cmp"]), _ptr(out["dv_cmp"]), _ptr(out["dgates"]), _ptr(ws), nws, _stream(stream)))
     return out
 
@@ -369,7 +407,7 @@ def backward(cfg: NSAConfig, fwd: dict, Q, K, V, w_k, w_v, pe_k, pe_v, gates, dO
     compressed branch in fwd["lse"]): nsa_sparse_attn_bwd then nsa_compress_bwd.  Returns
     dict(dq, dk, dv, dgates, dk_cmp, dv_cmp, dw_k, dw_v, dpe_k, dpe_v)."""
     g = sparse_attn_bwd(cfg, Q, K, V, fwd["k_cmp"], fwd["v_cmp"], fwd["sel"], fwd.get("lse"), fwd["o_cmp"], gates,
-                        dO, stream=stream)
+                        dO, saved_lse=fwd.get("saved_lse"), saved_o=fwd.get("saved_o"), stream=stream)
     if cfg.branches & 1:
         g.update(compress_bwd(cfg, K, V, w_k, w_v, pe_k, pe_v, g["dk_cmp"], g["dv_cmp"], g["dk"], g["dv"],
                               stream=stream))

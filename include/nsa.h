@@ -215,7 +215,9 @@ nsa_status nsa_full_attn_fwd(const nsa_config* cfg, const void* Q, const void* K
  * <= t of the listed blocks, tokens t-w+1 .. t.
  * Inputs as for the forward (bf16 Q [B,T,H,d_k], K/V [B,H_kv,T,d], K_cmp/V_cmp [B,H_kv,N,d],
  * sel_idx [B,T,H_kv,top_n], gate_logits [B,T,H,3] fp32 or NULL) plus lse_cmp [B,T,H] and o_cmp
- * [B,T,H,d_v] fp32 as written by nsa_score_select, and dO bf16 [B,T,H,d_v].
+ * [B,T,H,d_v] fp32 as written by nsa_score_select, optionally saved_lse / saved_o from
+ * nsa_sparse_attn_fwd_train (NULL: the two branches' statistics are recomputed), and dO bf16
+ * [B,T,H,d_v].
  * Outputs, fp32, overwritten: dQ [B,T,H,d_k], dK [B,H_kv,T,d_k], dV [B,H_kv,T,d_v], dK_cmp
  * [B,H_kv,N,d_k], dV_cmp [B,H_kv,N,d_v] (compressed branch only, else unused and may be NULL),
  * d_gate_logits [B,T,H,3] (may be NULL; zero for a disabled branch).  dK/dV hold the selected
@@ -227,9 +229,23 @@ nsa_status nsa_full_attn_fwd(const nsa_config* cfg, const void* Q, const void* K
 nsa_status nsa_sparse_attn_bwd(const nsa_config* cfg, const void* Q, const void* K, const void* V,
                                const void* K_cmp, const void* V_cmp, const int32_t* sel_idx,
                                const float* lse_cmp, const float* o_cmp, const float* gate_logits,
-                               const void* dO, float* dQ, float* dK, float* dV, float* dK_cmp,
-                               float* dV_cmp, float* d_gate_logits, void* ws, size_t ws_bytes,
-                               void* stream);
+                               const float* saved_lse, const float* saved_o, const void* dO,
+                               float* dQ, float* dK, float* dV, float* dK_cmp, float* dV_cmp,
+                               float* d_gate_logits, void* ws, size_t ws_bytes, void* stream);
+
+/* Training forward: nsa_sparse_attn_fwd (same inputs, same O) that also saves, for
+ * nsa_sparse_attn_bwd, the selected and window branches' base-2 log-sum-exp
+ * (saved_lse [B,T,H,2] fp32: log2 of the sum over the branch's keys of
+ * 2^(scale*log2(e)*q.k), order slc, win) and normalized outputs (saved_o [B,T,H,2,d_v] fp32,
+ * same order); a disabled branch saves zeros.  Both are required (NSA_ERR_NULL otherwise);
+ * saved_o 16-byte and saved_lse 8-byte aligned (NSA_ERR_SHAPE).  Every configuration runs the
+ * query-centric kernel here (also G = 1 with the selected branch only).  Passing both to
+ * nsa_sparse_attn_bwd replaces its recompute of the two branches by a pass over the saved
+ * values; either both or neither (NSA_ERR_NULL). */
+nsa_status nsa_sparse_attn_fwd_train(const nsa_config* cfg, const void* Q, const void* K, const void* V,
+                                     const int32_t* sel_idx, const float* o_cmp,
+                                     const float* gate_logits, void* O, float* saved_lse,
+                                     float* saved_o, void* ws, size_t ws_bytes, void* stream);
 
 /* Backward of the linear block map of nsa_compress (NSA_PHI_LINEAR; zjai.club notes,
  * section 14: the loss reaches the block representations through the compressed branch).

@@ -39,36 +39,42 @@ LP128 = TINY.replace(name="bwd_lp128", seq_len=1536, num_kv_heads=1, heads_per_g
                      slc_block=128, top_n=5, window=96, fp32_inputs=False, seed=43)
 LP32 = TINY.replace(name="bwd_lp32", seq_len=700, num_kv_heads=1, heads_per_group=2, d_k=64, d_v=64, slc_block=32,
                     cmp_block=16, cmp_stride=8, top_n=7, n_init=2, n_local=2, window=64, fp32_inputs=False, seed=44)
+# (config, with gates, training forward: the backward reads the saved branch statistics)
 CASES = [
-    (TINY.replace(fp32_inputs=False, seed=40), True),
-    (GQA, True),
-    (RAGGED, True),
-    (LP128, True),
-    (LP32, False),
-    (GQA.replace(name="bwd_slc_only", branches=BR_SLC), False),
-    (GQA.replace(name="bwd_cmp_only", branches=BR_CMP), True),
-    (RAGGED.replace(name="bwd_win_only", branches=BR_WIN), True),
+    (TINY.replace(fp32_inputs=False, seed=40), True, False),
+    (TINY.replace(fp32_inputs=False, seed=40), True, True),
+    (GQA, True, False),
+    (GQA, True, True),
+    (RAGGED, True, False),
+    (RAGGED, True, True),
+    (LP128, True, False),
+    (LP32, False, False),
+    (LP32, False, True),
+    (GQA.replace(name="bwd_slc_only", branches=BR_SLC), False, False),
+    (GQA.replace(name="bwd_cmp_only", branches=BR_CMP), True, False),
+    (RAGGED.replace(name="bwd_win_only", branches=BR_WIN), True, True),
 ]
 
 
-def _run(cfg, with_gates):
+def _run(cfg, with_gates, train=False):
     print(f"[case] backward {cfg.name} T={cfg.seq_len} Hkv={cfg.num_kv_heads} G={cfg.heads_per_group} "
-          f"d={cfg.d_k}/{cfg.d_v} br={cfg.branches} gates={with_gates}", flush=True)
+          f"d={cfg.d_k}/{cfg.d_v} br={cfg.branches} gates={with_gates} train={train}", flush=True)
     inp = inputs.prefill_inputs(cfg)
     dO_bits = inputs.grad_output(cfg)
     q, k, v = dev_bf16(inp["q"]), dev_bf16(inp["k"]), dev_bf16(inp["v"])
     wk, wv, pk, pv = ((dev_bf16(inp[n]) if cfg.phi == 0 else None) for n in ("w_k", "w_v", "pe_k", "pe_v"))
     gates = torch.as_tensor(inp["gates"], device="cuda") if with_gates else None
     dO = dev_bf16(dO_bits)
-    fwd = ops.prefill(cfg, q, k, v, wk, wv, pk, pv, gates)
+    fwd = ops.prefill(cfg, q, k, v, wk, wv, pk, pv, gates, train=train)
     g = ops.backward(cfg, fwd, q, k, v, wk, wv, pk, pv, gates, dO)
     torch.cuda.synchronize()
     return inp, dO_bits, fwd, g
 
 
-@pytest.mark.parametrize("cfg,with_gates", CASES, ids=[c.name + ("_g" if wg else "") for c, wg in CASES])
-def test_backward_matches_oracle(cfg, with_gates):
-    inp, dO_bits, fwd, g = _run(cfg, with_gates)
+@pytest.mark.parametrize("cfg,with_gates,train", CASES,
+                         ids=[c.name + ("_g" if wg else "") + ("_train" if tr else "") for c, wg, tr in CASES])
+def test_backward_matches_oracle(cfg, with_gates, train):
+    inp, dO_bits, fwd, g = _run(cfg, with_gates, train)
     use_c = bool(cfg.branches & 1)
     b = 0
     kc = bf16_dev_to_f64(fwd["k_cmp"][b]) if use_c else None
@@ -127,13 +133,14 @@ def test_backward_batch_two():
         check_grad(g["dgates"][b].cpu().numpy(), ref["dgates"], f"batch {b} dgates")
 
 
-def test_backward_moba_mode():
+@pytest.mark.parametrize("train", [False, True])
+def test_backward_moba_mode(train):
     """MoBA mode (mean-pooled block keys, G = 1, selected branch only): the selected-branch
     backward on its own block lists."""
     cfg = TINY.replace(name="bwd_moba", seq_len=2048, num_kv_heads=2, heads_per_group=1, d_k=128, d_v=128,
                        cmp_block=128, cmp_stride=128, slc_block=128, top_n=3, n_init=0, n_local=1, window=0,
                        phi=PHI_MEAN, score_mode=SCORE_MEAN_DOT, branches=BR_SLC, fp32_inputs=False, seed=46)
-    inp, dO_bits, fwd, g = _run(cfg, False)
+    inp, dO_bits, fwd, g = _run(cfg, False, train)
     ref = oracle.nsa_bwd(cfg, f64(inp["q"][0]), f64(inp["k"][0]), f64(inp["v"][0]), None, None,
                          fwd["sel"][0].cpu().numpy(), None, f64(dO_bits[0]))
     for k, r in (("dq", "dq"), ("dk", "dk"), ("dv", "dv")):
@@ -154,3 +161,33 @@ def test_backward_repeatable_shapes():
     assert torch.equal(g1["dgates"], g2["dgates"])
     d = (g1["dk"] - g2["dk"]).abs().max().item()
     assert d <= 1e-5 * max(g1["dk"].abs().max().item(), 1.0)
+
+
+@pytest.mark.parametrize("cfg", [GQA, RAGGED, TINY.replace(fp32_inputs=False, seed=48)], ids=lambda c: c.name)
+def test_training_forward_saves_branch_outputs(cfg):
+    """nsa_sparse_attn_fwd_train returns the forward's O bit for bit and saves each branch's
+    normalized output (checked against the oracle's o_slc / o_win for the same selection and
+    o_cmp) and base-2 log-sum-exp (checked against the oracle's scores of the same keys)."""
+    inp = inputs.prefill_inputs(cfg)
+    q, k, v = dev_bf16(inp["q"]), dev_bf16(inp["k"]), dev_bf16(inp["v"])
+    wk, wv, pk, pv = (dev_bf16(inp[n]) for n in ("w_k", "w_v", "pe_k", "pe_v"))
+    gates = torch.as_tensor(inp["gates"], device="cuda")
+    fwd = ops.prefill(cfg, q, k, v, wk, wv, pk, pv, gates)
+    out_t, s_lse, s_o = ops.sparse_attn_fwd_train(cfg, q, k, v, fwd["sel"], fwd["o_cmp"], gates)
+    torch.cuda.synchronize()
+    assert torch.equal(out_t, fwd["out"])
+    rows = np.arange(cfg.seq_len)
+    ref = oracle.attend(cfg, f64(inp["q"][0]), rows, f64(inp["k"][0]), f64(inp["v"][0]), fwd["sel"][0].cpu().numpy(),
+                        fwd["o_cmp"][0].cpu().numpy().astype(np.float64), inp["gates"][0].astype(np.float64))
+    so = s_o[0].cpu().numpy()
+    check_close(so[:, :, 0], ref["o_slc"], f"{cfg.name} saved o_slc")
+    check_close(so[:, :, 1], ref["o_win"], f"{cfg.name} saved o_win")
+    # window LSE of a few rows written out: log2 sum 2^(scale log2e q.k) over t-w+1 .. t
+    qq, kk = f64(inp["q"][0]), f64(inp["k"][0])
+    sl = s_lse[0].cpu().numpy()
+    for t in (0, 5, cfg.seq_len // 2, cfg.seq_len - 1):
+        for h in range(0, cfg.num_heads, max(1, cfg.num_heads // 4)):
+            g = h // cfg.heads_per_group
+            a = cfg.scale * (kk[g, max(0, t - cfg.window + 1):t + 1] @ qq[t, h])
+            ref_lse2 = (a.max() + np.log(np.exp(a - a.max()).sum())) / np.log(2.0)
+            assert abs(sl[t, h, 1] - ref_lse2) <= 1e-4 * max(1.0, abs(ref_lse2)), (t, h, sl[t, h, 1], ref_lse2)
