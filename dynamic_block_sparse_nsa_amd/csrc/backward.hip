@@ -12,11 +12,13 @@
 //                  column tile (as in the forward); for each branch its keys are walked in
 //                  32-key chunks: S^T = K.Q^T and dP^T = V.dO^T on the MFMA, dS^T in
 //                  registers, dQ^T += K^T.dS^T with K^T read through the transposing LDS
-//                  read from a row-major chunk staged in LDS.
+//                  read from a row-major chunk staged in LDS (dS as a bf16 high/low pair).
 // bwd_dkv_kernel   one workgroup per (64 keys, <= 128 query tokens) work item, a wave per
 //                  16 keys: the item's tokens are taken two at a time (32 head rows staged
 //                  in LDS), S = Q.K^T and dP = dO.V^T with the keys' fragments held in
-//                  registers, then dV^T += dO^T.(sigma P) and dK^T += Q^T.dS; the item's
+//                  registers, then dV^T += dO^T.(sigma P) and dK^T += Q^T.dS (sigma P and dS
+//                  as single bf16 values, fp32 sums on the MFMA, as in the usual attention
+//                  backward: about 2e-3 relative L2 on dK, dV); the item's
 //                  sums are added to the fp32 gradients with atomics.  Items: compressed
 //                  keys x 128-token query tiles (tokens that see the keys), window key
 //                  blocks x the tokens whose window covers them, and for the selected
@@ -130,6 +132,8 @@ __device__ __forceinline__ void dq_chunk(const u16* kt, const bf16x8 (&va)[2][DV
         ga[r] = pa * (st[2] * d0[r] - st[1]);
         gb[r] = pb * (st[2] * d1[r] - st[1]);
     }
+    // dS as a bf16 high/low pair (about 2^-17 relative): dQ keeps fp32-level accuracy for
+    // 12 more MFMAs per chunk (the dQ kernels are bound by their loads, not by these)
     bf16x8 gh, gl;
     pack_p_split(ga, gb, gh, gl);
 #pragma unroll
@@ -472,23 +476,15 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void bwd_dkv_kernel(BwdParams p, i
             gA[r] = PA * (stA[2] * pA[r] - stA[1]);
             gB[r] = PB * (stB[2] * pB[r] - stB[1]);
         }
-        // dV^T += dO^T . (sigma P) and dK^T += Q^T . dS; the row slots of pack_p_split (head
-        // rows 4lq..4lq+3 of token A, then of token B) match the transposing read's key order
-        bf16x8 h8, l8;
-        pack_p_split(wA, wB, h8, l8);
+        // dV^T += dO^T . (sigma P) and dK^T += Q^T . dS with sigma P and dS as single bf16
+        // values; the row slots of pack_p (head rows 4lq..4lq+3 of token A, then of token B)
+        // match the transposing read's key order
+        const bf16x8 w8 = pack_p(wA, wB);
 #pragma unroll
-        for (int dt = 0; dt < NDV; ++dt) {
-            const bf16x8 a = ld_vt_tr(os, OSTR, 0, 16 * dt);
-            dv_acc[dt] = mfma16(a, h8, dv_acc[dt]);
-            dv_acc[dt] = mfma16(a, l8, dv_acc[dt]);
-        }
-        pack_p_split(gA, gB, h8, l8);
+        for (int dt = 0; dt < NDV; ++dt) dv_acc[dt] = mfma16(ld_vt_tr(os, OSTR, 0, 16 * dt), w8, dv_acc[dt]);
+        const bf16x8 g8 = pack_p(gA, gB);
 #pragma unroll
-        for (int dt = 0; dt < NDK; ++dt) {
-            const bf16x8 a = ld_vt_tr(qs, QSTR, 0, 16 * dt);
-            dk_acc[dt] = mfma16(a, h8, dk_acc[dt]);
-            dk_acc[dt] = mfma16(a, l8, dk_acc[dt]);
-        }
+        for (int dt = 0; dt < NDK; ++dt) dk_acc[dt] = mfma16(ld_vt_tr(qs, QSTR, 0, 16 * dt), g8, dk_acc[dt]);
     }
     if (!key_ok) return;
     // C layout of dK^T / dV^T: lane (li = key, lq) holds dims 16 dt + 4 lq + r
