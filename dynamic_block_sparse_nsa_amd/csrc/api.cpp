@@ -605,6 +605,10 @@ nsa_status nsa_sparse_attn_bwd(const nsa_config* cfg, const void* Q, const void*
         return fail(NSA_ERR_NULL, "the compressed branch needs K_cmp, V_cmp, lse_cmp, o_cmp, dK_cmp and dV_cmp");
     if (d_gate_logits && !gate_logits) return fail(NSA_ERR_NULL, "d_gate_logits needs gate_logits");
     if ((saved_lse == nullptr) != (saved_o == nullptr)) return fail(NSA_ERR_NULL, "saved_lse and saved_o go together");
+    if (saved_o && ((reinterpret_cast<uintptr_t>(saved_o) & 15u) != 0 || (reinterpret_cast<uintptr_t>(saved_lse) & 7u) != 0))
+        return fail(NSA_ERR_SHAPE, "saved_o must be 16-byte and saved_lse 8-byte aligned");
+    if ((s.br & NSA_BR_CMP) && (reinterpret_cast<uintptr_t>(o_cmp) & 15u) != 0)
+        return fail(NSA_ERR_SHAPE, "o_cmp must be 16-byte aligned");
     if ((s.br & NSA_BR_WIN) && s.w <= 0) return fail(NSA_ERR_SHAPE, "window branch with window = 0");
     if ((long long)s.T >= (1LL << 26)) return fail(NSA_ERR_UNSUPPORTED, "sequence too long for the block lists");
     const BwdWs w = bwd_ws(s);

@@ -625,27 +625,50 @@ __global__ __launch_bounds__(256) void compress_bwd_dx_kernel(const float* __res
 }
 
 // ---------------------------------------------------------------------------
-// Statistics from a training forward's saved outputs: one wave per (token, head) row,
-// D_c = sigma_c <dO, o_c> reduced over the lanes, the LSEs copied (base 2).
+// Statistics from a training forward's saved outputs: 16 lanes per (token, head) row, each
+// lane DV/16 consecutive dims read as 16-byte vectors; D_c = sigma_c <dO, o_c> summed over
+// the row's lanes (DPP), the LSEs copied (base 2).
 template <int DV>
 __global__ __launch_bounds__(256) void stats_from_saved_kernel(AttnParams p) {
-    const int lane = threadIdx.x & 63;
+    constexpr int E = DV / 16;   // dims per lane (8 or 4)
+    const int lane = threadIdx.x & 63, l16 = lane & 15;
     const size_t rows = (size_t)p.B * p.T * p.Hkv * p.G;
-    const size_t row = (size_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (row >= rows) return;
+    const size_t row = (size_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+    const bool ok = row < rows;
+    const size_t rr = ok ? row : rows - 1;
     const bool on[3] = {(p.branches & 1) != 0, (p.branches & 2) != 0, (p.branches & 4) != 0};
-    float dot[3] = {0.f, 0.f, 0.f};
-    for (int d = lane; d < DV; d += 64) {
-        const float g = bf2f(p.dO[row * DV + d]);
-        if (on[0]) dot[0] += g * p.o_cmp[row * DV + d];
-        if (on[1]) dot[1] += g * p.saved_o[row * 2 * DV + d];
-        if (on[2]) dot[2] += g * p.saved_o[(row * 2 + 1) * DV + d];
+    float g[E];
+    {
+        const u16* src = p.dO + rr * DV + l16 * E;
+        if constexpr (E == 8) {
+            const u32x4 w = *reinterpret_cast<const u32x4*>(src);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                g[2 * i] = bf2f((u16)(w[i] & 0xFFFFu));
+                g[2 * i + 1] = bf2f((u16)(w[i] >> 16));
+            }
+        } else {
+            const u32x2 w = *reinterpret_cast<const u32x2*>(src);
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                g[2 * i] = bf2f((u16)(w[i] & 0xFFFFu));
+                g[2 * i + 1] = bf2f((u16)(w[i] >> 16));
+            }
+        }
     }
+    const float* srcs[3] = {p.o_cmp + rr * DV, p.saved_o + rr * 2 * DV, p.saved_o + (rr * 2 + 1) * DV};
+    float dot[3] = {0.f, 0.f, 0.f};
 #pragma unroll
-    for (int c = 0; c < 3; ++c)
+    for (int c = 0; c < 3; ++c) {
+        if (!on[c]) continue;
 #pragma unroll
-        for (int m = 32; m > 0; m >>= 1) dot[c] += __shfl_xor(dot[c], m);
-    if (lane != 0) return;
+        for (int i = 0; i < E / 4; ++i) {
+            const f32x4 o = ld_stream(reinterpret_cast<const f32x4*>(srcs[c] + l16 * E) + i);
+            dot[c] += g[4 * i] * o[0] + g[4 * i + 1] * o[1] + g[4 * i + 2] * o[2] + g[4 * i + 3] * o[3];
+        }
+        dot[c] = lane_group_sum<16>(dot[c]);
+    }
+    if (!ok || l16 != 0) return;
     float sg[3] = {1.f, 1.f, 1.f};
     if (p.gates)
 #pragma unroll
@@ -661,7 +684,7 @@ __global__ __launch_bounds__(256) void stats_from_saved_kernel(AttnParams p) {
 
 void launch_stats_from_saved(int DV, const AttnParams& p, hipStream_t st) {
     const size_t rows = (size_t)p.B * p.T * p.Hkv * p.G;
-    const unsigned grid = (unsigned)((rows + 3) / 4);
+    const unsigned grid = (unsigned)((rows + 15) / 16);
     if (DV == 128) stats_from_saved_kernel<128><<<grid, 256, 0, st>>>(p);
     else stats_from_saved_kernel<64><<<grid, 256, 0, st>>>(p);
 }
