@@ -58,6 +58,9 @@ def lib():
                                      + [_D] * 8)
         L.oracle_nsa_bwd.restype = ctypes.c_int
         L.oracle_compress_linear_bwd.argtypes = [ctypes.c_int] * 6 + [_D] * 7
+        L.oracle_nsa_bwd_rows.argtypes = ([ctypes.c_int] * 11 + [ctypes.c_double, ctypes.c_int, _D, _I, ctypes.c_int]
+                                          + [_D] * 4 + [_I] + [_D] * 4)
+        L.oracle_nsa_bwd_rows.restype = ctypes.c_int
         L.oracle_num_threads.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -265,4 +268,27 @@ def compress_linear_bwd(X, pe, W, dY, l: int, s: int) -> dict:
     out = {"dx": np.zeros_like(X), "dw": np.zeros_like(W), "dpe": np.zeros((l, d))}
     lib().oracle_compress_linear_bwd(n_tok, d, d_out, l, s, nblk, _pd(X), _pd(pe), _pd(W), _pd(dY),
                                      _pd(out["dx"]), _pd(out["dw"]), _pd(out["dpe"]))
+    return out
+
+
+def nsa_bwd_rows(cfg, Q_rows, rows, K, V, Kc, Vc, sel_rows, gates_rows, dO_rows, branches=None) -> dict:
+    """dq and the gate-logit gradients of listed rows of one batch element (the query side of
+    nsa_bwd).  Q_rows [nrows,H,dk], sel_rows [nrows,Hkv,top_n], gates_rows [nrows,H,3] or
+    None, dO_rows [nrows,H,dv]; K, V, Kc, Vc as for nsa_bwd.  Returns dict(dq, dgates)."""
+    Hkv, G = cfg.num_kv_heads, cfg.heads_per_group
+    branches = cfg.branches if branches is None else branches
+    Q_rows, K, V, dO_rows = _d(Q_rows), _d(K), _d(V), _d(dO_rows)
+    rows, sel_rows = _i(rows), _i(sel_rows)
+    use_c = bool(branches & 1)
+    Kc = _d(Kc) if use_c else None
+    Vc = _d(Vc) if use_c else None
+    gates_rows = None if gates_rows is None else _d(gates_rows)
+    out = {"dq": np.zeros_like(Q_rows),
+           "dgates": None if gates_rows is None else np.zeros_like(gates_rows)}
+    rc = lib().oracle_nsa_bwd_rows(Hkv, G, cfg.d_k, cfg.d_v, K.shape[1], Kc.shape[1] if use_c else 0, cfg.cmp_block,
+                                   cfg.cmp_stride, cfg.slc_block, sel_rows.shape[-1], cfg.window, float(cfg.scale),
+                                   branches, _pd(Q_rows), _pi(rows), rows.size, _pd(K), _pd(V), _pd(Kc), _pd(Vc),
+                                   _pi(sel_rows), _pd(gates_rows), _pd(dO_rows), _pd(out["dq"]), _pd(out["dgates"]))
+    if rc != 0:
+        raise MemoryError("oracle_nsa_bwd_rows failed")
     return out

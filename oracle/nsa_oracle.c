@@ -463,7 +463,8 @@ ORACLE_API void oracle_causal_attention_rows(int nrows, const int* rows, int dk,
  */
 
 /* Backward of one attention over an explicit key list (indices into K / V).  Adds into
- * dq [dk], dK, dV (rows indexed like K, V).  Returns <dout, o>, o recomputed here. */
+ * dq [dk], dK, dV (rows indexed like K, V; both NULL: the key side is skipped).  Returns
+ * <dout, o>, o recomputed here. */
 static double attend_list_bwd(const double* q, const double* K, const double* V, int dk, int dv, double scale,
                               const int* keys, int nk, const double* dout, double sig,
                               double* logit, double* p, double* o,
@@ -484,10 +485,9 @@ static double attend_list_bwd(const double* q, const double* K, const double* V,
     for (int c = 0; c < nk; ++c) {
         const int x = keys[c];
         const double da = p[c] * (logit[c] - pdp);
-        for (int e = 0; e < dk; ++e) {
-            dq[e] += scale * da * K[(size_t)x * dk + e];
-            dK[(size_t)x * dk + e] += scale * da * q[e];
-        }
+        for (int e = 0; e < dk; ++e) dq[e] += scale * da * K[(size_t)x * dk + e];
+        if (!dK) continue;
+        for (int e = 0; e < dk; ++e) dK[(size_t)x * dk + e] += scale * da * q[e];
         for (int e = 0; e < dv; ++e) dV[(size_t)x * dv + e] += p[c] * sig * dout[e];
     }
     return dot(dout, o, dv);
@@ -583,6 +583,76 @@ ORACLE_API int oracle_nsa_bwd(int H_kv, int G, int dk, int dv, int n_tok, int n_
             }
         }
         free(tK); free(tV); free(tKc); free(tVc); free(keys); free(logit); free(p); free(o);
+    }
+    return bad ? -2 : 0;
+}
+
+/* The query-side part of oracle_nsa_bwd for listed rows only (dq and the gate-logit
+ * gradients; the key side is not formed), so that rows of a long sequence can be checked one
+ * by one.  Q_rows [nrows, H, dk], sel_rows [nrows, H_kv, top_n], gates_rows [nrows, H, 3] or
+ * NULL, dO_rows [nrows, H, dv]; K, V, Kc, Vc as for oracle_nsa_bwd; dQ_rows [nrows, H, dk],
+ * dgates_rows [nrows, H, 3] or NULL (overwritten).  Returns 0, or -2 when memory runs out. */
+ORACLE_API int oracle_nsa_bwd_rows(int H_kv, int G, int dk, int dv, int n_tok, int n_cmp, int l, int s, int lp,
+                                   int top_n, int window, double scale, int branches,
+                                   const double* Q_rows, const int* rows, int nrows,
+                                   const double* K, const double* V, const double* Kc, const double* Vc,
+                                   const int* sel_rows, const double* gates_rows, const double* dO_rows,
+                                   double* dQ_rows, double* dgates_rows)
+{
+    const int H = H_kv * G;
+    int bad = 0;
+    memset(dQ_rows, 0, sizeof(double) * (size_t)nrows * H * dk);
+    if (dgates_rows) memset(dgates_rows, 0, sizeof(double) * (size_t)nrows * H * 3);
+#pragma omp parallel for schedule(dynamic) reduction(|: bad)
+    for (int rh = 0; rh < nrows * H; ++rh) {
+        const int r = rh / H, h = rh % H, g = h / G, t = rows[r];
+        const int cap = n_cmp + top_n * lp + window + 1;
+        int* keys = (int*)malloc(sizeof(int) * (size_t)cap);
+        double* logit = (double*)malloc(sizeof(double) * (size_t)cap);
+        double* p = (double*)malloc(sizeof(double) * (size_t)cap);
+        double* o = (double*)malloc(sizeof(double) * (size_t)dv);
+        if (!keys || !logit || !p || !o) { bad = 1; goto done; }
+        {
+            const double* q = Q_rows + (size_t)rh * dk;
+            const double* dout = dO_rows + (size_t)rh * dv;
+            double* dq = dQ_rows + (size_t)rh * dk;
+            const double* z = gates_rows ? gates_rows + (size_t)rh * 3 : NULL;
+            double sig[3], od[3] = {0.0, 0.0, 0.0};
+            for (int c = 0; c < 3; ++c) sig[c] = z ? sigmoid(z[c]) : 1.0;
+            const size_t kg = (size_t)g * n_tok, cg = (size_t)g * n_cmp;
+            if (branches & 1) {
+                const int nk = visible_cmp(t, l, s, n_cmp);
+                for (int i = 0; i < nk; ++i) keys[i] = i;
+                od[0] = attend_list_bwd(q, Kc + cg * dk, Vc + cg * dv, dk, dv, scale, keys, nk, dout, sig[0],
+                                        logit, p, o, dq, NULL, NULL);
+            }
+            if (branches & 2) {
+                int nk = 0;
+                const int* sl = sel_rows + ((size_t)r * H_kv + g) * top_n;
+                for (int c = 0; c < top_n; ++c) {
+                    const int j = sl[c];
+                    if (j < 0) continue;
+                    int dup = 0;
+                    for (int c2 = 0; c2 < c; ++c2) dup |= (sl[c2] == j);
+                    if (dup) continue;
+                    for (int x = j * lp; x < (j + 1) * lp && x <= t; ++x) keys[nk++] = x;
+                }
+                od[1] = attend_list_bwd(q, K + kg * dk, V + kg * dv, dk, dv, scale, keys, nk, dout, sig[1],
+                                        logit, p, o, dq, NULL, NULL);
+            }
+            if (branches & 4) {
+                int nk = 0;
+                const int t0 = (t - window + 1) > 0 ? (t - window + 1) : 0;
+                for (int x = t0; x <= t && window > 0; ++x) keys[nk++] = x;
+                od[2] = attend_list_bwd(q, K + kg * dk, V + kg * dv, dk, dv, scale, keys, nk, dout, sig[2],
+                                        logit, p, o, dq, NULL, NULL);
+            }
+            if (dgates_rows)
+                for (int c = 0; c < 3; ++c)
+                    if (branches & (1 << c)) dgates_rows[(size_t)rh * 3 + c] = sig[c] * (1.0 - sig[c]) * od[c];
+        }
+    done:
+        free(keys); free(logit); free(p); free(o);
     }
     return bad ? -2 : 0;
 }

@@ -17,8 +17,9 @@ import torch
 
 import oracle
 from dynamic_block_sparse_nsa_amd import inputs, ops
-from dynamic_block_sparse_nsa_amd.configs import TINY, BR_ALL, BR_CMP, BR_SLC, BR_WIN, PHI_MEAN, SCORE_MEAN_DOT
-from nsa_testlib import bf16_dev_to_f64, check_close, dev_bf16, OUT_ATOL, OUT_REL_L2
+from dynamic_block_sparse_nsa_amd.configs import (TINY, P8K, P64K, BR_ALL, BR_CMP, BR_SLC, BR_WIN, PHI_MEAN,
+                                                  SCORE_MEAN_DOT)
+from nsa_testlib import bf16_dev_to_f64, check_close, dev_bf16, sample_rows, OUT_ATOL, OUT_REL_L2
 
 pytestmark = pytest.mark.gpu
 
@@ -191,3 +192,51 @@ def test_training_forward_saves_branch_outputs(cfg):
             a = cfg.scale * (kk[g, max(0, t - cfg.window + 1):t + 1] @ qq[t, h])
             ref_lse2 = (a.max() + np.log(np.exp(a - a.max()).sum())) / np.log(2.0)
             assert abs(sl[t, h, 1] - ref_lse2) <= 1e-4 * max(1.0, abs(ref_lse2)), (t, h, sl[t, h, 1], ref_lse2)
+
+
+@pytest.mark.parametrize("cfg", [P8K, P64K], ids=lambda c: c.name)
+def test_backward_full_size(cfg):
+    """The 8K and 64K workloads in the benchmark's configuration (training forward, backward
+    on the saved statistics): dQ and the gate gradients on sampled rows against the oracle,
+    computed row by row; the key-side gradients through identities that hold at any size
+    (every branch's probabilities of a row sum to one):
+        sum over keys of dV  = sum over the group's (token, head) rows of sigma_c dO   (per branch
+                               group: raw keys carry the selected + window branches, compressed
+                               keys the compressed branch, counted for rows that see one)
+        sum over keys of dK  = 0   (each row's dS sums to zero)."""
+    print(f"[case] backward {cfg.name} full size", flush=True)
+    inp = inputs.prefill_inputs(cfg)
+    dO_bits = inputs.grad_output(cfg)
+    q, k, v = dev_bf16(inp["q"]), dev_bf16(inp["k"]), dev_bf16(inp["v"])
+    wk, wv, pk, pv = (dev_bf16(inp[n]) for n in ("w_k", "w_v", "pe_k", "pe_v"))
+    gates = torch.as_tensor(inp["gates"], device="cuda")
+    fwd = ops.prefill(cfg, q, k, v, wk, wv, pk, pv, gates, train=True)
+    g = ops.sparse_attn_bwd(cfg, q, k, v, fwd["k_cmp"], fwd["v_cmp"], fwd["sel"], fwd["lse"], fwd["o_cmp"], gates,
+                            dev_bf16(dO_bits), saved_lse=fwd["saved_lse"], saved_o=fwd["saved_o"])
+    torch.cuda.synchronize()
+    rows = sample_rows(cfg.seq_len, 24, 11)
+    kc, vc = bf16_dev_to_f64(fwd["k_cmp"][0]), bf16_dev_to_f64(fwd["v_cmp"][0])
+    ref = oracle.nsa_bwd_rows(cfg, f64(inp["q"][0, rows]), rows, f64(inp["k"][0]), f64(inp["v"][0]), kc, vc,
+                              fwd["sel"][0, rows].cpu().numpy(), inp["gates"][0, rows].astype(np.float64),
+                              f64(dO_bits[0, rows]))
+    check_grad(g["dq"][0, rows].cpu().numpy(), ref["dq"], f"{cfg.name} dQ sampled rows")
+    check_grad(g["dgates"][0, rows].cpu().numpy(), ref["dgates"], f"{cfg.name} dgates sampled rows")
+    # identities, per KV group
+    G, T, l = cfg.heads_per_group, cfg.seq_len, cfg.cmp_block
+    sig = 1.0 / (1.0 + np.exp(-inp["gates"][0].astype(np.float64)))      # [T, H, 3]
+    dO = inputs.bf16_bits_to_f32(dO_bits[0]).astype(np.float64)         # [T, H, dv]
+    seen = (np.arange(T) >= l - 1)[:, None]
+    for grp in range(cfg.num_kv_heads):
+        hs = slice(grp * G, (grp + 1) * G)
+        want_raw = np.einsum("th,thd->d", sig[:, hs, 1] + sig[:, hs, 2], dO[:, hs])
+        want_cmp = np.einsum("th,thd->d", sig[:, hs, 0] * seen, dO[:, hs])
+        for name, got, want in (("dV", g["dv"][0, grp], want_raw), ("dV_cmp", g["dv_cmp"][0, grp], want_cmp)):
+            s = got.double().sum(0).cpu().numpy()
+            err = np.linalg.norm(s - want) / np.linalg.norm(want)
+            print(f"[parity] {cfg.name} group {grp} sum of {name} over keys: rel err {err:.3e}", flush=True)
+            assert err <= 5e-3, (name, grp, err)
+        for name, got in (("dK", g["dk"][0, grp]), ("dK_cmp", g["dk_cmp"][0, grp])):
+            gd = got.double()
+            rel = (gd.sum(0).norm() / gd.norm()).item()
+            print(f"[parity] {cfg.name} group {grp} sum of {name} over keys / Frobenius norm: {rel:.3e}", flush=True)
+            assert rel <= 1e-2, (name, grp, rel)

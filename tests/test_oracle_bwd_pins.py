@@ -160,3 +160,16 @@ def test_select_all_equals_dense_causal_autograd():
     np.testing.assert_allclose(g["dq"], Q.grad.numpy(), rtol=1e-10, atol=1e-12)
     np.testing.assert_allclose(g["dk"], K.grad.numpy(), rtol=1e-10, atol=1e-12)
     np.testing.assert_allclose(g["dv"], V.grad.numpy(), rtol=1e-10, atol=1e-12)
+
+
+def test_rows_variant_equals_full_backward():
+    """oracle.nsa_bwd_rows (the query side for listed rows, used at sizes where the full
+    backward is too slow) gives exactly the full backward's dq and gate gradients; the full
+    backward is the one pinned above."""
+    c = case(BW, 5)
+    g = oracle.nsa_bwd(BW, c["Q"], c["K"], c["V"], c["Kc"], c["Vc"], c["sel"], c["gates"], c["dO"])
+    rows = np.array([0, 3, 7, 31, 64, 100, 149])
+    r = oracle.nsa_bwd_rows(BW, c["Q"][rows], rows, c["K"], c["V"], c["Kc"], c["Vc"], c["sel"][rows],
+                            c["gates"][rows], c["dO"][rows])
+    np.testing.assert_allclose(r["dq"], g["dq"][rows], rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(r["dgates"], g["dgates"][rows], rtol=1e-12, atol=1e-13)
