@@ -693,7 +693,7 @@ nsa_status nsa_sparse_attn_bwd(const nsa_config* cfg, const void* Q, const void*
         n_slc_items = (long long)nsa::moba_max_tiles((int)bg, s.T, s.n, s.n_slc) * p.nsb;
     }
     // 4. dK, dV, dK_cmp, dV_cmp
-    const int dense_keys = 16 * nsa::kDkvWavesDense;
+    const int dense_keys = 16 * nsa::kDkvWavesDense * nsa::kDkvTilesDense;
     p.qt_cmp = nsa::kBwdCmpTile;
     p.n_qt = (s.T + p.qt_cmp - 1) / p.qt_cmp;
     p.n_kb_cmp = cmp ? (s.n_cmp + dense_keys - 1) / dense_keys : 0;

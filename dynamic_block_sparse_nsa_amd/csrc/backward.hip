@@ -362,11 +362,14 @@ struct PairStage {   // Q and dO rows of two tokens (32 head rows) and their sta
     }
 };
 
-template <int DK, int DV, int NW>
-__global__ __launch_bounds__(64 * NW, 8 / NW) void bwd_dkv_kernel(BwdParams p, int item0) {
+// KT key tiles of 16 per wave: each Q / dO operand read from LDS feeds KT products, so the
+// LDS traffic per key falls by KT (with KT = 2 a wave needs more than 256 registers: one
+// wave per SIMD).
+template <int DK, int DV, int NW, int KT>
+__global__ __launch_bounds__(64 * NW, KT == 1 ? 8 / NW : 1) void bwd_dkv_kernel(BwdParams p, int item0) {
     constexpr int NDS = DK / 32, NDD = DV / 32, NDK = DK / 16, NDV = DV / 16;
     constexpr int QSTR = DK + 16, OSTR = DV + 16;
-    constexpr int KEYS = 16 * NW;
+    constexpr int KEYS = 16 * NW * KT;
     __shared__ __attribute__((aligned(16))) u16 qs[32 * QSTR];   // rows: token A heads, token B heads
     __shared__ __attribute__((aligned(16))) u16 os[32 * OSTR];
     __shared__ __attribute__((aligned(16))) float rs[32 * 4];   // lse2, D, sigma per row
@@ -426,20 +429,33 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void bwd_dkv_kernel(BwdParams p, i
     const int nrows = kind == 0 ? p.N : p.T;
     const u16* Kb = kind == 0 ? p.Kc + (size_t)bg * p.N * DK : p.K + (size_t)bg * p.T * DK;
     const u16* Vb = kind == 0 ? p.Vc + (size_t)bg * p.N * DV : p.V + (size_t)bg * p.T * DV;
-    const int key = kbase + 16 * wave + li;
-    const bool key_ok = key < kend && key < nrows;
+    int key[KT];
+    bool key_ok[KT];
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt) {
+        key[kt] = kbase + 16 * (wave * KT + kt) + li;
+        key_ok[kt] = key[kt] < kend && key[kt] < nrows;
+    }
 
-    // this lane's key row as the B operand of Q.K^T and dO.V^T
-    bf16x8 kfr[NDS], vfr[NDD];
+    // this lane's key rows as the B operands of Q.K^T and dO.V^T
+    bf16x8 kfr[KT][NDS], vfr[KT][NDD];
 #pragma unroll
-    for (int ds = 0; ds < NDS; ++ds) kfr[ds] = key_ok ? ld8(Kb + (size_t)key * DK + 32 * ds + 8 * lq) : zero8();
+    for (int kt = 0; kt < KT; ++kt) {
 #pragma unroll
-    for (int dd = 0; dd < NDD; ++dd) vfr[dd] = key_ok ? ld8(Vb + (size_t)key * DV + 32 * dd + 8 * lq) : zero8();
-    f32x4 dk_acc[NDK], dv_acc[NDV];
+        for (int ds = 0; ds < NDS; ++ds)
+            kfr[kt][ds] = key_ok[kt] ? ld8(Kb + (size_t)key[kt] * DK + 32 * ds + 8 * lq) : zero8();
 #pragma unroll
-    for (int dt = 0; dt < NDK; ++dt) dk_acc[dt] = zero4();
+        for (int dd = 0; dd < NDD; ++dd)
+            vfr[kt][dd] = key_ok[kt] ? ld8(Vb + (size_t)key[kt] * DV + 32 * dd + 8 * lq) : zero8();
+    }
+    f32x4 dk_acc[KT][NDK], dv_acc[KT][NDV];
 #pragma unroll
-    for (int dt = 0; dt < NDV; ++dt) dv_acc[dt] = zero4();
+    for (int kt = 0; kt < KT; ++kt) {
+#pragma unroll
+        for (int dt = 0; dt < NDK; ++dt) dk_acc[kt][dt] = zero4();
+#pragma unroll
+        for (int dt = 0; dt < NDV; ++dt) dv_acc[kt][dt] = zero4();
+    }
 
     PairStage<DK, DV, NW> stage;
     stage.load(p, b, g, kind, tok(0), tok(1));
@@ -450,54 +466,81 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void bwd_dkv_kernel(BwdParams p, i
         __syncthreads();
         stage.load(p, b, g, kind, tok(i + 2), tok(i + 3));   // in flight during this pair's math
         // S = Q.K^T and dP = dO.V^T: C lane (li = key, lq) holds head rows 4 lq + r
-        f32x4 sA = zero4(), sB = zero4(), pA = zero4(), pB = zero4();
+        f32x4 sA[KT], sB[KT], pA[KT], pB[KT];
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt) sA[kt] = sB[kt] = pA[kt] = pB[kt] = zero4();
 #pragma unroll
         for (int ds = 0; ds < NDS; ++ds) {
-            sA = mfma16(ld8(&qs[li * QSTR + 32 * ds + 8 * lq]), kfr[ds], sA);
-            sB = mfma16(ld8(&qs[(16 + li) * QSTR + 32 * ds + 8 * lq]), kfr[ds], sB);
+            const bf16x8 qa = ld8(&qs[li * QSTR + 32 * ds + 8 * lq]);
+            const bf16x8 qb = ld8(&qs[(16 + li) * QSTR + 32 * ds + 8 * lq]);
+#pragma unroll
+            for (int kt = 0; kt < KT; ++kt) {
+                sA[kt] = mfma16(qa, kfr[kt][ds], sA[kt]);
+                sB[kt] = mfma16(qb, kfr[kt][ds], sB[kt]);
+            }
         }
 #pragma unroll
         for (int dd = 0; dd < NDD; ++dd) {
-            pA = mfma16(ld8(&os[li * OSTR + 32 * dd + 8 * lq]), vfr[dd], pA);
-            pB = mfma16(ld8(&os[(16 + li) * OSTR + 32 * dd + 8 * lq]), vfr[dd], pB);
+            const bf16x8 oa = ld8(&os[li * OSTR + 32 * dd + 8 * lq]);
+            const bf16x8 ob = ld8(&os[(16 + li) * OSTR + 32 * dd + 8 * lq]);
+#pragma unroll
+            for (int kt = 0; kt < KT; ++kt) {
+                pA[kt] = mfma16(oa, vfr[kt][dd], pA[kt]);
+                pB[kt] = mfma16(ob, vfr[kt][dd], pB[kt]);
+            }
         }
-        const bool vA = key_ok && bwd_visible(p, kind, key, tA);
-        const bool vB = key_ok && bwd_visible(p, kind, key, tB);
-        f32x4 wA, wB, gA, gB;
+        bf16x8 w8[KT], g8[KT];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int hr = 4 * lq + r;
-            const f32x4 stA = *reinterpret_cast<const f32x4*>(&rs[hr * 4]);
-            const f32x4 stB = *reinterpret_cast<const f32x4*>(&rs[(16 + hr) * 4]);
-            const float PA = (vA && hr < G) ? fast_exp2(sA[r] * p.scale_log2 - stA[0]) : 0.f;
-            const float PB = (vB && hr < G) ? fast_exp2(sB[r] * p.scale_log2 - stB[0]) : 0.f;
-            wA[r] = stA[2] * PA;
-            wB[r] = stB[2] * PB;
-            gA[r] = PA * (stA[2] * pA[r] - stA[1]);
-            gB[r] = PB * (stB[2] * pB[r] - stB[1]);
+        for (int kt = 0; kt < KT; ++kt) {
+            const bool vA = key_ok[kt] && bwd_visible(p, kind, key[kt], tA);
+            const bool vB = key_ok[kt] && bwd_visible(p, kind, key[kt], tB);
+            f32x4 wA, wB, gA, gB;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int hr = 4 * lq + r;
+                const f32x4 stA = *reinterpret_cast<const f32x4*>(&rs[hr * 4]);
+                const f32x4 stB = *reinterpret_cast<const f32x4*>(&rs[(16 + hr) * 4]);
+                const float PA = (vA && hr < G) ? fast_exp2(sA[kt][r] * p.scale_log2 - stA[0]) : 0.f;
+                const float PB = (vB && hr < G) ? fast_exp2(sB[kt][r] * p.scale_log2 - stB[0]) : 0.f;
+                wA[r] = stA[2] * PA;
+                wB[r] = stB[2] * PB;
+                gA[r] = PA * (stA[2] * pA[kt][r] - stA[1]);
+                gB[r] = PB * (stB[2] * pB[kt][r] - stB[1]);
+            }
+            // sigma P and dS as single bf16 values; the row slots of pack_p (head rows
+            // 4lq..4lq+3 of token A, then of token B) match the transposing read's key order
+            w8[kt] = pack_p(wA, wB);
+            g8[kt] = pack_p(gA, gB);
         }
-        // dV^T += dO^T . (sigma P) and dK^T += Q^T . dS with sigma P and dS as single bf16
-        // values; the row slots of pack_p (head rows 4lq..4lq+3 of token A, then of token B)
-        // match the transposing read's key order
-        const bf16x8 w8 = pack_p(wA, wB);
+        // dV^T += dO^T . (sigma P) and dK^T += Q^T . dS
 #pragma unroll
-        for (int dt = 0; dt < NDV; ++dt) dv_acc[dt] = mfma16(ld_vt_tr(os, OSTR, 0, 16 * dt), w8, dv_acc[dt]);
-        const bf16x8 g8 = pack_p(gA, gB);
+        for (int dt = 0; dt < NDV; ++dt) {
+            const bf16x8 a = ld_vt_tr(os, OSTR, 0, 16 * dt);
 #pragma unroll
-        for (int dt = 0; dt < NDK; ++dt) dk_acc[dt] = mfma16(ld_vt_tr(qs, QSTR, 0, 16 * dt), g8, dk_acc[dt]);
+            for (int kt = 0; kt < KT; ++kt) dv_acc[kt][dt] = mfma16(a, w8[kt], dv_acc[kt][dt]);
+        }
+#pragma unroll
+        for (int dt = 0; dt < NDK; ++dt) {
+            const bf16x8 a = ld_vt_tr(qs, QSTR, 0, 16 * dt);
+#pragma unroll
+            for (int kt = 0; kt < KT; ++kt) dk_acc[kt][dt] = mfma16(a, g8[kt], dk_acc[kt][dt]);
+        }
     }
-    if (!key_ok) return;
     // C layout of dK^T / dV^T: lane (li = key, lq) holds dims 16 dt + 4 lq + r
-    float* dKr = (kind == 0 ? p.dKc + (size_t)bg * p.N * DK : p.dK + (size_t)bg * p.T * DK) + (size_t)key * DK;
-    float* dVr = (kind == 0 ? p.dVc + (size_t)bg * p.N * DV : p.dV + (size_t)bg * p.T * DV) + (size_t)key * DV;
 #pragma unroll
-    for (int dt = 0; dt < NDK; ++dt)
+    for (int kt = 0; kt < KT; ++kt) {
+        if (!key_ok[kt]) continue;
+        float* dKr = (kind == 0 ? p.dKc + (size_t)bg * p.N * DK : p.dK + (size_t)bg * p.T * DK) + (size_t)key[kt] * DK;
+        float* dVr = (kind == 0 ? p.dVc + (size_t)bg * p.N * DV : p.dV + (size_t)bg * p.T * DV) + (size_t)key[kt] * DV;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) unsafeAtomicAdd(dKr + 16 * dt + 4 * lq + r, dk_acc[dt][r] * p.scale);
+        for (int dt = 0; dt < NDK; ++dt)
 #pragma unroll
-    for (int dt = 0; dt < NDV; ++dt)
+            for (int r = 0; r < 4; ++r) unsafeAtomicAdd(dKr + 16 * dt + 4 * lq + r, dk_acc[kt][dt][r] * p.scale);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) unsafeAtomicAdd(dVr + 16 * dt + 4 * lq + r, dv_acc[dt][r]);
+        for (int dt = 0; dt < NDV; ++dt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) unsafeAtomicAdd(dVr + 16 * dt + 4 * lq + r, dv_acc[kt][dt][r]);
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -713,20 +756,21 @@ bool launch_bwd_dq(int DK, int DV, const BwdParams& p, hipStream_t st) {
     return true;
 }
 
-template <int NW>
+template <int NW, int KT>
 bool launch_dkv_nw(int DK, int DV, const BwdParams& p, int item0, int n, hipStream_t st) {
     if (n <= 0) return true;
-    if (DK == 192 && DV == 128) bwd_dkv_kernel<192, 128, NW><<<n, 64 * NW, 0, st>>>(p, item0);
-    else if (DK == 128 && DV == 128) bwd_dkv_kernel<128, 128, NW><<<n, 64 * NW, 0, st>>>(p, item0);
-    else if (DK == 64 && DV == 64) bwd_dkv_kernel<64, 64, NW><<<n, 64 * NW, 0, st>>>(p, item0);
+    if (DK == 192 && DV == 128) bwd_dkv_kernel<192, 128, NW, KT><<<n, 64 * NW, 0, st>>>(p, item0);
+    else if (DK == 128 && DV == 128) bwd_dkv_kernel<128, 128, NW, KT><<<n, 64 * NW, 0, st>>>(p, item0);
+    else if (DK == 64 && DV == 64) bwd_dkv_kernel<64, 64, NW, KT><<<n, 64 * NW, 0, st>>>(p, item0);
     else return false;
     return true;
 }
 
-// compressed and window items: 128 keys (8 waves); selected items: 64 keys (4 waves)
+// compressed and window items: kDkvWavesDense waves x kDkvTilesDense key tiles; selected
+// items: 64 keys (4 waves x 1 tile)
 bool launch_bwd_dkv(int DK, int DV, const BwdParams& p, int n_slc_items, hipStream_t st) {
-    return launch_dkv_nw<kDkvWavesDense>(DK, DV, p, 0, p.n_cmp_items + p.n_win_items, st) &&
-           launch_dkv_nw<kDkvWavesSlc>(DK, DV, p, p.n_cmp_items + p.n_win_items, n_slc_items, st);
+    return launch_dkv_nw<kDkvWavesDense, kDkvTilesDense>(DK, DV, p, 0, p.n_cmp_items + p.n_win_items, st) &&
+           launch_dkv_nw<kDkvWavesSlc, 1>(DK, DV, p, p.n_cmp_items + p.n_win_items, n_slc_items, st);
 }
 
 void launch_compress_bwd(const u16* X, const u16* W, const u16* pe, const float* dY, float* dX, float* dW, float* dpe,

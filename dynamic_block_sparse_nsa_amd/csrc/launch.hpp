@@ -114,7 +114,9 @@ bool launch_moba_attn(int DK, int DV, const MobaParams& p, hipStream_t st);
 // ---- backward ----
 constexpr int kBwdTile = 128;   // query tokens per dK/dV work item (= the block lists' tile)
 constexpr int kBwdCmpTile = 512;   // query tokens per compressed-branch dK/dV work item
-constexpr int kDkvWavesDense = 8;  // compressed / window items: 128 keys per workgroup
+constexpr int kDkvWavesDense = 8;  // compressed / window items: 8 waves x 1 key tile = 128 keys
+constexpr int kDkvTilesDense = 1;  // (4 waves x 2 tiles halves the LDS reads per key but runs
+                                   // one wave per SIMD: 34 ms against 24.5 ms at 64K)
 constexpr int kDkvWavesSlc = 4;    // selected items: 64 keys per workgroup
 struct BwdParams {
     const u16* Q;              // [B,T,H,DK]

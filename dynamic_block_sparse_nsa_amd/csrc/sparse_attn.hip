@@ -197,13 +197,15 @@ __global__ __launch_bounds__(256) void tile_kv_kernel(const u16* __restrict__ K,
 
 }  // namespace
 
-// STATS: the backward pass's statistics instead of the gated output.  Per (token, head)
-// and branch c: lse2_c = log2 of the branch's sum of exp2(scaled scores), D_c =
-// sigma_c <dO, o_c> and sigma_c (1 without gates); dgates = (1 - sigma_c) D_c, the gate
-// logit's gradient sigma (1 - sigma) <dO, o_c>.  The compressed branch takes its LSE and
-// o_cmp from the caller.
-template <int DK, int DV, bool STATS = false>
+// MODE 0: the forward.  MODE 2: the forward that also saves, for the backward, the selected
+// and window branches' base-2 LSE and normalized outputs (training forward).  MODE 1: the
+// backward pass's statistics instead of the gated output: per (token, head) and branch c,
+// lse2_c = log2 of the branch's sum of exp2(scaled scores), D_c = sigma_c <dO, o_c> and
+// sigma_c (1 without gates); dgates = (1 - sigma_c) D_c, the gate logit's gradient
+// sigma (1 - sigma) <dO, o_c>.  The compressed branch takes its LSE and o_cmp from the caller.
+template <int DK, int DV, int MODE = 0>
 __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnParams p) {
+    constexpr bool STATS = MODE == 1, SAVE = MODE == 2;
     constexpr int NDS = DK / 32;
     constexpr int NDT = DV / 16;
     using Tile = WinTile<DK, DV>;
@@ -382,7 +384,7 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnParams p) {
 
     float gc = 1.f, gs = 1.f, gw = 1.f;
     const size_t row = ((size_t)b * T + t) * H + h;
-    if (p.saved_o) {   // training forward: what the backward needs of the two branches
+    if constexpr (SAVE) {   // training forward: what the backward needs of the two branches
         if (lq == 0)
             *reinterpret_cast<float2*>(p.saved_lse + row * 2) =
                 float2{use_slc ? slc.m + __log2f(Ls) : 0.f, use_win ? win.m + __log2f(Lw) : 0.f};
@@ -421,9 +423,9 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnParams p) {
 
 bool launch_sparse_attn_stats(int DK, int DV, const AttnParams& p, hipStream_t st) {
     const int grid = xcd_grid(p.B * p.Hkv, (p.T + kTok - 1) / kTok);
-    if (DK == 192 && DV == 128) sparse_attn_kernel<192, 128, true><<<grid, 256, 0, st>>>(p);
-    else if (DK == 128 && DV == 128) sparse_attn_kernel<128, 128, true><<<grid, 256, 0, st>>>(p);
-    else if (DK == 64 && DV == 64) sparse_attn_kernel<64, 64, true><<<grid, 256, 0, st>>>(p);
+    if (DK == 192 && DV == 128) sparse_attn_kernel<192, 128, 1><<<grid, 256, 0, st>>>(p);
+    else if (DK == 128 && DV == 128) sparse_attn_kernel<128, 128, 1><<<grid, 256, 0, st>>>(p);
+    else if (DK == 64 && DV == 64) sparse_attn_kernel<64, 64, 1><<<grid, 256, 0, st>>>(p);
     else return false;
     return true;
 }
@@ -441,6 +443,13 @@ bool launch_tile_kv(int DK, int DV, const u16* K, const u16* V, u16* Kf, u16* Vf
 bool launch_sparse_attn(int DK, int DV, const AttnParams& p, int B, hipStream_t st) {
     (void)B;
     const int grid = xcd_grid(p.B * p.Hkv, (p.T + kTok - 1) / kTok);
+    if (p.saved_o) {
+        if (DK == 192 && DV == 128) sparse_attn_kernel<192, 128, 2><<<grid, 256, 0, st>>>(p);
+        else if (DK == 128 && DV == 128) sparse_attn_kernel<128, 128, 2><<<grid, 256, 0, st>>>(p);
+        else if (DK == 64 && DV == 64) sparse_attn_kernel<64, 64, 2><<<grid, 256, 0, st>>>(p);
+        else return false;
+        return true;
+    }
     if (DK == 192 && DV == 128) sparse_attn_kernel<192, 128><<<grid, 256, 0, st>>>(p);
     else if (DK == 128 && DV == 128) sparse_attn_kernel<128, 128><<<grid, 256, 0, st>>>(p);
     else if (DK == 64 && DV == 64) sparse_attn_kernel<64, 64><<<grid, 256, 0, st>>>(p);
