@@ -245,3 +245,69 @@ def test_block_lists_structure():
         assert (row[len(valid):] == -1).all()
         if jc >= 1:
             assert jc - 1 in valid
+
+
+def test_backward_validation():
+    """nsa_sparse_attn_bwd, nsa_sparse_attn_fwd_train and nsa_compress_bwd reject missing
+    pointers, a lone saved buffer, misalignment, a small workspace and the mean block map
+    before launching anything."""
+    L = ops.lib()
+    fake = ctypes.c_void_p(0x1000)
+    odd = ctypes.c_void_p(0x1004)
+    big = 1 << 40
+    for op in (ops.OP_SPARSE_BWD, ops.OP_COMPRESS_BWD):
+        rc, n = _ws(P8K, op)
+        assert rc == 0 and n > 0
+    ws_ok = ctypes.c_void_p(0x100000)
+
+    def bwd(**over):
+        a = dict(Q=fake, K=fake, V=fake, Kc=fake, Vc=fake, sel=fake, lse=fake, ocmp=fake, gates=fake, slse=None,
+                 so=None, dO=fake, dQ=fake, dK=fake, dV=fake, dKc=fake, dVc=fake, dg=fake, ws=ws_ok, nws=big)
+        a.update(over)
+        cfg = a.pop("cfg", _cfg())
+        return L.nsa_sparse_attn_bwd(cfg, a["Q"], a["K"], a["V"], a["Kc"], a["Vc"], a["sel"], a["lse"], a["ocmp"],
+                                     a["gates"], a["slse"], a["so"], a["dO"], a["dQ"], a["dK"], a["dV"], a["dKc"],
+                                     a["dVc"], a["dg"], a["ws"], a["nws"], None)
+
+    assert bwd(dO=None) == 1
+    assert bwd(dQ=None) == 1
+    assert bwd(sel=None) == 1                          # selected branch on
+    assert bwd(lse=None) == 1                          # compressed branch on
+    assert bwd(dKc=None) == 1
+    assert bwd(gates=None) == 1                        # d_gate_logits without gate logits
+    assert bwd(slse=fake) == 1                         # saved LSE without saved outputs
+    assert bwd(so=fake) == 1
+    assert bwd(slse=fake, so=odd) == 2                 # saved outputs misaligned
+    assert bwd(dK=odd) == 2
+    assert bwd(ws=None, nws=0) == 4
+    assert bwd(nws=16) == 4
+    assert bwd(cfg=_cfg(P8K, window=0)) == 2           # window branch with window 0
+    # with the compressed branch off, its buffers may be NULL (fails later only on the workspace)
+    assert bwd(cfg=_cfg(P8K, branches=6), Kc=None, Vc=None, lse=None, ocmp=None, dKc=None, dVc=None, nws=16) == 4
+
+    def train(**over):
+        a = dict(Q=fake, K=fake, V=fake, sel=fake, ocmp=fake, gates=None, O=fake, slse=fake, so=fake, ws=ws_ok,
+                 nws=big)
+        a.update(over)
+        return L.nsa_sparse_attn_fwd_train(_cfg(), a["Q"], a["K"], a["V"], a["sel"], a["ocmp"], a["gates"], a["O"],
+                                           a["slse"], a["so"], a["ws"], a["nws"], None)
+
+    assert train(slse=None) == 1
+    assert train(so=None) == 1
+    assert train(so=odd) == 2
+    assert train(O=None) == 1
+    assert train(nws=16) == 4
+
+    def cbwd(**over):
+        a = dict(K=fake, V=fake, wk=fake, wv=fake, pk=fake, pv=fake, dKc=fake, dVc=fake, dK=fake, dV=fake, dWk=fake,
+                 dWv=fake, dpk=fake, dpv=fake, ws=ws_ok, nws=big)
+        a.update(over)
+        cfg = a.pop("cfg", _cfg())
+        return L.nsa_compress_bwd(cfg, a["K"], a["V"], a["wk"], a["wv"], a["pk"], a["pv"], a["dKc"], a["dVc"], a["dK"],
+                                  a["dV"], a["dWk"], a["dWv"], a["dpk"], a["dpv"], a["ws"], a["nws"], None)
+
+    assert cbwd(dKc=None) == 1
+    assert cbwd(dpv=None) == 1
+    assert cbwd(dWk=odd) == 2
+    assert cbwd(nws=16) == 4
+    assert cbwd(cfg=_cfg(MOBA)) == 3
