@@ -208,6 +208,20 @@ def main():
     print("[bench] timing prefill", file=sys.stderr, flush=True)
     per_call, wall = time_calls(calls, args.steps, args.warmup, torch)
     ms = wall / args.steps * 1e3   # the K timed steps between two synchronizations
+    # cold caches: a 2 GiB write before each step evicts L2 and the memory-side cache; the
+    # step alone is timed with events (the flush is outside the pair)
+    scratch = torch.empty(1 << 29, dtype=torch.float32, device=dev)
+    cold = []
+    for _ in range(3):
+        scratch.fill_(1.0)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for f in calls:
+            f()
+        e1.record()
+        torch.cuda.synchronize()
+        cold.append(e0.elapsed_time(e1))
+    del scratch
     fl = prefill_flops(cfg)
     total_flops = sum(fl.values())
     tflops = total_flops / (ms * 1e-3) / 1e12
@@ -248,6 +262,7 @@ def main():
                    "top_n": cfg.top_n, "window": cfg.window},
         "tflops_algorithmic": round(tflops, 2),
         "mfma_peak_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "cold_ms_per_step": round(float(np.median(cold)), 4),
         "algorithmic_flops": {k: int(v) for k, v in fl.items()},
         "per_call_ms": {n: round(float(c), 4) for n, c in zip(names, call_ms)},
         "roofline": {"bound": "mfma", "kernel": dom_kernel, "call": names[dom], "call_kernels": dom_launches,
