@@ -28,8 +28,15 @@ f64 = inputs.bf16_bits_to_f64
 
 def check_grad(gpu, ref, what):
     ref = np.asarray(ref, dtype=np.float64)
-    scale = max(float(np.abs(ref).max()), 1e-30)
-    check_close(np.asarray(gpu, dtype=np.float64) / scale, ref / scale, what, atol=OUT_ATOL, rel=OUT_REL_L2)
+    gpu = np.asarray(gpu, dtype=np.float64)
+    scale = float(np.abs(ref).max())
+    if scale == 0.0:
+        # an exactly zero gradient (e.g. a single visible compressed key: its probability is 1
+        # for every row, so dS = 0): the GPU may only show rounding noise
+        print(f"[parity] {what}: reference exactly zero, GPU max abs {np.abs(gpu).max():.3e}", flush=True)
+        assert np.abs(gpu).max() <= 1e-4, what
+        return
+    check_close(gpu / scale, ref / scale, what, atol=OUT_ATOL, rel=OUT_REL_L2)
 
 
 GQA = TINY.replace(name="bwd_gqa16", num_kv_heads=2, heads_per_group=16, d_k=192, d_v=128, top_n=8, window=256,
@@ -54,6 +61,12 @@ CASES = [
     (GQA.replace(name="bwd_slc_only", branches=BR_SLC), False, False),
     (GQA.replace(name="bwd_cmp_only", branches=BR_CMP), True, False),
     (RAGGED.replace(name="bwd_win_only", branches=BR_WIN), True, True),
+    # edges: one compressed block and one selection block; a window longer than the
+    # sequence; one query head per group with all three branches
+    (TINY.replace(name="bwd_short", seq_len=40, window=16, fp32_inputs=False, seed=49), True, True),
+    (RAGGED.replace(name="bwd_wide_window", seq_len=200, window=512, seed=50), True, False),
+    (TINY.replace(name="bwd_g1", num_kv_heads=3, heads_per_group=1, seq_len=700, fp32_inputs=False, seed=51), True,
+     True),
 ]
 
 
