@@ -8,25 +8,33 @@
 // P = exp2(scaled score - lse2) recomputed from the forward's statistics:
 //   dS = P (sigma dP - D), dP = <dO, v>;   dq = tau sum_k dS k;   dk = tau dS q;   dv = sigma P dO.
 //
-// bwd_dq_kernel    one wave per (token, KV group): the group's G heads are the 16-wide MFMA
-//                  column tile (as in the forward); for each branch its keys are walked in
-//                  32-key chunks: S^T = K.Q^T and dP^T = V.dO^T on the MFMA, dS^T in
-//                  registers, dQ^T += K^T.dS^T with K^T read through the transposing LDS
-//                  read from a row-major chunk staged in LDS (dS as a bf16 high/low pair).
-// bwd_dkv_kernel   one workgroup per (64 keys, <= 128 query tokens) work item, a wave per
-//                  16 keys: the item's tokens are taken two at a time (32 head rows staged
-//                  in LDS), S = Q.K^T and dP = dO.V^T with the keys' fragments held in
-//                  registers, then dV^T += dO^T.(sigma P) and dK^T += Q^T.dS (sigma P and dS
+// stats_from_saved_kernel  the per-(token, head, branch) LSE, D and sigma, and the gate-logit
+//                  gradients, from the training forward's saved branch outputs.
+// bwd_dq_kernel    compressed and window branches, writes dQ: a workgroup owns 4 consecutive
+//                  tokens of one KV group, a wave per token with the group's G heads as the
+//                  16-wide MFMA column tile (as in the forward); 32-key chunks shared by the 4
+//                  tokens are staged once in LDS (the next chunk's loads in flight): S^T = K.Q^T
+//                  and dP^T = V.dO^T on the MFMA, dS^T in registers, dQ^T += K^T.dS^T with K^T
+//                  read through the transposing LDS read (dS as a bf16 high/low pair).
+// bwd_dq_slc_kernel  selected branch, adds into dQ: the same per-chunk math, each wave
+//                  walking its own token's selected chunks through its own LDS tile.
+// bwd_dkv_kernel   one workgroup per work item of 16 * NW * KT keys against up to 128 (512
+//                  for the compressed branch) query tokens, KT 16-key tiles per wave: the
+//                  tokens are taken two at a time (32 head rows staged in LDS, the next pair's
+//                  loads in flight), S = Q.K^T and dP = dO.V^T with the keys' fragments held
+//                  in registers, then dV^T += dO^T.(sigma P) and dK^T += Q^T.dS (sigma P and dS
 //                  as single bf16 values, fp32 sums on the MFMA, as in the usual attention
-//                  backward: about 2e-3 relative L2 on dK, dV); the item's
-//                  sums are added to the fp32 gradients with atomics.  Items: compressed
-//                  keys x 128-token query tiles (tokens that see the keys), window key
-//                  blocks x the tokens whose window covers them, and for the selected
-//                  branch a selection block x 128 of the tokens that selected it (the
-//                  inverted lists of the block-major forward, own block included).
+//                  backward: about 2e-3 relative L2 on dK, dV); the item's sums are added to
+//                  the fp32 gradients with atomics.  Items: compressed key blocks x query
+//                  tiles (tokens that see the keys), window key blocks x the tokens whose
+//                  window covers them, and for the selected branch a selection block x 128 of
+//                  the tokens that selected it (the inverted lists of the block-major forward,
+//                  own block included).
 // compress_bwd_*   the linear block map: column sums of dY, dPE = W.colsum, dW = X^T.dY
 //                  (X = block rows + PE, split over row ranges, atomics), dX = dY.W^T added
 //                  into the raw key/value gradients (a token lies in l/s blocks).  fp32 FMA.
+// Every MFMA runs under wave-uniform control flow: the instruction reads all 64 lanes'
+// operands, so padding rows (heads past G, tokens past a list) are masked in the values.
 #include <algorithm>
 
 #include "common.hpp"
@@ -35,8 +43,6 @@
 namespace nsa {
 
 namespace {
-
-constexpr int kItemKeys = 64;    // keys per dK/dV work item (4 waves x 16)
 
 // key `key` of a work item is attended by query token t in branch `kind`
 __device__ __forceinline__ bool bwd_visible(const BwdParams& p, int kind, int key, int t) {
