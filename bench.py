@@ -320,6 +320,33 @@ def main():
         del Q8, K8, V8, kc8, vc8, sel8, oc8, o8, wsf
         torch.cuda.empty_cache()
 
+    # ---------------- the selected branch with selection locality ----------------
+    # The headline inputs are random, so neighbouring tokens share no free pick.  For
+    # contrast: the same kernel on valid lists in which the 64 tokens of each selection block
+    # share their free picks (forced blocks as the rule has them), the locality trained
+    # attention tends to show.
+    rng = np.random.default_rng(cfg.seed + 77)
+    coh = np.full((T, Hkv, cfg.top_n), -1, dtype=np.int32)
+    for jc in range(cfg.n_slc):
+        t0, t1 = jc * cfg.slc_block, min((jc + 1) * cfg.slc_block, T)
+        forced = sorted(set(range(min(cfg.n_init, jc + 1))) | set(range(max(0, jc - cfg.n_local + 1), jc + 1)))
+        pool = [j for j in range(jc + 1) if j not in forced]
+        n_free = min(cfg.top_n, jc + 1) - len(forced)
+        for gg in range(Hkv):
+            picks = rng.choice(pool, n_free, replace=False).tolist() if n_free > 0 else []
+            row = sorted(forced + picks)
+            coh[t0:t1, gg, :len(row)] = row
+    sel_coh = torch.from_numpy(coh[None]).to(dev)
+    pcc, _ = time_calls([lambda: ops.sparse_attn_fwd(cfg, Q, K, V, sel_coh, ocmp, gates, out=out, workspace=ws[2])],
+                        5, 1, torch)
+    cms = float(pcc.mean())
+    result["selected_locality"] = {
+        "workload": "nsa_sparse_attn_fwd_64k_shared_picks", "ms": round(cms, 3),
+        "vs_random_picks_ms": round(float(call_ms[2]), 3),
+        "gathered_gbs": round(slc_pairs(cfg) // cfg.heads_per_group * (cfg.d_k + cfg.d_v) * 2 / (cms * 1e-3) / 1e9, 1),
+        "note": "free picks shared by the 64 tokens of each selection block"}
+    del sel_coh
+
     # ---------------- backward of the same step ----------------
     if not args.no_backward:
         print("[bench] backward", file=sys.stderr, flush=True)
