@@ -12,7 +12,7 @@ on), the oracle timed on the host cores on a bounded sample, the backward pass o
 65536-token caches, HBM GB/s) and MoBA (131072 and 1048576 tokens) figures.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-decode] [--no-moba]
-                       [--no-dense] [--no-backward]
+                       [--no-dense] [--no-backward] [--locality]
 """
 from __future__ import annotations
 
@@ -75,6 +75,35 @@ def backward_flops(cfg: NSAConfig) -> dict:
 
 
 # ---------------------------------------------------------------------------
+def locality(cfg, Q, K, V, ocmp, gates, out, ws, call_ms, result, time_calls, torch, dev):
+    """The headline inputs are random, so neighbouring tokens share no free pick.  For
+    contrast: the same kernel on valid lists in which the 64 tokens of each selection block
+    share their free picks (forced blocks as the rule has them), the locality trained
+    attention tends to show."""
+    from dynamic_block_sparse_nsa_amd import ops
+    T, Hkv = cfg.seq_len, cfg.num_kv_heads
+    rng = np.random.default_rng(cfg.seed + 77)
+    coh = np.full((T, Hkv, cfg.top_n), -1, dtype=np.int32)
+    for jc in range(cfg.n_slc):
+        t0, t1 = jc * cfg.slc_block, min((jc + 1) * cfg.slc_block, T)
+        forced = sorted(set(range(min(cfg.n_init, jc + 1))) | set(range(max(0, jc - cfg.n_local + 1), jc + 1)))
+        pool = [j for j in range(jc + 1) if j not in forced]
+        n_free = min(cfg.top_n, jc + 1) - len(forced)
+        for gg in range(Hkv):
+            picks = rng.choice(pool, n_free, replace=False).tolist() if n_free > 0 else []
+            row = sorted(forced + picks)
+            coh[t0:t1, gg, :len(row)] = row
+    sel_coh = torch.from_numpy(coh[None]).to(dev)
+    pcc, _ = time_calls([lambda: ops.sparse_attn_fwd(cfg, Q, K, V, sel_coh, ocmp, gates, out=out, workspace=ws[2])],
+                        5, 1, torch)
+    cms = float(pcc.mean())
+    result["selected_locality"] = {
+        "workload": "nsa_sparse_attn_fwd_64k_shared_picks", "ms": round(cms, 3),
+        "vs_random_picks_ms": round(float(call_ms[2]), 3),
+        "gathered_gbs": round(slc_pairs(cfg) // cfg.heads_per_group * (cfg.d_k + cfg.d_v) * 2 / (cms * 1e-3) / 1e9, 1),
+        "note": "free picks shared by the 64 tokens of each selection block"}
+
+
 def load_traffic(kernel: str, sources) -> dict | None:
     """HBM traffic per launch from the committed counter record, if it was taken on the
     current sources of the kernel (otherwise None: the kernel changed since)."""
@@ -159,6 +188,10 @@ def main():
     ap.add_argument("--no-moba", action="store_true")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense causal attention comparison")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward pass timing")
+    ap.add_argument("--locality", action="store_true",
+                    help="also time the selected-branch kernel on lists with shared picks per selection block "
+                         "(off by default: the same kernel and grid as the headline call, so a profile of the "
+                         "default command keeps the headline kernel's own average)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run one elementwise kernel over 1 GiB (reads and writes 1 GiB: the known-size kernel that scales HBM counters)")
     args = ap.parse_args()
@@ -320,32 +353,9 @@ def main():
         del Q8, K8, V8, kc8, vc8, sel8, oc8, o8, wsf
         torch.cuda.empty_cache()
 
-    # ---------------- the selected branch with selection locality ----------------
-    # The headline inputs are random, so neighbouring tokens share no free pick.  For
-    # contrast: the same kernel on valid lists in which the 64 tokens of each selection block
-    # share their free picks (forced blocks as the rule has them), the locality trained
-    # attention tends to show.
-    rng = np.random.default_rng(cfg.seed + 77)
-    coh = np.full((T, Hkv, cfg.top_n), -1, dtype=np.int32)
-    for jc in range(cfg.n_slc):
-        t0, t1 = jc * cfg.slc_block, min((jc + 1) * cfg.slc_block, T)
-        forced = sorted(set(range(min(cfg.n_init, jc + 1))) | set(range(max(0, jc - cfg.n_local + 1), jc + 1)))
-        pool = [j for j in range(jc + 1) if j not in forced]
-        n_free = min(cfg.top_n, jc + 1) - len(forced)
-        for gg in range(Hkv):
-            picks = rng.choice(pool, n_free, replace=False).tolist() if n_free > 0 else []
-            row = sorted(forced + picks)
-            coh[t0:t1, gg, :len(row)] = row
-    sel_coh = torch.from_numpy(coh[None]).to(dev)
-    pcc, _ = time_calls([lambda: ops.sparse_attn_fwd(cfg, Q, K, V, sel_coh, ocmp, gates, out=out, workspace=ws[2])],
-                        5, 1, torch)
-    cms = float(pcc.mean())
-    result["selected_locality"] = {
-        "workload": "nsa_sparse_attn_fwd_64k_shared_picks", "ms": round(cms, 3),
-        "vs_random_picks_ms": round(float(call_ms[2]), 3),
-        "gathered_gbs": round(slc_pairs(cfg) // cfg.heads_per_group * (cfg.d_k + cfg.d_v) * 2 / (cms * 1e-3) / 1e9, 1),
-        "note": "free picks shared by the 64 tokens of each selection block"}
-    del sel_coh
+    # ---------------- the selected branch with selection locality (opt-in) ----------------
+    if args.locality:
+        locality(cfg, Q, K, V, ocmp, gates, out, ws, call_ms, result, time_calls, torch, dev)
 
     # ---------------- backward of the same step ----------------
     if not args.no_backward:
@@ -427,6 +437,26 @@ def main():
         result["decode"] = {"workload": "nsa_decode_b32_l65536", "ms_per_step": round(dms, 4),
                             "bytes_per_step": int(bytes_step), "hbm_gbs": round(gbs, 1),
                             "hbm_peak_frac": round(gbs / PEAK_HBM_GBS, 4)}
+        # the same step replayed from a captured HIP graph of 20 steps (the serving loop's
+        # form: no host launch work between the kernels)
+        try:
+            gd_ = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gd_):
+                for _ in range(20):
+                    dcall[0]()
+            ea, eb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            gd_.replay()
+            torch.cuda.synchronize()
+            ea.record()
+            gd_.replay()
+            eb.record()
+            torch.cuda.synchronize()
+            gms = ea.elapsed_time(eb) / 20
+            result["decode"]["graph_ms_per_step"] = round(gms, 4)
+            result["decode"]["graph_hbm_gbs"] = round(bytes_step / (gms * 1e-3) / 1e9, 1)
+            del gd_
+        except RuntimeError as e:
+            result["decode"]["graph_note"] = f"graph capture failed: {e}"[:200]
         # cache maintenance before each step: one new token per sequence into the caches,
         # a new compressed entry every s calls (timed over 2*s calls, after the decode timing)
         prep = ops.compress_prepare(dc, wk, wv, pk, pv)
@@ -435,7 +465,28 @@ def main():
         clen2 = torch.full((Bd,), L - 4 * dc.cmp_stride * 4, dtype=torch.int32, device=dev)
         acall = [lambda: ops.cache_append(dc, kn, vn, Kd, Vd, clen2, kcd, vcd, prep)]
         pca, _ = time_calls(acall, 2 * dc.cmp_stride, 2, torch)
-        result["decode"]["append_us_per_token"] = round(float(pca.mean()) * 1e3, 2)
+        result["decode"]["append_us_per_token_eager"] = round(float(pca.mean()) * 1e3, 2)
+        # one eager call is bound by the host (a ctypes call and two launches); the GPU time
+        # comes from replaying a captured graph of s consecutive appends (one of which
+        # completes a compressed block)
+        try:
+            clen2.fill_(L - 4 * dc.cmp_stride * 4)
+            gr = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gr):
+                for _ in range(dc.cmp_stride):
+                    ops.cache_append(dc, kn, vn, Kd, Vd, clen2, kcd, vcd, prep)
+            ga, gb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            clen2.fill_(L - 4 * dc.cmp_stride * 4)
+            torch.cuda.synchronize()
+            ga.record()
+            gr.replay()
+            gb.record()
+            torch.cuda.synchronize()
+            result["decode"]["append_us_per_token"] = round(ga.elapsed_time(gb) * 1e3 / dc.cmp_stride, 2)
+            del gr
+        except RuntimeError as e:   # capture unavailable: the eager figure stands
+            result["decode"]["append_us_per_token"] = result["decode"]["append_us_per_token_eager"]
+            result["decode"]["append_note"] = f"graph capture failed: {e}"[:200]
         del Kd, Vd, kcd, vcd
         torch.cuda.empty_cache()
 
