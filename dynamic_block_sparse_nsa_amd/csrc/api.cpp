@@ -154,7 +154,7 @@ AttnWs attn_ws(const Shape& s) {
         w.entries = off; off = align_up(off + rows * 4, 256);
         w.pm = off; off = align_up(off + rows * 4, 256);
         w.pl = off; off = align_up(off + rows * 4, 256);
-        w.po = off; off = align_up(off + rows * s.dv * 4, 256);
+        w.po = off; off = align_up(off + rows * s.dv * 2, 256);
     }
     w.total = off;
     return w;
@@ -408,7 +408,7 @@ nsa_status sparse_attn_fwd_impl(const nsa_config* cfg, const void* Q, const void
         m.entries = at<int>(ws, w.entries);
         m.part_m = at<float>(ws, w.pm);
         m.part_l = at<float>(ws, w.pl);
-        m.part_o = at<float>(ws, w.po);
+        m.part_o = at<u16>(ws, w.po);
         m.B = s.B; m.T = s.T; m.Tpad = w.tpad; m.Hkv = s.Hkv; m.lp = s.lp; m.n_slc = s.n_slc; m.top_n = s.n;
         m.n_chunk = w.n_chunk; m.n_bucket = w.n_bucket; m.n_own = nsa::moba_n_own(s.B * s.Hkv, s.n_slc, s.lp);
         m.scale_log2 = s.scale * nsa::kLog2eHost;

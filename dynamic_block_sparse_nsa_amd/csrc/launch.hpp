@@ -98,7 +98,7 @@ struct MobaParams {
     int* entries;              // [B*Hkv*T*top_n] (token << 5 | slot), grouped by bucket
     float* part_m;             // [B,T,Hkv,top_n]
     float* part_l;             // [B,T,Hkv,top_n]
-    float* part_o;             // [B,T,Hkv,top_n,DV]
+    u16* part_o;               // [B,T,Hkv,top_n,DV] fp16, normalized by the slot's own sum
     int B, T, Tpad, Hkv, lp, n_slc, top_n, n_chunk, n_bucket, n_own;
     int keep_own;              // 1: the query's own block is listed too (backward lists)
     float scale_log2;

@@ -327,16 +327,25 @@ __global__ __launch_bounds__(256, 2) void moba_attn_kernel(MobaParams p) {
             p.part_m[pr] = m[c];
             p.part_l[pr] = L;
         }
-        float* op = p.part_o + pr * DV + 4 * lq;
+        // the slot's output normalized by its own sum (|o| <= max |v|), in fp16: half the
+        // bytes of the partial round trip, 2^-11 relative rounding
+        const float inv = L > 0.f ? 1.f / L : 0.f;
+        u16* op = p.part_o + pr * DV + 4 * lq;
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt)
-            *reinterpret_cast<float4*>(op + 16 * dt) = make_float4(o[c][dt][0], o[c][dt][1], o[c][dt][2], o[c][dt][3]);
+        for (int dt = 0; dt < NDT; ++dt) {
+            const _Float16 h0 = (_Float16)(o[c][dt][0] * inv), h1 = (_Float16)(o[c][dt][1] * inv);
+            const _Float16 h2 = (_Float16)(o[c][dt][2] * inv), h3 = (_Float16)(o[c][dt][3] * inv);
+            const u32x2 w = {(uint32_t)__builtin_bit_cast(u16, h0) | ((uint32_t)__builtin_bit_cast(u16, h1) << 16),
+                             (uint32_t)__builtin_bit_cast(u16, h2) | ((uint32_t)__builtin_bit_cast(u16, h3) << 16)};
+            *reinterpret_cast<u32x2*>(op + 16 * dt) = w;
+        }
     }
 }
 
 // per (token, head): combine the slots of the token's list.  A row of DV values is DV/4
-// lanes with one float4 each (a wave covers 64*4/DV rows); the slots' partial outputs are
-// read once (non-temporal) and the bf16 row is stored with 8-byte writes.
+// lanes with 4 values each (a wave covers 64*4/DV rows); the slots' fp16 partial outputs
+// are read once (non-temporal, 8 bytes per lane) and weighted by sum * 2^(m - M); the bf16
+// row is stored with 8-byte writes.
 template <int DV>
 __global__ __launch_bounds__(256) void moba_merge_kernel(MobaParams p) {
     constexpr int LPR = DV / 4;      // lanes per row
@@ -355,9 +364,14 @@ __global__ __launch_bounds__(256) void moba_merge_kernel(MobaParams p) {
             if (sel[s] < 0) continue;
             const float ms = p.part_m[row * p.top_n + s];
             if (ms == -INFINITY) continue;
-            const float w = fast_exp2(ms - M);
-            L += w * p.part_l[row * p.top_n + s];
-            acc += w * ld_stream(reinterpret_cast<const f32x4*>(p.part_o + (row * p.top_n + s) * DV) + li);
+            const float w = fast_exp2(ms - M) * p.part_l[row * p.top_n + s];   // the slot's weight
+            L += w;
+            const u32x2 hv = ld_stream(reinterpret_cast<const u32x2*>(p.part_o + (row * p.top_n + s) * DV) + li);
+            const f32x4 o = {(float)__builtin_bit_cast(_Float16, (u16)(hv[0] & 0xFFFFu)),
+                             (float)__builtin_bit_cast(_Float16, (u16)(hv[0] >> 16)),
+                             (float)__builtin_bit_cast(_Float16, (u16)(hv[1] & 0xFFFFu)),
+                             (float)__builtin_bit_cast(_Float16, (u16)(hv[1] >> 16))};
+            acc += w * o;
         }
     }
     const float g = p.gates ? sigmoidf_(p.gates[row * 3 + 1]) : 1.f;
