@@ -417,6 +417,32 @@ __device__ void select_unit(const DecodeParams& p, int g, int b, float* sm) {
     const int jc = t / p.lp;
     const size_t bg = (size_t)b * p.Hkv + g;
     const size_t pb0 = bg * p.n_split;
+    // block scores: compressed keys [ilo, ihi] overlap block j (s | l and s | l': with
+    // a = l'/s and c = l/s they are j*a - c + 1 .. j*a + a - 1); at most two splits hold them
+    // Thread tid scores blocks tid + 1024r (NU * 64 / 1024 of them).  The partial sums depend
+    // on cache_len only, so they are requested first and arrive while the split weights are
+    // formed.  Rows past jc read block jc's rows and are not stored.
+    const int a = p.lp / p.s, c = p.l / p.s;
+    constexpr int NR = NU * 64 / 1024 > 0 ? NU * 64 / 1024 : 1;
+    f32x4 v[NR][2][4];
+    int sa[NR], sb[NR];
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+        const int j = min((int)threadIdx.x + 1024 * r, jc);
+        const int ilo = max(0, j * a - c + 1);
+        const int ihi = max(ilo, min(j * a + a - 1, nv - 1));
+        sa[r] = ilo / kDecodeSplitKeys;
+        sb[r] = ihi / kDecodeSplitKeys;
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+            // clamped into the workspace; a clamped (unused) row may be any split's
+            const int s0 = min(min(sa[r] + h2, sb[r]), p.n_split - 1);
+            const int jj = min(max(j - (s0 * kDecodeSplitKeys) / a, 0), p.jb - 1);
+            const f32x4* pa = reinterpret_cast<const f32x4*>(p.part_a + ((pb0 + s0) * p.jb + jj) * 16);
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) v[r][h2][q4] = pa[q4];
+        }
+    }
     // per-head log-sum-exp over the splits: lane = head + 16 * q holds splits q + 4i
     // (at most kDecodeMaxSplits splits, all loads issued together)
     if (threadIdx.x < 64) {
@@ -450,31 +476,6 @@ __device__ void select_unit(const DecodeParams& p, int g, int b, float* sm) {
         }
     }
     __syncthreads();
-    // block scores: compressed keys [ilo, ihi] overlap block j (s | l and s | l': with
-    // a = l'/s and c = l/s they are j*a - c + 1 .. j*a + a - 1); at most two splits hold them
-    // Thread tid scores blocks tid + 1024r (NU * 64 / 1024 of them); every load is issued
-    // before any sum.  Rows past jc read block jc's rows and are not stored.
-    const int a = p.lp / p.s, c = p.l / p.s;
-    constexpr int NR = NU * 64 / 1024 > 0 ? NU * 64 / 1024 : 1;
-    f32x4 v[NR][2][4];
-    int sa[NR], sb[NR];
-#pragma unroll
-    for (int r = 0; r < NR; ++r) {
-        const int j = min((int)threadIdx.x + 1024 * r, jc);
-        const int ilo = max(0, j * a - c + 1);
-        const int ihi = max(ilo, min(j * a + a - 1, nv - 1));
-        sa[r] = ilo / kDecodeSplitKeys;
-        sb[r] = ihi / kDecodeSplitKeys;
-#pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) {
-            // clamped into the workspace; a clamped (unused) row may be any split's
-            const int s0 = min(min(sa[r] + h2, sb[r]), p.n_split - 1);
-            const int jj = min(max(j - (s0 * kDecodeSplitKeys) / a, 0), p.jb - 1);
-            const f32x4* pa = reinterpret_cast<const f32x4*>(p.part_a + ((pb0 + s0) * p.jb + jj) * 16);
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) v[r][h2][q4] = pa[q4];
-        }
-    }
 #pragma unroll
     for (int r = 0; r < NR; ++r) {
         const int j = (int)threadIdx.x + 1024 * r;
