@@ -78,7 +78,8 @@ def test_workspace_sizes(name):
     assert n == al(bg * c.d_k * tp * 2) + al(bg * c.d_v * tp * 2) + al(bg * 64 * 4) + al(bg * 4)
     # the attention workspace holds K and V in MFMA fragment order, padded:
     # B*Hkv*(d_k + d_v)*(roundup(T,64)+64)*2 bytes (each part 256-byte aligned)
-    # (G = 1 with only the selected branch adds the block lists and per-slot partials)
+    # (G = 1 with only the selected branch adds the block lists and per-slot partials: max and
+    # sum in fp32, the normalized partial output in fp16)
     rc, n = _ws(c, ops.OP_SPARSE_ATTN)
     tp = -(-c.seq_len // 64) * 64 + 64
     al = lambda x: -(-x // 256) * 256
@@ -88,7 +89,7 @@ def test_workspace_sizes(name):
         n_chunk = -(-c.seq_len // 1024)
         rows = bg * c.seq_len * c.top_n
         want += (al(bg * n_chunk * c.n_slc * 4) + al(bg * c.n_slc * 4) + 2 * al((bg * c.n_slc + 1) * 4)
-                 + 3 * al(rows * 4) + al(rows * c.d_v * 4))
+                 + 3 * al(rows * 4) + al(rows * c.d_v * 2))
     assert n == want
 
 
