@@ -32,7 +32,8 @@
 //                  own block included).
 // compress_bwd_*   the linear block map: column sums of dY, dPE = W.colsum, dW = X^T.dY
 //                  (X = block rows + PE, split over row ranges, atomics), dX = dY.W^T added
-//                  into the raw key/value gradients (a token lies in l/s blocks).  fp32 FMA.
+//                  into the raw key/value gradients as one GEMM per token position within the
+//                  stride (a token lies in l/s blocks; no atomics).  fp32 FMA.
 // Every MFMA runs under wave-uniform control flow: the instruction reads all 64 lanes'
 // operands, so padding rows (heads past G, tokens past a list) are masked in the values.
 #include <algorithm>
@@ -574,15 +575,16 @@ __global__ __launch_bounds__(256) void compress_bwd_dpe_kernel(const u16* __rest
     dpe[m] = s;
 }
 
-// dW[m][o] += sum over this workgroup's 256 rows of X[row][m] dY[row][o]: 64 x 64 output tile,
-// 4 x 4 per thread, 16 rows per LDS step
+// dW[m][o] += sum over this workgroup's kDwRows rows of X[row][m] dY[row][o]: 64 x 64 output
+// tile, 4 x 4 per thread, 16 rows per LDS step (one atomic add per output per row range)
+constexpr int kDwRows = 1024;
 __global__ __launch_bounds__(256) void compress_bwd_dw_kernel(const u16* __restrict__ X, const u16* __restrict__ pe,
                                                               const float* __restrict__ dY, float* __restrict__ dW,
                                                               int rows, int N, int T, int d, int l, int s) {
     __shared__ float xs[16][64 + 4], ys[16][64 + 4];
     const int KD = l * d;
     const int m0 = blockIdx.x * 64, o0 = blockIdx.y * 64;
-    const int rbeg = blockIdx.z * 256, rend = min(rbeg + 256, rows);
+    const int rbeg = blockIdx.z * kDwRows, rend = min(rbeg + kDwRows, rows);
     const int tm = threadIdx.x % 16, to = threadIdx.x / 16;
     float acc[4][4] = {};
     const int rr = m0 / d;   // block offset r of this tile (d is a multiple of 64)
@@ -625,51 +627,52 @@ __global__ __launch_bounds__(256) void compress_bwd_dw_kernel(const u16* __restr
         }
 }
 
-// dX[row][m] = sum_o dY[row][o] W[m][o], added to dK[bg][i*s + r][e]: 64 rows x 64 m per
-// workgroup, 4 x 4 per thread, 16 o per LDS step
+// dX added to dK without atomics: token tok = q*s + rho lies in blocks i = q - phi for
+// phi = 0 .. l/s - 1 at row rho + phi*s of each, so for a fixed rho
+//   dK[tok][e] += sum_phi sum_o dY[q - phi][o] W[(rho + phi*s)*d + e][o]
+// is one GEMM over (phi, o).  A workgroup owns 64 token slots q x 64 dims e of one (bg, rho),
+// 4 x 4 per thread, 16 o per LDS step; every output element has one writer.
 __global__ __launch_bounds__(256) void compress_bwd_dx_kernel(const float* __restrict__ dY, const u16* __restrict__ W,
-                                                              float* __restrict__ dX, int rows, int N, int T, int d,
-                                                              int l, int s) {
+                                                              float* __restrict__ dX, int N, int T, int d, int l,
+                                                              int s) {
     __shared__ float ys[16][64 + 4], ws[16][64 + 4];
-    const int KD = l * d;
-    const int row0 = blockIdx.x * 64, m0 = blockIdx.y * 64;
-    const int tr = threadIdx.x % 16, tm = threadIdx.x / 16;
+    const int q0 = blockIdx.x * 64, e0 = blockIdx.y * 64;
+    const int bg = blockIdx.z / s, rho = blockIdx.z % s;
+    const int tq = threadIdx.x % 16, te = threadIdx.x / 16;
     float acc[4][4] = {};
-    for (int k0 = 0; k0 < d; k0 += 16) {
-        __syncthreads();
-        for (int idx = threadIdx.x; idx < 16 * 64; idx += 256) {
-            const int k = idx % 16, c = idx / 16;
-            const int row = row0 + c, m = m0 + c;
-            ys[k][c] = row < rows ? dY[(size_t)row * d + k0 + k] : 0.f;
-            ws[k][c] = m < KD ? bf2f(W[(size_t)m * d + k0 + k]) : 0.f;
-        }
-        __syncthreads();
-#pragma unroll
-        for (int k = 0; k < 16; ++k) {
-            float a[4], bv[4];
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                a[u] = ys[k][tr + 16 * u];
-                bv[u] = ws[k][tm + 16 * u];
+    for (int phi = 0; phi < l / s; ++phi) {
+        const int wrow = (rho + phi * s) * d;
+        for (int k0 = 0; k0 < d; k0 += 16) {
+            __syncthreads();
+            for (int idx = threadIdx.x; idx < 16 * 64; idx += 256) {
+                const int k = idx % 16, c = idx / 16;
+                const int i = q0 + c - phi;   // block of token slot q0 + c at phase phi
+                ys[k][c] = (i >= 0 && i < N) ? dY[((size_t)bg * N + i) * d + k0 + k] : 0.f;
+                ws[k][c] = bf2f(W[(size_t)(wrow + e0 + c) * d + k0 + k]);
             }
+            __syncthreads();
 #pragma unroll
-            for (int u = 0; u < 4; ++u)
+            for (int k = 0; k < 16; ++k) {
+                float a[4], bv[4];
 #pragma unroll
-                for (int v = 0; v < 4; ++v) acc[u][v] += a[u] * bv[v];
+                for (int u = 0; u < 4; ++u) {
+                    a[u] = ys[k][tq + 16 * u];
+                    bv[u] = ws[k][te + 16 * u];
+                }
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) acc[u][v] += a[u] * bv[v];
+            }
         }
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-        const int row = row0 + tr + 16 * u;
-        if (row >= rows) continue;
-        const int bg = row / N, i = row % N;
+        const int tok = (q0 + tq + 16 * u) * s + rho;
+        if (tok >= T) continue;
+        float* row = dX + ((size_t)bg * T + tok) * d + e0;
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            const int m = m0 + tm + 16 * v;
-            if (m >= KD) continue;
-            const int r = m / d, e = m % d;
-            unsafeAtomicAdd(dX + ((size_t)bg * T + (size_t)i * s + r) * d + e, acc[u][v]);
-        }
+        for (int v = 0; v < 4; ++v) row[te + 16 * v] += acc[u][v];
     }
 }
 
@@ -790,9 +793,10 @@ void launch_compress_bwd(const u16* X, const u16* W, const u16* pe, const float*
     }
     compress_bwd_colsum_kernel<<<(rows + 63) / 64, 256, 0, st>>>(dY, rows, d, colsum);
     compress_bwd_dpe_kernel<<<(KD + 255) / 256, 256, 0, st>>>(W, colsum, KD, d, dpe);
-    compress_bwd_dw_kernel<<<dim3(KD / 64, (d + 63) / 64, (rows + 255) / 256), 256, 0, st>>>(X, pe, dY, dW, rows, N, T,
-                                                                                           d, l, s);
-    compress_bwd_dx_kernel<<<dim3((rows + 63) / 64, (KD + 63) / 64), 256, 0, st>>>(dY, W, dX, rows, N, T, d, l, s);
+    compress_bwd_dw_kernel<<<dim3(KD / 64, (d + 63) / 64, (rows + kDwRows - 1) / kDwRows), 256, 0, st>>>(
+        X, pe, dY, dW, rows, N, T, d, l, s);
+    const int nq = (T + s - 1) / s;   // token slots per position rho
+    compress_bwd_dx_kernel<<<dim3((nq + 63) / 64, d / 64, BG * s), 256, 0, st>>>(dY, W, dX, N, T, d, l, s);
 }
 
 }  // namespace nsa
