@@ -133,7 +133,7 @@ bool use_block_major(const Shape& s) { return s.G == 1 && s.br == NSA_BR_SLC; }
 // K and V copied into MFMA fragment order, padded with 64 zero keys past a multiple of 64; for the
 // block-major schedule also the bucket lists and the per-slot partial results.
 struct AttnWs {
-    size_t kf, vf, hist, bcnt, bstart, tstart, entries, pm, pl, po, total;
+    size_t kf, vf, vmax, vexp, hist, bcnt, bstart, tstart, entries, pm, pl, po, total;
     int tpad, n_chunk, n_bucket;
 };
 AttnWs attn_ws(const Shape& s) {
@@ -143,6 +143,8 @@ AttnWs attn_ws(const Shape& s) {
     size_t off = 0;
     w.kf = off; off = align_up(off + bg * w.tpad * s.dk * 2, 256);
     w.vf = off; off = align_up(off + bg * w.tpad * s.dv * 2, 256);
+    w.vmax = off; off = align_up(off + bg * nsa::cmp_vmax_parts() * 4, 256);   // V's fp16 scaling
+    w.vexp = off; off = align_up(off + bg * 4, 256);
     if (use_block_major(s)) {
         w.n_chunk = nsa::moba_n_chunk(s.T);
         w.n_bucket = (int)(bg * s.n_slc);
@@ -184,7 +186,7 @@ DecodeWs decode_ws(const Shape& s) {
 // backward of the branches: K, V in fragment order for the statistics pass, the per-row
 // statistics, and the selected branch's block lists (own block included)
 struct BwdWs {
-    size_t kf, vf, stats, hist, bcnt, bstart, tstart, entries, total;
+    size_t kf, vf, vmax, vexp, stats, hist, bcnt, bstart, tstart, entries, total;
     int tpad, n_chunk, n_bucket;
 };
 BwdWs bwd_ws(const Shape& s) {
@@ -194,6 +196,8 @@ BwdWs bwd_ws(const Shape& s) {
     size_t off = 0;
     w.kf = off; off = align_up(off + bg * w.tpad * s.dk * 2, 256);
     w.vf = off; off = align_up(off + bg * w.tpad * s.dv * 2, 256);
+    w.vmax = off; off = align_up(off + bg * nsa::cmp_vmax_parts() * 4, 256);
+    w.vexp = off; off = align_up(off + bg * 4, 256);
     w.stats = off; off = align_up(off + (size_t)s.B * s.T * s.H * 12 * 4, 256);
     if (s.br & NSA_BR_SLC) {
         w.n_chunk = nsa::moba_n_chunk(s.T);
@@ -389,10 +393,15 @@ nsa_status sparse_attn_fwd_impl(const nsa_config* cfg, const void* Q, const void
     using nsa::u16;
     u16* kf = at<u16>(ws, w.kf);
     u16* vf = at<u16>(ws, w.vf);
-    if (!nsa::launch_tile_kv(s.dk, s.dv, static_cast<const u16*>(K), static_cast<const u16*>(V), kf, vf, s.B * s.Hkv,
-                             s.T, w.tpad, hs))
+    const bool moba = use_block_major(s) && !train;
+    // fragment order: V in bf16 for the block-major kernel, as scaled fp16 for the attention kernel
+    if (moba ? !nsa::launch_tile_kv(s.dk, s.dv, static_cast<const u16*>(K), static_cast<const u16*>(V), kf, vf,
+                                    s.B * s.Hkv, s.T, w.tpad, hs)
+             : !nsa::launch_tile_cmp(s.dk, s.dv, static_cast<const u16*>(K), static_cast<const u16*>(V),
+                                     at<uint32_t>(ws, w.vmax), at<int>(ws, w.vexp), kf, vf, s.B * s.Hkv, s.T, w.tpad,
+                                     hs))
         return fail(NSA_ERR_UNSUPPORTED, "no layout kernel");
-    if (use_block_major(s) && !train) {
+    if (moba) {
         if ((long long)s.T >= (1LL << 26)) return fail(NSA_ERR_UNSUPPORTED, "sequence too long for the block lists");
         nsa::MobaParams m{};
         m.Q = static_cast<const u16*>(Q);
@@ -419,6 +428,7 @@ nsa_status sparse_attn_fwd_impl(const nsa_config* cfg, const void* Q, const void
     p.Q = static_cast<const u16*>(Q);
     p.Kf = kf;
     p.Vf = vf;
+    p.vexp = at<int>(ws, w.vexp);
     p.sel = sel_idx;
     p.o_cmp = o_cmp;
     p.gates = gate_logits;
@@ -634,13 +644,15 @@ nsa_status nsa_sparse_attn_bwd(const nsa_config* cfg, const void* Q, const void*
     //    selected and window branches recomputed
     u16* kf = at<u16>(ws, w.kf);
     u16* vf = at<u16>(ws, w.vf);
-    if (!saved_o && !nsa::launch_tile_kv(s.dk, s.dv, static_cast<const u16*>(K), static_cast<const u16*>(V), kf, vf,
-                                         (int)bg, s.T, w.tpad, hs))
+    if (!saved_o && !nsa::launch_tile_cmp(s.dk, s.dv, static_cast<const u16*>(K), static_cast<const u16*>(V),
+                                          at<uint32_t>(ws, w.vmax), at<int>(ws, w.vexp), kf, vf, (int)bg, s.T, w.tpad,
+                                          hs))
         return fail(NSA_ERR_UNSUPPORTED, "no layout kernel");
     nsa::AttnParams a{};
     a.Q = static_cast<const u16*>(Q);
     a.Kf = kf;
     a.Vf = vf;
+    a.vexp = at<int>(ws, w.vexp);
     a.sel = sel_idx;
     a.o_cmp = o_cmp;
     a.gates = gate_logits;

@@ -49,14 +49,15 @@ void launch_select_from_scores(const float* scores, int32_t* sel, int B, int T, 
                                int top_n, int n_init, int n_local, hipStream_t st);
 
 // ---- selected + window attention, gated sum ----
-// K and V in MFMA fragment order (written by launch_tile_kv): for every 16-key group kt
+// K and V in MFMA fragment order (written by launch_tile_cmp; V as scaled fp16): for every 16-key group kt
 // and contraction step ds, the 64 lanes' K operands are 1 KB contiguous
 // (Kf[bg][kt][ds][lane][8]); for every 32-key chunk c and 16-wide value slice dt, the
 // lanes' V^T operands likewise (Vf[bg][c][dt][lane][8]).  Keys >= T are zero.
 struct AttnParams {
     const u16* Q;        // [B,T,H,DK]
     const u16* Kf;       // [B,Hkv,Tpad/16,DK/32,64,8]
-    const u16* Vf;       // [B,Hkv,Tpad/32,DV/16,64,8]
+    const u16* Vf;       // [B,Hkv,Tpad/32,DV/16,64,8] fp16, V * 2^-vexp[b*Hkv+g] (launch_tile_cmp)
+    const int* vexp;     // [B*Hkv]
     const int32_t* sel;  // [B,T,Hkv,top_n]
     const float* o_cmp;  // [B,T,H,DV] (branch CMP)
     const float* gates;  // [B,T,H,3] or null

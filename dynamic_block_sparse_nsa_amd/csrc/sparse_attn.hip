@@ -8,11 +8,13 @@
 // Every attention product is key-major: S^T = K . Q^T on the MFMA, online softmax with
 // the running max and sum in registers (base-2), then O^T += V^T . P^T.
 //
-// K and V are first copied into MFMA fragment order (tile_kv_kernel): the operands a
-// wave needs for 16 keys x 32 dims of K, or 32 keys x 16 dims of V^T, are 1 KB of
-// contiguous memory in lane order.  Operand loads straight from row-major K would have
-// each lane read a different key row, so every 16-byte lane access costs the address
-// unit a cycle; in fragment order a wave's load is one contiguous, coalesced 1 KB.
+// K and V are first copied into MFMA fragment order (launch_tile_cmp, the layout pass of
+// the compressed branch): the operands a wave needs for 16 keys x 32 dims of K, or 32 keys
+// x 16 dims of V^T, are 1 KB of contiguous memory in lane order.  Operand loads straight
+// from row-major K would have each lane read a different key row, so every 16-byte lane
+// access costs the address unit a cycle; in fragment order a wave's load is one
+// contiguous, coalesced 1 KB.  V is copied as fp16 scaled by 2^-e (e per sequence and
+// group, from its largest |V|), so O^T += V^T.P^T is one fp16 product with P in fp16.
 //
 // Phase B (per token, first): the selected blocks before the window range are contiguous
 //   64-token spans gathered by block index straight from memory in 32-key chunks, two
@@ -46,9 +48,10 @@ struct SoftmaxState {
     }
 
     // One 32-key chunk starting at key0: s0 holds keys key0+4q+r, s1 keys key0+16+4q+r
-    // (q = lane/16); keys outside [lo, hi] are masked.  va: the V^T operand per d-tile.
+    // (q = lane/16); keys outside [lo, hi] are masked.  va: the V^T operand per d-tile, fp16
+    // (V scaled by a power of two; finish() undoes it).
     __device__ __forceinline__ void update(const f32x4& s0, const f32x4& s1, int key0, int lo, int hi, float scale_log2,
-                           const bf16x8 (&va)[NDT]) {
+                           const f16x8 (&va)[NDT]) {
         const int lq = (threadIdx.x & 63) >> 4;
         float x[8];
         float tmax = -INFINITY;
@@ -72,20 +75,21 @@ struct SoftmaxState {
         }
         l = l * alpha + ps;
         m = mnew;
-        bf16x8 bh, bl;
-        pack_p_split(pa, pb, bh, bl);
+        // P in fp16 against the fp16 V copy: one product per slice (2^-11 relative rounding
+        // of p); o is rescaled only when some column's running max moved
+        const f16x8 ph = pack_p_h(pa, pb);
+        if (__ballot(alpha != 1.f)) {
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) {
-            o[dt] *= alpha;
-            o[dt] = mfma16(va[dt], bh, o[dt]);
-            o[dt] = mfma16(va[dt], bl, o[dt]);
+            for (int dt = 0; dt < NDT; ++dt) o[dt] *= alpha;
         }
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) o[dt] = mfma16h(va[dt], ph, o[dt]);
     }
 
-    // normalizes o; returns the column's sum of exp2(x - m)
-    __device__ __forceinline__ float finish() {
+    // normalizes o (and undoes V's scaling by 2^-vexp); returns the column's sum of exp2(x - m)
+    __device__ __forceinline__ float finish(int vexp) {
         const float L = col_sum(l);
-        const float inv = L > 0.f ? 1.0f / L : 0.f;
+        const float inv = L > 0.f ? ldexpf(1.0f / L, vexp) : 0.f;
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) o[dt] *= inv;
         return L;
@@ -131,7 +135,8 @@ struct WinTile {
 template <int DK, int DV>
 struct GatherChunk {
     static constexpr int NDS = DK / 32, NDT = DV / 16;
-    bf16x8 ka[NDS], kb[NDS], va[NDT];
+    bf16x8 ka[NDS], kb[NDS];
+    f16x8 va[NDT];
     __device__ __forceinline__ void load(const u16* kg, const u16* vg, int key0) {
         const int lane = threadIdx.x & 63;
         const u16* k0 = kg + kfrag<DK>(key0 / 16, 0) + lane * 8;
@@ -142,7 +147,7 @@ struct GatherChunk {
             kb[ds] = ld8(k0 + (NDS + ds) * 512);
         }
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) va[dt] = ld8(v0 + dt * 512);
+        for (int dt = 0; dt < NDT; ++dt) va[dt] = ld8h(v0 + dt * 512);
     }
     __device__ __forceinline__ void scores(const bf16x8 (&qf)[NDS], f32x4& s0, f32x4& s1) const {
         s0 = zero4();
@@ -155,7 +160,8 @@ struct GatherChunk {
     }
 };
 
-// Copy of K and V into fragment order, one workgroup per 32-key chunk of one (b, g):
+// Copy of K and V into fragment order with V in bf16 (the MoBA block-major kernel's
+// layout), one workgroup per 32-key chunk of one (b, g):
 // row-major tiles are staged in LDS with coalesced loads; K fragments are plain 16-byte
 // pieces of a row, V^T fragments come from the transposing LDS read.
 template <int DK, int DV>
@@ -322,9 +328,9 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnParams p) {
                     s0 = mfma16(ld8(kb + ds * 512), qf[ds], s0);
                     s1 = mfma16(ld8(kb + (NDS + ds) * 512), qf[ds], s1);
                 }
-                bf16x8 va[NDT];
+                f16x8 va[NDT];
 #pragma unroll
-                for (int dt = 0; dt < NDT; ++dt) va[dt] = ld8(vbuf[buf] + (dt * 64 + lane) * 8);
+                for (int dt = 0; dt < NDT; ++dt) va[dt] = ld8h(vbuf[buf] + (dt * 64 + lane) * 8);
                 if (w_any) win.update(s0, s1, key0, wlo_t, t, p.scale_log2, va);
                 if (s_any) slc.update(s0, s1, key0, jch * p.lp, t, p.scale_log2, va);
             }
@@ -335,8 +341,9 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnParams p) {
     }
 
     if (!active) return;
-    const float Lw = win.finish();
-    const float Ls = slc.finish();
+    const int vexp = p.vexp[unit];
+    const float Lw = win.finish(vexp);
+    const float Ls = slc.finish(vexp);
     if constexpr (STATS) {
         const size_t row = ((size_t)b * T + t) * H + h;
         float sg[3] = {1.f, 1.f, 1.f};

@@ -77,14 +77,15 @@ def test_workspace_sizes(name):
     bg = c.batch * c.num_kv_heads
     assert n == al(bg * c.d_k * tp * 2) + al(bg * c.d_v * tp * 2) + al(bg * 64 * 4) + al(bg * 4)
     # the attention workspace holds K and V in MFMA fragment order, padded:
-    # B*Hkv*(d_k + d_v)*(roundup(T,64)+64)*2 bytes (each part 256-byte aligned)
+    # B*Hkv*(d_k + d_v)*(roundup(T,64)+64)*2 bytes (each part 256-byte aligned), then V's
+    # fp16 scaling (64 partial maxima and one exponent per (b, g))
     # (G = 1 with only the selected branch adds the block lists and per-slot partials: max and
     # sum in fp32, the normalized partial output in fp16)
     rc, n = _ws(c, ops.OP_SPARSE_ATTN)
     tp = -(-c.seq_len // 64) * 64 + 64
     al = lambda x: -(-x // 256) * 256
     bg = c.batch * c.num_kv_heads
-    want = al(bg * c.d_k * tp * 2) + al(bg * c.d_v * tp * 2)
+    want = al(bg * c.d_k * tp * 2) + al(bg * c.d_v * tp * 2) + al(bg * 64 * 4) + al(bg * 4)
     if c.heads_per_group == 1 and c.branches == 2:
         n_chunk = -(-c.seq_len // 1024)
         rows = bg * c.seq_len * c.top_n
