@@ -53,24 +53,35 @@ struct SoftmaxState {
     __device__ __forceinline__ void update(const f32x4& s0, const f32x4& s1, int key0, int lo, int hi, float scale_log2,
                            const f16x8 (&va)[NDT]) {
         const int lq = (threadIdx.x & 63) >> 4;
+        // raw scores (the scale is positive: the max is taken before scaling and the scale
+        // folds into the exponent's fma); a chunk inside [lo, hi] (wave-uniform) is unmasked
         float x[8];
-        float tmax = -INFINITY;
+        if (key0 >= lo && key0 + 31 <= hi) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int ka = key0 + 4 * lq + r, kb = key0 + 16 + 4 * lq + r;
-            x[r] = (ka >= lo && ka <= hi) ? s0[r] * scale_log2 : -INFINITY;
-            x[4 + r] = (kb >= lo && kb <= hi) ? s1[r] * scale_log2 : -INFINITY;
-            tmax = fmaxf(tmax, fmaxf(x[r], x[4 + r]));
+            for (int r = 0; r < 4; ++r) {
+                x[r] = s0[r];
+                x[4 + r] = s1[r];
+            }
+        } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int ka = key0 + 4 * lq + r, kb = key0 + 16 + 4 * lq + r;
+                x[r] = (ka >= lo && ka <= hi) ? s0[r] : -INFINITY;
+                x[4 + r] = (kb >= lo && kb <= hi) ? s1[r] : -INFINITY;
+            }
         }
+        float tmax = fmaxf(x[0], x[4]);
+#pragma unroll
+        for (int r = 1; r < 4; ++r) tmax = fmaxf(tmax, fmaxf(x[r], x[4 + r]));
         tmax = col_max(tmax);
-        const float mnew = fmaxf(m, tmax);
+        const float mnew = fmaxf(m, tmax * scale_log2);
         const float alpha = fast_exp2(m - mnew);
         f32x4 pa, pb;
         float ps = 0.f;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            pa[r] = fast_exp2(x[r] - mnew);
-            pb[r] = fast_exp2(x[4 + r] - mnew);
+            pa[r] = fast_exp2(__builtin_fmaf(x[r], scale_log2, -mnew));
+            pb[r] = fast_exp2(__builtin_fmaf(x[4 + r], scale_log2, -mnew));
             ps += pa[r] + pb[r];
         }
         l = l * alpha + ps;
