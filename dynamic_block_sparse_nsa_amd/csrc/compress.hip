@@ -95,15 +95,35 @@ __global__ __launch_bounds__(256) void compress_linear_kernel(const u16* __restr
     }
 }
 
-// Mean pooling: out[bg][i][e] = (1/l) sum_{r<l} X[bg][i*s + r][e]; grid (N, BG), block d.
-__global__ void compress_mean_kernel(const u16* __restrict__ X, u16* __restrict__ out, int T, int d, int l,
-                                     int s, int N) {
-    const int i = blockIdx.x, bg = blockIdx.y, e = threadIdx.x;
-    if (e >= d) return;
-    const u16* x = X + ((size_t)bg * T + (size_t)i * s) * d + e;
-    float acc = 0.f;
-    for (int r = 0; r < l; ++r) acc += bf2f(x[(size_t)r * d]);
-    out[((size_t)bg * N + i) * d + e] = f2bf(acc / (float)l);
+// Mean pooling: out[bg][i][e] = (1/l) sum_{r<l} X[bg][i*s + r][e]; grid (N, BG), 256 threads.
+// Thread (rg, c) adds the 8 dims 8c..8c+7 of rows rg, rg + RG, ... of the block with 16-byte
+// loads (RG = 256 / (D/8) rows in flight per step, a streaming read of the block); the RG
+// partial sums of each dim are then added in LDS.  fp32 sums, one bf16 rounding.
+template <int D>
+__global__ __launch_bounds__(256) void compress_mean_kernel(const u16* __restrict__ X, u16* __restrict__ out, int T,
+                                                            int l, int s, int N) {
+    constexpr int CPR = D / 8, RG = 256 / CPR;
+    __shared__ float part[RG][D + 4];
+    const int i = blockIdx.x, bg = blockIdx.y;
+    const int c = threadIdx.x % CPR, rg = threadIdx.x / CPR;
+    float acc[8] = {};
+    if (rg < RG) {
+        const u16* x = X + ((size_t)bg * T + (size_t)i * s) * D + 8 * c;
+#pragma unroll 4
+        for (int r = rg; r < l; r += RG) {
+            const u32x4 v = *reinterpret_cast<const u32x4*>(x + (size_t)r * D);
+#pragma unroll
+            for (int k = 0; k < 8; ++k) acc[k] += bf2f((u16)(v[k >> 1] >> (16 * (k & 1))));
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) part[rg][8 * c + k] = acc[k];
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < D; e += 256) {
+        float sum = 0.f;
+        for (int q = 0; q < RG; ++q) sum += part[q][e];
+        out[((size_t)bg * N + i) * D + e] = f2bf(sum / (float)l);
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -126,7 +146,9 @@ void launch_compress_linear(const u16* X, const u16* Wt, const float* bias, u16*
 
 void launch_compress_mean(const u16* X, u16* out, int BG, int T, int d, int l, int s, int N, hipStream_t st) {
     dim3 grid(N, BG);
-    compress_mean_kernel<<<grid, d, 0, st>>>(X, out, T, d, l, s, N);
+    if (d == 192) compress_mean_kernel<192><<<grid, 256, 0, st>>>(X, out, T, l, s, N);
+    else if (d == 128) compress_mean_kernel<128><<<grid, 256, 0, st>>>(X, out, T, l, s, N);
+    else compress_mean_kernel<64><<<grid, 256, 0, st>>>(X, out, T, l, s, N);
 }
 
 }  // namespace nsa

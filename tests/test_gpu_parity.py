@@ -12,7 +12,7 @@ import torch
 import oracle
 from oracle import pipeline
 from dynamic_block_sparse_nsa_amd import inputs, ops
-from dynamic_block_sparse_nsa_amd.configs import (TINY, P8K, P64K, DECODE, MOBA, BR_SLC, BR_WIN, PHI_LINEAR,
+from dynamic_block_sparse_nsa_amd.configs import (TINY, P8K, P64K, DECODE, MOBA, BR_SLC, BR_WIN, PHI_LINEAR, PHI_MEAN,
                                                   SCORE_CMP_OVERLAP)
 from nsa_testlib import (GAP, bf16_dev_to_f64, bf16_ulp, check_close, check_selection, check_ulp, dev_bf16, dev_f32,
                          dev_i32, f64_to_dev_bf16, sample_rows)
@@ -77,6 +77,25 @@ def test_compress_mean_moba_full():
     for h in range(cfg.num_kv_heads):
         ref = oracle.compress_mean(f64(k[0, h]), cfg.cmp_block, cfg.cmp_stride)
         check_ulp(g[0, h], ref, f"moba mean key h{h}")
+
+
+@pytest.mark.parametrize("cfg", [
+    TINY.replace(name="mean_d64_l32s16", seq_len=1000, num_kv_heads=2, d_k=64, d_v=64, cmp_block=32, cmp_stride=16,
+                 phi=PHI_MEAN, seed=51),
+    TINY.replace(name="mean_d192_l64s32", seq_len=777, num_kv_heads=3, d_k=192, d_v=128, cmp_block=64, cmp_stride=32,
+                 slc_block=64, phi=PHI_MEAN, seed=52)], ids=lambda c: c.name)
+def test_compress_mean_shapes(cfg):
+    """Mean pooling for the other head dims, with overlapping blocks (s < l) and a ragged
+    tail of tokens that no block covers: every block within one bf16 ulp of the fp64 mean."""
+    announce(f"compress mean {cfg.name}")
+    rng = np.random.Generator(np.random.PCG64(cfg.seed))
+    k = inputs._normal_bf16(rng, (1, cfg.num_kv_heads, cfg.seq_len, cfg.d_k))
+    kc, _ = ops.compress(cfg, dev_bf16(k))
+    torch.cuda.synchronize()
+    g = bf16_dev_to_f64(kc)
+    assert g.shape == (1, cfg.num_kv_heads, cfg.n_cmp, cfg.d_k)
+    for h in range(cfg.num_kv_heads):
+        check_ulp(g[0, h], oracle.compress_mean(f64(k[0, h]), cfg.cmp_block, cfg.cmp_stride), f"{cfg.name} h{h}")
 
 
 # ---------------------------------------------------------------------------
