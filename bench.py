@@ -268,7 +268,7 @@ def main():
     # every kernel the dominant call launches (the first is the main one)
     dom_launches = [["compress_linear_kernel", "transpose_w_kernel", "pe_bias_kernel"],
                     ["cmp_attn_kernel", "cmp_vmax_kernel", "tile_cmp_kernel", "select_from_scores_kernel"],
-                    ["sparse_attn_kernel", "tile_kv_kernel"]][dom]
+                    ["sparse_attn_kernel", "cmp_vmax_kernel", "tile_cmp_kernel"]][dom]
     dom_src = [["dynamic_block_sparse_nsa_amd/csrc/compress.hip"],
                ["dynamic_block_sparse_nsa_amd/csrc/score_select.hip", "dynamic_block_sparse_nsa_amd/csrc/select.hpp"],
                ["dynamic_block_sparse_nsa_amd/csrc/sparse_attn.hip"]][dom]
