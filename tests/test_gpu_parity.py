@@ -195,6 +195,32 @@ def test_sparse_attn_single_branch(branches):
     _attn_case(TINY, np.arange(TINY.seq_len, dtype=np.int32), branches=branches)
 
 
+def test_sparse_attn_value_scales():
+    """The attention kernel multiplies P by an fp16 copy of V scaled per (sequence, group) by
+    a power of two.  Groups whose values are 1e5 times (beyond fp16's range unscaled) and
+    1e-4 times those of others, in a batch of two: each group's heads within the output bar
+    once both sides are divided by the group's factor."""
+    cfg = TINY.replace(name="vscale", batch=2, seq_len=700, num_kv_heads=2, heads_per_group=4, d_k=128, d_v=128,
+                       top_n=5, window=96, branches=BR_SLC | BR_WIN, seed=71)
+    announce("sparse_attn value scales")
+    inp = inputs.prefill_inputs(cfg)
+    scale = np.array([[1e5, 1.0], [1e-4, 3.0]])   # [B, Hkv]
+    v_dev = f64_to_dev_bf16(f64(inp["v"]) * scale[:, :, None, None])
+    v = bf16_dev_to_f64(v_dev)                   # the values the kernel sees
+    sel = inputs.block_lists(cfg, seed=271)
+    out = ops.sparse_attn_fwd(cfg, dev_bf16(inp["q"]), dev_bf16(inp["k"]), v_dev, dev_i32(sel), None,
+                              dev_f32(inp["gates"]))
+    torch.cuda.synchronize()
+    gout = bf16_dev_to_f64(out)
+    rows = np.arange(cfg.seq_len, dtype=np.int32)
+    G = cfg.heads_per_group
+    for b in range(cfg.batch):
+        ref = oracle.attend(cfg, f64(inp["q"][b]), rows, f64(inp["k"][b]), v[b], sel[b], None, inp["gates"][b])["out"]
+        for g in range(cfg.num_kv_heads):
+            hs = slice(g * G, (g + 1) * G)
+            check_close(gout[b, :, hs] / scale[b, g], ref[:, hs] / scale[b, g], f"vscale b={b} g={g} x{scale[b, g]:g}")
+
+
 # ---------------------------------------------------------------------------
 # end to end (the GPU chain against the oracle chain)
 # ---------------------------------------------------------------------------
