@@ -7,8 +7,8 @@
 //   decode_cmp_kernel     split s covers 256 compressed keys of one (sequence, group);
 //                         4 waves x 64 keys, the group's heads packed in the MFMA column
 //                         tile; every load of the split is issued before any math.
-//                         Emits, relative to the split's per-head max m: the sum l, the
-//                         unnormalized o^T, and per-head partial block sums
+//                         Emits, relative to the split's per-head max m: the sum l, o^T
+//                         normalized by l (fp16: |o| <= max |V|), and per-head block sums
 //                         A[h][j] = sum over this split's keys overlapping block j of
 //                         2^(x - m).  The same launch runs the sliding window's item
 //                         groups (below), which do not depend on the selection.
@@ -20,9 +20,10 @@
 //   decode_attn_kernel    the selected blocks' item groups.  An item group is 4 waves, one
 //                         item each (a selected block, or a 64-token piece of the window):
 //                         exact softmax over its keys; the 4 items are combined in LDS into
-//                         one partial (m, l, o^T).
-//   decode_merge_kernel   o_cmp = sum_s w_s o_s, merges the partials of each branch and
-//                         applies the gates; one thread per output element.
+//                         one partial (m, l, o^T / l).
+//   decode_merge_kernel   o_cmp = sum_s w_s l_s o_s (o_s the normalized split partial),
+//                         merges the partials of each branch and applies the gates; one
+//                         thread per output element.
 // Value rows stay key-major: each wave stores its value tile row-major in LDS and builds
 // the V^T MFMA operand with the gfx950 transposing LDS read.
 #include "common.hpp"
@@ -264,13 +265,14 @@ __device__ void attn_group(const DecodeParams& p, int gi, int g, int b, unsigned
         e[w] = M > -INFINITY ? fast_exp2(mm[w * 16 + os.h] - M) : 0.f;
         L += e[w] * ml[w * 16 + os.h];
     }
+    const float inv = L > 0.f ? 1.0f / L : 0.f;   // stored normalized (within fp16's range)
     float acc[OutSlice<DV>::N];
 #pragma unroll
     for (int i = 0; i < OutSlice<DV>::N; ++i) {
         float a = 0.f;
 #pragma unroll
         for (int w = 0; w < 4; ++w) a += e[w] * mo[(w * 16 + os.h) * (DV + 4) + os.d0 + i];
-        acc[i] = a;
+        acc[i] = a * inv;
     }
     store_f16(p.att_o + (ib * 16 + os.h) * DV + os.d0, acc);
     if (os.d0 == 0) {
@@ -369,13 +371,15 @@ __global__ __launch_bounds__(256, 2) void decode_cmp_kernel(DecodeParams p) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) psum[li * kPsumStride + 64 * wave + 16 * kt + 4 * lq + r] = pv[kt][r];
     __syncthreads();
-    {
+    {   // stored normalized by the split's sum (|o| <= max |V|: within fp16's range)
         const OutSlice<DV> os;
+        const float Ls = wl[os.h] + wl[16 + os.h] + wl[32 + os.h] + wl[48 + os.h];
+        const float inv = Ls > 0.f ? 1.0f / Ls : 0.f;
         float v[OutSlice<DV>::N];
 #pragma unroll
         for (int i = 0; i < OutSlice<DV>::N; ++i) {
             const float* q = po + os.h * (DV + 4) + os.d0 + i;
-            v[i] = ((q[0] + q[16 * (DV + 4)]) + q[2 * 16 * (DV + 4)]) + q[3 * 16 * (DV + 4)];
+            v[i] = (((q[0] + q[16 * (DV + 4)]) + q[2 * 16 * (DV + 4)]) + q[3 * 16 * (DV + 4)]) * inv;
         }
         store_f16(p.part_o + (pbase * 16 + os.h) * DV + os.d0, v);
     }
@@ -470,8 +474,8 @@ __device__ void select_unit(const DecodeParams& p, int g, int b, float* sm) {
             const int s0 = q + 4 * i;
             if (s0 < ns) {
                 const float w = (L > 0.f && mv[i] > -INFINITY) ? fast_exp2(mv[i] - lse2) : 0.f;
-                f[s0 * 16 + hh] = w;
-                p.cmp_w[(pb0 + s0) * 16 + hh] = w;
+                f[s0 * 16 + hh] = w;                            // block scores: the split's probabilities
+                p.cmp_w[(pb0 + s0) * 16 + hh] = w * lv[i];      // o_cmp: the split's normalized partial
             }
         }
     }
@@ -587,7 +591,7 @@ __device__ void merge_unit(const DecodeParams& p, int g, int b, float* wsm) {   
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
             const int it = i0 + q + 4 * i;
-            if (it < i1) wsm[it * 16 + h4] = (mv[i] > -INFINITY && L > 0.f) ? fast_exp2(mv[i] - M) / L : 0.f;
+            if (it < i1) wsm[it * 16 + h4] = (mv[i] > -INFINITY && L > 0.f) ? fast_exp2(mv[i] - M) * lv[i] / L : 0.f;
         }
     }
     __syncthreads();

@@ -294,8 +294,10 @@ def test_decode_shape_matrix(cfg):
 # ---------------------------------------------------------------------------
 # decode
 # ---------------------------------------------------------------------------
-def _decode_case(cfg, cache_len, cmp_from_oracle):
+def _decode_case(cfg, cache_len, cmp_from_oracle, v_scale=1.0):
     inp = inputs.decode_inputs(cfg, cache_len=cache_len)
+    if v_scale != 1.0:
+        inp["v"] = inputs.f32_to_bf16_bits((f64(inp["v"]) * v_scale).astype(np.float32))
     if cmp_from_oracle:
         per_b = [pipeline.compress_all(cfg, f64(inp["k"][b]), f64(inp["v"][b]), f64(inp["w_k"]), f64(inp["w_v"]),
                                        f64(inp["pe_k"]), f64(inp["pe_v"])) for b in range(cfg.batch)]
@@ -322,7 +324,15 @@ def _decode_case(cfg, cache_len, cmp_from_oracle):
         scores.append(ss["scores"][0]); pos.append(t)
     check_selection(gsel, np.stack(refs_sel), np.stack(gaps), np.stack(scores), np.array(pos), cfg,
                     f"{cfg.name} decode selection")
-    check_close(gout, np.stack(refs_out), f"{cfg.name} decode output")
+    check_close(gout / v_scale, np.stack(refs_out) / v_scale, f"{cfg.name} decode output")
+
+
+def test_decode_large_values():
+    """Values 3000 times the usual scale: each decode partial is a sum over up to 256 keys,
+    so it is stored normalized by its own softmax sum to stay inside fp16's range."""
+    cfg = DECODE.replace(name="decode_large_v", batch=3, seq_len=4096, seed=24)
+    announce("decode large values")
+    _decode_case(cfg, np.array([4096, 2000, 700], dtype=np.int32), cmp_from_oracle=True, v_scale=3000.0)
 
 
 def test_decode_varlen_small():
