@@ -147,7 +147,9 @@ nsa_status nsa_select_from_scores(const nsa_config* cfg, const float* scores, in
  *   caller (as produced by nsa_score_select) when NSA_BR_CMP is set.
  * sel_idx rows must list distinct blocks <= t / l' in ascending order, padded with -1 at the
  * end (as nsa_score_select writes them).  gate_logits NULL = weight 1.
- * O is bf16 [B, T, H, d_v]. */
+ * O is bf16 [B, T, H, d_v].  Values: any bf16 magnitude (V's fp16 copy is scaled per
+ * sequence and group by a power of two), except in the MoBA configuration (G = 1, selected
+ * branch only), whose per-block partial outputs are fp16 and need |V| < 65504. */
 nsa_status nsa_sparse_attn_fwd(const nsa_config* cfg, const void* Q, const void* K, const void* V,
                                const int32_t* sel_idx, const float* o_cmp, const float* gate_logits,
                                void* O, void* ws, size_t ws_bytes, void* stream);
@@ -160,6 +162,8 @@ nsa_status nsa_sparse_attn_fwd(const nsa_config* cfg, const void* Q, const void*
  *   q [B, H, d_k] bf16; caches [B, H_kv, L, d] bf16; compressed caches [B, H_kv, N_cmp(L), d];
  *   cache_len [B] int32 device array (1 <= cache_len <= L); gate_logits [B, H, 3] (NULL = 1);
  *   O [B, H, d_v] bf16; sel_idx_out [B, H_kv, top_n] (optional).
+ * Partial outputs pass through fp16 normalized by their softmax sums: |V| and |V_cmp| must
+ * stay below 65504.
  * NSA_ERR_UNSUPPORTED for a mode other than linear phi with compressed-overlap scores, more
  * than 8192 compressed keys, top_n > 32, windows over 1920 tokens, or
  * (slc_block + cmp_block) / cmp_stride - 1 > 256. */
