@@ -393,20 +393,17 @@ nsa_status sparse_attn_fwd_impl(const nsa_config* cfg, const void* Q, const void
     using nsa::u16;
     u16* kf = at<u16>(ws, w.kf);
     u16* vf = at<u16>(ws, w.vf);
-    const bool moba = use_block_major(s) && !train;
-    // fragment order: V in bf16 for the block-major kernel, as scaled fp16 for the attention kernel
-    if (moba ? !nsa::launch_tile_kv(s.dk, s.dv, static_cast<const u16*>(K), static_cast<const u16*>(V), kf, vf,
-                                    s.B * s.Hkv, s.T, w.tpad, hs)
-             : !nsa::launch_tile_cmp(s.dk, s.dv, static_cast<const u16*>(K), static_cast<const u16*>(V),
-                                     at<uint32_t>(ws, w.vmax), at<int>(ws, w.vexp), kf, vf, s.B * s.Hkv, s.T, w.tpad,
-                                     hs))
+    // fragment order, V as fp16 scaled by a power of two per (sequence, group)
+    if (!nsa::launch_tile_cmp(s.dk, s.dv, static_cast<const u16*>(K), static_cast<const u16*>(V),
+                              at<uint32_t>(ws, w.vmax), at<int>(ws, w.vexp), kf, vf, s.B * s.Hkv, s.T, w.tpad, hs))
         return fail(NSA_ERR_UNSUPPORTED, "no layout kernel");
-    if (moba) {
+    if (use_block_major(s) && !train) {
         if ((long long)s.T >= (1LL << 26)) return fail(NSA_ERR_UNSUPPORTED, "sequence too long for the block lists");
         nsa::MobaParams m{};
         m.Q = static_cast<const u16*>(Q);
         m.Kf = kf;
         m.Vf = vf;
+        m.vexp = at<int>(ws, w.vexp);
         m.sel = sel_idx;
         m.gates = gate_logits;
         m.O = static_cast<u16*>(O);

@@ -79,15 +79,14 @@ bool launch_sparse_attn(int DK, int DV, const AttnParams& p, int B, hipStream_t 
 bool launch_sparse_attn_stats(int DK, int DV, const AttnParams& p, hipStream_t st);
 // the backward statistics from a training forward's saved LSE and outputs (no recompute)
 void launch_stats_from_saved(int DV, const AttnParams& p, hipStream_t st);
-bool launch_tile_kv(int DK, int DV, const u16* K, const u16* V, u16* Kf, u16* Vf, int BG, int T, int Tpad,
-                    hipStream_t st);
 
 // ---- G = 1 selected-only attention (MoBA): inverted, block-major schedule ----
 constexpr int kMobaChunk = 1024;   // tokens per histogram / scatter workgroup
 struct MobaParams {
     const u16* Q;              // [B,T,H,DK] (H = Hkv)
     const u16* Kf;             // fragment-order K (see AttnParams)
-    const u16* Vf;             // fragment-order V
+    const u16* Vf;             // fragment-order V, fp16 scaled by 2^-vexp (launch_tile_cmp)
+    const int* vexp;           // [B*Hkv]
     const int32_t* sel;        // [B,T,Hkv,top_n]
     const float* gates;        // [B,T,H,3] or null (slot 1 is used)
     u16* O;                    // [B,T,H,DV]

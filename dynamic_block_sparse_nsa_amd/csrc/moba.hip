@@ -300,18 +300,15 @@ __global__ __launch_bounds__(256, 2) void moba_attn_kernel(MobaParams p) {
             for (int dt = 0; dt < NDT; ++dt) o[c][dt] *= alpha;
         }
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            bf16x8 bh2[2], bl2[2];
+        for (int u = 0; u < 2; ++u) {   // P in fp16 against the scaled fp16 V copy: one product
+            f16x8 ph[2];
 #pragma unroll
-            for (int c = 0; c < 2; ++c) pack_p_split(pv[2 * u][c], pv[2 * u + 1][c], bh2[c], bl2[c]);
+            for (int c = 0; c < 2; ++c) ph[c] = pack_p_h(pv[2 * u][c], pv[2 * u + 1][c]);
 #pragma unroll
             for (int dt = 0; dt < NDT; ++dt) {
-                const bf16x8 a = ld8(&vbuf[buf][((u * NDT + dt) * 64 + lane) * 8]);
+                const f16x8 a = ld8h(&vbuf[buf][((u * NDT + dt) * 64 + lane) * 8]);
 #pragma unroll
-                for (int c = 0; c < 2; ++c) {
-                    o[c][dt] = mfma16(a, bh2[c], o[c][dt]);
-                    o[c][dt] = mfma16(a, bl2[c], o[c][dt]);
-                }
+                for (int c = 0; c < 2; ++c) o[c][dt] = mfma16h(a, ph[c], o[c][dt]);
             }
         }
         __builtin_amdgcn_sched_barrier(0);   // the staging stores stay after this tile's math
@@ -327,8 +324,8 @@ __global__ __launch_bounds__(256, 2) void moba_attn_kernel(MobaParams p) {
             p.part_m[pr] = m[c];
             p.part_l[pr] = L;
         }
-        // the slot's output normalized by its own sum (|o| <= max |v|), in fp16: half the
-        // bytes of the partial round trip, 2^-11 relative rounding
+        // the slot's output normalized by its own sum, in V's scaled units (|o| <= 2^14), in
+        // fp16: half the bytes of the partial round trip, 2^-11 relative rounding
         const float inv = L > 0.f ? 1.f / L : 0.f;
         u16* op = p.part_o + pr * DV + 4 * lq;
 #pragma unroll
@@ -375,7 +372,8 @@ __global__ __launch_bounds__(256) void moba_merge_kernel(MobaParams p) {
         }
     }
     const float g = p.gates ? sigmoidf_(p.gates[row * 3 + 1]) : 1.f;
-    const float inv = L > 0.f ? g / L : 0.f;
+    const size_t bh = row / ((size_t)p.T * p.Hkv) * p.Hkv + row % p.Hkv;
+    const float inv = L > 0.f ? ldexpf(g / L, p.vexp[bh]) : 0.f;   // V's scaling undone
     const u32x2 v = {(uint32_t)f2bf(acc[0] * inv) | ((uint32_t)f2bf(acc[1] * inv) << 16),
                      (uint32_t)f2bf(acc[2] * inv) | ((uint32_t)f2bf(acc[3] * inv) << 16)};
     st_stream(v, reinterpret_cast<u32x2*>(p.O + row * DV) + li);

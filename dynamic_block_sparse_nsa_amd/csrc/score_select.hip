@@ -78,11 +78,16 @@ __global__ __launch_bounds__(256) void cmp_vmax_kernel(const u16* __restrict__ V
                                                        int N, int DV) {
     __shared__ uint32_t red[256];
     const size_t unit = blockIdx.y;
-    const size_t n = (size_t)N * DV, per = (n + kVmaxParts - 1) / kVmaxParts;
-    const size_t lo = blockIdx.x * per, hi = min(lo + per, n);
+    // 16-byte loads: n and each part's bounds are multiples of 8 elements (DV is)
+    const size_t n = (size_t)N * DV, per = ((n + kVmaxParts - 1) / kVmaxParts + 7) / 8 * 8;
+    const size_t lo = min(blockIdx.x * per, n), hi = min(lo + per, n);
     const u16* v = V + unit * n;
     uint32_t mx = 0;
-    for (size_t i = lo + threadIdx.x; i < hi; i += 256) mx = max(mx, (uint32_t)(v[i] & 0x7FFFu));
+    for (size_t i = lo + 8 * threadIdx.x; i < hi; i += 8 * 256) {
+        const u32x4 w = *reinterpret_cast<const u32x4*>(v + i);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) mx = max(mx, max(w[k] & 0x7FFFu, (w[k] >> 16) & 0x7FFFu));
+    }
     red[threadIdx.x] = mx;
     __syncthreads();
     for (int off = 128; off > 0; off >>= 1) {

@@ -171,47 +171,6 @@ struct GatherChunk {
     }
 };
 
-// Copy of K and V into fragment order with V in bf16 (the MoBA block-major kernel's
-// layout), one workgroup per 32-key chunk of one (b, g):
-// row-major tiles are staged in LDS with coalesced loads; K fragments are plain 16-byte
-// pieces of a row, V^T fragments come from the transposing LDS read.
-template <int DK, int DV>
-__global__ __launch_bounds__(256) void tile_kv_kernel(const u16* __restrict__ K, const u16* __restrict__ V,
-                                                      u16* __restrict__ Kf, u16* __restrict__ Vf, int T, int Tpad) {
-    constexpr int NDS = DK / 32, NDT = DV / 16;
-    constexpr int KSTR = DK + 8, VSTR = DV + 16;
-    __shared__ __attribute__((aligned(16))) u16 ks[32 * KSTR];
-    __shared__ __attribute__((aligned(16))) u16 vs[32 * VSTR];
-    const int c = blockIdx.x;
-    const size_t bg = blockIdx.y;
-    const u16* kg = K + bg * (size_t)T * DK;
-    const u16* vg = V + bg * (size_t)T * DV;
-    for (int idx = threadIdx.x; idx < 32 * DK / 8; idx += 256) {
-        const int r = idx / (DK / 8), col = (idx % (DK / 8)) * 8;
-        const int key = 32 * c + r;
-        const u32x4 v = key < T ? *reinterpret_cast<const u32x4*>(kg + (size_t)key * DK + col) : u32x4{0u, 0u, 0u, 0u};
-        *reinterpret_cast<u32x4*>(&ks[r * KSTR + col]) = v;
-    }
-    for (int idx = threadIdx.x; idx < 32 * DV / 8; idx += 256) {
-        const int r = idx / (DV / 8), col = (idx % (DV / 8)) * 8;
-        const int key = 32 * c + r;
-        const u32x4 v = key < T ? *reinterpret_cast<const u32x4*>(vg + (size_t)key * DV + col) : u32x4{0u, 0u, 0u, 0u};
-        *reinterpret_cast<u32x4*>(&vs[r * VSTR + col]) = v;
-    }
-    __syncthreads();
-    u16* kout = Kf + bg * (size_t)Tpad * DK + kfrag<DK>(2 * c, 0);
-    for (int idx = threadIdx.x; idx < 2 * NDS * 64; idx += 256) {
-        const int kk = idx / (NDS * 64), ds = (idx / 64) % NDS, ln = idx % 64;
-        const int li = ln & 15, lq = ln >> 4;
-        *reinterpret_cast<u32x4*>(kout + (size_t)idx * 8) =
-            *reinterpret_cast<const u32x4*>(&ks[(16 * kk + li) * KSTR + 32 * ds + 8 * lq]);
-    }
-    u16* vout = Vf + bg * (size_t)Tpad * DV + vfrag<DV>(c, 0);
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    for (int dt = wave; dt < NDT; dt += 4)
-        *reinterpret_cast<bf16x8*>(vout + (size_t)(dt * 64 + lane) * 8) = ld_vt_tr(vs, VSTR, 0, 16 * dt);
-}
-
 }  // namespace
 
 // MODE 0: the forward.  MODE 2: the forward that also saves, for the backward, the selected
@@ -444,16 +403,6 @@ bool launch_sparse_attn_stats(int DK, int DV, const AttnParams& p, hipStream_t s
     if (DK == 192 && DV == 128) sparse_attn_kernel<192, 128, 1><<<grid, 256, 0, st>>>(p);
     else if (DK == 128 && DV == 128) sparse_attn_kernel<128, 128, 1><<<grid, 256, 0, st>>>(p);
     else if (DK == 64 && DV == 64) sparse_attn_kernel<64, 64, 1><<<grid, 256, 0, st>>>(p);
-    else return false;
-    return true;
-}
-
-bool launch_tile_kv(int DK, int DV, const u16* K, const u16* V, u16* Kf, u16* Vf, int BG, int T, int Tpad,
-                    hipStream_t st) {
-    dim3 grid(Tpad / 32, BG);
-    if (DK == 192 && DV == 128) tile_kv_kernel<192, 128><<<grid, 256, 0, st>>>(K, V, Kf, Vf, T, Tpad);
-    else if (DK == 128 && DV == 128) tile_kv_kernel<128, 128><<<grid, 256, 0, st>>>(K, V, Kf, Vf, T, Tpad);
-    else if (DK == 64 && DV == 64) tile_kv_kernel<64, 64><<<grid, 256, 0, st>>>(K, V, Kf, Vf, T, Tpad);
     else return false;
     return true;
 }

@@ -148,8 +148,8 @@ nsa_status nsa_select_from_scores(const nsa_config* cfg, const float* scores, in
  * sel_idx rows must list distinct blocks <= t / l' in ascending order, padded with -1 at the
  * end (as nsa_score_select writes them).  gate_logits NULL = weight 1.
  * O is bf16 [B, T, H, d_v].  Values: any bf16 magnitude (V's fp16 copy is scaled per
- * sequence and group by a power of two), except in the MoBA configuration (G = 1, selected
- * branch only), whose per-block partial outputs are fp16 and need |V| < 65504. */
+ * sequence and group by a power of two; the MoBA schedule's fp16 partials stay in those
+ * scaled units). */
 nsa_status nsa_sparse_attn_fwd(const nsa_config* cfg, const void* Q, const void* K, const void* V,
                                const int32_t* sel_idx, const float* o_cmp, const float* gate_logits,
                                void* O, void* ws, size_t ws_bytes, void* stream);

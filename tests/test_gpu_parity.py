@@ -407,6 +407,25 @@ def test_moba(T, top_n):
     check_close(bf16_dev_to_f64(out)[0, rows], at["out"], f"moba{T} output")
 
 
+def test_block_major_large_values():
+    """The block-major MoBA schedule keeps its per-slot partials in fp16 in V's scaled units,
+    so values far beyond fp16's range (1e5) pass; every row of a ragged batch of two."""
+    cfg = MOBA.replace(name="bm_large_v", batch=2, seq_len=900, num_kv_heads=2, cmp_block=64, cmp_stride=64,
+                       slc_block=64, top_n=3, seed=23)
+    announce("block-major large values")
+    inp = inputs.prefill_inputs(cfg)
+    v_dev = f64_to_dev_bf16(f64(inp["v"]) * 1e5)
+    v = bf16_dev_to_f64(v_dev)
+    lists = inputs.block_lists(cfg, seed=601)
+    out = ops.sparse_attn_fwd(cfg, dev_bf16(inp["q"]), dev_bf16(inp["k"]), v_dev, dev_i32(lists))
+    torch.cuda.synchronize()
+    gout = bf16_dev_to_f64(out)
+    rows = np.arange(cfg.seq_len, dtype=np.int32)
+    for b in range(cfg.batch):
+        ref = oracle.attend(cfg, f64(inp["q"][b]), rows, f64(inp["k"][b]), v[b], lists[b])["out"]
+        check_close(gout[b] / 1e5, ref / 1e5, f"block-major large values b={b}")
+
+
 @pytest.mark.parametrize("case", ["b2_lp64_gated", "lp128_own_optional"])
 def test_block_major_all_rows(case):
     """G = 1 with only the selected branch runs the block-major schedule (per-block query
