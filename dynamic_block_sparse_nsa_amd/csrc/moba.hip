@@ -352,10 +352,46 @@ __global__ __launch_bounds__(256) void moba_merge_kernel(MobaParams p) {
     if (row >= (size_t)p.B * p.T * p.Hkv) return;
     const int32_t* sel = p.sel + row * p.top_n;
     float M = -INFINITY;
-    for (int s = 0; s < p.top_n; ++s)
-        if (sel[s] >= 0) M = fmaxf(M, p.part_m[row * p.top_n + s]);
     float L = 0.f;
     f32x4 acc = zero4();
+    auto half4 = [](const u32x2& hv) {
+        return f32x4{(float)__builtin_bit_cast(_Float16, (u16)(hv[0] & 0xFFFFu)),
+                     (float)__builtin_bit_cast(_Float16, (u16)(hv[0] >> 16)),
+                     (float)__builtin_bit_cast(_Float16, (u16)(hv[1] & 0xFFFFu)),
+                     (float)__builtin_bit_cast(_Float16, (u16)(hv[1] >> 16))};
+    };
+    constexpr int SMAX = 8;
+    if (p.top_n <= SMAX) {
+        // every slot's list entry, (max, sum) and output slice requested together (one round
+        // trip); slots with no block may hold stale values and are dropped by selects
+        int js[SMAX];
+        float ms[SMAX], ls[SMAX];
+        u32x2 hv[SMAX];
+#pragma unroll
+        for (int s = 0; s < SMAX; ++s)
+            if (s < p.top_n) {
+                js[s] = sel[s];
+                ms[s] = p.part_m[row * p.top_n + s];
+                ls[s] = p.part_l[row * p.top_n + s];
+                hv[s] = ld_stream(reinterpret_cast<const u32x2*>(p.part_o + (row * p.top_n + s) * DV) + li);
+            }
+        bool ok[SMAX];
+#pragma unroll
+        for (int s = 0; s < SMAX; ++s) {
+            ok[s] = s < p.top_n && js[s] >= 0 && ms[s] > -INFINITY;
+            M = ok[s] ? fmaxf(M, ms[s]) : M;
+        }
+#pragma unroll
+        for (int s = 0; s < SMAX; ++s) {
+            const float w = ok[s] ? fast_exp2(ms[s] - M) * ls[s] : 0.f;   // the slot's weight
+            L += w;
+            const f32x4 o = half4(hv[s]);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) acc[k] += ok[s] ? w * o[k] : 0.f;
+        }
+    } else {
+    for (int s = 0; s < p.top_n; ++s)
+        if (sel[s] >= 0) M = fmaxf(M, p.part_m[row * p.top_n + s]);
     if (M > -INFINITY) {
         for (int s = 0; s < p.top_n; ++s) {
             if (sel[s] < 0) continue;
@@ -364,12 +400,9 @@ __global__ __launch_bounds__(256) void moba_merge_kernel(MobaParams p) {
             const float w = fast_exp2(ms - M) * p.part_l[row * p.top_n + s];   // the slot's weight
             L += w;
             const u32x2 hv = ld_stream(reinterpret_cast<const u32x2*>(p.part_o + (row * p.top_n + s) * DV) + li);
-            const f32x4 o = {(float)__builtin_bit_cast(_Float16, (u16)(hv[0] & 0xFFFFu)),
-                             (float)__builtin_bit_cast(_Float16, (u16)(hv[0] >> 16)),
-                             (float)__builtin_bit_cast(_Float16, (u16)(hv[1] & 0xFFFFu)),
-                             (float)__builtin_bit_cast(_Float16, (u16)(hv[1] >> 16))};
-            acc += w * o;
+            acc += w * half4(hv);
         }
+    }
     }
     const float g = p.gates ? sigmoidf_(p.gates[row * 3 + 1]) : 1.f;
     const size_t bh = row / ((size_t)p.T * p.Hkv) * p.Hkv + row % p.Hkv;
