@@ -197,7 +197,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: the NSA forward shards by KV group / batch with no exchange, "
-              "and this build runs on a single MI355X; use --gpus 1", file=sys.stderr)
+              "and the benchmark runs on a single MI355X; use --gpus 1", file=sys.stderr)
         sys.exit(2)
 
     import torch

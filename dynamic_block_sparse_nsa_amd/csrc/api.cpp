@@ -750,7 +750,7 @@ const char* nsa_status_string(nsa_status status) {
         case NSA_OK: return "ok";
         case NSA_ERR_NULL: return "required pointer is NULL";
         case NSA_ERR_SHAPE: return "inconsistent or invalid sizes";
-        case NSA_ERR_UNSUPPORTED: return "shape not implemented by this build";
+        case NSA_ERR_UNSUPPORTED: return "shape not implemented by the library's kernels";
         case NSA_ERR_WORKSPACE: return "workspace missing or too small";
         case NSA_ERR_HIP: return "HIP launch failure";
     }

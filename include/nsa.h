@@ -54,7 +54,7 @@ typedef enum {
     NSA_OK = 0,
     NSA_ERR_NULL = 1,          /* a required pointer is NULL */
     NSA_ERR_SHAPE = 2,         /* sizes are inconsistent or non-positive */
-    NSA_ERR_UNSUPPORTED = 3,   /* a shape this build's kernels do not implement */
+    NSA_ERR_UNSUPPORTED = 3,   /* a shape the library's kernels do not implement */
     NSA_ERR_WORKSPACE = 4,     /* workspace NULL or smaller than nsa_workspace_size */
     NSA_ERR_HIP = 5            /* a HIP launch failed (see nsa_last_error_detail) */
 } nsa_status;
