@@ -61,6 +61,9 @@ def lib():
         L.oracle_nsa_bwd_rows.argtypes = ([ctypes.c_int] * 11 + [ctypes.c_double, ctypes.c_int, _D, _I, ctypes.c_int]
                                           + [_D] * 4 + [_I] + [_D] * 4)
         L.oracle_nsa_bwd_rows.restype = ctypes.c_int
+        L.oracle_nsa_bwd_keys.argtypes = ([ctypes.c_int] * 11 + [ctypes.c_double, ctypes.c_int] + [_D] * 5 + [_I]
+                                          + [_D] * 2 + [_I, ctypes.c_int, _I, ctypes.c_int] + [_D] * 4)
+        L.oracle_nsa_bwd_keys.restype = ctypes.c_int
         L.oracle_num_threads.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -291,4 +294,38 @@ def nsa_bwd_rows(cfg, Q_rows, rows, K, V, Kc, Vc, sel_rows, gates_rows, dO_rows,
                                    _pi(sel_rows), _pd(gates_rows), _pd(dO_rows), _pd(out["dq"]), _pd(out["dgates"]))
     if rc != 0:
         raise MemoryError("oracle_nsa_bwd_rows failed")
+    return out
+
+
+def nsa_bwd_keys(cfg, Q, K, V, Kc, Vc, sel, gates, dO, raw_keys, cmp_keys=(), branches=None) -> dict:
+    """The key side of nsa_bwd for listed keys of one batch element: raw token indices
+    ``raw_keys`` and compressed-block indices ``cmp_keys`` (both applied to every KV group).
+    Q, K, V, Kc, Vc, sel, gates, dO as for nsa_bwd.  Returns dict(dk [Hkv,n_raw,dk],
+    dv [Hkv,n_raw,dv], dkc [Hkv,n_ck,dk], dvc [Hkv,n_ck,dv]) equal to nsa_bwd's gradients at
+    those keys."""
+    Hkv, G = cfg.num_kv_heads, cfg.heads_per_group
+    branches = cfg.branches if branches is None else branches
+    Q, K, V, dO = _d(Q), _d(K), _d(V), _d(dO)
+    sel = _i(sel)
+    T = Q.shape[0]
+    raw = _i(np.unique(np.asarray(raw_keys, dtype=np.int64)))
+    ck = _i(np.unique(np.asarray(cmp_keys, dtype=np.int64)))
+    use_c = bool(branches & 1)
+    Kc = _d(Kc) if use_c else None
+    Vc = _d(Vc) if use_c else None
+    n_cmp = Kc.shape[1] if use_c else 0
+    if not use_c:
+        ck = _i(np.zeros(0))
+    assert raw.size == 0 or (raw.min() >= 0 and raw.max() < T)
+    assert ck.size == 0 or (ck.min() >= 0 and ck.max() < n_cmp)
+    gates = None if gates is None else _d(gates)
+    out = {"dk": np.zeros((Hkv, raw.size, cfg.d_k)), "dv": np.zeros((Hkv, raw.size, cfg.d_v)),
+           "dkc": np.zeros((Hkv, ck.size, cfg.d_k)), "dvc": np.zeros((Hkv, ck.size, cfg.d_v)),
+           "raw_keys": raw, "cmp_keys": ck}
+    rc = lib().oracle_nsa_bwd_keys(Hkv, G, cfg.d_k, cfg.d_v, T, n_cmp, cfg.cmp_block, cfg.cmp_stride, cfg.slc_block,
+                                   sel.shape[-1], cfg.window, float(cfg.scale), branches, _pd(Q), _pd(K), _pd(V),
+                                   _pd(Kc), _pd(Vc), _pi(sel), _pd(gates), _pd(dO), _pi(raw), raw.size, _pi(ck),
+                                   ck.size, _pd(out["dk"]), _pd(out["dv"]), _pd(out["dkc"]), _pd(out["dvc"]))
+    if rc != 0:
+        raise MemoryError("oracle_nsa_bwd_keys failed")
     return out

@@ -657,6 +657,137 @@ ORACLE_API int oracle_nsa_bwd_rows(int H_kv, int G, int dk, int dv, int n_tok, i
     return bad ? -2 : 0;
 }
 
+/* The key-side part of oracle_nsa_bwd for listed keys only, so that keys of a long
+ * sequence can be checked without forming every gradient.  raw_keys [n_raw] are token
+ * indices and cmp_keys [n_ck] compressed-block indices (each ascending, no repeats); both
+ * lists apply to every KV group.  Outputs (overwritten): dK_l [H_kv, n_raw, dk], dV_l
+ * [H_kv, n_raw, dv], dKc_l [H_kv, n_ck, dk], dVc_l [H_kv, n_ck, dv] (the last two may be NULL
+ * when n_ck = 0) hold exactly the sums oracle_nsa_bwd forms for those keys: over every
+ * (token, head) row whose branch sees the key, dk += scale * da * q and dv += sigma * p * dO,
+ * with that row's softmax taken over all of the branch's keys.  Rows that see no listed key
+ * are skipped.  Other arguments as for oracle_nsa_bwd.  Returns 0, or -2 when memory runs
+ * out. */
+static void list_bwd_keys(const double* q, const double* K, const double* V, int dk, int dv, double scale,
+                          const int* keys, int nk, const double* dout, double sig, const int* slot,
+                          double* logit, double* p, double* dK_l, double* dV_l)
+{
+    for (int c = 0; c < nk; ++c) logit[c] = scale * dot(q, K + (size_t)keys[c] * dk, dk);
+    softmax(logit, nk, p);
+    double pdp = 0.0;
+    for (int c = 0; c < nk; ++c) {
+        logit[c] = sig * dot(dout, V + (size_t)keys[c] * dv, dv);   /* dp_k */
+        pdp += p[c] * logit[c];
+    }
+    for (int c = 0; c < nk; ++c) {
+        const int sl = slot[keys[c]];
+        if (sl < 0) continue;
+        const double da = p[c] * (logit[c] - pdp);
+        for (int e = 0; e < dk; ++e) dK_l[(size_t)sl * dk + e] += scale * da * q[e];
+        for (int e = 0; e < dv; ++e) dV_l[(size_t)sl * dv + e] += p[c] * sig * dout[e];
+    }
+}
+
+ORACLE_API int oracle_nsa_bwd_keys(int H_kv, int G, int dk, int dv, int n_tok, int n_cmp, int l, int s, int lp,
+                                   int top_n, int window, double scale, int branches,
+                                   const double* Q, const double* K, const double* V,
+                                   const double* Kc, const double* Vc, const int* sel,
+                                   const double* gates, const double* dO,
+                                   const int* raw_keys, int n_raw, const int* cmp_keys, int n_ck,
+                                   double* dK_l, double* dV_l, double* dKc_l, double* dVc_l)
+{
+    const int H = H_kv * G;
+    const size_t nRk = (size_t)H_kv * n_raw * dk, nRv = (size_t)H_kv * n_raw * dv;
+    const size_t nCk = (size_t)H_kv * n_ck * dk, nCv = (size_t)H_kv * n_ck * dv;
+    memset(dK_l, 0, sizeof(double) * nRk);
+    memset(dV_l, 0, sizeof(double) * nRv);
+    if (dKc_l) memset(dKc_l, 0, sizeof(double) * nCk);
+    if (dVc_l) memset(dVc_l, 0, sizeof(double) * nCv);
+    /* slot of every token / compressed block in the lists (-1: not listed), and the number
+     * of listed tokens before each position (a row sees a listed token of [a, b] exactly when
+     * before[b + 1] > before[a]) */
+    int* rslot = (int*)malloc(sizeof(int) * (size_t)(n_tok + 1));
+    int* before = (int*)malloc(sizeof(int) * (size_t)(n_tok + 1));
+    int* cslot = (int*)malloc(sizeof(int) * (size_t)(n_cmp + 1));
+    if (!rslot || !before || !cslot) { free(rslot); free(before); free(cslot); return -2; }
+    for (int x = 0; x < n_tok; ++x) rslot[x] = -1;
+    for (int i = 0; i < n_cmp; ++i) cslot[i] = -1;
+    for (int c = 0; c < n_raw; ++c) rslot[raw_keys[c]] = c;
+    for (int c = 0; c < n_ck; ++c) cslot[cmp_keys[c]] = c;
+    before[0] = 0;
+    for (int x = 0; x < n_tok; ++x) before[x + 1] = before[x] + (rslot[x] >= 0);
+    const int first_ck = n_ck > 0 ? cmp_keys[0] : n_cmp;
+    int bad = 0;
+#pragma omp parallel reduction(|: bad)
+    {
+        double* tK = (double*)calloc(nRk + 1, sizeof(double));
+        double* tV = (double*)calloc(nRv + 1, sizeof(double));
+        double* tKc = (double*)calloc(nCk + 1, sizeof(double));
+        double* tVc = (double*)calloc(nCv + 1, sizeof(double));
+        const int cap = n_cmp + top_n * lp + window + 1;
+        int* keys = (int*)malloc(sizeof(int) * (size_t)cap);
+        double* logit = (double*)malloc(sizeof(double) * (size_t)cap);
+        double* p = (double*)malloc(sizeof(double) * (size_t)cap);
+        if (!tK || !tV || !tKc || !tVc || !keys || !logit || !p) bad = 1;
+        else {
+#pragma omp for schedule(dynamic, 16)
+            for (int th = 0; th < n_tok * H; ++th) {
+                const int t = th / H, h = th % H, g = h / G;
+                const double* q = Q + (size_t)th * dk;
+                const double* dout = dO + (size_t)th * dv;
+                const double* z = gates ? gates + (size_t)th * 3 : NULL;
+                double sig[3];
+                for (int c = 0; c < 3; ++c) sig[c] = z ? sigmoid(z[c]) : 1.0;
+                const size_t kg = (size_t)g * n_tok, cg = (size_t)g * n_cmp;
+                if ((branches & 1) && n_ck > 0) {
+                    const int nk = visible_cmp(t, l, s, n_cmp);
+                    if (nk > first_ck) {
+                        for (int i = 0; i < nk; ++i) keys[i] = i;
+                        list_bwd_keys(q, Kc + cg * dk, Vc + cg * dv, dk, dv, scale, keys, nk, dout, sig[0], cslot,
+                                      logit, p, tKc + (size_t)g * n_ck * dk, tVc + (size_t)g * n_ck * dv);
+                    }
+                }
+                if ((branches & 2) && n_raw > 0) {
+                    int nk = 0, hit = 0;
+                    const int* sl = sel + ((size_t)t * H_kv + g) * top_n;
+                    for (int c = 0; c < top_n; ++c) {
+                        const int j = sl[c];
+                        if (j < 0) continue;
+                        int dup = 0;
+                        for (int c2 = 0; c2 < c; ++c2) dup |= (sl[c2] == j);
+                        if (dup) continue;
+                        const int a = j * lp, b = ((j + 1) * lp - 1 < t ? (j + 1) * lp - 1 : t);
+                        if (a > b) continue;
+                        hit |= before[b + 1] > before[a];
+                        for (int x = a; x <= b; ++x) keys[nk++] = x;
+                    }
+                    if (hit)
+                        list_bwd_keys(q, K + kg * dk, V + kg * dv, dk, dv, scale, keys, nk, dout, sig[1], rslot,
+                                      logit, p, tK + (size_t)g * n_raw * dk, tV + (size_t)g * n_raw * dv);
+                }
+                if ((branches & 4) && n_raw > 0 && window > 0) {
+                    const int t0 = (t - window + 1) > 0 ? (t - window + 1) : 0;
+                    if (before[t + 1] > before[t0]) {
+                        int nk = 0;
+                        for (int x = t0; x <= t; ++x) keys[nk++] = x;
+                        list_bwd_keys(q, K + kg * dk, V + kg * dv, dk, dv, scale, keys, nk, dout, sig[2], rslot,
+                                      logit, p, tK + (size_t)g * n_raw * dk, tV + (size_t)g * n_raw * dv);
+                    }
+                }
+            }
+#pragma omp critical
+            {
+                for (size_t i = 0; i < nRk; ++i) dK_l[i] += tK[i];
+                for (size_t i = 0; i < nRv; ++i) dV_l[i] += tV[i];
+                if (dKc_l) for (size_t i = 0; i < nCk; ++i) dKc_l[i] += tKc[i];
+                if (dVc_l) for (size_t i = 0; i < nCv; ++i) dVc_l[i] += tVc[i];
+            }
+        }
+        free(tK); free(tV); free(tKc); free(tVc); free(keys); free(logit); free(p);
+    }
+    free(rslot); free(before); free(cslot);
+    return bad ? -2 : 0;
+}
+
 /* Backward of the linear block map of step 1 over blocks 0 .. nblk-1 (block i covers
  * tokens i*s .. i*s+l-1), for the gradient dY [nblk, d_out] of its output.  Since
  * Y[i][o] = sum_{r,e} (X[i*s+r][e] + pe[r][e]) W[r*d+e][o]:

@@ -173,3 +173,32 @@ def test_rows_variant_equals_full_backward():
                             c["gates"][rows], c["dO"][rows])
     np.testing.assert_allclose(r["dq"], g["dq"][rows], rtol=1e-12, atol=1e-13)
     np.testing.assert_allclose(r["dgates"], g["dgates"][rows], rtol=1e-12, atol=1e-13)
+
+
+@pytest.mark.parametrize("branches,gated", [(BR_ALL, True), (BR_ALL, False), (BR_SLC, True), (BR_WIN | BR_CMP, True)],
+                         ids=["all_gated", "all", "slc", "win_cmp"])
+def test_keys_variant_equals_full_backward(branches, gated):
+    """oracle.nsa_bwd_keys (the key side for listed keys only, as the full-size GPU tests use
+    it) equals oracle.nsa_bwd's key-side gradients at those keys, which the finite-difference
+    pins above fix; also with lists that hold the first and last keys, several keys of one
+    selection block, and compressed blocks at both ends."""
+    cfg = BW.replace(branches=branches)
+    c = case(cfg, 60 + branches)
+    gates = c["gates"] if gated else None
+    full = oracle.nsa_bwd(cfg, c["Q"], c["K"], c["V"], c["Kc"], c["Vc"], c["sel"], gates, c["dO"])
+    T, n_cmp = cfg.seq_len, c["Kc"].shape[1]
+    raw = np.array([0, 1, 15, 16, 17, 40, 63, 64, 100, 127, 128, T - 2, T - 1])
+    ck = np.array([0, 3, n_cmp // 2, n_cmp - 1])
+    got = oracle.nsa_bwd_keys(cfg, c["Q"], c["K"], c["V"], c["Kc"], c["Vc"], c["sel"], gates, c["dO"], raw, ck)
+    np.testing.assert_allclose(got["dk"], full["dk"][:, raw], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(got["dv"], full["dv"][:, raw], rtol=1e-12, atol=1e-12)
+    assert np.abs(full["dk"][:, raw]).max() > 0
+    if branches & 1:
+        np.testing.assert_allclose(got["dkc"], full["dkc"][:, ck], rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(got["dvc"], full["dvc"][:, ck], rtol=1e-12, atol=1e-12)
+        assert np.abs(full["dkc"][:, ck]).max() > 0
+    # every raw key at once equals the whole array
+    allk = oracle.nsa_bwd_keys(cfg, c["Q"], c["K"], c["V"], c["Kc"], c["Vc"], c["sel"], gates, c["dO"],
+                               np.arange(T), np.arange(n_cmp) if branches & 1 else ())
+    np.testing.assert_allclose(allk["dk"], full["dk"], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(allk["dv"], full["dv"], rtol=1e-12, atol=1e-12)
