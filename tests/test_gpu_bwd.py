@@ -211,8 +211,9 @@ def test_training_forward_saves_branch_outputs(cfg):
 def test_backward_full_size(cfg):
     """The 8K and 64K workloads in the benchmark's configuration (training forward, backward
     on the saved statistics): dQ and the gate gradients on sampled rows against the oracle,
-    computed row by row; the key-side gradients through identities that hold at any size
-    (every branch's probabilities of a row sum to one):
+    computed row by row; dK, dV, dK_cmp and dV_cmp element by element on listed keys against
+    the oracle's sums over every row that sees them; and, as extra checks over all keys, two
+    identities that hold at any size (every branch's probabilities of a row sum to one):
         sum over keys of dV  = sum over the group's (token, head) rows of sigma_c dO   (per branch
                                group: raw keys carry the selected + window branches, compressed
                                keys the compressed branch, counted for rows that see one)
@@ -234,6 +235,38 @@ def test_backward_full_size(cfg):
                               f64(dO_bits[0, rows]))
     check_grad(g["dq"][0, rows].cpu().numpy(), ref["dq"], f"{cfg.name} dQ sampled rows")
     check_grad(g["dgates"][0, rows].cpu().numpy(), ref["dgates"], f"{cfg.name} dgates sampled rows")
+    # key side element by element: per KV group, the oracle's sums over every row that sees
+    # each listed key (oracle.nsa_bwd_keys).  At 8K every raw and compressed key; at 64K
+    # 8 selection blocks per group (32 in all, block 0 excluded, the last block included) and
+    # the last 32 compressed keys of each group (the rows that see a compressed key are every
+    # later row, so early ones would cost the fp64 oracle minutes).
+    G, Hkv = cfg.heads_per_group, cfg.num_kv_heads
+    rng = np.random.default_rng(12)
+    Qf, dOf = f64(inp["q"][0]), f64(dO_bits[0])
+    Kf, Vf = f64(inp["k"][0]), f64(inp["v"][0])
+    sel_all = fwd["sel"][0].cpu().numpy()
+    gk, gv = g["dk"][0].cpu().numpy(), g["dv"][0].cpu().numpy()
+    gkc, gvc = g["dk_cmp"][0].cpu().numpy(), g["dv_cmp"][0].cpu().numpy()
+    lp = cfg.slc_block
+    for grp in range(Hkv):
+        if cfg.seq_len <= 8192:
+            raw, ck = np.arange(cfg.seq_len), np.arange(cfg.n_cmp)
+        else:
+            blocks = rng.choice(np.arange(1, cfg.n_slc - 1), 8 if grp else 7, replace=False)
+            if grp == 0:
+                blocks = np.append(blocks, cfg.n_slc - 1)
+            raw = np.concatenate([np.arange(j * lp, min((j + 1) * lp, cfg.seq_len)) for j in np.sort(blocks)])
+            ck = np.arange(cfg.n_cmp - 32, cfg.n_cmp)
+        hs = slice(grp * G, (grp + 1) * G)
+        c1 = cfg.replace(num_kv_heads=1)
+        ref_k = oracle.nsa_bwd_keys(c1, Qf[:, hs], Kf[grp:grp + 1], Vf[grp:grp + 1], kc[grp:grp + 1],
+                                    vc[grp:grp + 1], sel_all[:, grp:grp + 1], inp["gates"][0, :, hs].astype(np.float64),
+                                    dOf[:, hs], raw, ck)
+        what = f"{cfg.name} group {grp} ({len(raw)} keys, {len(ck)} compressed keys)"
+        check_grad(gk[grp, raw], ref_k["dk"][0], f"{what} dK")
+        check_grad(gv[grp, raw], ref_k["dv"][0], f"{what} dV")
+        check_grad(gkc[grp, ck], ref_k["dkc"][0], f"{what} dK_cmp")
+        check_grad(gvc[grp, ck], ref_k["dvc"][0], f"{what} dV_cmp")
     # identities, per KV group
     G, T, l = cfg.heads_per_group, cfg.seq_len, cfg.cmp_block
     sig = 1.0 / (1.0 + np.exp(-inp["gates"][0].astype(np.float64)))      # [T, H, 3]
