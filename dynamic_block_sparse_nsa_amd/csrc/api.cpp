@@ -541,10 +541,15 @@ nsa_status nsa_full_attn_fwd(const nsa_config* cfg, const void* Q, const void* K
     return hip_check("full_attn");
 }
 
-nsa_status nsa_decode(const nsa_config* cfg, const void* q, const void* K_cache, const void* V_cache,
-                      const int32_t* cache_len, const void* K_cmp_cache, const void* V_cmp_cache,
-                      const float* gate_logits, void* O, int32_t* sel_idx_out, void* ws, size_t ws_bytes,
-                      void* stream) {
+}  // extern "C"
+
+namespace {
+// nsa_decode with its scratch either from the caller's workspace or, with ws == nullptr and
+// use_static, from the library's fixed per-device scratch array.
+nsa_status decode_impl(const nsa_config* cfg, const void* q, const void* K_cache, const void* V_cache,
+                       const int32_t* cache_len, const void* K_cmp_cache, const void* V_cmp_cache,
+                       const float* gate_logits, void* O, int32_t* sel_idx_out, void* ws, size_t ws_bytes,
+                       bool use_static, void* stream) {
     g_detail.clear();
     Shape s;
     nsa_status st = check_config(cfg, &s);
@@ -567,6 +572,16 @@ nsa_status nsa_decode(const nsa_config* cfg, const void* q, const void* K_cache,
         return fail(NSA_ERR_UNSUPPORTED, "decode supports at most " +
                                              std::to_string(nsa::kDecodeMaxSplits * nsa::kDecodeSplitKeys) +
                                              " compressed keys");
+    if (use_static) {
+        if (w.total > nsa::static_scratch_bytes())
+            return fail(NSA_ERR_WORKSPACE, "decode needs " + std::to_string(w.total) +
+                                               " bytes of scratch; the allocation-free entry point has " +
+                                               std::to_string(nsa::static_scratch_bytes()));
+        hipError_t e = hipSuccess;
+        ws = nsa::static_scratch(&e);
+        if (!ws) return fail(NSA_ERR_HIP, std::string("scratch address: ") + hipGetErrorString(e));
+        ws_bytes = nsa::static_scratch_bytes();
+    }
     if ((st = check_ws(ws, ws_bytes, w.total)) != NSA_OK) return st;
     using nsa::u16;
     nsa::DecodeParams p{};
@@ -594,6 +609,24 @@ nsa_status nsa_decode(const nsa_config* cfg, const void* q, const void* K_cache,
     p.scale_log2 = s.scale * nsa::kLog2eHost;
     if (!nsa::launch_decode(s.dk, s.dv, p, as_stream(stream))) return fail(NSA_ERR_UNSUPPORTED, "no decode kernel");
     return hip_check("decode");
+}
+}  // namespace
+
+extern "C" {
+
+nsa_status nsa_decode(const nsa_config* cfg, const void* q, const void* K_cache, const void* V_cache,
+                      const int32_t* cache_len, const void* K_cmp_cache, const void* V_cmp_cache,
+                      const float* gate_logits, void* O, int32_t* sel_idx_out, void* ws, size_t ws_bytes,
+                      void* stream) {
+    return decode_impl(cfg, q, K_cache, V_cache, cache_len, K_cmp_cache, V_cmp_cache, gate_logits, O, sel_idx_out,
+                       ws, ws_bytes, false, stream);
+}
+
+nsa_status nsa_decode_noalloc(const nsa_config* cfg, const void* q, const void* K_cache, const void* V_cache,
+                              const int32_t* cache_len, const void* K_cmp_cache, const void* V_cmp_cache,
+                              const float* gate_logits, void* O, int32_t* sel_idx_out, void* stream) {
+    return decode_impl(cfg, q, K_cache, V_cache, cache_len, K_cmp_cache, V_cmp_cache, gate_logits, O, sel_idx_out,
+                       nullptr, 0, true, stream);
 }
 
 nsa_status nsa_sparse_attn_bwd(const nsa_config* cfg, const void* Q, const void* K, const void* V,

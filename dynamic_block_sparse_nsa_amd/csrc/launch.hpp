@@ -214,4 +214,8 @@ struct AppendParams {
 int append_rows_per_group(int n_new, int s);
 void launch_cache_append(const AppendParams& p, hipStream_t st);
 
+// ---- fixed device scratch (scratch.hip) ----
+size_t static_scratch_bytes();
+void* static_scratch(hipError_t* err);
+
 }  // namespace nsa

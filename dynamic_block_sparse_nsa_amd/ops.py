@@ -65,6 +65,7 @@ def lib(build_if_missing: bool = True):
         L.nsa_select_from_scores.argtypes = [cp, _P, _P, _P]
         L.nsa_sparse_attn_fwd.argtypes = [cp] + [_P] * 8 + [ctypes.c_size_t, _P]
         L.nsa_decode.argtypes = [cp] + [_P] * 10 + [ctypes.c_size_t, _P]
+        L.nsa_decode_noalloc.argtypes = [cp] + [_P] * 10
         L.nsa_full_attn_fwd.argtypes = [cp] + [_P] * 5 + [ctypes.c_size_t, _P]
         L.nsa_compress_prepare.argtypes = [cp] + [_P] * 5 + [ctypes.c_size_t, _P]
         L.nsa_cache_append.argtypes = [cp, _P, _P, ctypes.c_int32] + [_P] * 6 + [ctypes.c_size_t, _P]
@@ -72,7 +73,7 @@ def lib(build_if_missing: bool = True):
         L.nsa_sparse_attn_fwd_train.argtypes = [cp] + [_P] * 10 + [ctypes.c_size_t, _P]
         L.nsa_compress_bwd.argtypes = [cp] + [_P] * 15 + [ctypes.c_size_t, _P]
         for f in ("nsa_workspace_size", "nsa_compress", "nsa_score_select", "nsa_select_from_scores",
-                  "nsa_sparse_attn_fwd", "nsa_decode", "nsa_full_attn_fwd", "nsa_compress_prepare",
+                  "nsa_sparse_attn_fwd", "nsa_decode", "nsa_decode_noalloc", "nsa_full_attn_fwd", "nsa_compress_prepare",
                   "nsa_cache_append"):
             getattr(L, f).restype = ctypes.c_int
         L.nsa_status_string.argtypes = [ctypes.c_int]
@@ -255,6 +256,29 @@ def decode(cfg: NSAConfig, q, K_cache, V_cache, cache_len, K_cmp, V_cmp, gates=N
     _check(lib().nsa_decode(ctypes.byref(c_config(cfg)), _ptr(q), _ptr(K_cache), _ptr(V_cache), _ptr(cache_len),
                             _ptr(K_cmp), _ptr(V_cmp), _ptr(gates), _ptr(out), _ptr(sel), _ptr(ws), nws,
                             _stream(stream)))
+    return out, sel
+
+
+def decode_noalloc(cfg: NSAConfig, q, K_cache, V_cache, cache_len, K_cmp, V_cmp, gates=None, *, out, sel=None,
+                   stream=None):
+    """nsa_decode_noalloc: nsa_decode with the library's fixed device scratch instead of a
+    workspace.  The caller passes the output ``out`` [B,H,dv] bf16 (and optionally ``sel``
+    [B,Hkv,n] int32); nothing is allocated here either.  Returns (out, sel)."""
+    B, L, H, Hkv = cfg.batch, cfg.seq_len, cfg.num_heads, cfg.num_kv_heads
+    _need(q, "q", torch.bfloat16, (B, H, cfg.d_k))
+    _need(K_cache, "K_cache", torch.bfloat16, (B, Hkv, L, cfg.d_k))
+    _need(V_cache, "V_cache", torch.bfloat16, (B, Hkv, L, cfg.d_v))
+    _need(cache_len, "cache_len", torch.int32, (B,))
+    _need(K_cmp, "K_cmp", torch.bfloat16, (B, Hkv, cfg.n_cmp, cfg.d_k))
+    _need(V_cmp, "V_cmp", torch.bfloat16, (B, Hkv, cfg.n_cmp, cfg.d_v))
+    if gates is not None:
+        _need(gates, "gates", torch.float32, (B, H, 3))
+    _need(out, "out", torch.bfloat16, (B, H, cfg.d_v))
+    if sel is not None:
+        _need(sel, "sel", torch.int32, (B, Hkv, cfg.top_n))
+    _check(lib().nsa_decode_noalloc(ctypes.byref(c_config(cfg)), _ptr(q), _ptr(K_cache), _ptr(V_cache),
+                                    _ptr(cache_len), _ptr(K_cmp), _ptr(V_cmp), _ptr(gates), _ptr(out), _ptr(sel),
+                                    _stream(stream)))
     return out, sel
 
 

@@ -33,7 +33,8 @@
  *       gate_logits     [B, T, H, 3]           fp32, order (compressed, selected, window)
  *       o_cmp, lse_cmp  [B, T, H, d_v], [B, T, H]   fp32
  *   - The caller owns every buffer.  The library never allocates device memory; calls
- *     that need scratch take a caller workspace whose size nsa_workspace_size reports.
+ *     that need scratch take a caller workspace whose size nsa_workspace_size reports
+ *     (nsa_decode_noalloc instead uses a fixed device array the library holds).
  *   - Calls are asynchronous on the given stream (a hipStream_t; NULL = default stream)
  *     and never synchronize.  Inputs are read-only; outputs are fully overwritten.
  *   - Arguments are validated on the host before anything is launched; a failing call
@@ -171,6 +172,22 @@ nsa_status nsa_decode(const nsa_config* cfg, const void* q, const void* K_cache,
                       const int32_t* cache_len, const void* K_cmp_cache, const void* V_cmp_cache,
                       const float* gate_logits, void* O, int32_t* sel_idx_out,
                       void* ws, size_t ws_bytes, void* stream);
+
+/* nsa_decode without a workspace, for callers that cannot allocate device memory (work
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).  Same
+ * arguments, kernels and results as nsa_decode, minus ws / ws_bytes: the scratch comes from
+ * a fixed 64 MiB array in device memory that the library holds on every GPU it runs on
+ * until the process ends (the B = 32, 65536-token decode step uses 30 MiB; nsa_workspace_size
+ * with NSA_OP_DECODE gives any configuration's need).  The call allocates and frees nothing.
+ * Errors: those of nsa_decode, NSA_ERR_WORKSPACE when the configuration needs more scratch
+ * than the array holds, NSA_ERR_HIP when the array's device address cannot be obtained.
+ * Every call on one GPU shares that GPU's array: calls that overlap in time on one GPU (on
+ * different streams, or from different threads) race and must be serialized by the caller.
+ * Nothing in the array needs clearing between calls (every value read is written earlier in
+ * the same call). */
+nsa_status nsa_decode_noalloc(const nsa_config* cfg, const void* q, const void* K_cache, const void* V_cache,
+                              const int32_t* cache_len, const void* K_cmp_cache, const void* V_cmp_cache,
+                              const float* gate_logits, void* O, int32_t* sel_idx_out, void* stream);
 
 /* Decode cache maintenance (zjai.club notes, section 5: the compressed cache gains one entry
  * every s tokens; section 13: decoding runs against these caches).

@@ -135,6 +135,8 @@ def test_calls_reject_null_pointers_before_launch():
     assert L.nsa_sparse_attn_fwd(_cfg(), fake, fake, fake, None, fake, None, fake, None, 0, None) == 1
     assert L.nsa_sparse_attn_fwd(_cfg(), fake, fake, fake, fake, None, None, fake, None, 0, None) == 1
     assert L.nsa_decode(_cfg(DECODE), fake, fake, fake, None, fake, fake, None, fake, None, None, 0, None) == 1
+    assert L.nsa_decode_noalloc(_cfg(DECODE), fake, fake, fake, None, fake, fake, None, fake, None, None) == 1
+    assert L.nsa_decode_noalloc(_cfg(DECODE), fake, fake, fake, fake, fake, fake, None, None, None, None) == 1
     assert L.nsa_select_from_scores(_cfg(), None, fake, None) == 1
     assert L.nsa_full_attn_fwd(_cfg(), fake, fake, fake, None, fake, 1 << 40, None) == 1
     assert L.nsa_full_attn_fwd(_cfg(), None, fake, fake, fake, fake, 1 << 40, None) == 1
@@ -147,6 +149,10 @@ def test_calls_reject_small_workspace_before_launch():
     assert L.nsa_score_select(_cfg(), fake, fake, fake, fake, None, fake, fake, 16, None) == 4
     assert L.nsa_sparse_attn_fwd(_cfg(), fake, fake, fake, fake, fake, None, fake, fake, 16, None) == 4
     assert L.nsa_decode(_cfg(DECODE), fake, fake, fake, fake, fake, fake, None, fake, None, fake, 16, None) == 4
+    # the allocation-free decode: a configuration whose scratch exceeds the fixed 64 MiB array
+    big_b = _cfg(DECODE.replace(batch=160))
+    assert L.nsa_decode_noalloc(big_b, fake, fake, fake, fake, fake, fake, None, fake, None, None) == 4
+    assert b"scratch" in L.nsa_last_error_detail()
     assert L.nsa_full_attn_fwd(_cfg(), fake, fake, fake, fake, fake, 16, None) == 4
     # unaligned workspace
     big = 1 << 40
