@@ -172,7 +172,16 @@ def cpu_baseline(cfg: NSAConfig, inp: dict, budget_rows: int = 3072, nb: int = 2
     oracle.attend(cfg, Qr, rows, K, V, ss["sel"], ss["o_cmp"], inp["gates"][0, rows])
     t_rows = time.perf_counter() - t1
     total = t_cmp + t_rows * cfg.seq_len / budget_rows
+    cpu_model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu_model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     return {"value": round(cfg.seq_len / total, 2), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "cpu_model": cpu_model, "host_cpus": os.cpu_count(),
             "sample": (f"fp64 oracle: compression of {nb} of {cfg.n_cmp} blocks per KV group ({t_cmp * nb / cfg.n_cmp:.2f} s, "
                        f"scaled) + score/select/attend of the last {budget_rows} of {cfg.seq_len} rows "
                        f"({t_rows:.2f} s, scaled to all rows); {threads} OpenMP threads")}
@@ -233,12 +242,22 @@ def main():
     out = torch.empty((B, T, H, cfg.d_v), dtype=torch.bfloat16, device=dev)
     ws = {op: torch.empty(max(ops.workspace_size(cfg, op), 256), dtype=torch.uint8, device=dev) for op in range(3)}
 
-    calls = [
+    ws[ops.OP_PREFILL] = torch.empty(ops.workspace_size(cfg, ops.OP_PREFILL), dtype=torch.uint8, device=dev)
+    calls3 = [
         lambda: ops.compress(cfg, K, V, wk, wv, pk, pv, out_k=kc, out_v=vc, workspace=ws[0]),
         lambda: ops.score_select(cfg, Q, kc, vc, sel=sel, o_cmp=ocmp, workspace=ws[1]),
         lambda: ops.sparse_attn_fwd(cfg, Q, K, V, sel, ocmp, gates, out=out, workspace=ws[2]),
     ]
-    print("[bench] timing prefill", file=sys.stderr, flush=True)
+    # the headline step: compression, then scoring + selection + attention + gate in the
+    # fused call (nsa_prefill_fwd: the same arithmetic as the two calls above, one launch)
+    calls = [
+        calls3[0],
+        lambda: ops.prefill_fwd(cfg, Q, K, V, kc, vc, gates, out=out, sel=sel, workspace=ws[ops.OP_PREFILL]),
+    ]
+    print("[bench] timing prefill (three calls)", file=sys.stderr, flush=True)
+    per_call3, wall3 = time_calls(calls3, args.steps, args.warmup, torch)
+    ms3 = wall3 / args.steps * 1e3
+    print("[bench] timing prefill (fused)", file=sys.stderr, flush=True)
     per_call, wall = time_calls(calls, args.steps, args.warmup, torch)
     ms = wall / args.steps * 1e3   # the K timed steps between two synchronizations
     # cold caches: a 2 GiB write before each step evicts L2 and the memory-side cache; the
@@ -259,21 +278,19 @@ def main():
     total_flops = sum(fl.values())
     tflops = total_flops / (ms * 1e-3) / 1e12
     call_ms = per_call.mean(axis=0)
-    names = ["nsa_compress", "nsa_score_select", "nsa_sparse_attn_fwd"]
-    # the dominant call and its algorithmic work
-    dom = int(np.argmax(call_ms))
-    dom_flops = [2 * (cfg.n_cmp * (cfg.cmp_block * cfg.d_k * cfg.d_k + cfg.cmp_block * cfg.d_v * cfg.d_v)) * Hkv,
-                 fl["cmp"], fl["slc"] + fl["win"]][dom]
-    dom_kernel = ["compress_linear_kernel", "cmp_attn_kernel", "sparse_attn_kernel"][dom]
-    # every kernel the dominant call launches (the first is the main one)
-    dom_launches = [["compress_linear_kernel", "transpose_w_kernel", "pe_bias_kernel"],
-                    ["cmp_attn_kernel", "cmp_vmax_kernel", "tile_cmp_kernel", "select_from_scores_kernel"],
-                    ["sparse_attn_kernel", "cmp_vmax_kernel", "tile_cmp_kernel"]][dom]
-    dom_src = [["dynamic_block_sparse_nsa_amd/csrc/compress.hip"],
-               ["dynamic_block_sparse_nsa_amd/csrc/score_select.hip", "dynamic_block_sparse_nsa_amd/csrc/select.hpp"],
-               ["dynamic_block_sparse_nsa_amd/csrc/sparse_attn.hip"]][dom]
+    call_ms3 = per_call3.mean(axis=0)
+    names = ["nsa_compress", "nsa_prefill_fwd"]
+    names3 = ["nsa_compress", "nsa_score_select", "nsa_sparse_attn_fwd"]
+    # the dominant call (the fused one) and its algorithmic work: the three branches
+    dom = 1
+    dom_flops = total_flops
+    dom_kernel = "prefill_fused_kernel"
+    # every kernel the call launches (the first is the main one)
+    dom_launches = ["prefill_fused_kernel", "cmp_vmax_kernel", "tile_cmp_kernel"]
+    csrc = "dynamic_block_sparse_nsa_amd/csrc/"
+    dom_src = [csrc + f for f in ("prefill.hip", "cmp_attn.hpp", "sparse_attn.hpp", "select.hpp", "common.hpp")]
     dom_tf = dom_flops / (call_ms[dom] * 1e-3) / 1e12
-    traffic = load_traffic(dom_kernel, dom_src + ["dynamic_block_sparse_nsa_amd/csrc/common.hpp"])
+    traffic = load_traffic(dom_kernel, dom_src)
     torch.cuda.synchronize()
 
     result = {
@@ -295,28 +312,37 @@ def main():
                    "top_n": cfg.top_n, "window": cfg.window},
         "tflops_algorithmic": round(tflops, 2),
         "mfma_peak_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "timing": "ms_per_step: warm mean over the timed steps; cold_ms_per_step: median of 3 steps "
+                  "each after a 2 GiB write that flushes L2 and the memory-side cache",
         "cold_ms_per_step": round(float(np.median(cold)), 4),
         "algorithmic_flops": {k: int(v) for k, v in fl.items()},
         "per_call_ms": {n: round(float(c), 4) for n, c in zip(names, call_ms)},
-        "roofline": {"bound": "mfma", "kernel": dom_kernel, "call": names[dom], "call_kernels": dom_launches,
-                     "achieved": round(dom_tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(dom_tf / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None if traffic is None else traffic.get("bytes_per_launch")},
+        "three_calls": {"ms_per_step": round(ms3, 4), "tokens_per_s": round(B * T / (ms3 * 1e-3), 1),
+                        "per_call_ms": {n: round(float(c), 4) for n, c in zip(names3, call_ms3)}},
         "wall_s_timed": round(wall, 3),
     }
-    if dom_kernel == "sparse_attn_kernel":
-        # The selected branch reads each chosen block's keys and values per (token, group):
-        # (d_k + d_v) * 2 bytes per selected key.  Part of it is served by L2; the counter
-        # record gives the bytes that reached HBM per launch (FETCH_SIZE + WRITE_SIZE).
-        gathered = slc_pairs(cfg) // cfg.heads_per_group * (cfg.d_k + cfg.d_v) * 2
-        sec = call_ms[dom] * 1e-3
-        result["roofline_gather"] = {
-            "kernel": dom_kernel, "gathered_bytes": int(gathered),
-            "gathered_gbs": round(gathered / sec / 1e9, 1),
-            "hbm_bytes": None if traffic is None else traffic.get("bytes_per_launch"),
-            "hbm_gbs": None if traffic is None else round(traffic["bytes_per_launch"] / sec / 1e9, 1),
-            "hbm_peak_gbs": PEAK_HBM_GBS,
-            "hbm_frac": None if traffic is None else round(traffic["bytes_per_launch"] / sec / 1e9 / PEAK_HBM_GBS, 4)}
+    # The roofline of the dominant kernel on both axes: its algorithmic flops against the
+    # bf16 MFMA peak, and the HBM bytes the counters record per launch (FETCH_SIZE +
+    # WRITE_SIZE, scaled) against the HBM peak.  The larger fraction names the bound.
+    sec = call_ms[dom] * 1e-3
+    hbm_bytes = None if traffic is None else traffic.get("bytes_per_launch")
+    hbm_frac = None if hbm_bytes is None else hbm_bytes / sec / 1e9 / PEAK_HBM_GBS
+    mfma_frac = dom_tf / PEAK_BF16_TFLOPS
+    result["roofline"] = {
+        "bound": "hbm" if (hbm_frac is not None and hbm_frac > mfma_frac) else "mfma",
+        "kernel": dom_kernel, "call": names[dom], "call_kernels": dom_launches,
+        "achieved": round(dom_tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(mfma_frac, 4),
+        "traffic": hbm_bytes,
+        "hbm_gbs": None if hbm_bytes is None else round(hbm_bytes / sec / 1e9, 1),
+        "hbm_peak_gbs": PEAK_HBM_GBS,
+        "hbm_frac": None if hbm_frac is None else round(hbm_frac, 4)}
+    if traffic is not None and traffic.get("mfma_busy_frac") is not None:
+        result["roofline"]["mfma_busy_frac"] = traffic["mfma_busy_frac"]
+    # The selected branch reads each chosen block's keys and values per (token, group):
+    # (d_k + d_v) * 2 bytes per selected key, most of it from L2 and the memory-side cache.
+    gathered = slc_pairs(cfg) // cfg.heads_per_group * (cfg.d_k + cfg.d_v) * 2
+    result["roofline_gather"] = {"kernel": dom_kernel, "gathered_bytes": int(gathered),
+                                 "gathered_gbs": round(gathered / sec / 1e9, 1)}
 
     # ---------------- decode ----------------
     # ---------------- dense causal attention on the same inputs ----------------
@@ -327,7 +353,7 @@ def main():
         fms = float(pcf.mean())
         dfl = 2 * (cfg.d_k + cfg.d_v) * H * T * (T + 1) / 2
         cmp8 = {}
-        # the same comparison at 8K tokens (NSA's three calls against the dense kernel)
+        # the same comparison at 8K tokens (NSA's compression and fused call against the dense kernel)
         c8 = P8K
         g8 = torch.Generator(device=dev).manual_seed(c8.seed)
         r8 = lambda *sh: torch.randn(sh, generator=g8, device=dev).to(torch.bfloat16)
@@ -340,8 +366,7 @@ def main():
         sel8, _, oc8 = ops.score_select(c8, Q8, kc8, vc8)
         o8 = torch.empty((1, c8.seq_len, c8.num_heads, c8.d_v), dtype=torch.bfloat16, device=dev)
         n8, _ = time_calls([lambda: ops.compress(c8, K8, V8, *w8, out_k=kc8, out_v=vc8),
-                            lambda: ops.score_select(c8, Q8, kc8, vc8, sel=sel8, o_cmp=oc8),
-                            lambda: ops.sparse_attn_fwd(c8, Q8, K8, V8, sel8, oc8, gt8, out=o8)], 10, 2, torch)
+                            lambda: ops.prefill_fwd(c8, Q8, K8, V8, kc8, vc8, gt8, out=o8, sel=sel8)], 10, 2, torch)
         f8, _ = time_calls([lambda: ops.full_attn_fwd(c8, Q8, K8, V8, out=o8)], 10, 2, torch)
         n8ms, f8ms = float(n8.sum(axis=1).mean()), float(f8.mean())
         result["vs_dense"] = {
@@ -355,7 +380,7 @@ def main():
 
     # ---------------- the selected branch with selection locality (opt-in) ----------------
     if args.locality:
-        locality(cfg, Q, K, V, ocmp, gates, out, ws, call_ms, result, time_calls, torch, dev)
+        locality(cfg, Q, K, V, ocmp, gates, out, ws, call_ms3, result, time_calls, torch, dev)
 
     # ---------------- backward of the same step ----------------
     if not args.no_backward:
@@ -510,7 +535,7 @@ def main():
             result[key] = {"workload": f"moba_{mc.seq_len}_h8_d128", "ms_per_step": round(mms, 3),
                            "tokens_per_s": round(mc.seq_len / (mms * 1e-3), 1),
                            "tflops_algorithmic": round(moba_flops(mc) / (mms * 1e-3) / 1e12, 2),
-                           "per_call_ms": {n: round(float(c), 3) for n, c in zip(names, pcm.mean(axis=0))}}
+                           "per_call_ms": {n: round(float(c), 3) for n, c in zip(names3, pcm.mean(axis=0))}}
             del Qm, Km, Vm, kbar, selm, om, wsm
             torch.cuda.empty_cache()
 

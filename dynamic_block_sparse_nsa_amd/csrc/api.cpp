@@ -183,6 +183,21 @@ DecodeWs decode_ws(const Shape& s) {
     return w;
 }
 
+// the fused prefill: the scoring call's and the attention call's workspaces side by side,
+// plus room for the lists and o_cmp when the caller does not take them
+struct PrefillWs { SelectWs sel; AttnWs attn; size_t attn_off, sel_out, ocmp_out, total; };
+PrefillWs prefill_ws(const Shape& s) {
+    PrefillWs w{};
+    w.sel = select_ws(s);
+    w.attn = attn_ws(s);
+    size_t off = w.sel.total;
+    w.attn_off = off; off = align_up(off + w.attn.total, 256);
+    w.sel_out = off; off = align_up(off + (size_t)s.B * s.T * s.Hkv * std::max(s.n, 1) * 4, 256);
+    w.ocmp_out = off; off = align_up(off + (size_t)s.B * s.T * s.H * s.dv * 4, 256);
+    w.total = off;
+    return w;
+}
+
 // backward of the branches: K, V in fragment order for the statistics pass, the per-row
 // statistics, and the selected branch's block lists (own block included)
 struct BwdWs {
@@ -249,6 +264,7 @@ nsa_status nsa_workspace_size(const nsa_config* cfg, int op, size_t* bytes) {
         case NSA_OP_FULL_ATTN: *bytes = full_ws(s).total; break;
         case NSA_OP_SPARSE_BWD: *bytes = bwd_ws(s).total; break;
         case NSA_OP_COMPRESS_BWD: *bytes = compress_bwd_ws(s); break;
+        case NSA_OP_PREFILL: *bytes = prefill_ws(s).total; break;
         default: return fail(NSA_ERR_SHAPE, "unknown op");
     }
     return NSA_OK;
@@ -460,6 +476,78 @@ nsa_status nsa_sparse_attn_fwd_train(const nsa_config* cfg, const void* Q, const
     }
     return sparse_attn_fwd_impl(cfg, Q, K, V, sel_idx, o_cmp, gate_logits, O, saved_lse, saved_o, ws, ws_bytes,
                                 stream);
+}
+
+nsa_status nsa_prefill_fwd(const nsa_config* cfg, const void* Q, const void* K, const void* V, const void* K_cmp,
+                           const void* V_cmp, const float* gate_logits, void* O, int32_t* sel_idx, float* lse_cmp,
+                           float* o_cmp, void* ws, size_t ws_bytes, void* stream) {
+    g_detail.clear();
+    Shape s;
+    nsa_status st = check_config(cfg, &s);
+    if (st != NSA_OK) return st;
+    if (!Q || !K || !V || !K_cmp || !V_cmp || !O) return fail(NSA_ERR_NULL, "Q, K, V, K_cmp, V_cmp and O are required");
+    if (s.mode != NSA_SCORE_CMP_OVERLAP)
+        return fail(NSA_ERR_UNSUPPORTED, "the fused prefill scores blocks by compressed attention (CMP_OVERLAP)");
+    if (s.n_cmp == 0) return fail(NSA_ERR_UNSUPPORTED, "seq_len shorter than cmp_block");
+    if (s.n_slc > 64 * 32) return fail(NSA_ERR_UNSUPPORTED, "at most 2048 selection blocks");
+    {
+        const int R = s.lp / s.s, L = s.l / s.s;
+        if (64 % R != 0 || L > 64)
+            return fail(NSA_ERR_UNSUPPORTED, "slc_block / cmp_stride must divide 64 and cmp_block / cmp_stride <= 64");
+    }
+    if (nsa::prefill_lds_bytes(s.dk, s.dv, s.G) > 160 * 1024)
+        return fail(NSA_ERR_UNSUPPORTED, "tile too large for one workgroup's LDS");
+    if ((s.br & NSA_BR_WIN) && s.w <= 0) return fail(NSA_ERR_SHAPE, "window branch with window = 0");
+    const PrefillWs w = prefill_ws(s);
+    if ((st = check_ws(ws, ws_bytes, w.total)) != NSA_OK) return st;
+    if (o_cmp && (reinterpret_cast<uintptr_t>(o_cmp) & 15u) != 0) return fail(NSA_ERR_SHAPE, "o_cmp must be 16-byte aligned");
+    const hipStream_t hs = as_stream(stream);
+    using nsa::u16;
+    int32_t* sel = sel_idx ? sel_idx : at<int32_t>(ws, w.sel_out);
+    float* oc = o_cmp ? o_cmp : at<float>(ws, w.ocmp_out);
+    // compressed keys/values in fragment order (V as scaled fp16)
+    nsa::SelParams sp{};
+    sp.Q = static_cast<const u16*>(Q);
+    sp.Kc = static_cast<const u16*>(K_cmp);
+    sp.scores = at<float>(ws, w.sel.scores);
+    sp.sel = sel;
+    sp.top_n = s.n; sp.n_init = s.n_init; sp.n_local = s.n_local;
+    sp.B = s.B; sp.T = s.T; sp.Hkv = s.Hkv; sp.N = s.n_cmp; sp.Npad = w.sel.npad; sp.l = s.l; sp.s = s.s; sp.lp = s.lp;
+    sp.n_slc = s.n_slc;
+    sp.scale_log2 = s.scale * nsa::kLog2eHost;
+    u16* ckf = at<u16>(ws, w.sel.kf);
+    u16* cvf = at<u16>(ws, w.sel.vf);
+    if (!nsa::launch_tile_cmp(s.dk, s.dv, sp.Kc, static_cast<const u16*>(V_cmp), at<uint32_t>(ws, w.sel.vmax),
+                              at<int>(ws, w.sel.vexp), ckf, cvf, s.B * s.Hkv, s.n_cmp, w.sel.npad, hs))
+        return fail(NSA_ERR_UNSUPPORTED, "no layout kernel for this shape");
+    sp.Kf = ckf;
+    sp.Vf = cvf;
+    sp.vexp = at<int>(ws, w.sel.vexp);
+    sp.lse = lse_cmp;
+    sp.o_cmp = oc;
+    // K and V in fragment order (V as scaled fp16)
+    void* aws = at<void>(ws, w.attn_off);
+    u16* kf = at<u16>(aws, w.attn.kf);
+    u16* vf = at<u16>(aws, w.attn.vf);
+    if (!nsa::launch_tile_cmp(s.dk, s.dv, static_cast<const u16*>(K), static_cast<const u16*>(V),
+                              at<uint32_t>(aws, w.attn.vmax), at<int>(aws, w.attn.vexp), kf, vf, s.B * s.Hkv, s.T,
+                              w.attn.tpad, hs))
+        return fail(NSA_ERR_UNSUPPORTED, "no layout kernel");
+    nsa::AttnParams ap{};
+    ap.Q = static_cast<const u16*>(Q);
+    ap.Kf = kf;
+    ap.Vf = vf;
+    ap.vexp = at<int>(aws, w.attn.vexp);
+    ap.sel = sel;
+    ap.o_cmp = oc;
+    ap.gates = gate_logits;
+    ap.O = static_cast<u16*>(O);
+    ap.B = s.B; ap.T = s.T; ap.Tpad = w.attn.tpad; ap.Hkv = s.Hkv; ap.G = s.G; ap.lp = s.lp; ap.top_n = s.n;
+    ap.window = s.w; ap.branches = s.br;
+    ap.scale_log2 = s.scale * nsa::kLog2eHost;
+    if (!nsa::launch_prefill_fused(s.dk, s.dv, s.G, sp, ap, hs))
+        return fail(NSA_ERR_UNSUPPORTED, "no fused prefill kernel for this shape");
+    return hip_check("prefill_fwd");
 }
 
 nsa_status nsa_compress_prepare(const nsa_config* cfg, const void* W_k, const void* W_v, const void* pe_k,

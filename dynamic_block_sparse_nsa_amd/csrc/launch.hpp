@@ -80,6 +80,12 @@ bool launch_sparse_attn_stats(int DK, int DV, const AttnParams& p, hipStream_t s
 // the backward statistics from a training forward's saved LSE and outputs (no recompute)
 void launch_stats_from_saved(int DV, const AttnParams& p, hipStream_t st);
 
+// ---- the fused prefill (prefill.hip): cmp_attn_tile, selection, sparse_attn_tokens per tile ----
+// sp as for launch_cmp_attn (with o_cmp, scores, sel, top_n, n_init, n_local set), ap as for
+// launch_sparse_attn (ap.sel = sp.sel, ap.o_cmp = sp.o_cmp: both read back after being written)
+size_t prefill_lds_bytes(int DK, int DV, int G);
+bool launch_prefill_fused(int DK, int DV, int G, const SelParams& sp, const AttnParams& ap, hipStream_t st);
+
 // ---- G = 1 selected-only attention (MoBA): inverted, block-major schedule ----
 constexpr int kMobaChunk = 1024;   // tokens per histogram / scatter workgroup
 struct MobaParams {

@@ -18,7 +18,8 @@ from .configs import NSAConfig
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libnsa.so")
 
-OP_COMPRESS, OP_SCORE_SELECT, OP_SPARSE_ATTN, OP_DECODE, OP_FULL_ATTN, OP_SPARSE_BWD, OP_COMPRESS_BWD = range(7)
+(OP_COMPRESS, OP_SCORE_SELECT, OP_SPARSE_ATTN, OP_DECODE, OP_FULL_ATTN, OP_SPARSE_BWD, OP_COMPRESS_BWD,
+ OP_PREFILL) = range(8)
 STATUS = {0: "ok", 1: "null", 2: "shape", 3: "unsupported", 4: "workspace", 5: "hip"}
 
 
@@ -66,6 +67,7 @@ def lib(build_if_missing: bool = True):
         L.nsa_sparse_attn_fwd.argtypes = [cp] + [_P] * 8 + [ctypes.c_size_t, _P]
         L.nsa_decode.argtypes = [cp] + [_P] * 10 + [ctypes.c_size_t, _P]
         L.nsa_decode_noalloc.argtypes = [cp] + [_P] * 10
+        L.nsa_prefill_fwd.argtypes = [cp] + [_P] * 11 + [ctypes.c_size_t, _P]
         L.nsa_full_attn_fwd.argtypes = [cp] + [_P] * 5 + [ctypes.c_size_t, _P]
         L.nsa_compress_prepare.argtypes = [cp] + [_P] * 5 + [ctypes.c_size_t, _P]
         L.nsa_cache_append.argtypes = [cp, _P, _P, ctypes.c_int32] + [_P] * 6 + [ctypes.c_size_t, _P]
@@ -74,6 +76,7 @@ def lib(build_if_missing: bool = True):
         L.nsa_compress_bwd.argtypes = [cp] + [_P] * 15 + [ctypes.c_size_t, _P]
         for f in ("nsa_workspace_size", "nsa_compress", "nsa_score_select", "nsa_select_from_scores",
                   "nsa_sparse_attn_fwd", "nsa_decode", "nsa_decode_noalloc", "nsa_full_attn_fwd", "nsa_compress_prepare",
+                  "nsa_prefill_fwd",
                   "nsa_cache_append"):
             getattr(L, f).restype = ctypes.c_int
         L.nsa_status_string.argtypes = [ctypes.c_int]
@@ -315,12 +318,54 @@ def cache_append(cfg: NSAConfig, K_new, V_new, K_cache, V_cache, cache_len, K_cm
                                   prep.numel(), _stream(stream)))
 
 
+def prefill_fwd(cfg: NSAConfig, Q, K, V, K_cmp, V_cmp, gates=None, *, out=None, sel=None, lse=None, o_cmp=None,
+                want_sel=True, want_lse=False, want_ocmp=False, workspace=None, stream=None):
+    """nsa_prefill_fwd: score_select + sparse_attn_fwd in one fused launch.  Returns
+    (O [B,T,H,dv] bf16, sel [B,T,Hkv,n] int32 or None, lse [B,T,H] or None, o_cmp
+    [B,T,H,dv] fp32 or None)."""
+    B, T, H, Hkv = cfg.batch, cfg.seq_len, cfg.num_heads, cfg.num_kv_heads
+    dev = Q.device
+    _need(Q, "Q", torch.bfloat16, (B, T, H, cfg.d_k))
+    _need(K, "K", torch.bfloat16, (B, Hkv, T, cfg.d_k))
+    _need(V, "V", torch.bfloat16, (B, Hkv, T, cfg.d_v))
+    _need(K_cmp, "K_cmp", torch.bfloat16, (B, Hkv, cfg.n_cmp, cfg.d_k))
+    _need(V_cmp, "V_cmp", torch.bfloat16, (B, Hkv, cfg.n_cmp, cfg.d_v))
+    if gates is not None:
+        _need(gates, "gates", torch.float32, (B, T, H, 3))
+    if out is None:
+        out = torch.empty((B, T, H, cfg.d_v), dtype=torch.bfloat16, device=dev)
+    _need(out, "out", torch.bfloat16, (B, T, H, cfg.d_v))
+    if sel is None and want_sel:
+        sel = torch.empty((B, T, Hkv, cfg.top_n), dtype=torch.int32, device=dev)
+    if sel is not None:
+        _need(sel, "sel", torch.int32, (B, T, Hkv, cfg.top_n))
+    if lse is None and want_lse:
+        lse = torch.empty((B, T, H), dtype=torch.float32, device=dev)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, (B, T, H))
+    if o_cmp is None and want_ocmp:
+        o_cmp = torch.empty((B, T, H, cfg.d_v), dtype=torch.float32, device=dev)
+    if o_cmp is not None:
+        _need(o_cmp, "o_cmp", torch.float32, (B, T, H, cfg.d_v))
+    ws, nws = _workspace(cfg, OP_PREFILL, dev, workspace)
+    _check(lib().nsa_prefill_fwd(ctypes.byref(c_config(cfg)), _ptr(Q), _ptr(K), _ptr(V), _ptr(K_cmp), _ptr(V_cmp),
+                                 _ptr(gates), _ptr(out), _ptr(sel), _ptr(lse), _ptr(o_cmp), _ptr(ws), nws,
+                                 _stream(stream)))
+    return out, sel, lse, o_cmp
+
+
 def prefill(cfg: NSAConfig, Q, K, V, w_k=None, w_v=None, pe_k=None, pe_v=None, gates=None, stream=None,
-            train=False):
+            train=False, fused=False):
     """The whole prefill hot path: compress -> score_select -> sparse_attn_fwd (or, with
-    ``train``, sparse_attn_fwd_train).  Returns dict(out, sel, o_cmp, lse, k_cmp, v_cmp and,
-    with ``train``, saved_lse, saved_o) (o_cmp and lse: compressed branch only)."""
+    ``train``, sparse_attn_fwd_train; with ``fused``, compress -> prefill_fwd).  Returns
+    dict(out, sel, o_cmp, lse, k_cmp, v_cmp and, with ``train``, saved_lse, saved_o) (o_cmp
+    and lse: compressed branch only)."""
     k_cmp, v_cmp = compress(cfg, K, V, w_k, w_v, pe_k, pe_v, stream=stream)
+    if fused:
+        use_c = bool(cfg.branches & 1)
+        out, sel, lse, o_cmp = prefill_fwd(cfg, Q, K, V, k_cmp, v_cmp, gates, want_lse=use_c, want_ocmp=use_c,
+                                           stream=stream)
+        return {"out": out, "sel": sel, "o_cmp": o_cmp, "lse": lse, "k_cmp": k_cmp, "v_cmp": v_cmp}
     use_c = bool(cfg.branches & 1)
     sel, lse, o_cmp = score_select(cfg, Q, k_cmp, v_cmp, want_lse=use_c, want_ocmp=use_c, stream=stream)
     r = {"sel": sel, "o_cmp": o_cmp, "lse": lse, "k_cmp": k_cmp, "v_cmp": v_cmp}

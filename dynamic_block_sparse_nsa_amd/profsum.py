@@ -3,6 +3,8 @@
 ``stats``   kernel_trace.csv (from ``rocprofv3 --kernel-trace -f csv``) -> a short text table
             of calls, average and total duration per kernel and launch size (workgroups),
             so launches of one kernel on different workloads get rows of their own.
+``counters`` counter_collection.csv files of several --pmc passes -> per-kernel table of
+            every counter and derived metric (MFMA busy, VALU busy, LDS use, L2 hits, ...).
 ``traffic`` two counter_collection.csv files (``--pmc FETCH_SIZE`` and ``--pmc WRITE_SIZE``)
             -> HBM bytes per launch of each named kernel (its largest launch, the headline
             workload), scaled by what the same counter reads for a plain device copy of
@@ -107,6 +109,41 @@ def traffic(fetch_csv, write_csv, copy_bytes, copy_regex, kernels, out_path, cmd
     return rec
 
 
+def counters(csvs, cmd: str, title: str, kernel_regex: str = "") -> str:
+    """Per-kernel table of every counter found in the given counter_collection.csv files
+    (several rocprofv3 --pmc passes of one command), each the mean over the kernel's largest
+    launches.  Derived metrics (MfmaUtil, VALUBusy, LdsUtil, ...) are reported as rocprofv3
+    computed them."""
+    table = defaultdict(dict)
+    names = []
+    for path in csvs:
+        acc = defaultdict(lambda: defaultdict(lambda: defaultdict(list)))
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                acc[r["Counter_Name"]][short_name(r["Kernel_Name"])][int(r["Grid_Size"])].append(
+                    float(r["Counter_Value"]))
+        for cname, per_k in acc.items():
+            if cname not in names:
+                names.append(cname)
+            for k, by_grid in per_k.items():
+                g = max(by_grid)
+                v = by_grid[g]
+                table[(k, g)][cname] = sum(v) / len(v)
+    rows = sorted(table.items(), key=lambda kv: kv[0][0])
+    out = [f"# {title}", "", f"command: {cmd}", "", "Each value: mean per dispatch over the kernel's largest launch "
+           "(grid size in threads).", ""]
+    for (k, g), vals in rows:
+        if kernel_regex and not re.search(kernel_regex, k):
+            continue
+        out.append(f"{k}  (grid {g})")
+        for c in names:
+            if c in vals:
+                v = vals[c]
+                out.append(f"    {c:34s} {v:18.4f}" if abs(v) < 1e6 else f"    {c:34s} {v:18.0f}")
+        out.append("")
+    return "\n".join(out)
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="what", required=True)
@@ -122,9 +159,16 @@ def main(argv=None):
     b.add_argument("--kernel", action="append", required=True)
     b.add_argument("--out", required=True)
     b.add_argument("--cmd", default="")
+    c = sub.add_parser("counters")
+    c.add_argument("csv", nargs="+")
+    c.add_argument("--cmd", required=True)
+    c.add_argument("--title", required=True)
+    c.add_argument("--kernels", default="")
     args = ap.parse_args(argv)
     if args.what == "stats":
         sys.stdout.write(stats(args.csv, args.cmd, args.title))
+    elif args.what == "counters":
+        sys.stdout.write(counters(args.csv, args.cmd, args.title, args.kernels))
     else:
         rec = traffic(args.fetch, args.write, args.copy_bytes, args.copy_regex, args.kernel, args.out, args.cmd)
         print(json.dumps(rec, indent=1))

@@ -80,7 +80,7 @@ enum { NSA_BR_CMP = 1, NSA_BR_SLC = 2, NSA_BR_WIN = 4 };
 
 /* Work items for nsa_workspace_size. */
 enum { NSA_OP_COMPRESS = 0, NSA_OP_SCORE_SELECT = 1, NSA_OP_SPARSE_ATTN = 2, NSA_OP_DECODE = 3,
-       NSA_OP_FULL_ATTN = 4, NSA_OP_SPARSE_BWD = 5, NSA_OP_COMPRESS_BWD = 6 };
+       NSA_OP_FULL_ATTN = 4, NSA_OP_SPARSE_BWD = 5, NSA_OP_COMPRESS_BWD = 6, NSA_OP_PREFILL = 7 };
 
 typedef struct nsa_config {
     uint32_t struct_size;      /* sizeof(nsa_config) */
@@ -154,6 +154,23 @@ nsa_status nsa_select_from_scores(const nsa_config* cfg, const float* scores, in
 nsa_status nsa_sparse_attn_fwd(const nsa_config* cfg, const void* Q, const void* K, const void* V,
                                const int32_t* sel_idx, const float* o_cmp, const float* gate_logits,
                                void* O, void* ws, size_t ws_bytes, void* stream);
+
+/* Steps "compressed attention, block scores, selection, selected attention, sliding window,
+ * gated sum" in one call: nsa_score_select followed by nsa_sparse_attn_fwd (zjai.club notes,
+ * sections 5, 6 and 8; sunshychen.top: compressed scores reused as selection scores), run as
+ * one fused launch whose workgroups each score, select and attend their own tile of tokens.
+ * Same arithmetic and results as the two calls, bit for bit.
+ *   Inputs: Q [B,T,H,d_k], K [B,H_kv,T,d_k], V [B,H_kv,T,d_v], K_cmp / V_cmp [B,H_kv,N_cmp,d]
+ *   (from nsa_compress) bf16; gate_logits [B,T,H,3] fp32 (NULL = weight 1).
+ *   Outputs: O [B,T,H,d_v] bf16 (required); sel_idx [B,T,H_kv,top_n] int32, lse_cmp [B,T,H]
+ *   and o_cmp [B,T,H,d_v] fp32 are optional (NULL = kept in the workspace / not written).
+ *   Workspace: nsa_workspace_size(cfg, NSA_OP_PREFILL).
+ * Needs the compressed-overlap scores (NSA_SCORE_CMP_OVERLAP); every branch mask is allowed
+ * (the compressed branch's output is formed in any case: the scores need it).  Errors as
+ * for the two calls; NSA_ERR_UNSUPPORTED for the MEAN_DOT scores. */
+nsa_status nsa_prefill_fwd(const nsa_config* cfg, const void* Q, const void* K, const void* V, const void* K_cmp,
+                           const void* V_cmp, const float* gate_logits, void* O, int32_t* sel_idx, float* lse_cmp,
+                           float* o_cmp, void* ws, size_t ws_bytes, void* stream);
 
 /* One decode step (zjai.club notes, section 13): every sequence b has one new query at
  * position t_b = cache_len[b] - 1 whose K/V are already in the caches; K_cmp_cache /

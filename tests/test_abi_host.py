@@ -92,6 +92,37 @@ def test_workspace_sizes(name):
         want += (al(bg * n_chunk * c.n_slc * 4) + al(bg * c.n_slc * 4) + 2 * al((bg * c.n_slc + 1) * 4)
                  + 3 * al(rows * 4) + al(rows * c.d_v * 2))
     assert n == want
+    # the fused prefill: the scoring call's and the attention call's workspaces side by side,
+    # then room for the lists (int32) and o_cmp (fp32) the caller may not take
+    rc, n = _ws(c, ops.OP_PREFILL)
+    assert rc == 0
+    if c.score_mode == 0:
+        _, n_sel = _ws(c, ops.OP_SCORE_SELECT)
+        _, n_att = _ws(c, ops.OP_SPARSE_ATTN)
+        assert n == n_sel + n_att + al(c.batch * c.seq_len * c.num_kv_heads * c.top_n * 4) + al(
+            c.batch * c.seq_len * c.num_heads * c.d_v * 4)
+
+
+def test_prefill_fwd_validation():
+    L = ops.lib()
+    fake = ctypes.c_void_p(0x1000)
+    big = 1 << 40
+    # Q, K, V, K_cmp, V_cmp and O are required
+    for i in range(6):
+        args = [fake] * 6
+        args[i] = None
+        q, k, v, kc, vc, o = args
+        assert L.nsa_prefill_fwd(_cfg(), q, k, v, kc, vc, None, o, None, None, None, fake, big, None) == 1
+    # workspace too small / unaligned
+    assert L.nsa_prefill_fwd(_cfg(), fake, fake, fake, fake, fake, None, fake, None, None, None, fake, 16, None) == 4
+    assert L.nsa_prefill_fwd(_cfg(), fake, fake, fake, fake, fake, None, fake, None, None, None,
+                             ctypes.c_void_p(0x1001), big, None) == 4
+    # mean-key scores are not fused
+    assert L.nsa_prefill_fwd(_cfg(MOBA), fake, fake, fake, fake, fake, None, fake, None, None, None, fake, big,
+                             None) == 3
+    # window branch with window 0
+    assert L.nsa_prefill_fwd(_cfg(P8K, window=0), fake, fake, fake, fake, fake, None, fake, None, None, None, fake,
+                             big, None) == 2
 
 
 @pytest.mark.parametrize("over,status", [

@@ -225,7 +225,7 @@ def test_sparse_attn_value_scales():
 # end to end: the GPU chain compress -> score_select -> sparse_attn_fwd, staged against
 # the oracle at each step on the GPU's own upstream bytes
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("cfg", [TINY, P8K, P64K], ids=lambda c: c.name)
+@pytest.mark.parametrize("cfg", [TINY, RAGGED, RAGGED16, P8K, P64K], ids=lambda c: c.name)
 def test_prefill_end_to_end(cfg):
     _prefill_end_to_end(cfg)
 
@@ -240,12 +240,19 @@ def _prefill_end_to_end(cfg):
       * the gated output of every checked row within the output bar, the oracle attending
         with its own o_cmp and its own list (the GPU's list on near-tie rows, which are
         validated first).
-    Rows: all of them up to 2100 tokens, else the edges plus 64 (64K) or 300 drawn ones."""
+    Rows: all of them up to 2100 tokens, else the edges plus 64 (64K) or 300 drawn ones.
+    The fused call nsa_prefill_fwd must reproduce the three calls' outputs, lists, LSE and
+    o_cmp bit for bit (same arithmetic, one launch)."""
     announce(f"end to end {cfg.name}")
     inp = inputs.prefill_inputs(cfg)
-    r = ops.prefill(cfg, dev_bf16(inp["q"]), dev_bf16(inp["k"]), dev_bf16(inp["v"]), dev_bf16(inp["w_k"]),
-                    dev_bf16(inp["w_v"]), dev_bf16(inp["pe_k"]), dev_bf16(inp["pe_v"]), dev_f32(inp["gates"]))
+    args = [dev_bf16(inp[n]) for n in ("q", "k", "v", "w_k", "w_v", "pe_k", "pe_v")] + [dev_f32(inp["gates"])]
+    r = ops.prefill(cfg, *args)
+    # the fused call (nsa_prefill_fwd) runs the same arithmetic in one launch: identical bits
+    rf = ops.prefill(cfg, *args, fused=True)
     torch.cuda.synchronize()
+    for key in ("out", "sel", "lse", "o_cmp", "k_cmp", "v_cmp"):
+        assert torch.equal(r[key], rf[key]), f"{cfg.name}: fused prefill differs from the three calls in {key}"
+    del rf
     if cfg.seq_len <= 2100:
         rows = np.arange(cfg.seq_len, dtype=np.int32)
     else:
