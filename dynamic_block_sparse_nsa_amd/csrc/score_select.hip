@@ -243,15 +243,15 @@ __global__ __launch_bounds__(256, 2) void mean_scores_kernel(SelParams p) {
 
 // mode 1 with the selection fused, for one query head per KV head (G = 1) and at most
 // kFusedMaxPicks picks besides the forced blocks (the MoBA configuration: top-3 with the
-// own block forced).  A workgroup owns 64 tokens (a wave's 16 MFMA columns are 16 tokens);
-// each lane keeps, for its column, the best kFusedMaxPicks candidates among the keys it
-// holds as 64-bit entries score-key:~index (larger = better score, then lower index), so no
-// score row is ever stored.  A tile is skipped when no lane of the wave has a candidate
-// above its current fourth best.  The four lanes of a column merge their lists (bitonic
-// top-K of two sorted lists, then a sort) across the 16- and 32-lane swaps.
-template <int DK>
+// own block forced, two picks).  A workgroup owns 64 tokens (a wave's 16 MFMA columns are
+// 16 tokens); each lane keeps, for its column, the best K candidates (K = the picks rounded
+// up to 1, 2 or 4) among the keys it holds as 64-bit entries score-key:~index (larger =
+// better score, then lower index), so no score row is ever stored.  A tile is skipped when
+// no lane of the wave has a candidate above its current K-th best.  The four lanes of a
+// column merge their lists (bitonic top-K of two sorted lists, then a sort) across the 16-
+// and 32-lane swaps.
+template <int DK, int K>
 __global__ __launch_bounds__(256, 2) void mean_select_kernel(SelParams p) {
-    constexpr int K = kFusedMaxPicks;
     constexpr int TQ = kWaves * 16;
     constexpr int KSTR = DK + 8;
     constexpr int NDS = DK / 32;
@@ -457,12 +457,23 @@ bool launch_cmp_attn(bool with_o, int DK, int DV, int G, const SelParams& p, hip
     return true;
 }
 
+namespace {
+// each lane keeps the best K candidates, K the free picks rounded up to a power of two
+template <int DK>
+void mean_select_k(int picks, int grid, const SelParams& p, hipStream_t st) {
+    if (picks <= 1) mean_select_kernel<DK, 1><<<grid, 256, 0, st>>>(p);
+    else if (picks <= 2) mean_select_kernel<DK, 2><<<grid, 256, 0, st>>>(p);
+    else mean_select_kernel<DK, kFusedMaxPicks><<<grid, 256, 0, st>>>(p);
+}
+}  // namespace
+
 bool launch_mean_select(int DK, const SelParams& p, hipStream_t st) {
     constexpr int TQ = kWaves * 16;
     const int grid = xcd_grid(p.B * p.Hkv, (p.T + TQ - 1) / TQ);
-    if (DK == 192) mean_select_kernel<192><<<grid, 256, 0, st>>>(p);
-    else if (DK == 128) mean_select_kernel<128><<<grid, 256, 0, st>>>(p);
-    else if (DK == 64) mean_select_kernel<64><<<grid, 256, 0, st>>>(p);
+    const int picks = p.top_n - p.n_local;   // at most this many blocks are picked by score
+    if (DK == 192) mean_select_k<192>(picks, grid, p, st);
+    else if (DK == 128) mean_select_k<128>(picks, grid, p, st);
+    else if (DK == 64) mean_select_k<64>(picks, grid, p, st);
     else return false;
     return true;
 }
