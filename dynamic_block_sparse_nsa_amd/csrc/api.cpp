@@ -133,7 +133,7 @@ bool use_block_major(const Shape& s) { return s.G == 1 && s.br == NSA_BR_SLC; }
 // K and V copied into MFMA fragment order, padded with 64 zero keys past a multiple of 64; for the
 // block-major schedule also the bucket lists and the per-slot partial results.
 struct AttnWs {
-    size_t kf, vf, vmax, vexp, hist, bcnt, bstart, tstart, entries, pm, pl, po, total;
+    size_t kf, vf, vmax, vexp, hist, bcnt, bstart, tstart, tbk, entries, pm, pl, po, total;
     int tpad, n_chunk, n_bucket;
 };
 AttnWs attn_ws(const Shape& s) {
@@ -153,6 +153,7 @@ AttnWs attn_ws(const Shape& s) {
         w.bcnt = off; off = align_up(off + (size_t)w.n_bucket * 4, 256);
         w.bstart = off; off = align_up(off + (size_t)(w.n_bucket + 1) * 4, 256);
         w.tstart = off; off = align_up(off + (size_t)(w.n_bucket + 1) * 4, 256);
+        w.tbk = off; off = align_up(off + (size_t)nsa::moba_max_tiles((int)bg, s.T, s.n, s.n_slc) * 4, 256);
         w.entries = off; off = align_up(off + rows * 4, 256);
         w.pm = off; off = align_up(off + rows * 4, 256);
         w.pl = off; off = align_up(off + rows * 4, 256);
@@ -201,7 +202,7 @@ PrefillWs prefill_ws(const Shape& s) {
 // backward of the branches: K, V in fragment order for the statistics pass, the per-row
 // statistics, and the selected branch's block lists (own block included)
 struct BwdWs {
-    size_t kf, vf, vmax, vexp, stats, hist, bcnt, bstart, tstart, entries, total;
+    size_t kf, vf, vmax, vexp, stats, hist, bcnt, bstart, tstart, tbk, entries, total;
     int tpad, n_chunk, n_bucket;
 };
 BwdWs bwd_ws(const Shape& s) {
@@ -221,6 +222,7 @@ BwdWs bwd_ws(const Shape& s) {
         w.bcnt = off; off = align_up(off + (size_t)w.n_bucket * 4, 256);
         w.bstart = off; off = align_up(off + (size_t)(w.n_bucket + 1) * 4, 256);
         w.tstart = off; off = align_up(off + (size_t)(w.n_bucket + 1) * 4, 256);
+        w.tbk = off; off = align_up(off + (size_t)nsa::moba_max_tiles((int)bg, s.T, s.n, s.n_slc) * 4, 256);
         w.entries = off; off = align_up(off + bg * s.T * s.n * 4, 256);
     }
     w.total = off;
@@ -427,6 +429,7 @@ nsa_status sparse_attn_fwd_impl(const nsa_config* cfg, const void* Q, const void
         m.bucket_cnt = at<int>(ws, w.bcnt);
         m.bucket_start = at<int>(ws, w.bstart);
         m.tile_start = at<int>(ws, w.tstart);
+        m.tile_bucket = at<int>(ws, w.tbk);
         m.entries = at<int>(ws, w.entries);
         m.part_m = at<float>(ws, w.pm);
         m.part_l = at<float>(ws, w.pl);
@@ -811,12 +814,14 @@ nsa_status nsa_sparse_attn_bwd(const nsa_config* cfg, const void* Q, const void*
         m.bucket_cnt = at<int>(ws, w.bcnt);
         m.bucket_start = at<int>(ws, w.bstart);
         m.tile_start = at<int>(ws, w.tstart);
+        m.tile_bucket = at<int>(ws, w.tbk);
         m.entries = at<int>(ws, w.entries);
         m.B = s.B; m.T = s.T; m.Hkv = s.Hkv; m.lp = s.lp; m.n_slc = s.n_slc; m.top_n = s.n;
         m.n_chunk = w.n_chunk; m.n_bucket = w.n_bucket; m.keep_own = 1;
         nsa::launch_block_lists(m, hs);
         p.bucket_start = m.bucket_start;
         p.tile_start = m.tile_start;
+        p.tile_bucket = m.tile_bucket;
         p.entries = m.entries;
         p.n_bucket = w.n_bucket;
         p.nsb = (s.lp + 16 * nsa::kDkvWavesSlc - 1) / (16 * nsa::kDkvWavesSlc);

@@ -414,12 +414,7 @@ __global__ __launch_bounds__(64 * NW, KT == 1 ? 8 / NW : 1) void bwd_dkv_kernel(
         const int sub = x % p.nsb;
         x /= p.nsb;
         if (x >= p.tile_start[p.n_bucket]) return;
-        int lo = 0, hi = p.n_bucket - 1;   // the bucket owning list tile x
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (p.tile_start[mid] <= x) lo = mid;
-            else hi = mid - 1;
-        }
+        const int lo = p.tile_bucket[x];   // the bucket owning list tile x
         bg = lo / p.n_slc;
         const int j = lo % p.n_slc;
         kbase = j * p.lp + KEYS * sub;

@@ -101,6 +101,7 @@ struct MobaParams {
     int* bucket_cnt;           // [n_bucket]
     int* bucket_start;         // [n_bucket + 1]
     int* tile_start;           // [n_bucket + 1]
+    int* tile_bucket;          // [moba_max_tiles] the bucket of every 128-entry list tile
     int* entries;              // [B*Hkv*T*top_n] (token << 5 | slot), grouped by bucket
     float* part_m;             // [B,T,Hkv,top_n]
     float* part_l;             // [B,T,Hkv,top_n]
@@ -109,8 +110,8 @@ struct MobaParams {
     int keep_own;              // 1: the query's own block is listed too (backward lists)
     float scale_log2;
 };
-// the bucket lists alone (hist, prefix, scan, scatter); uses sel, T, Hkv, lp, n_slc, top_n,
-// n_chunk, n_bucket, keep_own and the list buffers
+// the bucket lists alone (hist, prefix, scan, tiles, scatter); uses sel, T, Hkv, lp, n_slc,
+// top_n, n_chunk, n_bucket, keep_own and the list buffers
 void launch_block_lists(const MobaParams& p, hipStream_t st);
 int moba_n_chunk(int T);
 int moba_n_own(int BH, int n_slc, int lp);
@@ -140,6 +141,7 @@ struct BwdParams {
     float* dVc;
     const int* bucket_start;   // block lists of the selected branch (launch_block_lists)
     const int* tile_start;
+    const int* tile_bucket;
     const int* entries;
     int B, T, Hkv, G, N, l, s, lp, top_n, window, branches, n_slc, n_bucket;
     int nsb;                   // 64-key sub-blocks per selection block

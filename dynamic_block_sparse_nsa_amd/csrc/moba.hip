@@ -112,6 +112,14 @@ __global__ __launch_bounds__(1024) void moba_scan_kernel(MobaParams p) {
     }
 }
 
+// the bucket of every list tile (a direct lookup for the work items, instead of a search
+// over the tile starts)
+__global__ __launch_bounds__(256) void moba_tiles_kernel(MobaParams p) {
+    const int bk = blockIdx.x * 256 + threadIdx.x;
+    if (bk >= p.n_bucket) return;
+    for (int t = p.tile_start[bk]; t < p.tile_start[bk + 1]; ++t) p.tile_bucket[t] = bk;
+}
+
 __global__ __launch_bounds__(256) void moba_scatter_kernel(MobaParams p) {
     extern __shared__ int cursor[];   // [n_slc]
     const int c = blockIdx.x, bh = blockIdx.y;
@@ -176,13 +184,7 @@ __global__ __launch_bounds__(256, 2) void moba_attn_kernel(MobaParams p) {
     } else {
         own = false;
         const int it = item - p.n_own;
-        int lo = 0, hi = p.n_bucket - 1;   // bucket with tile_start[bk] <= it < tile_start[bk + 1]
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (p.tile_start[mid] <= it) lo = mid;
-            else hi = mid - 1;
-        }
-        const int bk = lo;
+        const int bk = p.tile_bucket[it];   // tile_start[bk] <= it < tile_start[bk + 1]
         bh = bk / p.n_slc;
         j = bk % p.n_slc;
         const int e0 = p.bucket_start[bk] + (it - p.tile_start[bk]) * kCol;
@@ -340,77 +342,85 @@ __global__ __launch_bounds__(256, 2) void moba_attn_kernel(MobaParams p) {
 }
 
 // per (token, head): combine the slots of the token's list.  A row of DV values is DV/4
-// lanes with 4 values each (a wave covers 64*4/DV rows); the slots' fp16 partial outputs
-// are read once (non-temporal, 8 bytes per lane) and weighted by sum * 2^(m - M); the bf16
-// row is stored with 8-byte writes.
-template <int DV>
+// lanes with 4 values each (a wave covers 64*4/DV rows); each thread takes R rows (RPB rows
+// apart) and requests every slot's list entry, (max, sum) and fp16 output slice of all of
+// them in one round trip (slots with no block may hold stale values and are dropped by
+// selects), so that a wave has R times the bytes in flight; the partial outputs are read
+// once (non-temporal, 8 bytes per lane) and weighted by sum * 2^(m - M); the bf16 rows are
+// stored with 8-byte writes.  SM >= top_n.
+template <int DV, int SM, int R>
 __global__ __launch_bounds__(256) void moba_merge_kernel(MobaParams p) {
     constexpr int LPR = DV / 4;      // lanes per row
-    constexpr int RPB = 256 / LPR;   // rows per workgroup
-    const size_t row = (size_t)blockIdx.x * RPB + threadIdx.x / LPR;   // (b, t, h)
+    constexpr int RPB = 256 / LPR;   // rows per workgroup and step
+    const size_t nrows = (size_t)p.B * p.T * p.Hkv;
     const int li = threadIdx.x % LPR;
-    if (row >= (size_t)p.B * p.T * p.Hkv) return;
-    const int32_t* sel = p.sel + row * p.top_n;
-    float M = -INFINITY;
-    float L = 0.f;
-    f32x4 acc = zero4();
     auto half4 = [](const u32x2& hv) {
         return f32x4{(float)__builtin_bit_cast(_Float16, (u16)(hv[0] & 0xFFFFu)),
                      (float)__builtin_bit_cast(_Float16, (u16)(hv[0] >> 16)),
                      (float)__builtin_bit_cast(_Float16, (u16)(hv[1] & 0xFFFFu)),
                      (float)__builtin_bit_cast(_Float16, (u16)(hv[1] >> 16))};
     };
-    constexpr int SMAX = 8;
-    if (p.top_n <= SMAX) {
-        // every slot's list entry, (max, sum) and output slice requested together (one round
-        // trip); slots with no block may hold stale values and are dropped by selects
-        int js[SMAX];
-        float ms[SMAX], ls[SMAX];
-        u32x2 hv[SMAX];
+    size_t row[R];
+    int js[R][SM];
+    float ms[R][SM], ls[R][SM];
+    u32x2 hv[R][SM];
 #pragma unroll
-        for (int s = 0; s < SMAX; ++s)
+    for (int r = 0; r < R; ++r) {
+        row[r] = ((size_t)blockIdx.x * R + r) * RPB + threadIdx.x / LPR;   // (b, t, h)
+        const size_t rr = row[r] < nrows ? row[r] : nrows - 1;
+#pragma unroll
+        for (int s = 0; s < SM; ++s)
             if (s < p.top_n) {
-                js[s] = sel[s];
-                ms[s] = p.part_m[row * p.top_n + s];
-                ls[s] = p.part_l[row * p.top_n + s];
-                hv[s] = ld_stream(reinterpret_cast<const u32x2*>(p.part_o + (row * p.top_n + s) * DV) + li);
+                js[r][s] = p.sel[rr * p.top_n + s];
+                ms[r][s] = p.part_m[rr * p.top_n + s];
+                ls[r][s] = p.part_l[rr * p.top_n + s];
+                hv[r][s] = ld_stream(reinterpret_cast<const u32x2*>(p.part_o + (rr * p.top_n + s) * DV) + li);
             }
-        bool ok[SMAX];
+    }
 #pragma unroll
-        for (int s = 0; s < SMAX; ++s) {
-            ok[s] = s < p.top_n && js[s] >= 0 && ms[s] > -INFINITY;
-            M = ok[s] ? fmaxf(M, ms[s]) : M;
+    for (int r = 0; r < R; ++r) {
+        if (row[r] >= nrows) continue;
+        float M = -INFINITY, L = 0.f;
+        f32x4 acc = zero4();
+        bool ok[SM];
+#pragma unroll
+        for (int s = 0; s < SM; ++s) {
+            ok[s] = s < p.top_n && js[r][s] >= 0 && js[r][s] < p.n_slc && ms[r][s] > -INFINITY;
+            M = ok[s] ? fmaxf(M, ms[r][s]) : M;
         }
 #pragma unroll
-        for (int s = 0; s < SMAX; ++s) {
-            const float w = ok[s] ? fast_exp2(ms[s] - M) * ls[s] : 0.f;   // the slot's weight
+        for (int s = 0; s < SM; ++s) {
+            const float w = ok[s] ? fast_exp2(ms[r][s] - M) * ls[r][s] : 0.f;   // the slot's weight
             L += w;
-            const f32x4 o = half4(hv[s]);
+            const f32x4 o = half4(hv[r][s]);
 #pragma unroll
             for (int k = 0; k < 4; ++k) acc[k] += ok[s] ? w * o[k] : 0.f;
         }
-    } else {
-    for (int s = 0; s < p.top_n; ++s)
-        if (sel[s] >= 0) M = fmaxf(M, p.part_m[row * p.top_n + s]);
-    if (M > -INFINITY) {
-        for (int s = 0; s < p.top_n; ++s) {
-            if (sel[s] < 0) continue;
-            const float ms = p.part_m[row * p.top_n + s];
-            if (ms == -INFINITY) continue;
-            const float w = fast_exp2(ms - M) * p.part_l[row * p.top_n + s];   // the slot's weight
-            L += w;
-            const u32x2 hv = ld_stream(reinterpret_cast<const u32x2*>(p.part_o + (row * p.top_n + s) * DV) + li);
-            acc += w * half4(hv);
-        }
+        const float g = p.gates ? sigmoidf_(p.gates[row[r] * 3 + 1]) : 1.f;
+        const size_t bh = row[r] / ((size_t)p.T * p.Hkv) * p.Hkv + row[r] % p.Hkv;
+        const float inv = L > 0.f ? ldexpf(g / L, p.vexp[bh]) : 0.f;   // V's scaling undone
+        const u32x2 v = {(uint32_t)f2bf(acc[0] * inv) | ((uint32_t)f2bf(acc[1] * inv) << 16),
+                         (uint32_t)f2bf(acc[2] * inv) | ((uint32_t)f2bf(acc[3] * inv) << 16)};
+        st_stream(v, reinterpret_cast<u32x2*>(p.O + row[r] * DV) + li);
     }
-    }
-    const float g = p.gates ? sigmoidf_(p.gates[row * 3 + 1]) : 1.f;
-    const size_t bh = row / ((size_t)p.T * p.Hkv) * p.Hkv + row % p.Hkv;
-    const float inv = L > 0.f ? ldexpf(g / L, p.vexp[bh]) : 0.f;   // V's scaling undone
-    const u32x2 v = {(uint32_t)f2bf(acc[0] * inv) | ((uint32_t)f2bf(acc[1] * inv) << 16),
-                     (uint32_t)f2bf(acc[2] * inv) | ((uint32_t)f2bf(acc[3] * inv) << 16)};
-    st_stream(v, reinterpret_cast<u32x2*>(p.O + row * DV) + li);
 }
+
+namespace {
+template <int DV>
+void moba_merge(const MobaParams& p, hipStream_t st) {
+    constexpr int RPB = 256 / (DV / 4);
+    const size_t rows = (size_t)p.B * p.T * p.Hkv;
+    if (p.top_n <= 4) {
+        constexpr int R = 4;
+        moba_merge_kernel<DV, 4, R><<<(unsigned)((rows + RPB * R - 1) / (RPB * R)), 256, 0, st>>>(p);
+    } else if (p.top_n <= 8) {
+        constexpr int R = 2;
+        moba_merge_kernel<DV, 8, R><<<(unsigned)((rows + RPB * R - 1) / (RPB * R)), 256, 0, st>>>(p);
+    } else {
+        moba_merge_kernel<DV, 32, 1><<<(unsigned)((rows + RPB - 1) / RPB), 256, 0, st>>>(p);
+    }
+}
+}  // namespace
 
 // ---------------------------------------------------------------------------
 int moba_n_chunk(int T) { return (T + kMobaChunk - 1) / kMobaChunk; }
@@ -427,6 +437,7 @@ void launch_block_lists(const MobaParams& p, hipStream_t st) {
     moba_hist_kernel<<<dim3(p.n_chunk, p.B * p.Hkv), 256, lds_cnt, st>>>(p);
     moba_prefix_kernel<<<(p.n_bucket + 255) / 256, 256, 0, st>>>(p);
     moba_scan_kernel<<<1, 1024, 0, st>>>(p);
+    moba_tiles_kernel<<<(p.n_bucket + 255) / 256, 256, 0, st>>>(p);
     moba_scatter_kernel<<<dim3(p.n_chunk, p.B * p.Hkv), 256, lds_cnt, st>>>(p);
 }
 
@@ -438,9 +449,8 @@ bool launch_moba_attn(int DK, int DV, const MobaParams& p, hipStream_t st) {
     else if (DK == 64 && DV == 64) moba_attn_kernel<64, 64><<<nwg, 256, 0, st>>>(p);
     else if (DK == 192 && DV == 128) moba_attn_kernel<192, 128><<<nwg, 256, 0, st>>>(p);
     else return false;
-    const size_t rows = (size_t)p.B * p.T * p.Hkv;
-    if (DV == 128) moba_merge_kernel<128><<<(unsigned)((rows + 7) / 8), 256, 0, st>>>(p);
-    else moba_merge_kernel<64><<<(unsigned)((rows + 15) / 16), 256, 0, st>>>(p);
+    if (DV == 128) moba_merge<128>(p, st);
+    else moba_merge<64>(p, st);
     return true;
 }
 

@@ -89,8 +89,9 @@ def test_workspace_sizes(name):
     if c.heads_per_group == 1 and c.branches == 2:
         n_chunk = -(-c.seq_len // 1024)
         rows = bg * c.seq_len * c.top_n
+        max_tiles = rows // 128 + bg * c.n_slc   # every bucket: at most ceil(n / 128) list tiles
         want += (al(bg * n_chunk * c.n_slc * 4) + al(bg * c.n_slc * 4) + 2 * al((bg * c.n_slc + 1) * 4)
-                 + 3 * al(rows * 4) + al(rows * c.d_v * 2))
+                 + al(max_tiles * 4) + 3 * al(rows * 4) + al(rows * c.d_v * 2))
     assert n == want
     # the fused prefill: the scoring call's and the attention call's workspaces side by side,
     # then room for the lists (int32) and o_cmp (fp32) the caller may not take
