@@ -12,7 +12,7 @@ on), the oracle timed on the host cores on a bounded sample, the backward pass o
 65536-token caches, HBM GB/s) and MoBA (131072 and 1048576 tokens) figures.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-decode] [--no-moba]
-                       [--no-dense] [--no-backward] [--locality]
+                       [--no-dense] [--no-backward] [--no-ceilings] [--locality]
 """
 from __future__ import annotations
 
@@ -187,6 +187,58 @@ def cpu_baseline(cfg: NSAConfig, inp: dict, budget_rows: int = 3072, nb: int = 2
                        f"({t_rows:.2f} s, scaled to all rows); {threads} OpenMP threads")}
 
 
+def ceilings(torch, dev) -> dict:
+    """Measured ceilings of the units the kernels are bound by (libnsa_ceilings.so): bf16 MFMA
+    from registers, a streaming read of 4 GiB, and random 40 KB block gathers (the selected
+    branch's access pattern: 24 KB of K + 16 KB of V per block) over a 168 MB buffer (the 64K
+    workload's K and V) and over a 4 MB one (one XCD's L2)."""
+    import ctypes
+    from dynamic_block_sparse_nsa_amd.build import CEIL_LIB, build_ceilings
+    if not os.path.exists(CEIL_LIB):
+        build_ceilings()
+    C = ctypes.CDLL(CEIL_LIB)
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    P = ctypes.c_void_p
+
+    def timed(launch, reps=5):
+        launch()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            rc = launch()
+            e1.record()
+            torch.cuda.synchronize()
+            assert rc == 0, rc
+            ts.append(e0.elapsed_time(e1) * 1e-3)
+        return float(np.median(ts))
+
+    res = {}
+    n_wg, iters = 4096, 400
+    out = torch.empty(n_wg * 256, dtype=torch.float32, device=dev)
+    sec = timed(lambda: C.nsa_ceiling_mfma(P(out.data_ptr()), n_wg, iters, st))
+    res["mfma_bf16_tflops"] = round(n_wg * 4 * iters * 32 * 16384 / sec / 1e12, 1)
+    buf = torch.empty(1 << 32, dtype=torch.uint8, device=dev).fill_(3)
+    wout = torch.empty(4096 * 256, dtype=torch.int32, device=dev)
+    sec = timed(lambda: C.nsa_ceiling_stream(P(buf.data_ptr()), ctypes.c_size_t(1 << 32), P(wout.data_ptr()), 4096, st))
+    res["hbm_stream_read_gbs"] = round((1 << 32) / sec / 1e9, 1)
+    blk = 40 * 1024
+    for name, span in (("gather_40k_168mb_gbs", 168 * (1 << 20)), ("gather_40k_4mb_gbs", 4 * (1 << 20))):
+        rng = np.random.default_rng(5)
+        n_blk = 100000
+        offs = torch.from_numpy(rng.integers(0, span // blk, n_blk).astype(np.int64) * blk).to(dev)
+        gout = torch.empty(n_blk * 256, dtype=torch.int32, device=dev)
+        sec = timed(lambda: C.nsa_ceiling_gather(P(buf.data_ptr()), P(offs.data_ptr()), n_blk, blk,
+                                                 P(gout.data_ptr()), st))
+        res[name] = round(n_blk * blk / sec / 1e9, 1)
+    del buf, wout, out
+    torch.cuda.empty_cache()
+    res["note"] = ("mfma: 4096 workgroups x 4 waves x 12800 bf16 16x16x32 products from registers; stream: 4 GiB "
+                   "read once; gather: 100000 random 40 KB blocks of the named buffer")
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -201,6 +253,7 @@ def main():
                     help="also time the selected-branch kernel on lists with shared picks per selection block "
                          "(off by default: the same kernel and grid as the headline call, so a profile of the "
                          "default command keeps the headline kernel's own average)")
+    ap.add_argument("--no-ceilings", action="store_true", help="skip the measured MFMA / HBM / gather ceilings")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run one elementwise kernel over 1 GiB (reads and writes 1 GiB: the known-size kernel that scales HBM counters)")
     args = ap.parse_args()
@@ -538,6 +591,11 @@ def main():
                            "per_call_ms": {n: round(float(c), 3) for n, c in zip(names3, pcm.mean(axis=0))}}
             del Qm, Km, Vm, kbar, selm, om, wsm
             torch.cuda.empty_cache()
+
+    # ---------------- measured ceilings ----------------
+    if not args.no_ceilings:
+        print("[bench] ceilings", file=sys.stderr, flush=True)
+        result["ceilings"] = ceilings(torch, dev)
 
     # ---------------- CPU baseline ----------------
     if not args.no_cpu:

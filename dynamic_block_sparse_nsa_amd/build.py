@@ -1,7 +1,8 @@
 """Build ``libnsa.so`` (the C-ABI library, HIP for gfx950) in-tree.
 
 ``python -m dynamic_block_sparse_nsa_amd.build`` compiles every source under ``csrc/``
-with hipcc in parallel into ``_build/`` and links ``libnsa.so`` next to this file.
+with hipcc in parallel into ``_build/`` and links ``libnsa.so`` next to this file, then
+builds ``libnsa_ceilings.so`` (the roofline microbenchmarks of ``ceilings/``).
 """
 from __future__ import annotations
 
@@ -56,6 +57,24 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+CEIL_SRC = os.path.join(HERE, "ceilings", "ceilings.hip")
+CEIL_LIB = os.path.join(HERE, "libnsa_ceilings.so")
+
+
+def build_ceilings(verbose: bool = False) -> str:
+    """libnsa_ceilings.so: the roofline microbenchmarks (include/nsa_ceilings.h)."""
+    tmp = CEIL_LIB + ".tmp"
+    cmd = [HIPCC, *FLAGS, "-shared", CEIL_SRC, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {CEIL_SRC}:\n{r.stderr[-4000:]}")
+    os.replace(tmp, CEIL_LIB)
+    if verbose:
+        print(f"built {CEIL_LIB}")
+    return CEIL_LIB
+
+
 if __name__ == "__main__":
     build(verbose=True)
+    build_ceilings(verbose=True)
     sys.exit(0)

@@ -39,6 +39,25 @@ def test_library_exports_every_declared_symbol():
     assert exported == names
 
 
+def test_ceilings_library_exports_its_header():
+    """libnsa_ceilings.so (the roofline microbenchmarks) exports exactly what
+    include/nsa_ceilings.h declares, and rejects invalid arguments before any launch."""
+    from dynamic_block_sparse_nsa_amd.build import CEIL_LIB, build_ceilings
+    if not os.path.exists(CEIL_LIB):
+        build_ceilings()
+    text = open(os.path.join(os.path.dirname(HEADER), "nsa_ceilings.h")).read()
+    names = sorted(set(re.findall(r"^int\s+(nsa_\w+)\(", text, re.M)))
+    assert names == ["nsa_ceiling_gather", "nsa_ceiling_mfma", "nsa_ceiling_stream"]
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", CEIL_LIB], capture_output=True, text=True).stdout
+    assert sorted(set(re.findall(r" T (nsa_\w+)", out))) == names
+    C = ctypes.CDLL(CEIL_LIB)
+    fake = ctypes.c_void_p(0x1000)
+    assert C.nsa_ceiling_mfma(None, 1, 1, None) == 1
+    assert C.nsa_ceiling_stream(fake, ctypes.c_size_t(17), fake, 1, None) == 1
+    assert C.nsa_ceiling_gather(fake, fake, 4, 1000, fake, None) == 1
+
+
 def test_struct_layout_matches_header():
     # 1 uint32 + 16 int32 + 1 float
     assert ctypes.sizeof(ops.CConfig) == 4 * 18
