@@ -87,9 +87,10 @@ def pick(values: dict, regex: str) -> float:
     return max(hits)
 
 
-def traffic(fetch_csv, write_csv, copy_bytes, copy_regex, kernels, out_path, cmd):
+def traffic(fetch_csv, write_csv, copy_bytes, copy_regex, kernels, out_path, cmd, util_csv=None):
     fetch = per_kernel_counter(fetch_csv, "FETCH_SIZE")
     write = per_kernel_counter(write_csv, "WRITE_SIZE")
+    util = per_kernel_counter(util_csv, "MfmaUtil") if util_csv else {}
     # counters are in KiB per dispatch; the copy reads and writes copy_bytes exactly
     f_scale = copy_bytes / (pick(fetch, copy_regex) * 1024.0)
     w_scale = copy_bytes / (pick(write, copy_regex) * 1024.0)
@@ -103,6 +104,9 @@ def traffic(fetch_csv, write_csv, copy_bytes, copy_regex, kernels, out_path, cmd
                      "bytes_per_launch": int(fb + wb), "fetch_scale": round(f_scale, 4),
                      "write_scale": round(w_scale, 4), "copy_bytes": copy_bytes,
                      "sources": srcs, "source_sha": source_sha(srcs), "command": cmd}
+        hits = [v for k, v in util.items() if re.search(rf"\b{re.escape(name)}\b", k)]
+        if hits:   # fraction of the MFMA pipes' cycles busy (rocprofv3 MfmaUtil, same command)
+            rec[name]["mfma_busy_frac"] = round(max(hits) / 100.0, 4)
     with open(out_path, "w") as f:
         json.dump(rec, f, indent=1, sort_keys=True)
         f.write("\n")
@@ -159,6 +163,7 @@ def main(argv=None):
     b.add_argument("--kernel", action="append", required=True)
     b.add_argument("--out", required=True)
     b.add_argument("--cmd", default="")
+    b.add_argument("--util", default=None, help="counter CSV with MfmaUtil (optional)")
     c = sub.add_parser("counters")
     c.add_argument("csv", nargs="+")
     c.add_argument("--cmd", required=True)
@@ -170,7 +175,8 @@ def main(argv=None):
     elif args.what == "counters":
         sys.stdout.write(counters(args.csv, args.cmd, args.title, args.kernels))
     else:
-        rec = traffic(args.fetch, args.write, args.copy_bytes, args.copy_regex, args.kernel, args.out, args.cmd)
+        rec = traffic(args.fetch, args.write, args.copy_bytes, args.copy_regex, args.kernel, args.out, args.cmd,
+                      args.util)
         print(json.dumps(rec, indent=1))
 
 
