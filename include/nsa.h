@@ -294,7 +294,9 @@ nsa_status nsa_sparse_attn_fwd_train(const nsa_config* cfg, const void* Q, const
  *   dW_k[r*d_k+e,o]  = sum_{b,g,i} (K[b,g,i*s+r,e] + pe_k[r,e]) dK_cmp[b,g,i,o]
  * and the same for V.  K, V, W_*, pe_* bf16 as for nsa_compress; dK, dV fp32 [B,H_kv,T,d]
  * (accumulated); dW_k [l*d_k,d_k], dW_v [l*d_v,d_v], dpe_k [l,d_k], dpe_v [l,d_v] fp32,
- * overwritten.  fp32 arithmetic, sums across blocks by fp32 atomics.  Workspace:
+ * overwritten.  fp32 arithmetic.  dK and dV get one add per element, with no atomics (each
+ * element's terms are summed by one thread); dW and dpe sum row ranges with fp32 atomics,
+ * so their rounding depends on the order of those sums.  Workspace:
  * nsa_workspace_size(cfg, NSA_OP_COMPRESS_BWD).  Errors: NSA_ERR_NULL for any missing
  * pointer, NSA_ERR_UNSUPPORTED for NSA_PHI_MEAN. */
 nsa_status nsa_compress_bwd(const nsa_config* cfg, const void* K, const void* V, const void* W_k,
