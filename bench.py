@@ -140,33 +140,24 @@ def time_calls(fns, steps, warmup, torch):
     return per_call, wall
 
 
-def cpu_baseline(cfg: NSAConfig, inp: dict, budget_rows: int = 3072, nb: int = 2048) -> dict:
-    """The fp64 oracle on a bounded sample of the same workload, scaled to tokens/s:
-    compression of ``nb`` blocks per KV group (scaled to all N_cmp blocks) plus the score,
-    select and attend stages for the last ``budget_rows`` rows (the most expensive ones;
-    scaled to T rows at that cost, which overstates the CPU's speed on earlier rows only
-    through their shorter compressed history)."""
+def cpu_baseline(cfg: NSAConfig, inp: dict, budget_rows: int = 3072) -> dict:
+    """The fp64 oracle on a bounded sample of the same workload, scaled to tokens/s: the
+    whole compression (every block of every KV group, rounded to bf16 as the path stores
+    it), then the score, select and attend stages on those compressed keys for the last
+    ``budget_rows`` rows (the most expensive ones; scaled to T rows at that cost, which
+    overstates the CPU's speed on earlier rows only through their shorter compressed
+    history)."""
+    from oracle import pipeline
     import oracle
-    from dynamic_block_sparse_nsa_amd import inputs as inputs_mod
     from dynamic_block_sparse_nsa_amd.inputs import bf16_bits_to_f64 as f64
 
     threads = oracle.num_threads()
-    nb = min(nb, cfg.n_cmp)
-    blocks = np.arange(nb)
+    K, V = f64(inp["k"][0]), f64(inp["v"][0])
     t0 = time.perf_counter()
-    for g in range(cfg.num_kv_heads):
-        oracle.compress_linear(f64(inp["k"][0, g]), f64(inp["pe_k"]), f64(inp["w_k"]), cfg.cmp_block, cfg.cmp_stride,
-                               blocks)
-        oracle.compress_linear(f64(inp["v"][0, g]), f64(inp["pe_v"]), f64(inp["w_v"]), cfg.cmp_block, cfg.cmp_stride,
-                               blocks)
-    t_cmp = (time.perf_counter() - t0) * cfg.n_cmp / nb
-    # stand-alone compressed keys/values for the row stages (their cost is the scaled
-    # compression time above)
-    ckv = inputs_mod.compressed_kv(cfg, seed=100 + cfg.seed)
-    Kc, Vc = f64(ckv["k_cmp"][0]), f64(ckv["v_cmp"][0])
+    Kc, Vc = pipeline.compress_all(cfg, K, V, f64(inp["w_k"]), f64(inp["w_v"]), f64(inp["pe_k"]), f64(inp["pe_v"]))
+    t_cmp = time.perf_counter() - t0
     rows = np.arange(cfg.seq_len - budget_rows, cfg.seq_len, dtype=np.int32)
     Qr = f64(inp["q"][0, rows])
-    K, V = f64(inp["k"][0]), f64(inp["v"][0])
     t1 = time.perf_counter()
     ss = oracle.score_select(cfg, Qr, rows, Kc, Vc, want_scores=False)
     oracle.attend(cfg, Qr, rows, K, V, ss["sel"], ss["o_cmp"], inp["gates"][0, rows])
@@ -182,9 +173,9 @@ def cpu_baseline(cfg: NSAConfig, inp: dict, budget_rows: int = 3072, nb: int = 2
         pass
     return {"value": round(cfg.seq_len / total, 2), "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "cpu_model": cpu_model, "host_cpus": os.cpu_count(),
-            "sample": (f"fp64 oracle: compression of {nb} of {cfg.n_cmp} blocks per KV group ({t_cmp * nb / cfg.n_cmp:.2f} s, "
-                       f"scaled) + score/select/attend of the last {budget_rows} of {cfg.seq_len} rows "
-                       f"({t_rows:.2f} s, scaled to all rows); {threads} OpenMP threads")}
+            "sample": (f"fp64 oracle: compression of all {cfg.n_cmp} blocks of every KV group ({t_cmp:.2f} s) + "
+                       f"score/select/attend on those compressed keys for the last {budget_rows} of {cfg.seq_len} "
+                       f"rows ({t_rows:.2f} s, scaled to all rows); {threads} OpenMP threads")}
 
 
 def ceilings(torch, dev) -> dict:

@@ -44,8 +44,6 @@ __host__ __device__ constexpr int cmp_waves(int) { return 4; }
 // Tokens per workgroup tile of the compressed-attention body.
 __host__ __device__ constexpr int cmp_tile_tokens(int G) { return cmp_waves(G) * (G == 1 ? 1 : 2) * 16 / G; }
 
-typedef __attribute__((address_space(3))) void lds_void;
-
 // ---------------------------------------------------------------------------
 // Compressed attention (log-sum-exp, o_cmp) and block scores of one workgroup's tile of
 // TQ = WAVES * NQ * 16 / G tokens starting at tok0 (a multiple of TQ) of KV group `unit`.  Every wave of the workgroup must call it.  Ends with the workgroup's

@@ -32,6 +32,8 @@ __device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const 
 
 // fp16 variant (P in fp16, 2^-11 relative rounding, against fp16 values)
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+// LDS address space, for the destination of the global -> LDS copies
+typedef __attribute__((address_space(3))) void lds_void;
 __device__ __forceinline__ f32x4 mfma16h(const f16x8& a, const f16x8& b, const f32x4& c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }

@@ -24,8 +24,6 @@ constexpr int kWaves = 4;
 constexpr int kKeys = 64;
 constexpr float kLazy = 8.f;   // log2 headroom before the softmax reference moves
 
-typedef __attribute__((address_space(3))) void lds_void;
-
 }  // namespace
 
 template <int DK, int DV, int G, int NQ>

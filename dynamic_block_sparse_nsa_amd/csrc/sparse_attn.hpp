@@ -203,7 +203,8 @@ __device__ __forceinline__ void sparse_attn_tokens(const AttnParams& p, int unit
     u16* kbuf[2] = {lds, lds + Tile::KE};
     u16* vbuf[2] = {lds + 2 * Tile::KE, lds + 2 * Tile::KE + Tile::VE};
 
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
     const int li = lane & 15, lq = lane >> 4;
     const int T = p.T;
     const int b = unit / p.Hkv, g = unit % p.Hkv;
