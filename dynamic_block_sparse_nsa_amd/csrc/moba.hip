@@ -18,8 +18,11 @@
 //   moba_merge_kernel     per (token, head): combine the slots, gate, bf16 store
 // The partial of a (token, slot) is written by exactly one work item, so results do not
 // depend on the order in which entries land in a bucket.
+#include <climits>
+
 #include "common.hpp"
 #include "launch.hpp"
+#include "select.hpp"
 
 namespace nsa {
 
@@ -27,6 +30,10 @@ namespace {
 
 constexpr int kCol = 128;    // query columns per work item (4 waves x 2 tiles x 16)
 constexpr int kKeys = 64;    // keys per LDS tile
+constexpr float kMobaLazy = 8.f;   // log2 headroom before a column's softmax reference moves
+
+// dynamic LDS of moba_attn_kernel: two K tiles and one V tile of 64 keys
+constexpr size_t moba_attn_lds(int DK, int DV) { return (size_t)kKeys * (2 * DK + DV) * 2; }
 static_assert(kCol == kBwdTile, "the backward's work items use the lists' 128-entry tiles");
 
 }  // namespace
@@ -143,15 +150,18 @@ __global__ __launch_bounds__(256) void moba_scatter_kernel(MobaParams p) {
 // XCD-aware: workgroups i, i + 8, i + 16, ... run on one XCD, so consecutive items (the
 // tiles of one bucket, sharing the block's K and V) are given to the same XCD's L2.
 template <int DK, int DV>
-__global__ __launch_bounds__(256, 2) void moba_attn_kernel(MobaParams p) {
+__global__ __launch_bounds__(256, DK >= 192 ? 2 : 3) void moba_attn_kernel(MobaParams p) {
     constexpr int NDS = DK / 32, NDT = DV / 16;
     constexpr int KE = 4 * NDS * 512;       // K elements of a 64-key tile (fragment order)
     constexpr int VE = 2 * NDT * 512;       // V elements
-    __shared__ __attribute__((aligned(16))) u16 kbuf[2][KE];
-    __shared__ __attribute__((aligned(16))) u16 vbuf[2][VE];
+    // K tiles double-buffered, the V tile single-buffered, both filled by global -> LDS copies
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    u16* kslot = reinterpret_cast<u16*>(smem);   // [2][KE]
+    u16* vbuf = kslot + 2 * KE;                   // [VE]
     __shared__ int col_tok[kCol], col_slot[kCol];
 
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int li = lane & 15, lq = lane >> 4;
     const int nwg = gridDim.x;
     const int item = (blockIdx.x % 8) * (nwg / 8) + blockIdx.x / 8;   // nwg is a multiple of 8
@@ -223,25 +233,25 @@ __global__ __launch_bounds__(256, 2) void moba_attn_kernel(MobaParams p) {
 
     const u16* kg = p.Kf + (size_t)bh * p.Tpad * DK;
     const u16* vg = p.Vf + (size_t)bh * p.Tpad * DV;
-    // a 64-key tile in fragment order is KE + VE contiguous elements of the copies; it is
-    // loaded to registers before a tile's math and stored to the other LDS buffer after it
-    u32x4 rk[KE / 2048], rv[VE / 2048];
-    auto load = [&](int tix) {
-        const int key0 = kbeg + kKeys * min(tix, max(ntile - 1, 0));
-        const u16* ks = kg + (size_t)(key0 / 16) * NDS * 512;
-        const u16* vs = vg + (size_t)(key0 / 32) * NDT * 512;
-#pragma unroll
-        for (int i = 0; i < KE / 2048; ++i) rk[i] = *reinterpret_cast<const u32x4*>(ks + (threadIdx.x + 256 * i) * 8);
-#pragma unroll
-        for (int i = 0; i < VE / 2048; ++i) rv[i] = *reinterpret_cast<const u32x4*>(vs + (threadIdx.x + 256 * i) * 8);
+    // a 64-key tile in fragment order is KE (K) and VE (V) contiguous elements of the copies
+    auto issue_k = [&](int tix, u16* dst) {
+        const u16* src = kg + (size_t)((kbeg + kKeys * tix) / 16) * NDS * 512;
+        for (int ch = wave; ch < KE / 512; ch += 4)
+            __builtin_amdgcn_global_load_lds(src + ch * 512 + lane * 8, (lds_void*)(dst + ch * 512), 16, 0, 0);
     };
-    auto store = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < KE / 2048; ++i) *reinterpret_cast<u32x4*>(&kbuf[buf][(threadIdx.x + 256 * i) * 8]) = rk[i];
-#pragma unroll
-        for (int i = 0; i < VE / 2048; ++i) *reinterpret_cast<u32x4*>(&vbuf[buf][(threadIdx.x + 256 * i) * 8]) = rv[i];
+    auto issue_v = [&](int tix) {
+        const u16* src = vg + (size_t)((kbeg + kKeys * tix) / 32) * NDT * 512;
+        for (int ch = wave; ch < VE / 512; ch += 4)
+            __builtin_amdgcn_global_load_lds(src + ch * 512 + lane * 8, (lds_void*)(vbuf + ch * 512), 16, 0, 0);
     };
+    // a column's last visible key (empty columns: none masked, their values are never stored)
+    int hi[2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) hi[c] = tok[c] >= 0 ? tok[c] : INT_MAX;
+    const int hi_min = (int)wave_min_u32((uint32_t)min(hi[0], hi[1]));   // the wave's earliest limit
 
+    // m: the column's reference (the same in its four lanes), moved only when a tile exceeds
+    // it by more than 2^8, so that o is rarely rescaled; p = 2^(x - m) <= 2^8 fits fp16
     float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
     f32x4 o[2][NDT];
 #pragma unroll
@@ -250,72 +260,89 @@ __global__ __launch_bounds__(256, 2) void moba_attn_kernel(MobaParams p) {
         for (int dt = 0; dt < NDT; ++dt) o[c][dt] = zero4();
 
     if (ntile > 0) {
-        load(0);
-        store(0);
+        issue_k(0, kslot);
+        issue_v(0);
     }
-    __syncthreads();
     for (int tix = 0; tix < ntile; ++tix) {
-        const int buf = tix & 1;
-        load(tix + 1);   // unconditional (clamped): every wait covers only what it consumes
+        // this thread's copies of tile tix have landed, then everyone's have
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        if (tix + 1 < ntile) issue_k(tix + 1, kslot + ((tix + 1) & 1) * KE);
+        const u16* kb = kslot + (tix & 1) * KE;
         const int key0 = kbeg + kKeys * tix;
         f32x4 s[4][2];
 #pragma unroll
-        for (int kt = 0; kt < 4; ++kt) {
+        for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
             for (int c = 0; c < 2; ++c) s[kt][c] = zero4();
 #pragma unroll
-            for (int ds = 0; ds < NDS; ++ds) {
-                const bf16x8 a = ld8(&kbuf[buf][((kt * NDS + ds) * 64 + lane) * 8]);
+        for (int ds = 0; ds < NDS; ++ds)
+#pragma unroll
+            for (int kt = 0; kt < 4; ++kt) {
+                const bf16x8 a = ld8(&kb[((kt * NDS + ds) * 64 + lane) * 8]);
 #pragma unroll
                 for (int c = 0; c < 2; ++c) s[kt][c] = mfma16(a, qf[c][ds], s[kt][c]);
             }
+        if (key0 + kKeys - 1 > hi_min) {   // some column's causal limit falls in this tile
+#pragma unroll
+            for (int c = 0; c < 2; ++c)
+#pragma unroll
+                for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        if (key0 + 16 * kt + 4 * lq + r > hi[c]) s[kt][c][r] = -INFINITY;
         }
-        f32x4 pv[4][2];
+        float mt[2];
+        bool grow = false;
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
-            const int hi_key = tok[c];   // causal limit of this column (whole block for earlier blocks)
-            float x[16];
-            float tm = -INFINITY;
+            float tmax = fmaxf(s[0][c][0], s[0][c][1]);
+#pragma unroll
+            for (int e = 2; e < 16; ++e) tmax = fmaxf(tmax, s[e >> 2][c][e & 3]);
+            mt[c] = col_max(tmax) * p.scale_log2;
+            grow |= mt[c] > m[c] + kMobaLazy;
+        }
+        if (__any(grow)) {   // move the references (wave-uniform branch)
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+                const float mnew = fmaxf(m[c], mt[c]);
+                const float alpha = m[c] == -INFINITY ? 0.f : fast_exp2(m[c] - mnew);
+                l[c] *= alpha;
+#pragma unroll
+                for (int dt = 0; dt < NDT; ++dt) o[c][dt] *= alpha;
+                m[c] = mnew;
+            }
+        }
+        // masked keys give 2^-inf = 0 (every column has a visible key in its first tile)
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            float acc = 0.f;
 #pragma unroll
             for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int key = key0 + 16 * kt + 4 * lq + r;
-                    x[kt * 4 + r] = key <= hi_key ? s[kt][c][r] * p.scale_log2 : -INFINITY;
-                    tm = fmaxf(tm, x[kt * 4 + r]);
+                    const float e = fast_exp2(__builtin_fmaf(s[kt][c][r], p.scale_log2, -m[c]));
+                    s[kt][c][r] = e;
+                    acc += e;
                 }
-            tm = col_max(tm);
-            const float mnew = fmaxf(m[c], tm);
-            const float alpha = mnew == -INFINITY ? 1.f : fast_exp2(m[c] - mnew);
-            float ps = 0.f;
-#pragma unroll
-            for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const float e = mnew == -INFINITY ? 0.f : fast_exp2(x[kt * 4 + r] - mnew);
-                    pv[kt][c][r] = e;
-                    ps += e;
-                }
-            l[c] = l[c] * alpha + ps;
-            m[c] = mnew;
-#pragma unroll
-            for (int dt = 0; dt < NDT; ++dt) o[c][dt] *= alpha;
+            l[c] += acc;
         }
 #pragma unroll
         for (int u = 0; u < 2; ++u) {   // P in fp16 against the scaled fp16 V copy: one product
             f16x8 ph[2];
 #pragma unroll
-            for (int c = 0; c < 2; ++c) ph[c] = pack_p_h(pv[2 * u][c], pv[2 * u + 1][c]);
+            for (int c = 0; c < 2; ++c) ph[c] = pack_p_h(s[2 * u][c], s[2 * u + 1][c]);
 #pragma unroll
             for (int dt = 0; dt < NDT; ++dt) {
-                const f16x8 a = ld8h(&vbuf[buf][((u * NDT + dt) * 64 + lane) * 8]);
+                const f16x8 a = ld8h(&vbuf[((u * NDT + dt) * 64 + lane) * 8]);
 #pragma unroll
                 for (int c = 0; c < 2; ++c) o[c][dt] = mfma16h(a, ph[c], o[c][dt]);
             }
         }
-        __builtin_amdgcn_sched_barrier(0);   // the staging stores stay after this tile's math
-        store(buf ^ 1);
-        __syncthreads();
+        // every wave has issued its value products, so its reads of the V tile returned; no
+        // wait on this thread's outstanding copies
+        asm volatile("s_barrier" ::: "memory");
+        if (tix + 1 < ntile) issue_v(tix + 1);
     }
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
@@ -445,9 +472,9 @@ bool launch_moba_attn(int DK, int DV, const MobaParams& p, hipStream_t st) {
     launch_block_lists(p, st);
     int nwg = p.n_own + moba_max_tiles(p.B * p.Hkv, p.T, p.top_n, p.n_slc);
     nwg = (nwg + 7) / 8 * 8;
-    if (DK == 128 && DV == 128) moba_attn_kernel<128, 128><<<nwg, 256, 0, st>>>(p);
-    else if (DK == 64 && DV == 64) moba_attn_kernel<64, 64><<<nwg, 256, 0, st>>>(p);
-    else if (DK == 192 && DV == 128) moba_attn_kernel<192, 128><<<nwg, 256, 0, st>>>(p);
+    if (DK == 128 && DV == 128) moba_attn_kernel<128, 128><<<nwg, 256, moba_attn_lds(128, 128), st>>>(p);
+    else if (DK == 64 && DV == 64) moba_attn_kernel<64, 64><<<nwg, 256, moba_attn_lds(64, 64), st>>>(p);
+    else if (DK == 192 && DV == 128) moba_attn_kernel<192, 128><<<nwg, 256, moba_attn_lds(192, 128), st>>>(p);
     else return false;
     if (DV == 128) moba_merge<128>(p, st);
     else moba_merge<64>(p, st);

@@ -246,8 +246,9 @@ __global__ __launch_bounds__(256, 2) void mean_scores_kernel(SelParams p) {
 // own block forced, two picks).  A workgroup owns 64 tokens (a wave's 16 MFMA columns are
 // 16 tokens); each lane keeps, for its column, the best K candidates (K = the picks rounded
 // up to 1, 2 or 4) among the keys it holds as 64-bit entries score-key:~index (larger =
-// better score, then lower index), so no score row is ever stored.  A tile is skipped when
-// no lane of the wave has a candidate above its current K-th best.  The four lanes of a
+// better score, then lower index), so no score row is ever stored.  A candidate's insertion
+// is skipped (wave-uniformly) when its score is below every lane's current K-th best.  The
+// four lanes of a
 // column merge their lists (bitonic top-K of two sorted lists, then a sort) across the 16-
 // and 32-lane swaps.
 template <int DK, int K>
@@ -293,8 +294,9 @@ __global__ __launch_bounds__(256, 2) void mean_select_kernel(SelParams p) {
         for (int ds = 0; ds < NDS; ++ds)
 #pragma unroll
             for (int kt = 0; kt < 4; ++kt) s[kt] = mfma16(ld8(&ks[(16 * kt + li) * KSTR + 32 * ds + lq * 8]), qf[ds], s[kt]);
-        uint64_t c[16];
-        bool improves = false;
+        // A candidate whose 32-bit score key is below the key of the lane's K-th entry cannot
+        // enter the list; the 64-bit insertion (score key : inverted index, so equal scores
+        // order by the lower index) runs only for candidates that some lane cannot rule out.
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
@@ -302,22 +304,18 @@ __global__ __launch_bounds__(256, 2) void mean_select_kernel(SelParams p) {
                 const int j = k0 + 16 * kt + 4 * lq + r;
                 // candidates are complete earlier blocks: the own block is forced (n_local >= 1)
                 const bool ok = live && fb.candidate(j);
-                const uint64_t e = ok ? (((uint64_t)f2key(s[kt][r]) << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)j)) : 0ull;
-                c[4 * kt + r] = e;
-                improves |= e > best[K - 1];
-            }
-        if (__any(improves)) {
+                const uint32_t key = f2key(s[kt][r]);
+                const bool pass = ok && key >= (uint32_t)(best[K - 1] >> 32);
+                if (__any(pass)) {   // wave-uniform
+                    uint64_t e = pass ? (((uint64_t)key << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)j)) : 0ull;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                uint64_t e = c[i];
-#pragma unroll
-                for (int q = 0; q < K; ++q) {   // insert into the descending list
-                    const uint64_t hi = e > best[q] ? e : best[q];
-                    e = e > best[q] ? best[q] : e;
-                    best[q] = hi;
+                    for (int q = 0; q < K; ++q) {   // insert into the descending list
+                        const uint64_t hi = e > best[q] ? e : best[q];
+                        e = e > best[q] ? best[q] : e;
+                        best[q] = hi;
+                    }
                 }
             }
-        }
     }
     // merge the column's four lists: lanes l and l ^ 16, then l and l ^ 32
 #pragma unroll
