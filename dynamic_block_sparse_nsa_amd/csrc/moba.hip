@@ -432,12 +432,77 @@ __global__ __launch_bounds__(256) void moba_merge_kernel(MobaParams p) {
     }
 }
 
+// The same merge for exactly S <= 4 slots and fewer than 2^32 rows (the MoBA workloads):
+// the slot count is a compile-time constant (no per-slot branches), a lane owns 8
+// consecutive values of a row (16-byte partial loads and output stores), row indices are
+// 32-bit, and the (sequence, head) of a row comes from two divisions by constants the host
+// passes (th = T * Hkv, hkv).  Rows past the end are clamped for the loads and not stored.
+template <int DV, int S, int R>
+__global__ __launch_bounds__(256) void moba_merge_small_kernel(MobaParams p, uint32_t nrows, uint32_t th, uint32_t hkv) {
+    constexpr int LPR = DV / 8;      // lanes per row
+    constexpr int RPB = 256 / LPR;   // rows per workgroup and step
+    const uint32_t li = threadIdx.x % LPR;
+    uint32_t row[R];
+    int js[R][S];
+    float ms[R][S], ls[R][S];
+    f16x8 hv[R][S];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        row[r] = ((uint32_t)blockIdx.x * R + r) * RPB + threadIdx.x / LPR;   // (b, t, h)
+        const uint32_t rr = min(row[r], nrows - 1);
+#pragma unroll
+        for (int s = 0; s < S; ++s) {
+            js[r][s] = p.sel[rr * S + s];
+            ms[r][s] = p.part_m[rr * S + s];
+            ls[r][s] = p.part_l[rr * S + s];
+            hv[r][s] = ld_stream(reinterpret_cast<const f16x8*>(p.part_o + (size_t)(rr * S + s) * DV) + li);
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        float M = -INFINITY;
+        bool ok[S];
+#pragma unroll
+        for (int s = 0; s < S; ++s) {
+            ok[s] = js[r][s] >= 0 && js[r][s] < p.n_slc && ms[r][s] > -INFINITY;
+            M = ok[s] ? fmaxf(M, ms[r][s]) : M;
+        }
+        float L = 0.f, acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < S; ++s) {
+            const float w = ok[s] ? fast_exp2(ms[r][s] - M) * ls[r][s] : 0.f;   // the slot's weight
+            L += w;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) acc[k] = __builtin_fmaf(w, ok[s] ? (float)hv[r][s][k] : 0.f, acc[k]);
+        }
+        const uint32_t rr = min(row[r], nrows - 1);
+        const float g = p.gates ? sigmoidf_(p.gates[(size_t)rr * 3 + 1]) : 1.f;
+        const uint32_t bh = rr / th * hkv + rr % hkv;
+        const float inv = L > 0.f ? ldexpf(g / L, p.vexp[bh]) : 0.f;   // V's scaling undone
+        u32x4 v;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) v[k] = (uint32_t)f2bf(acc[2 * k] * inv) | ((uint32_t)f2bf(acc[2 * k + 1] * inv) << 16);
+        if (row[r] < nrows) st_stream(v, reinterpret_cast<u32x4*>(p.O + (size_t)row[r] * DV) + li);
+    }
+}
+
 namespace {
 template <int DV>
 void moba_merge(const MobaParams& p, hipStream_t st) {
     constexpr int RPB = 256 / (DV / 4);
     const size_t rows = (size_t)p.B * p.T * p.Hkv;
-    if (p.top_n <= 4) {
+    if (p.top_n <= 4 && rows * (size_t)p.top_n < (1ull << 32)) {
+        constexpr int R = 4;
+        constexpr int RPBS = 256 / (DV / 8);
+        const unsigned grid = (unsigned)((rows + RPBS * R - 1) / (RPBS * R));
+        const uint32_t n = (uint32_t)rows, th = (uint32_t)p.T * (uint32_t)p.Hkv, hkv = (uint32_t)p.Hkv;
+        switch (p.top_n) {
+            case 1: moba_merge_small_kernel<DV, 1, R><<<grid, 256, 0, st>>>(p, n, th, hkv); break;
+            case 2: moba_merge_small_kernel<DV, 2, R><<<grid, 256, 0, st>>>(p, n, th, hkv); break;
+            case 3: moba_merge_small_kernel<DV, 3, R><<<grid, 256, 0, st>>>(p, n, th, hkv); break;
+            default: moba_merge_small_kernel<DV, 4, R><<<grid, 256, 0, st>>>(p, n, th, hkv); break;
+        }
+    } else if (p.top_n <= 4) {
         constexpr int R = 4;
         moba_merge_kernel<DV, 4, R><<<(unsigned)((rows + RPB * R - 1) / (RPB * R)), 256, 0, st>>>(p);
     } else if (p.top_n <= 8) {
