@@ -263,9 +263,15 @@ __global__ __launch_bounds__(256, DK >= 192 ? 2 : 3) void moba_attn_kernel(MobaP
         issue_k(0, kslot);
         issue_v(0);
     }
+    // copies per wave of a K tile and of a V tile; a wave's copies land in issue order, so
+    // a wait for "at most n outstanding" covers every copy but the last n
+    constexpr int NKW = KE / 512 / 4, NVW = VE / 512 / 4;
+    static_assert(KE % 2048 == 0 && VE % 2048 == 0, "the waves split a tile's copies evenly");
     for (int tix = 0; tix < ntile; ++tix) {
-        // this thread's copies of tile tix have landed, then everyone's have
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        // K(tix) has landed (this thread's copies, then everyone's); V(tix), issued after it,
+        // may still be in flight (the first tile also waits for the query loads)
+        if (tix == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NVW) : "memory");
         __syncthreads();
         if (tix + 1 < ntile) issue_k(tix + 1, kslot + ((tix + 1) & 1) * KE);
         const u16* kb = kslot + (tix & 1) * KE;
@@ -292,21 +298,23 @@ __global__ __launch_bounds__(256, DK >= 192 ? 2 : 3) void moba_attn_kernel(MobaP
                     for (int r = 0; r < 4; ++r)
                         if (key0 + 16 * kt + 4 * lq + r > hi[c]) s[kt][c][r] = -INFINITY;
         }
+        // a column's reference moves only on its own tile maximum, so its result does not
+        // depend on which columns share its wave
         float mt[2];
-        bool grow = false;
+        bool grow[2];
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
             float tmax = fmaxf(s[0][c][0], s[0][c][1]);
 #pragma unroll
             for (int e = 2; e < 16; ++e) tmax = fmaxf(tmax, s[e >> 2][c][e & 3]);
             mt[c] = col_max(tmax) * p.scale_log2;
-            grow |= mt[c] > m[c] + kMobaLazy;
+            grow[c] = mt[c] > m[c] + kMobaLazy;
         }
-        if (__any(grow)) {   // move the references (wave-uniform branch)
+        if (__any(grow[0] || grow[1])) {   // rescale (wave-uniform branch; factor 1 elsewhere)
 #pragma unroll
             for (int c = 0; c < 2; ++c) {
-                const float mnew = fmaxf(m[c], mt[c]);
-                const float alpha = m[c] == -INFINITY ? 0.f : fast_exp2(m[c] - mnew);
+                const float mnew = grow[c] ? mt[c] : m[c];
+                const float alpha = !grow[c] ? 1.f : m[c] == -INFINITY ? 0.f : fast_exp2(m[c] - mnew);
                 l[c] *= alpha;
 #pragma unroll
                 for (int dt = 0; dt < NDT; ++dt) o[c][dt] *= alpha;
@@ -327,6 +335,10 @@ __global__ __launch_bounds__(256, DK >= 192 ? 2 : 3) void moba_attn_kernel(MobaP
                 }
             l[c] += acc;
         }
+        // V(tix) has landed; K(tix + 1), issued after it, may still be in flight
+        if (tix + 1 < ntile) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NKW) : "memory");
+        else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
 #pragma unroll
         for (int u = 0; u < 2; ++u) {   // P in fp16 against the scaled fp16 V copy: one product
             f16x8 ph[2];
@@ -339,9 +351,8 @@ __global__ __launch_bounds__(256, DK >= 192 ? 2 : 3) void moba_attn_kernel(MobaP
                 for (int c = 0; c < 2; ++c) o[c][dt] = mfma16h(a, ph[c], o[c][dt]);
             }
         }
-        // every wave has issued its value products, so its reads of the V tile returned; no
-        // wait on this thread's outstanding copies
-        asm volatile("s_barrier" ::: "memory");
+        // every wave's reads of the V tile have returned; no wait on outstanding copies
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
         if (tix + 1 < ntile) issue_v(tix + 1);
     }
 #pragma unroll

@@ -445,10 +445,16 @@ def test_moba(T, top_n):
     lists = inputs.block_lists(cfg, seed=500, positions=None) if T <= 8192 else None
     if lists is None:
         lists = inputs.block_lists(cfg.replace(seq_len=T), seed=500)
-    out = ops.sparse_attn_fwd(cfg, dev_bf16(inp["q"]), dev_bf16(inp["k"]), dev_bf16(inp["v"]), dev_i32(lists))
+    args = (dev_bf16(inp["q"]), dev_bf16(inp["k"]), dev_bf16(inp["v"]), dev_i32(lists))
+    out = ops.sparse_attn_fwd(cfg, *args)
     torch.cuda.synchronize()
     at = oracle.attend(cfg, f64(inp["q"][0, rows]), rows, f64(inp["k"][0]), f64(inp["v"][0]), lists[0, rows])
     check_close(bf16_dev_to_f64(out)[0, rows], at["out"], f"moba{T} output")
+    # the block lists are filled with atomics, so a second run groups the queries of a block
+    # into work items differently; each (query, slot) result must not depend on its companions
+    out2 = ops.sparse_attn_fwd(cfg, *args)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2), f"moba{T}: the output differs between two runs"
 
 
 def test_block_major_large_values():
