@@ -106,7 +106,8 @@ SelectWs select_ws(const Shape& s) {
         w.vexp = off; off = align_up(off + bg * 4, 256);
     }
     w.scores = off;
-    if (!fused_mean_select(s)) off = align_up(off + (size_t)s.B * s.T * s.Hkv * s.n_slc * 4, 256);
+    // (with no complete compressed block the selection runs on a zero score row)
+    if (!fused_mean_select(s) || s.n_cmp == 0) off = align_up(off + (size_t)s.B * s.T * s.Hkv * s.n_slc * 4, 256);
     w.total = off;
     return w;
 }
@@ -293,8 +294,8 @@ nsa_status nsa_compress(const nsa_config* cfg, const void* K, const void* V, con
     Shape s;
     nsa_status st = check_config(cfg, &s);
     if (st != NSA_OK) return st;
+    if (s.n_cmp == 0) return NSA_OK;   // shorter than one block: nothing to compress
     if (!K || !K_cmp) return fail(NSA_ERR_NULL, "K and K_cmp are required");
-    if (s.n_cmp == 0) return NSA_OK;
     const int BG = s.B * s.Hkv;
     const hipStream_t hs = as_stream(stream);
     using nsa::u16;
@@ -321,6 +322,20 @@ nsa_status nsa_compress(const nsa_config* cfg, const void* K, const void* V, con
     return hip_check("compress_linear");
 }
 
+namespace {
+// Steps a2-a4 when the sequence is shorter than one compressed block (no compressed key is
+// visible to any query): o_cmp = 0, LSE = -inf, every block score 0, so the selection keeps
+// the forced blocks and fills any other slot by the lowest eligible index.
+nsa_status no_block_select(const Shape& s, float* scores, int32_t* sel_idx, float* lse_cmp, float* o_cmp,
+                           hipStream_t hs) {
+    nsa::launch_fill_f32(scores, (size_t)s.B * s.T * s.Hkv * s.n_slc, 0.f, hs);
+    if (lse_cmp) nsa::launch_fill_f32(lse_cmp, (size_t)s.B * s.T * s.H, -INFINITY, hs);
+    if (o_cmp) nsa::launch_fill_f32(o_cmp, (size_t)s.B * s.T * s.H * s.dv, 0.f, hs);
+    nsa::launch_select_from_scores(scores, sel_idx, s.B, s.T, s.Hkv, s.n_slc, s.lp, s.n, s.n_init, s.n_local, hs);
+    return hip_check("score_select");
+}
+}  // namespace
+
 nsa_status nsa_score_select(const nsa_config* cfg, const void* Q, const void* K_cmp, const void* V_cmp,
                             int32_t* sel_idx, float* lse_cmp, float* o_cmp, void* ws, size_t ws_bytes,
                             void* stream) {
@@ -328,13 +343,12 @@ nsa_status nsa_score_select(const nsa_config* cfg, const void* Q, const void* K_
     Shape s;
     nsa_status st = check_config(cfg, &s);
     if (st != NSA_OK) return st;
-    if (!Q || !sel_idx || !K_cmp) return fail(NSA_ERR_NULL, "Q, K_cmp and sel_idx are required");
-    if (s.n_cmp == 0) return fail(NSA_ERR_UNSUPPORTED, "seq_len shorter than cmp_block");
+    if (!Q || !sel_idx || (!K_cmp && s.n_cmp > 0)) return fail(NSA_ERR_NULL, "Q, K_cmp and sel_idx are required");
     if (s.n_slc > 64 * 32) return fail(NSA_ERR_UNSUPPORTED, "at most 2048 selection blocks");
     if (s.mode == NSA_SCORE_MEAN_DOT && (lse_cmp || o_cmp))
         return fail(NSA_ERR_SHAPE, "MEAN_DOT mode produces no lse_cmp / o_cmp");
     const bool with_o = o_cmp != nullptr;
-    if (with_o && !V_cmp) return fail(NSA_ERR_NULL, "o_cmp needs V_cmp");
+    if (with_o && !V_cmp && s.n_cmp > 0) return fail(NSA_ERR_NULL, "o_cmp needs V_cmp");
     if (s.mode == NSA_SCORE_CMP_OVERLAP && nsa::cmp_attn_lds_bytes(s.dk, s.dv, s.G, with_o) > 160 * 1024)
         return fail(NSA_ERR_UNSUPPORTED, "tile too large for one workgroup's LDS");
     if (s.mode == NSA_SCORE_CMP_OVERLAP) {
@@ -345,6 +359,7 @@ nsa_status nsa_score_select(const nsa_config* cfg, const void* Q, const void* K_
     const SelectWs w = select_ws(s);
     if ((st = check_ws(ws, ws_bytes, w.total)) != NSA_OK) return st;
     const hipStream_t hs = as_stream(stream);
+    if (s.n_cmp == 0) return no_block_select(s, at<float>(ws, w.scores), sel_idx, lse_cmp, o_cmp, hs);
     using nsa::u16;
     nsa::SelParams p{};
     p.Q = static_cast<const u16*>(Q);
@@ -488,10 +503,10 @@ nsa_status nsa_prefill_fwd(const nsa_config* cfg, const void* Q, const void* K, 
     Shape s;
     nsa_status st = check_config(cfg, &s);
     if (st != NSA_OK) return st;
-    if (!Q || !K || !V || !K_cmp || !V_cmp || !O) return fail(NSA_ERR_NULL, "Q, K, V, K_cmp, V_cmp and O are required");
+    if (!Q || !K || !V || !O || ((!K_cmp || !V_cmp) && s.n_cmp > 0))
+        return fail(NSA_ERR_NULL, "Q, K, V, K_cmp, V_cmp and O are required");
     if (s.mode != NSA_SCORE_CMP_OVERLAP)
         return fail(NSA_ERR_UNSUPPORTED, "the fused prefill scores blocks by compressed attention (CMP_OVERLAP)");
-    if (s.n_cmp == 0) return fail(NSA_ERR_UNSUPPORTED, "seq_len shorter than cmp_block");
     if (s.n_slc > 64 * 32) return fail(NSA_ERR_UNSUPPORTED, "at most 2048 selection blocks");
     {
         const int R = s.lp / s.s, L = s.l / s.s;
@@ -510,24 +525,28 @@ nsa_status nsa_prefill_fwd(const nsa_config* cfg, const void* Q, const void* K, 
     float* oc = o_cmp ? o_cmp : at<float>(ws, w.ocmp_out);
     // compressed keys/values in fragment order (V as scaled fp16)
     nsa::SelParams sp{};
-    sp.Q = static_cast<const u16*>(Q);
-    sp.Kc = static_cast<const u16*>(K_cmp);
-    sp.scores = at<float>(ws, w.sel.scores);
-    sp.sel = sel;
-    sp.top_n = s.n; sp.n_init = s.n_init; sp.n_local = s.n_local;
-    sp.B = s.B; sp.T = s.T; sp.Hkv = s.Hkv; sp.N = s.n_cmp; sp.Npad = w.sel.npad; sp.l = s.l; sp.s = s.s; sp.lp = s.lp;
-    sp.n_slc = s.n_slc;
-    sp.scale_log2 = s.scale * nsa::kLog2eHost;
-    u16* ckf = at<u16>(ws, w.sel.kf);
-    u16* cvf = at<u16>(ws, w.sel.vf);
-    if (!nsa::launch_tile_cmp(s.dk, s.dv, sp.Kc, static_cast<const u16*>(V_cmp), at<uint32_t>(ws, w.sel.vmax),
-                              at<int>(ws, w.sel.vexp), ckf, cvf, s.B * s.Hkv, s.n_cmp, w.sel.npad, hs))
-        return fail(NSA_ERR_UNSUPPORTED, "no layout kernel for this shape");
-    sp.Kf = ckf;
-    sp.Vf = cvf;
-    sp.vexp = at<int>(ws, w.sel.vexp);
-    sp.lse = lse_cmp;
-    sp.o_cmp = oc;
+    if (s.n_cmp == 0) {   // no complete compressed block: steps a2-a4 without the scoring kernel
+        if ((st = no_block_select(s, at<float>(ws, w.sel.scores), sel, lse_cmp, oc, hs)) != NSA_OK) return st;
+    } else {
+        sp.Q = static_cast<const u16*>(Q);
+        sp.Kc = static_cast<const u16*>(K_cmp);
+        sp.scores = at<float>(ws, w.sel.scores);
+        sp.sel = sel;
+        sp.top_n = s.n; sp.n_init = s.n_init; sp.n_local = s.n_local;
+        sp.B = s.B; sp.T = s.T; sp.Hkv = s.Hkv; sp.N = s.n_cmp; sp.Npad = w.sel.npad; sp.l = s.l; sp.s = s.s; sp.lp = s.lp;
+        sp.n_slc = s.n_slc;
+        sp.scale_log2 = s.scale * nsa::kLog2eHost;
+        u16* ckf = at<u16>(ws, w.sel.kf);
+        u16* cvf = at<u16>(ws, w.sel.vf);
+        if (!nsa::launch_tile_cmp(s.dk, s.dv, sp.Kc, static_cast<const u16*>(V_cmp), at<uint32_t>(ws, w.sel.vmax),
+                                  at<int>(ws, w.sel.vexp), ckf, cvf, s.B * s.Hkv, s.n_cmp, w.sel.npad, hs))
+            return fail(NSA_ERR_UNSUPPORTED, "no layout kernel for this shape");
+        sp.Kf = ckf;
+        sp.Vf = cvf;
+        sp.vexp = at<int>(ws, w.sel.vexp);
+        sp.lse = lse_cmp;
+        sp.o_cmp = oc;
+    }
     // K and V in fragment order (V as scaled fp16)
     void* aws = at<void>(ws, w.attn_off);
     u16* kf = at<u16>(aws, w.attn.kf);
@@ -548,8 +567,11 @@ nsa_status nsa_prefill_fwd(const nsa_config* cfg, const void* Q, const void* K, 
     ap.B = s.B; ap.T = s.T; ap.Tpad = w.attn.tpad; ap.Hkv = s.Hkv; ap.G = s.G; ap.lp = s.lp; ap.top_n = s.n;
     ap.window = s.w; ap.branches = s.br;
     ap.scale_log2 = s.scale * nsa::kLog2eHost;
-    if (!nsa::launch_prefill_fused(s.dk, s.dv, s.G, sp, ap, hs))
+    if (s.n_cmp == 0) {   // the lists are ready: steps a5-a7 alone
+        if (!nsa::launch_sparse_attn(s.dk, s.dv, ap, s.B, hs)) return fail(NSA_ERR_UNSUPPORTED, "no attention kernel");
+    } else if (!nsa::launch_prefill_fused(s.dk, s.dv, s.G, sp, ap, hs)) {
         return fail(NSA_ERR_UNSUPPORTED, "no fused prefill kernel for this shape");
+    }
     return hip_check("prefill_fwd");
 }
 

@@ -63,6 +63,12 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(float* __restrict__ x, s
     for (size_t i = n4 * 4 + (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += stride) x[i] = 0.f;
 }
 
+// x[0 .. n) = v (no alignment assumed)
+__global__ __launch_bounds__(256) void fill_f32_kernel(float* __restrict__ x, size_t n, float v) {
+    const size_t stride = (size_t)gridDim.x * 256;
+    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += stride) x[i] = v;
+}
+
 // ---------------------------------------------------------------------------
 // dQ.  A workgroup owns kDqTok consecutive tokens of one (sequence, group), a wave per token.
 // bwd_dq_kernel: the compressed keys and the window range are shared by the tokens: their
@@ -740,6 +746,12 @@ void launch_fill_zero(float* x, size_t n, hipStream_t st) {
     if (n == 0) return;
     const size_t blocks = std::min<size_t>((n / 4 + 255) / 256 + 1, 8192);
     fill_zero_kernel<<<(unsigned)blocks, 256, 0, st>>>(x, n);
+}
+
+void launch_fill_f32(float* x, size_t n, float v, hipStream_t st) {
+    if (n == 0) return;
+    const size_t blocks = std::min<size_t>((n + 255) / 256, 8192);
+    fill_f32_kernel<<<(unsigned)blocks, 256, 0, st>>>(x, n, v);
 }
 
 bool launch_bwd_dq(int DK, int DV, const BwdParams& p, hipStream_t st) {

@@ -150,7 +150,8 @@ struct BwdParams {
     int n_cmp_items, n_win_items;
     float scale, scale_log2;
 };
-void launch_fill_zero(float* x, size_t n, hipStream_t st);
+void launch_fill_zero(float* x, size_t n, hipStream_t st);   // x 16-byte aligned
+void launch_fill_f32(float* x, size_t n, float v, hipStream_t st);
 bool launch_bwd_dq(int DK, int DV, const BwdParams& p, hipStream_t st);
 bool launch_bwd_dkv(int DK, int DV, const BwdParams& p, int n_slc_items, hipStream_t st);
 // linear block map backward for one of K / V: dX += dY.W^T scattered to tokens, dW and dpe

@@ -112,7 +112,8 @@ nsa_status nsa_workspace_size(const nsa_config* cfg, int op, size_t* bytes);
  *                   and the same for V with W_v [l*d_v, d_v] and pe_v [l, d_v].
  *                   W_k [l*d_k, d_k] and pe_k [l, d_k] are bf16 and shared by all KV heads.
  *   NSA_PHI_MEAN:   K_cmp[b,g,i,:] = (1/l) * sum_{r<l} K[b,g,i*s+r,:]; V, W_*, pe_*, V_cmp unused.
- * Accumulates in fp32 and rounds once to bf16.  Works for the decode caches too (T = L). */
+ * Accumulates in fp32 and rounds once to bf16.  Works for the decode caches too (T = L).
+ * With T < l there is no block: nothing is written and every pointer may be NULL. */
 nsa_status nsa_compress(const nsa_config* cfg, const void* K, const void* V,
                         const void* W_k, const void* W_v, const void* pe_k, const void* pe_v,
                         void* K_cmp, void* V_cmp, void* ws, size_t ws_bytes, void* stream);
@@ -129,7 +130,10 @@ nsa_status nsa_compress(const nsa_config* cfg, const void* K, const void* V,
  *   jc-n_local+1..jc (within 0..jc); the other blocks 0..jc are taken by descending score,
  *   ties to the lower index, until min(top_n, jc+1) blocks are chosen.
  * Outputs: sel_idx (required); lse_cmp and o_cmp optional (NULL = not produced; o_cmp
- *   needs V_cmp; both must be NULL in MEAN_DOT mode).  Scores are fp32. */
+ *   needs V_cmp; both must be NULL in MEAN_DOT mode).  Scores are fp32.
+ * With T < l no compressed block exists (K_cmp / V_cmp may be NULL): o_cmp = 0, lse_cmp =
+ *   -inf, every score 0, so the rows hold the forced blocks and, in any other slot, the
+ *   lowest eligible indices. */
 nsa_status nsa_score_select(const nsa_config* cfg, const void* Q, const void* K_cmp,
                             const void* V_cmp, int32_t* sel_idx, float* lse_cmp, float* o_cmp,
                             void* ws, size_t ws_bytes, void* stream);
@@ -166,8 +170,9 @@ nsa_status nsa_sparse_attn_fwd(const nsa_config* cfg, const void* Q, const void*
  *   and o_cmp [B,T,H,d_v] fp32 are optional (NULL = kept in the workspace / not written).
  *   Workspace: nsa_workspace_size(cfg, NSA_OP_PREFILL).
  * Needs the compressed-overlap scores (NSA_SCORE_CMP_OVERLAP); every branch mask is allowed
- * (the compressed branch's output is formed in any case: the scores need it).  Errors as
- * for the two calls; NSA_ERR_UNSUPPORTED for the MEAN_DOT scores. */
+ * (the compressed branch's output is formed in any case: the scores need it).  With T < l
+ * (no compressed block; K_cmp / V_cmp may be NULL) the call runs the two calls' no-block
+ * path.  Errors as for the two calls; NSA_ERR_UNSUPPORTED for the MEAN_DOT scores. */
 nsa_status nsa_prefill_fwd(const nsa_config* cfg, const void* Q, const void* K, const void* V, const void* K_cmp,
                            const void* V_cmp, const float* gate_logits, void* O, int32_t* sel_idx, float* lse_cmp,
                            float* o_cmp, void* ws, size_t ws_bytes, void* stream);

@@ -224,8 +224,14 @@ def test_mode_specific_rules():
     assert "cmp_stride" in L.nsa_last_error_detail().decode()
     # window branch needs a window
     assert L.nsa_sparse_attn_fwd(_cfg(P8K, window=0), fake, fake, fake, fake, fake, None, fake, None, 0, None) == 2
-    # shorter than one compressed block
-    assert L.nsa_score_select(_cfg(P8K, seq_len=16), fake, fake, fake, fake, None, None, fake, 1 << 40, None) == 3
+    # shorter than one compressed block: supported (no compressed key; the compressed tensors
+    # may be NULL), still validated before any launch
+    short = _cfg(P8K, seq_len=16)
+    assert L.nsa_score_select(short, fake, None, None, None, None, None, fake, 1 << 40, None) == 1
+    assert L.nsa_score_select(short, fake, None, None, fake, None, None, fake, 0, None) == 4
+    n = ctypes.c_size_t(0)
+    assert L.nsa_workspace_size(short, ops.OP_SCORE_SELECT, ctypes.byref(n)) == 0
+    assert n.value >= 16 * 4 * 1 * 4   # the zero score rows [B, T, H_kv, N_slc]
 
 
 def test_cache_maintenance_validation():

@@ -298,6 +298,32 @@ def _prefill_end_to_end(cfg):
             print(f"[diag] {cfg.name} b={b} selection agreement with the pure-fp64 chain: {agree:.5f}", flush=True)
 
 
+@pytest.mark.parametrize("T", [1, 20, 31])
+def test_prefill_shorter_than_one_compressed_block(T):
+    """Sequences with no complete compressed block (T < l = 32): o_cmp = 0 and LSE = -inf on
+    every row, the selection holds the forced blocks only, and the selected and window
+    branches and the gated sum are as usual; the fused call equals the three calls."""
+    cfg = TINY.replace(name=f"short{T}", seq_len=T, seed=60 + T)
+    announce(f"prefill T={T} < cmp_block")
+    inp = inputs.prefill_inputs(cfg)
+    args = [dev_bf16(inp[n]) for n in ("q", "k", "v", "w_k", "w_v", "pe_k", "pe_v")] + [dev_f32(inp["gates"])]
+    r = ops.prefill(cfg, *args)
+    rf = ops.prefill(cfg, *args, fused=True)
+    torch.cuda.synchronize()
+    for key in ("out", "sel", "lse", "o_cmp"):
+        assert torch.equal(r[key], rf[key]), f"T={T}: fused prefill differs from the three calls in {key}"
+    rows = np.arange(T, dtype=np.int32)
+    Kc, Vc = pipeline.compress_all(cfg, f64(inp["k"][0]), f64(inp["v"][0]), f64(inp["w_k"]), f64(inp["w_v"]),
+                                   f64(inp["pe_k"]), f64(inp["pe_v"]))
+    assert Kc.shape[1] == 0
+    ref = pipeline.forward_rows(cfg, f64(inp["q"][0]), f64(inp["k"][0]), f64(inp["v"][0]), Kc, Vc, inp["gates"][0],
+                                rows)
+    np.testing.assert_array_equal(r["sel"][0].cpu().numpy(), ref["sel"])
+    assert np.isneginf(r["lse"].cpu().numpy()).all()
+    assert not r["o_cmp"].any().item()
+    check_close(bf16_dev_to_f64(r["out"])[0], ref["out"], f"T={T} output")
+
+
 # Other shapes the kernels support: group sizes 1, 2, 8; head dims 128/128 and 64/64;
 # other block geometries, top-n and windows; a batch of two; every row checked.
 SHAPES = [
