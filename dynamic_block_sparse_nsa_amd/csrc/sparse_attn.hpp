@@ -215,17 +215,20 @@ __device__ __forceinline__ void sparse_attn_tokens(const AttnParams& p, int unit
     const bool head_ok = li < G;
     const int h = g * G + min(li, G - 1);
 
+    const bool use_slc = (p.branches & 2) != 0, use_win = (p.branches & 4) != 0;
+    // the query rows (not read when only the compressed branch is on: then the call is the
+    // gated sum of the caller's o_cmp alone)
+    const bool need_q = head_ok && (use_slc || use_win);
     bf16x8 qf[NDS];
     {
         const u16* qp = p.Q + (((size_t)b * T + tq) * H + h) * DK;
 #pragma unroll
         for (int ds = 0; ds < NDS; ++ds)
-            qf[ds] = head_ok ? __builtin_bit_cast(bf16x8, ld_stream(reinterpret_cast<const u32x4*>(qp + 32 * ds + 8 * lq)))
-                             : zero8();
+            qf[ds] = need_q ? __builtin_bit_cast(bf16x8, ld_stream(reinterpret_cast<const u32x4*>(qp + 32 * ds + 8 * lq)))
+                            : zero8();
     }
     const u16* kg = p.Kf + ((size_t)b * p.Hkv + g) * (size_t)p.Tpad * DK;
     const u16* vg = p.Vf + ((size_t)b * p.Hkv + g) * (size_t)p.Tpad * DV;
-    const bool use_slc = (p.branches & 2) != 0, use_win = (p.branches & 4) != 0;
     // the token's block list, one entry per lane, read back with readlane (no memory
     // access on the dependency chain of a gather's address)
     const int sel_lane = (use_slc && lane < p.top_n)
@@ -276,6 +279,16 @@ __device__ __forceinline__ void sparse_attn_tokens(const AttnParams& p, int unit
                 slc.update(s0, s1, kB, c + 1 < nck ? kB : INT_MAX, t, p.scale_log2, B.va);
             }
         }
+    }
+
+    // The forward's o_cmp rows are requested here, so they arrive during phase A instead of
+    // after it (the gather registers of phase B are free by now).
+    f32x4 ocv[NDT];
+    if constexpr (!STATS) {
+        const bool want = active && head_ok && (p.branches & 1);
+        const f32x4* op = reinterpret_cast<const f32x4*>(p.o_cmp + (((size_t)b * T + tq) * H + h) * DV + 4 * lq);
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) ocv[dt] = want ? ld_stream(op + 4 * dt) : zero4();
     }
 
     // ---- phase A: the window range of the workgroup's tokens, shared through LDS ----
@@ -393,8 +406,7 @@ __device__ __forceinline__ void sparse_attn_tokens(const AttnParams& p, int unit
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
         const int d0 = 16 * dt + 4 * lq;
-        f32x4 oc = zero4();
-        if (p.branches & 1) oc = ld_stream(reinterpret_cast<const f32x4*>(p.o_cmp + row * DV + d0));
+        const f32x4 oc = ocv[dt];
         const float vc[4] = {oc[0], oc[1], oc[2], oc[3]};
         float v[4];
 #pragma unroll

@@ -12,8 +12,8 @@ import torch
 import oracle
 from oracle import pipeline
 from dynamic_block_sparse_nsa_amd import inputs, ops
-from dynamic_block_sparse_nsa_amd.configs import (TINY, P8K, P64K, DECODE, MOBA, BR_SLC, BR_WIN, PHI_LINEAR, PHI_MEAN,
-                                                  SCORE_CMP_OVERLAP)
+from dynamic_block_sparse_nsa_amd.configs import (TINY, P8K, P64K, DECODE, MOBA, BR_CMP, BR_SLC, BR_WIN, PHI_LINEAR,
+                                                  PHI_MEAN, SCORE_CMP_OVERLAP)
 from nsa_testlib import (GAP, bf16_dev_to_f64, bf16_ulp, check_close, check_selection, check_ulp, dev_bf16, dev_f32,
                          dev_i32, f64_to_dev_bf16, sample_rows)
 
@@ -189,7 +189,7 @@ def test_sparse_attn_64k_sampled():
     _attn_case(P64K, sample_rows(P64K.seq_len, 40, 4))
 
 
-@pytest.mark.parametrize("branches", [BR_SLC, BR_WIN], ids=["slc", "win"])
+@pytest.mark.parametrize("branches", [BR_SLC, BR_WIN, BR_CMP], ids=["slc", "win", "cmp"])
 def test_sparse_attn_single_branch(branches):
     announce(f"sparse_attn single branch {branches}")
     _attn_case(TINY, np.arange(TINY.seq_len, dtype=np.int32), branches=branches)
