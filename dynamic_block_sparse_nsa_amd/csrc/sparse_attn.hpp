@@ -292,48 +292,61 @@ __device__ __forceinline__ void sparse_attn_tokens(const AttnParams& p, int unit
     }
 
     // ---- phase A: the window range of the workgroup's tokens, shared through LDS ----
-    Tile tile;
-    if (nch > 0) {
-        tile.load(kg, vg, c_begin);
-        tile.store(kbuf[0], vbuf[0]);
-    }
-    __syncthreads();
+    // Tiles are loaded to registers two tiles ahead (two register stages used alternately),
+    // stored to the LDS buffer one tile ahead, and computed from LDS.  Tile indices past the
+    // range are clamped to the last tile (never computed), so no load is conditional.
     const int wlo_t = t - p.window + 1;
-    for (int i = 0; i < nch; ++i) {
+    auto tile_key = [&](int i) { return c_begin + sattn::kChunk * min(i, nch - 1); };
+    auto compute = [&](int i) {
+        if (!active) return;
         const int key0 = c_begin + sattn::kChunk * i;
         const int buf = i & 1;
-        // prefetch of the next tile (the last iteration reloads its own tile into the
-        // unused buffer, so no load is conditional)
-        tile.load(kg, vg, key0 + (i + 1 < nch ? sattn::kChunk : 0));
-        if (active) {
-            const bool w_any = key0 + sattn::kChunk - 1 >= wlo_t && key0 <= t;
-            const int jch = key0 / p.lp;
-            bool s_any = false;
-            if (use_slc && key0 <= t && jch * p.lp >= c_begin) {
-                for (int c = 0; c < p.top_n; ++c) {
-                    const int j = sl(c);
-                    if (j < 0 || j > jch) break;
-                    s_any |= (j == jch);
-                }
-            }
-            if (w_any || s_any) {
-                f32x4 s0 = zero4(), s1 = zero4();
-                const u16* kb = kbuf[buf] + lane * 8;
-#pragma unroll
-                for (int ds = 0; ds < NDS; ++ds) {
-                    s0 = mfma16(ld8(kb + ds * 512), qf[ds], s0);
-                    s1 = mfma16(ld8(kb + (NDS + ds) * 512), qf[ds], s1);
-                }
-                f16x8 va[NDT];
-#pragma unroll
-                for (int dt = 0; dt < NDT; ++dt) va[dt] = ld8h(vbuf[buf] + (dt * 64 + lane) * 8);
-                if (w_any) win.update(s0, s1, key0, wlo_t, t, p.scale_log2, va);
-                if (s_any) slc.update(s0, s1, key0, jch * p.lp, t, p.scale_log2, va);
+        const bool w_any = key0 + sattn::kChunk - 1 >= wlo_t && key0 <= t;
+        const int jch = key0 / p.lp;
+        bool s_any = false;
+        if (use_slc && key0 <= t && jch * p.lp >= c_begin) {
+            for (int c = 0; c < p.top_n; ++c) {
+                const int j = sl(c);
+                if (j < 0 || j > jch) break;
+                s_any |= (j == jch);
             }
         }
+        if (w_any || s_any) {
+            f32x4 s0 = zero4(), s1 = zero4();
+            const u16* kb = kbuf[buf] + lane * 8;
+#pragma unroll
+            for (int ds = 0; ds < NDS; ++ds) {
+                s0 = mfma16(ld8(kb + ds * 512), qf[ds], s0);
+                s1 = mfma16(ld8(kb + (NDS + ds) * 512), qf[ds], s1);
+            }
+            f16x8 va[NDT];
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt) va[dt] = ld8h(vbuf[buf] + (dt * 64 + lane) * 8);
+            if (w_any) win.update(s0, s1, key0, wlo_t, t, p.scale_log2, va);
+            if (s_any) slc.update(s0, s1, key0, jch * p.lp, t, p.scale_log2, va);
+        }
+    };
+    Tile ta, tb;   // register stages: after the prologue tb holds tile 1
+    if (nch > 0) {
+        ta.load(kg, vg, tile_key(0));
+        ta.store(kbuf[0], vbuf[0]);
+        tb.load(kg, vg, tile_key(1));
+    }
+    __syncthreads();
+    for (int i = 0; i < nch; i += 2) {
+        // tile i in LDS buffer 0, tile i + 1 in tb
+        ta.load(kg, vg, tile_key(i + 2));
+        compute(i);
         __builtin_amdgcn_sched_barrier(0);   // keep the staging stores after this tile's math
-        tile.store(kbuf[buf ^ 1], vbuf[buf ^ 1]);
+        tb.store(kbuf[1], vbuf[1]);
         __syncthreads();
+        if (i + 1 < nch) {   // tile i + 1 in LDS buffer 1, tile i + 2 in ta
+            tb.load(kg, vg, tile_key(i + 3));
+            compute(i + 1);
+            __builtin_amdgcn_sched_barrier(0);
+            ta.store(kbuf[0], vbuf[0]);
+            __syncthreads();
+        }
     }
 
     if (!active) return;
