@@ -6,8 +6,8 @@
 // A workgroup owns 4 consecutive tokens of one KV group, one token per wave.  The group's
 // G query heads form the 16-wide MFMA column tile (the pages' NSA kernel packs the
 // group's heads into the matrix dimension so every KV tile feeds all of them at once).
-// Every attention product is key-major: S^T = K . Q^T on the MFMA, online softmax with
-// the running max and sum in registers (base-2), then O^T += V^T . P^T.
+// Every attention product is key-major: S^T = K . Q^T on the MFMA, online softmax with a
+// lazily moved reference and the sum in registers (base-2), then O^T += V^T . P^T.
 //
 // K and V are first copied into MFMA fragment order (launch_tile_cmp, the layout pass of
 // the compressed branch): the operands a wave needs for 16 keys x 32 dims of K, or 32 keys
@@ -39,12 +39,13 @@ namespace sattn {
 
 constexpr int kTok = 4;      // tokens (= waves) per workgroup
 constexpr int kChunk = 32;   // keys per tile
+constexpr float kLazy = 8.f; // log2 headroom before a column's softmax reference moves
 
 template <int DV>
 struct SoftmaxState {
     static constexpr int NDT = DV / 16;
     f32x4 o[NDT];
-    float m, l;
+    float m, l;   // the column's softmax reference (log2 units) and its sum of 2^(x - m)
 
     __device__ __forceinline__ void reset() {
 #pragma unroll
@@ -79,26 +80,32 @@ struct SoftmaxState {
         float tmax = fmaxf(x[0], x[4]);
 #pragma unroll
         for (int r = 1; r < 4; ++r) tmax = fmaxf(tmax, fmaxf(x[r], x[4 + r]));
-        tmax = col_max(tmax);
-        const float mnew = fmaxf(m, tmax * scale_log2);
-        const float alpha = fast_exp2(m - mnew);
+        // m is a lazily moved reference, not the running max: a column's m moves (and its l
+        // and o are rescaled) only when the chunk's max exceeds it by more than 2^kLazy, so
+        // p = 2^(x - m) <= 2^kLazy (within fp16's range) and the rescale is rare after the
+        // first chunk.  The decision is per column, so a column's result does not depend on
+        // the other heads in the tile.
+        const float mt = col_max(tmax) * scale_log2;
+        const bool grow = mt > m + kLazy;
+        if (__ballot(grow)) {   // wave-uniform branch
+            const float alpha = !grow ? 1.f : m == -INFINITY ? 0.f : fast_exp2(m - mt);
+            m = grow ? mt : m;
+            l *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt) o[dt] *= alpha;
+        }
         f32x4 pa, pb;
         float ps = 0.f;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            pa[r] = fast_exp2(__builtin_fmaf(x[r], scale_log2, -mnew));
-            pb[r] = fast_exp2(__builtin_fmaf(x[4 + r], scale_log2, -mnew));
+            pa[r] = fast_exp2(__builtin_fmaf(x[r], scale_log2, -m));
+            pb[r] = fast_exp2(__builtin_fmaf(x[4 + r], scale_log2, -m));
             ps += pa[r] + pb[r];
         }
-        l = l * alpha + ps;
-        m = mnew;
+        l += ps;
         // P in fp16 against the fp16 V copy: one product per slice (2^-11 relative rounding
-        // of p); o is rescaled only when some column's running max moved
+        // of p)
         const f16x8 ph = pack_p_h(pa, pb);
-        if (__ballot(alpha != 1.f)) {
-#pragma unroll
-            for (int dt = 0; dt < NDT; ++dt) o[dt] *= alpha;
-        }
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) o[dt] = mfma16h(va[dt], ph, o[dt]);
     }
