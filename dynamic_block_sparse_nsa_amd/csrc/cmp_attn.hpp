@@ -8,7 +8,7 @@
 //
 // A workgroup owns 128 query rows = 128/G tokens of one KV group, each wave two 16-column
 // MFMA tiles laid out by QMap so a token's heads share lanes and tiles.
-//   sweep 1: S^T = K_cmp . Q^T over 64-key tiles, per-lane running max and sum, combined
+//   sweep 1: S^T = K_cmp . Q^T over 64-key tiles, a per-lane lazily moved reference and sum, combined
 //            into the log-sum-exp b (base 2) of every query row.
 //   sweep 2: the same S^T again; p = 2^(x - b) are the normalized probabilities (nothing is
 //            rescaled afterwards); o_cmp += V_cmp^T.P^T on the MFMA; p summed over the
@@ -133,27 +133,56 @@ __device__ __forceinline__ void cmp_attn_tile(const SelParams& p, int unit, int 
 
     int nb = 0;   // sweep 1: K slot of the current tile
 
-    // ---- sweep 1: per-lane running max and sum over the lane's keys ----
+    // ---- sweep 1: per-lane reference and sum over the lane's keys ----
+    // m is a lazily moved reference (log2 units) and lsum the lane's sum of 2^(x - m).  The
+    // common path only adds 2^(x - m) (no maximum, no rescale); a lane's reference moves
+    // when the sum of the values just added leaves [0, 2^32] (the first keys, where
+    // m = -inf, or a value about 2^28 above m), which is rare after the first tile.  fp32
+    // keeps the sum's relative precision at any such scale.
     float m[NQ], lsum[NQ];
 #pragma unroll
     for (int c = 0; c < NQ; ++c) { m[c] = -INFINITY; lsum[c] = 0.f; }
     const int nfull = nv_min / cmpk::kKeysPerTile;   // tiles [0, nfull) are visible to every row
     auto k1buf = [&](int buf) { return kslot + buf * KE; };
-    // statistics update from key sub-tiles 2h, 2h+1 of s (all keys visible: mnew is finite,
-    // and a first update from m = -inf, lsum = 0 gives 0 * 0)
-    auto stats_half = [&](const f32x4 (&s)[4][NQ], int h) {
+    constexpr float kOver = 0x1p32f;
+    // sum of 2^(x - m) over the lane's 8 values of key sub-tiles 2h, 2h+1, column c
+    auto half_sum = [&](const f32x4 (&s)[4][NQ], int h, int c) {
+        float acc = 0.f;
 #pragma unroll
-        for (int c = 0; c < NQ; ++c) {
-            float tmax = fmaxf(s[2 * h][c][0], s[2 * h][c][1]);
+        for (int e = 0; e < 8; ++e) acc += fast_exp2(__builtin_fmaf(s[2 * h + (e >> 2)][c][e & 3], sl2, -m[c]));
+        return acc;
+    };
+    // acc holds the sums of half (sa, ha) and, if two, of half (sb, hb) against m: fold them
+    // into lsum, first moving the reference of the columns whose sum left the range and
+    // summing those halves again against it
+    auto settle = [&](const f32x4 (&sa)[4][NQ], int ha, const f32x4 (&sb)[4][NQ], int hb, bool two,
+                      float (&acc)[NQ]) {
+        bool over = false;
 #pragma unroll
-            for (int e = 2; e < 8; ++e) tmax = fmaxf(tmax, s[2 * h + (e >> 2)][c][e & 3]);
-            const float mnew = fmaxf(m[c], tmax * sl2);
-            float acc = lsum[c] * fast_exp2(m[c] - mnew);
+        for (int c = 0; c < NQ; ++c) over |= !(acc[c] <= kOver);
+        if (__any(over)) {   // wave-uniform branch
 #pragma unroll
-            for (int e = 0; e < 8; ++e) acc += fast_exp2(__builtin_fmaf(s[2 * h + (e >> 2)][c][e & 3], sl2, -mnew));
-            lsum[c] = acc;
-            m[c] = mnew;
+            for (int c = 0; c < NQ; ++c) {
+                if (acc[c] <= kOver) continue;
+                float tmax = -INFINITY;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    tmax = fmaxf(tmax, sa[2 * ha + (e >> 2)][c][e & 3]);
+                    if (two) tmax = fmaxf(tmax, sb[2 * hb + (e >> 2)][c][e & 3]);
+                }
+                const float mnew = fmaxf(m[c], tmax * sl2);
+                float a = 0.f;
+                if (mnew != -INFINITY) {
+                    lsum[c] = m[c] == -INFINITY ? 0.f : lsum[c] * fast_exp2(m[c] - mnew);
+                    m[c] = mnew;
+                    a = half_sum(sa, ha, c);
+                    if (two) a += half_sum(sb, hb, c);
+                }
+                acc[c] = a;
+            }
         }
+#pragma unroll
+        for (int c = 0; c < NQ; ++c) lsum[c] += acc[c];
     };
     auto tile_start1 = [&](int tix) {   // tile tix landed; copy of tile tix + 1 under way
         copies_done();
@@ -163,31 +192,43 @@ __device__ __forceinline__ void cmp_attn_tile(const SelParams& p, int unit, int 
         return kb;
     };
     if (ntile > 0) issue_k(0, kslot);
-    // Tiles visible to every row, software-pipelined: the statistics of each half tile are
-    // updated under the QK products of the next half (across the tile barrier too).
+    // Tiles visible to every row, software-pipelined: the sums of each half tile are taken
+    // under the QK products of the next half (across the tile barrier too).
     if (nfull > 0) {
         f32x4 s[4][NQ];
         const u16* kb = tile_start1(0);
         qk_half(kb, s, 0);
         qk_half(kb, s, 1);
-        stats_half(s, 0);
+        {
+            float acc[NQ];
+#pragma unroll
+            for (int c = 0; c < NQ; ++c) acc[c] = half_sum(s, 0, c);
+            settle(s, 0, s, 0, false, acc);
+        }
         for (int tix = 1; tix < nfull; ++tix) {
             f32x4 prev[4][NQ];
 #pragma unroll
             for (int c = 0; c < NQ; ++c) { prev[2][c] = s[2][c]; prev[3][c] = s[3][c]; }
             kb = tile_start1(tix);
+            float acc[NQ];
             qk_half(kb, s, 0);
-            stats_half(prev, 1);
+#pragma unroll
+            for (int c = 0; c < NQ; ++c) acc[c] = half_sum(prev, 1, c);
             qk_half(kb, s, 1);
-            stats_half(s, 0);
+#pragma unroll
+            for (int c = 0; c < NQ; ++c) acc[c] += half_sum(s, 0, c);
             constexpr int NMQ = 2 * NDS * NQ;   // MFMAs of a QK half
 #pragma unroll
             for (int i = 0; i < 2 * NMQ; ++i) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-                __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);   // VALU
+                __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);   // VALU
             }
+            settle(prev, 1, s, 0, true, acc);
         }
-        stats_half(s, 1);
+        float acc[NQ];
+#pragma unroll
+        for (int c = 0; c < NQ; ++c) acc[c] = half_sum(s, 1, c);
+        settle(s, 1, s, 1, false, acc);
     }
     // tiles with keys invisible to some rows
     for (int tix = nfull; tix < ntile; ++tix) {
