@@ -106,13 +106,19 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ u32x2 swap16(uint32_t v) { return __builtin_amdgcn_permlane16_swap(v, v, false, false); }
 __device__ __forceinline__ u32x2 swap32(uint32_t v) { return __builtin_amdgcn_permlane32_swap(v, v, false, false); }
 
+// IEEE maximum of two floats.  fmaxf first quiets each operand that is not known to be
+// canonical (one extra instruction per MFMA result); this form needs none, and chains of it
+// become gfx950's three-input v_maximum3_f32.  NaN propagates and -0 < +0, which no softmax
+// reference here depends on.
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
 // Max / sum over the four lanes that share a query column (lanes l, l^16, l^32, l^48);
 // every lane ends with the result.
 __device__ __forceinline__ float col_max(float v) {
     u32x2 r = swap16(__float_as_uint(v));
-    v = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    v = vmax(__uint_as_float(r[0]), __uint_as_float(r[1]));
     r = swap32(__float_as_uint(v));
-    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    return vmax(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float col_sum(float v) {
     u32x2 r = swap16(__float_as_uint(v));

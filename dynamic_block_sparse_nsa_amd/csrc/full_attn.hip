@@ -122,9 +122,9 @@ __global__ __launch_bounds__(256, 2) void full_attn_kernel(FullParams p) {
         bool grow = false;
 #pragma unroll
         for (int c = 0; c < NQ; ++c) {
-            float tmax = fmaxf(s[0][c][0], s[0][c][1]);
+            float tmax = vmax(s[0][c][0], s[0][c][1]);
 #pragma unroll
-            for (int e = 2; e < 16; ++e) tmax = fmaxf(tmax, s[e >> 2][c][e & 3]);
+            for (int e = 2; e < 16; e += 2) tmax = vmax(vmax(tmax, s[e >> 2][c][e & 3]), s[e >> 2][c][(e & 3) + 1]);
             mt[c] = col_max(tmax) * sl2;
             grow |= mt[c] > m[c] + kLazy;
         }

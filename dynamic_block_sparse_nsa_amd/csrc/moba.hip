@@ -304,9 +304,9 @@ __global__ __launch_bounds__(256, DK >= 192 ? 2 : 3) void moba_attn_kernel(MobaP
         bool grow[2];
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
-            float tmax = fmaxf(s[0][c][0], s[0][c][1]);
+            float tmax = vmax(s[0][c][0], s[0][c][1]);
 #pragma unroll
-            for (int e = 2; e < 16; ++e) tmax = fmaxf(tmax, s[e >> 2][c][e & 3]);
+            for (int e = 2; e < 16; e += 2) tmax = vmax(vmax(tmax, s[e >> 2][c][e & 3]), s[e >> 2][c][(e & 3) + 1]);
             mt[c] = col_max(tmax) * p.scale_log2;
             grow[c] = mt[c] > m[c] + kMobaLazy;
         }

@@ -77,9 +77,9 @@ struct SoftmaxState {
                 x[4 + r] = (kb >= lo && kb <= hi) ? s1[r] : -INFINITY;
             }
         }
-        float tmax = fmaxf(x[0], x[4]);
+        float tmax = vmax(x[0], x[4]);
 #pragma unroll
-        for (int r = 1; r < 4; ++r) tmax = fmaxf(tmax, fmaxf(x[r], x[4 + r]));
+        for (int r = 1; r < 4; ++r) tmax = vmax(vmax(tmax, x[r]), x[4 + r]);
         // m is a lazily moved reference, not the running max: a column's m moves (and its l
         // and o are rescaled) only when the chunk's max exceeds it by more than 2^kLazy, so
         // p = 2^(x - m) <= 2^kLazy (within fp16's range) and the rescale is rare after the
