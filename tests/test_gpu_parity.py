@@ -1,7 +1,8 @@
 """GPU parity of every library call against the fp64 oracle (needs an MI355X).
 
 Each call is checked on its own, with both sides fed identical inputs: the seeded
-generator's draws, or the oracle's own upstream results (never the GPU's).  Sizes span
+generator's draws, the oracle's own upstream results, or (in the chained prefill tests) the
+GPU's upstream bytes after the oracle has checked them against its own.  Sizes span
 several tiles plus ragged tails; the full-size workloads (8K, 64K, decode at 65536, MoBA
 at 131072) are checked on sampled rows that the oracle computes one by one.
 """
