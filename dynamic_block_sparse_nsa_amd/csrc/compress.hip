@@ -11,9 +11,6 @@
 
 namespace nsa {
 
-// 16-row tiles per workgroup of the linear phi (64K workload: 1, 2, 4 row tiles take
-// 0.53, 0.36, 0.27 ms for nsa_compress)
-constexpr int kCompressRowTiles = 4;
 
 // ---------------------------------------------------------------------------
 // W [KD, dout] -> Wt [dout, KD]  (bf16, 64x64 tiles through LDS)
@@ -185,9 +182,15 @@ void launch_pe_bias(const u16* pe, const u16* Wt, float* bias, int KD, int dout,
 
 void launch_compress_linear(const u16* X, const u16* Wt, const float* bias, u16* out, int BG, int T, int d,
                             int dout, int l, int s, int N, hipStream_t st) {
-    constexpr int RT = kCompressRowTiles;
-    dim3 grid((N + 16 * RT - 1) / (16 * RT), dout / 64, BG);
-    compress_linear_kernel<RT><<<grid, 256, 0, st>>>(X, Wt, bias, out, T, d, dout, l, s, N);
+    // the most row tiles per workgroup (1, 2 or 4) that still give every CU a workgroup; the
+    // results do not depend on the choice (nsa_compress with 1 / 4 row tiles: 64K workload
+    // 0.53 / 0.27 ms, at 32K 0.31 / 0.20 ms, at 8K 0.146 / 0.156 ms)
+    auto n_wg = [&](int rt) { return (size_t)((N + 16 * rt - 1) / (16 * rt)) * (dout / 64) * BG; };
+    const int rt = n_wg(4) >= 256 ? 4 : n_wg(2) >= 256 ? 2 : 1;
+    dim3 grid((N + 16 * rt - 1) / (16 * rt), dout / 64, BG);
+    if (rt == 4) compress_linear_kernel<4><<<grid, 256, 0, st>>>(X, Wt, bias, out, T, d, dout, l, s, N);
+    else if (rt == 2) compress_linear_kernel<2><<<grid, 256, 0, st>>>(X, Wt, bias, out, T, d, dout, l, s, N);
+    else compress_linear_kernel<1><<<grid, 256, 0, st>>>(X, Wt, bias, out, T, d, dout, l, s, N);
 }
 
 void launch_compress_mean(const u16* X, u16* out, int BG, int T, int d, int l, int s, int N, hipStream_t st) {
