@@ -50,9 +50,12 @@ def test_compress_linear_all_blocks(cfg):
     check_ulp(gv[0], rv, f"{cfg.name} V_cmp")
 
 
-def test_compress_linear_64k_sampled_blocks():
-    cfg = P64K
-    announce("compress linear 64k sampled")
+@pytest.mark.parametrize("T", [16384, 65536])
+def test_compress_linear_64k_sampled_blocks(T):
+    """Sampled blocks of the 64K workload's shapes at 16K and 64K tokens (the kernel takes two
+    and four 16-row tiles per workgroup there; the all-blocks test at 8K covers one)."""
+    cfg = P64K.replace(seq_len=T)
+    announce(f"compress linear T={T} sampled")
     inp = inputs.prefill_inputs(cfg)
     kc, vc = ops.compress(cfg, dev_bf16(inp["k"]), dev_bf16(inp["v"]), dev_bf16(inp["w_k"]), dev_bf16(inp["w_v"]),
                           dev_bf16(inp["pe_k"]), dev_bf16(inp["pe_v"]))
@@ -63,8 +66,8 @@ def test_compress_linear_64k_sampled_blocks():
     for g in range(cfg.num_kv_heads):
         rk = oracle.compress_linear(f64(inp["k"][0, g]), f64(inp["pe_k"]), f64(inp["w_k"]), 32, 16, blocks)
         rv = oracle.compress_linear(f64(inp["v"][0, g]), f64(inp["pe_v"]), f64(inp["w_v"]), 32, 16, blocks)
-        check_ulp(gk[0, g, blocks], rk, f"64k K_cmp g{g}")
-        check_ulp(gv[0, g, blocks], rv, f"64k V_cmp g{g}")
+        check_ulp(gk[0, g, blocks], rk, f"T={T} K_cmp g{g}")
+        check_ulp(gv[0, g, blocks], rv, f"T={T} V_cmp g{g}")
 
 
 def test_compress_mean_moba_full():
