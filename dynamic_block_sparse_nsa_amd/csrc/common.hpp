@@ -170,8 +170,9 @@ __device__ __forceinline__ void compress_k_range(int KD, int w, int& k_lo, int& 
 }
 
 // acc[c] += A . B over k in [k_lo, k_hi) (ascending, 32 per MFMA) for the 16-row A operand
-// at xa (element kk of this lane's row at xa + kk) and the four 16-column B tiles at
-// wb + c*16*KD; loads are issued 8 steps ahead of their products.
+// whose element kk (this lane's row) is at xa_at(kk) and the four 16-column B tiles at
+// wb + c*16*KD; loads are issued 8 steps ahead of their products.  The cache append uses
+// it; compress_linear_kernel runs the same per-output order over several row tiles.
 template <typename XAt>
 __device__ __forceinline__ void compress_mfma_range_at(XAt xa_at, const u16* wb, int KD, int k_lo, int k_hi,
                                                        f32x4 (&acc)[4]) {
@@ -195,11 +196,6 @@ __device__ __forceinline__ void compress_mfma_range_at(XAt xa_at, const u16* wb,
 #pragma unroll
         for (int c = 0; c < 4; ++c) acc[c] = mfma16(a, ld8(wb + (size_t)c * 16 * KD + kk), acc[c]);
     }
-}
-
-__device__ __forceinline__ void compress_mfma_range(const u16* xa, const u16* wb, int KD, int k_lo, int k_hi,
-                                                    f32x4 (&acc)[4]) {
-    compress_mfma_range_at([&](int kk) { return xa + kk; }, wb, KD, k_lo, k_hi, acc);
 }
 
 // Workgroup barrier that orders LDS accesses only: this wave's LDS operations complete,
