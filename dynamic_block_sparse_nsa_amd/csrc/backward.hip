@@ -15,7 +15,7 @@
 //                  16-wide MFMA column tile (as in the forward); 32-key chunks shared by the 4
 //                  tokens are staged once in LDS (the next chunk's loads in flight): S^T = K.Q^T
 //                  and dP^T = V.dO^T on the MFMA, dS^T in registers, dQ^T += K^T.dS^T with K^T
-//                  read through the transposing LDS read (dS as a bf16 high/low pair).
+//                  read through the transposing LDS read (dS as single bf16 values).
 // bwd_dq_slc_kernel  selected branch, adds into dQ: the same per-chunk math, each wave
 //                  walking its own token's selected chunks through its own LDS tile.
 // bwd_dkv_kernel   one workgroup per work item of 16 * NW * KT keys against up to 128 (512
@@ -145,15 +145,13 @@ __device__ __forceinline__ void dq_chunk(const u16* kt, const bf16x8 (&va)[2][DV
         ga[r] = pa * (st[2] * d0[r] - st[1]);
         gb[r] = pb * (st[2] * d1[r] - st[1]);
     }
-    // dS as a bf16 high/low pair (about 2^-17 relative): dQ keeps fp32-level accuracy for
-    // 12 more MFMAs per chunk (the dQ kernels are bound by their loads, not by these)
-    bf16x8 gh, gl;
-    pack_p_split(ga, gb, gh, gl);
+    // dS as single bf16 values, as for dK and dV (a high/low pair, 2^-17 relative, cost 12
+    // more MFMAs per chunk: 17.9 against 15.2 ms for the dense dQ at 64K)
+    const bf16x8 gh = pack_p(ga, gb);
 #pragma unroll
     for (int dt = 0; dt < NDK; ++dt) {
         const bf16x8 a = ld_vt_tr(kt, KSTR, 0, 16 * dt);
         acc[dt] = mfma16(a, gh, acc[dt]);
-        acc[dt] = mfma16(a, gl, acc[dt]);
     }
 }
 
