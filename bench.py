@@ -365,15 +365,17 @@ def main():
                         "per_call_ms": {n: round(float(c), 4) for n, c in zip(names3, call_ms3)}},
         "wall_s_timed": round(wall, 3),
     }
-    # The roofline of the dominant kernel on both axes: its algorithmic flops against the
-    # bf16 MFMA peak, and the HBM bytes the counters record per launch (FETCH_SIZE +
-    # WRITE_SIZE, scaled) against the HBM peak.  The larger fraction names the bound.
+    # The roofline of the dominant kernel: its algorithmic flops against the bf16 MFMA peak
+    # (the prefill's roofline: the path's algorithmic work is counted in flops), and beside
+    # it the HBM axis, the bytes the counters record per launch (FETCH_SIZE + WRITE_SIZE,
+    # scaled) against the HBM peak.  "limiter" names the axis with the larger fraction.
     sec = call_ms[dom] * 1e-3
     hbm_bytes = None if traffic is None else traffic.get("bytes_per_launch")
     hbm_frac = None if hbm_bytes is None else hbm_bytes / sec / 1e9 / PEAK_HBM_GBS
     mfma_frac = dom_tf / PEAK_BF16_TFLOPS
     result["roofline"] = {
-        "bound": "hbm" if (hbm_frac is not None and hbm_frac > mfma_frac) else "mfma",
+        "bound": "mfma",
+        "limiter": None if hbm_frac is None else ("hbm" if hbm_frac > mfma_frac else "mfma"),
         "kernel": dom_kernel, "call": names[dom], "call_kernels": dom_launches,
         "achieved": round(dom_tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(mfma_frac, 4),
         "traffic": hbm_bytes,
