@@ -234,7 +234,7 @@ def test_prefill_end_to_end(cfg):
     _prefill_end_to_end(cfg)
 
 
-def _prefill_end_to_end(cfg):
+def _prefill_end_to_end(cfg, inp=None):
     """The whole prefill path as one chain on the GPU, each step against the oracle:
       * the GPU's compressed keys/values within one bf16 ulp of the oracle's compression of
         the same inputs (sampled blocks at 64K);
@@ -248,7 +248,7 @@ def _prefill_end_to_end(cfg):
     The fused call nsa_prefill_fwd must reproduce the three calls' outputs, lists, LSE and
     o_cmp bit for bit (same arithmetic, one launch)."""
     announce(f"end to end {cfg.name}")
-    inp = inputs.prefill_inputs(cfg)
+    inp = inputs.prefill_inputs(cfg) if inp is None else inp
     args = [dev_bf16(inp[n]) for n in ("q", "k", "v", "w_k", "w_v", "pe_k", "pe_v")] + [dev_f32(inp["gates"])]
     r = ops.prefill(cfg, *args)
     # the fused call (nsa_prefill_fwd) runs the same arithmetic in one launch: identical bits
@@ -345,6 +345,33 @@ SHAPES = [
 @pytest.mark.parametrize("cfg", SHAPES, ids=lambda c: c.name)
 def test_prefill_shape_matrix(cfg):
     _prefill_end_to_end(cfg)
+
+
+def _ramped_keys(inp, top=16.0, v_scale=1.0):
+    """The inputs with every key row scaled from x1 at the first token to x`top` at the last
+    (bf16 again), so that scores grow along the sequence: the largest scaled scores of the
+    last keys lie tens of log2 units above those of the first ones.  v_scale scales the
+    values: attention this peaked makes a branch's output nearly one value row, and the
+    gated sum of three such rows reaches |O| ~ 13, where half a bf16 ulp (2^-5) exceeds the
+    output bar's absolute tolerance; 1/4 keeps |O| below 4 (half an ulp 2^-8)."""
+    k = f64(inp["k"])
+    T = k.shape[2]
+    ramp = 1.0 + (top - 1.0) * np.arange(T) / max(T - 1, 1)
+    out = dict(inp)
+    out["k"] = inputs.f32_to_bf16_bits((k * ramp[None, None, :, None]).astype(np.float32))
+    if v_scale != 1.0:
+        out["v"] = inputs.f32_to_bf16_bits((f64(inp["v"]) * v_scale).astype(np.float32))
+    return out
+
+
+def test_prefill_growing_scores():
+    """Keys growing along the sequence (_ramped_keys): later chunks exceed the softmax
+    references that the kernels move lazily (by more than 2^8 in the selected / window
+    branches, by more than 2^32 in the sum of the compressed branch's statistics), so the
+    paths that move a reference and rescale run; the whole chain still matches the oracle
+    on every row of the 64K workload's shapes."""
+    cfg = RAGGED16.replace(name="kramp16", seed=81)
+    _prefill_end_to_end(cfg, _ramped_keys(inputs.prefill_inputs(cfg), v_scale=0.25))
 
 
 DECODE_SHAPES = [
@@ -542,8 +569,8 @@ def test_block_major_all_rows(case):
 # ---------------------------------------------------------------------------
 # dense causal attention (the comparison kernel)
 # ---------------------------------------------------------------------------
-def _full_case(cfg, rows):
-    inp = inputs.prefill_inputs(cfg)
+def _full_case(cfg, rows, inp=None):
+    inp = inputs.prefill_inputs(cfg) if inp is None else inp
     out = ops.full_attn_fwd(cfg, dev_bf16(inp["q"]), dev_bf16(inp["k"]), dev_bf16(inp["v"]))
     torch.cuda.synchronize()
     got = bf16_dev_to_f64(out)[0, rows]
@@ -559,6 +586,14 @@ def _full_case(cfg, rows):
 def test_full_attn_all_rows(cfg):
     announce(f"dense attention {cfg.name} all rows")
     _full_case(cfg, np.arange(cfg.seq_len, dtype=np.int32))
+
+
+def test_full_attn_growing_scores():
+    """Dense causal attention on keys growing along the sequence: its lazily moved softmax
+    reference moves (and rescales) on later tiles; every row against the oracle."""
+    cfg = RAGGED16.replace(name="kramp16_dense", seed=82)
+    announce("dense attention growing scores")
+    _full_case(cfg, np.arange(cfg.seq_len, dtype=np.int32), _ramped_keys(inputs.prefill_inputs(cfg)))
 
 
 @pytest.mark.parametrize("cfg", [P8K, RAGGED16, P64K], ids=lambda c: c.name)
