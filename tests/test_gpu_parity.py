@@ -533,10 +533,12 @@ def test_block_major_large_values():
         check_close(gout[b] / 1e5, ref / 1e5, f"block-major large values b={b}")
 
 
-@pytest.mark.parametrize("case", ["b2_lp64_gated", "lp128_own_optional", "top12", "top32"])
+@pytest.mark.parametrize("case", ["b2_lp64_gated", "lp128_own_optional", "top12", "top32", "ramp"])
 def test_block_major_all_rows(case):
     """G = 1 with only the selected branch runs the block-major schedule (per-block query
-    lists, per-slot partials, merge); every row of a ragged batch is checked."""
+    lists, per-slot partials, merge); every row of a ragged batch is checked.  "ramp": keys
+    growing x1 -> x16 along the sequence, so within a 512-token block later tiles exceed a
+    column's lazily moved softmax reference and it moves."""
     if case == "b2_lp64_gated":
         cfg = MOBA.replace(name=case, batch=2, seq_len=1000, num_kv_heads=3, cmp_block=64, cmp_stride=64,
                            slc_block=64, top_n=3, seed=21)
@@ -544,12 +546,16 @@ def test_block_major_all_rows(case):
         cfg = MOBA.replace(name=case, batch=1, seq_len=1500, num_kv_heads=2, cmp_block=128, cmp_stride=128,
                            slc_block=128, top_n=4, n_local=0, n_init=1, phi=PHI_LINEAR,
                            score_mode=SCORE_CMP_OVERLAP, seed=22)
+    elif case == "ramp":
+        cfg = MOBA.replace(name=case, batch=1, seq_len=3000, num_kv_heads=2, seed=29)
     else:   # longer lists: the merge's 8-slot and 32-slot forms (ragged, 64-token blocks)
         n = 12 if case == "top12" else 32
         cfg = MOBA.replace(name=case, batch=1, seq_len=2500, num_kv_heads=2, cmp_block=64, cmp_stride=64,
                            slc_block=64, top_n=n, seed=24 + n)
     announce(f"block-major {case}")
     inp = inputs.prefill_inputs(cfg)
+    if case == "ramp":
+        inp = _ramped_keys(inp)
     lists = inputs.block_lists(cfg, seed=600)
     gates = None
     if case == "b2_lp64_gated":
