@@ -563,7 +563,7 @@ def main():
 
     # ---------------- MoBA (the 128K workload, and 1M tokens) ----------------
     if not args.no_moba:
-        for mc, key, steps in ((MOBA, "moba", 3), (MOBA.replace(name="moba_1m", seq_len=1 << 20), "moba_1m", 2)):
+        for mc, key, steps in ((MOBA, "moba", 10), (MOBA.replace(name="moba_1m", seq_len=1 << 20), "moba_1m", 3)):
             print(f"[bench] {key} inputs", file=sys.stderr, flush=True)
             g = torch.Generator(device=dev).manual_seed(mc.seed)
             Qm = torch.randn((1, mc.seq_len, mc.num_heads, mc.d_k), generator=g, device=dev).to(torch.bfloat16)

@@ -424,17 +424,20 @@ nsa_status sparse_attn_fwd_impl(const nsa_config* cfg, const void* Q, const void
     if ((st = check_ws(ws, ws_bytes, w.total)) != NSA_OK) return st;
     const hipStream_t hs = as_stream(stream);
     using nsa::u16;
-    u16* kf = at<u16>(ws, w.kf);
+    const bool block_major = use_block_major(s) && !train;
+    if (block_major && (long long)s.T >= (1LL << 26))
+        return fail(NSA_ERR_UNSUPPORTED, "sequence too long for the block lists");
+    // the block-major kernel gathers K from the row-major keys: only V is copied for it
+    u16* kf = block_major ? nullptr : at<u16>(ws, w.kf);
     u16* vf = at<u16>(ws, w.vf);
     // fragment order, V as fp16 scaled by a power of two per (sequence, group)
     if (!nsa::launch_tile_cmp(s.dk, s.dv, static_cast<const u16*>(K), static_cast<const u16*>(V),
                               at<uint32_t>(ws, w.vmax), at<int>(ws, w.vexp), kf, vf, s.B * s.Hkv, s.T, w.tpad, hs))
         return fail(NSA_ERR_UNSUPPORTED, "no layout kernel");
-    if (use_block_major(s) && !train) {
-        if ((long long)s.T >= (1LL << 26)) return fail(NSA_ERR_UNSUPPORTED, "sequence too long for the block lists");
+    if (block_major) {
         nsa::MobaParams m{};
         m.Q = static_cast<const u16*>(Q);
-        m.Kf = kf;
+        m.K = static_cast<const u16*>(K);
         m.Vf = vf;
         m.vexp = at<int>(ws, w.vexp);
         m.sel = sel_idx;

@@ -90,7 +90,7 @@ bool launch_prefill_fused(int DK, int DV, int G, const SelParams& sp, const Attn
 constexpr int kMobaChunk = 1024;   // tokens per histogram / scatter workgroup
 struct MobaParams {
     const u16* Q;              // [B,T,H,DK] (H = Hkv)
-    const u16* Kf;             // fragment-order K (see AttnParams)
+    const u16* K;              // [B,Hkv,T,DK] row-major (tiles gathered into fragment order)
     const u16* Vf;             // fragment-order V, fp16 scaled by 2^-vexp (launch_tile_cmp)
     const int* vexp;           // [B*Hkv]
     const int32_t* sel;        // [B,T,Hkv,top_n]

@@ -168,14 +168,41 @@ __global__ __launch_bounds__(256, DK >= 192 ? 2 : 3) void moba_attn_kernel(MobaP
     const int n_tiles = p.n_own + p.tile_start[p.n_bucket];
     if (item >= n_tiles) return;
 
-    int bh, j, ncol;
-    bool own;
-    if (item < p.n_own) {
-        own = true;
-        const int per_blk = (p.lp + kCol - 1) / kCol;
-        bh = item / (p.n_slc * per_blk);
+    // the item's (sequence, head) and block: arithmetic for own-block items, one table read
+    // for bucket tiles (tile_start[bk] <= it < tile_start[bk + 1])
+    const bool own = item < p.n_own;
+    const int per_blk = (p.lp + kCol - 1) / kCol;
+    const int it = item - p.n_own;
+    const int bk = own ? 0 : p.tile_bucket[it];
+    const int bh = own ? item / (p.n_slc * per_blk) : bk / p.n_slc;
+    const int j = own ? (item % (p.n_slc * per_blk)) / per_blk : bk % p.n_slc;
+    const int kbeg = j * p.lp;   // < T: every block holds a token
+
+    // K rows are gathered straight from [B,Hkv,T,DK] into the fragment order of the LDS tile
+    // (lane (li, lq) of 16-key group kt and step ds brings K[16kt + li][32ds + 8lq ..+8];
+    // rows past T are clamped, their scores are masked or never formed); V comes from the
+    // scaled fp16 copy.  (Requesting tile 0 before the lists are read was slower: the list
+    // and query loads then wait behind the copies.)
+    const u16* kg = p.K + (size_t)bh * p.T * DK;
+    const u16* vg = p.Vf + (size_t)bh * p.Tpad * DV;
+    auto issue_k = [&](int tix, u16* dst) {
+        const int key_t = kbeg + kKeys * tix;
+        for (int ch = wave; ch < KE / 512; ch += 4) {
+            const int kt = ch / NDS, ds = ch % NDS;
+            const int row = min(key_t + 16 * kt + li, p.T - 1);
+            __builtin_amdgcn_global_load_lds(kg + (size_t)row * DK + 32 * ds + 8 * lq, (lds_void*)(dst + ch * 512), 16,
+                                             0, 0);
+        }
+    };
+    auto issue_v = [&](int tix) {
+        const u16* src = vg + (size_t)((kbeg + kKeys * tix) / 32) * NDT * 512;
+        for (int ch = wave; ch < VE / 512; ch += 4)
+            __builtin_amdgcn_global_load_lds(src + ch * 512 + lane * 8, (lds_void*)(vbuf + ch * 512), 16, 0, 0);
+    };
+
+    int ncol;
+    if (own) {
         const int r = item % (p.n_slc * per_blk);
-        j = r / per_blk;
         const int t0 = j * p.lp + (r % per_blk) * kCol;
         const int t1 = min(min(t0 + kCol, (j + 1) * p.lp), p.T);
         ncol = max(0, t1 - t0);
@@ -192,11 +219,6 @@ __global__ __launch_bounds__(256, DK >= 192 ? 2 : 3) void moba_attn_kernel(MobaP
             col_slot[cix] = sl;
         }
     } else {
-        own = false;
-        const int it = item - p.n_own;
-        const int bk = p.tile_bucket[it];   // tile_start[bk] <= it < tile_start[bk + 1]
-        bh = bk / p.n_slc;
-        j = bk % p.n_slc;
         const int e0 = p.bucket_start[bk] + (it - p.tile_start[bk]) * kCol;
         ncol = min(kCol, p.bucket_start[bk + 1] - e0);
         for (int cix = threadIdx.x; cix < kCol; cix += 256) {
@@ -228,27 +250,16 @@ __global__ __launch_bounds__(256, DK >= 192 ? 2 : 3) void moba_attn_kernel(MobaP
         for (int cix = 0; cix < kCol; ++cix) tmax_wg = max(tmax_wg, col_tok[cix]);
         kend = min(kend, tmax_wg);
     }
-    const int kbeg = j * p.lp;
     const int ntile = kend >= kbeg ? (kend - kbeg) / kKeys + 1 : 0;
-
-    const u16* kg = p.Kf + (size_t)bh * p.Tpad * DK;
-    const u16* vg = p.Vf + (size_t)bh * p.Tpad * DV;
-    // a 64-key tile in fragment order is KE (K) and VE (V) contiguous elements of the copies
-    auto issue_k = [&](int tix, u16* dst) {
-        const u16* src = kg + (size_t)((kbeg + kKeys * tix) / 16) * NDS * 512;
-        for (int ch = wave; ch < KE / 512; ch += 4)
-            __builtin_amdgcn_global_load_lds(src + ch * 512 + lane * 8, (lds_void*)(dst + ch * 512), 16, 0, 0);
-    };
-    auto issue_v = [&](int tix) {
-        const u16* src = vg + (size_t)((kbeg + kKeys * tix) / 32) * NDT * 512;
-        for (int ch = wave; ch < VE / 512; ch += 4)
-            __builtin_amdgcn_global_load_lds(src + ch * 512 + lane * 8, (lds_void*)(vbuf + ch * 512), 16, 0, 0);
-    };
     // a column's last visible key (empty columns: none masked, their values are never stored)
     int hi[2];
 #pragma unroll
     for (int c = 0; c < 2; ++c) hi[c] = tok[c] >= 0 ? tok[c] : INT_MAX;
     const int hi_min = (int)wave_min_u32((uint32_t)min(hi[0], hi[1]));   // the wave's earliest limit
+    if (ntile > 0) {
+        issue_k(0, kslot);
+        issue_v(0);
+    }
 
     // m: the column's reference (the same in its four lanes), moved only when a tile exceeds
     // it by more than 2^8, so that o is rarely rescaled; p = 2^(x - m) <= 2^8 fits fp16
@@ -259,10 +270,6 @@ __global__ __launch_bounds__(256, DK >= 192 ? 2 : 3) void moba_attn_kernel(MobaP
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) o[c][dt] = zero4();
 
-    if (ntile > 0) {
-        issue_k(0, kslot);
-        issue_v(0);
-    }
     // copies per wave of a K tile and of a V tile; a wave's copies land in issue order, so
     // a wait for "at most n outstanding" covers every copy but the last n
     constexpr int NKW = KE / 512 / 4, NVW = VE / 512 / 4;

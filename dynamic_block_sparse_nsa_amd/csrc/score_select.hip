@@ -108,7 +108,8 @@ __device__ __forceinline__ int cmp_v_exponent(const uint32_t* part) {
 // operand holds K[16kt + li][32ds + 8lq .. +7], the 64 lanes' pieces contiguous; for
 // 32-key chunk c and value slice dt, lane (li, lq) holds V^T[16dt + li] at keys
 // 32c + {4lq..4lq+3, 16+4lq..16+4lq+3}, as fp16 scaled by 2^-e (cmp_v_exponent; e is
-// written to vexp[unit]).  Keys >= N are zero.
+// written to vexp[unit]).  Keys >= N are zero.  With Kf null only the values are copied
+// (the block-major kernel gathers its K tiles from the row-major keys itself).
 // ---------------------------------------------------------------------------
 template <int DK, int DV>
 __global__ __launch_bounds__(256) void tile_cmp_kernel(const u16* __restrict__ K, const u16* __restrict__ V,
@@ -122,7 +123,7 @@ __global__ __launch_bounds__(256) void tile_cmp_kernel(const u16* __restrict__ K
     const int c = blockIdx.x;
     const size_t bg = blockIdx.y;
     const u16* kg = K + bg * (size_t)N * DK;
-    for (int idx = threadIdx.x; idx < 32 * DK / 8; idx += 256) {
+    for (int idx = threadIdx.x; Kf && idx < 32 * DK / 8; idx += 256) {
         const int r = idx / (DK / 8), col = (idx % (DK / 8)) * 8;
         const int key = 32 * c + r;
         const u32x4 v = key < N ? *reinterpret_cast<const u32x4*>(kg + (size_t)key * DK + col) : u32x4{0u, 0u, 0u, 0u};
@@ -150,7 +151,7 @@ __global__ __launch_bounds__(256) void tile_cmp_kernel(const u16* __restrict__ K
     }
     __syncthreads();
     u16* kout = Kf + bg * (size_t)Npad * DK + (size_t)(2 * c) * NDS * 512;
-    for (int idx = threadIdx.x; idx < 2 * NDS * 64; idx += 256) {
+    for (int idx = threadIdx.x; Kf && idx < 2 * NDS * 64; idx += 256) {
         const int kk = idx / (NDS * 64), ds = (idx / 64) % NDS, ln = idx % 64;
         const int li = ln & 15, lq = ln >> 4;
         *reinterpret_cast<u32x4*>(kout + (size_t)idx * 8) =
