@@ -32,8 +32,8 @@ constexpr int kCol = 128;    // query columns per work item (4 waves x 2 tiles x
 constexpr int kKeys = 64;    // keys per LDS tile
 constexpr float kMobaLazy = 8.f;   // log2 headroom before a column's softmax reference moves
 
-// dynamic LDS of moba_attn_kernel: two K tiles and one V tile of 64 keys
-constexpr size_t moba_attn_lds(int DK, int DV) { return (size_t)kKeys * (2 * DK + DV) * 2; }
+// dynamic LDS of moba_attn_kernel: one K tile and two V tiles of 64 keys
+constexpr size_t moba_attn_lds(int DK, int DV) { return (size_t)kKeys * (DK + 2 * DV) * 2; }
 static_assert(kCol == kBwdTile, "the backward's work items use the lists' 128-entry tiles");
 
 }  // namespace
@@ -154,10 +154,10 @@ __global__ __launch_bounds__(256, DK >= 192 ? 2 : 3) void moba_attn_kernel(MobaP
     constexpr int NDS = DK / 32, NDT = DV / 16;
     constexpr int KE = 4 * NDS * 512;       // K elements of a 64-key tile (fragment order)
     constexpr int VE = 2 * NDT * 512;       // V elements
-    // K tiles double-buffered, the V tile single-buffered, both filled by global -> LDS copies
+    // the K tile single-buffered, V tiles double-buffered, all filled by global -> LDS copies
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-    u16* kslot = reinterpret_cast<u16*>(smem);   // [2][KE]
-    u16* vbuf = kslot + 2 * KE;                   // [VE]
+    u16* kslot = reinterpret_cast<u16*>(smem);   // [KE]
+    u16* vslot = kslot + KE;                      // [2][VE]
     __shared__ int col_tok[kCol], col_slot[kCol];
 
     const int lane = threadIdx.x & 63;
@@ -196,8 +196,9 @@ __global__ __launch_bounds__(256, DK >= 192 ? 2 : 3) void moba_attn_kernel(MobaP
     };
     auto issue_v = [&](int tix) {
         const u16* src = vg + (size_t)((kbeg + kKeys * tix) / 32) * NDT * 512;
+        u16* dst = vslot + (tix & 1) * VE;
         for (int ch = wave; ch < VE / 512; ch += 4)
-            __builtin_amdgcn_global_load_lds(src + ch * 512 + lane * 8, (lds_void*)(vbuf + ch * 512), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(src + ch * 512 + lane * 8, (lds_void*)(dst + ch * 512), 16, 0, 0);
     };
 
     int ncol;
@@ -270,18 +271,18 @@ __global__ __launch_bounds__(256, DK >= 192 ? 2 : 3) void moba_attn_kernel(MobaP
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) o[c][dt] = zero4();
 
-    // copies per wave of a K tile and of a V tile; a wave's copies land in issue order, so
-    // a wait for "at most n outstanding" covers every copy but the last n
-    constexpr int NKW = KE / 512 / 4, NVW = VE / 512 / 4;
+    // Copy schedule of tile tix: V(tix + 1) is requested at the tile's start (its slot held
+    // V(tix - 1), whose reads ended before the barrier) and K(tix + 1) once every wave has
+    // read K(tix) (the barrier after the QK products); the start of the next tile waits for
+    // both.  So V's copy has a whole tile to land and K's the value products.  (A single V
+    // slot refilled after the value products left V's copy no compute to hide under: the
+    // barriers' own waits cover every outstanding copy.)
     static_assert(KE % 2048 == 0 && VE % 2048 == 0, "the waves split a tile's copies evenly");
     for (int tix = 0; tix < ntile; ++tix) {
-        // K(tix) has landed (this thread's copies, then everyone's); V(tix), issued after it,
-        // may still be in flight (the first tile also waits for the query loads)
-        if (tix == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NVW) : "memory");
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this thread's copies, then everyone's
         __syncthreads();
-        if (tix + 1 < ntile) issue_k(tix + 1, kslot + ((tix + 1) & 1) * KE);
-        const u16* kb = kslot + (tix & 1) * KE;
+        if (tix + 1 < ntile) issue_v(tix + 1);
+        const u16* kb = kslot;
         const int key0 = kbeg + kKeys * tix;
         f32x4 s[4][2];
 #pragma unroll
@@ -342,10 +343,9 @@ __global__ __launch_bounds__(256, DK >= 192 ? 2 : 3) void moba_attn_kernel(MobaP
                 }
             l[c] += acc;
         }
-        // V(tix) has landed; K(tix + 1), issued after it, may still be in flight
-        if (tix + 1 < ntile) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NKW) : "memory");
-        else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
+        // every wave's reads of K(tix) have returned (no wait on the copies in flight)
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        if (tix + 1 < ntile) issue_k(tix + 1, kslot);
 #pragma unroll
         for (int u = 0; u < 2; ++u) {   // P in fp16 against the scaled fp16 V copy: one product
             f16x8 ph[2];
@@ -353,14 +353,11 @@ __global__ __launch_bounds__(256, DK >= 192 ? 2 : 3) void moba_attn_kernel(MobaP
             for (int c = 0; c < 2; ++c) ph[c] = pack_p_h(s[2 * u][c], s[2 * u + 1][c]);
 #pragma unroll
             for (int dt = 0; dt < NDT; ++dt) {
-                const f16x8 a = ld8h(&vbuf[((u * NDT + dt) * 64 + lane) * 8]);
+                const f16x8 a = ld8h(&vslot[(tix & 1) * VE + ((u * NDT + dt) * 64 + lane) * 8]);
 #pragma unroll
                 for (int c = 0; c < 2; ++c) o[c][dt] = mfma16h(a, ph[c], o[c][dt]);
             }
         }
-        // every wave's reads of the V tile have returned; no wait on outstanding copies
-        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-        if (tix + 1 < ntile) issue_v(tix + 1);
     }
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
