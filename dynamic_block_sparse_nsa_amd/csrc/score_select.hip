@@ -256,12 +256,14 @@ __global__ __launch_bounds__(256, 2) void mean_scores_kernel(SelParams p) {
 // kFusedMaxPicks picks besides the forced blocks (the MoBA configuration: top-3 with the
 // own block forced, two picks).  A workgroup owns 64 tokens (a wave's 16 MFMA columns are
 // 16 tokens); each lane keeps, for its column, the best K candidates (K = the picks rounded
-// up to 1, 2 or 4) among the keys it holds as 64-bit entries score-key:~index (larger =
-// better score, then lower index), so no score row is ever stored.  A candidate's insertion
-// is skipped (wave-uniformly) when its score is below every lane's current K-th best.  The
-// four lanes of a
-// column merge their lists (bitonic top-K of two sorted lists, then a sort) across the 16-
-// and 32-lane swaps.
+// up to 1, 2 or 4) among the keys it holds, as fp32 scores with their block indices, so no
+// score row is ever stored.  A lane meets its keys in ascending index order, so a candidate
+// enters the list only on a strictly larger score (equal scores keep the lower index), and
+// the entries it displaces move down unconditionally; every candidate goes through the
+// branch-free insertion (an invalid one as -inf).  The four lanes of a
+// column then merge their lists as 64-bit entries score-key:~index (larger = better score,
+// then lower index): bitonic top-K of two sorted lists, then a sort, across the 16- and
+// 32-lane swaps.
 template <int DK, int K>
 __global__ __launch_bounds__(256, 2) void mean_select_kernel(SelParams p) {
     constexpr int TQ = kWaves * 16;
@@ -291,9 +293,15 @@ __global__ __launch_bounds__(256, 2) void mean_select_kernel(SelParams p) {
     const int nv_max = min(t_last / p.lp, N);
     const u16* kbase = p.Kc + (size_t)unit * N * DK;
 
-    uint64_t best[K];
+    // this lane's candidates: blocks f_init <= j < f_loc_lo (the initial and local blocks are
+    // forced; f_loc_lo <= jc, so every candidate is a complete earlier block)
+    const int clo = live ? fb.f_init : 0, chi = live ? fb.f_loc_lo : 0;
+    // tiles whose 64 keys are candidates of every lane of the wave skip the range test
+    const int wclo = (int)wave_max_u32((uint32_t)clo), wchi = (int)wave_min_u32((uint32_t)chi);
+    float bs[K];
+    int bi[K];
 #pragma unroll
-    for (int i = 0; i < K; ++i) best[i] = 0ull;
+    for (int i = 0; i < K; ++i) { bs[i] = -INFINITY; bi[i] = -1; }
     for (int k0 = 0; k0 < nv_max; k0 += kKeysPerTile) {
         __syncthreads();
         stage_rows<DK, KSTR>(kbase, k0, N, ks);
@@ -305,29 +313,37 @@ __global__ __launch_bounds__(256, 2) void mean_select_kernel(SelParams p) {
         for (int ds = 0; ds < NDS; ++ds)
 #pragma unroll
             for (int kt = 0; kt < 4; ++kt) s[kt] = mfma16(ld8(&ks[(16 * kt + li) * KSTR + 32 * ds + lq * 8]), qf[ds], s[kt]);
-        // A candidate whose 32-bit score key is below the key of the lane's K-th entry cannot
-        // enter the list; the 64-bit insertion (score key : inverted index, so equal scores
-        // order by the lower index) runs only for candidates that some lane cannot rule out.
+        const bool inside = k0 >= wclo && k0 + kKeysPerTile <= wchi;   // wave-uniform
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int j = k0 + 16 * kt + 4 * lq + r;
-                // candidates are complete earlier blocks: the own block is forced (n_local >= 1)
-                const bool ok = live && fb.candidate(j);
-                const uint32_t key = f2key(s[kt][r]);
-                const bool pass = ok && key >= (uint32_t)(best[K - 1] >> 32);
-                if (__any(pass)) {   // wave-uniform
-                    uint64_t e = pass ? (((uint64_t)key << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)j)) : 0ull;
+                float x = (inside || (j >= clo && j < chi)) ? s[kt][r] : -INFINITY;
+                int jx = j;
+                // insert into the descending list: the candidate takes the first slot it
+                // beats; every later slot then takes the entry above it (ranked higher by
+                // the list's order even on an equal score, being of a lower index)
+                bool shift = false;
 #pragma unroll
-                    for (int q = 0; q < K; ++q) {   // insert into the descending list
-                        const uint64_t hi = e > best[q] ? e : best[q];
-                        e = e > best[q] ? best[q] : e;
-                        best[q] = hi;
+                for (int q = 0; q < K; ++q) {
+                    const bool c = shift || x > bs[q];
+                    shift = c;
+                    const float tb = bs[q];
+                    const int ti = bi[q];
+                    bs[q] = c ? x : tb;
+                    bi[q] = c ? jx : ti;
+                    if (q + 1 < K) {
+                        x = c ? tb : x;
+                        jx = c ? ti : jx;
                     }
                 }
             }
     }
+    uint64_t best[K];
+#pragma unroll
+    for (int q = 0; q < K; ++q)
+        best[q] = bi[q] >= 0 ? (((uint64_t)f2key(bs[q]) << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)bi[q])) : 0ull;
     // merge the column's four lists: lanes l and l ^ 16, then l and l ^ 32
 #pragma unroll
     for (int step = 0; step < 2; ++step) {
