@@ -298,6 +298,7 @@ __global__ __launch_bounds__(256, 2) void mean_select_kernel(SelParams p) {
     const int clo = live ? fb.f_init : 0, chi = live ? fb.f_loc_lo : 0;
     // tiles whose 64 keys are candidates of every lane of the wave skip the range test
     const int wclo = (int)wave_max_u32((uint32_t)clo), wchi = (int)wave_min_u32((uint32_t)chi);
+    const uint32_t span = chi > clo ? (uint32_t)(chi - clo) : 0u;   // j is a candidate iff j - clo < span
     float bs[K];
     int bi[K];
 #pragma unroll
@@ -313,32 +314,40 @@ __global__ __launch_bounds__(256, 2) void mean_select_kernel(SelParams p) {
         for (int ds = 0; ds < NDS; ++ds)
 #pragma unroll
             for (int kt = 0; kt < 4; ++kt) s[kt] = mfma16(ld8(&ks[(16 * kt + li) * KSTR + 32 * ds + lq * 8]), qf[ds], s[kt]);
-        const bool inside = k0 >= wclo && k0 + kKeysPerTile <= wchi;   // wave-uniform
+        // insert into the descending list: the candidate takes the first slot it beats (the
+        // tests x > bs[q] are monotone in q and independent of each other); every later slot
+        // takes the entry above it (ranked higher by the list's order even on an equal score,
+        // being of a lower index)
+        auto insert = [&](float x, int jx) {
+            bool cp = false;   // the slot above was taken by the candidate or shifted
+            float bp = 0.f;
+            int ip = 0;
 #pragma unroll
-        for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int j = k0 + 16 * kt + 4 * lq + r;
-                float x = (inside || (j >= clo && j < chi)) ? s[kt][r] : -INFINITY;
-                int jx = j;
-                // insert into the descending list: the candidate takes the first slot it
-                // beats; every later slot then takes the entry above it (ranked higher by
-                // the list's order even on an equal score, being of a lower index)
-                bool shift = false;
-#pragma unroll
-                for (int q = 0; q < K; ++q) {
-                    const bool c = shift || x > bs[q];
-                    shift = c;
-                    const float tb = bs[q];
-                    const int ti = bi[q];
-                    bs[q] = c ? x : tb;
-                    bi[q] = c ? jx : ti;
-                    if (q + 1 < K) {
-                        x = c ? tb : x;
-                        jx = c ? ti : jx;
-                    }
-                }
+            for (int q = 0; q < K; ++q) {
+                const bool c = x > bs[q];
+                const float tb = bs[q];
+                const int ti = bi[q];
+                bs[q] = cp ? bp : (c ? x : tb);
+                bi[q] = cp ? ip : (c ? jx : ti);
+                cp = c;
+                bp = tb;
+                ip = ti;
             }
+        };
+        if (k0 >= wclo && k0 + kKeysPerTile <= wchi) {   // wave-uniform: every key a candidate
+#pragma unroll
+            for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) insert(s[kt][r], k0 + 16 * kt + 4 * lq + r);
+        } else {
+#pragma unroll
+            for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int j = k0 + 16 * kt + 4 * lq + r;
+                    insert((uint32_t)(j - clo) < span ? s[kt][r] : -INFINITY, j);
+                }
+        }
     }
     uint64_t best[K];
 #pragma unroll
