@@ -131,8 +131,11 @@ FullWs full_ws(const Shape& s) {
 // the block-major schedule of moba.hip.
 bool use_block_major(const Shape& s) { return s.G == 1 && s.br == NSA_BR_SLC; }
 
-// K and V copied into MFMA fragment order, padded with 64 zero keys past a multiple of 64; for the
-// block-major schedule also the bucket lists and the per-slot partial results.
+// V (and K) copied into MFMA fragment order, padded with 64 zero keys past a multiple of 64,
+// V's fp16 scaling; then either the K copy or, for the block-major schedule (which gathers K
+// from the row-major keys), the bucket lists and the per-slot partial results, over the same
+// bytes (the training forward runs the query-centric kernel on the K copy even for those
+// shapes).
 struct AttnWs {
     size_t kf, vf, vmax, vexp, hist, bcnt, bstart, tstart, tbk, entries, pm, pl, po, total;
     int tpad, n_chunk, n_bucket;
@@ -142,10 +145,13 @@ AttnWs attn_ws(const Shape& s) {
     w.tpad = round_up(s.T, 64) + 64;   // a 64-key tile may start at any multiple of 32 below T
     const size_t bg = (size_t)s.B * s.Hkv;
     size_t off = 0;
-    w.kf = off; off = align_up(off + bg * w.tpad * s.dk * 2, 256);
     w.vf = off; off = align_up(off + bg * w.tpad * s.dv * 2, 256);
     w.vmax = off; off = align_up(off + bg * nsa::cmp_vmax_parts() * 4, 256);   // V's fp16 scaling
     w.vexp = off; off = align_up(off + bg * 4, 256);
+    const size_t u0 = off;
+    w.kf = u0;
+    const size_t kf_end = align_up(u0 + bg * w.tpad * s.dk * 2, 256);
+    off = u0;
     if (use_block_major(s)) {
         w.n_chunk = nsa::moba_n_chunk(s.T);
         w.n_bucket = (int)(bg * s.n_slc);
@@ -160,7 +166,7 @@ AttnWs attn_ws(const Shape& s) {
         w.pl = off; off = align_up(off + rows * 4, 256);
         w.po = off; off = align_up(off + rows * s.dv * 2, 256);
     }
-    w.total = off;
+    w.total = std::max(off, kf_end);
     return w;
 }
 

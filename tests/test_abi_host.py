@@ -95,22 +95,23 @@ def test_workspace_sizes(name):
     al = lambda x: -(-x // 256) * 256
     bg = c.batch * c.num_kv_heads
     assert n == al(bg * c.d_k * tp * 2) + al(bg * c.d_v * tp * 2) + al(bg * 64 * 4) + al(bg * 4)
-    # the attention workspace holds K and V in MFMA fragment order, padded:
-    # B*Hkv*(d_k + d_v)*(roundup(T,64)+64)*2 bytes (each part 256-byte aligned), then V's
-    # fp16 scaling (64 partial maxima and one exponent per (b, g))
-    # (G = 1 with only the selected branch adds the block lists and per-slot partials: max and
-    # sum in fp32, the normalized partial output in fp16)
+    # the attention workspace holds V in MFMA fragment order, padded:
+    # B*Hkv*d_v*(roundup(T,64)+64)*2 bytes (each part 256-byte aligned), V's fp16 scaling (64
+    # partial maxima and one exponent per (b, g)), then K in the same order; G = 1 with only
+    # the selected branch puts the block lists and per-slot partials (max and sum in fp32,
+    # the normalized partial output in fp16) over the K copy's bytes, the larger of the two
     rc, n = _ws(c, ops.OP_SPARSE_ATTN)
     tp = -(-c.seq_len // 64) * 64 + 64
     al = lambda x: -(-x // 256) * 256
     bg = c.batch * c.num_kv_heads
-    want = al(bg * c.d_k * tp * 2) + al(bg * c.d_v * tp * 2) + al(bg * 64 * 4) + al(bg * 4)
+    union = al(bg * c.d_k * tp * 2)
     if c.heads_per_group == 1 and c.branches == 2:
         n_chunk = -(-c.seq_len // 1024)
         rows = bg * c.seq_len * c.top_n
         max_tiles = rows // 128 + bg * c.n_slc   # every bucket: at most ceil(n / 128) list tiles
-        want += (al(bg * n_chunk * c.n_slc * 4) + al(bg * c.n_slc * 4) + 2 * al((bg * c.n_slc + 1) * 4)
-                 + al(max_tiles * 4) + 3 * al(rows * 4) + al(rows * c.d_v * 2))
+        union = max(union, al(bg * n_chunk * c.n_slc * 4) + al(bg * c.n_slc * 4) + 2 * al((bg * c.n_slc + 1) * 4)
+                    + al(max_tiles * 4) + 3 * al(rows * 4) + al(rows * c.d_v * 2))
+    want = al(bg * c.d_v * tp * 2) + al(bg * 64 * 4) + al(bg * 4) + union
     assert n == want
     # the fused prefill: the scoring call's and the attention call's workspaces side by side,
     # then room for the lists (int32) and o_cmp (fp32) the caller may not take
