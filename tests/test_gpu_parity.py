@@ -514,19 +514,21 @@ def test_moba(T, top_n):
     assert torch.equal(out, out2), f"moba{T}: the output differs between two runs"
 
 
-@pytest.mark.parametrize("top_n", [2, 3, 5], ids=["picks1", "picks2", "picks4"])
-def test_moba_fused_selection_exact_ties(top_n):
+@pytest.mark.parametrize("top_n,T", [(2, 8192), (3, 8192), (5, 8192), (3, 8100)],
+                         ids=["picks1", "picks2", "picks4", "picks2_ragged"])
+def test_moba_fused_selection_exact_ties(top_n, T):
     """The fused MoBA scoring + selection (one, two or four free picks per row) on integer
     queries and keys, so that every score is an exact small integer on both sides and equal
     scores are common (blocks repeat in pairs): the lists equal the oracle's on every row and
-    head, the lower block index winning each tie."""
-    cfg = MOBA.replace(name=f"moba_ties{top_n}", seq_len=8192, top_n=top_n, num_kv_heads=4)
-    announce(f"moba fused selection, exact ties, top{top_n}")
+    head, the lower block index winning each tie.  T = 8100 ends inside a block and inside a
+    workgroup's 64 tokens (rows past T, an own block with no mean key)."""
+    cfg = MOBA.replace(name=f"moba_ties{top_n}_{T}", seq_len=T, top_n=top_n, num_kv_heads=4)
+    announce(f"moba fused selection, exact ties, top{top_n}, T={T}")
     rng = np.random.default_rng(70 + top_n)
-    T, Hkv, d, lp = cfg.seq_len, cfg.num_kv_heads, cfg.d_k, cfg.slc_block
-    blocks = rng.integers(-2, 3, size=(Hkv, T // lp, d)).astype(np.float64)
+    Hkv, d, lp = cfg.num_kv_heads, cfg.d_k, cfg.slc_block
+    blocks = rng.integers(-2, 3, size=(Hkv, -(-T // lp), d)).astype(np.float64)
     blocks[:, 1::2] = blocks[:, 0::2]   # blocks 2i and 2i+1 equal: their scores tie exactly
-    K = np.repeat(blocks, lp, axis=1)   # every row of a block equal: its mean is exact
+    K = np.repeat(blocks, lp, axis=1)[:, :T]   # every row of a block equal: its mean is exact
     Q = rng.integers(-2, 3, size=(T, Hkv, d)).astype(np.float64)
     kbar, _ = ops.compress(cfg, f64_to_dev_bf16(K[None]))
     sel, _, _ = ops.score_select(cfg, f64_to_dev_bf16(Q[None]), kbar)
