@@ -31,6 +31,7 @@ namespace {
 constexpr int kCol = 128;    // query columns per work item (4 waves x 2 tiles x 16)
 constexpr int kKeys = 64;    // keys per LDS tile
 constexpr float kMobaLazy = 8.f;   // log2 headroom before a column's softmax reference moves
+constexpr int kRun = 16;     // consecutive work items dealt to one XCD
 
 // dynamic LDS of moba_attn_kernel: one K tile and two V tiles of 64 keys
 constexpr size_t moba_attn_lds(int DK, int DV) { return (size_t)kKeys * (DK + 2 * DV) * 2; }
@@ -147,8 +148,12 @@ __global__ __launch_bounds__(256) void moba_scatter_kernel(MobaParams p) {
 
 // ---------------------------------------------------------------------------
 // Work items: [0, n_own) own-block items, then bucket tiles.  Item -> workgroup mapping is
-// XCD-aware: workgroups i, i + 8, i + 16, ... run on one XCD, so consecutive items (the
-// tiles of one bucket, sharing the block's K and V) are given to the same XCD's L2.
+// XCD-aware: workgroups i, i + 8, i + 16, ... run on one XCD, and the items are dealt to the
+// XCDs in runs of kRun consecutive ones, so the tiles of one bucket (which share the block's
+// K and V) mostly meet in one XCD's L2, while every XCD walks the item range in the same
+// order: the items past the real count (the grid is an upper bound) fall at the end on every
+// XCD alike.  (Dealing each XCD one contiguous eighth of the grid left the last XCDs with
+// nothing but those empty items.)
 template <int DK, int DV>
 __global__ __launch_bounds__(256, DK >= 192 ? 2 : 3) void moba_attn_kernel(MobaParams p) {
     constexpr int NDS = DK / 32, NDT = DV / 16;
@@ -163,8 +168,8 @@ __global__ __launch_bounds__(256, DK >= 192 ? 2 : 3) void moba_attn_kernel(MobaP
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int li = lane & 15, lq = lane >> 4;
-    const int nwg = gridDim.x;
-    const int item = (blockIdx.x % 8) * (nwg / 8) + blockIdx.x / 8;   // nwg is a multiple of 8
+    const int xq = blockIdx.x & 7, kq = blockIdx.x >> 3;   // gridDim.x is a multiple of 8 * kRun
+    const int item = (kq / kRun) * (8 * kRun) + xq * kRun + kq % kRun;
     const int n_tiles = p.n_own + p.tile_start[p.n_bucket];
     if (item >= n_tiles) return;
 
@@ -551,7 +556,7 @@ void launch_block_lists(const MobaParams& p, hipStream_t st) {
 bool launch_moba_attn(int DK, int DV, const MobaParams& p, hipStream_t st) {
     launch_block_lists(p, st);
     int nwg = p.n_own + moba_max_tiles(p.B * p.Hkv, p.T, p.top_n, p.n_slc);
-    nwg = (nwg + 7) / 8 * 8;
+    nwg = (nwg + 8 * kRun - 1) / (8 * kRun) * (8 * kRun);
     if (DK == 128 && DV == 128) moba_attn_kernel<128, 128><<<nwg, 256, moba_attn_lds(128, 128), st>>>(p);
     else if (DK == 64 && DV == 64) moba_attn_kernel<64, 64><<<nwg, 256, moba_attn_lds(64, 64), st>>>(p);
     else if (DK == 192 && DV == 128) moba_attn_kernel<192, 128><<<nwg, 256, moba_attn_lds(192, 128), st>>>(p);
