@@ -12,7 +12,8 @@
 //                         own block is excluded; it is scheduled implicitly, see below)
 //   moba_prefix_kernel    per bucket (bh, j): exclusive prefix over chunks, bucket total
 //   moba_scan_kernel      one workgroup: bucket starts and 128-query tile starts
-//   moba_scatter_kernel   per chunk: (token, slot) entries into their bucket
+//   moba_scatter_kernel   per chunk: (token, slot) entries into their bucket, and the
+//                         bucket of every 128-entry list tile
 //   moba_attn_kernel      work item = own-block item (128 consecutive tokens of block j,
 //                         causal) or bucket item (128 listed queries of block j, no mask)
 //   moba_merge_kernel     per (token, head): combine the slots, gate, bf16 store
@@ -120,18 +121,22 @@ __global__ __launch_bounds__(1024) void moba_scan_kernel(MobaParams p) {
     }
 }
 
-// the bucket of every list tile (a direct lookup for the work items, instead of a search
-// over the tile starts)
-__global__ __launch_bounds__(256) void moba_tiles_kernel(MobaParams p) {
-    const int bk = blockIdx.x * 256 + threadIdx.x;
-    if (bk >= p.n_bucket) return;
-    for (int t = p.tile_start[bk]; t < p.tile_start[bk + 1]; ++t) p.tile_bucket[t] = bk;
-}
-
+// per chunk: (token, slot) entries into their bucket.  The chunks' workgroups of a
+// (sequence, head) also write the bucket of every list tile of its buckets (a direct lookup
+// for the work items, instead of a search over the tile starts), the buckets split over the
+// chunks.
 __global__ __launch_bounds__(256) void moba_scatter_kernel(MobaParams p) {
     extern __shared__ int cursor[];   // [n_slc]
     const int c = blockIdx.x, bh = blockIdx.y;
     const int b = bh / p.Hkv, h = bh % p.Hkv;
+    {
+        const int jb0 = (int)((long long)c * p.n_slc / p.n_chunk);
+        const int jb1 = (int)((long long)(c + 1) * p.n_slc / p.n_chunk);
+        for (int jj = jb0; jj < jb1; ++jj) {
+            const int bk = bh * p.n_slc + jj;
+            for (int t = p.tile_start[bk] + (int)threadIdx.x; t < p.tile_start[bk + 1]; t += 256) p.tile_bucket[t] = bk;
+        }
+    }
     const int* pre = p.hist + ((size_t)bh * p.n_chunk + c) * p.n_slc;
     for (int j = threadIdx.x; j < p.n_slc; j += 256) cursor[j] = p.bucket_start[bh * p.n_slc + j] + pre[j];
     __syncthreads();
@@ -549,7 +554,6 @@ void launch_block_lists(const MobaParams& p, hipStream_t st) {
     moba_hist_kernel<<<dim3(p.n_chunk, p.B * p.Hkv), 256, lds_cnt, st>>>(p);
     moba_prefix_kernel<<<(p.n_bucket + 255) / 256, 256, 0, st>>>(p);
     moba_scan_kernel<<<1, 1024, 0, st>>>(p);
-    moba_tiles_kernel<<<(p.n_bucket + 255) / 256, 256, 0, st>>>(p);
     moba_scatter_kernel<<<dim3(p.n_chunk, p.B * p.Hkv), 256, lds_cnt, st>>>(p);
 }
 
