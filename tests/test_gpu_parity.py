@@ -558,7 +558,7 @@ def test_block_major_large_values():
         check_close(gout[b] / 1e5, ref / 1e5, f"block-major large values b={b}")
 
 
-@pytest.mark.parametrize("case", ["b2_lp64_gated", "lp128_own_optional", "top12", "top32", "ramp"])
+@pytest.mark.parametrize("case", ["b2_lp64_gated", "lp128_own_optional", "top1", "top2", "top12", "top32", "ramp"])
 def test_block_major_all_rows(case):
     """G = 1 with only the selected branch runs the block-major schedule (per-block query
     lists, per-slot partials, merge); every row of a ragged batch is checked.  "ramp": keys
@@ -573,6 +573,10 @@ def test_block_major_all_rows(case):
                            score_mode=SCORE_CMP_OVERLAP, seed=22)
     elif case == "ramp":
         cfg = MOBA.replace(name=case, batch=1, seq_len=3000, num_kv_heads=2, seed=29)
+    elif case in ("top1", "top2"):   # the merge's one- and two-slot forms
+        n = int(case[3:])
+        cfg = MOBA.replace(name=case, batch=1, seq_len=1800, num_kv_heads=2, cmp_block=64, cmp_stride=64,
+                           slc_block=64, top_n=n, seed=40 + n)
     else:   # longer lists: the merge's 8-slot and 32-slot forms (ragged, 64-token blocks)
         n = 12 if case == "top12" else 32
         cfg = MOBA.replace(name=case, batch=1, seq_len=2500, num_kv_heads=2, cmp_block=64, cmp_stride=64,
