@@ -320,14 +320,16 @@ __global__ __launch_bounds__(256, 2) void mean_select_kernel(SelParams p) {
         // being of a lower index)
         auto insert = [&](float x, int jx) {
             bool cp = false;   // the slot above was taken by the candidate or shifted
-            float bp = 0.f;
             int ip = 0;
+            float bp = 0.f;
 #pragma unroll
             for (int q = 0; q < K; ++q) {
                 const bool c = x > bs[q];
                 const float tb = bs[q];
                 const int ti = bi[q];
-                bs[q] = cp ? bp : (c ? x : tb);
+                // the new value of slot q is the middle one of (bs[q], x, bs[q-1]) as
+                // bs[q] <= bs[q-1]: the one above if x beat it, else x if x beats bs[q]
+                bs[q] = q == 0 ? (c ? x : tb) : __builtin_amdgcn_fmed3f(tb, x, bp);
                 bi[q] = cp ? ip : (c ? jx : ti);
                 cp = c;
                 bp = tb;
